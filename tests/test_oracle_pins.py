@@ -1,0 +1,392 @@
+"""Pins of the fp64 oracle to facts other than itself (CPU only).
+
+Each step of oracle/hy_oracle.c is checked against brute force on tiny inputs,
+closed forms, invariants, hand-worked fixtures or an independent library
+routine (numpy fp64), chosen so that a dropped term, a wrong sign or index, a
+transposed operand or a wrong tie-break fails at least one test.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+
+import hy_inputs as hi
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+BF16_ONE = 0x3F80
+
+
+def f32_to_bf16_bits(a):
+    """Round fp32 -> bf16 (nearest even) as uint16 bit patterns (test helper)."""
+    u = np.asarray(a, np.float32).view(np.uint32).astype(np.uint64)
+    u = u + 0x7FFF + ((u >> 16) & 1)
+    return (u >> 16).astype(np.uint16)
+
+
+def bf(a):
+    return hi.bf16_to_f32(np.asarray(a, np.uint16)).astype(np.float64)
+
+
+def np_silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def np_swiglu(x, wg, wu, wd):
+    """Dense SwiGLU with numpy fp64 matmuls: x [n][d] -> [n][d]."""
+    g = x @ wg.T
+    u = x @ wu.T
+    return (np_silu(g) * u) @ wd.T
+
+
+# ------------------------------------------------------------------ selection
+def brute_force_sets(lg, k):
+    """The k-subset with the largest logit sum; among equal sums the
+    lexicographically smallest index tuple (== lower index wins ties)."""
+    T, E = lg.shape
+    combos = np.array(list(itertools.combinations(range(E), k)), dtype=np.int64)
+    out = np.empty((T, k), np.int32)
+    for t in range(T):
+        sums = lg[t][combos].sum(axis=1)
+        out[t] = combos[int(np.argmax(sums))]  # argmax returns the first maximum
+    return out
+
+
+@pytest.mark.parametrize("E,k,T", [(16, 2, 40), (10, 3, 40), (8, 4, 40), (64, 4, 6), (5, 5, 3), (7, 1, 30)])
+@pytest.mark.parametrize("kind", ["integers", "continuous"])
+def test_select_matches_brute_force(E, k, T, kind):
+    rng = np.random.default_rng(E * 100 + k)
+    if kind == "integers":
+        lg = rng.integers(-3, 4, size=(T, E)).astype(np.float64)  # many exact ties
+    else:
+        lg = rng.standard_normal((T, E))
+    sets, margin = oracle.select(lg, k)
+    assert np.array_equal(sets, brute_force_sets(lg, k))
+    srt = -np.sort(-lg, axis=1)
+    expect_margin = np.full(T, np.inf) if k == E else srt[:, k - 1] - srt[:, k]
+    assert np.array_equal(margin, expect_margin)
+    # exactly k distinct experts, ascending
+    assert (np.diff(sets, axis=1) > 0).all()
+
+
+def test_select_all_equal_takes_lowest_indices():
+    sets, margin = oracle.select(np.zeros((3, 16)), 4)
+    assert (sets == np.arange(4)).all() and (margin == 0).all()
+
+
+def test_routing_toy_example_from_pages():
+    # tests/golden/routing_toy.txt: 64 experts, K=4 -> 4 active and 60 idle per token;
+    # 256 experts, K=8 -> 8 active, 248 idle.
+    rows = [l for l in open(os.path.join(GOLDEN, "routing_toy.txt")) if l[0] != "#" and l.strip()]
+    for row in rows:
+        f = dict(kv.split("=") for kv in row.split())
+        E, K = int(f["E"]), int(f["K"])
+        rng = np.random.default_rng(E)
+        lg = rng.standard_normal((50, E))
+        sets, _ = oracle.select(lg, K)
+        counts, _, _, _ = oracle.permute(sets, E)
+        for t in range(50):
+            assert len(set(sets[t].tolist())) == int(f["active"])
+            assert E - len(set(sets[t].tolist())) == int(f["idle"])
+        assert counts.sum() == 50 * K
+
+
+# -------------------------------------------------------------------- weights
+def test_weights_closed_forms():
+    rng = np.random.default_rng(1)
+    lg = rng.standard_normal((20, 12)) * 3
+    s1, _ = oracle.select(lg, 1)
+    assert (oracle.weights(lg, s1) == 1.0).all()
+    s2, _ = oracle.select(lg, 2)
+    w2 = oracle.weights(lg, s2)
+    for t in range(20):
+        a, b = s2[t]
+        sig = 1.0 / (1.0 + math.exp(-(lg[t, a] - lg[t, b])))
+        assert abs(w2[t, 0] - sig) < 1e-15 and abs(w2[t, 1] - (1 - sig)) < 1e-15
+    s4, _ = oracle.select(np.full((2, 9), 0.7), 4)
+    assert np.allclose(oracle.weights(np.full((2, 9), 0.7), s4), 0.25, atol=0, rtol=1e-15)
+
+
+def test_weights_are_softmax_renormalised_over_set():
+    rng = np.random.default_rng(2)
+    lg = rng.standard_normal((30, 32)) * 4
+    sets, _ = oracle.select(lg, 8)
+    w = oracle.weights(lg, sets)
+    p = np.exp(lg) / np.exp(lg).sum(axis=1, keepdims=True)  # full softmax first
+    ps = np.take_along_axis(p, sets.astype(np.int64), axis=1)
+    assert np.allclose(w, ps / ps.sum(axis=1, keepdims=True), rtol=1e-13, atol=0)
+    assert np.allclose(w.sum(axis=1), 1.0, atol=1e-15)
+    # ordering: the largest logit in the set carries the largest weight
+    lsel = np.take_along_axis(lg, sets.astype(np.int64), axis=1)
+    assert (np.argmax(w, axis=1) == np.argmax(lsel, axis=1)).all()
+
+
+# -------------------------------------------------------------------- permute
+def test_permute_equals_stable_sort():
+    rng = np.random.default_rng(3)
+    T, E, k = 300, 24, 3
+    lg = rng.standard_normal((T, E))
+    sets, _ = oracle.select(lg, k)
+    counts, offsets, perm_src, pos = oracle.permute(sets, E)
+    flat = sets.ravel()
+    assert np.array_equal(perm_src, np.argsort(flat, kind="stable"))
+    assert np.array_equal(counts, np.bincount(flat, minlength=E))
+    assert np.array_equal(offsets, np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=E))]))
+    assert np.array_equal(pos[perm_src], np.arange(T * k))
+    assert np.array_equal(np.sort(perm_src), np.arange(T * k))
+    assert counts.sum() == T * k
+
+
+def test_permute_empty_and_full_experts():
+    sets = np.tile(np.array([[1, 4]], np.int32), (5, 1))
+    counts, offsets, perm_src, _ = oracle.permute(sets, 6)
+    assert counts.tolist() == [0, 5, 0, 0, 5, 0]
+    assert offsets.tolist() == [0, 0, 5, 5, 5, 10, 10]
+    assert perm_src.tolist() == [0, 2, 4, 6, 8, 1, 3, 5, 7, 9]
+
+
+# --------------------------------------------------------------------- logits
+def test_logits_unit_vectors_and_bias():
+    rng = np.random.default_rng(4)
+    E, d = 6, 10
+    wr = f32_to_bf16_bits(rng.standard_normal((E, d)))
+    x = np.zeros((d, d), np.uint16)
+    x[np.arange(d), np.arange(d)] = BF16_ONE  # token t is the unit vector e_t
+    bias = rng.standard_normal(E).astype(np.float32)
+    lg = oracle.logits(x, wr, bias)
+    assert np.array_equal(lg, bf(wr).T + bias.astype(np.float64)[None, :])
+    assert np.array_equal(oracle.logits(x, wr), bf(wr).T)
+
+
+def test_logits_match_numpy_matmul():
+    rng = np.random.default_rng(5)
+    x = f32_to_bf16_bits(rng.standard_normal((17, 96)))
+    wr = f32_to_bf16_bits(rng.standard_normal((11, 96)) / 10)
+    assert np.allclose(oracle.logits(x, wr), bf(x) @ bf(wr).T, rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------------------------- expert FFN
+def test_ffn_scalar_closed_form():
+    for xv, g, u, dn in [(1.5, 0.75, -2.0, 0.5), (-3.0, 1.25, 1.0, -1.0), (0.0, 1.0, 1.0, 1.0)]:
+        x = f32_to_bf16_bits([[xv]])
+        y = oracle.ffn(x, f32_to_bf16_bits([[g]]), f32_to_bf16_bits([[u]]), f32_to_bf16_bits([[dn]]))
+        z = g * xv
+        assert y[0, 0] == pytest.approx(dn * (z / (1 + math.exp(-z))) * (u * xv), rel=1e-15, abs=0)
+
+
+def test_ffn_index_order_with_one_hot_weights():
+    # d != I so a transposed operand would address different entries.
+    d, I = 12, 5
+    a, g, u, v = 1.5, 0.5, -1.25, 2.0
+    for j0, i0, m0 in [(0, 0, 0), (11, 4, 7), (3, 2, 11)]:
+        x = np.zeros((1, d), np.uint16); x[0, j0] = f32_to_bf16_bits([a])[0]
+        wg = np.zeros((I, d), np.uint16); wg[i0, j0] = f32_to_bf16_bits([g])[0]
+        wu = np.zeros((I, d), np.uint16); wu[i0, j0] = f32_to_bf16_bits([u])[0]
+        wd = np.zeros((d, I), np.uint16); wd[m0, i0] = f32_to_bf16_bits([v])[0]
+        y = oracle.ffn(x, wg, wu, wd)
+        expect = np.zeros(d)
+        expect[m0] = v * (g * a / (1 + math.exp(-g * a))) * (u * a)
+        assert np.array_equal(y[0], expect)
+
+
+def test_ffn_matches_numpy():
+    rng = np.random.default_rng(6)
+    n, d, I = 5, 64, 48
+    x = f32_to_bf16_bits(rng.standard_normal((n, d)))
+    wg = f32_to_bf16_bits(rng.standard_normal((I, d)) / 8)
+    wu = f32_to_bf16_bits(rng.standard_normal((I, d)) / 8)
+    wd = f32_to_bf16_bits(rng.standard_normal((d, I)) / 7)
+    y = oracle.ffn(x, wg, wu, wd, nthreads=3)
+    assert np.allclose(y, np_swiglu(bf(x), bf(wg), bf(wu), bf(wd)), rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- whole layer
+def small_layer(seed=0, T=24, d=64, E=8, k=2, I=32, bias=False):
+    cfg = hi.LayerConfig("t", T=T, d=d, E=E, k=k, I=I, seed=seed)
+    L = hi.host_layer(cfg)
+    if bias:
+        L["bias"] = hi.zipf_bias(E, seed)
+    return cfg, L
+
+
+def run_forward(L, k, **kw):
+    return oracle.forward(L["x"], L["router"], L["bias"], L["gate"], L["up"], L["down"],
+                          L["shared"]["gate"], L["shared"]["up"], L["shared"]["down"], k, **kw)
+
+
+def dense_masked_reference(L, k):
+    """Independent formulation: every expert on every token (numpy), top-k by a
+    lexsort on (-logit, index), softmax renormalised, masked sum."""
+    x = bf(L["x"]); wr = bf(L["router"])
+    lg = x @ wr.T
+    if L["bias"] is not None:
+        lg = lg + L["bias"].astype(np.float64)
+    T, E = lg.shape
+    out = np_swiglu(x, bf(L["shared"]["gate"]), bf(L["shared"]["up"]), bf(L["shared"]["down"]))
+    ys = np.stack([np_swiglu(x, bf(L["gate"][e]), bf(L["up"][e]), bf(L["down"][e])) for e in range(E)])
+    for t in range(T):
+        order = np.lexsort((np.arange(E), -lg[t]))[:k]
+        p = np.exp(lg[t, order] - lg[t, order].max())
+        p /= p.sum()
+        out[t] += (p[:, None] * ys[order, t]).sum(axis=0)
+    return out
+
+
+@pytest.mark.parametrize("bias", [False, True])
+def test_forward_matches_dense_masked_numpy(bias):
+    cfg, L = small_layer(bias=bias)
+    ref = run_forward(L, cfg.k)
+    assert np.allclose(ref["out"], dense_masked_reference(L, cfg.k), rtol=1e-11, atol=1e-11)
+
+
+def test_tiny_config_forward_matches_dense_masked_numpy():
+    cfg = hi.CONFIGS["tiny"]
+    L = hi.host_layer(cfg)
+    ref = run_forward(L, cfg.k)
+    assert np.allclose(ref["out"], dense_masked_reference(L, cfg.k), rtol=1e-11, atol=1e-11)
+    assert np.allclose(ref["w"].sum(axis=1), 1.0, atol=1e-15)
+
+
+def test_identical_experts_reduce_to_dense_swiglu():
+    cfg, L = small_layer(seed=1, bias=True)
+    for key in ("gate", "up", "down"):
+        L[key] = np.repeat(L[key][2:3], cfg.E, axis=0)
+    ref = run_forward(L, cfg.k)
+    x = bf(L["x"])
+    dense = np_swiglu(x, bf(L["shared"]["gate"]), bf(L["shared"]["up"]), bf(L["shared"]["down"])) + \
+        np_swiglu(x, bf(L["gate"][0]), bf(L["up"][0]), bf(L["down"][0]))
+    assert np.allclose(ref["out"], dense, rtol=1e-12, atol=1e-12)
+
+
+def test_zero_down_projection_leaves_shared_expert():
+    cfg, L = small_layer(seed=2)
+    L["down"] = np.zeros_like(L["down"])
+    ref = run_forward(L, cfg.k)
+    shared = oracle.ffn(L["x"], L["shared"]["gate"], L["shared"]["up"], L["shared"]["down"])
+    assert np.array_equal(ref["out"], shared)
+
+
+def test_linear_in_routed_down_projection():
+    cfg, L = small_layer(seed=3)
+    base = run_forward(L, cfg.k)["out"]
+    shared = oracle.ffn(L["x"], L["shared"]["gate"], L["shared"]["up"], L["shared"]["down"])
+    L2 = dict(L)
+    L2["down"] = f32_to_bf16_bits(bf(L["down"]) * 2.0)  # exact in bf16
+    doubled = run_forward(L2, cfg.k)["out"]
+    assert np.allclose(doubled - shared, 2.0 * (base - shared), rtol=1e-12, atol=1e-13)
+
+
+def test_sets_override_substitutes_routing():
+    cfg, L = small_layer(seed=4)
+    ref = run_forward(L, cfg.k)
+    alt = ref["sets"].copy()
+    alt[0] = [e for e in range(cfg.E) if e not in ref["sets"][0]][: cfg.k]
+    sub = run_forward(L, cfg.k, sets_in=alt)
+    assert np.array_equal(sub["out"][1:], ref["out"][1:])
+    assert not np.allclose(sub["out"][0], ref["out"][0])
+    assert np.array_equal(sub["sets"], alt)
+
+
+def test_combine_closed_form():
+    ys = np.array([[1.0, 2.0]]); yr = np.array([[[10.0, 20.0], [100.0, 200.0]]])
+    w = np.array([[0.25, 0.75]])
+    assert np.array_equal(oracle.combine(ys, yr, w), np.array([[1 + 2.5 + 75, 2 + 5 + 150]]))
+
+
+def test_invalid_arguments_rejected():
+    with pytest.raises(ValueError):
+        oracle.select(np.zeros((2, 4)), 5)
+    with pytest.raises(ValueError):
+        oracle.permute(np.array([[0, 9]], np.int32), 4)
+
+
+# --------------------------------------------------------------------- Sherry
+def pack_codes(codes):
+    """Independent packer for the test: 32 codes -> 5 words (160-bit LE)."""
+    B = 0
+    for g, c in enumerate(codes):
+        B |= int(c) << (5 * g)
+    return np.array([(B >> (32 * i)) & 0xFFFFFFFF for i in range(5)], np.uint32)
+
+
+def expected_group(code):
+    z = code & 3
+    vals, nz = [], 0
+    for q in range(4):
+        if q == z:
+            vals.append(0)
+        else:
+            vals.append(-1 if (code >> (2 + nz)) & 1 else 1)
+            nz += 1
+    return vals
+
+
+def test_sherry_all_32_codes():
+    words = pack_codes(range(32))
+    tern, _ = oracle.sherry_decode(words[None, :])
+    groups = tern.reshape(32, 4)
+    patterns = set()
+    for c in range(32):
+        g = groups[c].tolist()
+        assert g.count(0) == 1, "exactly one zero per group"
+        assert g.index(0) == (c & 3)
+        nonzero = [v for v in g if v != 0]
+        assert nonzero == [(-1 if (c >> (2 + i)) & 1 else 1) for i in range(3)]
+        patterns.add(tuple(g))
+    # bijection onto the 4 * 2^3 = 32 one-zero ternary groups
+    every = {p for p in itertools.product([-1, 0, 1], repeat=4) if p.count(0) == 1}
+    assert patterns == every and len(every) == 32
+
+
+def test_sherry_hand_worked_blocks():
+    for line in open(os.path.join(GOLDEN, "sherry_blocks.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        left, right = line.split("|")
+        words = np.array([int(w, 16) for w in left.split()], np.uint32)
+        tern, _ = oracle.sherry_decode(words[None, :])
+        groups = tern.reshape(32, 4)
+        listed = {}
+        for item in right.split():
+            g, vals = item.split(":")
+            listed[int(g)] = [int(v) for v in vals.split(",")]
+        for g in range(32):
+            if g in listed:
+                assert groups[g].tolist() == listed[g], (line, g)
+            elif not (words == 0xFFFFFFFF).all():
+                # groups not listed decode from code 0 unless their bits are set
+                code = (sum(int(w) << (32 * i) for i, w in enumerate(words)) >> (5 * g)) & 31
+                assert groups[g].tolist() == expected_group(code)
+
+
+def test_sherry_random_round_trip_and_scales():
+    rng = np.random.default_rng(7)
+    rows, cols = 6, 384
+    codes = rng.integers(0, 32, size=(rows, cols // 4))
+    packed = np.stack([np.concatenate([pack_codes(codes[r, b * 32:(b + 1) * 32]) for b in range(cols // 128)])
+                       for r in range(rows)])
+    scale = f32_to_bf16_bits(rng.uniform(0.5, 1.5, rows) / 16)
+    tern, w = oracle.sherry_decode(packed, scale)
+    for r in range(rows):
+        for g in range(cols // 4):
+            assert tern[r, 4 * g:4 * g + 4].tolist() == expected_group(int(codes[r, g]))
+    # repack from the decoded values: invert expected_group
+    inv = {tuple(expected_group(c)): c for c in range(32)}
+    recodes = np.array([[inv[tuple(tern[r, 4 * g:4 * g + 4])] for g in range(cols // 4)] for r in range(rows)])
+    assert np.array_equal(recodes, codes)
+    assert np.array_equal(bf(w), bf(scale)[:, None] * tern)
+    # 1.25 bits per weight: 5 words of 32 bits per 128 weights
+    assert packed.nbytes * 8 == 1.25 * rows * cols
+
+
+def test_sherry_ternary_gemv_equals_dense_gemv():
+    rng = np.random.default_rng(8)
+    packed = hi.words_u32(0, 10, 4 * 10).reshape(4, 10)
+    scale = f32_to_bf16_bits(rng.uniform(0.5, 1.5, 4) / 16)
+    tern, w = oracle.sherry_decode(packed, scale)
+    x = rng.standard_normal(256)
+    dense = bf(w) @ x
+    factored = bf(scale) * (tern.astype(np.float64) @ x)
+    assert np.allclose(dense, factored, rtol=1e-14, atol=1e-15)
