@@ -1,0 +1,159 @@
+/*
+ * hy_moe.h — C ABI of an MI355X-native (gfx950) forward pass of one sparse
+ * Mixture-of-Experts FFN layer.
+ *
+ * What the layer computes (m.xxqk.cn Hy4 preview explainer, sections 2.1
+ * "FFN 层拆分" and 2.2 "路由机制"; Tencent Hy4 preview model card; the
+ * app.myzaker.com Hy4 Preview news, section "770B 不是简单堆参数"):
+ *   the FFN is split into E routed experts plus one shared expert; a router
+ *   scores each token against every routed expert, the top-k are activated,
+ *   every token also passes through the shared expert, and the expert outputs
+ *   are merged into the layer output. Hy4 preview: E = 256, k = 8, d = 6144.
+ * Readings taken where the pages are silent (each is a fixed part of this ABI):
+ *   logits   l[t][e] = sum_i x[t][i] W_router[e][i] (+ router_bias[e]), fp32 accumulate
+ *   select   the k largest logits, ties to the lower expert index
+ *   weights  w[t][e] = softmax over the selected set: exp(l_e - l_max) / sum
+ *   expert   y = W_down (silu(W_gate x) * (W_up x)), silu(z) = z / (1 + e^-z)
+ *   output   out[t] = bf16( y_shared(x_t) + sum_{e in S_t} w[t][e] y_e(x_t) ),
+ *            the sum taken in fp32 over the set in ascending expert order and
+ *            rounded once (nearest even).
+ *
+ * Conventions for every entry point:
+ *  - Tensors are row-major and contiguous. "bf16" means IEEE bfloat16 bit
+ *    patterns. Weight matrices are stored [out][in] (the input dimension is
+ *    contiguous): W_gate/W_up [E][I][d], W_down [E][d][I], shared [I][d]/[d][I].
+ *  - Pointers documented as DEVICE must point to memory of the device current on
+ *    the calling thread; the caller owns every buffer and the library never
+ *    frees caller memory.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). Work
+ *    is enqueued on it and the call returns without waiting; device-side faults
+ *    surface at the caller's next synchronisation.
+ *  - Every argument check runs before anything is enqueued. On error nothing is
+ *    enqueued and the outputs are untouched.
+ *  - Results are deterministic: the same inputs on the same device give
+ *    bitwise-identical outputs (no floating-point atomics anywhere).
+ *  - Supported envelope: 1 <= k <= min(E, 16), E <= 1024, d % 128 == 0,
+ *    I % 128 == 0, T * k < 2^31. T == 0 is a no-op returning HY_MOE_OK.
+ */
+#ifndef HY_MOE_H
+#define HY_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HY_MOE_OK = 0,
+  HY_MOE_ERR_INVALID_ARG = -1, /* null required pointer, negative size, k < 1, k > E */
+  HY_MOE_ERR_UNSUPPORTED = -2, /* shape outside the supported envelope */
+  HY_MOE_ERR_WORKSPACE = -3,   /* workspace given but smaller than hy_moe_workspace_size() */
+  HY_MOE_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+} hy_moe_status;
+
+/* Storage format of the routed experts' weights (the shared expert is bf16). */
+typedef enum {
+  HY_MOE_WEIGHTS_BF16 = 0,
+  /* Sherry sparse-ternary weights (ai.chattools.top article on compressing Hy4
+   * preview to 214GB, section "极限压缩背后的技术支柱：Sherry 与 MIX-STQ1_0"):
+   * groups of 4 consecutive weights along a row hold values in {-1,0,+1} with
+   * exactly one zero (4 positions x 2^3 signs = 32 codes = 5 bits, 1.25 bits
+   * per weight); weight = row scale (bf16) * ternary value.
+   * Packed layout: a row of C weights is C/128 blocks of 5 uint32 words. The
+   * 5 words of a block, little-endian, form a 160-bit integer B; group g of the
+   * block (weights 4g..4g+3) has code (B >> 5g) & 31. Code bits 0-1 give the
+   * position of the zero in the group; bits 2, 3, 4 give the signs of the
+   * first, second and third non-zero weight in ascending position (1 means -1).
+   * Every bit pattern is a valid block. */
+  HY_MOE_WEIGHTS_SHERRY_TERNARY = 1
+} hy_moe_wfmt;
+
+/* Which kernels run the experts. AUTO picks by the average rows per expert. */
+typedef enum {
+  HY_MOE_PATH_AUTO = 0,
+  HY_MOE_PATH_STREAM = 1,  /* weight-streaming kernels: each touched expert's weights read once per
+                              32 rows; meant for decode-sized batches */
+  HY_MOE_PATH_GROUPED = 2  /* LDS-tiled grouped GEMM on bf16 MFMA; prefill-sized batches (bf16 only) */
+} hy_moe_path;
+
+/*
+ * hy_moe_forward — the whole layer, bf16 weights, no router bias.
+ *   x         DEVICE bf16 [T][d]       token activations
+ *   W_router  DEVICE bf16 [E][d]
+ *   W_gate    DEVICE bf16 [E][I][d]    routed experts
+ *   W_up      DEVICE bf16 [E][I][d]
+ *   W_down    DEVICE bf16 [E][d][I]
+ *   Ws_gate   DEVICE bf16 [I][d]       shared expert
+ *   Ws_up     DEVICE bf16 [I][d]
+ *   Ws_down   DEVICE bf16 [d][I]
+ *   out       DEVICE bf16 [T][d]       written in full
+ * Scratch memory is allocated stream-ordered on `stream` (hipMallocAsync) and
+ * released stream-ordered before returning; use hy_moe_forward_ex with a
+ * caller workspace to avoid any allocation.
+ */
+int hy_moe_forward(const void* x, const void* W_router, const void* W_gate, const void* W_up,
+                   const void* W_down, const void* Ws_gate, const void* Ws_up, const void* Ws_down,
+                   int64_t T, int64_t d, int64_t E, int64_t k, int64_t I, void* out, void* stream);
+
+/* Full argument set of hy_moe_forward_ex. Zero-initialise, then fill. */
+typedef struct hy_moe_args {
+  /* inputs (DEVICE) */
+  const void* x;             /* bf16 [T][d] */
+  const void* W_router;      /* bf16 [E][d] */
+  const float* router_bias;  /* fp32 [E] or NULL; added to the logits before both the
+                                selection and the softmax */
+  hy_moe_wfmt expert_format;
+  const void* W_gate;        /* BF16: bf16 [E][I][d] */
+  const void* W_up;          /* BF16: bf16 [E][I][d] */
+  const void* W_down;        /* BF16: bf16 [E][d][I] */
+  const void* Wq_gate;       /* SHERRY_TERNARY: uint32 [E][I][d/128*5] */
+  const void* Wq_up;         /* SHERRY_TERNARY: uint32 [E][I][d/128*5] */
+  const void* Wq_down;       /* SHERRY_TERNARY: uint32 [E][d][I/128*5] */
+  const void* S_gate;        /* SHERRY_TERNARY: bf16 [E][I] row scales */
+  const void* S_up;          /* SHERRY_TERNARY: bf16 [E][I] */
+  const void* S_down;        /* SHERRY_TERNARY: bf16 [E][d] */
+  const void* Ws_gate;       /* bf16 [I][d] */
+  const void* Ws_up;         /* bf16 [I][d] */
+  const void* Ws_down;       /* bf16 [d][I] */
+  int64_t T, d, E, k, I;
+  /* output (DEVICE) */
+  void* out;                 /* bf16 [T][d] */
+  /* scratch (DEVICE): NULL => allocated stream-ordered on the stream */
+  void* workspace;
+  size_t workspace_bytes;
+  /* optional routing outputs (DEVICE, NULL to skip) */
+  int32_t* topk_idx;         /* [T][k] selected experts, ascending expert id */
+  float* topk_w;             /* [T][k] merge weights, same order */
+  int32_t* counts;           /* [E]    tokens per routed expert */
+  int32_t* offsets;          /* [E+1]  exclusive prefix sum of counts */
+  int32_t* perm_src;         /* [T*k]  t*k+j of the pair at expert-contiguous row p
+                                (experts ascending, tokens ascending within one) */
+  float* margin;             /* [T]    k-th minus (k+1)-th largest logit (fp32); +inf if k == E */
+  hy_moe_path path;
+} hy_moe_args;
+
+/* hy_moe_forward_ex — the layer with every option. Returns a hy_moe_status. */
+int hy_moe_forward_ex(const hy_moe_args* args, void* stream);
+
+/* Bytes of DEVICE workspace hy_moe_forward_ex needs for this shape (for the
+ * largest of the paths it may pick); 0 for invalid shapes. Alignment: 256 B. */
+size_t hy_moe_workspace_size(int64_t T, int64_t d, int64_t E, int64_t k, int64_t I, int expert_format);
+
+/* Static text for a status code. */
+const char* hy_moe_status_string(int status);
+
+/*
+ * hy_moe_sherry_pack_host — HOST helper: pack ternary values into the layout
+ * above. tern: HOST int8 [rows][cols] in {-1,0,+1}, exactly one zero per group
+ * of 4 along a row, cols % 128 == 0; packed: HOST uint32 [rows][cols/128*5].
+ * Returns HY_MOE_ERR_INVALID_ARG (packed untouched) if a group breaks the rule.
+ */
+int hy_moe_sherry_pack_host(const int8_t* tern, int64_t rows, int64_t cols, uint32_t* packed);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HY_MOE_H */

@@ -1,0 +1,179 @@
+"""Python binding of libhy_moe.so, the MI355X (gfx950) forward pass of one
+sparse-MoE FFN layer (router -> top-k -> dispatch -> SwiGLU experts + shared
+expert -> weighted combine).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels. PyTorch supplies device memory and the stream. The entry points carry
+the C ABI's names (include/hy_moe.h documents each). There is no fallback: if
+the library is missing, importing this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["forward", "forward_ex", "forward_layer", "workspace_size", "status_string", "sherry_pack_host",
+           "HyMoeError", "lib", "LIB_PATH"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhy_moe.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+WEIGHTS_BF16, WEIGHTS_SHERRY_TERNARY = 0, 1
+PATH_AUTO, PATH_STREAM, PATH_GROUPED = 0, 1, 2
+
+EXPORTED = ["hy_moe_forward", "hy_moe_forward_ex", "hy_moe_workspace_size", "hy_moe_status_string",
+            "hy_moe_sherry_pack_host"]
+
+
+class HyMoeArgs(ctypes.Structure):
+    """Mirror of struct hy_moe_args."""
+    _fields_ = [
+        ("x", ctypes.c_void_p), ("W_router", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
+        ("expert_format", ctypes.c_int),
+        ("W_gate", ctypes.c_void_p), ("W_up", ctypes.c_void_p), ("W_down", ctypes.c_void_p),
+        ("Wq_gate", ctypes.c_void_p), ("Wq_up", ctypes.c_void_p), ("Wq_down", ctypes.c_void_p),
+        ("S_gate", ctypes.c_void_p), ("S_up", ctypes.c_void_p), ("S_down", ctypes.c_void_p),
+        ("Ws_gate", ctypes.c_void_p), ("Ws_up", ctypes.c_void_p), ("Ws_down", ctypes.c_void_p),
+        ("T", ctypes.c_int64), ("d", ctypes.c_int64), ("E", ctypes.c_int64), ("k", ctypes.c_int64),
+        ("I", ctypes.c_int64),
+        ("out", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("topk_idx", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("counts", ctypes.c_void_p),
+        ("offsets", ctypes.c_void_p), ("perm_src", ctypes.c_void_p), ("margin", ctypes.c_void_p),
+        ("path", ctypes.c_int),
+    ]
+
+
+class HyMoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    L.hy_moe_forward.argtypes = [vp] * 8 + [i64] * 5 + [vp, vp]
+    L.hy_moe_forward.restype = ctypes.c_int
+    L.hy_moe_forward_ex.argtypes = [ctypes.POINTER(HyMoeArgs), vp]
+    L.hy_moe_forward_ex.restype = ctypes.c_int
+    L.hy_moe_workspace_size.argtypes = [i64] * 5 + [ctypes.c_int]
+    L.hy_moe_workspace_size.restype = ctypes.c_size_t
+    L.hy_moe_status_string.argtypes = [ctypes.c_int]
+    L.hy_moe_status_string.restype = ctypes.c_char_p
+    L.hy_moe_sherry_pack_host.argtypes = [vp, i64, i64, vp]
+    L.hy_moe_sherry_pack_host.restype = ctypes.c_int
+    return L
+
+
+_lib = _load()
+
+
+def lib():
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return _lib.hy_moe_status_string(status).decode()
+
+
+def workspace_size(T, d, E, k, I, expert_format=WEIGHTS_BF16) -> int:
+    return int(_lib.hy_moe_workspace_size(T, d, E, k, I, expert_format))
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def forward(x, W_router, W_gate, W_up, W_down, Ws_gate, Ws_up, Ws_down, k, out=None, stream=None):
+    """hy_moe_forward on torch tensors (bf16, contiguous, on the GPU). Returns out [T][d]."""
+    import torch
+    T, d = x.shape
+    E, I = W_gate.shape[0], W_gate.shape[1]
+    if out is None:
+        out = torch.empty(T, d, dtype=torch.bfloat16, device=x.device)
+    rc = _lib.hy_moe_forward(_ptr(x), _ptr(W_router), _ptr(W_gate), _ptr(W_up), _ptr(W_down), _ptr(Ws_gate),
+                             _ptr(Ws_up), _ptr(Ws_down), T, d, E, k, I, _ptr(out), _stream(stream))
+    if rc != OK:
+        raise HyMoeError(rc, "hy_moe_forward")
+    return out
+
+
+def forward_ex(args: HyMoeArgs, stream=None) -> int:
+    """hy_moe_forward_ex; returns the status code unchanged."""
+    return _lib.hy_moe_forward_ex(ctypes.byref(args), _stream(stream))
+
+
+def forward_layer(inp: dict, k: int, *, want_routing=False, path=PATH_AUTO, workspace=None, out=None,
+                  stream=None):
+    """Runs hy_moe_forward_ex on a dict of device tensors as made by
+    hy_inputs.dev_layer(): x, router, bias, shared{gate,up,down} and either
+    gate/up/down (bf16) or qgate/qup/qdown + sgate/sup/sdown (ternary).
+    Returns dict(out, and with want_routing: topk_idx, topk_w, counts, offsets,
+    perm_src, margin)."""
+    import torch
+    x = inp["x"]
+    T, d = x.shape
+    E = inp["router"].shape[0]
+    ternary = "qgate" in inp
+    I = inp["sgate"].shape[1] if ternary else inp["gate"].shape[1]
+    dev = x.device
+    a = HyMoeArgs()
+    a.x, a.W_router, a.router_bias = _ptr(x), _ptr(inp["router"]), _ptr(inp.get("bias"))
+    a.expert_format = WEIGHTS_SHERRY_TERNARY if ternary else WEIGHTS_BF16
+    if ternary:
+        a.Wq_gate, a.Wq_up, a.Wq_down = _ptr(inp["qgate"]), _ptr(inp["qup"]), _ptr(inp["qdown"])
+        a.S_gate, a.S_up, a.S_down = _ptr(inp["sgate"]), _ptr(inp["sup"]), _ptr(inp["sdown"])
+    else:
+        a.W_gate, a.W_up, a.W_down = _ptr(inp["gate"]), _ptr(inp["up"]), _ptr(inp["down"])
+    sh = inp["shared"]
+    a.Ws_gate, a.Ws_up, a.Ws_down = _ptr(sh["gate"]), _ptr(sh["up"]), _ptr(sh["down"])
+    a.T, a.d, a.E, a.k, a.I = T, d, E, k, I
+    if out is None:
+        out = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+    a.out = _ptr(out)
+    if workspace is not None:
+        a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    res = {"out": out}
+    if want_routing:
+        i32, f32 = torch.int32, torch.float32
+        res.update(topk_idx=torch.empty(T, k, dtype=i32, device=dev), topk_w=torch.empty(T, k, dtype=f32, device=dev),
+                   counts=torch.empty(E, dtype=i32, device=dev), offsets=torch.empty(E + 1, dtype=i32, device=dev),
+                   perm_src=torch.empty(T * k, dtype=i32, device=dev), margin=torch.empty(T, dtype=f32, device=dev))
+        a.topk_idx, a.topk_w = _ptr(res["topk_idx"]), _ptr(res["topk_w"])
+        a.counts, a.offsets = _ptr(res["counts"]), _ptr(res["offsets"])
+        a.perm_src, a.margin = _ptr(res["perm_src"]), _ptr(res["margin"])
+    a.path = path
+    rc = forward_ex(a, stream)
+    if rc != OK:
+        raise HyMoeError(rc, "hy_moe_forward_ex")
+    return res
+
+
+def alloc_workspace(T, d, E, k, I, expert_format=WEIGHTS_BF16, device="cuda"):
+    import torch
+    n = workspace_size(T, d, E, k, I, expert_format)
+    if n == 0:
+        raise HyMoeError(ERR_INVALID_ARG, "hy_moe_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def sherry_pack_host(tern):
+    """hy_moe_sherry_pack_host on a host int8 numpy array [rows][cols]."""
+    import numpy as np
+    tern = np.ascontiguousarray(tern, dtype=np.int8)
+    rows, cols = tern.shape
+    packed = np.zeros((rows, cols // 128 * 5), np.uint32)
+    rc = _lib.hy_moe_sherry_pack_host(tern.ctypes.data, rows, cols, packed.ctypes.data)
+    if rc != OK:
+        raise HyMoeError(rc, "hy_moe_sherry_pack_host")
+    return packed

@@ -1,0 +1,77 @@
+// Device helpers shared by the MoE layer's HIP kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hymoe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// Rows per expert-block in the dispatch masks (one bit per token of a block).
+constexpr int kMaskBlock = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// D[16x16] += A[16x32] B[32x16]; lane l holds row (l&15) of A, column (l&15) of B and
+// column (l&15), rows 4*(l>>4)+[0,4) of D. Each lane's 8 k-values of A and B sit at the
+// same k positions, so any fixed assignment of k to (lane>>4, element) is a valid
+// reduction order: the kernels use it to load longer contiguous runs per lane.
+__device__ __forceinline__ f32x4 mfma16x16x32(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// D[32x32] += A[32x16] B[16x32]; lane l holds row (l&31) of A, column (l&31) of B and
+// column (l&31) of D, rows 8*(i/4) + 4*(l>>5) + (i%4) for accumulator i.
+__device__ __forceinline__ f32x16 mfma32x32x16(uint4 a, uint4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Streaming load of data read exactly once (expert weights): non-temporal hint.
+__device__ __forceinline__ uint4 ldg16_stream(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// Wave-wide inclusive prefix sum (64 lanes).
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int n = __shfl_up(v, o, 64);
+    if (lane >= o) v += n;
+  }
+  return v;
+}
+
+// Row r of the dispatched row space -> token index. Rows [0, T*k) are the routed
+// (token, slot) pairs in expert-contiguous order; rows [T*k, T*k+T) belong to the
+// shared expert in token order.
+__device__ __forceinline__ int row_token(int r, const int* __restrict__ perm_src, int Tk, int k) {
+  return r < Tk ? perm_src[r] / k : r - Tk;
+}
+
+}  // namespace hymoe

@@ -1,0 +1,65 @@
+// Launchers of the MoE layer's kernels; each enqueues on `stream` and returns the
+// launch status. Argument shapes are validated by the C ABI before any launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hymoe {
+
+// Per-call device state carved from the workspace.
+struct Plan {
+  int T, d, E, k, I;
+  int Tk;          // routed rows, T*k
+  int rows;        // routed + shared rows, T*k + T
+  int nblk;        // token blocks of kMaskBlock
+  int ks;          // router split-K factor
+  int gemm_bm;     // grouped-GEMM M tile
+  int max_tiles;   // upper bound of grouped-GEMM M tiles
+  // workspace buffers
+  float* part;               // [ks][T][E] router partial logits
+  int32_t* topk_idx;         // [T][k]
+  float* topk_w;             // [T][k]
+  unsigned long long* mask;  // [nblk][E] token bitmask per (block, expert)
+  int32_t* blk_base;         // [nblk][E] first row of (block, expert)
+  int32_t* offs;             // [E+2] row offsets, expert E = shared
+  int32_t* meta;             // [4] {touched experts incl. shared, grouped-GEMM tiles, -, -}
+  int32_t* touched;          // [E+1] touched experts, ascending, shared (E) last
+  int2* tiles;               // [max_tiles] {expert, first row within expert}
+  int32_t* perm_src;         // [T*k]
+  int32_t* pos;              // [T*k] inverse of perm_src
+  uint16_t* h;               // bf16 [rows][I]
+  void* y;                   // [rows][d]: fp32 (stream path) or bf16 (grouped path)
+};
+
+hipError_t launch_route(const Plan& p, const uint16_t* x, const uint16_t* w_router, const float* bias,
+                        float* margin_out, hipStream_t s);
+hipError_t launch_permute(const Plan& p, int32_t* counts_out, int32_t* offsets_out, hipStream_t s);
+
+struct ExpertWeights {
+  // bf16 routed experts
+  const uint16_t* gate;
+  const uint16_t* up;
+  const uint16_t* down;
+  // Sherry ternary routed experts
+  const uint32_t* qgate;
+  const uint32_t* qup;
+  const uint32_t* qdown;
+  const uint16_t* sgate;
+  const uint16_t* sup;
+  const uint16_t* sdown;
+  // bf16 shared expert
+  const uint16_t* s_gate;
+  const uint16_t* s_up;
+  const uint16_t* s_down;
+  bool ternary;
+};
+
+hipError_t launch_stream_experts(const Plan& p, const uint16_t* x, const ExpertWeights& w, hipStream_t s);
+hipError_t launch_grouped_experts(const Plan& p, const uint16_t* x, const ExpertWeights& w, hipStream_t s);
+hipError_t launch_combine(const Plan& p, bool y_is_f32, uint16_t* out, hipStream_t s);
+
+int grouped_gemm_bm();
+int route_split_for(int T, int d, int E);
+
+}  // namespace hymoe

@@ -1,0 +1,67 @@
+// moe_combine: the merge of expert outputs into the layer output (m.xxqk.cn Hy4
+// preview explainer, section 2.2 "路由机制": the selected experts' results are merged
+// as the layer's output), plus the always-on shared expert (Tencent Hy4 preview model
+// card):
+//   out[t] = bf16( sum_j w[t][j] * y[pos(t, j)] + y_shared[t] )
+// summed in fp32 over the slots in ascending expert order and rounded once to nearest
+// even. Each output element is owned by one thread, so the sum order is fixed.
+#include "common.h"
+#include "kernels.h"
+
+namespace hymoe {
+
+__device__ __forceinline__ void load8(const float* p, float* v) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+__device__ __forceinline__ void load8(const uint16_t* p, float* v) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  const uint32_t u[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_bits_to_f32(u[i] & 0xFFFFu);
+    v[2 * i + 1] = bf16_bits_to_f32(u[i] >> 16);
+  }
+}
+
+template <typename YT>
+__global__ void __launch_bounds__(256) combine_kernel(const YT* __restrict__ y, const int32_t* __restrict__ pos,
+                                                      const float* __restrict__ topk_w, int k, int d, int Tk,
+                                                      uint16_t* __restrict__ out) {
+  const int t = blockIdx.x;
+  const int32_t* pp = pos + (size_t)t * k;
+  const float* ww = topk_w + (size_t)t * k;
+  for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      const float wj = ww[j];
+      float v[8];
+      load8(y + (size_t)pp[j] * d + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wj, v[i], acc[i]);
+    }
+    float s[8];
+    load8(y + (size_t)(Tk + t) * d + c, s);
+    uint4 o;
+    o.x = pack_bf16x2(acc[0] + s[0], acc[1] + s[1]);
+    o.y = pack_bf16x2(acc[2] + s[2], acc[3] + s[3]);
+    o.z = pack_bf16x2(acc[4] + s[4], acc[5] + s[5]);
+    o.w = pack_bf16x2(acc[6] + s[6], acc[7] + s[7]);
+    *reinterpret_cast<uint4*>(out + (size_t)t * d + c) = o;
+  }
+}
+
+hipError_t launch_combine(const Plan& p, bool y_is_f32, uint16_t* out, hipStream_t s) {
+  if (y_is_f32)
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(p.T), dim3(256), 0, s, (const float*)p.y, p.pos, p.topk_w, p.k,
+                       p.d, p.Tk, out);
+  else
+    hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(p.T), dim3(256), 0, s, (const uint16_t*)p.y, p.pos,
+                       p.topk_w, p.k, p.d, p.Tk, out);
+  return hipGetLastError();
+}
+
+}  // namespace hymoe

@@ -1,0 +1,158 @@
+"""CPU tests of the C-ABI boundary: the library loads and exports every entry
+point the header declares, the ctypes struct matches the C layout, and every
+argument check fires before any HIP call (so they run without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import sparse_moe_transformer_route_amd as hm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hy_moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hy_moe_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) == set(hm.EXPORTED)
+    L = ctypes.CDLL(hm.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", hm.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (hy_moe_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_struct_layout_matches_c(tmp_path):
+    fields = [f[0] for f in hm.HyMoeArgs._fields_]
+    src = tmp_path / "layout.c"
+    body = "\n".join(f'  printf("{f} %zu\\n", offsetof(hy_moe_args, {f}));' for f in fields)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "hy_moe.h"\nint main(void){\n'
+                   f'  printf("sizeof %zu\\n", sizeof(hy_moe_args));\n{body}\n  return 0;\n}}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split("\n")
+               if line)
+    assert int(got["sizeof"]) == ctypes.sizeof(hm.HyMoeArgs)
+    for f in fields:
+        assert int(got[f]) == getattr(hm.HyMoeArgs, f).offset, f
+
+
+FAKE = 0x100000  # 16-byte aligned non-null address; never dereferenced by the checks
+
+
+def base_args(T=4, d=256, E=16, k=2, I=128):
+    a = hm.HyMoeArgs()
+    a.x = a.W_router = a.W_gate = a.W_up = a.W_down = FAKE
+    a.Ws_gate = a.Ws_up = a.Ws_down = a.out = FAKE
+    a.T, a.d, a.E, a.k, a.I = T, d, E, k, I
+    return a
+
+
+def call(a):
+    return hm.lib().hy_moe_forward_ex(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("k", 0, hm.ERR_INVALID_ARG), ("k", 17, hm.ERR_INVALID_ARG), ("T", -1, hm.ERR_INVALID_ARG),
+    ("d", 0, hm.ERR_INVALID_ARG), ("I", -128, hm.ERR_INVALID_ARG), ("E", 0, hm.ERR_INVALID_ARG),
+    ("d", 192, hm.ERR_UNSUPPORTED), ("I", 64, hm.ERR_UNSUPPORTED), ("x", None, hm.ERR_INVALID_ARG),
+    ("out", None, hm.ERR_INVALID_ARG), ("W_down", None, hm.ERR_INVALID_ARG), ("Ws_up", None, hm.ERR_INVALID_ARG),
+    ("x", FAKE + 2, hm.ERR_INVALID_ARG), ("expert_format", 7, hm.ERR_INVALID_ARG), ("path", 9, hm.ERR_INVALID_ARG),
+    ("workspace", FAKE + 64, hm.ERR_INVALID_ARG), ("topk_idx", FAKE + 2, hm.ERR_INVALID_ARG),
+])
+def test_argument_checks(field, value, status):
+    a = base_args()
+    setattr(a, field, value)
+    assert call(a) == status
+
+
+def test_envelope_limits():
+    a = base_args(E=2048, k=8)
+    assert call(a) == hm.ERR_UNSUPPORTED
+    a = base_args(E=32, k=17)
+    assert call(a) == hm.ERR_UNSUPPORTED
+    a = base_args(T=2 ** 28, k=8, E=64)
+    assert call(a) == hm.ERR_UNSUPPORTED
+    assert hm.lib().hy_moe_forward_ex(None, None) == hm.ERR_INVALID_ARG
+
+
+def test_ternary_requires_codes_and_scales():
+    a = base_args()
+    a.expert_format = hm.WEIGHTS_SHERRY_TERNARY
+    assert call(a) == hm.ERR_INVALID_ARG
+    a.Wq_gate = a.Wq_up = a.Wq_down = a.S_gate = a.S_up = a.S_down = FAKE
+    a.path = hm.PATH_GROUPED
+    assert call(a) == hm.ERR_UNSUPPORTED
+
+
+def test_small_workspace_rejected():
+    a = base_args()
+    a.workspace = FAKE
+    a.workspace_bytes = hm.workspace_size(4, 256, 16, 2, 128) - 1
+    assert call(a) == hm.ERR_WORKSPACE
+
+
+def test_empty_batch_is_a_no_op_without_touching_pointers():
+    a = hm.HyMoeArgs()
+    a.T, a.d, a.E, a.k, a.I = 0, 256, 16, 2, 128
+    assert call(a) == hm.OK
+    L = hm.lib()
+    assert L.hy_moe_forward(None, None, None, None, None, None, None, None, 0, 256, 16, 2, 128, None, None) == hm.OK
+
+
+def test_workspace_size_monotone_and_zero_for_invalid():
+    sizes = [hm.workspace_size(T, 6144, 256, 8, 2048) for T in (1, 32, 1024, 8192)]
+    assert all(s > 0 for s in sizes) and sizes == sorted(sizes)
+    assert hm.workspace_size(8, 6144, 256, 0, 2048) == 0
+    assert hm.workspace_size(8, 100, 256, 8, 2048) == 0
+    assert hm.workspace_size(8, 6144, 256, 8, 2048, 5) == 0
+    assert hm.workspace_size(8192, 6144, 256, 8, 2048) % 256 == 0
+
+
+def test_status_strings():
+    assert hm.status_string(hm.OK) == "ok"
+    for s in (hm.ERR_INVALID_ARG, hm.ERR_UNSUPPORTED, hm.ERR_WORKSPACE, hm.ERR_HIP):
+        assert hm.status_string(s) not in ("ok", "unknown status")
+    assert hm.status_string(12345) == "unknown status"
+
+
+def test_sherry_pack_host_round_trips_with_oracle_decoder():
+    rng = np.random.default_rng(0)
+    rows, cols = 5, 256
+    zpos = rng.integers(0, 4, size=(rows, cols // 4))
+    signs = rng.choice([-1, 1], size=(rows, cols))
+    tern = signs.astype(np.int8)
+    for r in range(rows):
+        for g in range(cols // 4):
+            tern[r, 4 * g + zpos[r, g]] = 0
+    packed = hm.sherry_pack_host(tern)
+    assert packed.shape == (rows, cols // 128 * 5)
+    dec, _ = oracle.sherry_decode(packed)
+    assert np.array_equal(dec, tern)
+    # all 32 codes in one block, in code order: packing the oracle's decoding of
+    # words 0..31-coded block reproduces the words
+    B = sum(c << (5 * c) for c in range(32))
+    words = np.array([[(B >> (32 * i)) & 0xFFFFFFFF for i in range(5)]], np.uint32)
+    dec, _ = oracle.sherry_decode(words)
+    assert np.array_equal(hm.sherry_pack_host(dec), words)
+
+
+def test_sherry_pack_host_rejects_bad_groups():
+    tern = np.ones((1, 128), np.int8)  # no zero in any group
+    packed = np.full((1, 5), 0xDEADBEEF, np.uint32)
+    rc = hm.lib().hy_moe_sherry_pack_host(tern.ctypes.data, 1, 128, packed.ctypes.data)
+    assert rc == hm.ERR_INVALID_ARG and (packed == 0xDEADBEEF).all()
+    tern = np.zeros((1, 128), np.int8)  # four zeros per group
+    assert hm.lib().hy_moe_sherry_pack_host(tern.ctypes.data, 1, 128, packed.ctypes.data) == hm.ERR_INVALID_ARG
+    assert hm.lib().hy_moe_sherry_pack_host(tern.ctypes.data, 1, 100, packed.ctypes.data) == hm.ERR_INVALID_ARG

@@ -1,0 +1,186 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Small shapes are compared element by element over every token; the full-size
+Hy4-shape workloads compare the routing of every token and the outputs of
+sampled tokens (the oracle regenerates the sampled tokens' experts on the host
+from the same seeded streams). Rules and tolerances: tests/parity.py.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import hy_inputs as hi
+import oracle
+from parity import (bf16_tensor_bits, bf16_tensor_to_np, check_out, check_permutation, check_routing,
+                    check_weights, routing_to_np)
+
+torch = pytest.importorskip("torch")
+hm = pytest.importorskip("sparse_moe_transformer_route_amd")
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def host_weights_bf16(cfg, L):
+    """(gate, up, down) bf16 bit arrays for the oracle; ternary experts decoded."""
+    if not cfg.ternary:
+        return L["gate"], L["up"], L["down"]
+    gate = np.stack([oracle.sherry_decode(L["qgate"][e], L["sgate"][e])[1] for e in range(cfg.E)])
+    up = np.stack([oracle.sherry_decode(L["qup"][e], L["sup"][e])[1] for e in range(cfg.E)])
+    down = np.stack([oracle.sherry_decode(L["qdown"][e], L["sdown"][e])[1] for e in range(cfg.E)])
+    return gate, up, down
+
+
+def run_small(cfg, path, bias=None, x_host=None, label=""):
+    """Full element-by-element comparison on a small layer."""
+    say(f"[case] {label or cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} I={cfg.I} "
+        f"ternary={cfg.ternary} path={path}")
+    L = hi.host_layer(cfg)
+    inp = hi.dev_layer(cfg, device=DEV)
+    if bias is not None:
+        L["bias"] = bias
+        inp["bias"] = torch.from_numpy(bias).to(DEV)
+    if x_host is not None:
+        L["x"] = x_host
+        inp["x"] = torch.from_numpy(x_host.view(np.int16)).to(DEV).view(torch.bfloat16)
+    res = hm.forward_layer(inp, cfg.k, want_routing=True, path=path)
+    torch.cuda.synchronize()
+    g = routing_to_np(res)
+    gate, up, down = host_weights_bf16(cfg, L)
+    lg = oracle.logits(L["x"], L["router"], L["bias"])
+    sets, near, subst = check_routing(g["topk_idx"], lg, cfg.k)
+    check_permutation(g, sets, cfg.E)
+    check_weights(g["topk_w"], lg, sets)
+    ref = oracle.forward(L["x"], L["router"], L["bias"], gate, up, down, L["shared"]["gate"], L["shared"]["up"],
+                         L["shared"]["down"], cfg.k, sets_in=sets)
+    worst, mean = check_out(bf16_tensor_to_np(res["out"]), ref["out"])
+    # margins: fp32 GPU margin vs fp64 oracle margin
+    fin = np.isfinite(ref["margin"])
+    assert np.array_equal(np.isfinite(g["margin"]), fin)
+    assert np.allclose(g["margin"][fin], ref["margin"][fin], atol=1e-4)
+    say(f"       near-ties={near} substituted={subst} max_rel_err={worst:.3e} mean_abs_err={mean:.3e}")
+    return res, ref
+
+
+# ------------------------------------------------------------------ generator
+def test_device_generator_matches_host():
+    say("[case] generator twin")
+    t = torch.empty(100_003, dtype=torch.bfloat16, device=DEV)
+    hi.dev_gauss_(t, 5, 3, 0.25, start=777)
+    assert np.array_equal(bf16_tensor_bits(t), hi.gauss_bf16(5, 3, 100_003, 0.25, start=777))
+    w = torch.empty(4099, dtype=torch.int32, device=DEV)
+    hi.dev_words_(w, 1, 10, start=3)
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), hi.words_u32(1, 10, 4099, start=3))
+    u = torch.empty(5001, dtype=torch.bfloat16, device=DEV)
+    hi.dev_uniform_(u, 2, 13, 0.01, 0.02)
+    assert np.array_equal(bf16_tensor_bits(u), hi.uniform_bf16(2, 13, 5001, 0.01, 0.02))
+
+
+# ------------------------------------------------------------ small layers
+PATHS = [hm.PATH_STREAM, hm.PATH_GROUPED]
+
+
+@pytest.mark.parametrize("path", [hm.PATH_AUTO] + PATHS)
+def test_tiny_config(path):
+    run_small(hi.CONFIGS["tiny"], path)
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("shape", [
+    dict(T=1, d=256, E=16, k=2, I=128),
+    dict(T=77, d=256, E=16, k=1, I=128),          # ragged token block, k=1
+    dict(T=130, d=384, E=64, k=4, I=256),         # the pages' 64-expert / top-4 example
+    dict(T=40, d=256, E=16, k=16, I=128),         # k = E: margin +inf
+    dict(T=50, d=256, E=100, k=3, I=128),         # E not a multiple of 64
+    dict(T=33, d=128, E=1024, k=16, I=128),       # largest E and k
+    dict(T=600, d=256, E=4, k=2, I=128),          # ~300 rows per expert: several M tiles
+    dict(T=300, d=512, E=8, k=8, I=384),          # every expert takes every token
+])
+def test_small_shapes(shape, path):
+    cfg = hi.LayerConfig("shape", seed=1, **shape)
+    run_small(cfg, path)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_router_bias_and_empty_experts(path):
+    cfg = hi.LayerConfig("bias", T=96, d=256, E=64, k=4, I=128, seed=2)
+    run_small(cfg, path, bias=hi.zipf_bias(64, 2, 1.2))
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_all_tokens_on_one_expert(path):
+    cfg = hi.LayerConfig("hot", T=300, d=256, E=16, k=2, I=128, seed=3)
+    b = np.zeros(16, np.float32)
+    b[11] = 1000.0
+    res, _ = run_small(cfg, path, bias=b)
+    counts = res["counts"].cpu().numpy()
+    assert counts[11] == 300
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_all_logits_tied(path):
+    cfg = hi.LayerConfig("ties", T=70, d=256, E=16, k=3, I=128, seed=4)
+    x0 = np.zeros((70, 256), np.uint16)  # x = 0: every logit is 0, ties to the lowest indices
+    res, ref = run_small(cfg, path, x_host=x0)
+    assert (res["topk_idx"].cpu().numpy() == np.arange(3)).all()
+    assert np.allclose(res["topk_w"].cpu().numpy(), 1.0 / 3.0, atol=1e-7)
+
+
+@pytest.mark.parametrize("T", [1, 32, 100])
+def test_ternary_small(T):
+    cfg = hi.LayerConfig("tern", T=T, d=256, E=16, k=2, I=256, ternary=True, seed=5)
+    run_small(cfg, hm.PATH_STREAM)
+
+
+def test_ternary_grouped_path_unsupported():
+    cfg = hi.LayerConfig("tern", T=8, d=256, E=16, k=2, I=128, ternary=True, seed=5)
+    inp = hi.dev_layer(cfg, device=DEV)
+    with pytest.raises(hm.HyMoeError):
+        hm.forward_layer(inp, cfg.k, path=hm.PATH_GROUPED)
+
+
+# ------------------------------------------------------------- determinism
+@pytest.mark.parametrize("path", PATHS)
+def test_bitwise_deterministic_and_workspace_independent(path):
+    say(f"[case] determinism path={path}")
+    cfg = hi.LayerConfig("det", T=200, d=512, E=32, k=4, I=256, seed=6)
+    inp = hi.dev_layer(cfg, device=DEV)
+    ws1 = hm.alloc_workspace(cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, device=DEV)
+    big = torch.empty(ws1.numel() + 4096, dtype=torch.uint8, device=DEV)
+    ws2 = big[4096:]
+    r1 = hm.forward_layer(inp, cfg.k, want_routing=True, path=path, workspace=ws1)
+    r2 = hm.forward_layer(inp, cfg.k, want_routing=True, path=path, workspace=ws2)
+    r3 = hm.forward_layer(inp, cfg.k, want_routing=True, path=path)
+    torch.cuda.synchronize()
+    for key in r1:
+        assert torch.equal(r1[key], r2[key]), key
+        assert torch.equal(r1[key], r3[key]), key
+
+
+def test_plain_entry_point_matches_ex():
+    say("[case] hy_moe_forward vs hy_moe_forward_ex")
+    cfg = hi.LayerConfig("plain", T=64, d=256, E=16, k=2, I=128, seed=7)
+    inp = hi.dev_layer(cfg, device=DEV)
+    out = hm.forward(inp["x"], inp["router"], inp["gate"], inp["up"], inp["down"], inp["shared"]["gate"],
+                     inp["shared"]["up"], inp["shared"]["down"], cfg.k)
+    r = hm.forward_layer(inp, cfg.k)
+    torch.cuda.synchronize()
+    assert torch.equal(out, r["out"])
+
+
+def test_paths_agree_mid_size():
+    say("[case] stream vs grouped at T=256 d=1024 E=32 k=4 I=512")
+    cfg = hi.LayerConfig("mid", T=256, d=1024, E=32, k=4, I=512, seed=8)
+    inp = hi.dev_layer(cfg, device=DEV)
+    a = hm.forward_layer(inp, cfg.k, want_routing=True, path=hm.PATH_STREAM)
+    b = hm.forward_layer(inp, cfg.k, want_routing=True, path=hm.PATH_GROUPED)
+    torch.cuda.synchronize()
+    for key in ("topk_idx", "topk_w", "counts", "offsets", "perm_src", "margin"):
+        assert torch.equal(a[key], b[key]), key
+    fa, fb = a["out"].float(), b["out"].float()
+    assert ((fa - fb).abs() <= 2e-2 * (1 + fb.abs())).all()
