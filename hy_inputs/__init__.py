@@ -84,6 +84,7 @@ def _load_host():
 
 
 def _load_dev():
+    import torch  # noqa: F401  (bind to torch's HIP runtime, loaded first)
     path = os.path.join(_HERE, "libhy_gen_dev.so")
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")

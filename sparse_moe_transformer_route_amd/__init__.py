@@ -12,6 +12,11 @@ from __future__ import annotations
 import ctypes
 import os
 
+# torch provides the device memory and streams, and brings its own HIP runtime
+# (soname libamdhip64.so.7). It must be loaded before libhy_moe.so so that the
+# library binds to that same runtime instead of loading a second copy.
+import torch  # noqa: F401
+
 __all__ = ["forward", "forward_ex", "forward_layer", "workspace_size", "status_string", "sherry_pack_host",
            "HyMoeError", "lib", "LIB_PATH"]
 

@@ -156,3 +156,13 @@ def test_sherry_pack_host_rejects_bad_groups():
     tern = np.zeros((1, 128), np.int8)  # four zeros per group
     assert hm.lib().hy_moe_sherry_pack_host(tern.ctypes.data, 1, 128, packed.ctypes.data) == hm.ERR_INVALID_ARG
     assert hm.lib().hy_moe_sherry_pack_host(tern.ctypes.data, 1, 100, packed.ctypes.data) == hm.ERR_INVALID_ARG
+
+
+def test_one_hip_runtime_in_process():
+    # The library must bind to the HIP runtime torch loaded (device memory and
+    # streams come from torch); a second runtime copy would not share them.
+    import hy_inputs
+    hy_inputs.dev_lib()
+    maps = open("/proc/self/maps").read().splitlines()
+    runtimes = {line.split()[-1] for line in maps if "libamdhip64" in line}
+    assert len(runtimes) == 1, runtimes
