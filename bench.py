@@ -1,0 +1,298 @@
+"""Benchmark of the MoE FFN layer forward pass on one MI355X.
+
+A step is one full layer forward (router -> top-k -> dispatch -> experts +
+shared expert -> combine) over one batch of seeded synthetic inputs already
+resident in HBM, through the C ABI (hy_moe_forward_ex, automatic path choice,
+caller workspace). Default workload: the Hy4-shape decode layer (T=32 tokens,
+d=6144, 256 routed experts top-8 + 1 shared, I=2048, bf16), which is bound by
+streaming every touched expert's weights from HBM. The same run also measures
+the prefill layer (T=8192), bound by bf16 MFMA, because the headline metric
+names both.
+
+Prints one JSON line. Per-kernel durations come from HIP events the library
+records on its stream around each kernel (stage_events), over the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s; %bf16 MFMA peak (T=8192), %HBM BW (T=32)"
+PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
+PEAK_BF16 = 2.5e15         # flop/s, MI355X dense bf16 MFMA
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Events:
+    """hipEvent_t handles from the HIP runtime torch loaded (same process runtime)."""
+
+    def __init__(self, n):
+        self.rt = ctypes.CDLL("libamdhip64.so.7")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.handles = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self.rt.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.handles.append(h.value)
+
+    def array(self, i, m):
+        return (ctypes.c_void_p * m)(*self.handles[i * m:(i + 1) * m])
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        if self.rt.hipEventElapsedTime(ctypes.byref(out), self.handles[a], self.handles[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return out.value
+
+    def close(self):
+        for h in self.handles:
+            self.rt.hipEventDestroy(h)
+
+
+def source_digest(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_for(kernel_key, units):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None when
+    absent or taken on a different version of the kernel's source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        rec = json.load(open(TRAFFIC_FILE)).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec:
+        return None
+    src = os.path.join(ROOT, rec["source"])
+    if not os.path.exists(src) or source_digest(src) != rec["source_sha256_16"]:
+        return None
+    return rec["bytes_per_launch"]
+
+
+def time_layer(hm, torch, inp, k, ws, steps, warmup):
+    """Times `steps` forwards; returns (total ms by the host clock around syncs,
+    mean ms per kernel from the stage events)."""
+    nk = len(hm.KERNELS)
+    ev = Events((nk + 1) * steps)
+    for _ in range(warmup):
+        hm.forward_layer(inp, k, workspace=ws)
+    torch.cuda.synchronize()
+    arrays = [ev.array(i, nk + 1) for i in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        hm.forward_layer(inp, k, workspace=ws, stage_events=arrays[i])
+    torch.cuda.synchronize()
+    total_ms = (time.perf_counter() - t0) * 1e3
+    per = [0.0] * nk
+    for i in range(steps):
+        for j in range(nk):
+            per[j] += ev.ms(i * (nk + 1) + j, i * (nk + 1) + j + 1) / steps
+    ev.close()
+    return total_ms, dict(zip(hm.KERNELS, per))
+
+
+def run_config(name, args, hi, hm, torch, weights=None):
+    cfg = hi.CONFIGS[name]
+    dev = "cuda:0"
+    if weights is None:
+        log(f"[bench] generating inputs for {name} on the GPU")
+        inp = hi.dev_layer(cfg, device=dev)
+    else:
+        inp = dict(weights)
+        inp["x"] = weights["x"][: cfg.T].contiguous()
+        b = hi.host_bias(cfg)
+        inp["bias"] = None if b is None else torch.from_numpy(b).to(dev)
+    fmt = hm.WEIGHTS_SHERRY_TERNARY if cfg.ternary else hm.WEIGHTS_BF16
+    ws = hm.alloc_workspace(cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, fmt, device=dev)
+    steps = args.steps
+    total_ms, kern = time_layer(hm, torch, inp, cfg.k, ws, steps, args.warmup)
+    ms = total_ms / steps
+    routing = hm.forward_layer(inp, cfg.k, want_routing=True, workspace=ws)
+    torch.cuda.synchronize()
+    counts = routing["counts"].cpu()
+    touched = int((counts > 0).sum())
+    stream_path = cfg.ternary or cfg.T * cfg.k <= 16 * cfg.E
+    d, I = cfg.d, cfg.I
+    kernel_file = "sparse_moe_transformer_route_amd/csrc/" + ("moe_stream.hip" if stream_path else "moe_gemm.hip")
+    if stream_path:
+        # dominant kernel: gate/up streaming; unit = one touched expert's gate+up weights
+        if cfg.ternary:
+            unit = 2 * I * (d // 128 * 5 * 4) + 2 * I * 2    # packed codes + row scales
+            shared = 2 * I * d * 2
+            alg = touched * unit + shared
+            per_unit = f"{unit} B packed gate+up codes and scales per touched routed expert, plus {shared} B bf16 shared"
+        else:
+            unit = 2 * I * d * 2
+            alg = (touched + 1) * unit
+            per_unit = f"{unit} B of bf16 gate+up weights per touched expert (routed + shared)"
+        sec = kern["expert_gateup"] * 1e-3
+        roof = {"bound": "hbm", "achieved": alg / sec / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                "frac": alg / sec / PEAK_HBM, "traffic": traffic_for(f"stream_gateup/{name}", touched + 1),
+                "kernel": "stream_gateup_kernel", "per_unit": per_unit, "units_per_launch": touched + 1,
+                "kernel_ms": kern["expert_gateup"]}
+        # whole-layer HBM fraction: every touched expert's weights once + router + x/out
+        if cfg.ternary:
+            layer_bytes = touched * (3 * I * (d // 128 * 5 * 4) + 2 * I * 2 + d * 2) + 3 * I * d * 2
+        else:
+            layer_bytes = (touched + 1) * 3 * I * d * 2
+        layer_bytes += cfg.E * d * 2 + 2 * cfg.T * d * 2
+        layer = {"bytes": layer_bytes, "hbm_frac": layer_bytes / (ms * 1e-3) / PEAK_HBM}
+    else:
+        rows = cfg.T * cfg.k + cfg.T
+        alg = 4 * rows * d * I
+        sec = kern["expert_gateup"] * 1e-3
+        roof = {"bound": "mfma", "achieved": alg / sec / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                "frac": alg / sec / PEAK_BF16, "traffic": traffic_for(f"grouped_gemm_gateup/{name}", rows),
+                "kernel": "grouped_gemm_kernel<true>", "per_unit": f"{4 * d * I} flop per dispatched row "
+                f"(gate and up: 2*d*I each)", "units_per_launch": rows, "kernel_ms": kern["expert_gateup"]}
+        flops = 2 * cfg.T * d * cfg.E + 6 * rows * d * I
+        layer = {"flop": flops, "mfma_frac": flops / (ms * 1e-3) / PEAK_BF16}
+    roof["kernel_source_sha256_16"] = source_digest(os.path.join(ROOT, kernel_file))
+    return {"cfg": cfg, "inp": inp, "ms": ms, "tokens_per_s": cfg.T / (ms * 1e-3), "kernels_ms": kern,
+            "roofline": roof, "layer": layer, "touched": touched, "counts": counts, "routing": routing}
+
+
+def cpu_baseline(cfg, hi, torch, inp, routing, budget_s):
+    """The oracle timed on this host's cores on the first tokens of the same batch.
+    Expert weights are copied from the device tensors (generator output, never
+    the HIP path's results); only the oracle's calls are timed."""
+    import numpy as np
+
+    import oracle
+    nthreads = max(1, min(16, os.cpu_count() or 1))
+
+    def bits(t):
+        return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    x = bits(inp["x"])
+    wr = bits(inp["router"])
+    bias = None if inp.get("bias") is None else inp["bias"].cpu().numpy()
+    sh = {key: bits(v) for key, v in inp["shared"].items()}
+    sets_all = routing["topk_idx"].cpu().numpy()
+    cache = {}
+
+    def expert(e):
+        # bf16 weights of routed expert e; Sherry codes are decoded by the oracle
+        # here, outside the timed region (weight materialisation)
+        if e not in cache:
+            if "qgate" in inp:
+                cache[e] = tuple(oracle.sherry_decode(inp[q][e].cpu().numpy().view(np.uint32), bits(inp[s][e]))[1]
+                                 for q, s in (("qgate", "sgate"), ("qup", "sup"), ("qdown", "sdown")))
+            else:
+                cache[e] = tuple(bits(inp[key][e]) for key in ("gate", "up", "down"))
+        return cache[e]
+
+    def oracle_tokens(tok):
+        for t in tok:
+            for e in sets_all[t]:
+                expert(int(e))
+        t0 = time.perf_counter()
+        lg = oracle.logits(x[tok], wr, bias, nthreads=nthreads)
+        sets, _ = oracle.select(lg, cfg.k)
+        w = oracle.weights(lg, sets)
+        ys = oracle.ffn(x[tok], sh["gate"], sh["up"], sh["down"], nthreads=nthreads)
+        yr = np.zeros((len(tok), cfg.k, cfg.d))
+        for i in range(len(tok)):
+            for j, e in enumerate(sets[i]):
+                g, u, dn = expert(int(e))
+                yr[i, j] = oracle.ffn(x[tok[i]:tok[i] + 1], g, u, dn, nthreads=nthreads)[0]
+        oracle.combine(ys, yr, w)
+        return time.perf_counter() - t0
+
+    first = oracle_tokens([0])
+    n = max(1, min(cfg.T, int(budget_s / max(first, 1e-3))))
+    tok = list(range(1, 1 + n)) if n < cfg.T else list(range(cfg.T))
+    el = oracle_tokens(tok)
+    return {"value": len(tok) / el, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{len(tok)} of the {cfg.T} tokens of the same batch (full fp64 layer per token: "
+                      f"router over {cfg.E} experts, top-{cfg.k}, {cfg.k} routed + 1 shared SwiGLU experts, "
+                      f"combine); {el:.1f} s on {nthreads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="decode", choices=["tiny", "decode", "prefill", "skewed", "ternary"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the T=8192 measurement")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no multi-GPU "
+              f"path: the layer is sharded by expert only in design)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import hy_inputs as hi
+    import sparse_moe_transformer_route_amd as hm
+    torch.cuda.set_device(0)
+
+    cfg = hi.CONFIGS[args.config]
+    shared_weights = None
+    if not cfg.ternary and cfg.d == 6144:
+        log("[bench] generating the Hy4-shape bf16 layer (19.3 GB of expert weights) on the GPU")
+        shared_weights = hi.dev_layer(hi.CONFIGS["prefill"], device="cuda:0")
+        torch.cuda.synchronize()
+    main_res = run_config(args.config, args, hi, hm, torch, shared_weights)
+    log(f"[bench] {args.config}: {main_res['ms']:.3f} ms/step, {main_res['tokens_per_s']:.1f} tokens/s, "
+        f"kernels {json.dumps({k: round(v, 4) for k, v in main_res['kernels_ms'].items()})}")
+
+    extra = {}
+    if args.config == "decode" and not args.no_prefill:
+        pre_args = argparse.Namespace(**vars(args))
+        pre_args.steps = min(args.steps, 10)
+        pre = run_config("prefill", pre_args, hi, hm, torch, shared_weights)
+        log(f"[bench] prefill: {pre['ms']:.3f} ms/step, {pre['tokens_per_s']:.0f} tokens/s")
+        extra["prefill"] = {"workload": "prefill T=8192 d=6144 E=256 k=8 I=2048 bf16", "ms_per_step": pre["ms"],
+                            "tokens_per_s": pre["tokens_per_s"], "layer_mfma_frac": pre["layer"]["mfma_frac"],
+                            "roofline": pre["roofline"], "kernels_ms": pre["kernels_ms"]}
+        del pre
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host")
+        cpu = cpu_baseline(cfg, hi, torch, main_res["inp"], main_res["routing"], args.cpu_seconds)
+
+    c = main_res["cfg"]
+    line = {
+        "metric": METRIC, "value": main_res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_res["ms"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "sherry-ternary+bf16" if c.ternary else "bf16", "data": "synthetic",
+        "config": {"workload": f"{c.name} MoE FFN layer T={c.T} d={c.d} E={c.E} top-{c.k} + 1 shared I={c.I}"
+                               + (" Sherry-ternary routed experts" if c.ternary else " bf16")
+                               + (" Zipf(1.2) router bias" if c.zipf_s else ""),
+                   "T": c.T, "d": c.d, "E": c.E, "k": c.k, "I": c.I, "seed": c.seed,
+                   "touched_experts": main_res["touched"]},
+        "roofline": main_res["roofline"],
+        "layer": main_res["layer"],
+        "kernels_ms": main_res["kernels_ms"],
+        "cpu_baseline": cpu,
+    }
+    line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

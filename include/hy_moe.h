@@ -132,7 +132,24 @@ typedef struct hy_moe_args {
                                 (experts ascending, tokens ascending within one) */
   float* margin;             /* [T]    k-th minus (k+1)-th largest logit (fp32); +inf if k == E */
   hy_moe_path path;
+  /* optional profiling hook: NULL, or HY_MOE_NUM_STAGE_EVENTS hipEvent_t handles (created
+     by the caller) recorded on the stream before the first kernel and after each kernel,
+     in the order listed below; event i+1 minus event i is the duration of kernel i */
+  void** stage_events;
 } hy_moe_args;
+
+/* Kernels of one call, in launch order (indices into the stage events). */
+enum {
+  HY_MOE_K_ROUTE_LOGITS = 0, /* router logits (MFMA) */
+  HY_MOE_K_ROUTE_TOPK = 1,   /* top-k selection, weights, dispatch masks */
+  HY_MOE_K_PERMUTE_SCAN = 2, /* per-expert counts, offsets, work lists */
+  HY_MOE_K_PERMUTE_SCATTER = 3,
+  HY_MOE_K_EXPERT_GATEUP = 4, /* gate/up + SwiGLU of every touched expert and the shared expert */
+  HY_MOE_K_EXPERT_DOWN = 5,   /* down projection */
+  HY_MOE_K_COMBINE = 6,       /* weighted merge + shared-expert add */
+  HY_MOE_NUM_KERNELS = 7,
+  HY_MOE_NUM_STAGE_EVENTS = 8
+};
 
 /* hy_moe_forward_ex — the layer with every option. Returns a hy_moe_status. */
 int hy_moe_forward_ex(const hy_moe_args* args, void* stream);

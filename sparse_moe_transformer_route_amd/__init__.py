@@ -26,6 +26,9 @@ LIB_PATH = os.path.join(_HERE, "libhy_moe.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 WEIGHTS_BF16, WEIGHTS_SHERRY_TERNARY = 0, 1
 PATH_AUTO, PATH_STREAM, PATH_GROUPED = 0, 1, 2
+KERNELS = ["route_logits", "route_topk", "permute_scan", "permute_scatter", "expert_gateup", "expert_down",
+           "combine"]
+NUM_STAGE_EVENTS = len(KERNELS) + 1
 
 EXPORTED = ["hy_moe_forward", "hy_moe_forward_ex", "hy_moe_workspace_size", "hy_moe_status_string",
             "hy_moe_sherry_pack_host"]
@@ -47,6 +50,7 @@ class HyMoeArgs(ctypes.Structure):
         ("topk_idx", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("counts", ctypes.c_void_p),
         ("offsets", ctypes.c_void_p), ("perm_src", ctypes.c_void_p), ("margin", ctypes.c_void_p),
         ("path", ctypes.c_int),
+        ("stage_events", ctypes.c_void_p),
     ]
 
 
@@ -119,7 +123,7 @@ def forward_ex(args: HyMoeArgs, stream=None) -> int:
 
 
 def forward_layer(inp: dict, k: int, *, want_routing=False, path=PATH_AUTO, workspace=None, out=None,
-                  stream=None):
+                  stream=None, stage_events=None):
     """Runs hy_moe_forward_ex on a dict of device tensors as made by
     hy_inputs.dev_layer(): x, router, bias, shared{gate,up,down} and either
     gate/up/down (bf16) or qgate/qup/qdown + sgate/sup/sdown (ternary).
@@ -158,6 +162,8 @@ def forward_layer(inp: dict, k: int, *, want_routing=False, path=PATH_AUTO, work
         a.counts, a.offsets = _ptr(res["counts"]), _ptr(res["offsets"])
         a.perm_src, a.margin = _ptr(res["perm_src"]), _ptr(res["margin"])
     a.path = path
+    if stage_events is not None:
+        a.stage_events = ctypes.cast(stage_events, ctypes.c_void_p)
     rc = forward_ex(a, stream)
     if rc != OK:
         raise HyMoeError(rc, "hy_moe_forward_ex")

@@ -160,11 +160,13 @@ extern "C" int hy_moe_forward_ex(const hy_moe_args* a, void* stream) {
     stream_path = w.ternary || (int64_t)p.Tk <= 16 * (int64_t)p.E;
 
   const uint16_t* x = (const uint16_t*)a->x;
-  hipError_t err = launch_route(p, x, (const uint16_t*)a->W_router, a->router_bias, a->margin, s);
-  if (err == hipSuccess) err = launch_permute(p, a->counts, a->offsets, s);
+  Marks marks{a->stage_events, 0};
+  hipError_t err = marks.mark(s);
+  if (err == hipSuccess) err = launch_route(p, x, (const uint16_t*)a->W_router, a->router_bias, a->margin, s, marks);
+  if (err == hipSuccess) err = launch_permute(p, a->counts, a->offsets, s, marks);
   if (err == hipSuccess)
-    err = stream_path ? launch_stream_experts(p, x, w, s) : launch_grouped_experts(p, x, w, s);
-  if (err == hipSuccess) err = launch_combine(p, stream_path, (uint16_t*)a->out, s);
+    err = stream_path ? launch_stream_experts(p, x, w, s, marks) : launch_grouped_experts(p, x, w, s, marks);
+  if (err == hipSuccess) err = launch_combine(p, stream_path, (uint16_t*)a->out, s, marks);
   if (owned) {
     if (hipFreeAsync(ws, s) != hipSuccess && err == hipSuccess) err = hipErrorUnknown;
   }

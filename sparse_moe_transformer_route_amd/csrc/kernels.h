@@ -7,6 +7,17 @@
 
 namespace hymoe {
 
+// Optional profiling events recorded after each kernel (caller-created hipEvent_t).
+struct Marks {
+  void* const* ev;
+  int next;
+  hipError_t mark(hipStream_t s) {
+    hipError_t e = ev ? hipEventRecord((hipEvent_t)ev[next], s) : hipSuccess;
+    ++next;
+    return e;
+  }
+};
+
 // Per-call device state carved from the workspace.
 struct Plan {
   int T, d, E, k, I;
@@ -33,8 +44,8 @@ struct Plan {
 };
 
 hipError_t launch_route(const Plan& p, const uint16_t* x, const uint16_t* w_router, const float* bias,
-                        float* margin_out, hipStream_t s);
-hipError_t launch_permute(const Plan& p, int32_t* counts_out, int32_t* offsets_out, hipStream_t s);
+                        float* margin_out, hipStream_t s, Marks& m);
+hipError_t launch_permute(const Plan& p, int32_t* counts_out, int32_t* offsets_out, hipStream_t s, Marks& m);
 
 struct ExpertWeights {
   // bf16 routed experts
@@ -55,9 +66,11 @@ struct ExpertWeights {
   bool ternary;
 };
 
-hipError_t launch_stream_experts(const Plan& p, const uint16_t* x, const ExpertWeights& w, hipStream_t s);
-hipError_t launch_grouped_experts(const Plan& p, const uint16_t* x, const ExpertWeights& w, hipStream_t s);
-hipError_t launch_combine(const Plan& p, bool y_is_f32, uint16_t* out, hipStream_t s);
+hipError_t launch_stream_experts(const Plan& p, const uint16_t* x, const ExpertWeights& w, hipStream_t s,
+                                 Marks& m);
+hipError_t launch_grouped_experts(const Plan& p, const uint16_t* x, const ExpertWeights& w, hipStream_t s,
+                                  Marks& m);
+hipError_t launch_combine(const Plan& p, bool y_is_f32, uint16_t* out, hipStream_t s, Marks& m);
 
 int grouped_gemm_bm();
 int route_split_for(int T, int d, int E);

@@ -54,14 +54,15 @@ __global__ void __launch_bounds__(256) combine_kernel(const YT* __restrict__ y, 
   }
 }
 
-hipError_t launch_combine(const Plan& p, bool y_is_f32, uint16_t* out, hipStream_t s) {
+hipError_t launch_combine(const Plan& p, bool y_is_f32, uint16_t* out, hipStream_t s, Marks& m) {
   if (y_is_f32)
     hipLaunchKernelGGL(combine_kernel<float>, dim3(p.T), dim3(256), 0, s, (const float*)p.y, p.pos, p.topk_w, p.k,
                        p.d, p.Tk, out);
   else
     hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(p.T), dim3(256), 0, s, (const uint16_t*)p.y, p.pos,
                        p.topk_w, p.k, p.d, p.Tk, out);
-  return hipGetLastError();
+  hipError_t err = hipGetLastError();
+  return err == hipSuccess ? m.mark(s) : err;
 }
 
 }  // namespace hymoe

@@ -195,15 +195,18 @@ static int persistent_grid(int phase, const void* kernel) {
   return gsz;
 }
 
-hipError_t launch_grouped_experts(const Plan& p, const uint16_t* x, const ExpertWeights& w, hipStream_t s) {
+hipError_t launch_grouped_experts(const Plan& p, const uint16_t* x, const ExpertWeights& w, hipStream_t s,
+                                  Marks& m) {
   GemmArgs a{x, p.perm_src, p.offs, p.meta, p.tiles, p.Tk, p.k, p.d, p.I, p.E};
   const int g1 = persistent_grid(0, reinterpret_cast<const void*>(&grouped_gemm_kernel<true>));
   hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3(g1), dim3(256), 0, s, a, w, p.h, (uint16_t*)p.y);
   hipError_t err = hipGetLastError();
+  if (err == hipSuccess) err = m.mark(s);
   if (err != hipSuccess) return err;
   const int g2 = persistent_grid(1, reinterpret_cast<const void*>(&grouped_gemm_kernel<false>));
   hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3(g2), dim3(256), 0, s, a, w, p.h, (uint16_t*)p.y);
-  return hipGetLastError();
+  err = hipGetLastError();
+  return err == hipSuccess ? m.mark(s) : err;
 }
 
 }  // namespace hymoe

@@ -105,14 +105,16 @@ __global__ void __launch_bounds__(256) permute_scatter_kernel(const int32_t* __r
   }
 }
 
-hipError_t launch_permute(const Plan& p, int32_t* counts_out, int32_t* offsets_out, hipStream_t s) {
+hipError_t launch_permute(const Plan& p, int32_t* counts_out, int32_t* offsets_out, hipStream_t s, Marks& m) {
   hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, s, p.mask, p.nblk, p.T, p.E, p.k, p.gemm_bm,
                      p.blk_base, p.offs, p.meta, p.touched, p.tiles, counts_out, offsets_out);
   hipError_t err = hipGetLastError();
+  if (err == hipSuccess) err = m.mark(s);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(permute_scatter_kernel, dim3(p.nblk), dim3(256), 0, s, p.topk_idx, p.mask, p.blk_base, p.T,
                      p.E, p.k, p.perm_src, p.pos);
-  return hipGetLastError();
+  err = hipGetLastError();
+  return err == hipSuccess ? m.mark(s) : err;
 }
 
 }  // namespace hymoe

@@ -180,10 +180,11 @@ static int pick_split(int T, int d, int E) {
 int route_split_for(int T, int d, int E) { return pick_split(T, d, E); }
 
 hipError_t launch_route(const Plan& p, const uint16_t* x, const uint16_t* w_router, const float* bias,
-                        float* margin_out, hipStream_t s) {
+                        float* margin_out, hipStream_t s, Marks& m) {
   dim3 g1((p.T + 31) / 32, (p.E + 63) / 64, p.ks);
   hipLaunchKernelGGL(route_logits_kernel, g1, dim3(64), 0, s, x, w_router, p.part, p.T, p.d, p.E, p.d / p.ks);
   hipError_t err = hipGetLastError();
+  if (err == hipSuccess) err = m.mark(s);
   if (err != hipSuccess) return err;
   dim3 g2(p.nblk);
   const int R = (p.E + 63) / 64;
@@ -202,7 +203,8 @@ hipError_t launch_route(const Plan& p, const uint16_t* x, const uint16_t* w_rout
   else
     hipLaunchKernelGGL(route_topk_kernel<16>, g2, dim3(256), 0, s, p.part, p.ks, bias, p.T, p.E, p.k, p.topk_idx,
                        p.topk_w, margin_out, p.mask);
-  return hipGetLastError();
+  err = hipGetLastError();
+  return err == hipSuccess ? m.mark(s) : err;
 }
 
 }  // namespace hymoe

@@ -331,7 +331,8 @@ __global__ void __launch_bounds__(256) stream_down_kernel(StreamArgs a, ExpertWe
   }
 }
 
-hipError_t launch_stream_experts(const Plan& p, const uint16_t* x, const ExpertWeights& w, hipStream_t s) {
+hipError_t launch_stream_experts(const Plan& p, const uint16_t* x, const ExpertWeights& w, hipStream_t s,
+                                 Marks& m) {
   StreamArgs a{x, p.touched, p.meta, p.offs, p.perm_src, p.Tk, p.k, p.d, p.I, p.E};
   const int slots = (p.Tk < p.E ? p.Tk : p.E) + 1;
   dim3 g1(p.I / 64, slots), g2(p.d / 64, slots);
@@ -341,13 +342,15 @@ hipError_t launch_stream_experts(const Plan& p, const uint16_t* x, const ExpertW
     hipLaunchKernelGGL(stream_gateup_kernel<false>, g1, dim3(256), 0, s, a, w, p.h);
   }
   hipError_t err = hipGetLastError();
+  if (err == hipSuccess) err = m.mark(s);
   if (err != hipSuccess) return err;
   if (w.ternary) {
     hipLaunchKernelGGL(stream_down_kernel<true>, g2, dim3(256), 0, s, a, w, p.h, (float*)p.y);
   } else {
     hipLaunchKernelGGL(stream_down_kernel<false>, g2, dim3(256), 0, s, a, w, p.h, (float*)p.y);
   }
-  return hipGetLastError();
+  err = hipGetLastError();
+  return err == hipSuccess ? m.mark(s) : err;
 }
 
 }  // namespace hymoe
