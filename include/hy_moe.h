@@ -141,7 +141,8 @@ typedef struct hy_moe_args {
 /* Kernels of one call, in launch order (indices into the stage events). */
 enum {
   HY_MOE_K_ROUTE_LOGITS = 0, /* router logits (MFMA) */
-  HY_MOE_K_ROUTE_TOPK = 1,   /* top-k selection, weights, dispatch masks */
+  HY_MOE_K_ROUTE_TOPK = 1,   /* top-k selection, weights, dispatch masks (and, for T <= 64, the
+                                dispatch lists and permutation: kernels 2 and 3 are then empty) */
   HY_MOE_K_PERMUTE_SCAN = 2, /* per-expert counts, offsets, work lists */
   HY_MOE_K_PERMUTE_SCATTER = 3,
   HY_MOE_K_EXPERT_GATEUP = 4, /* gate/up + SwiGLU of every touched expert and the shared expert */

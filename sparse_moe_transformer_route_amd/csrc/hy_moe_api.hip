@@ -162,7 +162,8 @@ extern "C" int hy_moe_forward_ex(const hy_moe_args* a, void* stream) {
   const uint16_t* x = (const uint16_t*)a->x;
   Marks marks{a->stage_events, 0};
   hipError_t err = marks.mark(s);
-  if (err == hipSuccess) err = launch_route(p, x, (const uint16_t*)a->W_router, a->router_bias, a->margin, s, marks);
+  if (err == hipSuccess) err = launch_route(p, x, (const uint16_t*)a->W_router, a->router_bias, a->margin, a->counts,
+                                              a->offsets, s, marks);
   if (err == hipSuccess) err = launch_permute(p, a->counts, a->offsets, s, marks);
   if (err == hipSuccess)
     err = stream_path ? launch_stream_experts(p, x, w, s, marks) : launch_grouped_experts(p, x, w, s, marks);

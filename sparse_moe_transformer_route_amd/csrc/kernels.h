@@ -44,7 +44,7 @@ struct Plan {
 };
 
 hipError_t launch_route(const Plan& p, const uint16_t* x, const uint16_t* w_router, const float* bias,
-                        float* margin_out, hipStream_t s, Marks& m);
+                        float* margin_out, int32_t* counts_out, int32_t* offsets_out, hipStream_t s, Marks& m);
 hipError_t launch_permute(const Plan& p, int32_t* counts_out, int32_t* offsets_out, hipStream_t s, Marks& m);
 
 struct ExpertWeights {

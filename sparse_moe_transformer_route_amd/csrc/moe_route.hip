@@ -9,6 +9,7 @@
 #include <float.h>
 
 #include "common.h"
+#include "dispatch.h"
 #include "kernels.h"
 
 namespace hymoe {
@@ -80,129 +81,213 @@ __global__ void __launch_bounds__(64) route_logits_kernel(const uint16_t* __rest
 }
 
 // ---------------------------------------------------------------------------
-// Selection: one wave per token, R = ceil(E/64) logits per lane; k rounds of a
-// wave-wide argmax on (logit, -index), plus one round for the k/k+1 margin.
-// The block of kMaskBlock tokens also builds mask[blk][e] (bit tl set when token
-// blk*64+tl selected e), from which the permutation is derived.
+// Selection: one wave per token. Logits (the split-d partials summed in fixed order,
+// plus the bias) are mapped to order-preserving 32-bit keys; the k-th largest key is
+// found by an MSB-first radix select whose counts are wave ballots, then ties at the
+// threshold go to the lowest expert indices. No lane shuffles in the search loop.
+// The block of kMaskBlock tokens builds mask[blk][e] (bit tl set when token
+// blk*64+tl selected e). With a single block (FUSED) the same workgroup also builds
+// the dispatch lists and the permutation.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void better(float& bv, int& be, float ov, int oe) {
-  if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+constexpr int kMaxSplit = 16;  // router split of d: at most this many partial sums per logit
+
+__device__ __forceinline__ uint32_t mono_key(float v) {
+  const uint32_t u = __float_as_uint(v + 0.0f);  // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int R>
-__global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict__ part, int ks,
-                                                         const float* __restrict__ bias, int T, int E, int k,
-                                                         int32_t* __restrict__ topk_idx,
-                                                         float* __restrict__ topk_w, float* __restrict__ margin,
-                                                         unsigned long long* __restrict__ mask) {
+__device__ __forceinline__ float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+template <int R, bool FUSED>
+__global__ void __launch_bounds__(1024) route_select_kernel(const float* __restrict__ part, int ks,
+                                                            const float* __restrict__ bias, int T, int E, int k,
+                                                            int32_t* __restrict__ topk_idx,
+                                                            float* __restrict__ topk_w, float* __restrict__ margin,
+                                                            unsigned long long* __restrict__ mask, Plan p,
+                                                            int32_t* __restrict__ counts_out,
+                                                            int32_t* __restrict__ offsets_out) {
   __shared__ unsigned long long smask[1024];
+  __shared__ int sidx[FUSED ? kMaskBlock * 16 : 1];
+  __shared__ int soff[FUSED ? 1024 : 1];
+  __shared__ int wsum[17];
   for (int i = threadIdx.x; i < E; i += blockDim.x) smask[i] = 0ull;
   __syncthreads();
 
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nwv = blockDim.x >> 6;
+  const unsigned long long below_lane = (1ull << lane) - 1ull;
   const int blk = blockIdx.x;
-  for (int tl = wv; tl < kMaskBlock; tl += 4) {
+  const size_t TE = (size_t)T * E;
+  for (int tl = wv; tl < kMaskBlock; tl += nwv) {
     const int t = blk * kMaskBlock + tl;
     if (t >= T) break;
-    float v[R];
+    float val[R];
+    uint32_t key[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int e = lane + 64 * r;
       if (e < E) {
-        float s = 0.f;
-        for (int z = 0; z < ks; ++z) s += part[((size_t)z * T + t) * E + e];
-        if (bias) s += bias[e];
-        v[r] = s;
+        // all partial loads issued before the (fixed-order) sum
+        float pz[kMaxSplit];
+#pragma unroll
+        for (int z = 0; z < kMaxSplit; ++z) pz[z] = z < ks ? part[(size_t)z * TE + (size_t)t * E + e] : 0.f;
+        float sum = 0.f;
+#pragma unroll
+        for (int z = 0; z < kMaxSplit; ++z)
+          if (z < ks) sum += pz[z];
+        if (bias) sum += bias[e];
+        val[r] = sum;
+        key[r] = mono_key(sum);
       } else {
-        v[r] = -FLT_MAX;
+        val[r] = 0.f;
+        key[r] = 0u;  // below every finite logit's key
       }
     }
-    unsigned taken = 0u;
-    float myv = 0.f, top = 0.f, last = 0.f;
-    int mye = 0;
-    const int rounds = k < E ? k + 1 : k;
-    for (int j = 0; j < rounds; ++j) {
-      float bv = -INFINITY;
-      int be = 0x7FFFFFFF;
+    // k-th largest key
+    uint32_t tau = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = tau | (1u << bit);
+      int c = 0;
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
+      for (int r = 0; r < R; ++r) c += __popcll(__ballot(key[r] >= cand));
+      if (c >= k) tau = cand;
+    }
+    int cgt = 0;
+    unsigned long long eqm[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      cgt += __popcll(__ballot(key[r] > tau));
+      eqm[r] = __ballot(key[r] == tau);
+    }
+    const int need = k - cgt;  // experts taken from those tied at the threshold
+    bool sel[R];
+    int eq_before = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int mine = __popcll(eqm[r] & below_lane);
+      sel[r] = key[r] > tau || (((eqm[r] >> lane) & 1ull) && eq_before + mine < need);
+      eq_before += __popcll(eqm[r]);
+    }
+    // margin = k-th minus (k+1)-th largest logit (wave-uniform branches)
+    if (margin) {
+      if (k == E) {
+        if (lane == 0) margin[t] = INFINITY;
+      } else if (eq_before > need) {
+        if (lane == 0) margin[t] = 0.f;  // the (k+1)-th is tied with the k-th
+      } else {
+        uint32_t nb = 0u;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          if (key[r] < tau && key[r] > nb) nb = key[r];
+        nb = wave_max_u32(nb);
+        if (lane == 0) margin[t] = key_value(tau) - key_value(nb);
+      }
+    }
+    // softmax over the selected set, shifted by its largest logit
+    uint32_t kmax = 0u;
+#pragma unroll
+    for (int r = 0; r < R; ++r) kmax = max(kmax, key[r]);
+    const float top = key_value(wave_max_u32(kmax));
+    float ex[R], part_sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      ex[r] = sel[r] ? expf(val[r] - top) : 0.f;
+      part_sum += ex[r];
+    }
+    const float zsum = wave_sum(part_sum);
+    // ascending expert order: rank = selected experts with a smaller index
+    int before = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const unsigned long long sm = __ballot(sel[r]);
+      if (sel[r]) {
         const int e = lane + 64 * r;
-        if (e < E && !((taken >> r) & 1u) && v[r] > bv) { bv = v[r]; be = e; }
+        const int rank = before + __popcll(sm & below_lane);
+        topk_idx[(size_t)t * k + rank] = e;
+        topk_w[(size_t)t * k + rank] = ex[r] / zsum;
+        atomicOr(&smask[e], 1ull << tl);
+        if (FUSED) sidx[tl * 16 + rank] = e;
       }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        float ov = __shfl_xor(bv, o, 64);
-        int oe = __shfl_xor(be, o, 64);
-        better(bv, be, ov, oe);
-      }
-      if (j < k) {
-        if (lane == j) { myv = bv; mye = be; }
-        if ((be & 63) == lane) taken |= 1u << (be >> 6);
-        if (j == 0) top = bv;
-        last = bv;
-      } else if (lane == 0 && margin) {
-        margin[t] = last - bv;
-      }
-    }
-    if (k == E && lane == 0 && margin) margin[t] = INFINITY;
-
-    // merge weights: softmax over the selected set, shifted by its maximum
-    const float ex = lane < k ? expf(myv - top) : 0.f;
-    float zsum = ex;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) zsum += __shfl_xor(zsum, o, 64);
-    // ascending expert order: rank of this lane's expert among the selected
-    int rank = 0;
-    for (int j = 0; j < k; ++j) {
-      const int oe = __shfl(mye, j, 64);
-      rank += (oe < mye) ? 1 : 0;
-    }
-    if (lane < k) {
-      topk_idx[(size_t)t * k + rank] = mye;
-      topk_w[(size_t)t * k + rank] = ex / zsum;
-      atomicOr(&smask[mye], 1ull << tl);
+      before += __popcll(sm);
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < E; i += blockDim.x) mask[(size_t)blk * E + i] = smask[i];
+  if (!FUSED) {
+    for (int i = threadIdx.x; i < E; i += blockDim.x) mask[(size_t)blk * E + i] = smask[i];
+    return;
+  }
+  // single token block: counts, work lists and permutation here
+  const int e = threadIdx.x;
+  const int cnt = e < E ? __popcll(smask[e]) : 0;
+  const int excl = build_work_lists(cnt, T, E, k, p.gemm_bm, wsum, p.offs, p.meta, p.touched, p.tiles, counts_out,
+                                    offsets_out);
+  if (e < E) soff[e] = excl;
+  __syncthreads();
+  for (int i = threadIdx.x; i < T * k; i += blockDim.x) {
+    const int t = i / k, j = i - t * k;
+    const int ee = sidx[t * 16 + j];
+    const int row = dispatch_row(soff[ee], smask[ee], t);
+    p.perm_src[row] = i;
+    p.pos[i] = row;
+  }
 }
 
+// Split of d for the router: enough waves to stream W_router from HBM at small T,
+// at most 16 partial sums per logit.
 static int pick_split(int T, int d, int E) {
   const int base = ((T + 31) / 32) * ((E + 63) / 64);
-  const int target = 512;
+  const int target = 256;
   const int steps = d / 64;
   int best = 1;
-  for (int s = 1; s <= steps; ++s)
+  for (int s = 1; s <= steps && s <= kMaxSplit; ++s)
     if (steps % s == 0 && base * s <= target) best = s;
   return best;
 }
 
 int route_split_for(int T, int d, int E) { return pick_split(T, d, E); }
 
+template <int R>
+static void launch_select(const Plan& p, const float* bias, float* margin_out, int32_t* counts_out,
+                          int32_t* offsets_out, hipStream_t s) {
+  if (p.nblk == 1)
+    hipLaunchKernelGGL((route_select_kernel<R, true>), dim3(1), dim3(1024), 0, s, p.part, p.ks, bias, p.T, p.E, p.k,
+                       p.topk_idx, p.topk_w, margin_out, p.mask, p, counts_out, offsets_out);
+  else
+    hipLaunchKernelGGL((route_select_kernel<R, false>), dim3(p.nblk), dim3(1024), 0, s, p.part, p.ks, bias, p.T,
+                       p.E, p.k, p.topk_idx, p.topk_w, margin_out, p.mask, p, counts_out, offsets_out);
+}
+
 hipError_t launch_route(const Plan& p, const uint16_t* x, const uint16_t* w_router, const float* bias,
-                        float* margin_out, hipStream_t s, Marks& m) {
+                        float* margin_out, int32_t* counts_out, int32_t* offsets_out, hipStream_t s, Marks& m) {
   dim3 g1((p.T + 31) / 32, (p.E + 63) / 64, p.ks);
   hipLaunchKernelGGL(route_logits_kernel, g1, dim3(64), 0, s, x, w_router, p.part, p.T, p.d, p.E, p.d / p.ks);
   hipError_t err = hipGetLastError();
   if (err == hipSuccess) err = m.mark(s);
   if (err != hipSuccess) return err;
-  dim3 g2(p.nblk);
   const int R = (p.E + 63) / 64;
   if (R <= 1)
-    hipLaunchKernelGGL(route_topk_kernel<1>, g2, dim3(256), 0, s, p.part, p.ks, bias, p.T, p.E, p.k, p.topk_idx,
-                       p.topk_w, margin_out, p.mask);
+    launch_select<1>(p, bias, margin_out, counts_out, offsets_out, s);
   else if (R <= 2)
-    hipLaunchKernelGGL(route_topk_kernel<2>, g2, dim3(256), 0, s, p.part, p.ks, bias, p.T, p.E, p.k, p.topk_idx,
-                       p.topk_w, margin_out, p.mask);
+    launch_select<2>(p, bias, margin_out, counts_out, offsets_out, s);
   else if (R <= 4)
-    hipLaunchKernelGGL(route_topk_kernel<4>, g2, dim3(256), 0, s, p.part, p.ks, bias, p.T, p.E, p.k, p.topk_idx,
-                       p.topk_w, margin_out, p.mask);
+    launch_select<4>(p, bias, margin_out, counts_out, offsets_out, s);
   else if (R <= 8)
-    hipLaunchKernelGGL(route_topk_kernel<8>, g2, dim3(256), 0, s, p.part, p.ks, bias, p.T, p.E, p.k, p.topk_idx,
-                       p.topk_w, margin_out, p.mask);
+    launch_select<8>(p, bias, margin_out, counts_out, offsets_out, s);
   else
-    hipLaunchKernelGGL(route_topk_kernel<16>, g2, dim3(256), 0, s, p.part, p.ks, bias, p.T, p.E, p.k, p.topk_idx,
-                       p.topk_w, margin_out, p.mask);
+    launch_select<16>(p, bias, margin_out, counts_out, offsets_out, s);
   err = hipGetLastError();
   return err == hipSuccess ? m.mark(s) : err;
 }

@@ -9,10 +9,10 @@
 // preview model card).
 //
 // Work split: one workgroup = one touched expert x 64 output rows; a wave owns 16 rows
-// and streams them along k, 32 contiguous bytes per lane per weight matrix per 64-wide
-// step... in 128-wide chunks: lane (r, g) reads row r, bytes [64g, 64g+64) of the chunk.
-// The 16 rows x up-to-32 tokens product runs on 16x16x32 bf16 MFMA with fp32
-// accumulation. Sherry-ternary experts are decoded in registers from 5-bit codes
+// and streams them along k in 64-element chunks: lane (r, g) reads row r, bytes
+// [32g, 32g+32) of each chunk, with several chunks in flight. The 16 rows x 16 tokens
+// product runs on 16x16x32 bf16 MFMA with fp32 accumulation (experts with more than
+// 16 tokens take several passes). Sherry-ternary experts are decoded in registers from 5-bit codes
 // through a 32-entry LDS table into bf16 +-1/0 and scaled per row after the sum.
 #include "common.h"
 #include "kernels.h"
@@ -31,79 +31,90 @@ struct StreamArgs {
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
 // ------------------------------------------------------------- bf16 experts
-template <int NCB>
+// Weight streaming with a register ring: each lane keeps kDepth chunks of loads in
+// flight (per chunk: 2 x 16 bytes of each weight row it covers, and the matching
+// activations). Activations ride in the same ring as the weights because the
+// vector-memory counter retires loads in issue order: a shallower activation
+// prefetch would make every wait also wait for the newer weight loads.
+// Plain loads: non-temporal hints measured markedly slower on gfx950.
+constexpr int kKV = 2;                  // 16-byte loads per lane per matrix per chunk
+constexpr int kChunk = 4 * kKV * 8;     // elements of a row per chunk (4 lane groups)
+constexpr int kDepthGateUp = 5;         // chunks in flight, gate/up (two matrices)
+constexpr int kDepthDown = 7;           // chunks in flight, down (one matrix)
+
+template <int D>
 __device__ __forceinline__ void gateup_bf16_block(const uint16_t* __restrict__ wg, const uint16_t* __restrict__ wu,
-                                                  const uint16_t* const* xr, const bool* xv, int d, f32x4* accg,
-                                                  f32x4* accu) {
-  uint4 cg[4], cu[4], cx[NCB][4];
-  uint4 ng[4], nu[4], nx[NCB][4];
+                                                  const uint16_t* __restrict__ xr, bool xv, int d, f32x4& accg,
+                                                  f32x4& accu) {
+  const int nch = d / kChunk;
+  uint4 rg[D + 1][kKV], ru[D + 1][kKV], rx[D + 1][kKV];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    cg[s] = ldg16_stream(wg + 8 * s);
-    cu[s] = ldg16_stream(wu + 8 * s);
+  for (int s = 0; s < D; ++s) {
+    if (s < nch) {
 #pragma unroll
-    for (int c = 0; c < NCB; ++c) cx[c][s] = xv[c] ? ldg16(xr[c] + 8 * s) : zero4();
-  }
-  for (int kk = 128; kk <= d; kk += 128) {
-    const bool more = kk < d;
-    if (more) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        ng[s] = ldg16_stream(wg + kk + 8 * s);
-        nu[s] = ldg16_stream(wu + kk + 8 * s);
-#pragma unroll
-        for (int c = 0; c < NCB; ++c) nx[c][s] = xv[c] ? ldg16(xr[c] + kk + 8 * s) : zero4();
+      for (int v = 0; v < kKV; ++v) {
+        rg[s][v] = ldg16(wg + s * kChunk + 8 * v);
+        ru[s][v] = ldg16(wu + s * kChunk + 8 * v);
+        rx[s][v] = xv ? ldg16(xr + s * kChunk + 8 * v) : zero4();
       }
     }
+  }
+  for (int c0 = 0; c0 < nch; c0 += D + 1) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int u = 0; u <= D; ++u) {
+      const int ch = c0 + u;
+      if (ch < nch) {
+        const int nx = ch + D;
+        const int ns = (u + D) % (D + 1);
+        if (nx < nch) {
 #pragma unroll
-      for (int c = 0; c < NCB; ++c) {
-        accg[c] = mfma16x16x32(cg[s], cx[c][s], accg[c]);
-        accu[c] = mfma16x16x32(cu[s], cx[c][s], accu[c]);
-      }
-    if (more) {
+          for (int v = 0; v < kKV; ++v) {
+            rg[ns][v] = ldg16(wg + nx * kChunk + 8 * v);
+            ru[ns][v] = ldg16(wu + nx * kChunk + 8 * v);
+            rx[ns][v] = xv ? ldg16(xr + nx * kChunk + 8 * v) : zero4();
+          }
+        }
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        cg[s] = ng[s];
-        cu[s] = nu[s];
-#pragma unroll
-        for (int c = 0; c < NCB; ++c) cx[c][s] = nx[c][s];
+        for (int v = 0; v < kKV; ++v) {
+          accg = mfma16x16x32(rg[u][v], rx[u][v], accg);
+          accu = mfma16x16x32(ru[u][v], rx[u][v], accu);
+        }
       }
     }
   }
 }
 
-template <int NCB>
-__device__ __forceinline__ void down_bf16_block(const uint16_t* __restrict__ wd, const uint16_t* const* hr,
-                                                const bool* hv, int I, f32x4* acc) {
-  uint4 cw[4], cx[NCB][4], nw[4], nx[NCB][4];
+template <int D>
+__device__ __forceinline__ void down_bf16_block(const uint16_t* __restrict__ wd, const uint16_t* __restrict__ hr,
+                                                bool hv, int I, f32x4& acc) {
+  const int nch = I / kChunk;
+  uint4 rw[D + 1][kKV], rx[D + 1][kKV];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    cw[s] = ldg16_stream(wd + 8 * s);
+  for (int s = 0; s < D; ++s) {
+    if (s < nch) {
 #pragma unroll
-    for (int c = 0; c < NCB; ++c) cx[c][s] = hv[c] ? ldg16(hr[c] + 8 * s) : zero4();
-  }
-  for (int kk = 128; kk <= I; kk += 128) {
-    const bool more = kk < I;
-    if (more) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        nw[s] = ldg16_stream(wd + kk + 8 * s);
-#pragma unroll
-        for (int c = 0; c < NCB; ++c) nx[c][s] = hv[c] ? ldg16(hr[c] + kk + 8 * s) : zero4();
+      for (int v = 0; v < kKV; ++v) {
+        rw[s][v] = ldg16(wd + s * kChunk + 8 * v);
+        rx[s][v] = hv ? ldg16(hr + s * kChunk + 8 * v) : zero4();
       }
     }
+  }
+  for (int c0 = 0; c0 < nch; c0 += D + 1) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int u = 0; u <= D; ++u) {
+      const int ch = c0 + u;
+      if (ch < nch) {
+        const int nx = ch + D;
+        const int ns = (u + D) % (D + 1);
+        if (nx < nch) {
 #pragma unroll
-      for (int c = 0; c < NCB; ++c) acc[c] = mfma16x16x32(cw[s], cx[c][s], acc[c]);
-    if (more) {
+          for (int v = 0; v < kKV; ++v) {
+            rw[ns][v] = ldg16(wd + nx * kChunk + 8 * v);
+            rx[ns][v] = hv ? ldg16(hr + nx * kChunk + 8 * v) : zero4();
+          }
+        }
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        cw[s] = nw[s];
-#pragma unroll
-        for (int c = 0; c < NCB; ++c) cx[c][s] = nx[c][s];
+        for (int v = 0; v < kKV; ++v) acc = mfma16x16x32(rw[u][v], rx[u][v], acc);
       }
     }
   }
@@ -196,6 +207,25 @@ __global__ void __launch_bounds__(256) stream_gateup_kernel(StreamArgs a, Expert
   const int d = a.d, I = a.I;
   const bool routed = e < a.E;
 
+  if (!TERN || !routed) {
+    // bf16 weights: 16 token columns per pass
+    const uint16_t* wg = (routed ? w.gate + (size_t)e * I * d : w.s_gate) + (size_t)(i0 + r16) * d + kKV * 8 * g;
+    const uint16_t* wu = (routed ? w.up + (size_t)e * I * d : w.s_up) + (size_t)(i0 + r16) * d + kKV * 8 * g;
+    for (int cb = 0; cb < n; cb += 16) {
+      const bool valid = cb + r16 < n;
+      const int col = valid ? row0 + cb + r16 : row0;
+      const uint16_t* xr = a.x + (size_t)row_token(col, a.perm_src, a.Tk, a.k) * d + kKV * 8 * g;
+      f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+      gateup_bf16_block<kDepthGateUp>(wg, wu, xr, valid, d, accg, accu);
+      if (valid) {
+        uint2 v = make_uint2(pack_bf16x2(silu(accg[0]) * accu[0], silu(accg[1]) * accu[1]),
+                             pack_bf16x2(silu(accg[2]) * accu[2], silu(accg[3]) * accu[3]));
+        *reinterpret_cast<uint2*>(h + (size_t)col * I + i0 + 4 * g) = v;
+      }
+    }
+    return;
+  }
+
   for (int cb = 0; cb < n; cb += 32) {
     const TokenCols tc = token_cols(a, row0, n, cb, r16);
     const bool two = n - cb > 16;
@@ -204,16 +234,7 @@ __global__ void __launch_bounds__(256) stream_gateup_kernel(StreamArgs a, Expert
     const uint16_t* xrow[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) xrow[c] = a.x + (size_t)row_token(tc.col[c], a.perm_src, a.Tk, a.k) * d;
-
-    if (!TERN || !routed) {
-      const uint16_t* wg = (routed ? w.gate + (size_t)e * I * d : w.s_gate) + (size_t)(i0 + r16) * d + 32 * g;
-      const uint16_t* wu = (routed ? w.up + (size_t)e * I * d : w.s_up) + (size_t)(i0 + r16) * d + 32 * g;
-      const uint16_t* xr[2] = {xrow[0] + 32 * g, xrow[1] + 32 * g};
-      if (two)
-        gateup_bf16_block<2>(wg, wu, xr, tc.valid, d, accg, accu);
-      else
-        gateup_bf16_block<1>(wg, wu, xr, tc.valid, d, accg, accu);
-    } else {
+    {
       const int nb = d / 128, wpr = nb * 5;
       const uint32_t* qg = w.qgate + ((size_t)e * I + i0 + r16) * wpr;
       const uint32_t* qu = w.qup + ((size_t)e * I + i0 + r16) * wpr;
@@ -283,18 +304,24 @@ __global__ void __launch_bounds__(256) stream_down_kernel(StreamArgs a, ExpertWe
   const int d = a.d, I = a.I;
   const bool routed = e < a.E;
 
+  if (!TERN || !routed) {
+    const uint16_t* wd = (routed ? w.down + (size_t)e * d * I : w.s_down) + (size_t)(m0 + r16) * I + kKV * 8 * g;
+    for (int cb = 0; cb < n; cb += 16) {
+      const bool valid = cb + r16 < n;
+      const int col = valid ? row0 + cb + r16 : row0;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      down_bf16_block<kDepthDown>(wd, h + (size_t)col * I + kKV * 8 * g, valid, I, acc);
+      if (valid)
+        *reinterpret_cast<float4*>(y + (size_t)col * d + m0 + 4 * g) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+    return;
+  }
+
   for (int cb = 0; cb < n; cb += 32) {
     const TokenCols tc = token_cols(a, row0, n, cb, r16);
     const bool two = n - cb > 16;
     f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    if (!TERN || !routed) {
-      const uint16_t* wd = (routed ? w.down + (size_t)e * d * I : w.s_down) + (size_t)(m0 + r16) * I + 32 * g;
-      const uint16_t* hr[2] = {h + (size_t)tc.col[0] * I + 32 * g, h + (size_t)tc.col[1] * I + 32 * g};
-      if (two)
-        down_bf16_block<2>(wd, hr, tc.valid, I, acc);
-      else
-        down_bf16_block<1>(wd, hr, tc.valid, I, acc);
-    } else {
+    {
       const int nb = I / 128, wpr = nb * 5;
       const uint32_t* qd = w.qdown + ((size_t)e * d + m0 + r16) * wpr;
       for (int b0 = 0; b0 < nb; b0 += 4) {
