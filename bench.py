@@ -235,6 +235,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the T=8192 measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
+                    help="only run 3 device-to-device copies of this many GiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no multi-GPU "
@@ -246,6 +248,15 @@ def main():
     import hy_inputs as hi
     import sparse_moe_transformer_route_amd as hm
     torch.cuda.set_device(0)
+    if args.calibrate_copy_gib > 0:
+        n = int(args.calibrate_copy_gib * 2 ** 30)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n}))
+        return
 
     cfg = hi.CONFIGS[args.config]
     shared_weights = None

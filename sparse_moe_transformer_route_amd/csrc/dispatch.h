@@ -31,13 +31,21 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total
   return res;
 }
 
+// Splits n rows into ceil(n/bm) tiles: full tiles of bm rows, then the remainder.
+// Tile i = {e, first row, rows, index of the expert's first tile}.
+__device__ __forceinline__ void write_tiles(int e, int n, int bm, int first, int4* __restrict__ tiles) {
+  const int nt = (n + bm - 1) / bm;
+  for (int i = 0; i < nt; ++i) tiles[first + i] = make_int4(e, i * bm, min(bm, n - i * bm), first);
+}
+
 // Thread e (< E) holds cnt = tokens routed to expert e; every thread of the block
 // (blockDim >= E) must call. Writes offs[0..E+1], the touched-expert list (shared
 // expert first, then routed experts with rows in ascending order), the grouped-GEMM
-// M tiles and meta {touched count, tile count}; returns expert e's first row.
+// M tiles (routed experts ascending, then the shared expert) and meta {touched
+// count, tile count}; returns expert e's first row.
 __device__ __forceinline__ int build_work_lists(int cnt, int T, int E, int k, int bm, int* wsum,
                                                 int32_t* __restrict__ offs, int32_t* __restrict__ meta,
-                                                int32_t* __restrict__ touched, int2* __restrict__ tiles,
+                                                int32_t* __restrict__ touched, int4* __restrict__ tiles,
                                                 int32_t* __restrict__ counts_out,
                                                 int32_t* __restrict__ offsets_out) {
   const int e = threadIdx.x;
@@ -59,16 +67,15 @@ __device__ __forceinline__ int build_work_lists(int cnt, int T, int E, int k, in
   const int tpos = block_exclusive_scan(flag, wsum, &ntouched);
   if (flag) touched[1 + tpos] = e;
   if (e == 0) touched[0] = E;
-  // grouped-GEMM M tiles: ceil(count/bm) per routed expert, then the shared expert's
+  // grouped-GEMM M tiles
   const int nt = (e < E) ? (cnt + bm - 1) / bm : 0;
   int routed_tiles = 0;
   const int toff = block_exclusive_scan(nt, wsum, &routed_tiles);
-  for (int i = 0; i < nt; ++i) tiles[toff + i] = make_int2(e, i * bm);
-  const int shared_tiles = (T + bm - 1) / bm;
-  for (int i = e; i < shared_tiles; i += blockDim.x) tiles[routed_tiles + i] = make_int2(E, i * bm);
+  if (nt > 0) write_tiles(e, cnt, bm, toff, tiles);
   if (e == 0) {
+    write_tiles(E, T, bm, routed_tiles, tiles);
     meta[0] = ntouched + 1;
-    meta[1] = routed_tiles + shared_tiles;
+    meta[1] = routed_tiles + (T + bm - 1) / bm;
   }
   return excl;
 }

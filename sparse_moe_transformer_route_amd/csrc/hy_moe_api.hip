@@ -42,7 +42,7 @@ Layout make_layout(int64_t T, int64_t d, int64_t E, int64_t k, int64_t I) {
   L.offs = take(sizeof(int32_t) * (size_t)(E + 2));
   L.meta = take(sizeof(int32_t) * 4);
   L.touched = take(sizeof(int32_t) * (size_t)(E + 1));
-  L.tiles = take(sizeof(int2) * (size_t)L.max_tiles);
+  L.tiles = take(sizeof(int4) * (size_t)L.max_tiles);
   L.perm_src = take(sizeof(int32_t) * (size_t)Tk);
   L.pos = take(sizeof(int32_t) * (size_t)Tk);
   L.h = take(sizeof(uint16_t) * (size_t)rows * I);
@@ -130,7 +130,7 @@ extern "C" int hy_moe_forward_ex(const hy_moe_args* a, void* stream) {
   p.offs = (int32_t*)(ws + L.offs);
   p.meta = (int32_t*)(ws + L.meta);
   p.touched = (int32_t*)(ws + L.touched);
-  p.tiles = (int2*)(ws + L.tiles);
+  p.tiles = (int4*)(ws + L.tiles);
   p.perm_src = a->perm_src ? a->perm_src : (int32_t*)(ws + L.perm_src);
   p.pos = (int32_t*)(ws + L.pos);
   p.h = (uint16_t*)(ws + L.h);

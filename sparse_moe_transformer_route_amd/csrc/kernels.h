@@ -36,7 +36,7 @@ struct Plan {
   int32_t* offs;             // [E+2] row offsets, expert E = shared
   int32_t* meta;             // [4] {touched experts incl. shared, grouped-GEMM tiles, -, -}
   int32_t* touched;          // [E+1] touched experts, ascending, shared (E) last
-  int2* tiles;               // [max_tiles] {expert, first row within expert}
+  int4* tiles;               // [max_tiles] {expert, first row within expert, rows, 0}
   int32_t* perm_src;         // [T*k]
   int32_t* pos;              // [T*k] inverse of perm_src
   uint16_t* h;               // bf16 [rows][I]

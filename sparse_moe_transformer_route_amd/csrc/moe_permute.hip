@@ -19,7 +19,7 @@ __global__ void __launch_bounds__(1024) permute_scan_kernel(const unsigned long 
                                                             int T, int E, int k, int bm,
                                                             int32_t* __restrict__ blk_base,
                                                             int32_t* __restrict__ offs, int32_t* __restrict__ meta,
-                                                            int32_t* __restrict__ touched, int2* __restrict__ tiles,
+                                                            int32_t* __restrict__ touched, int4* __restrict__ tiles,
                                                             int32_t* __restrict__ counts_out,
                                                             int32_t* __restrict__ offsets_out) {
   __shared__ int wsum[17];
