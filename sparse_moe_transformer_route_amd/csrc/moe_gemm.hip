@@ -13,21 +13,25 @@
 // Phase 2 (down): an item is (M tile, 256 output columns) over k = I; y is bf16.
 //
 // M tiles: an expert's rows are cut into tiles of 256 rows plus a remainder. A
-// workgroup is 4 waves, one per SIMD; wave w owns the tile's 32-row blocks w and w+4
-// and all 256 columns (256 fp32 accumulators in AGPRs), so activation rows are
-// loaded once per workgroup.
+// workgroup is 4 waves, one per SIMD, in a 2 x 2 layout: wave (wm, wn) owns the 32-row
+// blocks 2j + wm (j < 4, dealt alternately so a short tile keeps both M-waves busy) and
+// the 128 columns [128 wn, 128 wn + 128) of the 256 x 256 tile: 256 fp32 accumulators
+// in AGPRs.
 //
-// Pipeline, per 32-wide k step: the 256 x 32 weight tile arrives in LDS by direct
-// global->LDS loads into an 8-stage ring (16-byte chunks XOR-swizzled by row, so the
-// MFMA fragment reads are conflict free), seven steps ahead: a slot is refilled right
-// after the barrier that certifies it was read. Each wave's activation rows come into
-// a 4-slot register ring, three steps ahead. Every step issues the same loads (steps
-// outside the range reload a clamped one) so single vector-memory counts cover all
-// waits; the barrier is a bare s_barrier so loads of later steps stay in flight.
+// Pipeline, per 32-wide k step: the step's 256 activation rows and 256 weight rows
+// (64 B each) arrive in LDS by direct global->LDS loads into a 4-stage ring of 32 KB
+// stages; 16-byte chunks are XOR-swizzled by row so the MFMA fragment reads are
+// conflict free. Activation rows are gathered from x through the permutation (gate/up)
+// or read from h (down). Only LDS-bound loads are in flight in the k loop, so the
+// vector-memory wait is an explicit count. One bare barrier per step, placed between
+// the step's two 16-deep MFMA halves, certifies that the next step has landed and that
+// the slot read two steps back is free; it then gets the load of the step three ahead,
+// and the next step's first fragments are read while the second half's MFMAs run.
+// The last four steps are peeled so no load runs past the end.
 // Persistent schedule: items are split into 8 contiguous ranges, one per XCD
 // (workgroup i runs on XCD i mod 8); within an expert they are ordered so that the
-// 32 workgroups running together on an XCD cover a block of up to 4 M tiles x 8-32
-// N tiles and share activations and weights through that XCD's L2.
+// workgroups running together on an XCD cover a block of up to 4 M tiles x 8-32 N
+// tiles and share activations and weights through that XCD's L2.
 #include <type_traits>
 
 #include "common.h"
@@ -38,21 +42,15 @@ namespace hymoe {
 constexpr int kThreads = 256;   // 4 waves, one per SIMD
 constexpr int kRowsMax = 256;   // rows per M tile
 constexpr int kBlk = 32;        // rows per MFMA block (32x32x16)
-constexpr int kWaveBlocks = 2;  // row blocks per wave (4 waves x 2 x 32 = 256), dealt round-robin
-constexpr int kNB = 8;          // 32-column blocks per wave and tile (256 columns)
+constexpr int kWaveBlocks = 4;  // row blocks per wave (2 M-waves x 4 x 32 = 256)
+constexpr int kNB = 4;          // 32-column blocks per wave (2 N-waves x 4 x 32 = 256)
 constexpr int kBK = 32;         // k per step (two 32x32x16 MFMAs deep)
-constexpr int kStages = 8;      // weight ring in LDS, kStages - 1 steps ahead
-constexpr int kASlots = 4;      // activation ring in registers
-constexpr int kAhead = kASlots - 1;              // activation prefetch distance (steps)
-constexpr int kBRows = 256;                      // weight rows per tile
-constexpr int kRowBytes = kBK * 2;               // 64 B per weight row per step
-constexpr int kStageBytes = kBRows * kRowBytes;  // 16 KB
-constexpr int kDma = kStageBytes / 16 / kThreads;  // direct-to-LDS ops per thread per step (4)
-constexpr int kLoadsPerStep = kDma + 2 * kWaveBlocks;  // vector-memory ops a wave issues per step (8)
-// When step ks starts, B(ks) must have landed. It was the first op of step
-// ks-(kStages-1); after it come that step's A loads and the ops of the kStages-2
-// following steps.
-constexpr int kWaitB = 2 * kWaveBlocks + (kStages - 2) * kLoadsPerStep;
+constexpr int kStages = 4;      // LDS ring; K must be a multiple of kStages * kBK
+constexpr int kRowBytes = kBK * 2;               // 64 B per row per step
+constexpr int kHalf = kRowsMax * kRowBytes;      // 16 KB: activation or weight part of a stage
+constexpr int kStageBytes = 2 * kHalf;           // 32 KB
+constexpr int kDma = kHalf / 16 / kThreads;      // direct-to-LDS ops per operand per thread per step (4)
+constexpr int kOpsPerStep = 2 * kDma;            // vector-memory ops a thread issues per step (8)
 
 int grouped_gemm_bm() { return kRowsMax; }
 
@@ -88,9 +86,8 @@ __device__ __forceinline__ void bare_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// 16-byte chunk c (of 4) of a 64-byte B-tile row sits at physical chunk c ^ f(row). f
-// spreads the 16 rows read by one fragment load over distinct bank groups whether LDS
-// serves 8 lanes (128 B) or 16 lanes (256 B) of a 16-byte read per cycle.
+// 16-byte chunk c (of 4) of a 64-byte row sits at physical chunk c ^ f(row). f spreads
+// the rows read by one fragment load over distinct bank groups.
 __device__ __forceinline__ int swz_key(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
 
 template <bool GATEUP>
@@ -101,14 +98,10 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
   __shared__ __attribute__((aligned(16))) uint8_t st1[kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t st2[kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t st3[kStageBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t st4[kStageBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t st5[kStageBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t st6[kStageBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t st7[kStageBytes];
-  uint8_t* const stage[kStages] = {st0, st1, st2, st3, st4, st5, st6, st7};
+  uint8_t* const stage[kStages] = {st0, st1, st2, st3};
 
   const int K = GATEUP ? a.d : a.I;
-  const int NT = GATEUP ? a.I / (kBRows / 2) : (a.d + kBRows - 1) / kBRows;
+  const int NT = GATEUP ? a.I / (kRowsMax / 2) : (a.d + kRowsMax - 1) / kRowsMax;
   const int total = a.meta[1] * NT;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslot = gridDim.x >> 3;
   const int per = (total + 7) >> 3;
@@ -116,6 +109,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
   const int hi = min(total, lo + per);
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, kept scalar
+  const int wm = wv & 1, wn = wv >> 1;
   const int r32 = lane & 31, hf = lane >> 5;
   const int nks = K / kBK;
   // per-lane part of a fragment read for k-substep s: row r32 of a 32-row block, chunk
@@ -123,6 +117,8 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
   // depends only on r32 because blocks start at multiples of 32
   const uint32_t frag_lo[2] = {(uint32_t)(r32 * kRowBytes + (((2 * hf) ^ swz_key(r32)) << 4)),
                                (uint32_t)(r32 * kRowBytes + (((2 * hf + 1) ^ swz_key(r32)) << 4))};
+  const uint32_t fa_off = wm * kBlk * kRowBytes;                      // block 2j + wm
+  const uint32_t fb_off = kHalf + wn * (kRowsMax / 2) * kRowBytes;    // columns 128 wn..
 
   for (int item = lo + slot; item < hi; item += nslot) {
     // items of one expert (its c M tiles x NT N tiles) are ordered in blocks of up to
@@ -139,8 +135,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
     const int nt = r / mgh;
     const int mt = g0 + blk * MG + (r - nt * mgh);
     const int4 tile = a.tiles[mt];
-    // tile fields are workgroup-uniform: keep them scalar so the per-block guards below
-    // are scalar branches
+    // tile fields are workgroup-uniform: keep them scalar
     const int e = __builtin_amdgcn_readfirstlane(tile.x);
     const int m0 = __builtin_amdgcn_readfirstlane(tile.y);
     const int mrows = __builtin_amdgcn_readfirstlane(tile.z);
@@ -148,37 +143,41 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
     const int nrb = (mrows + kBlk - 1) / kBlk;
     const bool routed = e < a.E;
 
-    // A: block j of this wave is tile block wv + 4j; lane row r32, k run [16hf, 16hf+16)
-    // of a step (32 contiguous bytes); 32-bit element offsets from x (gate/up) or h (down)
-    const uint16_t* abase = GATEUP ? a.x : h;
-    uint32_t aoff[kWaveBlocks];
-#pragma unroll
-    for (int j = 0; j < kWaveBlocks; ++j) {
-      const int rr = min((wv + 4 * j) * kBlk + r32, mrows - 1);
-      const int grow = ebase + m0 + rr;
-      aoff[j] = GATEUP ? (uint32_t)(row_token(grow, a.perm_src, a.Tk, a.k) * a.d + 16 * hf)
-                       : (uint32_t)(grow * a.I + 16 * hf);
-    }
-    // B: stage chunk q = 256 i + 64 wv + lane holds row q>>2, physical chunk q&3.
-    // gate/up: rows 0..127 are gate units nt*128.., rows 128..255 the matching up units
-    // (ops i < kDma/2 read gate rows, the rest up rows); down: rows are output columns
-    // nt*256.. (clamped past d; those columns are not stored)
-    const uint16_t* bbase[kDma];
-    uint32_t boff[kDma];
+    // Loads: op i of a thread covers stage rows 64 i + 16 wv + lane/4, physical chunk
+    // lane % 4, i.e. chunk (lane % 4) ^ key(row) of the row's 64-byte k window.
+    // Activations: tile rows past the tile's end reload its last row (never used).
+    // Weights: gate/up rows 64 i .. 64 i + 63 are gate (i even) or up (i odd) units
+    // nt*128 + 64 (i / 2) + [0, 64), so wave (., wn) holds gate and up of the same 64
+    // units; down rows are output columns nt*256 + row, clamped past d (not stored).
+    const uint16_t* ap[kDma];
+    const uint16_t* bp[kDma];
 #pragma unroll
     for (int i = 0; i < kDma; ++i) {
       const int q = kThreads * i + 64 * wv + lane;
-      const int br = q >> 2, lc = (q & 3) ^ swz_key(br);
+      const int row = q >> 2, lc = (q & 3) ^ swz_key(row);
+      const int grow = ebase + m0 + min(row, mrows - 1);
       if (GATEUP) {
-        const uint16_t* mat = i < kDma / 2 ? (routed ? w.gate + (size_t)e * a.I * a.d : w.s_gate)
+        ap[i] = a.x + (size_t)row_token(grow, a.perm_src, a.Tk, a.k) * a.d + 8 * lc;
+        const uint16_t* mat = (i & 1) == 0 ? (routed ? w.gate + (size_t)e * a.I * a.d : w.s_gate)
                                            : (routed ? w.up + (size_t)e * a.I * a.d : w.s_up);
-        bbase[i] = mat + (size_t)nt * (kBRows / 2) * a.d;
-        boff[i] = (uint32_t)((br & (kBRows / 2 - 1)) * a.d + 8 * lc);
+        bp[i] = mat + (size_t)(nt * (kRowsMax / 2) + 64 * (i >> 1) + (row & 63)) * a.d + 8 * lc;
       } else {
-        bbase[i] = routed ? w.down + (size_t)e * a.d * a.I : w.s_down;
-        boff[i] = (uint32_t)(min(nt * kBRows + br, a.d - 1) * a.I + 8 * lc);
+        ap[i] = h + (size_t)grow * a.I + 8 * lc;
+        const uint16_t* mat = routed ? w.down + (size_t)e * a.d * a.I : w.s_down;
+        bp[i] = mat + (size_t)min(nt * kRowsMax + row, a.d - 1) * a.I + 8 * lc;
       }
     }
+    auto issue = [&](int ks, uint8_t* st) {
+      const int kk = ks * kBK;
+      uint8_t* da = st + (64 * wv) * 16;
+#pragma unroll
+      for (int i = 0; i < kDma; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(ap[i] + kk), HY_LDS(da + kThreads * 16 * i), 16, 0, 0);
+#pragma unroll
+      for (int i = 0; i < kDma; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(bp[i] + kk), HY_LDS(da + kHalf + kThreads * 16 * i), 16, 0,
+                                         0);
+    };
 
     f32x16 acc[kWaveBlocks][kNB];
 #pragma unroll
@@ -187,107 +186,140 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
       for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[j][nb][i] = 0.f;
-    uint4 ar[kASlots][kWaveBlocks][2];
 
-    // Every step t issues B(t + kStages - 1) then A(t + kAhead); steps outside [0, nks)
-    // load a clamped (in-range) step, so each step issues the same ops in the same
-    // order and a single vector-memory count covers every wait.
-    auto issue_a = [&](int ks, int u) {
-      const int kk = min(max(ks, 0), nks - 1) * kBK;
+    // prologue: steps 0..kStages-2 in flight, step 0 landed everywhere
 #pragma unroll
-      for (int j = 0; j < kWaveBlocks; ++j) {
-        ar[u][j][0] = ldg16(abase + aoff[j] + kk);
-        ar[u][j][1] = ldg16(abase + aoff[j] + kk + 8);
-      }
-    };
-    auto issue_b = [&](int ks, int u) {
-      const int kk = min(ks, nks - 1) * kBK;
-      uint8_t* dst = stage[u] + (64 * wv) * 16;
-#pragma unroll
-      for (int i = 0; i < kDma; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(bbase[i] + boff[i] + kk), HY_LDS(dst + kThreads * 16 * i),
-                                         16, 0, 0);
-    };
+    for (int t = 0; t < kStages - 1; ++t) issue(t, stage[t]);
+    wait_vm<(kStages - 2) * kOpsPerStep>();
+    bare_barrier();
 
-    // prologue: steps -(kStages-1)..-1 fill the B ring (and issue A(0..kAhead-1) plus
-    // clamped duplicates, so the op pattern matches the steady state)
-#pragma unroll
-    for (int t = -(kStages - 1); t < 0; ++t) {
-      issue_b(t + kStages - 1, t + kStages - 1);
-      issue_a(t + kAhead, (t + kAhead + 2 * kASlots) % kASlots);
-    }
-
-    const int nsteps = (nks + kStages - 1) / kStages * kStages;
     // the k loop, with this wave's number of active row blocks fixed at compile time
-    // (no branches around the MFMAs: they would make the compiler wait for every load)
+    // (no branches around the MFMAs)
     auto k_loop = [&](auto nact_tag) {
       constexpr int NACT = decltype(nact_tag)::value;
-      for (int k0 = 0; k0 < nsteps; k0 += kStages) {
+      uint4 fa[2][kWaveBlocks], fb[2][kNB];
+      // The previous group's reads are waited for (long done: a whole MFMA group ran
+      // since) before this group's are issued, so at most 8 are in flight and the
+      // MFMAs that follow need no wait.
+      auto read_frags = [&](const uint8_t* L, int s) {
+        wait_lds();
 #pragma unroll
-        for (int u = 0; u < kStages; ++u) {
-          const int ks = k0 + u;
-          wait_vm<kWaitB>();  // own B(ks) landed
-          wait_lds();         // own fragment reads of the previous step done
-          bare_barrier();     // everyone's B(ks) landed; the previous step's slot is free
-          issue_b(ks + kStages - 1, (u + kStages - 1) % kStages);
-          issue_a(ks + kAhead, (u + kAhead) % kASlots);
-          if (NACT > 0 && ks < nks) {
-            const uint8_t* L = stage[u];
+        for (int j = 0; j < NACT; ++j)
+          fa[s][j] = *reinterpret_cast<const uint4*>(L + fa_off + j * 2 * kBlk * kRowBytes + frag_lo[s]);
 #pragma unroll
-            for (int sub = 0; sub < 2; ++sub) {
+        for (int nb = 0; nb < kNB; ++nb)
+          fb[s][nb] = *reinterpret_cast<const uint4*>(L + fb_off + nb * kBlk * kRowBytes + frag_lo[s]);
+      };
+      auto mfmas = [&](int s) {
 #pragma unroll
-              for (int q4 = 0; q4 < kNB / 4; ++q4) {
-                uint4 bf[4];
+        for (int j = 0; j < NACT; ++j)
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb)
-                  bf[nb] = *reinterpret_cast<const uint4*>(&L[(4 * q4 + nb) * 32 * kRowBytes + frag_lo[sub]]);
-#pragma unroll
-                for (int j = 0; j < NACT; ++j)
-#pragma unroll
-                  for (int nb = 0; nb < 4; ++nb)
-                    acc[j][4 * q4 + nb] = mfma32x32x16(ar[u % kASlots][j][sub], bf[nb], acc[j][4 * q4 + nb]);
-              }
-            }
-          }
+          for (int nb = 0; nb < kNB; ++nb) acc[j][nb] = mfma32x32x16(fa[s][j], fb[s][nb], acc[j][nb]);
+      };
+      // One step on ring slot U. WAITN: own loads allowed in flight once the next step
+      // has landed; ISSUE: load the step kStages-1 ahead; NEXT: there is a next step.
+      auto step = [&](auto u_tag, auto issue_tag, auto waitn_tag, auto next_tag, int ks) {
+        constexpr int U = decltype(u_tag)::value;
+        constexpr bool ISSUE = decltype(issue_tag)::value;
+        constexpr int WAITN = decltype(waitn_tag)::value;
+        constexpr bool NEXT = decltype(next_tag)::value;
+        // sched_barrier(0) keeps each group in place: the fragment reads stay ahead of
+        // the MFMAs that run while they are in flight
+        read_frags(stage[U], 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(0);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (NEXT) {
+          wait_vm<WAITN>();  // own loads of step ks+1 landed
+          bare_barrier();    // everyone's step ks+1 landed; slot of step ks-1 is free
+          if constexpr (ISSUE) issue(ks + kStages - 1, stage[(U + kStages - 1) % kStages]);
+          read_frags(stage[(U + 1) % kStages], 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(1);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      using I0 = std::integral_constant<int, 0>;
+      using I1 = std::integral_constant<int, 1>;
+      using I2 = std::integral_constant<int, 2>;
+      using I3 = std::integral_constant<int, 3>;
+      using T_ = std::true_type;
+      using F_ = std::false_type;
+      using W8 = std::integral_constant<int, kOpsPerStep>;
+      read_frags(stage[0], 0);
+      int k0 = 0;
+      for (; k0 < nks - kStages; k0 += kStages) {
+        step(I0{}, T_{}, W8{}, T_{}, k0);
+        step(I1{}, T_{}, W8{}, T_{}, k0 + 1);
+        step(I2{}, T_{}, W8{}, T_{}, k0 + 2);
+        step(I3{}, T_{}, W8{}, T_{}, k0 + 3);
       }
+      // last four steps: the first still loads the final step; then nothing new
+      step(I0{}, T_{}, W8{}, T_{}, k0);
+      step(I1{}, F_{}, W8{}, T_{}, k0 + 1);
+      step(I2{}, F_{}, I0{}, T_{}, k0 + 2);
+      step(I3{}, F_{}, I0{}, F_{}, k0 + 3);
     };
-    const int nact = (wv + 4 < nrb) ? 2 : (wv < nrb ? 1 : 0);
-    if (nact == 2)
+    const int nact = min(kWaveBlocks, max(0, (nrb - wm + 1) >> 1));
+    if (nact == 4)
+      k_loop(std::integral_constant<int, 4>{});
+    else if (nact == 3)
+      k_loop(std::integral_constant<int, 3>{});
+    else if (nact == 2)
       k_loop(std::integral_constant<int, 2>{});
     else if (nact == 1)
       k_loop(std::integral_constant<int, 1>{});
     else
       k_loop(std::integral_constant<int, 0>{});
-    // all waves are done with the ring before the next item refills it
+    // all waves are done with the ring: it now stages the output tile
     __builtin_amdgcn_s_waitcnt(0);
     bare_barrier();
 
+    // Epilogue through LDS: the tile is written as 256-row x 64-column bf16 pieces, one
+    // ring stage each (128 B per row; 16-byte chunk c of row r sits at c ^ 4*bit2(r), so
+    // the two lane halves of a write, 4 rows apart, hit different banks), then leaves
+    // with 16-byte stores of whole row segments. gate/up: piece wn holds h units
+    // nt*128 + 64 wn + [0, 64); down: piece 2 wn + nb/2 holds y columns
+    // nt*256 + 64 (2 wn + nb/2) + [0, 64).
 #pragma unroll
     for (int j = 0; j < kWaveBlocks; ++j) {
-      const int rb = wv + 4 * j;
-      if (rb >= nrb) continue;
+      const int rb = 2 * j + wm;
+      if (rb >= nrb) continue;  // wave-uniform
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         // 32x32 accumulator i of lane (r32, hf): row 8(i/4) + 4hf + i%4, column r32
-        const int rr = rb * kBlk + 8 * (i >> 2) + 4 * hf + (i & 3);
-        if (rr >= mrows) continue;
-        const size_t grow = (size_t)(ebase + m0 + rr);
-        if (GATEUP) {
+        const int row = rb * kBlk + 8 * (i >> 2) + 4 * hf + (i & 3);
 #pragma unroll
-          for (int nb = 0; nb < kNB / 2; ++nb) {
-            const float hv = silu(acc[j][nb][i]) * acc[j][nb + kNB / 2][i];
-            h[grow * a.I + nt * (kBRows / 2) + nb * 32 + r32] = (uint16_t)f32_to_bf16_bits(hv);
-          }
-        } else {
-#pragma unroll
-          for (int nb = 0; nb < kNB; ++nb) {
-            const int col = nt * kBRows + nb * 32 + r32;
-            if (col < a.d) y[grow * a.d + col] = (uint16_t)f32_to_bf16_bits(acc[j][nb][i]);
-          }
+        for (int nb = 0; nb < (GATEUP ? kNB / 2 : kNB); ++nb) {
+          const float v = GATEUP ? silu(acc[j][nb][i]) * acc[j][nb + kNB / 2][i] : acc[j][nb][i];
+          const int piece = GATEUP ? wn : 2 * wn + (nb >> 1);
+          const int pcol = GATEUP ? nb * 32 + r32 : (nb & 1) * 32 + r32;
+          const uint32_t off = row * 128 + ((((pcol >> 3) ^ (4 * hf)) << 4) | ((pcol & 7) * 2));
+          uint8_t* const pb = piece == 0 ? st0 : piece == 1 ? st1 : piece == 2 ? st2 : st3;
+          *reinterpret_cast<__bf16*>(pb + off) = (__bf16)v;
         }
       }
     }
+    wait_lds();
+    bare_barrier();
+#pragma unroll
+    for (int pc = 0; pc < (GATEUP ? 2 : 4); ++pc) {
+      const int col0 = GATEUP ? nt * (kRowsMax / 2) + 64 * pc : nt * kRowsMax + 64 * pc;
+      if (!GATEUP && col0 >= a.d) continue;  // d is a multiple of 128: whole pieces fall outside
+#pragma unroll
+      for (int it = 0; it < kRowsMax / 32; ++it) {
+        const int row = it * 32 + (threadIdx.x >> 3), ch = threadIdx.x & 7;
+        if (row < mrows) {
+          const uint4 v = *reinterpret_cast<const uint4*>(stage[pc] + row * 128 + ((ch ^ (4 * ((row >> 2) & 1))) << 4));
+          const size_t grow = (size_t)(ebase + m0 + row);
+          uint16_t* dst = GATEUP ? h + grow * a.I + col0 + ch * 8 : y + grow * a.d + col0 + ch * 8;
+          *reinterpret_cast<uint4*>(dst) = v;
+        }
+      }
+    }
+    // every thread has read its pieces before the next item's loads overwrite them
+    wait_lds();
+    bare_barrier();
   }
 }
 
