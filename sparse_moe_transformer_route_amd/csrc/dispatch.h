@@ -31,11 +31,16 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total
   return res;
 }
 
-// Splits n rows into ceil(n/bm) tiles: full tiles of bm rows, then the remainder.
+// Splits n rows into c = ceil(n/bm) tiles of (nearly) equal size in whole 32-row
+// blocks: ceil(ceil(n/32)/c) blocks each, the last tile taking the rest (never empty).
+// Equal tiles of one expert do the same work per k step, so running side by side they
+// stay in step and share the expert's weight tiles through L2 (a short remainder tile
+// would run ahead and fetch the weights again).
 // Tile i = {e, first row, rows, index of the expert's first tile}.
 __device__ __forceinline__ void write_tiles(int e, int n, int bm, int first, int4* __restrict__ tiles) {
   const int nt = (n + bm - 1) / bm;
-  for (int i = 0; i < nt; ++i) tiles[first + i] = make_int4(e, i * bm, min(bm, n - i * bm), first);
+  const int span = ((n + 31) / 32 + nt - 1) / nt * 32;
+  for (int i = 0; i < nt; ++i) tiles[first + i] = make_int4(e, i * span, min(span, n - i * span), first);
 }
 
 // Thread e (< E) holds cnt = tokens routed to expert e; every thread of the block
