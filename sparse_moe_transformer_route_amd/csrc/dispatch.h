@@ -7,6 +7,7 @@
 #pragma once
 
 #include "common.h"
+#include "kernels.h"
 
 namespace hymoe {
 
@@ -82,6 +83,8 @@ __device__ __forceinline__ int build_work_lists(int cnt, int T, int E, int k, in
     meta[0] = ntouched + 1;
     meta[1] = routed_tiles + (T + bm - 1) / bm;
   }
+  // the grouped GEMM's work counters start at zero on every forward
+  if (e >= kMetaSched && e < kMetaInts) meta[e] = 0;
   return excl;
 }
 

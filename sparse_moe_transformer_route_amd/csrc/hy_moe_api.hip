@@ -40,7 +40,7 @@ Layout make_layout(int64_t T, int64_t d, int64_t E, int64_t k, int64_t I) {
   L.mask = take(sizeof(unsigned long long) * (size_t)L.nblk * E);
   L.blk_base = take(sizeof(int32_t) * (size_t)L.nblk * E);
   L.offs = take(sizeof(int32_t) * (size_t)(E + 2));
-  L.meta = take(sizeof(int32_t) * 4);
+  L.meta = take(sizeof(int32_t) * kMetaInts);
   L.touched = take(sizeof(int32_t) * (size_t)(E + 1));
   L.tiles = take(sizeof(int4) * (size_t)L.max_tiles);
   L.perm_src = take(sizeof(int32_t) * (size_t)Tk);

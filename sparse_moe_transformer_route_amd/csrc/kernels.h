@@ -19,6 +19,9 @@ struct Marks {
 };
 
 // Per-call device state carved from the workspace.
+constexpr int kMetaInts = 32;
+constexpr int kMetaSched = 16;  // first grouped-GEMM work counter in meta
+
 struct Plan {
   int T, d, E, k, I;
   int Tk;          // routed rows, T*k
@@ -34,9 +37,10 @@ struct Plan {
   unsigned long long* mask;  // [nblk][E] token bitmask per (block, expert)
   int32_t* blk_base;         // [nblk][E] first row of (block, expert)
   int32_t* offs;             // [E+2] row offsets, expert E = shared
-  int32_t* meta;             // [4] {touched experts incl. shared, grouped-GEMM tiles, -, -}
-  int32_t* touched;          // [E+1] touched experts, ascending, shared (E) last
-  int4* tiles;               // [max_tiles] {expert, first row within expert, rows, 0}
+  int32_t* meta;             // [kMetaInts]: [0] touched experts incl. shared, [1] grouped-GEMM M tiles,
+                             // [16..23] gate/up and [24..31] down work counters, one per XCD
+  int32_t* touched;          // [E+1] touched experts: shared (E) first, then routed ascending
+  int4* tiles;               // [max_tiles] {expert, first row within expert, rows, expert's first tile}
   int32_t* perm_src;         // [T*k]
   int32_t* pos;              // [T*k] inverse of perm_src
   uint16_t* h;               // bf16 [rows][I]

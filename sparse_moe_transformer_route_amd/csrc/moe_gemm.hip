@@ -29,9 +29,10 @@
 // and the next step's first fragments are read while the second half's MFMAs run.
 // The last four steps are peeled so no load runs past the end.
 // Persistent schedule: items are split into 8 contiguous ranges, one per XCD
-// (workgroup i runs on XCD i mod 8); within an expert they are ordered so that the
-// workgroups running together on an XCD cover a block of up to 4 M tiles x 8-32 N
-// tiles and share activations and weights through that XCD's L2.
+// (workgroup i runs on XCD i mod 8) and claimed in order through per-XCD counters, so
+// workgroups that finish early take more work; within an expert, items are ordered so
+// that the workgroups running together on an XCD cover a block of up to 4 M tiles x
+// 8-32 N tiles and share activations and weights through that XCD's L2.
 #include <type_traits>
 
 #include "common.h"
@@ -58,7 +59,7 @@ struct GemmArgs {
   const uint16_t* x;
   const int32_t* perm_src;
   const int32_t* offs;
-  const int32_t* meta;
+  int32_t* meta;  // [1] M tiles; [kMetaSched..] per-XCD work counters, zeroed by the routing kernels
   const int4* tiles;
   int Tk, k, d, I, E;
 };
@@ -100,13 +101,27 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
   __shared__ __attribute__((aligned(16))) uint8_t st3[kStageBytes];
   uint8_t* const stage[kStages] = {st0, st1, st2, st3};
 
+  __shared__ int next_item;
+
   const int K = GATEUP ? a.d : a.I;
   const int NT = GATEUP ? a.I / (kRowsMax / 2) : (a.d + kRowsMax - 1) / kRowsMax;
   const int total = a.meta[1] * NT;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslot = gridDim.x >> 3;
+  const int xcd = blockIdx.x & 7;
   const int per = (total + 7) >> 3;
-  const int lo = xcd * per;
-  const int hi = min(total, lo + per);
+  int32_t* const counters = a.meta + kMetaSched + (GATEUP ? 0 : 8);
+  // Items are split into 8 contiguous ranges, one per XCD; a workgroup takes the next
+  // item of its own XCD's range (so the items in flight on an XCD are neighbours), and
+  // once that range is used up, the next unclaimed item of another XCD's range.
+  auto claim = [&]() -> int {
+    for (int t = 0; t < 8; ++t) {
+      const int x = (xcd + t) & 7;
+      const int lo = x * per, hi = min(total, lo + per);
+      if (lo >= hi) continue;
+      const int v = atomicAdd(&counters[x], 1);
+      if (lo + v < hi) return lo + v;
+    }
+    return -1;
+  };
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, kept scalar
   const int wm = wv & 1, wn = wv >> 1;
@@ -120,7 +135,11 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
   const uint32_t fa_off = wm * kBlk * kRowBytes;                      // block 2j + wm
   const uint32_t fb_off = kHalf + wn * (kRowsMax / 2) * kRowBytes;    // columns 128 wn..
 
-  for (int item = lo + slot; item < hi; item += nslot) {
+  for (;;) {
+    if (threadIdx.x == 0) next_item = claim();
+    __syncthreads();
+    const int item = next_item;
+    if (item < 0) break;
     // items of one expert (its c M tiles x NT N tiles) are ordered in blocks of up to
     // 4 M tiles, N tile major within a block, so the workgroups running together on
     // an XCD share both the activation rows and the weight tiles through its L2
