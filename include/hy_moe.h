@@ -134,7 +134,8 @@ typedef struct hy_moe_args {
   hy_moe_path path;
   /* optional profiling hook: NULL, or HY_MOE_NUM_STAGE_EVENTS hipEvent_t handles (created
      by the caller) recorded on the stream before the first kernel and after each kernel,
-     in the order listed below; event i+1 minus event i is the duration of kernel i */
+     in the order listed below; event i+1 minus event i is the duration of kernel i. A NULL
+     entry is skipped (that point is not recorded). */
   void** stage_events;
 } hy_moe_args;
 

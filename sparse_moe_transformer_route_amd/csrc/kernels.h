@@ -12,7 +12,7 @@ struct Marks {
   void* const* ev;
   int next;
   hipError_t mark(hipStream_t s) {
-    hipError_t e = ev ? hipEventRecord((hipEvent_t)ev[next], s) : hipSuccess;
+    hipError_t e = (ev && ev[next]) ? hipEventRecord((hipEvent_t)ev[next], s) : hipSuccess;
     ++next;
     return e;
   }

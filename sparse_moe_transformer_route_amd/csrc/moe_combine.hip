@@ -27,39 +27,46 @@ __device__ __forceinline__ void load8(const uint16_t* p, float* v) {
   }
 }
 
+// One workgroup = one token x kCols output columns, 8 consecutive columns per thread
+// (a decode batch of a few tokens still spreads over many CUs).
+constexpr int kCombineThreads = 128;
+constexpr int kCols = kCombineThreads * 8;
+
 template <typename YT>
-__global__ void __launch_bounds__(256) combine_kernel(const YT* __restrict__ y, const int32_t* __restrict__ pos,
-                                                      const float* __restrict__ topk_w, int k, int d, int Tk,
-                                                      uint16_t* __restrict__ out) {
+__global__ void __launch_bounds__(kCombineThreads) combine_kernel(const YT* __restrict__ y,
+                                                                   const int32_t* __restrict__ pos,
+                                                                   const float* __restrict__ topk_w, int k, int d,
+                                                                   int Tk, uint16_t* __restrict__ out) {
   const int t = blockIdx.x;
+  const int c = blockIdx.y * kCols + threadIdx.x * 8;
+  if (c >= d) return;
   const int32_t* pp = pos + (size_t)t * k;
   const float* ww = topk_w + (size_t)t * k;
-  for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const float wj = ww[j];
-      float v[8];
-      load8(y + (size_t)pp[j] * d + c, v);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) {
+    const float wj = ww[j];
+    float v[8];
+    load8(y + (size_t)pp[j] * d + c, v);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wj, v[i], acc[i]);
-    }
-    float s[8];
-    load8(y + (size_t)(Tk + t) * d + c, s);
-    uint4 o;
-    o.x = pack_bf16x2(acc[0] + s[0], acc[1] + s[1]);
-    o.y = pack_bf16x2(acc[2] + s[2], acc[3] + s[3]);
-    o.z = pack_bf16x2(acc[4] + s[4], acc[5] + s[5]);
-    o.w = pack_bf16x2(acc[6] + s[6], acc[7] + s[7]);
-    *reinterpret_cast<uint4*>(out + (size_t)t * d + c) = o;
+    for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wj, v[i], acc[i]);
   }
+  float s[8];
+  load8(y + (size_t)(Tk + t) * d + c, s);
+  uint4 o;
+  o.x = pack_bf16x2(acc[0] + s[0], acc[1] + s[1]);
+  o.y = pack_bf16x2(acc[2] + s[2], acc[3] + s[3]);
+  o.z = pack_bf16x2(acc[4] + s[4], acc[5] + s[5]);
+  o.w = pack_bf16x2(acc[6] + s[6], acc[7] + s[7]);
+  *reinterpret_cast<uint4*>(out + (size_t)t * d + c) = o;
 }
 
 hipError_t launch_combine(const Plan& p, bool y_is_f32, uint16_t* out, hipStream_t s, Marks& m) {
+  const dim3 grid(p.T, (p.d + kCols - 1) / kCols);
   if (y_is_f32)
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(p.T), dim3(256), 0, s, (const float*)p.y, p.pos, p.topk_w, p.k,
-                       p.d, p.Tk, out);
+    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(kCombineThreads), 0, s, (const float*)p.y, p.pos,
+                       p.topk_w, p.k, p.d, p.Tk, out);
   else
-    hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(p.T), dim3(256), 0, s, (const uint16_t*)p.y, p.pos,
+    hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(kCombineThreads), 0, s, (const uint16_t*)p.y, p.pos,
                        p.topk_w, p.k, p.d, p.Tk, out);
   hipError_t err = hipGetLastError();
   return err == hipSuccess ? m.mark(s) : err;
