@@ -12,22 +12,23 @@
 // bf16. A rows are gathered straight from x through the permutation.
 // Phase 2 (down): an item is (M tile, 256 output columns) over k = I; y is bf16.
 //
-// M tiles: an expert's rows are cut into tiles of 256 rows plus a remainder. A
-// workgroup is 4 waves, one per SIMD, in a 2 x 2 layout: wave (wm, wn) owns the 32-row
-// blocks 2j + wm (j < 4, dealt alternately so a short tile keeps both M-waves busy) and
-// the 128 columns [128 wn, 128 wn + 128) of the 256 x 256 tile: 256 fp32 accumulators
-// in AGPRs.
+// M tiles: an expert's rows are cut into near-equal tiles of at most 256 rows (whole
+// 32-row blocks). A workgroup is 4 waves, one per SIMD, in a 2 x 2 layout: wave
+// (wm, wn) owns the 32-row blocks 2j + wm (j < 4, dealt alternately so a short tile
+// keeps both M-waves busy) and the 128 columns [128 wn, 128 wn + 128) of the 256 x 256
+// tile: 256 fp32 accumulators in AGPRs.
 //
-// Pipeline, per 32-wide k step: the step's 256 activation rows and 256 weight rows
-// (64 B each) arrive in LDS by direct global->LDS loads into a 4-stage ring of 32 KB
-// stages; 16-byte chunks are XOR-swizzled by row so the MFMA fragment reads are
-// conflict free. Activation rows are gathered from x through the permutation (gate/up)
-// or read from h (down). Only LDS-bound loads are in flight in the k loop, so the
-// vector-memory wait is an explicit count. One bare barrier per step, placed between
-// the step's two 16-deep MFMA halves, certifies that the next step has landed and that
-// the slot read two steps back is free; it then gets the load of the step three ahead,
-// and the next step's first fragments are read while the second half's MFMAs run.
-// The last four steps are peeled so no load runs past the end.
+// Pipeline, per 64-wide k step: the step's 256 activation rows and 256 weight rows
+// (128 B each: one cache line per row, so the vector L1's limited number of
+// outstanding misses carries twice the bytes of 64-byte pieces) arrive in LDS by
+// direct global->LDS loads into a 2-stage ring of 64 KB stages; 16-byte chunks are
+// XOR-swizzled by row so the MFMA fragment reads are conflict free. Activation rows
+// are gathered from x through the permutation (gate/up) or read from h (down). Only
+// LDS-bound loads are in flight in the k loop, so the vector-memory wait is an
+// explicit count. A step runs 4 MFMA groups (k = 16 each), each group's fragments read
+// while the previous group's MFMAs run; at the end of the step one bare barrier
+// certifies that the next step has landed and that this step's slot is free, which
+// then receives the step after next.
 // Persistent schedule: items are split into 8 contiguous ranges, one per XCD
 // (workgroup i runs on XCD i mod 8) and claimed in order through per-XCD counters, so
 // workgroups that finish early take more work; within an expert, items are ordered so
@@ -45,13 +46,14 @@ constexpr int kRowsMax = 256;   // rows per M tile
 constexpr int kBlk = 32;        // rows per MFMA block (32x32x16)
 constexpr int kWaveBlocks = 4;  // row blocks per wave (2 M-waves x 4 x 32 = 256)
 constexpr int kNB = 4;          // 32-column blocks per wave (2 N-waves x 4 x 32 = 256)
-constexpr int kBK = 32;         // k per step (two 32x32x16 MFMAs deep)
-constexpr int kStages = 4;      // LDS ring; K must be a multiple of kStages * kBK
-constexpr int kRowBytes = kBK * 2;               // 64 B per row per step
-constexpr int kHalf = kRowsMax * kRowBytes;      // 16 KB: activation or weight part of a stage
-constexpr int kStageBytes = 2 * kHalf;           // 32 KB
-constexpr int kDma = kHalf / 16 / kThreads;      // direct-to-LDS ops per operand per thread per step (4)
-constexpr int kOpsPerStep = 2 * kDma;            // vector-memory ops a thread issues per step (8)
+constexpr int kBK = 64;         // k per step (four 32x32x16 MFMAs deep); K % (2 kBK) == 0
+constexpr int kSub = kBK / 16;  // MFMA groups per step
+constexpr int kRowBytes = kBK * 2;               // 128 B per row per step
+constexpr int kChunks = kRowBytes / 16;          // 8 chunks of 16 B per row
+constexpr int kHalf = kRowsMax * kRowBytes;      // 32 KB: activation or weight part of a stage
+constexpr int kStageBytes = 2 * kHalf;           // 64 KB
+constexpr int kDma = kHalf / 16 / kThreads;      // direct-to-LDS ops per operand per thread per step (8)
+constexpr int kOpsPerStep = 2 * kDma;            // vector-memory ops a thread issues per step (16)
 
 int grouped_gemm_bm() { return kRowsMax; }
 
@@ -87,9 +89,9 @@ __device__ __forceinline__ void bare_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// 16-byte chunk c (of 4) of a 64-byte row sits at physical chunk c ^ f(row). f spreads
-// the rows read by one fragment load over distinct bank groups.
-__device__ __forceinline__ int swz_key(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+// 16-byte chunk c (of 8) of a 128-byte row sits at physical chunk c ^ (row % 8): the
+// eight rows read together by one fragment load fall on eight different bank groups.
+__device__ __forceinline__ int swz_key(int row) { return row & 7; }
 
 template <bool GATEUP>
 __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, ExpertWeights w,
@@ -97,9 +99,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
                                                                    uint16_t* __restrict__ y) {
   __shared__ __attribute__((aligned(16))) uint8_t st0[kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t st1[kStageBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t st2[kStageBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t st3[kStageBytes];
-  uint8_t* const stage[kStages] = {st0, st1, st2, st3};
+  uint8_t* const stage[2] = {st0, st1};
 
   __shared__ int next_item;
 
@@ -127,11 +127,12 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
   const int wm = wv & 1, wn = wv >> 1;
   const int r32 = lane & 31, hf = lane >> 5;
   const int nks = K / kBK;
-  // per-lane part of a fragment read for k-substep s: row r32 of a 32-row block, chunk
-  // 2*hf + s (lane half hf holds k [16hf, 16hf+16) of a step), swizzled; the key
+  // per-lane part of a fragment read for k group s: row r32 of a 32-row block, chunk
+  // 2s + hf (lane half hf holds k [8(2s+hf), 8(2s+hf)+8) of the step), swizzled; the key
   // depends only on r32 because blocks start at multiples of 32
-  const uint32_t frag_lo[2] = {(uint32_t)(r32 * kRowBytes + (((2 * hf) ^ swz_key(r32)) << 4)),
-                               (uint32_t)(r32 * kRowBytes + (((2 * hf + 1) ^ swz_key(r32)) << 4))};
+  uint32_t frag_lo[kSub];
+#pragma unroll
+  for (int s = 0; s < kSub; ++s) frag_lo[s] = (uint32_t)(r32 * kRowBytes + (((2 * s + hf) ^ swz_key(r32)) << 4));
   const uint32_t fa_off = wm * kBlk * kRowBytes;                      // block 2j + wm
   const uint32_t fb_off = kHalf + wn * (kRowsMax / 2) * kRowBytes;    // columns 128 wn..
 
@@ -162,24 +163,26 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
     const int nrb = (mrows + kBlk - 1) / kBlk;
     const bool routed = e < a.E;
 
-    // Loads: op i of a thread covers stage rows 64 i + 16 wv + lane/4, physical chunk
-    // lane % 4, i.e. chunk (lane % 4) ^ key(row) of the row's 64-byte k window.
+    // Loads: op i of a thread covers stage rows 32 i + 8 wv + lane/8, physical chunk
+    // lane % 8, i.e. chunk (lane % 8) ^ key(row) of the row's 128-byte k window.
     // Activations: tile rows past the tile's end reload its last row (never used).
-    // Weights: gate/up rows 64 i .. 64 i + 63 are gate (i even) or up (i odd) units
-    // nt*128 + 64 (i / 2) + [0, 64), so wave (., wn) holds gate and up of the same 64
-    // units; down rows are output columns nt*256 + row, clamped past d (not stored).
+    // Weights: gate/up rows 64 q .. 64 q + 63 (q = i / 2) are gate (q even) or up (q odd)
+    // units nt*128 + 64 (q / 2) + [0, 64), so wave (., wn) holds gate and up of the
+    // same 64 units; down rows are output columns nt*256 + row, clamped past d (not
+    // stored).
     const uint16_t* ap[kDma];
     const uint16_t* bp[kDma];
 #pragma unroll
     for (int i = 0; i < kDma; ++i) {
       const int q = kThreads * i + 64 * wv + lane;
-      const int row = q >> 2, lc = (q & 3) ^ swz_key(row);
+      const int row = q >> 3, lc = (q & 7) ^ swz_key(row);
       const int grow = ebase + m0 + min(row, mrows - 1);
       if (GATEUP) {
         ap[i] = a.x + (size_t)row_token(grow, a.perm_src, a.Tk, a.k) * a.d + 8 * lc;
-        const uint16_t* mat = (i & 1) == 0 ? (routed ? w.gate + (size_t)e * a.I * a.d : w.s_gate)
-                                           : (routed ? w.up + (size_t)e * a.I * a.d : w.s_up);
-        bp[i] = mat + (size_t)(nt * (kRowsMax / 2) + 64 * (i >> 1) + (row & 63)) * a.d + 8 * lc;
+        const int qq = i >> 1;  // 64-row quarter of the tile
+        const uint16_t* mat = (qq & 1) == 0 ? (routed ? w.gate + (size_t)e * a.I * a.d : w.s_gate)
+                                            : (routed ? w.up + (size_t)e * a.I * a.d : w.s_up);
+        bp[i] = mat + (size_t)(nt * (kRowsMax / 2) + 64 * (qq >> 1) + (row & 63)) * a.d + 8 * lc;
       } else {
         ap[i] = h + (size_t)grow * a.I + 8 * lc;
         const uint16_t* mat = routed ? w.down + (size_t)e * a.d * a.I : w.s_down;
@@ -206,10 +209,10 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[j][nb][i] = 0.f;
 
-    // prologue: steps 0..kStages-2 in flight, step 0 landed everywhere
-#pragma unroll
-    for (int t = 0; t < kStages - 1; ++t) issue(t, stage[t]);
-    wait_vm<(kStages - 2) * kOpsPerStep>();
+    // prologue: steps 0 and 1 in flight (K >= 128), step 0 landed everywhere
+    issue(0, st0);
+    issue(1, st1);
+    wait_vm<kOpsPerStep>();
     bare_barrier();
 
     // the k loop, with this wave's number of active row blocks fixed at compile time
@@ -224,60 +227,56 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
         wait_lds();
 #pragma unroll
         for (int j = 0; j < NACT; ++j)
-          fa[s][j] = *reinterpret_cast<const uint4*>(L + fa_off + j * 2 * kBlk * kRowBytes + frag_lo[s]);
+          fa[s & 1][j] = *reinterpret_cast<const uint4*>(L + fa_off + j * 2 * kBlk * kRowBytes + frag_lo[s]);
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb)
-          fb[s][nb] = *reinterpret_cast<const uint4*>(L + fb_off + nb * kBlk * kRowBytes + frag_lo[s]);
+          fb[s & 1][nb] = *reinterpret_cast<const uint4*>(L + fb_off + nb * kBlk * kRowBytes + frag_lo[s]);
       };
       auto mfmas = [&](int s) {
 #pragma unroll
         for (int j = 0; j < NACT; ++j)
 #pragma unroll
-          for (int nb = 0; nb < kNB; ++nb) acc[j][nb] = mfma32x32x16(fa[s][j], fb[s][nb], acc[j][nb]);
+          for (int nb = 0; nb < kNB; ++nb) acc[j][nb] = mfma32x32x16(fa[s & 1][j], fb[s & 1][nb], acc[j][nb]);
       };
-      // One step on ring slot U. WAITN: own loads allowed in flight once the next step
-      // has landed; ISSUE: load the step kStages-1 ahead; NEXT: there is a next step.
-      auto step = [&](auto u_tag, auto issue_tag, auto waitn_tag, auto next_tag, int ks) {
+      // One step on ring slot U. ISSUE: load the step after next into this slot once
+      // it is free; NEXT: there is a next step. sched_barrier(0) keeps each group in
+      // place: the fragment reads stay ahead of the MFMAs that run while they are in
+      // flight.
+      auto step = [&](auto u_tag, auto issue_tag, auto next_tag, int ks) {
         constexpr int U = decltype(u_tag)::value;
         constexpr bool ISSUE = decltype(issue_tag)::value;
-        constexpr int WAITN = decltype(waitn_tag)::value;
         constexpr bool NEXT = decltype(next_tag)::value;
-        // sched_barrier(0) keeps each group in place: the fragment reads stay ahead of
-        // the MFMAs that run while they are in flight
-        read_frags(stage[U], 1);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(0);
-        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 1; s < kSub; ++s) {
+          read_frags(stage[U], s);
+          __builtin_amdgcn_sched_barrier(0);
+          mfmas(s - 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
         if constexpr (NEXT) {
-          wait_vm<WAITN>();  // own loads of step ks+1 landed
-          bare_barrier();    // everyone's step ks+1 landed; slot of step ks-1 is free
-          if constexpr (ISSUE) issue(ks + kStages - 1, stage[(U + kStages - 1) % kStages]);
-          read_frags(stage[(U + 1) % kStages], 0);
+          wait_vm<0>();   // own loads of step ks+1 landed
+          wait_lds();     // own reads of this step done
+          bare_barrier(); // everyone's step ks+1 landed; this step's slot is free
+          if constexpr (ISSUE) issue(ks + 2, stage[U]);
+          read_frags(stage[U ^ 1], 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        mfmas(1);
+        mfmas(kSub - 1);
         __builtin_amdgcn_sched_barrier(0);
       };
       using I0 = std::integral_constant<int, 0>;
       using I1 = std::integral_constant<int, 1>;
-      using I2 = std::integral_constant<int, 2>;
-      using I3 = std::integral_constant<int, 3>;
       using T_ = std::true_type;
       using F_ = std::false_type;
-      using W8 = std::integral_constant<int, kOpsPerStep>;
       read_frags(stage[0], 0);
       int k0 = 0;
-      for (; k0 < nks - kStages; k0 += kStages) {
-        step(I0{}, T_{}, W8{}, T_{}, k0);
-        step(I1{}, T_{}, W8{}, T_{}, k0 + 1);
-        step(I2{}, T_{}, W8{}, T_{}, k0 + 2);
-        step(I3{}, T_{}, W8{}, T_{}, k0 + 3);
+      for (; k0 + 3 < nks; k0 += 2) {
+        step(I0{}, T_{}, T_{}, k0);
+        step(I1{}, T_{}, T_{}, k0 + 1);
       }
-      // last four steps: the first still loads the final step; then nothing new
-      step(I0{}, T_{}, W8{}, T_{}, k0);
-      step(I1{}, F_{}, W8{}, T_{}, k0 + 1);
-      step(I2{}, F_{}, I0{}, T_{}, k0 + 2);
-      step(I3{}, F_{}, I0{}, F_{}, k0 + 3);
+      // last two steps (nks is even): nothing new to load
+      step(I0{}, F_{}, T_{}, k0);
+      step(I1{}, F_{}, F_{}, k0 + 1);
     };
     const int nact = min(kWaveBlocks, max(0, (nrb - wm + 1) >> 1));
     if (nact == 4)
@@ -294,11 +293,11 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
     __builtin_amdgcn_s_waitcnt(0);
     bare_barrier();
 
-    // Epilogue through LDS: the tile is written as 256-row x 64-column bf16 pieces, one
-    // ring stage each (128 B per row; 16-byte chunk c of row r sits at c ^ 4*bit2(r), so
-    // the two lane halves of a write, 4 rows apart, hit different banks), then leaves
-    // with 16-byte stores of whole row segments. gate/up: piece wn holds h units
-    // nt*128 + 64 wn + [0, 64); down: piece 2 wn + nb/2 holds y columns
+    // Epilogue through LDS: the tile is written as 256-row x 64-column bf16 pieces of
+    // 32 KB (half a ring stage each; 128 B per row; 16-byte chunk c of row r sits at
+    // c ^ 4*bit2(r), so the two lane halves of a write, 4 rows apart, hit different
+    // banks), then leaves with 16-byte stores of whole row segments. gate/up: piece wn
+    // holds h units nt*128 + 64 wn + [0, 64); down: piece 2 wn + nb/2 holds y columns
     // nt*256 + 64 (2 wn + nb/2) + [0, 64).
 #pragma unroll
     for (int j = 0; j < kWaveBlocks; ++j) {
@@ -313,8 +312,8 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
           const float v = GATEUP ? silu(acc[j][nb][i]) * acc[j][nb + kNB / 2][i] : acc[j][nb][i];
           const int piece = GATEUP ? wn : 2 * wn + (nb >> 1);
           const int pcol = GATEUP ? nb * 32 + r32 : (nb & 1) * 32 + r32;
-          const uint32_t off = row * 128 + ((((pcol >> 3) ^ (4 * hf)) << 4) | ((pcol & 7) * 2));
-          uint8_t* const pb = piece == 0 ? st0 : piece == 1 ? st1 : piece == 2 ? st2 : st3;
+          const uint32_t off = (piece & 1) * kHalf + row * 128 + ((((pcol >> 3) ^ (4 * hf)) << 4) | ((pcol & 7) * 2));
+          uint8_t* const pb = (piece >> 1) == 0 ? st0 : st1;
           *reinterpret_cast<__bf16*>(pb + off) = (__bf16)v;
         }
       }
@@ -325,11 +324,12 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
     for (int pc = 0; pc < (GATEUP ? 2 : 4); ++pc) {
       const int col0 = GATEUP ? nt * (kRowsMax / 2) + 64 * pc : nt * kRowsMax + 64 * pc;
       if (!GATEUP && col0 >= a.d) continue;  // d is a multiple of 128: whole pieces fall outside
+      const uint8_t* pbase = stage[pc >> 1] + (pc & 1) * kHalf;
 #pragma unroll
       for (int it = 0; it < kRowsMax / 32; ++it) {
         const int row = it * 32 + (threadIdx.x >> 3), ch = threadIdx.x & 7;
         if (row < mrows) {
-          const uint4 v = *reinterpret_cast<const uint4*>(stage[pc] + row * 128 + ((ch ^ (4 * ((row >> 2) & 1))) << 4));
+          const uint4 v = *reinterpret_cast<const uint4*>(pbase + row * 128 + ((ch ^ (4 * ((row >> 2) & 1))) << 4));
           const size_t grow = (size_t)(ebase + m0 + row);
           uint16_t* dst = GATEUP ? h + grow * a.I + col0 + ch * 8 : y + grow * a.d + col0 + ch * 8;
           *reinterpret_cast<uint4*>(dst) = v;
