@@ -30,6 +30,11 @@ struct StreamArgs {
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
+// Activation loads are unconditional: lanes of unused token columns point at a valid
+// row (the expert's first token) and their output columns, which depend only on their
+// own activations, are never stored. A load guarded by the lane's own condition would
+// become a branch, after which the compiler can no longer count the loads in flight.
+
 // ------------------------------------------------------------- bf16 experts
 // Weight streaming with a register ring: each lane keeps kDepth chunks of loads in
 // flight (per chunk: 2 x 16 bytes of each weight row it covers, and the matching
@@ -40,44 +45,43 @@ __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 constexpr int kKV = 2;                  // 16-byte loads per lane per matrix per chunk
 constexpr int kChunk = 4 * kKV * 8;     // elements of a row per chunk (4 lane groups)
 constexpr int kDepthGateUp = 5;         // chunks in flight, gate/up (two matrices)
-constexpr int kDepthDown = 7;           // chunks in flight, down (one matrix)
+constexpr int kDepthDown = 3;           // chunks in flight, down (one matrix)
+// In the ternary kernels only the shared expert streams bf16: a shallow ring keeps their
+// register count, and so the number of waves hiding the code-table lookups, in check.
+constexpr int kDepthSharedTern = 2;
 
-template <int D>
-__device__ __forceinline__ void gateup_bf16_block(const uint16_t* __restrict__ wg, const uint16_t* __restrict__ wu,
-                                                  const uint16_t* __restrict__ xr, bool xv, int d, f32x4& accg,
-                                                  f32x4& accu) {
-  const int nch = d / kChunk;
-  uint4 rg[D + 1][kKV], ru[D + 1][kKV], rx[D + 1][kKV];
+// Drives a register ring of D + 1 slots over n items in order: load(i, slot) issues
+// the loads of item i into a slot, use(slot) consumes it, D items ahead of the loads.
+// When n is a multiple of D + 1 the loop body has no branch (loads past the end fetch
+// item n - 1 again, from cache), so the compiler can count the loads in flight and
+// waits for exactly the item it consumes; a guarded prefetch would make it drain the
+// whole ring once per period. Other n take uniform guards.
+template <int D, class Load, class Use>
+__device__ __forceinline__ void ring_stream(int n, Load&& load, Use&& use) {
+  if (n % (D + 1) == 0) {
 #pragma unroll
-  for (int s = 0; s < D; ++s) {
-    if (s < nch) {
+    for (int s = 0; s < D; ++s) load(min(s, n - 1), s);
+    for (int c0 = 0; c0 < n; c0 += D + 1) {
 #pragma unroll
-      for (int v = 0; v < kKV; ++v) {
-        rg[s][v] = ldg16(wg + s * kChunk + 8 * v);
-        ru[s][v] = ldg16(wu + s * kChunk + 8 * v);
-        rx[s][v] = xv ? ldg16(xr + s * kChunk + 8 * v) : zero4();
+      for (int u = 0; u <= D; ++u) {
+        // sched_barrier(0): the scheduler would otherwise sink the loads below the
+        // MFMAs (shorter live ranges) and shrink the ring
+        load(min(c0 + u + D, n - 1), (u + D) % (D + 1));
+        __builtin_amdgcn_sched_barrier(0);
+        use(u);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-  }
-  for (int c0 = 0; c0 < nch; c0 += D + 1) {
+  } else {
 #pragma unroll
-    for (int u = 0; u <= D; ++u) {
-      const int ch = c0 + u;
-      if (ch < nch) {
-        const int nx = ch + D;
-        const int ns = (u + D) % (D + 1);
-        if (nx < nch) {
+    for (int s = 0; s < D; ++s)
+      if (s < n) load(s, s);
+    for (int c0 = 0; c0 < n; c0 += D + 1) {
 #pragma unroll
-          for (int v = 0; v < kKV; ++v) {
-            rg[ns][v] = ldg16(wg + nx * kChunk + 8 * v);
-            ru[ns][v] = ldg16(wu + nx * kChunk + 8 * v);
-            rx[ns][v] = xv ? ldg16(xr + nx * kChunk + 8 * v) : zero4();
-          }
-        }
-#pragma unroll
-        for (int v = 0; v < kKV; ++v) {
-          accg = mfma16x16x32(rg[u][v], rx[u][v], accg);
-          accu = mfma16x16x32(ru[u][v], rx[u][v], accu);
+      for (int u = 0; u <= D; ++u) {
+        if (c0 + u < n) {
+          if (c0 + u + D < n) load(c0 + u + D, (u + D) % (D + 1));
+          use(u);
         }
       }
     }
@@ -85,39 +89,46 @@ __device__ __forceinline__ void gateup_bf16_block(const uint16_t* __restrict__ w
 }
 
 template <int D>
-__device__ __forceinline__ void down_bf16_block(const uint16_t* __restrict__ wd, const uint16_t* __restrict__ hr,
-                                                bool hv, int I, f32x4& acc) {
-  const int nch = I / kChunk;
-  uint4 rw[D + 1][kKV], rx[D + 1][kKV];
+__device__ __forceinline__ void gateup_bf16_block(const uint16_t* __restrict__ wg, const uint16_t* __restrict__ wu,
+                                                  const uint16_t* __restrict__ xr, int d, f32x4& accg,
+                                                  f32x4& accu) {
+  uint4 rg[D + 1][kKV], ru[D + 1][kKV], rx[D + 1][kKV];
+  ring_stream<D>(
+      d / kChunk,
+      [&](int ch, int slot) {
 #pragma unroll
-  for (int s = 0; s < D; ++s) {
-    if (s < nch) {
-#pragma unroll
-      for (int v = 0; v < kKV; ++v) {
-        rw[s][v] = ldg16(wd + s * kChunk + 8 * v);
-        rx[s][v] = hv ? ldg16(hr + s * kChunk + 8 * v) : zero4();
-      }
-    }
-  }
-  for (int c0 = 0; c0 < nch; c0 += D + 1) {
-#pragma unroll
-    for (int u = 0; u <= D; ++u) {
-      const int ch = c0 + u;
-      if (ch < nch) {
-        const int nx = ch + D;
-        const int ns = (u + D) % (D + 1);
-        if (nx < nch) {
-#pragma unroll
-          for (int v = 0; v < kKV; ++v) {
-            rw[ns][v] = ldg16(wd + nx * kChunk + 8 * v);
-            rx[ns][v] = hv ? ldg16(hr + nx * kChunk + 8 * v) : zero4();
-          }
+        for (int v = 0; v < kKV; ++v) {
+          rg[slot][v] = ldg16(wg + ch * kChunk + 8 * v);
+          ru[slot][v] = ldg16(wu + ch * kChunk + 8 * v);
+          rx[slot][v] = ldg16(xr + ch * kChunk + 8 * v);
         }
+      },
+      [&](int u) {
+#pragma unroll
+        for (int v = 0; v < kKV; ++v) {
+          accg = mfma16x16x32(rg[u][v], rx[u][v], accg);
+          accu = mfma16x16x32(ru[u][v], rx[u][v], accu);
+        }
+      });
+}
+
+template <int D>
+__device__ __forceinline__ void down_bf16_block(const uint16_t* __restrict__ wd, const uint16_t* __restrict__ hr,
+                                                int I, f32x4& acc) {
+  uint4 rw[D + 1][kKV], rx[D + 1][kKV];
+  ring_stream<D>(
+      I / kChunk,
+      [&](int ch, int slot) {
+#pragma unroll
+        for (int v = 0; v < kKV; ++v) {
+          rw[slot][v] = ldg16(wd + ch * kChunk + 8 * v);
+          rx[slot][v] = ldg16(hr + ch * kChunk + 8 * v);
+        }
+      },
+      [&](int u) {
 #pragma unroll
         for (int v = 0; v < kKV; ++v) acc = mfma16x16x32(rw[u][v], rx[u][v], acc);
-      }
-    }
-  }
+      });
 }
 
 // ---------------------------------------------------------- ternary experts
@@ -141,55 +152,55 @@ __device__ __forceinline__ void build_code_table(uint2* lut) {
   }
 }
 
-// 5-bit code of group q (0..31) of a 160-bit block held in w[0..4].
-__device__ __forceinline__ uint32_t group_code(const uint32_t* w, int q) {
-  const int bit = 5 * q;
-  const int wi = bit >> 5, sh = bit & 31;
-  uint32_t v = w[wi] >> sh;
-  if (sh > 27) v |= w[wi + 1] << (32 - sh);
-  return v & 31u;
+// Ternary streaming with the same register ring as the bf16 path, over packed blocks of
+// 128 weights (5 words, 1.25 bits per weight). The MFMA's k assignment gives lane
+// group g the 32 weights [32g, 32g + 32) of a block, i.e. groups 8g .. 8g+7, whose 40
+// code bits start at bit 40g: words (5g)/4 and (5g)/4 + 1, shifted right by 8g. Code
+// bits [10m, 10m + 10) of that window are the two groups of k-step m (m < 4), decoded
+// through the LDS table into the 8 bf16 weights of the MFMA's A operand; the matching
+// activations are x[128 b + 32 g + 8 m, +8).
+constexpr int kTernDepth = 3;  // blocks in flight (48 and 16 blocks per row divide by 4)
+
+__device__ __forceinline__ uint4 tern_operand(uint64_t v, int m, const uint2* lut) {
+  const uint2 lo = lut[(uint32_t)(v >> (10 * m)) & 31u];
+  const uint2 hi = lut[(uint32_t)(v >> (10 * m + 5)) & 31u];
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
-// Accumulates one packed block (128 weights of this lane's row) against NCB token
-// blocks; xr[c] points at the matching 128 activations of the lane's token.
-template <int NCB>
-__device__ __forceinline__ void ternary_block_mfma(const uint32_t* w, const uint2* lut, const uint16_t* const* xr,
-                                                   const bool* xv, f32x4* acc) {
-#pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    const uint2 lo = lut[group_code(w, 2 * s)];
-    const uint2 hi = lut[group_code(w, 2 * s + 1)];
-    const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
-#pragma unroll
-    for (int c = 0; c < NCB; ++c) {
-      const uint4 b = xv[c] ? ldg16(xr[c] + 8 * s) : zero4();
-      acc[c] = mfma16x16x32(a, b, acc[c]);
-    }
-  }
+__device__ __forceinline__ uint64_t tern_window(const uint32_t* c, int g) {
+  return ((uint64_t)c[0] | ((uint64_t)c[1] << 32)) >> (8 * g);
 }
 
-__device__ __forceinline__ void load_block5(const uint32_t* p, uint32_t* w) {
+// NM weight matrices (gate and up, or down) of 16 rows against up to 16 token columns.
+// q[mi]: this lane's row of matrix mi, already offset by the lane's first code word;
+// xr: this lane's token row offset by 32 g.
+template <int NM, int D>
+__device__ __forceinline__ void tern_rows_block(const uint32_t* const* q, const uint16_t* __restrict__ xr, int nb,
+                                                int g, const uint2* lut, f32x4* acc) {
+  uint32_t rc[D + 1][NM][2];
+  uint4 rx[D + 1][4];
+  ring_stream<D>(
+      nb,
+      [&](int blk, int slot) {
 #pragma unroll
-  for (int i = 0; i < 5; ++i) w[i] = __builtin_nontemporal_load(p + i);
+        for (int mi = 0; mi < NM; ++mi) {
+          rc[slot][mi][0] = q[mi][5 * blk];
+          rc[slot][mi][1] = q[mi][5 * blk + 1];
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) rx[slot][m] = ldg16(xr + 128 * blk + 8 * m);
+      },
+      [&](int u) {
+#pragma unroll
+        for (int mi = 0; mi < NM; ++mi) {
+          const uint64_t v = tern_window(rc[u][mi], g);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) acc[mi] = mfma16x16x32(tern_operand(v, m, lut), rx[u][m], acc[mi]);
+        }
+      });
 }
 
 // ------------------------------------------------------------------ kernels
-struct TokenCols {
-  int col[2];
-  bool valid[2];
-};
-
-__device__ __forceinline__ TokenCols token_cols(const StreamArgs& a, int row0, int n, int cb, int r16) {
-  TokenCols tc;
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int j = cb + 16 * c + r16;
-    tc.valid[c] = j < n;
-    tc.col[c] = tc.valid[c] ? row0 + j : row0;
-  }
-  return tc;
-}
-
 template <bool TERN>
 __global__ void __launch_bounds__(256) stream_gateup_kernel(StreamArgs a, ExpertWeights w, uint16_t* __restrict__ h) {
   __shared__ uint2 lut[32];
@@ -216,7 +227,7 @@ __global__ void __launch_bounds__(256) stream_gateup_kernel(StreamArgs a, Expert
       const int col = valid ? row0 + cb + r16 : row0;
       const uint16_t* xr = a.x + (size_t)row_token(col, a.perm_src, a.Tk, a.k) * d + kKV * 8 * g;
       f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-      gateup_bf16_block<kDepthGateUp>(wg, wu, xr, valid, d, accg, accu);
+      gateup_bf16_block<TERN ? kDepthSharedTern : kDepthGateUp>(wg, wu, xr, d, accg, accu);
       if (valid) {
         uint2 v = make_uint2(pack_bf16x2(silu(accg[0]) * accu[0], silu(accg[1]) * accu[1]),
                              pack_bf16x2(silu(accg[2]) * accu[2], silu(accg[3]) * accu[3]));
@@ -226,62 +237,30 @@ __global__ void __launch_bounds__(256) stream_gateup_kernel(StreamArgs a, Expert
     return;
   }
 
-  for (int cb = 0; cb < n; cb += 32) {
-    const TokenCols tc = token_cols(a, row0, n, cb, r16);
-    const bool two = n - cb > 16;
-    f32x4 accg[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    f32x4 accu[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    const uint16_t* xrow[2];
+  // Sherry-ternary routed expert: 16 token columns per pass, scaled per row at the end
+  const int nb = d / 128, wpr = nb * 5;
+  const int w0 = (5 * g) >> 2;
+  const uint32_t* q[2] = {w.qgate + ((size_t)e * I + i0 + r16) * wpr + w0,
+                          w.qup + ((size_t)e * I + i0 + r16) * wpr + w0};
+  float sg[4], su[4];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) xrow[c] = a.x + (size_t)row_token(tc.col[c], a.perm_src, a.Tk, a.k) * d;
-    {
-      const int nb = d / 128, wpr = nb * 5;
-      const uint32_t* qg = w.qgate + ((size_t)e * I + i0 + r16) * wpr;
-      const uint32_t* qu = w.qup + ((size_t)e * I + i0 + r16) * wpr;
-      for (int b0 = 0; b0 < nb; b0 += 4) {
-        const int b = b0 + g;
-        const bool bv = b < nb;
-        uint32_t bg[5], bu[5];
-        if (bv) {
-          load_block5(qg + 5 * b, bg);
-          load_block5(qu + 5 * b, bu);
-        } else {
+  for (int r = 0; r < 4; ++r) {
+    // D row 4g + r is hidden unit i0 + 4g + r
+    sg[r] = bf16_bits_to_f32(w.sgate[(size_t)e * I + i0 + 4 * g + r]);
+    su[r] = bf16_bits_to_f32(w.sup[(size_t)e * I + i0 + 4 * g + r]);
+  }
+  for (int cb = 0; cb < n; cb += 16) {
+    const bool valid = cb + r16 < n;
+    const int col = valid ? row0 + cb + r16 : row0;
+    const uint16_t* xr = a.x + (size_t)row_token(col, a.perm_src, a.Tk, a.k) * d + 32 * g;
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    tern_rows_block<2, kTernDepth>(q, xr, nb, g, lut, acc);
+    if (valid) {
+      float hv[4];
 #pragma unroll
-          for (int i = 0; i < 5; ++i) bg[i] = bu[i] = 0u;
-        }
-        const uint16_t* xr[2] = {xrow[0] + 128 * b, xrow[1] + 128 * b};
-        const bool xv[2] = {tc.valid[0] && bv, tc.valid[1] && bv};
-        if (two) {
-          ternary_block_mfma<2>(bg, lut, xr, xv, accg);
-          ternary_block_mfma<2>(bu, lut, xr, xv, accu);
-        } else {
-          ternary_block_mfma<1>(bg, lut, xr, xv, accg);
-          ternary_block_mfma<1>(bu, lut, xr, xv, accu);
-        }
-      }
-      // per-row scales: D row 4g+q is hidden unit i0 + 4g + q
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float sg = bf16_bits_to_f32(w.sgate[(size_t)e * I + i0 + 4 * g + q]);
-        const float su = bf16_bits_to_f32(w.sup[(size_t)e * I + i0 + 4 * g + q]);
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          accg[c][q] *= sg;
-          accu[c][q] *= su;
-        }
-      }
-    }
-    // h[row][i0 + 4g + q] = silu(gate) * up, as bf16
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      if (c == 1 && !two) break;
-      if (!tc.valid[c]) continue;
-      const float h0 = silu(accg[c][0]) * accu[c][0];
-      const float h1 = silu(accg[c][1]) * accu[c][1];
-      const float h2 = silu(accg[c][2]) * accu[c][2];
-      const float h3 = silu(accg[c][3]) * accu[c][3];
-      uint2 v = make_uint2(pack_bf16x2(h0, h1), pack_bf16x2(h2, h3));
-      *reinterpret_cast<uint2*>(h + (size_t)tc.col[c] * I + i0 + 4 * g) = v;
+      for (int r = 0; r < 4; ++r) hv[r] = silu(acc[0][r] * sg[r]) * (acc[1][r] * su[r]);
+      *reinterpret_cast<uint2*>(h + (size_t)col * I + i0 + 4 * g) =
+          make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
     }
   }
 }
@@ -310,51 +289,27 @@ __global__ void __launch_bounds__(256) stream_down_kernel(StreamArgs a, ExpertWe
       const bool valid = cb + r16 < n;
       const int col = valid ? row0 + cb + r16 : row0;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      down_bf16_block<kDepthDown>(wd, h + (size_t)col * I + kKV * 8 * g, valid, I, acc);
+      down_bf16_block<TERN ? kDepthSharedTern : kDepthDown>(wd, h + (size_t)col * I + kKV * 8 * g, I, acc);
       if (valid)
         *reinterpret_cast<float4*>(y + (size_t)col * d + m0 + 4 * g) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
     return;
   }
 
-  for (int cb = 0; cb < n; cb += 32) {
-    const TokenCols tc = token_cols(a, row0, n, cb, r16);
-    const bool two = n - cb > 16;
-    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    {
-      const int nb = I / 128, wpr = nb * 5;
-      const uint32_t* qd = w.qdown + ((size_t)e * d + m0 + r16) * wpr;
-      for (int b0 = 0; b0 < nb; b0 += 4) {
-        const int b = b0 + g;
-        const bool bv = b < nb;
-        uint32_t bw[5];
-        if (bv) {
-          load_block5(qd + 5 * b, bw);
-        } else {
+  // Sherry-ternary routed expert: 16 token columns per pass, scaled per row at the end
+  const int nb = I / 128, wpr = nb * 5;
+  const uint32_t* q[1] = {w.qdown + ((size_t)e * d + m0 + r16) * wpr + ((5 * g) >> 2)};
+  float sd[4];
 #pragma unroll
-          for (int i = 0; i < 5; ++i) bw[i] = 0u;
-        }
-        const uint16_t* hr[2] = {h + (size_t)tc.col[0] * I + 128 * b, h + (size_t)tc.col[1] * I + 128 * b};
-        const bool hv[2] = {tc.valid[0] && bv, tc.valid[1] && bv};
-        if (two)
-          ternary_block_mfma<2>(bw, lut, hr, hv, acc);
-        else
-          ternary_block_mfma<1>(bw, lut, hr, hv, acc);
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float sd = bf16_bits_to_f32(w.sdown[(size_t)e * d + m0 + 4 * g + q]);
-        acc[0][q] *= sd;
-        acc[1][q] *= sd;
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      if (c == 1 && !two) break;
-      if (!tc.valid[c]) continue;
-      *reinterpret_cast<float4*>(y + (size_t)tc.col[c] * d + m0 + 4 * g) =
-          make_float4(acc[c][0], acc[c][1], acc[c][2], acc[c][3]);
-    }
+  for (int r = 0; r < 4; ++r) sd[r] = bf16_bits_to_f32(w.sdown[(size_t)e * d + m0 + 4 * g + r]);
+  for (int cb = 0; cb < n; cb += 16) {
+    const bool valid = cb + r16 < n;
+    const int col = valid ? row0 + cb + r16 : row0;
+    f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+    tern_rows_block<1, kTernDepth>(q, h + (size_t)col * I + 32 * g, nb, g, lut, acc);
+    if (valid)
+      *reinterpret_cast<float4*>(y + (size_t)col * d + m0 + 4 * g) =
+          make_float4(acc[0][0] * sd[0], acc[0][1] * sd[1], acc[0][2] * sd[2], acc[0][3] * sd[3]);
   }
 }
 
