@@ -160,6 +160,7 @@ __device__ __forceinline__ void build_code_table(uint2* lut) {
 // through the LDS table into the 8 bf16 weights of the MFMA's A operand; the matching
 // activations are x[128 b + 32 g + 8 m, +8).
 constexpr int kTernDepth = 3;  // blocks in flight (48 and 16 blocks per row divide by 4)
+constexpr int kTernRowBlocks = 2;  // 16-row blocks per wave: a workgroup covers 128 rows
 
 __device__ __forceinline__ uint4 tern_operand(uint64_t v, int m, const uint2* lut) {
   const uint2 lo = lut[(uint32_t)(v >> (10 * m)) & 31u];
@@ -171,36 +172,51 @@ __device__ __forceinline__ uint64_t tern_window(const uint32_t* c, int g) {
   return ((uint64_t)c[0] | ((uint64_t)c[1] << 32)) >> (8 * g);
 }
 
-// NM weight matrices (gate and up, or down) of 16 rows against up to 16 token columns.
-// q[mi]: this lane's row of matrix mi, already offset by the lane's first code word;
-// xr: this lane's token row offset by 32 g.
-template <int NM, int D>
-__device__ __forceinline__ void tern_rows_block(const uint32_t* const* q, const uint16_t* __restrict__ xr, int nb,
-                                                int g, const uint2* lut, f32x4* acc) {
-  uint32_t rc[D + 1][NM][2];
+// NM weight matrices (gate and up, or down) x NR blocks of 16 rows against up to 16
+// token columns; the row blocks share each activation operand. q[mi][r]: this lane's
+// row in row block r of matrix mi, already offset by the lane's first code word; xr:
+// this lane's token row offset by 32 g.
+template <int NM, int NR, int D>
+__device__ __forceinline__ void tern_rows_block(const uint32_t* const (*q)[NR], const uint16_t* __restrict__ xr,
+                                                int nb, int g, const uint2* lut, f32x4 (*acc)[NR]) {
+  uint32_t rc[D + 1][NM][NR][2];
   uint4 rx[D + 1][4];
   ring_stream<D>(
       nb,
       [&](int blk, int slot) {
 #pragma unroll
-        for (int mi = 0; mi < NM; ++mi) {
-          rc[slot][mi][0] = q[mi][5 * blk];
-          rc[slot][mi][1] = q[mi][5 * blk + 1];
-        }
+        for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            rc[slot][mi][r][0] = q[mi][r][5 * blk];
+            rc[slot][mi][r][1] = q[mi][r][5 * blk + 1];
+          }
 #pragma unroll
         for (int m = 0; m < 4; ++m) rx[slot][m] = ldg16(xr + 128 * blk + 8 * m);
       },
       [&](int u) {
 #pragma unroll
-        for (int mi = 0; mi < NM; ++mi) {
-          const uint64_t v = tern_window(rc[u][mi], g);
+        for (int mi = 0; mi < NM; ++mi)
 #pragma unroll
-          for (int m = 0; m < 4; ++m) acc[mi] = mfma16x16x32(tern_operand(v, m, lut), rx[u][m], acc[mi]);
-        }
+          for (int r = 0; r < NR; ++r) {
+            const uint64_t v = tern_window(rc[u][mi][r], g);
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+              acc[mi][r] = mfma16x16x32(tern_operand(v, m, lut), rx[u][m], acc[mi][r]);
+          }
       });
 }
 
 // ------------------------------------------------------------------ kernels
+// Grid rows (blockIdx.y): in the ternary kernels the first ones each take one 16-token
+// pass and one 64-row half of the shared expert (bf16 there, and much larger than a
+// ternary expert), so its passes run side by side from the start instead of one after
+// another; in the bf16 kernels the shared expert has one row. Then one touched routed
+// expert each (touched[0] is the shared expert).
+__device__ __forceinline__ int shared_slots(const StreamArgs& a, bool tern) {
+  return tern ? ((a.Tk / a.k + 15) / 16) * 2 : 1;
+}
+
 template <bool TERN>
 __global__ void __launch_bounds__(256) stream_gateup_kernel(StreamArgs a, ExpertWeights w, uint16_t* __restrict__ h) {
   __shared__ uint2 lut[32];
@@ -208,21 +224,32 @@ __global__ void __launch_bounds__(256) stream_gateup_kernel(StreamArgs a, Expert
     build_code_table(lut);
     __syncthreads();
   }
-  const int slot = blockIdx.y;
-  if (slot >= a.meta[0]) return;
-  const int e = a.touched[slot];
-  const int row0 = a.offs[e], n = a.offs[e + 1] - row0;
+  // plain scalars (a struct here ended up in scratch memory)
+  const int sh = shared_slots(a, TERN), slot = blockIdx.y;
+  const bool shared_part = slot < sh;
+  const int ridx = slot - sh + 1;
+  if (!shared_part && ridx >= a.meta[0]) return;
+  const int e = shared_part ? a.E : a.touched[ridx];
+  // ternary kernels: a shared-expert row takes one 16-token pass and one 64-row half
+  const int cb_first = (TERN && shared_part) ? 16 * (slot >> 1) : 0;
+  const int sub_first = (TERN && shared_part) ? (slot & 1) : 0;
+  const int sub_last = TERN ? (shared_part ? sub_first + 1 : 2) : 1;
+  const int row0 = a.offs[e];
+  const int n = (TERN && shared_part) ? min(a.offs[e + 1] - row0, cb_first + 16) : a.offs[e + 1] - row0;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int r16 = lane & 15, g = lane >> 4;
-  const int i0 = blockIdx.x * 64 + wv * 16;
   const int d = a.d, I = a.I;
   const bool routed = e < a.E;
 
   if (!TERN || !routed) {
-    // bf16 weights: 16 token columns per pass
+    // bf16 weights: 64 rows per pass (a ternary-kernel workgroup covers 128 rows),
+    // 16 token columns per pass
+#pragma unroll 1
+    for (int sub = sub_first; sub < sub_last; ++sub) {
+    const int i0 = blockIdx.x * (TERN ? 128 : 64) + sub * 64 + wv * 16;
     const uint16_t* wg = (routed ? w.gate + (size_t)e * I * d : w.s_gate) + (size_t)(i0 + r16) * d + kKV * 8 * g;
     const uint16_t* wu = (routed ? w.up + (size_t)e * I * d : w.s_up) + (size_t)(i0 + r16) * d + kKV * 8 * g;
-    for (int cb = 0; cb < n; cb += 16) {
+    for (int cb = cb_first; cb < n; cb += 16) {
       const bool valid = cb + r16 < n;
       const int col = valid ? row0 + cb + r16 : row0;
       const uint16_t* xr = a.x + (size_t)row_token(col, a.perm_src, a.Tk, a.k) * d + kKV * 8 * g;
@@ -234,33 +261,48 @@ __global__ void __launch_bounds__(256) stream_gateup_kernel(StreamArgs a, Expert
         *reinterpret_cast<uint2*>(h + (size_t)col * I + i0 + 4 * g) = v;
       }
     }
+    }
     return;
   }
 
-  // Sherry-ternary routed expert: 16 token columns per pass, scaled per row at the end
+  // Sherry-ternary routed expert: rows i0 + 16 r + r16 (r < kTernRowBlocks), 16 token
+  // columns per pass, scaled per row at the end
+  constexpr int NR = kTernRowBlocks;
+  const int i0 = blockIdx.x * 128 + wv * 16 * NR;
   const int nb = d / 128, wpr = nb * 5;
   const int w0 = (5 * g) >> 2;
-  const uint32_t* q[2] = {w.qgate + ((size_t)e * I + i0 + r16) * wpr + w0,
-                          w.qup + ((size_t)e * I + i0 + r16) * wpr + w0};
-  float sg[4], su[4];
+  const uint32_t* q[2][NR];
+  float sg[NR][4], su[NR][4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    // D row 4g + r is hidden unit i0 + 4g + r
-    sg[r] = bf16_bits_to_f32(w.sgate[(size_t)e * I + i0 + 4 * g + r]);
-    su[r] = bf16_bits_to_f32(w.sup[(size_t)e * I + i0 + 4 * g + r]);
+  for (int r = 0; r < NR; ++r) {
+    q[0][r] = w.qgate + ((size_t)e * I + i0 + 16 * r + r16) * wpr + w0;
+    q[1][r] = w.qup + ((size_t)e * I + i0 + 16 * r + r16) * wpr + w0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // D row 4g + j of row block r is hidden unit i0 + 16r + 4g + j
+      sg[r][j] = bf16_bits_to_f32(w.sgate[(size_t)e * I + i0 + 16 * r + 4 * g + j]);
+      su[r][j] = bf16_bits_to_f32(w.sup[(size_t)e * I + i0 + 16 * r + 4 * g + j]);
+    }
   }
   for (int cb = 0; cb < n; cb += 16) {
     const bool valid = cb + r16 < n;
     const int col = valid ? row0 + cb + r16 : row0;
     const uint16_t* xr = a.x + (size_t)row_token(col, a.perm_src, a.Tk, a.k) * d + 32 * g;
-    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    tern_rows_block<2, kTernDepth>(q, xr, nb, g, lut, acc);
-    if (valid) {
-      float hv[4];
+    f32x4 acc[2][NR];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) hv[r] = silu(acc[0][r] * sg[r]) * (acc[1][r] * su[r]);
-      *reinterpret_cast<uint2*>(h + (size_t)col * I + i0 + 4 * g) =
-          make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int r = 0; r < NR; ++r) acc[mi][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    tern_rows_block<2, NR, kTernDepth>(q, xr, nb, g, lut, acc);
+    if (valid) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        float hv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hv[j] = silu(acc[0][r][j] * sg[r][j]) * (acc[1][r][j] * su[r][j]);
+        *reinterpret_cast<uint2*>(h + (size_t)col * I + i0 + 16 * r + 4 * g) =
+            make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+      }
     }
   }
 }
@@ -273,19 +315,29 @@ __global__ void __launch_bounds__(256) stream_down_kernel(StreamArgs a, ExpertWe
     build_code_table(lut);
     __syncthreads();
   }
-  const int slot = blockIdx.y;
-  if (slot >= a.meta[0]) return;
-  const int e = a.touched[slot];
-  const int row0 = a.offs[e], n = a.offs[e + 1] - row0;
+  // plain scalars (a struct here ended up in scratch memory)
+  const int sh = shared_slots(a, TERN), slot = blockIdx.y;
+  const bool shared_part = slot < sh;
+  const int ridx = slot - sh + 1;
+  if (!shared_part && ridx >= a.meta[0]) return;
+  const int e = shared_part ? a.E : a.touched[ridx];
+  // ternary kernels: a shared-expert row takes one 16-token pass and one 64-row half
+  const int cb_first = (TERN && shared_part) ? 16 * (slot >> 1) : 0;
+  const int sub_first = (TERN && shared_part) ? (slot & 1) : 0;
+  const int sub_last = TERN ? (shared_part ? sub_first + 1 : 2) : 1;
+  const int row0 = a.offs[e];
+  const int n = (TERN && shared_part) ? min(a.offs[e + 1] - row0, cb_first + 16) : a.offs[e + 1] - row0;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int r16 = lane & 15, g = lane >> 4;
-  const int m0 = blockIdx.x * 64 + wv * 16;
   const int d = a.d, I = a.I;
   const bool routed = e < a.E;
 
   if (!TERN || !routed) {
+#pragma unroll 1
+    for (int sub = sub_first; sub < sub_last; ++sub) {
+    const int m0 = blockIdx.x * (TERN ? 128 : 64) + sub * 64 + wv * 16;
     const uint16_t* wd = (routed ? w.down + (size_t)e * d * I : w.s_down) + (size_t)(m0 + r16) * I + kKV * 8 * g;
-    for (int cb = 0; cb < n; cb += 16) {
+    for (int cb = cb_first; cb < n; cb += 16) {
       const bool valid = cb + r16 < n;
       const int col = valid ? row0 + cb + r16 : row0;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -293,31 +345,47 @@ __global__ void __launch_bounds__(256) stream_down_kernel(StreamArgs a, ExpertWe
       if (valid)
         *reinterpret_cast<float4*>(y + (size_t)col * d + m0 + 4 * g) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
+    }
     return;
   }
 
-  // Sherry-ternary routed expert: 16 token columns per pass, scaled per row at the end
+  // Sherry-ternary routed expert: output rows m0 + 16 r + r16 (r < kTernRowBlocks), 16
+  // token columns per pass, scaled per row at the end
+  constexpr int NR = kTernRowBlocks;
+  const int m0 = blockIdx.x * 128 + wv * 16 * NR;
   const int nb = I / 128, wpr = nb * 5;
-  const uint32_t* q[1] = {w.qdown + ((size_t)e * d + m0 + r16) * wpr + ((5 * g) >> 2)};
-  float sd[4];
+  const uint32_t* q[1][NR];
+  float sd[NR][4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) sd[r] = bf16_bits_to_f32(w.sdown[(size_t)e * d + m0 + 4 * g + r]);
+  for (int r = 0; r < NR; ++r) {
+    q[0][r] = w.qdown + ((size_t)e * d + m0 + 16 * r + r16) * wpr + ((5 * g) >> 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sd[r][j] = bf16_bits_to_f32(w.sdown[(size_t)e * d + m0 + 16 * r + 4 * g + j]);
+  }
   for (int cb = 0; cb < n; cb += 16) {
     const bool valid = cb + r16 < n;
     const int col = valid ? row0 + cb + r16 : row0;
-    f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
-    tern_rows_block<1, kTernDepth>(q, h + (size_t)col * I + 32 * g, nb, g, lut, acc);
-    if (valid)
-      *reinterpret_cast<float4*>(y + (size_t)col * d + m0 + 4 * g) =
-          make_float4(acc[0][0] * sd[0], acc[0][1] * sd[1], acc[0][2] * sd[2], acc[0][3] * sd[3]);
+    f32x4 acc[1][NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) acc[0][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    tern_rows_block<1, NR, kTernDepth>(q, h + (size_t)col * I + 32 * g, nb, g, lut, acc);
+    if (valid) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+        *reinterpret_cast<float4*>(y + (size_t)col * d + m0 + 16 * r + 4 * g) =
+            make_float4(acc[0][r][0] * sd[r][0], acc[0][r][1] * sd[r][1], acc[0][r][2] * sd[r][2],
+                        acc[0][r][3] * sd[r][3]);
+    }
   }
 }
 
 hipError_t launch_stream_experts(const Plan& p, const uint16_t* x, const ExpertWeights& w, hipStream_t s,
                                  Marks& m) {
   StreamArgs a{x, p.touched, p.meta, p.offs, p.perm_src, p.Tk, p.k, p.d, p.I, p.E};
-  const int slots = (p.Tk < p.E ? p.Tk : p.E) + 1;
-  dim3 g1(p.I / 64, slots), g2(p.d / 64, slots);
+  const int slots = (p.Tk < p.E ? p.Tk : p.E) + (w.ternary ? ((p.T + 15) / 16) * 2 : 1);
+  // ternary kernels: 128 rows per workgroup (d and I are multiples of 128)
+  const int rows_wg = w.ternary ? 128 : 64;
+  dim3 g1(p.I / rows_wg, slots), g2(p.d / rows_wg, slots);
   if (w.ternary) {
     hipLaunchKernelGGL(stream_gateup_kernel<true>, g1, dim3(256), 0, s, a, w, p.h);
   } else {
