@@ -21,14 +21,17 @@
 // Pipeline, per 64-wide k step: the step's 256 activation rows and 256 weight rows
 // (128 B each: one cache line per row, so the vector L1's limited number of
 // outstanding misses carries twice the bytes of 64-byte pieces) arrive in LDS by
-// direct global->LDS loads into a 2-stage ring of 64 KB stages; 16-byte chunks are
-// XOR-swizzled by row so the MFMA fragment reads are conflict free. Activation rows
-// are gathered from x through the permutation (gate/up) or read from h (down). Only
-// LDS-bound loads are in flight in the k loop, so the vector-memory wait is an
-// explicit count. A step runs 4 MFMA groups (k = 16 each), each group's fragments read
-// while the previous group's MFMAs run; at the end of the step one bare barrier
-// certifies that the next step has landed and that this step's slot is free, which
-// then receives the step after next.
+// direct global->LDS loads into two rings of 32 KB slots: 2 activation slots and BS
+// weight slots (BS = 3 when the step count allows, using all 160 KB: the weights come
+// from HBM and get one more step of lead than the activations, mostly L2 hits). 16-byte
+// chunks are XOR-swizzled by row so the MFMA fragment reads are conflict free.
+// Activation rows are gathered from x through the permutation (gate/up) or read from h
+// (down). Only LDS-bound loads are in flight in the k loop, so the vector-memory wait
+// is an explicit count. A step runs 4 MFMA groups (k = 16 each), each group's
+// fragments read while the previous group's MFMAs run; at the end of the step one bare
+// barrier certifies that the next step has landed and that this step's slots are
+// free, which then receive the activations 2 steps ahead and the weights BS steps
+// ahead (clamped to the last step, so every step issues the same loads).
 // Persistent schedule: items are split into 8 contiguous ranges, one per XCD
 // (workgroup i runs on XCD i mod 8) and claimed in order through per-XCD counters, so
 // workgroups that finish early take more work; within an expert, items are ordered so
@@ -50,10 +53,8 @@ constexpr int kBK = 64;         // k per step (four 32x32x16 MFMAs deep); K % (2
 constexpr int kSub = kBK / 16;  // MFMA groups per step
 constexpr int kRowBytes = kBK * 2;               // 128 B per row per step
 constexpr int kChunks = kRowBytes / 16;          // 8 chunks of 16 B per row
-constexpr int kHalf = kRowsMax * kRowBytes;      // 32 KB: activation or weight part of a stage
-constexpr int kStageBytes = 2 * kHalf;           // 64 KB
+constexpr int kHalf = kRowsMax * kRowBytes;      // 32 KB: one operand's ring slot
 constexpr int kDma = kHalf / 16 / kThreads;      // direct-to-LDS ops per operand per thread per step (8)
-constexpr int kOpsPerStep = 2 * kDma;            // vector-memory ops a thread issues per step (16)
 
 int grouped_gemm_bm() { return kRowsMax; }
 
@@ -93,15 +94,28 @@ __device__ __forceinline__ void bare_barrier() {
 // eight rows read together by one fragment load fall on eight different bank groups.
 __device__ __forceinline__ int swz_key(int row) { return row & 7; }
 
-template <bool GATEUP>
+// Calls f(integral_constant<int, T>) for T in the sequence, in order.
+template <int... T, class F>
+__device__ __forceinline__ void for_seq(std::integer_sequence<int, T...>, F&& f) {
+  (f(std::integral_constant<int, T>{}), ...);
+}
+
+// BS: weight ring slots (2, or 3 when K / kBK is a multiple of 6).
+template <bool GATEUP, int BS>
 __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, ExpertWeights w,
                                                                    uint16_t* __restrict__ h,
                                                                    uint16_t* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) uint8_t st0[kStageBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t st1[kStageBytes];
-  uint8_t* const stage[2] = {st0, st1};
-
-  __shared__ int next_item;
+  static_assert(BS == 2 || BS == 3, "weight ring slots");
+  __shared__ __attribute__((aligned(16))) uint8_t sa0[kHalf];
+  __shared__ __attribute__((aligned(16))) uint8_t sa1[kHalf];
+  __shared__ __attribute__((aligned(16))) uint8_t sb0[kHalf];
+  __shared__ __attribute__((aligned(16))) uint8_t sb1[kHalf];
+  __shared__ __attribute__((aligned(16))) uint8_t sb2[BS == 3 ? kHalf : 16];
+  uint8_t* const sa[2] = {sa0, sa1};
+  uint8_t* const sb[3] = {sb0, sb1, sb2};
+  // the claimed item is handed to the workgroup through the first activation slot,
+  // idle between items
+  int* const next_item = reinterpret_cast<int*>(sa0);
 
   const int K = GATEUP ? a.d : a.I;
   const int NT = GATEUP ? a.I / (kRowsMax / 2) : (a.d + kRowsMax - 1) / kRowsMax;
@@ -133,13 +147,14 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
   uint32_t frag_lo[kSub];
 #pragma unroll
   for (int s = 0; s < kSub; ++s) frag_lo[s] = (uint32_t)(r32 * kRowBytes + (((2 * s + hf) ^ swz_key(r32)) << 4));
-  const uint32_t fa_off = wm * kBlk * kRowBytes;                      // block 2j + wm
-  const uint32_t fb_off = kHalf + wn * (kRowsMax / 2) * kRowBytes;    // columns 128 wn..
+  const uint32_t fa_off = wm * kBlk * kRowBytes;              // block 2j + wm
+  const uint32_t fb_off = wn * (kRowsMax / 2) * kRowBytes;    // columns 128 wn..
 
   for (;;) {
-    if (threadIdx.x == 0) next_item = claim();
+    if (threadIdx.x == 0) *next_item = claim();
     __syncthreads();
-    const int item = next_item;
+    const int item = *next_item;
+    __syncthreads();  // everyone has read it before the slot is loaded
     if (item < 0) break;
     // items of one expert (its c M tiles x NT N tiles) are ordered in blocks of up to
     // 4 M tiles, N tile major within a block, so the workgroups running together on
@@ -189,16 +204,19 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
         bp[i] = mat + (size_t)min(nt * kRowsMax + row, a.d - 1) * a.I + 8 * lc;
       }
     }
-    auto issue = [&](int ks, uint8_t* st) {
+    auto issue_a = [&](int ks, uint8_t* st) {
       const int kk = ks * kBK;
       uint8_t* da = st + (64 * wv) * 16;
 #pragma unroll
       for (int i = 0; i < kDma; ++i)
         __builtin_amdgcn_global_load_lds((const void*)(ap[i] + kk), HY_LDS(da + kThreads * 16 * i), 16, 0, 0);
+    };
+    auto issue_b = [&](int ks, uint8_t* st) {
+      const int kk = ks * kBK;
+      uint8_t* db = st + (64 * wv) * 16;
 #pragma unroll
       for (int i = 0; i < kDma; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(bp[i] + kk), HY_LDS(da + kHalf + kThreads * 16 * i), 16, 0,
-                                         0);
+        __builtin_amdgcn_global_load_lds((const void*)(bp[i] + kk), HY_LDS(db + kThreads * 16 * i), 16, 0, 0);
     };
 
     f32x16 acc[kWaveBlocks][kNB];
@@ -209,10 +227,14 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[j][nb][i] = 0.f;
 
-    // prologue: steps 0 and 1 in flight (K >= 128), step 0 landed everywhere
-    issue(0, st0);
-    issue(1, st1);
-    wait_vm<kOpsPerStep>();
+    // prologue: activations of steps 0, 1 and weights of steps 0 .. BS-1 in flight
+    // (K >= 128 gives 2 steps; BS = 3 only with 6 or more), step 0 landed everywhere
+    issue_a(0, sa0);
+    issue_b(0, sb0);
+    issue_a(1, sa1);
+    issue_b(1, sb1);
+    if constexpr (BS == 3) issue_b(2, sb2);
+    wait_vm<(BS == 3 ? 3 : 2) * kDma>();
     bare_barrier();
 
     // the k loop, with this wave's number of active row blocks fixed at compile time
@@ -223,14 +245,14 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
       // The previous group's reads are waited for (long done: a whole MFMA group ran
       // since) before this group's are issued, so at most 8 are in flight and the
       // MFMAs that follow need no wait.
-      auto read_frags = [&](const uint8_t* L, int s) {
+      auto read_frags = [&](const uint8_t* La, const uint8_t* Lb, int s) {
         wait_lds();
 #pragma unroll
         for (int j = 0; j < NACT; ++j)
-          fa[s & 1][j] = *reinterpret_cast<const uint4*>(L + fa_off + j * 2 * kBlk * kRowBytes + frag_lo[s]);
+          fa[s & 1][j] = *reinterpret_cast<const uint4*>(La + fa_off + j * 2 * kBlk * kRowBytes + frag_lo[s]);
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb)
-          fb[s & 1][nb] = *reinterpret_cast<const uint4*>(L + fb_off + nb * kBlk * kRowBytes + frag_lo[s]);
+          fb[s & 1][nb] = *reinterpret_cast<const uint4*>(Lb + fb_off + nb * kBlk * kRowBytes + frag_lo[s]);
       };
       auto mfmas = [&](int s) {
 #pragma unroll
@@ -238,45 +260,49 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
 #pragma unroll
           for (int nb = 0; nb < kNB; ++nb) acc[j][nb] = mfma32x32x16(fa[s & 1][j], fb[s & 1][nb], acc[j][nb]);
       };
-      // One step on ring slot U. ISSUE: load the step after next into this slot once
-      // it is free; NEXT: there is a next step. sched_barrier(0) keeps each group in
-      // place: the fragment reads stay ahead of the MFMAs that run while they are in
-      // flight.
-      auto step = [&](auto u_tag, auto issue_tag, auto next_tag, int ks) {
-        constexpr int U = decltype(u_tag)::value;
-        constexpr bool ISSUE = decltype(issue_tag)::value;
+      // One step ks on activation slot UA = ks % 2 and weight slot UB = ks % BS; NEXT:
+      // there is a next step. sched_barrier(0) keeps each group in place: the fragment
+      // reads stay ahead of the MFMAs that run while they are in flight.
+      auto step = [&](auto ua_tag, auto ub_tag, auto next_tag, int ks) {
+        constexpr int UA = decltype(ua_tag)::value;
+        constexpr int UB = decltype(ub_tag)::value;
         constexpr bool NEXT = decltype(next_tag)::value;
 #pragma unroll
         for (int s = 1; s < kSub; ++s) {
-          read_frags(stage[U], s);
+          read_frags(sa[UA], sb[UB], s);
           __builtin_amdgcn_sched_barrier(0);
           mfmas(s - 1);
           __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (NEXT) {
-          wait_vm<0>();   // own loads of step ks+1 landed
-          wait_lds();     // own reads of this step done
-          bare_barrier(); // everyone's step ks+1 landed; this step's slot is free
-          if constexpr (ISSUE) issue(ks + 2, stage[U]);
-          read_frags(stage[U ^ 1], 0);
+          // own activations and weights of step ks+1 landed: issued at the end of step
+          // ks-1 (activations, the newest op group but one with BS = 3) and ks+1-BS
+          wait_vm<BS == 3 ? kDma : 0>();
+          wait_lds();      // own reads of this step done
+          bare_barrier();  // everyone's step ks+1 landed; this step's slots are free
+          issue_a(min(ks + 2, nks - 1), sa[UA]);
+          issue_b(min(ks + BS, nks - 1), sb[UB]);
+          read_frags(sa[UA ^ 1], sb[(UB + 1) % BS], 0);
         }
         __builtin_amdgcn_sched_barrier(0);
         mfmas(kSub - 1);
         __builtin_amdgcn_sched_barrier(0);
       };
-      using I0 = std::integral_constant<int, 0>;
-      using I1 = std::integral_constant<int, 1>;
-      using T_ = std::true_type;
-      using F_ = std::false_type;
-      read_frags(stage[0], 0);
+      // whole periods of P steps (slots repeat with period P; nks is a multiple of P)
+      constexpr int P = BS == 3 ? 6 : 2;
+      read_frags(sa[0], sb[0], 0);
       int k0 = 0;
-      for (; k0 + 3 < nks; k0 += 2) {
-        step(I0{}, T_{}, T_{}, k0);
-        step(I1{}, T_{}, T_{}, k0 + 1);
-      }
-      // last two steps (nks is even): nothing new to load
-      step(I0{}, F_{}, T_{}, k0);
-      step(I1{}, F_{}, F_{}, k0 + 1);
+      for (; k0 + P < nks; k0 += P)
+        for_seq(std::make_integer_sequence<int, P>{}, [&](auto t) {
+          constexpr int T = decltype(t)::value;
+          step(std::integral_constant<int, T % 2>{}, std::integral_constant<int, T % BS>{}, std::true_type{},
+               k0 + T);
+        });
+      for_seq(std::make_integer_sequence<int, P>{}, [&](auto t) {
+        constexpr int T = decltype(t)::value;
+        step(std::integral_constant<int, T % 2>{}, std::integral_constant<int, T % BS>{},
+             std::integral_constant<bool, (T + 1 < P)>{}, k0 + T);
+      });
     };
     const int nact = min(kWaveBlocks, max(0, (nrb - wm + 1) >> 1));
     if (nact == 4)
@@ -294,7 +320,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
     bare_barrier();
 
     // Epilogue through LDS: the tile is written as 256-row x 64-column bf16 pieces of
-    // 32 KB (half a ring stage each; 128 B per row; 16-byte chunk c of row r sits at
+    // 32 KB (one ring slot each: sa0, sa1, sb0, sb1; 128 B per row; 16-byte chunk c of row r sits at
     // c ^ 4*bit2(r), so the two lane halves of a write, 4 rows apart, hit different
     // banks), then leaves with 16-byte stores of whole row segments. gate/up: piece wn
     // holds h units nt*128 + 64 wn + [0, 64); down: piece 2 wn + nb/2 holds y columns
@@ -312,8 +338,8 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
           const float v = GATEUP ? silu(acc[j][nb][i]) * acc[j][nb + kNB / 2][i] : acc[j][nb][i];
           const int piece = GATEUP ? wn : 2 * wn + (nb >> 1);
           const int pcol = GATEUP ? nb * 32 + r32 : (nb & 1) * 32 + r32;
-          const uint32_t off = (piece & 1) * kHalf + row * 128 + ((((pcol >> 3) ^ (4 * hf)) << 4) | ((pcol & 7) * 2));
-          uint8_t* const pb = (piece >> 1) == 0 ? st0 : st1;
+          const uint32_t off = row * 128 + ((((pcol >> 3) ^ (4 * hf)) << 4) | ((pcol & 7) * 2));
+          uint8_t* const pb = piece == 0 ? sa0 : piece == 1 ? sa1 : piece == 2 ? sb0 : sb1;
           *reinterpret_cast<__bf16*>(pb + off) = (__bf16)v;
         }
       }
@@ -324,7 +350,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
     for (int pc = 0; pc < (GATEUP ? 2 : 4); ++pc) {
       const int col0 = GATEUP ? nt * (kRowsMax / 2) + 64 * pc : nt * kRowsMax + 64 * pc;
       if (!GATEUP && col0 >= a.d) continue;  // d is a multiple of 128: whole pieces fall outside
-      const uint8_t* pbase = stage[pc >> 1] + (pc & 1) * kHalf;
+      const uint8_t* pbase = pc == 0 ? sa0 : pc == 1 ? sa1 : pc == 2 ? sb0 : sb1;
 #pragma unroll
       for (int it = 0; it < kRowsMax / 32; ++it) {
         const int row = it * 32 + (threadIdx.x >> 3), ch = threadIdx.x & 7;
@@ -342,7 +368,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
   }
 }
 
-static int g_grid[2][64];  // persistent grid per (phase, device), 0 = not yet computed
+static int g_grid[4][64];  // persistent grid per (kernel variant, device), 0 = not yet computed
 
 static int persistent_grid(int phase, const void* kernel) {
   int dev = 0;
@@ -360,13 +386,25 @@ static int persistent_grid(int phase, const void* kernel) {
 hipError_t launch_grouped_experts(const Plan& p, const uint16_t* x, const ExpertWeights& w, hipStream_t s,
                                   Marks& m) {
   GemmArgs a{x, p.perm_src, p.offs, p.meta, p.tiles, p.Tk, p.k, p.d, p.I, p.E};
-  const int g1 = persistent_grid(0, reinterpret_cast<const void*>(&grouped_gemm_kernel<true>));
-  hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3(g1), dim3(kThreads), 0, s, a, w, p.h, (uint16_t*)p.y);
+  // a 3-slot weight ring needs the step count (K / kBK) to be a multiple of 6
+  const bool deep1 = (p.d / kBK) % 6 == 0, deep2 = (p.I / kBK) % 6 == 0;
+  const void* k1 = deep1 ? reinterpret_cast<const void*>(&grouped_gemm_kernel<true, 3>)
+                         : reinterpret_cast<const void*>(&grouped_gemm_kernel<true, 2>);
+  const void* k2 = deep2 ? reinterpret_cast<const void*>(&grouped_gemm_kernel<false, 3>)
+                         : reinterpret_cast<const void*>(&grouped_gemm_kernel<false, 2>);
+  const int g1 = persistent_grid(deep1 ? 2 : 0, k1);
+  if (deep1)
+    hipLaunchKernelGGL((grouped_gemm_kernel<true, 3>), dim3(g1), dim3(kThreads), 0, s, a, w, p.h, (uint16_t*)p.y);
+  else
+    hipLaunchKernelGGL((grouped_gemm_kernel<true, 2>), dim3(g1), dim3(kThreads), 0, s, a, w, p.h, (uint16_t*)p.y);
   hipError_t err = hipGetLastError();
   if (err == hipSuccess) err = m.mark(s);
   if (err != hipSuccess) return err;
-  const int g2 = persistent_grid(1, reinterpret_cast<const void*>(&grouped_gemm_kernel<false>));
-  hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3(g2), dim3(kThreads), 0, s, a, w, p.h, (uint16_t*)p.y);
+  const int g2 = persistent_grid(deep2 ? 3 : 1, k2);
+  if (deep2)
+    hipLaunchKernelGGL((grouped_gemm_kernel<false, 3>), dim3(g2), dim3(kThreads), 0, s, a, w, p.h, (uint16_t*)p.y);
+  else
+    hipLaunchKernelGGL((grouped_gemm_kernel<false, 2>), dim3(g2), dim3(kThreads), 0, s, a, w, p.h, (uint16_t*)p.y);
   err = hipGetLastError();
   return err == hipSuccess ? m.mark(s) : err;
 }
