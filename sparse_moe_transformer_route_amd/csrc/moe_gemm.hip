@@ -21,9 +21,9 @@
 // Pipeline, per 64-wide k step: the step's 256 activation rows and 256 weight rows
 // (128 B each: one cache line per row, so the vector L1's limited number of
 // outstanding misses carries twice the bytes of 64-byte pieces) arrive in LDS by
-// direct global->LDS loads into two rings of 32 KB slots: 2 activation slots and BS
-// weight slots (BS = 3 when the step count allows, using all 160 KB: the weights come
-// from HBM and get one more step of lead than the activations, mostly L2 hits). 16-byte
+// direct global->LDS loads into two rings of 32 KB slots: 2 activation slots and 3
+// weight slots (all 160 KB: the weights come from HBM and get one more step of lead
+// than the activations, mostly L2 hits). 16-byte
 // chunks are XOR-swizzled by row so the MFMA fragment reads are conflict free.
 // Activation rows are gathered from x through the permutation (gate/up) or read from h
 // (down). Only LDS-bound loads are in flight in the k loop, so the vector-memory wait
@@ -100,17 +100,18 @@ __device__ __forceinline__ void for_seq(std::integer_sequence<int, T...>, F&& f)
   (f(std::integral_constant<int, T>{}), ...);
 }
 
-// BS: weight ring slots (2, or 3 when K / kBK is a multiple of 6).
-template <bool GATEUP, int BS>
+// TAILR = (K / kBK) mod 6 (0, 2 or 4: K is a multiple of 128): the k loop runs whole
+// periods of the 2 x 3 slot pattern and ends with a tail of that many steps.
+template <bool GATEUP, int TAILR>
 __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, ExpertWeights w,
                                                                    uint16_t* __restrict__ h,
                                                                    uint16_t* __restrict__ y) {
-  static_assert(BS == 2 || BS == 3, "weight ring slots");
+  constexpr int BS = 3;  // weight ring slots
   __shared__ __attribute__((aligned(16))) uint8_t sa0[kHalf];
   __shared__ __attribute__((aligned(16))) uint8_t sa1[kHalf];
   __shared__ __attribute__((aligned(16))) uint8_t sb0[kHalf];
   __shared__ __attribute__((aligned(16))) uint8_t sb1[kHalf];
-  __shared__ __attribute__((aligned(16))) uint8_t sb2[BS == 3 ? kHalf : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sb2[kHalf];
   uint8_t* const sa[2] = {sa0, sa1};
   uint8_t* const sb[3] = {sb0, sb1, sb2};
   // the claimed item is handed to the workgroup through the first activation slot,
@@ -228,13 +229,13 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
         for (int i = 0; i < 16; ++i) acc[j][nb][i] = 0.f;
 
     // prologue: activations of steps 0, 1 and weights of steps 0 .. BS-1 in flight
-    // (K >= 128 gives 2 steps; BS = 3 only with 6 or more), step 0 landed everywhere
+    // (K >= 128 gives at least 2 steps; later ones clamp), step 0 landed everywhere
     issue_a(0, sa0);
     issue_b(0, sb0);
     issue_a(1, sa1);
     issue_b(1, sb1);
-    if constexpr (BS == 3) issue_b(2, sb2);
-    wait_vm<(BS == 3 ? 3 : 2) * kDma>();
+    issue_b(min(2, nks - 1), sb2);
+    wait_vm<3 * kDma>();
     bare_barrier();
 
     // the k loop, with this wave's number of active row blocks fixed at compile time
@@ -276,8 +277,8 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
         }
         if constexpr (NEXT) {
           // own activations and weights of step ks+1 landed: issued at the end of step
-          // ks-1 (activations, the newest op group but one with BS = 3) and ks+1-BS
-          wait_vm<BS == 3 ? kDma : 0>();
+          // ks-1 (activations, the newest op group but one) and ks-2 (weights)
+          wait_vm<kDma>();
           wait_lds();      // own reads of this step done
           bare_barrier();  // everyone's step ks+1 landed; this step's slots are free
           issue_a(min(ks + 2, nks - 1), sa[UA]);
@@ -288,20 +289,22 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
         mfmas(kSub - 1);
         __builtin_amdgcn_sched_barrier(0);
       };
-      // whole periods of P steps (slots repeat with period P; nks is a multiple of P)
-      constexpr int P = BS == 3 ? 6 : 2;
+      // whole periods of P = 6 steps (slots repeat with period 6), then the last R steps
+      // (R = TAILR, or 6 when TAILR is 0), all with compile-time slots
+      constexpr int P = 6;
+      constexpr int R = TAILR == 0 ? P : TAILR;
       read_frags(sa[0], sb[0], 0);
       int k0 = 0;
-      for (; k0 + P < nks; k0 += P)
+      for (; k0 + R < nks; k0 += P)
         for_seq(std::make_integer_sequence<int, P>{}, [&](auto t) {
           constexpr int T = decltype(t)::value;
-          step(std::integral_constant<int, T % 2>{}, std::integral_constant<int, T % BS>{}, std::true_type{},
+          step(std::integral_constant<int, T % 2>{}, std::integral_constant<int, T % 3>{}, std::true_type{},
                k0 + T);
         });
-      for_seq(std::make_integer_sequence<int, P>{}, [&](auto t) {
+      for_seq(std::make_integer_sequence<int, R>{}, [&](auto t) {
         constexpr int T = decltype(t)::value;
-        step(std::integral_constant<int, T % 2>{}, std::integral_constant<int, T % BS>{},
-             std::integral_constant<bool, (T + 1 < P)>{}, k0 + T);
+        step(std::integral_constant<int, T % 2>{}, std::integral_constant<int, T % 3>{},
+             std::integral_constant<bool, (T + 1 < R)>{}, k0 + T);
       });
     };
     const int nact = min(kWaveBlocks, max(0, (nrb - wm + 1) >> 1));
@@ -368,7 +371,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
   }
 }
 
-static int g_grid[4][64];  // persistent grid per (kernel variant, device), 0 = not yet computed
+static int g_grid[2][64];  // persistent grid per (phase, device), 0 = not yet computed
 
 static int persistent_grid(int phase, const void* kernel) {
   int dev = 0;
@@ -386,25 +389,21 @@ static int persistent_grid(int phase, const void* kernel) {
 hipError_t launch_grouped_experts(const Plan& p, const uint16_t* x, const ExpertWeights& w, hipStream_t s,
                                   Marks& m) {
   GemmArgs a{x, p.perm_src, p.offs, p.meta, p.tiles, p.Tk, p.k, p.d, p.I, p.E};
-  // a 3-slot weight ring needs the step count (K / kBK) to be a multiple of 6
-  const bool deep1 = (p.d / kBK) % 6 == 0, deep2 = (p.I / kBK) % 6 == 0;
-  const void* k1 = deep1 ? reinterpret_cast<const void*>(&grouped_gemm_kernel<true, 3>)
-                         : reinterpret_cast<const void*>(&grouped_gemm_kernel<true, 2>);
-  const void* k2 = deep2 ? reinterpret_cast<const void*>(&grouped_gemm_kernel<false, 3>)
-                         : reinterpret_cast<const void*>(&grouped_gemm_kernel<false, 2>);
-  const int g1 = persistent_grid(deep1 ? 2 : 0, k1);
-  if (deep1)
-    hipLaunchKernelGGL((grouped_gemm_kernel<true, 3>), dim3(g1), dim3(kThreads), 0, s, a, w, p.h, (uint16_t*)p.y);
-  else
-    hipLaunchKernelGGL((grouped_gemm_kernel<true, 2>), dim3(g1), dim3(kThreads), 0, s, a, w, p.h, (uint16_t*)p.y);
+  using Kern = void (*)(GemmArgs, ExpertWeights, uint16_t*, uint16_t*);
+  // indexed by (K / kBK) mod 6 / 2
+  static const Kern k_gateup[3] = {grouped_gemm_kernel<true, 0>, grouped_gemm_kernel<true, 2>,
+                                   grouped_gemm_kernel<true, 4>};
+  static const Kern k_down[3] = {grouped_gemm_kernel<false, 0>, grouped_gemm_kernel<false, 2>,
+                                 grouped_gemm_kernel<false, 4>};
+  const Kern k1 = k_gateup[(p.d / kBK) % 6 / 2];
+  const Kern k2 = k_down[(p.I / kBK) % 6 / 2];
+  const int g1 = persistent_grid(0, reinterpret_cast<const void*>(k1));
+  hipLaunchKernelGGL(k1, dim3(g1), dim3(kThreads), 0, s, a, w, p.h, (uint16_t*)p.y);
   hipError_t err = hipGetLastError();
   if (err == hipSuccess) err = m.mark(s);
   if (err != hipSuccess) return err;
-  const int g2 = persistent_grid(deep2 ? 3 : 1, k2);
-  if (deep2)
-    hipLaunchKernelGGL((grouped_gemm_kernel<false, 3>), dim3(g2), dim3(kThreads), 0, s, a, w, p.h, (uint16_t*)p.y);
-  else
-    hipLaunchKernelGGL((grouped_gemm_kernel<false, 2>), dim3(g2), dim3(kThreads), 0, s, a, w, p.h, (uint16_t*)p.y);
+  const int g2 = persistent_grid(1, reinterpret_cast<const void*>(k2));
+  hipLaunchKernelGGL(k2, dim3(g2), dim3(kThreads), 0, s, a, w, p.h, (uint16_t*)p.y);
   err = hipGetLastError();
   return err == hipSuccess ? m.mark(s) : err;
 }
