@@ -151,8 +151,12 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
   const uint32_t fa_off = wm * kBlk * kRowBytes;              // block 2j + wm
   const uint32_t fb_off = wn * (kRowsMax / 2) * kRowBytes;    // columns 128 wn..
 
+  // thread 0 claims each item one item ahead (the atomic's latency hides behind the
+  // current item's k loop) and hands it over through LDS between items
+  int claimed = 0;
+  if (threadIdx.x == 0) claimed = claim();
   for (;;) {
-    if (threadIdx.x == 0) *next_item = claim();
+    if (threadIdx.x == 0) *next_item = claimed;
     __syncthreads();
     const int item = *next_item;
     __syncthreads();  // everyone has read it before the slot is loaded
@@ -235,7 +239,8 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
     issue_a(1, sa1);
     issue_b(1, sb1);
     issue_b(min(2, nks - 1), sb2);
-    wait_vm<3 * kDma>();
+    if (threadIdx.x == 0) claimed = claim();
+    wait_vm<3 * kDma>();  // (an outstanding claim is older than the loads: counted in)
     bare_barrier();
 
     // the k loop, with this wave's number of active row blocks fixed at compile time
