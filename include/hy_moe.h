@@ -34,6 +34,9 @@
  *    bitwise-identical outputs (no floating-point atomics anywhere).
  *  - Supported envelope: 1 <= k <= min(E, 16), E <= 1024, d % 128 == 0,
  *    I % 128 == 0, T * k < 2^31. T == 0 is a no-op returning HY_MOE_OK.
+ *    HY_MOE_PATH_GROUPED further needs T * d * 2 and T * (k + 1) * I * 2 (the bytes
+ *    of x and of the hidden activations) below 2^32; HY_MOE_PATH_AUTO takes the
+ *    streaming path where they are not.
  */
 #ifndef HY_MOE_H
 #define HY_MOE_H

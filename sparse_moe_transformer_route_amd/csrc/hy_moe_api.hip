@@ -51,6 +51,12 @@ Layout make_layout(int64_t T, int64_t d, int64_t E, int64_t k, int64_t I) {
   return L;
 }
 
+// The grouped GEMM addresses x and h with 32-bit byte offsets from their bases.
+bool grouped_fits(int64_t T, int64_t d, int64_t k, int64_t I) {
+  const int64_t lim = (int64_t)1 << 32;
+  return T * d * 2 < lim && T * (k + 1) * I * 2 < lim;
+}
+
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 int check_shape(int64_t T, int64_t d, int64_t E, int64_t k, int64_t I) {
@@ -86,6 +92,7 @@ int check_args(const hy_moe_args* a) {
       if (!p || !aligned(p, 4)) return HY_MOE_ERR_INVALID_ARG;
     if (a->path == HY_MOE_PATH_GROUPED) return HY_MOE_ERR_UNSUPPORTED;
   }
+  if (a->path == HY_MOE_PATH_GROUPED && !grouped_fits(a->T, a->d, a->k, a->I)) return HY_MOE_ERR_UNSUPPORTED;
   const void* opt4[] = {a->topk_idx, a->topk_w, a->counts, a->offsets, a->perm_src, a->margin};
   for (const void* p : opt4)
     if (p && !aligned(p, 4)) return HY_MOE_ERR_INVALID_ARG;
@@ -157,7 +164,7 @@ extern "C" int hy_moe_forward_ex(const hy_moe_args* a, void* stream) {
   else if (a->path == HY_MOE_PATH_GROUPED)
     stream_path = false;
   else
-    stream_path = w.ternary || (int64_t)p.Tk <= 16 * (int64_t)p.E;
+    stream_path = w.ternary || (int64_t)p.Tk <= 16 * (int64_t)p.E || !grouped_fits(p.T, p.d, p.k, p.I);
 
   const uint16_t* x = (const uint16_t*)a->x;
   Marks marks{a->stage_events, 0};

@@ -137,17 +137,9 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
     }
     return -1;
   };
-  const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, kept scalar
   const int wm = wv & 1, wn = wv >> 1;
-  const int r32 = lane & 31, hf = lane >> 5;
   const int nks = K / kBK;
-  // per-lane part of a fragment read for k group s: row r32 of a 32-row block, chunk
-  // 2s + hf (lane half hf holds k [8(2s+hf), 8(2s+hf)+8) of the step), swizzled; the key
-  // depends only on r32 because blocks start at multiples of 32
-  uint32_t frag_lo[kSub];
-#pragma unroll
-  for (int s = 0; s < kSub; ++s) frag_lo[s] = (uint32_t)(r32 * kRowBytes + (((2 * s + hf) ^ swz_key(r32)) << 4));
   const uint32_t fa_off = wm * kBlk * kRowBytes;              // block 2j + wm
   const uint32_t fb_off = wn * (kRowsMax / 2) * kRowBytes;    // columns 128 wn..
 
@@ -158,9 +150,22 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
   for (;;) {
     if (threadIdx.x == 0) *next_item = claimed;
     __syncthreads();
-    const int item = *next_item;
+    const int item = __builtin_amdgcn_readfirstlane(*next_item);  // uniform: kept scalar
     __syncthreads();  // everyone has read it before the slot is loaded
     if (item < 0) break;
+    // The thread index is made opaque once per item so that per-lane address math is
+    // redone per item (a few ALU ops) rather than hoisted out of the item loop, where it
+    // would be spilled across the k loop and reloaded with full vector-memory waits.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int r32 = lane & 31, hf = lane >> 5;
+    // per-lane part of a fragment read for k group s: row r32 of a 32-row block, chunk
+    // 2s + hf (lane half hf holds k [8(2s+hf), 8(2s+hf)+8) of the step), swizzled; the key
+    // depends only on r32 because blocks start at multiples of 32
+    uint32_t frag_lo[kSub];
+#pragma unroll
+    for (int s = 0; s < kSub; ++s) frag_lo[s] = (uint32_t)(r32 * kRowBytes + (((2 * s + hf) ^ swz_key(r32)) << 4));
     // items of one expert (its c M tiles x NT N tiles) are ordered in blocks of up to
     // 4 M tiles, N tile major within a block, so the workgroups running together on
     // an XCD share both the activation rows and the weight tiles through its L2
@@ -190,23 +195,28 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
     // units nt*128 + 64 (q / 2) + [0, 64), so wave (., wn) holds gate and up of the
     // same 64 units; down rows are output columns nt*256 + row, clamped past d (not
     // stored).
-    const uint16_t* ap[kDma];
-    const uint16_t* bp[kDma];
+    // Addresses are a workgroup-uniform base (scalar registers) plus a 32-bit byte offset
+    // per lane (the grouped path requires x, h and every expert matrix under 4 GiB).
+    const char* const abase = reinterpret_cast<const char*>(GATEUP ? a.x : h);
+    uint32_t aoff[kDma], boff[kDma];
+    const char* bbase[kDma];
 #pragma unroll
     for (int i = 0; i < kDma; ++i) {
       const int q = kThreads * i + 64 * wv + lane;
       const int row = q >> 3, lc = (q & 7) ^ swz_key(row);
       const int grow = ebase + m0 + min(row, mrows - 1);
       if (GATEUP) {
-        ap[i] = a.x + (size_t)row_token(grow, a.perm_src, a.Tk, a.k) * a.d + 8 * lc;
+        aoff[i] = ((uint32_t)row_token(grow, a.perm_src, a.Tk, a.k) * (uint32_t)a.d + 8 * lc) * 2u;
         const int qq = i >> 1;  // 64-row quarter of the tile
         const uint16_t* mat = (qq & 1) == 0 ? (routed ? w.gate + (size_t)e * a.I * a.d : w.s_gate)
                                             : (routed ? w.up + (size_t)e * a.I * a.d : w.s_up);
-        bp[i] = mat + (size_t)(nt * (kRowsMax / 2) + 64 * (qq >> 1) + (row & 63)) * a.d + 8 * lc;
+        bbase[i] = reinterpret_cast<const char*>(mat + (size_t)(nt * (kRowsMax / 2) + 64 * (qq >> 1)) * a.d);
+        boff[i] = ((uint32_t)(row & 63) * (uint32_t)a.d + 8 * lc) * 2u;
       } else {
-        ap[i] = h + (size_t)grow * a.I + 8 * lc;
+        aoff[i] = ((uint32_t)grow * (uint32_t)a.I + 8 * lc) * 2u;
         const uint16_t* mat = routed ? w.down + (size_t)e * a.d * a.I : w.s_down;
-        bp[i] = mat + (size_t)min(nt * kRowsMax + row, a.d - 1) * a.I + 8 * lc;
+        bbase[i] = reinterpret_cast<const char*>(mat + (size_t)nt * kRowsMax * a.I);
+        boff[i] = ((uint32_t)(min(nt * kRowsMax + row, a.d - 1) - nt * kRowsMax) * (uint32_t)a.I + 8 * lc) * 2u;
       }
     }
     auto issue_a = [&](int ks, uint8_t* st) {
@@ -214,14 +224,16 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
       uint8_t* da = st + (64 * wv) * 16;
 #pragma unroll
       for (int i = 0; i < kDma; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(ap[i] + kk), HY_LDS(da + kThreads * 16 * i), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(abase + aoff[i] + 2 * kk), HY_LDS(da + kThreads * 16 * i), 16, 0,
+                                         0);
     };
     auto issue_b = [&](int ks, uint8_t* st) {
       const int kk = ks * kBK;
       uint8_t* db = st + (64 * wv) * 16;
 #pragma unroll
       for (int i = 0; i < kDma; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(bp[i] + kk), HY_LDS(db + kThreads * 16 * i), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(bbase[i] + boff[i] + 2 * kk), HY_LDS(db + kThreads * 16 * i), 16,
+                                         0, 0);
     };
 
     f32x16 acc[kWaveBlocks][kNB];
@@ -354,21 +366,24 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
     }
     wait_lds();
     bare_barrier();
+    // A piece's 8 row groups are read from LDS first, then stored, so no store waits on
+    // another.
+    const int ldc = GATEUP ? a.I : a.d;
+    const int orow = tid >> 3, ch = tid & 7;
+    const uint32_t pl_off = (uint32_t)(orow * 128 + ((ch ^ (4 * ((orow >> 2) & 1))) << 4));
+    uint16_t* const obase = (GATEUP ? h : y) + (size_t)(ebase + m0 + orow) * ldc + ch * 8;
 #pragma unroll
     for (int pc = 0; pc < (GATEUP ? 2 : 4); ++pc) {
       const int col0 = GATEUP ? nt * (kRowsMax / 2) + 64 * pc : nt * kRowsMax + 64 * pc;
       if (!GATEUP && col0 >= a.d) continue;  // d is a multiple of 128: whole pieces fall outside
       const uint8_t* pbase = pc == 0 ? sa0 : pc == 1 ? sa1 : pc == 2 ? sb0 : sb1;
+      uint4 v[kRowsMax / 32];
 #pragma unroll
-      for (int it = 0; it < kRowsMax / 32; ++it) {
-        const int row = it * 32 + (threadIdx.x >> 3), ch = threadIdx.x & 7;
-        if (row < mrows) {
-          const uint4 v = *reinterpret_cast<const uint4*>(pbase + row * 128 + ((ch ^ (4 * ((row >> 2) & 1))) << 4));
-          const size_t grow = (size_t)(ebase + m0 + row);
-          uint16_t* dst = GATEUP ? h + grow * a.I + col0 + ch * 8 : y + grow * a.d + col0 + ch * 8;
-          *reinterpret_cast<uint4*>(dst) = v;
-        }
-      }
+      for (int it = 0; it < kRowsMax / 32; ++it)  // row it*32 + orow: same swizzle bit as orow
+        v[it] = *reinterpret_cast<const uint4*>(pbase + pl_off + it * 32 * 128);
+#pragma unroll
+      for (int it = 0; it < kRowsMax / 32; ++it)
+        if (it * 32 + orow < mrows) *reinterpret_cast<uint4*>(obase + (size_t)it * 32 * ldc + col0) = v[it];
     }
     // every thread has read its pieces before the next item's loads overwrite them
     wait_lds();

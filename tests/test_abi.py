@@ -87,6 +87,16 @@ def test_envelope_limits():
     assert hm.lib().hy_moe_forward_ex(None, None) == hm.ERR_INVALID_ARG
 
 
+def test_grouped_path_byte_limit():
+    # the grouped GEMM addresses x and the hidden activations with 32-bit byte offsets
+    a = base_args(T=2 ** 18, d=8192, E=64, k=8, I=128)  # x: 2^32 bytes
+    a.path = hm.PATH_GROUPED
+    assert call(a) == hm.ERR_UNSUPPORTED
+    a = base_args(T=2 ** 18, d=128, E=64, k=7, I=2048)  # h: 8 * 2^18 rows * 4 KiB = 2^33 bytes
+    a.path = hm.PATH_GROUPED
+    assert call(a) == hm.ERR_UNSUPPORTED
+
+
 def test_ternary_requires_codes_and_scales():
     a = base_args()
     a.expert_format = hm.WEIGHTS_SHERRY_TERNARY
