@@ -127,8 +127,9 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
   // Items are split into 8 contiguous ranges, one per XCD; a workgroup takes the next
   // item of its own XCD's range (so the items in flight on an XCD are neighbours), and
   // once that range is used up, the next unclaimed item of another XCD's range.
-  auto claim = [&]() -> int {
-    for (int t = 0; t < 8; ++t) {
+  // steal: the next unclaimed item of the other XCDs' ranges, or -1
+  auto steal = [&]() -> int {
+    for (int t = 1; t < 8; ++t) {
       const int x = (xcd + t) & 7;
       const int lo = x * per, hi = min(total, lo + per);
       if (lo >= hi) continue;
@@ -137,16 +138,22 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
     }
     return -1;
   };
+  // v: the value an atomic increment of this XCD's own counter returned
+  auto own_or_steal = [&](int v) -> int {
+    const int lo = xcd * per, hi = min(total, lo + per);
+    return lo + v < hi ? lo + v : steal();
+  };
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, kept scalar
   const int wm = wv & 1, wn = wv >> 1;
   const int nks = K / kBK;
   const uint32_t fa_off = wm * kBlk * kRowBytes;              // block 2j + wm
   const uint32_t fb_off = wn * (kRowsMax / 2) * kRowBytes;    // columns 128 wn..
 
-  // thread 0 claims each item one item ahead (the atomic's latency hides behind the
-  // current item's k loop) and hands it over through LDS between items
-  int claimed = 0;
-  if (threadIdx.x == 0) claimed = claim();
+  // Thread 0 claims each item during the previous item's last k step (the atomic's
+  // latency hides behind that step's MFMAs; its result is read after the k loop) and
+  // hands it over through LDS between items.
+  int claimed = 0, own_ticket = 0;
+  if (threadIdx.x == 0) claimed = own_or_steal(atomicAdd(&counters[xcd], 1));
   for (;;) {
     if (threadIdx.x == 0) *next_item = claimed;
     __syncthreads();
@@ -200,13 +207,28 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
     const char* const abase = reinterpret_cast<const char*>(GATEUP ? a.x : h);
     uint32_t aoff[kDma], boff[kDma];
     const char* bbase[kDma];
+    // gate/up: the token of each loaded row (rows past Tk are the shared expert's, in
+    // token order); the permutation entries are all loaded before any is used
+    uint32_t src[kDma];
+    if (GATEUP) {
+#pragma unroll
+      for (int i = 0; i < kDma; ++i) {
+        const int grow = ebase + m0 + min((kThreads * i + 64 * wv + lane) >> 3, mrows - 1);
+        src[i] = (uint32_t)a.perm_src[min(grow, a.Tk - 1)];
+      }
+#pragma unroll
+      for (int i = 0; i < kDma; ++i) {
+        const int grow = ebase + m0 + min((kThreads * i + 64 * wv + lane) >> 3, mrows - 1);
+        src[i] = grow < a.Tk ? src[i] / (uint32_t)a.k : (uint32_t)(grow - a.Tk);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < kDma; ++i) {
       const int q = kThreads * i + 64 * wv + lane;
       const int row = q >> 3, lc = (q & 7) ^ swz_key(row);
       const int grow = ebase + m0 + min(row, mrows - 1);
       if (GATEUP) {
-        aoff[i] = ((uint32_t)row_token(grow, a.perm_src, a.Tk, a.k) * (uint32_t)a.d + 8 * lc) * 2u;
+        aoff[i] = (src[i] * (uint32_t)a.d + 8 * lc) * 2u;
         const int qq = i >> 1;  // 64-row quarter of the tile
         const uint16_t* mat = (qq & 1) == 0 ? (routed ? w.gate + (size_t)e * a.I * a.d : w.s_gate)
                                             : (routed ? w.up + (size_t)e * a.I * a.d : w.s_up);
@@ -219,22 +241,26 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
         boff[i] = ((uint32_t)(min(nt * kRowsMax + row, a.d - 1) - nt * kRowsMax) * (uint32_t)a.I + 8 * lc) * 2u;
       }
     }
-    auto issue_a = [&](int ks, uint8_t* st) {
+    // ops [I0, I1) of a step's activation / weight load group
+    auto issue_a = [&](int ks, uint8_t* st, auto i0_tag, auto i1_tag) {
       const int kk = ks * kBK;
       uint8_t* da = st + (64 * wv) * 16;
 #pragma unroll
-      for (int i = 0; i < kDma; ++i)
+      for (int i = decltype(i0_tag)::value; i < decltype(i1_tag)::value; ++i)
         __builtin_amdgcn_global_load_lds((const void*)(abase + aoff[i] + 2 * kk), HY_LDS(da + kThreads * 16 * i), 16, 0,
                                          0);
     };
-    auto issue_b = [&](int ks, uint8_t* st) {
+    auto issue_b = [&](int ks, uint8_t* st, auto i0_tag, auto i1_tag) {
       const int kk = ks * kBK;
       uint8_t* db = st + (64 * wv) * 16;
 #pragma unroll
-      for (int i = 0; i < kDma; ++i)
+      for (int i = decltype(i0_tag)::value; i < decltype(i1_tag)::value; ++i)
         __builtin_amdgcn_global_load_lds((const void*)(bbase[i] + boff[i] + 2 * kk), HY_LDS(db + kThreads * 16 * i), 16,
                                          0, 0);
     };
+    using C0 = std::integral_constant<int, 0>;
+    using CH = std::integral_constant<int, kDma / 2>;
+    using CF = std::integral_constant<int, kDma>;
 
     f32x16 acc[kWaveBlocks][kNB];
 #pragma unroll
@@ -244,15 +270,14 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[j][nb][i] = 0.f;
 
-    // prologue: activations of steps 0, 1 and weights of steps 0 .. BS-1 in flight
-    // (K >= 128 gives at least 2 steps; later ones clamp), step 0 landed everywhere
-    issue_a(0, sa0);
-    issue_b(0, sb0);
-    issue_a(1, sa1);
-    issue_b(1, sb1);
-    issue_b(min(2, nks - 1), sb2);
-    if (threadIdx.x == 0) claimed = claim();
-    wait_vm<3 * kDma>();  // (an outstanding claim is older than the loads: counted in)
+    // prologue: steps 0 and 1 of the weights, step 0 and the first half of step 1 of
+    // the activations in flight (K >= 128 gives at least 2 steps), step 0 landed
+    // everywhere; the rest of step 1 and the weights of step 2 follow in step 0
+    issue_a(0, sa0, C0{}, CF{});
+    issue_b(0, sb0, C0{}, CF{});
+    issue_b(1, sb1, C0{}, CF{});
+    issue_a(1, sa1, C0{}, CH{});
+    wait_vm<kDma + kDma / 2>();
     bare_barrier();
 
     // the k loop, with this wave's number of active row blocks fixed at compile time
@@ -278,29 +303,42 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
 #pragma unroll
           for (int nb = 0; nb < kNB; ++nb) acc[j][nb] = mfma32x32x16(fa[s & 1][j], fb[s & 1][nb], acc[j][nb]);
       };
-      // One step ks on activation slot UA = ks % 2 and weight slot UB = ks % BS; NEXT:
-      // there is a next step. sched_barrier(0) keeps each group in place: the fragment
-      // reads stay ahead of the MFMAs that run while they are in flight.
-      auto step = [&](auto ua_tag, auto ub_tag, auto next_tag, int ks) {
+      // One step ks on activation slot UA = ks % 2 and weight slot UB = ks % BS. The
+      // slots step ks-1 used were freed by the barrier that ended it; their next loads
+      // (the second half of the activations of step ks+1, the weights of step ks+2) go
+      // out in 4-op pieces between this step's MFMA groups, so the address unit works
+      // through them while the MFMAs run instead of stalling the waves in one burst.
+      // PA: step ks+1 exists (its activations are loaded); PB: step ks+2 exists (its
+      // weights, and the first half of its activations at the end of this step, are
+      // loaded); NEXT: there is a next step. sched_barrier(0) keeps each group
+      // in place: the fragment reads stay ahead of the MFMAs that run while they are in
+      // flight.
+      auto step = [&](auto ua_tag, auto ub_tag, auto next_tag, auto pa_tag, auto pb_tag, int ks) {
         constexpr int UA = decltype(ua_tag)::value;
         constexpr int UB = decltype(ub_tag)::value;
         constexpr bool NEXT = decltype(next_tag)::value;
-#pragma unroll
-        for (int s = 1; s < kSub; ++s) {
-          read_frags(sa[UA], sb[UB], s);
+        constexpr bool PA = decltype(pa_tag)::value;
+        constexpr bool PB = decltype(pb_tag)::value;
+        for_seq(std::integer_sequence<int, 1, 2, 3>{}, [&](auto s_tag) {
+          constexpr int S = decltype(s_tag)::value;
+          read_frags(sa[UA], sb[UB], S);
+          if constexpr (S == 1 && PA) issue_a(ks + 1, sa[UA ^ 1], CH{}, CF{});
+          if constexpr (S == 2 && PB) issue_b(ks + 2, sb[(UB + 2) % BS], C0{}, CH{});
+          if constexpr (S == 3 && PB) issue_b(ks + 2, sb[(UB + 2) % BS], CH{}, CF{});
           __builtin_amdgcn_sched_barrier(0);
-          mfmas(s - 1);
+          mfmas(S - 1);
           __builtin_amdgcn_sched_barrier(0);
-        }
+        });
         if constexpr (NEXT) {
-          // own activations and weights of step ks+1 landed: issued at the end of step
-          // ks-1 (activations, the newest op group but one) and ks-2 (weights)
-          wait_vm<kDma>();
+          // own loads of step ks+1 landed: all but this step's weight loads (the newest)
+          wait_vm<PB ? kDma : 0>();
           wait_lds();      // own reads of this step done
           bare_barrier();  // everyone's step ks+1 landed; this step's slots are free
-          issue_a(min(ks + 2, nks - 1), sa[UA]);
-          issue_b(min(ks + BS, nks - 1), sb[UB]);
+          if constexpr (PB) issue_a(ks + 2, sa[UA], C0{}, CH{});
           read_frags(sa[UA ^ 1], sb[(UB + 1) % BS], 0);
+        } else {
+          // the last step: claim the next item (read after the k loop)
+          if (threadIdx.x == 0) own_ticket = atomicAdd(&counters[xcd], 1);
         }
         __builtin_amdgcn_sched_barrier(0);
         mfmas(kSub - 1);
@@ -316,12 +354,13 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
         for_seq(std::make_integer_sequence<int, P>{}, [&](auto t) {
           constexpr int T = decltype(t)::value;
           step(std::integral_constant<int, T % 2>{}, std::integral_constant<int, T % 3>{}, std::true_type{},
-               k0 + T);
+               std::true_type{}, std::true_type{}, k0 + T);
         });
       for_seq(std::make_integer_sequence<int, R>{}, [&](auto t) {
         constexpr int T = decltype(t)::value;
         step(std::integral_constant<int, T % 2>{}, std::integral_constant<int, T % 3>{},
-             std::integral_constant<bool, (T + 1 < R)>{}, k0 + T);
+             std::integral_constant<bool, (T + 1 < R)>{}, std::integral_constant<bool, (T + 1 < R)>{},
+             std::integral_constant<bool, (T + 2 < R)>{}, k0 + T);
       });
     };
     const int nact = min(kWaveBlocks, max(0, (nrb - wm + 1) >> 1));
@@ -337,6 +376,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
       k_loop(std::integral_constant<int, 0>{});
     // all waves are done with the ring: it now stages the output tile
     __builtin_amdgcn_s_waitcnt(0);
+    if (threadIdx.x == 0) claimed = own_or_steal(own_ticket);
     bare_barrier();
 
     // Epilogue through LDS: the tile is written as 256-row x 64-column bf16 pieces of
