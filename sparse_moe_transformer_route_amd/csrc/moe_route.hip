@@ -81,6 +81,124 @@ __global__ void __launch_bounds__(64) route_logits_kernel(const uint16_t* __rest
 }
 
 // ---------------------------------------------------------------------------
+// Logits for large T: a workgroup of 4 waves computes a 64-token x 256-expert tile
+// over a slice of d (wave w: experts 64 w .. 64 w + 63). Each 64-wide k step of the
+// 64 x-rows and 256 W_router rows (128 B per row, 40 KB) arrives in LDS through
+// direct global->LDS loads in which 8 consecutive lanes cover one row (whole cache
+// lines per lane quad: the address unit's fast case), then feeds 16x16x32 MFMAs
+// from LDS. Two ring slots; 16-byte chunk c of row r sits at c ^ (r mod 8), so the
+// 16 rows of a fragment read fall on distinct bank groups.
+// Work w enumerates (slice, token tile, expert tile), expert tile fastest, and block
+// b runs work (b mod 8) * per + b / 8: XCD x (b mod 8) takes the x-th contiguous
+// eighth, so its workgroups share one or two slices of W_router in its L2.
+// ---------------------------------------------------------------------------
+constexpr int kLgTok = 64;                       // tokens per tile
+constexpr int kLgExp = 256;                      // experts per tile
+constexpr int kLgRows = kLgTok + kLgExp;         // staged rows per step
+constexpr int kLgSlot = kLgRows * 128;           // 40 KB per ring slot
+constexpr int kLgOps = kLgRows * 128 / 16 / 256; // 16-byte loads per thread per step (10)
+
+template <int N>
+__device__ __forceinline__ void lg_wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__global__ void __launch_bounds__(256, 2) route_logits_lds_kernel(const uint16_t* __restrict__ x,
+                                                                 const uint16_t* __restrict__ wr,
+                                                                 float* __restrict__ part, int T, int d, int E,
+                                                                 int kc, int ks) {
+  __shared__ __attribute__((aligned(16))) uint8_t s0[kLgSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t s1[kLgSlot];
+  const int ntt = (T + kLgTok - 1) / kLgTok, nte = (E + kLgExp - 1) / kLgExp;
+  const int nw = ntt * nte * ks;
+  const int per = (nw + 7) >> 3;
+  const int w = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (w >= nw) return;  // whole workgroup
+  const int te = w % nte, rest = w / nte;
+  const int tt = rest % ntt, z = rest / ntt;
+  const int t0 = tt * kLgTok, e0 = te * kLgExp;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // load op i of thread tid: staged row (256 i + tid) / 8, physical chunk tid % 8
+  // holding logical chunk (tid % 8) ^ (row % 8); rows 0..63 are tokens, 64.. experts,
+  // both clamped to the last valid row (never stored)
+  const uint16_t* src[kLgOps];
+#pragma unroll
+  for (int i = 0; i < kLgOps; ++i) {
+    const int row = (256 * i + tid) >> 3, lc = (tid & 7) ^ (row & 7);
+    const uint16_t* base = row < kLgTok ? x + (size_t)min(t0 + row, T - 1) * d
+                                        : wr + (size_t)min(e0 + row - kLgTok, E - 1) * d;
+    src[i] = base + (size_t)z * kc + 8 * lc;
+  }
+  // (the LDS address operand is the wave's base: lane l writes 16 bytes at base + 16 l)
+  auto issue = [&](int st, uint8_t* slot) {
+#pragma unroll
+    for (int i = 0; i < kLgOps; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(src[i] + 64 * st),
+                                       (__attribute__((address_space(3))) void*)(slot + 4096 * i + 1024 * wv), 16, 0,
+                                       0);
+  };
+
+  // fragment of 16 rows starting at row r0 for k group s (k 32 s .. 32 s + 31): lane
+  // (r16, g) reads row r0 + r16, logical chunk 4 s + g
+  const int r16 = lane & 15, g = lane >> 4;
+  auto frag = [&](const uint8_t* slot, int r0, int s) {
+    const int row = r0 + r16;
+    return *reinterpret_cast<const uint4*>(slot + row * 128 + (((4 * s + g) ^ (row & 7)) << 4));
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+    for (int eb = 0; eb < 4; ++eb) acc[tb][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const uint8_t* slot) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      uint4 a[4], b[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) a[tb] = frag(slot, 16 * tb, s);
+#pragma unroll
+      for (int eb = 0; eb < 4; ++eb) b[eb] = frag(slot, kLgTok + 64 * wv + 16 * eb, s);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int eb = 0; eb < 4; ++eb) acc[tb][eb] = mfma16x16x32(a[tb], b[eb], acc[tb][eb]);
+    }
+  };
+  // step st: its loads (issued one step earlier) landed everywhere, and every wave is
+  // done with step st-1, whose slot then receives step st+1 while step st computes
+  auto step = [&](int st, const uint8_t* cur, uint8_t* nxt, int nst) {
+    lg_wait_vm<0>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (st + 1 < nst) issue(st + 1, nxt);
+    compute(cur);
+  };
+  const int nst = kc / 64;
+  issue(0, s0);
+  for (int st = 0; st < nst; st += 2) {
+    step(st, s0, s1, nst);
+    if (st + 1 < nst) step(st + 1, s1, s0, nst);
+  }
+
+  float* dst = part + (size_t)z * T * E;
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+    for (int eb = 0; eb < 4; ++eb) {
+      const int e = e0 + 64 * wv + 16 * eb + r16;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int t = t0 + 16 * tb + 4 * g + q;
+        if (t < T && e < E) dst[(size_t)t * E + e] = acc[tb][eb][q];
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Selection: one wave per token. Logits (the split-d partials summed in fixed order,
 // plus the bias) are mapped to order-preserving 32-bit keys; the k-th largest key is
 // found by an MSB-first radix select whose counts are wave ballots, then ties at the
@@ -245,11 +363,17 @@ __global__ void __launch_bounds__(1024) route_select_kernel(const float* __restr
   }
 }
 
-// Split of d for the router: enough waves to stream W_router from HBM at small T,
-// at most 16 partial sums per logit.
+// The LDS-tiled logits kernel takes batches of at least this many tokens.
+constexpr int kLgMinT = 1024;
+
+// Split of d for the router: enough waves to stream W_router from HBM at small T
+// (one-wave tiles), enough workgroups for two per CU at large T (LDS tiles); at most
+// 16 partial sums per logit.
 static int pick_split(int T, int d, int E) {
-  const int base = ((T + 31) / 32) * ((E + 63) / 64);
-  const int target = 256;
+  const bool lds = T >= kLgMinT;
+  const int base = lds ? ((T + kLgTok - 1) / kLgTok) * ((E + kLgExp - 1) / kLgExp)
+                       : ((T + 31) / 32) * ((E + 63) / 64);
+  const int target = lds ? 512 : 256;
   const int steps = d / 64;
   int best = 1;
   for (int s = 1; s <= steps && s <= kMaxSplit; ++s)
@@ -272,8 +396,14 @@ static void launch_select(const Plan& p, const float* bias, float* margin_out, i
 
 hipError_t launch_route(const Plan& p, const uint16_t* x, const uint16_t* w_router, const float* bias,
                         float* margin_out, int32_t* counts_out, int32_t* offsets_out, hipStream_t s, Marks& m) {
-  dim3 g1((p.T + 31) / 32, (p.E + 63) / 64, p.ks);
-  hipLaunchKernelGGL(route_logits_kernel, g1, dim3(64), 0, s, x, w_router, p.part, p.T, p.d, p.E, p.d / p.ks);
+  if (p.T >= kLgMinT) {
+    const int nw = ((p.T + kLgTok - 1) / kLgTok) * ((p.E + kLgExp - 1) / kLgExp) * p.ks;
+    hipLaunchKernelGGL(route_logits_lds_kernel, dim3(8 * ((nw + 7) / 8)), dim3(256), 0, s, x, w_router, p.part, p.T,
+                       p.d, p.E, p.d / p.ks, p.ks);
+  } else {
+    dim3 g1((p.T + 31) / 32, (p.E + 63) / 64, p.ks);
+    hipLaunchKernelGGL(route_logits_kernel, g1, dim3(64), 0, s, x, w_router, p.part, p.T, p.d, p.E, p.d / p.ks);
+  }
   hipError_t err = hipGetLastError();
   if (err == hipSuccess) err = m.mark(s);
   if (err != hipSuccess) return err;

@@ -100,6 +100,8 @@ def test_tiny_config(path):
     dict(T=33, d=128, E=1024, k=16, I=128),       # largest E and k
     dict(T=600, d=256, E=4, k=2, I=128),          # ~300 rows per expert: several M tiles
     dict(T=300, d=512, E=8, k=8, I=384),          # every expert takes every token
+    dict(T=1100, d=256, E=40, k=3, I=128),        # LDS-tiled router: ragged token tile, E < 256, 1 k step
+    dict(T=1030, d=1024, E=300, k=2, I=128),      # LDS-tiled router: two expert tiles, 2 k steps per slice
 ])
 def test_small_shapes(shape, path):
     cfg = hi.LayerConfig("shape", seed=1, **shape)
