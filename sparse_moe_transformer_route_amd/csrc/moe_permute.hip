@@ -14,7 +14,9 @@
 
 namespace hymoe {
 
-// One block of 1024 threads; thread e owns routed expert e.
+// One block of 1024 threads. Expert e's token blocks are split into J = 1024 / E
+// contiguous chunks, chunk j counted by thread j E + e; the chunk counts are combined
+// in chunk order, so every position depends on the routing alone.
 __global__ void __launch_bounds__(1024) permute_scan_kernel(const unsigned long long* __restrict__ mask, int nblk,
                                                             int T, int E, int k, int bm,
                                                             int32_t* __restrict__ blk_base,
@@ -23,14 +25,36 @@ __global__ void __launch_bounds__(1024) permute_scan_kernel(const unsigned long 
                                                             int32_t* __restrict__ counts_out,
                                                             int32_t* __restrict__ offsets_out) {
   __shared__ int wsum[17];
-  const int e = threadIdx.x;
+  __shared__ int part[1024];  // chunk counts, then chunk starts, [j][e]
+  const int tid = threadIdx.x;
+  const int J = max(1, (int)blockDim.x / E);
+  const int cb = (nblk + J - 1) / J;  // blocks per chunk
+  const int e = tid % E, j = tid / E;
+  const bool mine = j < J;
+  const int b0 = mine ? min(nblk, j * cb) : 0, b1 = mine ? min(nblk, b0 + cb) : 0;
+  int c = 0;
+#pragma unroll 8
+  for (int b = b0; b < b1; ++b) c += __popcll(mask[(size_t)b * E + e]);
+  if (mine) part[tid] = c;
+  __syncthreads();
+  // thread e < E: its total and the start of each chunk relative to the expert's first row
   int cnt = 0;
-  if (e < E)
-    for (int b = 0; b < nblk; ++b) cnt += __popcll(mask[(size_t)b * E + e]);
-  const int excl = build_work_lists(cnt, T, E, k, bm, wsum, offs, meta, touched, tiles, counts_out, offsets_out);
-  if (e < E) {
-    int run = excl;
-    for (int b = 0; b < nblk; ++b) {
+  if (tid < E) {
+    for (int jj = 0; jj < J; ++jj) {
+      const int v = part[jj * E + tid];
+      part[jj * E + tid] = cnt;
+      cnt += v;
+    }
+  }
+  const int excl = build_work_lists(tid < E ? cnt : 0, T, E, k, bm, wsum, offs, meta, touched, tiles, counts_out,
+                                    offsets_out);  // (synchronises the block)
+  if (tid < E)
+    for (int jj = 0; jj < J; ++jj) part[jj * E + tid] += excl;  // the expert's first row
+  __syncthreads();
+  if (mine) {
+    int run = part[tid];
+#pragma unroll 8
+    for (int b = b0; b < b1; ++b) {
       blk_base[(size_t)b * E + e] = run;
       run += __popcll(mask[(size_t)b * E + e]);
     }
