@@ -306,6 +306,26 @@ def main():
         del pre
         torch.cuda.empty_cache()
 
+    # measured peaks next to the published ones: bf16 MFMA on random operand bits (the
+    # power-capped clock depends on operand activity) and one streaming read of HBM
+    gen = torch.Generator(device="cuda:0").manual_seed(0)
+    ops = torch.randn(hm.PROBE_OPERAND_BYTES // 2, generator=gen, device="cuda:0").to(torch.bfloat16)
+    read_buf = shared_weights["gate"] if shared_weights is not None else torch.empty(4 << 30, dtype=torch.uint8,
+                                                                                     device="cuda:0")
+    peaks = {"mfma_bf16_tflops": hm.probe_mfma_bf16(ops), "hbm_read_gbs": hm.probe_hbm_read(read_buf),
+             "hbm_read_bytes": read_buf.numel() * read_buf.element_size(),
+             "how": "hy_moe_probe_mfma_bf16 (32x32x16 bf16 MFMAs, 4 workgroups per CU, random N(0,1) operands, "
+                    "~40 ms) and hy_moe_probe_hbm_read (one timed pass of 16-byte loads after an untimed one)"}
+    del read_buf
+    log(f"[bench] measured peaks: {peaks['mfma_bf16_tflops']:.0f} TFLOP/s bf16 MFMA, "
+        f"{peaks['hbm_read_gbs']:.0f} GB/s HBM read")
+    roof = main_res["roofline"]
+    meas = peaks["hbm_read_gbs"] if roof["unit"] == "GB/s" else peaks["mfma_bf16_tflops"]
+    roof["frac_of_measured_peak"] = roof["achieved"] / meas
+    if "prefill" in extra:
+        extra["prefill"]["roofline"]["frac_of_measured_peak"] = (extra["prefill"]["roofline"]["achieved"]
+                                                                 / peaks["mfma_bf16_tflops"])
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host")
@@ -325,6 +345,7 @@ def main():
         "roofline": main_res["roofline"],
         "layer": main_res["layer"],
         "kernels_ms": main_res["kernels_ms"],
+        "measured_peak": peaks,
         "cpu_baseline": cpu,
     }
     line.update(extra)

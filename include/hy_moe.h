@@ -174,6 +174,27 @@ const char* hy_moe_status_string(int status);
  */
 int hy_moe_sherry_pack_host(const int8_t* tern, int64_t rows, int64_t cols, uint32_t* packed);
 
+/*
+ * Machine-peak probes (not part of the layer): the rates this GPU reaches, for
+ * reporting a layer's roofline fraction against measured as well as published
+ * peaks. Each enqueues its kernels on `stream` (a hipStream_t, NULL = default),
+ * waits for them, and returns HY_MOE_OK or HY_MOE_ERR_HIP; bad arguments give
+ * HY_MOE_ERR_INVALID_ARG with nothing enqueued. They allocate nothing.
+ *
+ * hy_moe_probe_mfma_bf16: dense 32x32x16 bf16 MFMAs with fp32 accumulation on 4
+ *   workgroups per CU for about 40 ms. operands: DEVICE, 16-byte aligned, at least
+ *   HY_MOE_PROBE_OPERAND_BYTES of bf16 bit patterns filled by the caller (random
+ *   values give the rate of real data: under the power cap the clock depends on
+ *   operand bit activity). Writes TFLOP/s (2 flop per multiply-add) to *tflops
+ *   (HOST).
+ * hy_moe_probe_hbm_read: reads buf (DEVICE, 16-byte aligned, `bytes` >= 16; use
+ *   much more than the 256 MB last-level cache) once untimed, then once timed with
+ *   16-byte loads. Writes GB/s (1e9 B/s) to *gbps (HOST).
+ */
+#define HY_MOE_PROBE_OPERAND_BYTES 65536
+int hy_moe_probe_mfma_bf16(const void* operands, size_t operand_bytes, float* tflops, void* stream);
+int hy_moe_probe_hbm_read(const void* buf, size_t bytes, float* gbps, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,8 @@ KERNELS = ["route_logits", "route_topk", "permute_scan", "permute_scatter", "exp
 NUM_STAGE_EVENTS = len(KERNELS) + 1
 
 EXPORTED = ["hy_moe_forward", "hy_moe_forward_ex", "hy_moe_workspace_size", "hy_moe_status_string",
-            "hy_moe_sherry_pack_host"]
+            "hy_moe_sherry_pack_host", "hy_moe_probe_mfma_bf16", "hy_moe_probe_hbm_read"]
+PROBE_OPERAND_BYTES = 65536
 
 
 class HyMoeArgs(ctypes.Structure):
@@ -75,6 +76,10 @@ def _load():
     L.hy_moe_status_string.restype = ctypes.c_char_p
     L.hy_moe_sherry_pack_host.argtypes = [vp, i64, i64, vp]
     L.hy_moe_sherry_pack_host.restype = ctypes.c_int
+    L.hy_moe_probe_mfma_bf16.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_float), vp]
+    L.hy_moe_probe_mfma_bf16.restype = ctypes.c_int
+    L.hy_moe_probe_hbm_read.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_float), vp]
+    L.hy_moe_probe_hbm_read.restype = ctypes.c_int
     return L
 
 
@@ -188,3 +193,24 @@ def sherry_pack_host(tern):
     if rc != OK:
         raise HyMoeError(rc, "hy_moe_sherry_pack_host")
     return packed
+
+
+def probe_mfma_bf16(operands, stream=None) -> float:
+    """hy_moe_probe_mfma_bf16: TFLOP/s of dense bf16 MFMAs on the given operand bits
+    (a device tensor of at least PROBE_OPERAND_BYTES bytes)."""
+    tf = ctypes.c_float()
+    rc = _lib.hy_moe_probe_mfma_bf16(operands.data_ptr(), operands.numel() * operands.element_size(),
+                                     ctypes.byref(tf), _stream(stream))
+    if rc != OK:
+        raise HyMoeError(rc, "hy_moe_probe_mfma_bf16")
+    return tf.value
+
+
+def probe_hbm_read(buf, stream=None) -> float:
+    """hy_moe_probe_hbm_read: GB/s of one streaming read pass over a device tensor."""
+    gb = ctypes.c_float()
+    rc = _lib.hy_moe_probe_hbm_read(buf.data_ptr(), buf.numel() * buf.element_size(), ctypes.byref(gb),
+                                    _stream(stream))
+    if rc != OK:
+        raise HyMoeError(rc, "hy_moe_probe_hbm_read")
+    return gb.value

@@ -87,6 +87,20 @@ def test_envelope_limits():
     assert hm.lib().hy_moe_forward_ex(None, None) == hm.ERR_INVALID_ARG
 
 
+def test_probe_argument_checks():
+    m = re.search(r"#define HY_MOE_PROBE_OPERAND_BYTES (\d+)", open(HEADER).read())
+    assert m and int(m.group(1)) == hm.PROBE_OPERAND_BYTES
+    L = hm.lib()
+    out = ctypes.c_float()
+    assert L.hy_moe_probe_mfma_bf16(None, hm.PROBE_OPERAND_BYTES, ctypes.byref(out), None) == hm.ERR_INVALID_ARG
+    assert L.hy_moe_probe_mfma_bf16(FAKE, hm.PROBE_OPERAND_BYTES - 16, ctypes.byref(out), None) == hm.ERR_INVALID_ARG
+    assert L.hy_moe_probe_mfma_bf16(FAKE + 8, hm.PROBE_OPERAND_BYTES, ctypes.byref(out), None) == hm.ERR_INVALID_ARG
+    assert L.hy_moe_probe_mfma_bf16(FAKE, hm.PROBE_OPERAND_BYTES, None, None) == hm.ERR_INVALID_ARG
+    assert L.hy_moe_probe_hbm_read(None, 1 << 20, ctypes.byref(out), None) == hm.ERR_INVALID_ARG
+    assert L.hy_moe_probe_hbm_read(FAKE, 8, ctypes.byref(out), None) == hm.ERR_INVALID_ARG
+    assert L.hy_moe_probe_hbm_read(FAKE + 4, 1 << 20, ctypes.byref(out), None) == hm.ERR_INVALID_ARG
+
+
 def test_grouped_path_byte_limit():
     # the grouped GEMM addresses x and the hidden activations with 32-bit byte offsets
     a = base_args(T=2 ** 18, d=8192, E=64, k=8, I=128)  # x: 2^32 bytes
