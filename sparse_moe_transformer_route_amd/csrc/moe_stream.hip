@@ -379,27 +379,257 @@ __global__ void __launch_bounds__(256) stream_down_kernel(StreamArgs a, ExpertWe
   }
 }
 
+// The shared expert (bf16, rows = all T tokens in order) beside the LDS-staged ternary
+// kernels: one wave, 16 rows (gate/up: hidden units i0w..; down: output rows m0w..),
+// token columns [cb, min(n, cb + 16)).
+__device__ __forceinline__ void shared_gateup_pass(const StreamArgs& a, const ExpertWeights& w,
+                                                   uint16_t* __restrict__ h, int i0w, int row0, int cb, int n) {
+  const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
+  const int d = a.d;
+  const uint16_t* wg = w.s_gate + (size_t)(i0w + r16) * d + kKV * 8 * g;
+  const uint16_t* wu = w.s_up + (size_t)(i0w + r16) * d + kKV * 8 * g;
+  const bool valid = cb + r16 < n;
+  const int col = valid ? row0 + cb + r16 : row0;
+  const uint16_t* xr = a.x + (size_t)row_token(col, a.perm_src, a.Tk, a.k) * d + kKV * 8 * g;
+  f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+  gateup_bf16_block<kDepthSharedTern>(wg, wu, xr, d, accg, accu);
+  if (valid)
+    *reinterpret_cast<uint2*>(h + (size_t)col * a.I + i0w + 4 * g) =
+        make_uint2(pack_bf16x2(silu(accg[0]) * accu[0], silu(accg[1]) * accu[1]),
+                   pack_bf16x2(silu(accg[2]) * accu[2], silu(accg[3]) * accu[3]));
+}
+
+__device__ __forceinline__ void shared_down_pass(const StreamArgs& a, const ExpertWeights& w,
+                                                 const uint16_t* __restrict__ h, float* __restrict__ y, int m0w,
+                                                 int row0, int cb, int n) {
+  const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
+  const int I = a.I;
+  const uint16_t* wd = w.s_down + (size_t)(m0w + r16) * I + kKV * 8 * g;
+  const bool valid = cb + r16 < n;
+  const int col = valid ? row0 + cb + r16 : row0;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  down_bf16_block<kDepthSharedTern>(wd, h + (size_t)col * I + kKV * 8 * g, I, acc);
+  if (valid)
+    *reinterpret_cast<float4*>(y + (size_t)col * a.d + m0w + 4 * g) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+}
+
+// ------------------------------------------- ternary experts, staged in LDS
+// Routed Sherry experts when d and I are multiples of 512. Loading the operands
+// straight into registers in the MFMA layout (above) puts 16 rows on consecutive
+// lanes, so each lane quad touches four cache lines and the address unit, not HBM,
+// bounds the kernel. Here a workgroup covers 256 code rows (gate/up: 128 hidden units
+// of both matrices; down: 256 output rows) of one touched expert and walks k in
+// chunks of 4 blocks (512 weights): the chunk's code bytes (80 B per row) and the
+// pass's 16 activation rows (1 KB each) arrive in LDS by direct global->LDS loads
+// with consecutive lanes on consecutive 16-byte pieces, in a 2-slot ring; the four
+// waves share the activations. Activation piece c of token slot t is stored at
+// c ^ (t mod 16), so the 16 token rows of a fragment read fall on distinct banks.
+constexpr int kTlBlocks = 4;                             // 128-weight blocks per chunk
+constexpr int kTlRows = 256;                             // code rows per workgroup
+constexpr int kTlRowBytes = kTlBlocks * 20;              // code bytes per row per chunk
+constexpr int kTlCodeBytes = kTlRows * kTlRowBytes;      // 20 KB
+constexpr int kTlTokBytes = kTlBlocks * 128 * 2;         // activation bytes per token per chunk
+constexpr int kTlXBytes = 16 * kTlTokBytes;              // 16 KB
+constexpr int kTlSlot = kTlCodeBytes + kTlXBytes;        // 36 KB per ring slot
+constexpr int kTlCodeOps = kTlCodeBytes / (256 * 16);    // 16-byte loads per thread per chunk: 5
+constexpr int kTlXOps = kTlXBytes / (256 * 16);          // 4
+static_assert(kTlCodeOps * 256 * 16 == kTlCodeBytes && kTlXOps * 256 * 16 == kTlXBytes, "whole load ops");
+
+bool tern_lds_eligible(const Plan& p, const ExpertWeights& w) {
+  auto a16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
+  return w.ternary && p.d % 512 == 0 && p.I % 512 == 0 && a16(w.qgate) && a16(w.qup) && a16(w.qdown);
+}
+
+// NM = 2: gate and up (act = x through the permutation, out = h bf16, K = d);
+// NM = 1: down (act = h rows, out = y fp32, K = I). Grid (rows / (256 / NM),
+// shared slots + touched routed experts). The first grid rows run the bf16 shared
+// expert, one 16-token pass and one 64-row quarter (down) or half (gate/up) of the
+// workgroup's rows each, so that they start first and overlap the routed experts.
+template <int NM>
+__host__ __device__ constexpr int tern_shared_subs() { return kTlRows / NM / 64; }
+
+template <int NM>
+__global__ void __launch_bounds__(256, 2) tern_lds_kernel(StreamArgs a, ExpertWeights w,
+                                                        const uint16_t* __restrict__ act, void* __restrict__ out) {
+  __shared__ uint2 lut[32];
+  __shared__ __attribute__((aligned(16))) uint8_t s0[kTlSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t s1[kTlSlot];
+  constexpr int SUBS = tern_shared_subs<NM>();
+  const int T = a.Tk / a.k;
+  const int sh = ((T + 15) / 16) * SUBS;
+  if ((int)blockIdx.y < sh) {
+    const int pass = blockIdx.y / SUBS, sub = blockIdx.y - pass * SUBS;
+    const int r0 = blockIdx.x * (kTlRows / NM) + sub * 64 + (threadIdx.x >> 6) * 16;
+    if (NM == 2)
+      shared_gateup_pass(a, w, reinterpret_cast<uint16_t*>(out), r0, a.offs[a.E], 16 * pass, T);
+    else
+      shared_down_pass(a, w, act, reinterpret_cast<float*>(out), r0, a.offs[a.E], 16 * pass, T);
+    return;
+  }
+  const int ridx = blockIdx.y - sh + 1;  // touched[0] is the shared expert
+  if (ridx >= a.meta[0]) return;         // whole workgroup
+  build_code_table(lut);                 // visible after the first barrier below
+  const int e = a.touched[ridx];
+  const int row0 = a.offs[e], n = a.offs[e + 1] - row0;
+  const int K = NM == 2 ? a.d : a.I;
+  const int R = NM == 2 ? a.I : a.d;  // rows of each matrix
+  const int wpr = K / 128 * 5;        // code words per row
+  const int rbase = blockIdx.x * (kTlRows / NM);
+  const int nch = K / (128 * kTlBlocks);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+
+  // code piece j = 256 i + tid: workgroup code row j / 5 (matrix row / 128 when NM = 2),
+  // 16-byte piece j % 5 of the row's 80 chunk bytes; LDS [row][80 B]
+  const char* csrc[kTlCodeOps];
+#pragma unroll
+  for (int i = 0; i < kTlCodeOps; ++i) {
+    const int j = 256 * i + tid, row = j / 5, piece = j - 5 * row;
+    const int mat = NM == 2 ? row >> 7 : 0, rr = NM == 2 ? (row & 127) : row;
+    const uint32_t* q = (NM == 2 ? (mat ? w.qup : w.qgate) : w.qdown) + ((size_t)e * R + rbase + rr) * wpr;
+    csrc[i] = reinterpret_cast<const char*>(q) + 16 * piece;
+  }
+  // this wave's row blocks: NM = 2: (gate, up) x 2 blocks of 16 units at rbase + 32 wv;
+  // NM = 1: 4 blocks of 16 output rows at rbase + 64 wv
+  auto crow = [&](int qb) { return NM == 2 ? (qb >> 1) * 128 + 32 * wv + 16 * (qb & 1) + r16 : 64 * wv + 16 * qb + r16; };
+  const int w0 = (5 * g) >> 2;  // lane group g's first code word of a block
+  float sc[4][4];               // row scales of the rows this lane's results belong to
+#pragma unroll
+  for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int orow = crow(qb) - r16 + 4 * g + j;  // D row 4g + j of the block
+      const int mat = NM == 2 ? orow >> 7 : 0, rr = NM == 2 ? (orow & 127) : orow;
+      const uint16_t* sp = NM == 2 ? (mat ? w.sup : w.sgate) : w.sdown;
+      sc[qb][j] = bf16_bits_to_f32(sp[(size_t)e * R + rbase + rr]);
+    }
+
+  for (int cb = 0; cb < n; cb += 16) {  // token passes of 16 (uniform)
+    // activation piece j = 256 i + tid: token slot j / 64 of the pass, stored piece j % 64
+    const char* xsrc[kTlXOps];
+#pragma unroll
+    for (int i = 0; i < kTlXOps; ++i) {
+      const int j = 256 * i + tid, t = j >> 6, pp = j & 63;
+      const int col = cb + t < n ? row0 + cb + t : row0;  // unused slots repeat a valid row
+      // (routed rows are below Tk: their token is perm_src / k, loaded without a branch)
+      const uint16_t* arow = NM == 2 ? act + (size_t)((uint32_t)a.perm_src[col] / (uint32_t)a.k) * a.d
+                                     : act + (size_t)col * a.I;
+      xsrc[i] = reinterpret_cast<const char*>(arow) + 16 * (pp ^ (t & 15));
+    }
+    auto issue = [&](int c, uint8_t* slot) {
+      // (the LDS operand is the wave's base: lane l writes 16 bytes at base + 16 l)
+#pragma unroll
+      for (int i = 0; i < kTlCodeOps; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(csrc[i] + kTlRowBytes * c),
+                                         (__attribute__((address_space(3))) void*)(slot + 4096 * i + 1024 * wv), 16, 0,
+                                         0);
+#pragma unroll
+      for (int i = 0; i < kTlXOps; ++i)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(xsrc[i] + kTlTokBytes * c),
+            (__attribute__((address_space(3))) void*)(slot + kTlCodeBytes + 4096 * i + 1024 * wv), 16, 0, 0);
+    };
+    f32x4 acc[4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) acc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](const uint8_t* slot) {
+#pragma unroll
+      for (int b = 0; b < kTlBlocks; ++b) {
+        uint4 xf[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          xf[m] = *reinterpret_cast<const uint4*>(slot + kTlCodeBytes + r16 * kTlTokBytes +
+                                                  16 * ((16 * b + 4 * g + m) ^ r16));
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) {
+          const uint32_t* cw = reinterpret_cast<const uint32_t*>(slot + crow(qb) * kTlRowBytes + 20 * b) + w0;
+          const uint32_t c2[2] = {cw[0], cw[1]};
+          const uint64_t v = tern_window(c2, g);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) acc[qb] = mfma16x16x32(tern_operand(v, m, lut), xf[m], acc[qb]);
+        }
+      }
+    };
+    // chunk c: its loads (issued a chunk earlier) landed everywhere and every wave is
+    // done with chunk c-1, whose slot then receives chunk c+1 while chunk c computes
+    auto step = [&](int c, const uint8_t* cur, uint8_t* nxt) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), other counters untouched (gfx9 encoding)
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (c + 1 < nch) issue(c + 1, nxt);
+      compute(cur);
+    };
+    issue(0, s0);
+    for (int c = 0; c < nch; c += 2) {
+      step(c, s0, s1);
+      if (c + 1 < nch) step(c + 1, s1, s0);
+    }
+    if (cb + r16 < n) {
+      const int col = row0 + cb + r16;
+      if (NM == 2) {
+        uint16_t* h = reinterpret_cast<uint16_t*>(out);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          float hv[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) hv[j] = silu(acc[r][j] * sc[r][j]) * (acc[2 + r][j] * sc[2 + r][j]);
+          *reinterpret_cast<uint2*>(h + (size_t)col * a.I + rbase + 32 * wv + 16 * r + 4 * g) =
+              make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+        }
+      } else {
+        float* y = reinterpret_cast<float*>(out);
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb)
+          *reinterpret_cast<float4*>(y + (size_t)col * a.d + rbase + 64 * wv + 16 * qb + 4 * g) =
+              make_float4(acc[qb][0] * sc[qb][0], acc[qb][1] * sc[qb][1], acc[qb][2] * sc[qb][2],
+                          acc[qb][3] * sc[qb][3]);
+      }
+    }
+    __syncthreads();  // every wave is done with both slots before the next pass loads them
+  }
+}
+
 hipError_t launch_stream_experts(const Plan& p, const uint16_t* x, const ExpertWeights& w, hipStream_t s,
                                  Marks& m) {
   StreamArgs a{x, p.touched, p.meta, p.offs, p.perm_src, p.Tk, p.k, p.d, p.I, p.E};
-  const int slots = (p.Tk < p.E ? p.Tk : p.E) + (w.ternary ? ((p.T + 15) / 16) * 2 : 1);
+  const int routed = p.Tk < p.E ? p.Tk : p.E;  // at most this many touched routed experts
+  const int sh = w.ternary ? ((p.T + 15) / 16) * 2 : 1;
+  const int passes = (p.T + 15) / 16;
+  if (tern_lds_eligible(p, w)) {
+    // LDS-staged ternary kernels, the shared expert's rows first in each grid
+    hipLaunchKernelGGL(tern_lds_kernel<2>, dim3(p.I / (kTlRows / 2), passes * tern_shared_subs<2>() + routed),
+                       dim3(256), 0, s, a, w, x, (void*)p.h);
+    hipError_t err = hipGetLastError();
+    if (err == hipSuccess) err = m.mark(s);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(tern_lds_kernel<1>, dim3(p.d / kTlRows, passes * tern_shared_subs<1>() + routed), dim3(256),
+                       0, s, a, w, (const uint16_t*)p.h, (void*)p.y);
+    err = hipGetLastError();
+    return err == hipSuccess ? m.mark(s) : err;
+  }
+  const int slots = routed + sh;
   // ternary kernels: 128 rows per workgroup (d and I are multiples of 128)
   const int rows_wg = w.ternary ? 128 : 64;
   dim3 g1(p.I / rows_wg, slots), g2(p.d / rows_wg, slots);
+  hipError_t err;
   if (w.ternary) {
     hipLaunchKernelGGL(stream_gateup_kernel<true>, g1, dim3(256), 0, s, a, w, p.h);
+    err = hipGetLastError();
   } else {
     hipLaunchKernelGGL(stream_gateup_kernel<false>, g1, dim3(256), 0, s, a, w, p.h);
+    err = hipGetLastError();
   }
-  hipError_t err = hipGetLastError();
   if (err == hipSuccess) err = m.mark(s);
   if (err != hipSuccess) return err;
   if (w.ternary) {
     hipLaunchKernelGGL(stream_down_kernel<true>, g2, dim3(256), 0, s, a, w, p.h, (float*)p.y);
+    err = hipGetLastError();
   } else {
     hipLaunchKernelGGL(stream_down_kernel<false>, g2, dim3(256), 0, s, a, w, p.h, (float*)p.y);
+    err = hipGetLastError();
   }
-  err = hipGetLastError();
   return err == hipSuccess ? m.mark(s) : err;
 }
 

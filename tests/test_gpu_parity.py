@@ -139,6 +139,16 @@ def test_ternary_small(T):
     run_small(cfg, hm.PATH_STREAM)
 
 
+@pytest.mark.parametrize("shape", [
+    dict(T=1, d=512, E=16, k=2, I=512),       # LDS-staged ternary kernels: one token
+    dict(T=40, d=1024, E=16, k=4, I=512),     # ~10 tokens per expert, 2 k chunks per row in down
+    dict(T=150, d=512, E=8, k=2, I=1024),     # ~38 tokens per expert: three 16-token passes
+])
+def test_ternary_lds_small(shape):
+    cfg = hi.LayerConfig("tern", ternary=True, seed=5, **shape)
+    run_small(cfg, hm.PATH_STREAM)
+
+
 def test_ternary_grouped_path_unsupported():
     cfg = hi.LayerConfig("tern", T=8, d=256, E=16, k=2, I=128, ternary=True, seed=5)
     inp = hi.dev_layer(cfg, device=DEV)
