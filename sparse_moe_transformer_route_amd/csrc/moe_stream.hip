@@ -420,19 +420,26 @@ __device__ __forceinline__ void shared_down_pass(const StreamArgs& a, const Expe
 // bounds the kernel. Here a workgroup covers 256 code rows (gate/up: 128 hidden units
 // of both matrices; down: 256 output rows) of one touched expert and walks k in
 // chunks of 4 blocks (512 weights): the chunk's code bytes (80 B per row) and the
-// pass's 16 activation rows (1 KB each) arrive in LDS by direct global->LDS loads
-// with consecutive lanes on consecutive 16-byte pieces, in a 2-slot ring; the four
-// waves share the activations. Activation piece c of token slot t is stored at
-// c ^ (t mod 16), so the 16 token rows of a fragment read fall on distinct banks.
+// pass's 4 activation rows (1 KB each) arrive in LDS by direct global->LDS loads
+// with consecutive lanes on consecutive 16-byte pieces, in a 2-slot ring filled one
+// chunk ahead; the four waves share the activations. The kernel is bound by latency
+// (code-table lookups feeding each MFMA), so occupancy matters more than ring depth:
+// 4 tokens per pass keep a slot at 24 KB and 3 workgroups fit per CU (decode experts
+// have ~1.6 tokens; a 3-slot ring at 2 workgroups per CU measured 15-20% slower). The
+// MFMA's other 12 token columns repeat token 3 and are not stored. Activation piece c
+// of token slot t is stored at c ^ t, so a fragment read's token rows fall on
+// distinct banks.
 constexpr int kTlBlocks = 4;                             // 128-weight blocks per chunk
 constexpr int kTlRows = 256;                             // code rows per workgroup
 constexpr int kTlRowBytes = kTlBlocks * 20;              // code bytes per row per chunk
 constexpr int kTlCodeBytes = kTlRows * kTlRowBytes;      // 20 KB
+constexpr int kTlTok = 4;                                // tokens per pass
 constexpr int kTlTokBytes = kTlBlocks * 128 * 2;         // activation bytes per token per chunk
-constexpr int kTlXBytes = 16 * kTlTokBytes;              // 16 KB
-constexpr int kTlSlot = kTlCodeBytes + kTlXBytes;        // 36 KB per ring slot
+constexpr int kTlXBytes = kTlTok * kTlTokBytes;          // 4 KB
+constexpr int kTlSlot = kTlCodeBytes + kTlXBytes;        // 24 KB per ring slot
 constexpr int kTlCodeOps = kTlCodeBytes / (256 * 16);    // 16-byte loads per thread per chunk: 5
-constexpr int kTlXOps = kTlXBytes / (256 * 16);          // 4
+constexpr int kTlXOps = kTlXBytes / (256 * 16);          // 1
+constexpr int kTlWgPerCu = 3;                            // workgroups per CU (2 slots: 48 KB each)
 static_assert(kTlCodeOps * 256 * 16 == kTlCodeBytes && kTlXOps * 256 * 16 == kTlXBytes, "whole load ops");
 
 bool tern_lds_eligible(const Plan& p, const ExpertWeights& w) {
@@ -449,7 +456,7 @@ template <int NM>
 __host__ __device__ constexpr int tern_shared_subs() { return kTlRows / NM / 64; }
 
 template <int NM>
-__global__ void __launch_bounds__(256, 2) tern_lds_kernel(StreamArgs a, ExpertWeights w,
+__global__ void __launch_bounds__(256, kTlWgPerCu) tern_lds_kernel(StreamArgs a, ExpertWeights w,
                                                         const uint16_t* __restrict__ act, void* __restrict__ out) {
   __shared__ uint2 lut[32];
   __shared__ __attribute__((aligned(16))) uint8_t s0[kTlSlot];
@@ -505,7 +512,7 @@ __global__ void __launch_bounds__(256, 2) tern_lds_kernel(StreamArgs a, ExpertWe
       sc[qb][j] = bf16_bits_to_f32(sp[(size_t)e * R + rbase + rr]);
     }
 
-  for (int cb = 0; cb < n; cb += 16) {  // token passes of 16 (uniform)
+  for (int cb = 0; cb < n; cb += kTlTok) {  // token passes (uniform)
     // activation piece j = 256 i + tid: token slot j / 64 of the pass, stored piece j % 64
     const char* xsrc[kTlXOps];
 #pragma unroll
@@ -515,7 +522,7 @@ __global__ void __launch_bounds__(256, 2) tern_lds_kernel(StreamArgs a, ExpertWe
       // (routed rows are below Tk: their token is perm_src / k, loaded without a branch)
       const uint16_t* arow = NM == 2 ? act + (size_t)((uint32_t)a.perm_src[col] / (uint32_t)a.k) * a.d
                                      : act + (size_t)col * a.I;
-      xsrc[i] = reinterpret_cast<const char*>(arow) + 16 * (pp ^ (t & 15));
+      xsrc[i] = reinterpret_cast<const char*>(arow) + 16 * (pp ^ t);
     }
     auto issue = [&](int c, uint8_t* slot) {
       // (the LDS operand is the wave's base: lane l writes 16 bytes at base + 16 l)
@@ -537,10 +544,11 @@ __global__ void __launch_bounds__(256, 2) tern_lds_kernel(StreamArgs a, ExpertWe
 #pragma unroll
       for (int b = 0; b < kTlBlocks; ++b) {
         uint4 xf[4];
+        const int tk = min(r16, kTlTok - 1);  // this lane's token column (repeats past the pass)
 #pragma unroll
         for (int m = 0; m < 4; ++m)
-          xf[m] = *reinterpret_cast<const uint4*>(slot + kTlCodeBytes + r16 * kTlTokBytes +
-                                                  16 * ((16 * b + 4 * g + m) ^ r16));
+          xf[m] = *reinterpret_cast<const uint4*>(slot + kTlCodeBytes + tk * kTlTokBytes +
+                                                  16 * ((16 * b + 4 * g + m) ^ tk));
 #pragma unroll
         for (int qb = 0; qb < 4; ++qb) {
           const uint32_t* cw = reinterpret_cast<const uint32_t*>(slot + crow(qb) * kTlRowBytes + 20 * b) + w0;
@@ -554,7 +562,7 @@ __global__ void __launch_bounds__(256, 2) tern_lds_kernel(StreamArgs a, ExpertWe
     // chunk c: its loads (issued a chunk earlier) landed everywhere and every wave is
     // done with chunk c-1, whose slot then receives chunk c+1 while chunk c computes
     auto step = [&](int c, const uint8_t* cur, uint8_t* nxt) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), other counters untouched (gfx9 encoding)
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) (gfx9 encoding, other counters untouched)
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
@@ -566,7 +574,7 @@ __global__ void __launch_bounds__(256, 2) tern_lds_kernel(StreamArgs a, ExpertWe
       step(c, s0, s1);
       if (c + 1 < nch) step(c + 1, s1, s0);
     }
-    if (cb + r16 < n) {
+    if (r16 < kTlTok && cb + r16 < n) {
       const int col = row0 + cb + r16;
       if (NM == 2) {
         uint16_t* h = reinterpret_cast<uint16_t*>(out);
