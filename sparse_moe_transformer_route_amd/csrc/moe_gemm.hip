@@ -94,6 +94,13 @@ __device__ __forceinline__ void bare_barrier() {
 // eight rows read together by one fragment load fall on eight different bank groups.
 __device__ __forceinline__ int swz_key(int row) { return row & 7; }
 
+// Two floats to packed bf16 (round to nearest even, one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+
 // Calls f(integral_constant<int, T>) for T in the sequence, in order.
 template <int... T, class F>
 __device__ __forceinline__ void for_seq(std::integer_sequence<int, T...>, F&& f) {
@@ -297,11 +304,14 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
         for (int nb = 0; nb < kNB; ++nb)
           fb[s & 1][nb] = *reinterpret_cast<const uint4*>(Lb + fb_off + nb * kBlk * kRowBytes + frag_lo[s]);
       };
+      // operands in (weights, activations) order: the accumulators hold the transposed
+      // tile, so lane (r32, hf) has output row r32 and 4 consecutive columns per
+      // accumulator quad (see the epilogue)
       auto mfmas = [&](int s) {
 #pragma unroll
         for (int j = 0; j < NACT; ++j)
 #pragma unroll
-          for (int nb = 0; nb < kNB; ++nb) acc[j][nb] = mfma32x32x16(fa[s & 1][j], fb[s & 1][nb], acc[j][nb]);
+          for (int nb = 0; nb < kNB; ++nb) acc[j][nb] = mfma32x32x16(fb[s & 1][nb], fa[s & 1][j], acc[j][nb]);
       };
       // One step ks on activation slot UA = ks % 2 and weight slot UB = ks % BS. The
       // slots step ks-1 used were freed by the barrier that ended it; their next loads
@@ -380,27 +390,33 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
     bare_barrier();
 
     // Epilogue through LDS: the tile is written as 256-row x 64-column bf16 pieces of
-    // 32 KB (one ring slot each: sa0, sa1, sb0, sb1; 128 B per row; 16-byte chunk c of row r sits at
-    // c ^ 4*bit2(r), so the two lane halves of a write, 4 rows apart, hit different
-    // banks), then leaves with 16-byte stores of whole row segments. gate/up: piece wn
-    // holds h units nt*128 + 64 wn + [0, 64); down: piece 2 wn + nb/2 holds y columns
+    // 32 KB (one ring slot each: sa0, sa1, sb0, sb1; 128 B per row; 16-byte chunk c of
+    // row r sits at c ^ (r mod 8)), then leaves with 16-byte stores of whole row
+    // segments. Accumulator i of lane (r32, hf) is output row r32 of its 32-row block,
+    // column 8 (i / 4) + 4 hf + i % 4 of its 32-column block, so each quad of
+    // accumulators is 8 contiguous bytes: one 8-byte LDS write. gate/up: piece wn holds
+    // h units nt*128 + 64 wn + [0, 64); down: piece 2 wn + nb/2 holds y columns
     // nt*256 + 64 (2 wn + nb/2) + [0, 64).
 #pragma unroll
     for (int j = 0; j < kWaveBlocks; ++j) {
       const int rb = 2 * j + wm;
       if (rb >= nrb) continue;  // wave-uniform
+      const int row = rb * kBlk + r32;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        // 32x32 accumulator i of lane (r32, hf): row 8(i/4) + 4hf + i%4, column r32
-        const int row = rb * kBlk + 8 * (i >> 2) + 4 * hf + (i & 3);
+      for (int nb = 0; nb < (GATEUP ? kNB / 2 : kNB); ++nb) {
+        const int piece = GATEUP ? wn : 2 * wn + (nb >> 1);
+        uint8_t* const pb = piece == 0 ? sa0 : piece == 1 ? sa1 : piece == 2 ? sb0 : sb1;
 #pragma unroll
-        for (int nb = 0; nb < (GATEUP ? kNB / 2 : kNB); ++nb) {
-          const float v = GATEUP ? silu(acc[j][nb][i]) * acc[j][nb + kNB / 2][i] : acc[j][nb][i];
-          const int piece = GATEUP ? wn : 2 * wn + (nb >> 1);
-          const int pcol = GATEUP ? nb * 32 + r32 : (nb & 1) * 32 + r32;
-          const uint32_t off = row * 128 + ((((pcol >> 3) ^ (4 * hf)) << 4) | ((pcol & 7) * 2));
-          uint8_t* const pb = piece == 0 ? sa0 : piece == 1 ? sa1 : piece == 2 ? sb0 : sb1;
-          *reinterpret_cast<__bf16*>(pb + off) = (__bf16)v;
+        for (int qd = 0; qd < 4; ++qd) {
+          float v[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int i = 4 * qd + t;
+            v[t] = GATEUP ? silu(acc[j][nb][i]) * acc[j][nb + kNB / 2][i] : acc[j][nb][i];
+          }
+          const int chunk = GATEUP ? 4 * nb + qd : 4 * (nb & 1) + qd;  // 16-byte chunk of the piece row
+          const uint32_t off = row * 128 + ((chunk ^ (row & 7)) << 4) + 8 * hf;
+          *reinterpret_cast<uint2*>(pb + off) = make_uint2(pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3]));
         }
       }
     }
@@ -410,7 +426,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
     // another.
     const int ldc = GATEUP ? a.I : a.d;
     const int orow = tid >> 3, ch = tid & 7;
-    const uint32_t pl_off = (uint32_t)(orow * 128 + ((ch ^ (4 * ((orow >> 2) & 1))) << 4));
+    const uint32_t pl_off = (uint32_t)(orow * 128 + ((ch ^ (orow & 7)) << 4));
     uint16_t* const obase = (GATEUP ? h : y) + (size_t)(ebase + m0 + orow) * ldc + ch * 8;
 #pragma unroll
     for (int pc = 0; pc < (GATEUP ? 2 : 4); ++pc) {
@@ -419,7 +435,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
       const uint8_t* pbase = pc == 0 ? sa0 : pc == 1 ? sa1 : pc == 2 ? sb0 : sb1;
       uint4 v[kRowsMax / 32];
 #pragma unroll
-      for (int it = 0; it < kRowsMax / 32; ++it)  // row it*32 + orow: same swizzle bit as orow
+      for (int it = 0; it < kRowsMax / 32; ++it)  // row it*32 + orow: same swizzle as orow
         v[it] = *reinterpret_cast<const uint4*>(pbase + pl_off + it * 32 * 128);
 #pragma unroll
       for (int it = 0; it < kRowsMax / 32; ++it)
