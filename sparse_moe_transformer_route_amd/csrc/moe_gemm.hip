@@ -101,6 +101,13 @@ __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
+// silu(z) = z / (1 + e^-z) with the hardware exp2 and reciprocal (about 1 ulp each;
+// the result is rounded to bf16 right after). Large negative z gives -0, large
+// positive z gives z.
+__device__ __forceinline__ float silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504088896341f * z));
+}
+
 // Calls f(integral_constant<int, T>) for T in the sequence, in order.
 template <int... T, class F>
 __device__ __forceinline__ void for_seq(std::integer_sequence<int, T...>, F&& f) {
@@ -412,7 +419,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const int i = 4 * qd + t;
-            v[t] = GATEUP ? silu(acc[j][nb][i]) * acc[j][nb + kNB / 2][i] : acc[j][nb][i];
+            v[t] = GATEUP ? silu_fast(acc[j][nb][i]) * acc[j][nb + kNB / 2][i] : acc[j][nb][i];
           }
           const int chunk = GATEUP ? 4 * nb + qd : 4 * (nb & 1) + qd;  // 16-byte chunk of the piece row
           const uint32_t off = row * 128 + ((chunk ^ (row & 7)) << 4) + 8 * hf;
