@@ -90,9 +90,13 @@ __device__ __forceinline__ void bare_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// 16-byte chunk c (of 8) of a 128-byte row sits at physical chunk c ^ (row % 8): the
-// eight rows read together by one fragment load fall on eight different bank groups.
-__device__ __forceinline__ int swz_key(int row) { return row & 7; }
+// 16-byte chunk c (of 8) of a 128-byte row sits at physical chunk c ^ ((row / 2) % 8).
+// The LDS has 64 banks of 4 bytes and serves a 16-byte read 16 lanes at a time; the 16
+// rows of one such group fall pairwise (even, odd row) on the two 128-byte halves of
+// the banks, and the key gives each pair a different chunk: no conflicts. (A key of
+// row % 8 puts rows r and r + 8 on the same banks: every fragment read took twice
+// as long.)
+__device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
 
 // Two floats to packed bf16 (round to nearest even, one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
@@ -398,7 +402,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
 
     // Epilogue through LDS: the tile is written as 256-row x 64-column bf16 pieces of
     // 32 KB (one ring slot each: sa0, sa1, sb0, sb1; 128 B per row; 16-byte chunk c of
-    // row r sits at c ^ (r mod 8)), then leaves with 16-byte stores of whole row
+    // row r sits at c ^ swz_key(r)), then leaves with 16-byte stores of whole row
     // segments. Accumulator i of lane (r32, hf) is output row r32 of its 32-row block,
     // column 8 (i / 4) + 4 hf + i % 4 of its 32-column block, so each quad of
     // accumulators is 8 contiguous bytes: one 8-byte LDS write. gate/up: piece wn holds
@@ -422,7 +426,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
             v[t] = GATEUP ? silu_fast(acc[j][nb][i]) * acc[j][nb + kNB / 2][i] : acc[j][nb][i];
           }
           const int chunk = GATEUP ? 4 * nb + qd : 4 * (nb & 1) + qd;  // 16-byte chunk of the piece row
-          const uint32_t off = row * 128 + ((chunk ^ (row & 7)) << 4) + 8 * hf;
+          const uint32_t off = row * 128 + ((chunk ^ swz_key(row)) << 4) + 8 * hf;
           *reinterpret_cast<uint2*>(pb + off) = make_uint2(pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3]));
         }
       }
@@ -433,7 +437,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
     // another.
     const int ldc = GATEUP ? a.I : a.d;
     const int orow = tid >> 3, ch = tid & 7;
-    const uint32_t pl_off = (uint32_t)(orow * 128 + ((ch ^ (orow & 7)) << 4));
+    const uint32_t pl_off = (uint32_t)(orow * 128 + ((ch ^ swz_key(orow)) << 4));
     uint16_t* const obase = (GATEUP ? h : y) + (size_t)(ebase + m0 + orow) * ldc + ch * 8;
 #pragma unroll
     for (int pc = 0; pc < (GATEUP ? 2 : 4); ++pc) {

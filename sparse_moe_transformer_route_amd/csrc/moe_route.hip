@@ -86,8 +86,9 @@ __global__ void __launch_bounds__(64) route_logits_kernel(const uint16_t* __rest
 // 64 x-rows and 256 W_router rows (128 B per row, 40 KB) arrives in LDS through
 // direct global->LDS loads in which 8 consecutive lanes cover one row (whole cache
 // lines per lane quad: the address unit's fast case), then feeds 16x16x32 MFMAs
-// from LDS. Two ring slots; 16-byte chunk c of row r sits at c ^ (r mod 8), so the
-// 16 rows of a fragment read fall on distinct bank groups.
+// from LDS. Two ring slots; 16-byte chunk c of row r sits at c ^ ((r / 2) mod 8): the
+// LDS serves a 16-byte read 16 lanes at a time over 64 four-byte banks, and this key
+// puts the 16 rows of such a group on distinct bank groups.
 // Work w enumerates (slice, token tile, expert tile), expert tile fastest, and block
 // b runs work (b mod 8) * per + b / 8: XCD x (b mod 8) takes the x-th contiguous
 // eighth, so its workgroups share one or two slices of W_router in its L2.
@@ -121,12 +122,12 @@ __global__ void __launch_bounds__(256, 2) route_logits_lds_kernel(const uint16_t
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // load op i of thread tid: staged row (256 i + tid) / 8, physical chunk tid % 8
-  // holding logical chunk (tid % 8) ^ (row % 8); rows 0..63 are tokens, 64.. experts,
+  // holding logical chunk (tid % 8) ^ ((row / 2) % 8); rows 0..63 are tokens, 64.. experts,
   // both clamped to the last valid row (never stored)
   const uint16_t* src[kLgOps];
 #pragma unroll
   for (int i = 0; i < kLgOps; ++i) {
-    const int row = (256 * i + tid) >> 3, lc = (tid & 7) ^ (row & 7);
+    const int row = (256 * i + tid) >> 3, lc = (tid & 7) ^ ((row >> 1) & 7);
     const uint16_t* base = row < kLgTok ? x + (size_t)min(t0 + row, T - 1) * d
                                         : wr + (size_t)min(e0 + row - kLgTok, E - 1) * d;
     src[i] = base + (size_t)z * kc + 8 * lc;
@@ -145,7 +146,7 @@ __global__ void __launch_bounds__(256, 2) route_logits_lds_kernel(const uint16_t
   const int r16 = lane & 15, g = lane >> 4;
   auto frag = [&](const uint8_t* slot, int r0, int s) {
     const int row = r0 + r16;
-    return *reinterpret_cast<const uint4*>(slot + row * 128 + (((4 * s + g) ^ (row & 7)) << 4));
+    return *reinterpret_cast<const uint4*>(slot + row * 128 + (((4 * s + g) ^ ((row >> 1) & 7)) << 4));
   };
 
   f32x4 acc[4][4];
