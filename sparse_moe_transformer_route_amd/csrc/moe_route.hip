@@ -259,10 +259,12 @@ __global__ void __launch_bounds__(1024) route_select_kernel(const float* __restr
     for (int r = 0; r < R; ++r) {
       const int e = lane + 64 * r;
       if (e < E) {
-        // all partial loads issued before the (fixed-order) sum
+        // all partial loads issued before the (fixed-order) sum: unconditional, slices
+        // past ks re-read the last one (cache hits) and are not added, so no load waits
+        // behind a branch
         float pz[kMaxSplit];
 #pragma unroll
-        for (int z = 0; z < kMaxSplit; ++z) pz[z] = z < ks ? part[(size_t)z * TE + (size_t)t * E + e] : 0.f;
+        for (int z = 0; z < kMaxSplit; ++z) pz[z] = part[(size_t)min(z, ks - 1) * TE + (size_t)t * E + e];
         float sum = 0.f;
 #pragma unroll
         for (int z = 0; z < kMaxSplit; ++z)
