@@ -160,10 +160,13 @@ def run_config(name, args, hi, hm, torch, weights=None):
             alg = (touched + 1) * unit
             per_unit = f"{unit} B of bf16 gate+up weights per touched expert (routed + shared)"
         sec = dom_ms * 1e-3
+        # ternary weights with d and I multiples of 512 run in the LDS-staged kernel
+        tern_lds = cfg.ternary and d % 512 == 0 and I % 512 == 0
+        key = "ternary_gateup" if tern_lds else "stream_gateup"
         roof = {"bound": "hbm", "achieved": alg / sec / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                "frac": alg / sec / PEAK_HBM, "traffic": traffic_for(f"stream_gateup/{name}", touched + 1),
-                "kernel": "stream_gateup_kernel", "per_unit": per_unit, "units_per_launch": touched + 1,
-                "kernel_ms": dom_ms}
+                "frac": alg / sec / PEAK_HBM, "traffic": traffic_for(f"{key}/{name}", touched + 1),
+                "kernel": "tern_lds_kernel<2>" if tern_lds else "stream_gateup_kernel", "per_unit": per_unit,
+                "units_per_launch": touched + 1, "kernel_ms": dom_ms}
         # whole-layer HBM fraction: every touched expert's weights once + router + x/out
         if cfg.ternary:
             layer_bytes = touched * (3 * I * (d // 128 * 5 * 4) + 2 * I * 2 + d * 2) + 3 * I * d * 2
