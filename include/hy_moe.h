@@ -77,7 +77,9 @@ typedef enum {
 typedef enum {
   HY_MOE_PATH_AUTO = 0,
   HY_MOE_PATH_STREAM = 1,  /* weight-streaming kernels: each touched expert's weights read once per
-                              32 rows; meant for decode-sized batches */
+                              pass of up to 16 of its tokens (4 in the LDS-staged Sherry kernels,
+                              used when d and I are multiples of 512); meant for decode-sized
+                              batches */
   HY_MOE_PATH_GROUPED = 2  /* LDS-tiled grouped GEMM on bf16 MFMA; prefill-sized batches (bf16 only) */
 } hy_moe_path;
 
