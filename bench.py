@@ -20,6 +20,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -66,7 +67,12 @@ class Events:
 
 
 def source_digest(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """sha256 (first 16 hex digits) of a C/HIP source with comments and whitespace
+    removed: the code that the counters were taken on, not its commentary."""
+    text = open(path, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256("".join(text.split()).encode()).hexdigest()[:16]
 
 
 def traffic_for(kernel_key, units):

@@ -22,16 +22,17 @@
 // (128 B each: one cache line per row, so the vector L1's limited number of
 // outstanding misses carries twice the bytes of 64-byte pieces) arrive in LDS by
 // direct global->LDS loads into two rings of 32 KB slots: 2 activation slots and 3
-// weight slots (all 160 KB: the weights come from HBM and get one more step of lead
-// than the activations, mostly L2 hits). 16-byte
-// chunks are XOR-swizzled by row so the MFMA fragment reads are conflict free.
-// Activation rows are gathered from x through the permutation (gate/up) or read from h
-// (down). Only LDS-bound loads are in flight in the k loop, so the vector-memory wait
-// is an explicit count. A step runs 4 MFMA groups (k = 16 each), each group's
-// fragments read while the previous group's MFMAs run; at the end of the step one bare
-// barrier certifies that the next step has landed and that this step's slots are
-// free, which then receive the activations 2 steps ahead and the weights BS steps
-// ahead (clamped to the last step, so every step issues the same loads).
+// weight slots (all 160 KB: the weights come from HBM and get more lead than the
+// activations, mostly L2 hits). 16-byte chunks are XOR-swizzled by row so the MFMA
+// fragment reads are conflict free. Activation rows are gathered from x through the
+// permutation (gate/up) or read from h (down). Only LDS-bound loads are in flight in
+// the k loop, so the vector-memory wait is an explicit count. A step runs 4 MFMA
+// groups (k = 16 each), each group's fragments read while the previous group's MFMAs
+// run; at the end of the step one bare barrier certifies that the next step has
+// landed and that this step's slots are free. Their next loads (the activations of
+// the step after next, the weights of the step after that) go out in 4-op pieces
+// between the following step's MFMA groups, so the address unit works through them
+// while MFMAs run.
 // Persistent schedule: items are split into 8 contiguous ranges, one per XCD
 // (workgroup i runs on XCD i mod 8) and claimed in order through per-XCD counters, so
 // workgroups that finish early take more work; within an expert, items are ordered so
