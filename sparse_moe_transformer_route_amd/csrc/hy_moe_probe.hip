@@ -93,7 +93,7 @@ float time_launch(hipStream_t s, F&& launch) {
   hipEvent_t e0, e1;
   if (hipEventCreate(&e0) != hipSuccess) return -1.f;
   if (hipEventCreate(&e1) != hipSuccess) {
-    hipEventDestroy(e0);
+    (void)hipEventDestroy(e0);
     return -1.f;
   }
   float ms = -1.f;
@@ -103,8 +103,8 @@ float time_launch(hipStream_t s, F&& launch) {
         hipEventElapsedTime(&ms, e0, e1) != hipSuccess)
       ms = -1.f;
   }
-  hipEventDestroy(e0);
-  hipEventDestroy(e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
   return ms;
 }
 

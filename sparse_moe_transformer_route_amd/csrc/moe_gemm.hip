@@ -53,7 +53,6 @@ constexpr int kNB = 4;          // 32-column blocks per wave (2 N-waves x 4 x 32
 constexpr int kBK = 64;         // k per step (four 32x32x16 MFMAs deep); K % (2 kBK) == 0
 constexpr int kSub = kBK / 16;  // MFMA groups per step
 constexpr int kRowBytes = kBK * 2;               // 128 B per row per step
-constexpr int kChunks = kRowBytes / 16;          // 8 chunks of 16 B per row
 constexpr int kHalf = kRowsMax * kRowBytes;      // 32 KB: one operand's ring slot
 constexpr int kDma = kHalf / 16 / kThreads;      // direct-to-LDS ops per operand per thread per step (8)
 
