@@ -42,16 +42,30 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(const YT* __re
   if (c >= d) return;
   const int32_t* pp = pos + (size_t)t * k;
   const float* ww = topk_w + (size_t)t * k;
+  float s[8];  // the shared expert's row, loaded first (added last)
+  load8(y + (size_t)(Tk + t) * d + c, s);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
+  // slots in groups of 4 with all 4 rows in flight before they are added, then the
+  // remaining slots one by one; ascending slot order throughout
+  int j = 0;
+  for (; j + 4 <= k; j += 4) {
+    float v[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load8(y + (size_t)pp[j + u] * d + c, v[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float wj = ww[j + u];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wj, v[u][i], acc[i]);
+    }
+  }
+  for (; j < k; ++j) {
     const float wj = ww[j];
     float v[8];
     load8(y + (size_t)pp[j] * d + c, v);
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wj, v[i], acc[i]);
   }
-  float s[8];
-  load8(y + (size_t)(Tk + t) * d + c, s);
   uint4 o;
   o.x = pack_bf16x2(acc[0] + s[0], acc[1] + s[1]);
   o.y = pack_bf16x2(acc[2] + s[2], acc[3] + s[3]);
