@@ -324,7 +324,8 @@ def main():
     peaks = {"mfma_bf16_tflops": hm.probe_mfma_bf16(ops), "hbm_read_gbs": hm.probe_hbm_read(read_buf),
              "hbm_read_bytes": read_buf.numel() * read_buf.element_size(),
              "how": "hy_moe_probe_mfma_bf16 (32x32x16 bf16 MFMAs, 4 workgroups per CU, random N(0,1) operands, "
-                    "~40 ms) and hy_moe_probe_hbm_read (one timed pass of 16-byte loads after an untimed one)"}
+                    "~40 ms) and hy_moe_probe_hbm_read (best of three timed streaming passes of 16-byte loads after "
+                    "an untimed one)"}
     del read_buf
     log(f"[bench] measured peaks: {peaks['mfma_bf16_tflops']:.0f} TFLOP/s bf16 MFMA, "
         f"{peaks['hbm_read_gbs']:.0f} GB/s HBM read")

@@ -190,8 +190,8 @@ int hy_moe_sherry_pack_host(const int8_t* tern, int64_t rows, int64_t cols, uint
  *   operand bit activity). Writes TFLOP/s (2 flop per multiply-add) to *tflops
  *   (HOST).
  * hy_moe_probe_hbm_read: reads buf (DEVICE, 16-byte aligned, `bytes` >= 16; use
- *   much more than the 256 MB last-level cache) once untimed, then once timed with
- *   16-byte loads. Writes GB/s (1e9 B/s) to *gbps (HOST).
+ *   much more than the 256 MB last-level cache) once untimed, then three times timed
+ *   with 16-byte loads. Writes the best pass's GB/s (1e9 B/s) to *gbps (HOST).
  */
 #define HY_MOE_PROBE_OPERAND_BYTES 65536
 int hy_moe_probe_mfma_bf16(const void* operands, size_t operand_bytes, float* tflops, void* stream);
