@@ -114,6 +114,26 @@ __device__ __forceinline__ float silu_fast(float z) {
 
 // Calls f(integral_constant<int, T>) for T in the sequence, in order.
 template <int... T, class F>
+__device__ __forceinline__ void for_seq(std::integer_sequence<int, T...>, F&& f);
+
+// Scheduling pattern for one MFMA group's region: MFMA, LDS read, MFMA, LDS read, ...,
+// then MFMA, global load, ..., then the rest, so the reads and loads issue while the
+// MFMA pipe is busy instead of ahead of the group's first MFMA.
+template <int NMFMA, int NREAD, int NVMEM>
+__device__ __forceinline__ void interleave_group() {
+  constexpr int N = NMFMA > NREAD + NVMEM ? NMFMA : NREAD + NVMEM;
+  for_seq(std::make_integer_sequence<int, N>{}, [&](auto i_tag) {
+    constexpr int I = decltype(i_tag)::value;
+    if constexpr (I < NMFMA) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    if constexpr (I < NREAD)
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    else if constexpr (I - NREAD < NVMEM)
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // vector memory
+  });
+}
+
+// Calls f(integral_constant<int, T>) for T in the sequence, in order.
+template <int... T, class F>
 __device__ __forceinline__ void for_seq(std::integer_sequence<int, T...>, F&& f) {
   (f(std::integral_constant<int, T>{}), ...);
 }
@@ -346,8 +366,9 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
           if constexpr (S == 1 && PA) issue_a(ks + 1, sa[UA ^ 1], CH{}, CF{});
           if constexpr (S == 2 && PB) issue_b(ks + 2, sb[(UB + 2) % BS], C0{}, CH{});
           if constexpr (S == 3 && PB) issue_b(ks + 2, sb[(UB + 2) % BS], CH{}, CF{});
-          __builtin_amdgcn_sched_barrier(0);
           mfmas(S - 1);
+          constexpr int NV = ((S == 1 && PA) || (S >= 2 && PB)) ? kDma / 2 : 0;
+          interleave_group<NACT * kNB, NACT + kNB, NV>();
           __builtin_amdgcn_sched_barrier(0);
         });
         if constexpr (NEXT) {
@@ -357,12 +378,14 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
           bare_barrier();  // everyone's step ks+1 landed; this step's slots are free
           if constexpr (PB) issue_a(ks + 2, sa[UA], C0{}, CH{});
           read_frags(sa[UA ^ 1], sb[(UB + 1) % BS], 0);
+          mfmas(kSub - 1);
+          interleave_group<NACT * kNB, NACT + kNB, PB ? kDma / 2 : 0>();
         } else {
           // the last step: claim the next item (read after the k loop)
           if (threadIdx.x == 0) own_ticket = atomicAdd(&counters[xcd], 1);
+          __builtin_amdgcn_sched_barrier(0);
+          mfmas(kSub - 1);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(kSub - 1);
         __builtin_amdgcn_sched_barrier(0);
       };
       // whole periods of P = 6 steps (slots repeat with period 6), then the last R steps
