@@ -116,19 +116,20 @@ __device__ __forceinline__ float silu_fast(float z) {
 template <int... T, class F>
 __device__ __forceinline__ void for_seq(std::integer_sequence<int, T...>, F&& f);
 
-// Scheduling pattern for one MFMA group's region: MFMA, LDS read, MFMA, LDS read, ...,
-// then MFMA, global load, ..., then the rest, so the reads and loads issue while the
-// MFMA pipe is busy instead of ahead of the group's first MFMA.
+// Scheduling pattern for one MFMA group's region: MFMA, global load, MFMA, global
+// load, ..., then MFMA, LDS read, ..., then the rest, so the loads and reads issue
+// while the MFMA pipe is busy instead of ahead of the group's first MFMA (loads first:
+// measured ~1% faster than reads first; spreading them evenly was slower).
 template <int NMFMA, int NREAD, int NVMEM>
 __device__ __forceinline__ void interleave_group() {
   constexpr int N = NMFMA > NREAD + NVMEM ? NMFMA : NREAD + NVMEM;
   for_seq(std::make_integer_sequence<int, N>{}, [&](auto i_tag) {
     constexpr int I = decltype(i_tag)::value;
     if constexpr (I < NMFMA) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    if constexpr (I < NREAD)
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-    else if constexpr (I - NREAD < NVMEM)
+    if constexpr (I < NVMEM)
       __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // vector memory
+    else if constexpr (I - NVMEM < NREAD)
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
   });
 }
 
