@@ -92,15 +92,29 @@ def traffic_for(kernel_key, units):
     return rec["bytes_per_launch"]
 
 
+WARMUP_MIN_S = 0.5  # default warm-up length: the shader clock climbs for ~60 ms of load after idle
+
+
 def time_layer(hm, torch, inp, k, ws, steps, warmup, dominant):
-    """Times `steps` forwards. Returns (total ms by the host clock around the syncs,
+    """Times `steps` forwards after `warmup` untimed ones (None: at least 5 steps and
+    WARMUP_MIN_S seconds of them). Returns (total ms by the host clock around the syncs,
     mean ms of kernel `dominant` from events recorded around it in those same steps,
-    mean ms per kernel from a separate pass of stage events after the timed region).
-    Only the dominant kernel's two events are recorded while timing: an event between
-    every kernel would add its own gaps to the step."""
+    mean ms per kernel from a separate pass of stage events after the timed region,
+    warm-up steps run). Only the dominant kernel's two events are recorded while timing:
+    an event between every kernel would add its own gaps to the step."""
     nk = len(hm.KERNELS)
-    for _ in range(warmup):
-        hm.forward_layer(inp, k, workspace=ws)
+    done = 0
+    t_w = time.perf_counter()
+    if warmup is not None:
+        for _ in range(warmup):
+            hm.forward_layer(inp, k, workspace=ws)
+        done = warmup
+    else:
+        while done < 5 or time.perf_counter() - t_w < WARMUP_MIN_S:
+            for _ in range(5):
+                hm.forward_layer(inp, k, workspace=ws)
+            done += 5
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     ev = Events(2 * steps)
     arrays = []
@@ -127,7 +141,7 @@ def time_layer(hm, torch, inp, k, ws, steps, warmup, dominant):
         for j in range(nk):
             per[j] += ev.ms(i * (nk + 1) + j, i * (nk + 1) + j + 1) / nb
     ev.close()
-    return total_ms, dom_ms, dict(zip(hm.KERNELS, per))
+    return total_ms, dom_ms, dict(zip(hm.KERNELS, per)), done
 
 
 def run_config(name, args, hi, hm, torch, weights=None):
@@ -145,7 +159,7 @@ def run_config(name, args, hi, hm, torch, weights=None):
     ws = hm.alloc_workspace(cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, fmt, device=dev)
     steps = args.steps
     dominant = hm.KERNELS.index("expert_gateup")
-    total_ms, dom_ms, kern = time_layer(hm, torch, inp, cfg.k, ws, steps, args.warmup, dominant)
+    total_ms, dom_ms, kern, warmup_done = time_layer(hm, torch, inp, cfg.k, ws, steps, args.warmup, dominant)
     ms = total_ms / steps
     routing = hm.forward_layer(inp, cfg.k, want_routing=True, workspace=ws)
     torch.cuda.synchronize()
@@ -192,7 +206,8 @@ def run_config(name, args, hi, hm, torch, weights=None):
         layer = {"flop": flops, "mfma_frac": flops / (ms * 1e-3) / PEAK_BF16}
     roof["kernel_source_sha256_16"] = source_digest(os.path.join(ROOT, kernel_file))
     return {"cfg": cfg, "inp": inp, "ms": ms, "tokens_per_s": cfg.T / (ms * 1e-3), "kernels_ms": kern,
-            "roofline": roof, "layer": layer, "touched": touched, "counts": counts, "routing": routing}
+            "roofline": roof, "layer": layer, "touched": touched, "counts": counts, "routing": routing,
+            "warmup": warmup_done}
 
 
 def cpu_baseline(cfg, hi, torch, inp, routing, budget_s):
@@ -265,7 +280,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before the timed ones (default: at least 5 and %.1f s of them)" % WARMUP_MIN_S)
     ap.add_argument("--config", default="decode", choices=["tiny", "decode", "prefill", "skewed", "ternary"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the T=8192 measurement")
@@ -274,8 +290,8 @@ def main():
                     help="only run 3 device-to-device copies of this many GiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no multi-GPU "
-              f"path: the layer is sharded by expert only in design)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer has no multi-GPU "
+              f"path: sharding by expert is designed, not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -310,6 +326,7 @@ def main():
         pre = run_config("prefill", pre_args, hi, hm, torch, shared_weights)
         log(f"[bench] prefill: {pre['ms']:.3f} ms/step, {pre['tokens_per_s']:.0f} tokens/s")
         extra["prefill"] = {"workload": "prefill T=8192 d=6144 E=256 k=8 I=2048 bf16", "ms_per_step": pre["ms"],
+                            "steps": pre_args.steps, "warmup": pre["warmup"],
                             "tokens_per_s": pre["tokens_per_s"], "layer_mfma_frac": pre["layer"]["mfma_frac"],
                             "roofline": pre["roofline"], "kernels_ms": pre["kernels_ms"]}
         del pre
@@ -344,7 +361,7 @@ def main():
     c = main_res["cfg"]
     line = {
         "metric": METRIC, "value": main_res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_res["ms"], "higher_is_better": True,
+        "steps": args.steps, "warmup": main_res["warmup"], "ms_per_step": main_res["ms"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
         "dtype": "sherry-ternary+bf16" if c.ternary else "bf16", "data": "synthetic",
         "config": {"workload": f"{c.name} MoE FFN layer T={c.T} d={c.d} E={c.E} top-{c.k} + 1 shared I={c.I}"

@@ -549,33 +549,14 @@ __global__ void __launch_bounds__(256, kTlWgPerCu) tern_lds_kernel(StreamArgs a,
         for (int m = 0; m < 4; ++m)
           xf[m] = *reinterpret_cast<const uint4*>(slot + kTlCodeBytes + tk * kTlTokBytes +
                                                   16 * ((16 * b + 4 * g + m) ^ tk));
-        // the block's four code windows first, then its 32 table lookups issue up to 6
-        // MFMAs ahead of use (12 up front, then 2 per MFMA; the LDS counter allows 15 in
-        // flight), which covers the LDS latency: ~7% faster than the compiler's 1-MFMA lead
-        uint64_t vv[4];
 #pragma unroll
         for (int qb = 0; qb < 4; ++qb) {
           const uint32_t* cw = reinterpret_cast<const uint32_t*>(slot + crow(qb) * kTlRowBytes + 20 * b) + w0;
           const uint32_t c2[2] = {cw[0], cw[1]};
-          vv[qb] = tern_window(c2, g);
+          const uint64_t v = tern_window(c2, g);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) acc[qb] = mfma16x16x32(tern_operand(v, m, lut), xf[m], acc[qb]);
         }
-        uint4 op[4][4];
-#pragma unroll
-        for (int qb = 0; qb < 4; ++qb)
-#pragma unroll
-          for (int m = 0; m < 4; ++m) op[qb][m] = tern_operand(vv[qb], m, lut);
-#pragma unroll
-        for (int qb = 0; qb < 4; ++qb)
-#pragma unroll
-          for (int m = 0; m < 4; ++m) acc[qb] = mfma16x16x32(op[qb][m], xf[m], acc[qb]);
-        __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // LDS reads
-#pragma unroll
-        for (int i = 0; i < 10; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
-        __builtin_amdgcn_sched_barrier(0);
       }
     };
     // chunk c: its loads (issued a chunk earlier) landed everywhere and every wave is
