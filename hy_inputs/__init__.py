@@ -62,6 +62,8 @@ CONFIGS = {
     "prefill": LayerConfig("prefill", T=8192, d=6144, E=256, k=8, I=2048),
     "skewed": LayerConfig("skewed", T=4096, d=6144, E=256, k=8, I=2048, zipf_s=1.2),
     "ternary": LayerConfig("ternary", T=32, d=6144, E=256, k=8, I=2048, ternary=True),
+    # the ternary experts at a prefill-sized batch (grouped GEMM on decoded codes)
+    "ternary_prefill": LayerConfig("ternary_prefill", T=8192, d=6144, E=256, k=8, I=2048, ternary=True),
 }
 
 

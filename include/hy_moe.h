@@ -80,7 +80,10 @@ typedef enum {
                               pass of up to 16 of its tokens (4 in the LDS-staged Sherry kernels,
                               used when d and I are multiples of 512); meant for decode-sized
                               batches */
-  HY_MOE_PATH_GROUPED = 2  /* LDS-tiled grouped GEMM on bf16 MFMA; prefill-sized batches (bf16 only) */
+  HY_MOE_PATH_GROUPED = 2  /* LDS-tiled grouped GEMM on bf16 MFMA; prefill-sized batches. Sherry
+                              codes are decoded to bf16 +1/0/-1 operands on the fly (the row scales
+                              are applied to the sums); the bf16 shared expert runs in its own
+                              launches of the bf16 kernel */
 } hy_moe_path;
 
 /*

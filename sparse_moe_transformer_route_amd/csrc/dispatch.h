@@ -48,7 +48,7 @@ __device__ __forceinline__ void write_tiles(int e, int n, int bm, int first, int
 // (blockDim >= E) must call. Writes offs[0..E+1], the touched-expert list (shared
 // expert first, then routed experts with rows in ascending order), the grouped-GEMM
 // M tiles (routed experts ascending, then the shared expert) and meta {touched
-// count, tile count}; returns expert e's first row.
+// count, tile count, routed tile count}; returns expert e's first row.
 __device__ __forceinline__ int build_work_lists(int cnt, int T, int E, int k, int bm, int* wsum,
                                                 int32_t* __restrict__ offs, int32_t* __restrict__ meta,
                                                 int32_t* __restrict__ touched, int4* __restrict__ tiles,
@@ -82,6 +82,7 @@ __device__ __forceinline__ int build_work_lists(int cnt, int T, int E, int k, in
     write_tiles(E, T, bm, routed_tiles, tiles);
     meta[0] = ntouched + 1;
     meta[1] = routed_tiles + (T + bm - 1) / bm;
+    meta[2] = routed_tiles;
   }
   // the grouped GEMM's work counters start at zero on every forward
   if (e >= kMetaSched && e < kMetaInts) meta[e] = 0;

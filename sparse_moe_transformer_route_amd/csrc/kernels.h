@@ -19,7 +19,7 @@ struct Marks {
 };
 
 // Per-call device state carved from the workspace.
-constexpr int kMetaInts = 32;
+constexpr int kMetaInts = 64;
 constexpr int kMetaSched = 16;  // first grouped-GEMM work counter in meta
 
 struct Plan {
@@ -38,7 +38,9 @@ struct Plan {
   int32_t* blk_base;         // [nblk][E] first row of (block, expert)
   int32_t* offs;             // [E+2] row offsets, expert E = shared
   int32_t* meta;             // [kMetaInts]: [0] touched experts incl. shared, [1] grouped-GEMM M tiles,
-                             // [16..23] gate/up and [24..31] down work counters, one per XCD
+                             // [2] routed experts' M tiles (the shared expert's follow), [16..23] gate/up and
+                             // [24..31] down work counters, one per XCD; [32..47] the same for a launch over
+                             // the shared expert's tiles alone
   int32_t* touched;          // [E+1] touched experts: shared (E) first, then routed ascending
   int4* tiles;               // [max_tiles] {expert, first row within expert, rows, expert's first tile}
   int32_t* perm_src;         // [T*k]

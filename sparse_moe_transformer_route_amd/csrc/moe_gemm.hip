@@ -55,6 +55,15 @@ constexpr int kSub = kBK / 16;  // MFMA groups per step
 constexpr int kRowBytes = kBK * 2;               // 128 B per row per step
 constexpr int kHalf = kRowsMax * kRowBytes;      // 32 KB: one operand's ring slot
 constexpr int kDma = kHalf / 16 / kThreads;      // direct-to-LDS ops per operand per thread per step (8)
+// Sherry ternary weights: a row's 64 weights of a k step are 16 five-bit codes (10
+// bytes at byte 10 ks of the row); each row gets a 16-byte line of a 4 KB code slot
+// holding the 3 words from byte 4 floor(10 ks / 4) (the codes start at bit 16 (ks % 2)
+// of them), loaded with 4 one-word direct-to-LDS ops per thread per step.
+constexpr int kCodePitch = 16;
+constexpr int kCodeSlot = kRowsMax * kCodePitch;  // 4 KB
+constexpr int kCodeOps = kCodeSlot / 4 / kThreads;  // 4
+constexpr int kScaleBytes = 512;                    // an item's 256 row scales (bf16)
+
 
 int grouped_gemm_bm() { return kRowsMax; }
 
@@ -62,9 +71,11 @@ struct GemmArgs {
   const uint16_t* x;
   const int32_t* perm_src;
   const int32_t* offs;
-  int32_t* meta;  // [1] M tiles; [kMetaSched..] per-XCD work counters, zeroed by the routing kernels
+  int32_t* meta;  // [1] M tiles, [2] routed M tiles; [kMetaSched..] per-XCD work counters, zeroed by the
+                  // routing kernels
   const int4* tiles;
   int Tk, k, d, I, E;
+  int sel;  // M tiles to run: 0 every one, 1 the routed experts', 2 the shared expert's
 };
 
 #define HY_LDS(p) ((__attribute__((address_space(3))) void*)(p))
@@ -116,6 +127,21 @@ __device__ __forceinline__ float silu_fast(float z) {
 template <int... T, class F>
 __device__ __forceinline__ void for_seq(std::integer_sequence<int, T...>, F&& f);
 
+// The 5-bit code at bit P of a 3-word window (P + 5 <= 96).
+template <int P>
+__device__ __forceinline__ uint32_t code5(const uint32_t (&w)[3]) {
+  constexpr int W = P / 32, O = P % 32;
+  static_assert(P >= 0 && P + 5 <= 96, "code position");
+  if constexpr (O <= 27)
+    return (w[W] >> O) & 31u;
+  else
+    return __builtin_amdgcn_alignbit(w[W + 1], w[W], O) & 31u;
+}
+
+// bf16 pair to floats.
+__device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
 // Scheduling pattern for one MFMA group's region: MFMA, global load, MFMA, global
 // load, ..., then MFMA, LDS read, ..., then the rest, so the loads and reads issue
 // while the MFMA pipe is busy instead of ahead of the group's first MFMA (loads first:
@@ -141,28 +167,78 @@ __device__ __forceinline__ void for_seq(std::integer_sequence<int, T...>, F&& f)
 
 // TAILR = (K / kBK) mod 6 (0, 2 or 4: K is a multiple of 128): the k loop runs whole
 // periods of the 2 x 3 slot pattern and ends with a tail of that many steps.
-template <bool GATEUP, int TAILR>
+// TERN: routed experts' weights are Sherry ternary codes with bf16 row scales (the
+// shared expert's tiles run in the bf16 kernel); each lane decodes the codes of its
+// B fragments through a 32-entry LDS table into bf16 +1/0/-1, and the scales are
+// applied in the epilogue.
+template <bool GATEUP, int TAILR, bool TERN>
 __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, ExpertWeights w,
                                                                    uint16_t* __restrict__ h,
                                                                    uint16_t* __restrict__ y) {
-  constexpr int BS = 3;  // weight ring slots
-  __shared__ __attribute__((aligned(16))) uint8_t sa0[kHalf];
-  __shared__ __attribute__((aligned(16))) uint8_t sa1[kHalf];
-  __shared__ __attribute__((aligned(16))) uint8_t sb0[kHalf];
-  __shared__ __attribute__((aligned(16))) uint8_t sb1[kHalf];
-  __shared__ __attribute__((aligned(16))) uint8_t sb2[kHalf];
+  constexpr int BS = 3;                          // weight (or code) ring slots
+  constexpr int kBOps = TERN ? kCodeOps : kDma;  // weight-side load ops per thread per step
+  // Separate LDS arrays rather than one carved buffer: the compiler tells direct-to-LDS
+  // loads and LDS reads of different arrays apart; within one array it would wait for
+  // every such load in flight before each LDS read.
+  uint8_t *sa0, *sa1, *sb0, *sb1;  // activation slots; sb0, sb1: epilogue pieces 2 and 3
+  uint8_t* sr[3];                  // weight (bf16) or code (ternary) ring slots
+  uint2* lut = nullptr;            // ternary: the code table
+  uint8_t* ssc = nullptr;          // ternary: the item's row scales
+  if constexpr (TERN) {
+    __shared__ __attribute__((aligned(16))) uint8_t ta0[kHalf];
+    __shared__ __attribute__((aligned(16))) uint8_t ta1[kHalf];
+    __shared__ __attribute__((aligned(16))) uint8_t te0[GATEUP ? 16 : kHalf];  // the down epilogue only
+    __shared__ __attribute__((aligned(16))) uint8_t te1[GATEUP ? 16 : kHalf];
+    __shared__ __attribute__((aligned(16))) uint8_t tc0[kCodeSlot];
+    __shared__ __attribute__((aligned(16))) uint8_t tc1[kCodeSlot];
+    __shared__ __attribute__((aligned(16))) uint8_t tc2[kCodeSlot];
+    __shared__ __attribute__((aligned(16))) uint8_t tsc[kScaleBytes];
+    __shared__ uint2 tlut[32];
+    sa0 = ta0, sa1 = ta1, sb0 = te0, sb1 = te1;
+    sr[0] = tc0, sr[1] = tc1, sr[2] = tc2;
+    lut = tlut, ssc = tsc;
+  } else {
+    __shared__ __attribute__((aligned(16))) uint8_t ba0[kHalf];
+    __shared__ __attribute__((aligned(16))) uint8_t ba1[kHalf];
+    __shared__ __attribute__((aligned(16))) uint8_t bb0[kHalf];
+    __shared__ __attribute__((aligned(16))) uint8_t bb1[kHalf];
+    __shared__ __attribute__((aligned(16))) uint8_t bb2[kHalf];
+    sa0 = ba0, sa1 = ba1, sb0 = bb0, sb1 = bb1;
+    sr[0] = bb0, sr[1] = bb1, sr[2] = bb2;
+  }
   uint8_t* const sa[2] = {sa0, sa1};
-  uint8_t* const sb[3] = {sb0, sb1, sb2};
+  uint8_t* const* const sb = sr;
+  if constexpr (TERN) {
+    // code -> four bf16 values: bits 0-1 the position of the zero, bits 2-4 the signs
+    // of the other three in order (1 = negative)
+    const int c = threadIdx.x;
+    if (c < 32) {
+      uint32_t v[4];
+      int nz = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (q == (c & 3)) {
+          v[q] = 0u;
+        } else {
+          v[q] = ((c >> (2 + nz)) & 1) ? 0xBF80u : 0x3F80u;
+          ++nz;
+        }
+      }
+      lut[c] = make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
+    }
+  }
   // the claimed item is handed to the workgroup through the first activation slot,
   // idle between items
   int* const next_item = reinterpret_cast<int*>(sa0);
 
   const int K = GATEUP ? a.d : a.I;
   const int NT = GATEUP ? a.I / (kRowsMax / 2) : (a.d + kRowsMax - 1) / kRowsMax;
-  const int total = a.meta[1] * NT;
+  const int t_lo = a.sel == 2 ? a.meta[2] : 0;  // this launch's M tiles [t_lo, t_hi)
+  const int t_hi = a.sel == 1 ? a.meta[2] : a.meta[1];
+  const int total = (t_hi - t_lo) * NT;
   const int xcd = blockIdx.x & 7;
   const int per = (total + 7) >> 3;
-  int32_t* const counters = a.meta + kMetaSched + (GATEUP ? 0 : 8);
+  int32_t* const counters = a.meta + kMetaSched + (GATEUP ? 0 : 8) + (a.sel == 2 ? 16 : 0);
   // Items are split into 8 contiguous ranges, one per XCD; a workgroup takes the next
   // item of its own XCD's range (so the items in flight on an XCD are neighbours), and
   // once that range is used up, the next unclaimed item of another XCD's range.
@@ -196,9 +272,10 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
   for (;;) {
     if (threadIdx.x == 0) *next_item = claimed;
     __syncthreads();
-    const int item = __builtin_amdgcn_readfirstlane(*next_item);  // uniform: kept scalar
+    const int claim = __builtin_amdgcn_readfirstlane(*next_item);  // uniform: kept scalar
     __syncthreads();  // everyone has read it before the slot is loaded
-    if (item < 0) break;
+    if (claim < 0) break;
+    const int item = claim + t_lo * NT;
     // The thread index is made opaque once per item so that per-lane address math is
     // redone per item (a few ALU ops) rather than hoisted out of the item loop, where it
     // would be spilled across the k loop and reloaded with full vector-memory waits.
@@ -280,6 +357,47 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
         boff[i] = ((uint32_t)(min(nt * kRowsMax + row, a.d - 1) - nt * kRowsMax) * (uint32_t)a.I + 8 * lc) * 2u;
       }
     }
+    // Ternary codes: op i of a thread loads word min(lane % 4, 2) of the step's window of
+    // tile row 64 i + 16 wv + lane / 4 (gate/up: the rows of quarter i, as above; down:
+    // output columns clamped past d) into byte 16 row + 4 (lane % 4) of the code slot.
+    const char* cbase[kCodeOps];  // workgroup-uniform
+    uint32_t coff[kCodeOps];
+    if constexpr (TERN) {
+      const uint32_t rw = (uint32_t)(K / 128 * 20);  // code bytes per weight row
+      const int rr = 16 * wv + (lane >> 2);
+      const uint32_t wo = 4u * (uint32_t)min(lane & 3, 2);
+#pragma unroll
+      for (int i = 0; i < kCodeOps; ++i) {
+        if (GATEUP) {
+          const uint32_t* mat = (i & 1) == 0 ? w.qgate : w.qup;
+          cbase[i] = reinterpret_cast<const char*>(mat) + ((size_t)e * a.I + nt * (kRowsMax / 2) + 64 * (i >> 1)) * rw;
+          coff[i] = (uint32_t)rr * rw + wo;
+        } else {
+          cbase[i] = reinterpret_cast<const char*>(w.qdown) + ((size_t)e * a.d + nt * kRowsMax) * rw;
+          coff[i] = (uint32_t)(min(nt * kRowsMax + 64 * i + rr, a.d - 1) - nt * kRowsMax) * rw + wo;
+        }
+      }
+      // the item's row scales into LDS (wave 0; these loads are older than every k-loop
+      // load, so the counted waits below cover them): gate/up units nt*128 + [0, 128) of
+      // the gate then the up matrix, or down columns nt*256 + [0, 256) clamped past d
+      if (wv == 0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const uint16_t* src =
+              GATEUP ? (i == 0 ? w.sgate : w.sup) + (size_t)e * a.I + nt * (kRowsMax / 2) + 2 * lane
+                     : w.sdown + (size_t)e * a.d + min(nt * kRowsMax + 2 * (64 * i + lane), a.d - 2);
+          __builtin_amdgcn_global_load_lds((const void*)src, HY_LDS(ssc + 256 * i), 4, 0, 0);
+        }
+      }
+    }
+    // the step's code words: byte 4 floor(10 ks / 4) of each row
+    auto issue_c = [&](int ks, uint8_t* st) {
+      const uint32_t so = (uint32_t)(10 * ks) & ~3u;
+      uint8_t* dc = st + 256 * wv;
+#pragma unroll
+      for (int i = 0; i < kCodeOps; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(cbase[i] + coff[i] + so), HY_LDS(dc + 1024 * i), 4, 0, 0);
+    };
     // ops [I0, I1) of a step's activation / weight load group
     auto issue_a = [&](int ks, uint8_t* st, auto i0_tag, auto i1_tag) {
       const int kk = ks * kBK;
@@ -313,10 +431,15 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
     // the activations in flight (K >= 128 gives at least 2 steps), step 0 landed
     // everywhere; the rest of step 1 and the weights of step 2 follow in step 0
     issue_a(0, sa0, C0{}, CF{});
-    issue_b(0, sb0, C0{}, CF{});
-    issue_b(1, sb1, C0{}, CF{});
+    if constexpr (TERN) {
+      issue_c(0, sb[0]);
+      issue_c(1, sb[1]);
+    } else {
+      issue_b(0, sb[0], C0{}, CF{});
+      issue_b(1, sb[1], C0{}, CF{});
+    }
     issue_a(1, sa1, C0{}, CH{});
-    wait_vm<kDma + kDma / 2>();
+    wait_vm<kBOps + kDma / 2>();
     bare_barrier();
 
     // the k loop, with this wave's number of active row blocks fixed at compile time
@@ -336,15 +459,53 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
         for (int nb = 0; nb < kNB; ++nb)
           fb[s & 1][nb] = *reinterpret_cast<const uint4*>(Lb + fb_off + nb * kBlk * kRowBytes + frag_lo[s]);
       };
-      // operands in (weights, activations) order: the accumulators hold the transposed
-      // tile, so lane (r32, hf) has output row r32 and 4 consecutive columns per
-      // accumulator quad (see the epilogue)
-      auto mfmas = [&](int s) {
+      // Ternary: the step's code windows of the lane's 4 weight rows (128 wn + 32 nb +
+      // r32), read once per step; group S of the step (k [8 (2S + hf), +8)) takes the two
+      // codes at bit 16 PAR + 20 S + 10 hf of its row's window, PAR = step parity (the
+      // windows are shifted right by 10 hf when group 0 is read).
+      uint32_t cw[kNB][3];
+      auto read_codes = [&](const uint8_t* Lc) {
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) {
+          const uint4 t = *reinterpret_cast<const uint4*>(Lc + kCodePitch * (128 * wn + 32 * nb + r32));
+          cw[nb][0] = t.x;
+          cw[nb][1] = t.y;
+          cw[nb][2] = t.z;
+        }
+      };
+      auto read_frags_t = [&](const uint8_t* La, auto s_tag, auto par_tag) {
+        constexpr int S = decltype(s_tag)::value;
+        constexpr int PAR = decltype(par_tag)::value;
+        wait_lds();
+        if constexpr (S == 0) {
+          const uint32_t sh = 10u * (uint32_t)hf;
+#pragma unroll
+          for (int nb = 0; nb < kNB; ++nb) {
+            cw[nb][0] = __builtin_amdgcn_alignbit(cw[nb][1], cw[nb][0], sh);
+            cw[nb][1] = __builtin_amdgcn_alignbit(cw[nb][2], cw[nb][1], sh);
+            cw[nb][2] >>= sh;
+          }
+        }
 #pragma unroll
         for (int j = 0; j < NACT; ++j)
+          fa[S & 1][j] = *reinterpret_cast<const uint4*>(La + fa_off + j * 2 * kBlk * kRowBytes + frag_lo[S]);
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) {
+          const uint2 lo = lut[code5<16 * PAR + 20 * S>(cw[nb])];
+          const uint2 hi = lut[code5<16 * PAR + 20 * S + 5>(cw[nb])];
+          fb[S & 1][nb] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
+      };
+      // operands in (weights, activations) order: the accumulators hold the transposed
+      // tile, so lane (r32, hf) has output row r32 and 4 consecutive columns per
+      // accumulator quad (see the epilogue); row blocks [J0, J1)
+      auto mfmas_rows = [&](int s, auto j0_tag, auto j1_tag) {
+#pragma unroll
+        for (int j = decltype(j0_tag)::value; j < decltype(j1_tag)::value; ++j)
 #pragma unroll
           for (int nb = 0; nb < kNB; ++nb) acc[j][nb] = mfma32x32x16(fb[s & 1][nb], fa[s & 1][j], acc[j][nb]);
       };
+      auto mfmas = [&](int s) { mfmas_rows(s, std::integral_constant<int, 0>{}, std::integral_constant<int, NACT>{}); };
       // One step ks on activation slot UA = ks % 2 and weight slot UB = ks % BS. The
       // slots step ks-1 used were freed by the barrier that ended it; their next loads
       // (the second half of the activations of step ks+1, the weights of step ks+2) go
@@ -363,24 +524,46 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
         constexpr bool PB = decltype(pb_tag)::value;
         for_seq(std::integer_sequence<int, 1, 2, 3>{}, [&](auto s_tag) {
           constexpr int S = decltype(s_tag)::value;
-          read_frags(sa[UA], sb[UB], S);
+          if constexpr (TERN)
+            read_frags_t(sa[UA], s_tag, ua_tag);  // ks % 2 == UA
+          else
+            read_frags(sa[UA], sb[UB], S);
           if constexpr (S == 1 && PA) issue_a(ks + 1, sa[UA ^ 1], CH{}, CF{});
-          if constexpr (S == 2 && PB) issue_b(ks + 2, sb[(UB + 2) % BS], C0{}, CH{});
-          if constexpr (S == 3 && PB) issue_b(ks + 2, sb[(UB + 2) % BS], CH{}, CF{});
+          if constexpr (TERN) {
+            if constexpr (S == 2 && PB) issue_c(ks + 2, sb[(UB + 2) % BS]);
+          } else {
+            if constexpr (S == 2 && PB) issue_b(ks + 2, sb[(UB + 2) % BS], C0{}, CH{});
+            if constexpr (S == 3 && PB) issue_b(ks + 2, sb[(UB + 2) % BS], CH{}, CF{});
+          }
           mfmas(S - 1);
-          constexpr int NV = ((S == 1 && PA) || (S >= 2 && PB)) ? kDma / 2 : 0;
-          interleave_group<NACT * kNB, NACT + kNB, NV>();
+          constexpr int NV = TERN ? ((S == 1 && PA) ? kDma / 2 : (S == 2 && PB) ? kCodeOps : 0)
+                                  : ((S == 1 && PA) || (S >= 2 && PB)) ? kDma / 2 : 0;
+          interleave_group<NACT * kNB, NACT + (TERN ? 2 : 1) * kNB, NV>();
           __builtin_amdgcn_sched_barrier(0);
         });
         if constexpr (NEXT) {
           // own loads of step ks+1 landed: all but this step's weight loads (the newest)
-          wait_vm<PB ? kDma : 0>();
+          wait_vm<PB ? kBOps : 0>();
           wait_lds();      // own reads of this step done
           bare_barrier();  // everyone's step ks+1 landed; this step's slots are free
           if constexpr (PB) issue_a(ks + 2, sa[UA], C0{}, CH{});
-          read_frags(sa[UA ^ 1], sb[(UB + 1) % BS], 0);
-          mfmas(kSub - 1);
-          interleave_group<NACT * kNB, NACT + kNB, PB ? kDma / 2 : 0>();
+          if constexpr (TERN) {
+            // the next step's code windows first; half of this step's last MFMA group
+            // runs while they are read, then group 0 of the next step is decoded
+            constexpr int H = (NACT + 1) / 2;
+            read_codes(sb[(UB + 1) % BS]);
+            mfmas_rows(kSub - 1, std::integral_constant<int, 0>{}, std::integral_constant<int, H>{});
+            __builtin_amdgcn_sched_group_barrier(0x100, kNB, 0);  // the code reads
+            interleave_group<H * kNB, 0, PB ? kDma / 2 : 0>();
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags_t(sa[UA ^ 1], std::integral_constant<int, 0>{}, std::integral_constant<int, UA ^ 1>{});
+            mfmas_rows(kSub - 1, std::integral_constant<int, H>{}, std::integral_constant<int, NACT>{});
+            interleave_group<(NACT - H) * kNB, NACT + 2 * kNB, 0>();
+          } else {
+            read_frags(sa[UA ^ 1], sb[(UB + 1) % BS], 0);
+            mfmas(kSub - 1);
+            interleave_group<NACT * kNB, NACT + kNB, PB ? kDma / 2 : 0>();
+          }
         } else {
           // the last step: claim the next item (read after the k loop)
           if (threadIdx.x == 0) own_ticket = atomicAdd(&counters[xcd], 1);
@@ -393,7 +576,12 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
       // (R = TAILR, or 6 when TAILR is 0), all with compile-time slots
       constexpr int P = 6;
       constexpr int R = TAILR == 0 ? P : TAILR;
-      read_frags(sa[0], sb[0], 0);
+      if constexpr (TERN) {
+        read_codes(sb[0]);
+        read_frags_t(sa[0], std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+      } else {
+        read_frags(sa[0], sb[0], 0);
+      }
       int k0 = 0;
       for (; k0 + R < nks; k0 += P)
         for_seq(std::make_integer_sequence<int, P>{}, [&](auto t) {
@@ -443,11 +631,28 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
         uint8_t* const pb = piece == 0 ? sa0 : piece == 1 ? sa1 : piece == 2 ? sb0 : sb1;
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
+          // ternary: the row scales of the quad's 4 columns (gate/up: unit 64 wn + 32 nb +
+          // 8 qd + 4 hf + t of the item's gate scales, then of its up scales at +128;
+          // down: column 128 wn + 32 nb + 8 qd + 4 hf + t)
+          float sg[4] = {1.f, 1.f, 1.f, 1.f}, su[4] = {1.f, 1.f, 1.f, 1.f};
+          if constexpr (TERN) {
+            const int c0 = (GATEUP ? 64 : 128) * wn + 32 * nb + 8 * qd + 4 * hf;
+            const uint2 g2 = *reinterpret_cast<const uint2*>(ssc + 2 * c0);
+            sg[0] = bf_lo(g2.x), sg[1] = bf_hi(g2.x), sg[2] = bf_lo(g2.y), sg[3] = bf_hi(g2.y);
+            if constexpr (GATEUP) {
+              const uint2 u2 = *reinterpret_cast<const uint2*>(ssc + 2 * (c0 + kRowsMax / 2));
+              su[0] = bf_lo(u2.x), su[1] = bf_hi(u2.x), su[2] = bf_lo(u2.y), su[3] = bf_hi(u2.y);
+            }
+          }
           float v[4];
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const int i = 4 * qd + t;
-            v[t] = GATEUP ? silu_fast(acc[j][nb][i]) * acc[j][nb + kNB / 2][i] : acc[j][nb][i];
+            if constexpr (TERN)
+              v[t] = GATEUP ? silu_fast(acc[j][nb][i] * sg[t]) * (acc[j][nb + kNB / 2][i] * su[t])
+                            : acc[j][nb][i] * sg[t];
+            else
+              v[t] = GATEUP ? silu_fast(acc[j][nb][i]) * acc[j][nb + kNB / 2][i] : acc[j][nb][i];
           }
           const int chunk = GATEUP ? 4 * nb + qd : 4 * (nb & 1) + qd;  // 16-byte chunk of the piece row
           const uint32_t off = row * 128 + ((chunk ^ swz_key(row)) << 4) + 8 * hf;
@@ -482,40 +687,55 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
   }
 }
 
-static int g_grid[2][64];  // persistent grid per (phase, device), 0 = not yet computed
+static int g_grid[4][64];  // persistent grid per (kernel kind, device), 0 = not yet computed
 
-static int persistent_grid(int phase, const void* kernel) {
+static int persistent_grid(int kind, const void* kernel) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  int gsz = __atomic_load_n(&g_grid[phase][dev], __ATOMIC_ACQUIRE);
+  int gsz = __atomic_load_n(&g_grid[kind][dev], __ATOMIC_ACQUIRE);
   if (gsz > 0) return gsz;
   int cus = 0, occ = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kThreads, 0) != hipSuccess || occ <= 0) occ = 1;
   gsz = ((cus * occ + 7) / 8) * 8;
-  __atomic_store_n(&g_grid[phase][dev], gsz, __ATOMIC_RELEASE);
+  __atomic_store_n(&g_grid[kind][dev], gsz, __ATOMIC_RELEASE);
   return gsz;
+}
+
+using GemmKern = void (*)(GemmArgs, ExpertWeights, uint16_t*, uint16_t*);
+
+// kernel for (phase, weight format, K): indexed by (K / kBK) mod 6 / 2
+template <bool GATEUP, bool TERN>
+static GemmKern pick_gemm(int K) {
+  static const GemmKern k[3] = {grouped_gemm_kernel<GATEUP, 0, TERN>, grouped_gemm_kernel<GATEUP, 2, TERN>,
+                                grouped_gemm_kernel<GATEUP, 4, TERN>};
+  return k[(K / kBK) % 6 / 2];
+}
+
+static hipError_t launch_gemm(GemmKern kern, int kind, GemmArgs a, int sel, const ExpertWeights& w, const Plan& p,
+                              hipStream_t s) {
+  a.sel = sel;
+  const int g = persistent_grid(kind, reinterpret_cast<const void*>(kern));
+  hipLaunchKernelGGL(kern, dim3(g), dim3(kThreads), 0, s, a, w, p.h, (uint16_t*)p.y);
+  return hipGetLastError();
 }
 
 hipError_t launch_grouped_experts(const Plan& p, const uint16_t* x, const ExpertWeights& w, hipStream_t s,
                                   Marks& m) {
-  GemmArgs a{x, p.perm_src, p.offs, p.meta, p.tiles, p.Tk, p.k, p.d, p.I, p.E};
-  using Kern = void (*)(GemmArgs, ExpertWeights, uint16_t*, uint16_t*);
-  // indexed by (K / kBK) mod 6 / 2
-  static const Kern k_gateup[3] = {grouped_gemm_kernel<true, 0>, grouped_gemm_kernel<true, 2>,
-                                   grouped_gemm_kernel<true, 4>};
-  static const Kern k_down[3] = {grouped_gemm_kernel<false, 0>, grouped_gemm_kernel<false, 2>,
-                                 grouped_gemm_kernel<false, 4>};
-  const Kern k1 = k_gateup[(p.d / kBK) % 6 / 2];
-  const Kern k2 = k_down[(p.I / kBK) % 6 / 2];
-  const int g1 = persistent_grid(0, reinterpret_cast<const void*>(k1));
-  hipLaunchKernelGGL(k1, dim3(g1), dim3(kThreads), 0, s, a, w, p.h, (uint16_t*)p.y);
-  hipError_t err = hipGetLastError();
+  GemmArgs a{x, p.perm_src, p.offs, p.meta, p.tiles, p.Tk, p.k, p.d, p.I, p.E, 0};
+  hipError_t err;
+  if (!w.ternary) {
+    err = launch_gemm(pick_gemm<true, false>(p.d), 0, a, 0, w, p, s);
+    if (err == hipSuccess) err = m.mark(s);
+    if (err == hipSuccess) err = launch_gemm(pick_gemm<false, false>(p.I), 1, a, 0, w, p, s);
+    return err == hipSuccess ? m.mark(s) : err;
+  }
+  // ternary routed experts, then the bf16 shared expert, per phase
+  err = launch_gemm(pick_gemm<true, true>(p.d), 2, a, 1, w, p, s);
+  if (err == hipSuccess) err = launch_gemm(pick_gemm<true, false>(p.d), 0, a, 2, w, p, s);
   if (err == hipSuccess) err = m.mark(s);
-  if (err != hipSuccess) return err;
-  const int g2 = persistent_grid(1, reinterpret_cast<const void*>(k2));
-  hipLaunchKernelGGL(k2, dim3(g2), dim3(kThreads), 0, s, a, w, p.h, (uint16_t*)p.y);
-  err = hipGetLastError();
+  if (err == hipSuccess) err = launch_gemm(pick_gemm<false, true>(p.I), 3, a, 1, w, p, s);
+  if (err == hipSuccess) err = launch_gemm(pick_gemm<false, false>(p.I), 1, a, 2, w, p, s);
   return err == hipSuccess ? m.mark(s) : err;
 }
 

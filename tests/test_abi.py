@@ -116,8 +116,11 @@ def test_ternary_requires_codes_and_scales():
     a.expert_format = hm.WEIGHTS_SHERRY_TERNARY
     assert call(a) == hm.ERR_INVALID_ARG
     a.Wq_gate = a.Wq_up = a.Wq_down = a.S_gate = a.S_up = a.S_down = FAKE
-    a.path = hm.PATH_GROUPED
-    assert call(a) == hm.ERR_UNSUPPORTED
+    a.Wq_down = FAKE + 2  # codes and scales must be 4-byte aligned
+    assert call(a) == hm.ERR_INVALID_ARG
+    a.Wq_down = FAKE
+    a.S_up = FAKE + 2
+    assert call(a) == hm.ERR_INVALID_ARG
 
 
 def test_small_workspace_rejected():

@@ -5,6 +5,7 @@ path choice, caller workspace):
   prefill  T=8192, bf16 experts
   skewed   T=4096, bf16 experts, Zipf(1.2) router bias
   ternary  T=32,   Sherry ternary routed experts, bf16 shared expert
+  ternary_prefill  T=8192, the same weights on the grouped path
 The routing of every token (sets, weights, counts, offsets, permutation) is
 compared with the oracle; outputs are compared on sampled tokens, for which the
 oracle regenerates the touched experts' weights on the host from the same
@@ -133,3 +134,11 @@ def test_ternary_full_size():
     cfg = hi.CONFIGS["ternary"]
     inp = hi.dev_layer(cfg, device=DEV)
     run_full(cfg, inp, sample=[0, 9, 31])
+
+
+def test_ternary_prefill_full_size():
+    cfg = hi.CONFIGS["ternary_prefill"]
+    inp = hi.dev_layer(cfg, device=DEV)
+    run_full(cfg, inp, sample=[0, 4095, 8191])
+    del inp
+    torch.cuda.empty_cache()

@@ -149,11 +149,29 @@ def test_ternary_lds_small(shape):
     run_small(cfg, hm.PATH_STREAM)
 
 
-def test_ternary_grouped_path_unsupported():
-    cfg = hi.LayerConfig("tern", T=8, d=256, E=16, k=2, I=128, ternary=True, seed=5)
+@pytest.mark.parametrize("shape", [
+    # grouped GEMM on decoded Sherry codes; K / 64 mod 6 picks the k-loop tail (gate/up: d, down: I)
+    dict(T=64, d=256, E=16, k=2, I=128),     # ~8 rows per expert (one 32-row block); tails 4 and 2
+    dict(T=300, d=768, E=8, k=2, I=384),     # ~75 rows per expert, ragged; whole 6-step periods; 3 N tiles
+    dict(T=1100, d=640, E=4, k=1, I=256),    # ~275 rows per expert: two M tiles; last down N tile half past d
+    dict(T=200, d=512, E=16, k=4, I=512),    # ~50 rows per expert; tails 2 and 2
+])
+def test_ternary_grouped_small(shape):
+    cfg = hi.LayerConfig("terng", ternary=True, seed=5, **shape)
+    run_small(cfg, hm.PATH_GROUPED)
+
+
+def test_ternary_paths_agree_mid_size():
+    say("[case] ternary stream vs grouped at T=256 d=1024 E=32 k=4 I=512")
+    cfg = hi.LayerConfig("ternmid", T=256, d=1024, E=32, k=4, I=512, ternary=True, seed=9)
     inp = hi.dev_layer(cfg, device=DEV)
-    with pytest.raises(hm.HyMoeError):
-        hm.forward_layer(inp, cfg.k, path=hm.PATH_GROUPED)
+    a = hm.forward_layer(inp, cfg.k, want_routing=True, path=hm.PATH_STREAM)
+    b = hm.forward_layer(inp, cfg.k, want_routing=True, path=hm.PATH_GROUPED)
+    torch.cuda.synchronize()
+    for key in ("topk_idx", "topk_w", "counts", "offsets", "perm_src", "margin"):
+        assert torch.equal(a[key], b[key]), key
+    fa, fb = a["out"].float(), b["out"].float()
+    assert ((fa - fb).abs() <= 2e-2 * (1 + fb.abs())).all()
 
 
 # ------------------------------------------------------------- determinism
