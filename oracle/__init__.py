@@ -35,6 +35,9 @@ def lib():
         L.hyo_combine.argtypes = [vp, vp, vp, i64, i64, i64, vp]
         L.hyo_sherry_decode.argtypes = [vp, vp, i64, i64, vp, vp]
         L.hyo_forward.argtypes = [vp] * 9 + [i64] * 5 + [vp] * 6 + [ci]
+        L.hyo_fp8_decode.argtypes = [vp, vp, i64, i64, vp]
+        L.hyo_ffn_w64.argtypes = [vp, i64, vp, vp, vp, i64, i64, vp, ci]
+        L.hyo_forward_w64.argtypes = [vp] * 9 + [i64] * 5 + [vp] * 6 + [ci]
         _lib = L
     return _lib
 
@@ -144,4 +147,47 @@ def forward(x, wr, bias, wg, wu, wd, sg, su, sd, k, sets_in=None, nthreads=None)
     _check(lib().hyo_forward(_p(x), _p(wr), _p(bias), _p(wg), _p(wu), _p(wd), _p(sg), _p(su), _p(sd),
                              T, d, E, k, I, _p(sets_in), _p(out), _p(sets), _p(w), _p(margin), _p(lg),
                              _threads(nthreads)), "hyo_forward")
+    return {"out": out, "sets": sets, "w": w, "margin": margin, "logits": lg}
+
+
+def fp8_decode(q, scale=None):
+    """E4M3 codes uint8 [rows][cols] (and fp32 row scales) -> fp64 weights [rows][cols]."""
+    q = _c(np.atleast_2d(q), np.uint8)
+    rows, cols = q.shape
+    scale = None if scale is None else _c(scale, np.float32)
+    w = np.empty((rows, cols), np.float64)
+    _check(lib().hyo_fp8_decode(_p(q), _p(scale), rows, cols, _p(w)), "hyo_fp8_decode")
+    return w
+
+
+def ffn_w64(x_rows, wg, wu, wd, nthreads=None):
+    """Expert FFN with fp64 weights wg, wu [I][d], wd [d][I] on bf16 token rows."""
+    x_rows = _c(np.atleast_2d(x_rows), np.uint16)
+    wg, wu, wd = _c(wg, np.float64), _c(wu, np.float64), _c(wd, np.float64)
+    n, d = x_rows.shape
+    I = wg.shape[0]
+    y = np.empty((n, d), np.float64)
+    _check(lib().hyo_ffn_w64(_p(x_rows), n, _p(wg), _p(wu), _p(wd), d, I, _p(y), _threads(nthreads)),
+           "hyo_ffn_w64")
+    return y
+
+
+def forward_w64(x, wr, bias, fg, fu, fd, sg, su, sd, k, sets_in=None, nthreads=None):
+    """Whole layer with fp64 routed weights (fg, fu [E][I][d], fd [E][d][I]) and a bf16
+    shared expert. Returns dict(out, sets, w, margin, logits)."""
+    x, wr, bias = _c(x, np.uint16), _c(wr, np.uint16), _c(bias, np.float32)
+    fg, fu, fd = _c(fg, np.float64), _c(fu, np.float64), _c(fd, np.float64)
+    sg, su, sd = _c(sg, np.uint16), _c(su, np.uint16), _c(sd, np.uint16)
+    sets_in = _c(sets_in, np.int32)
+    T, d = x.shape
+    E = wr.shape[0]
+    I = sg.shape[0]
+    out = np.empty((T, d), np.float64)
+    sets = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    margin = np.empty(T, np.float64)
+    lg = np.empty((T, E), np.float64)
+    _check(lib().hyo_forward_w64(_p(x), _p(wr), _p(bias), _p(fg), _p(fu), _p(fd), _p(sg), _p(su), _p(sd),
+                                 T, d, E, k, I, _p(sets_in), _p(out), _p(sets), _p(w), _p(margin), _p(lg),
+                                 _threads(nthreads)), "hyo_forward_w64")
     return {"out": out, "sets": sets, "w": w, "margin": margin, "logits": lg}

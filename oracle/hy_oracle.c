@@ -38,6 +38,16 @@
  * the zero's position in the group, bits 2, 3, 4 the signs (1 = negative) of
  * the first, second and third non-zero in ascending position. The weight is
  * the row's bf16 scale times the ternary value.
+ *
+ * FP8 weights (the Hy4 preview release ships BF16 and FP8 weights, FP8 halving
+ * the weight storage: fengxiaobai.com Hy4 preview overview, section "MTP、FP8
+ * 与低价 API"; the model card lists an official FP8 checkpoint). The pages fix
+ * no format, scale layout or activation precision. Reading taken here: routed
+ * experts' weights are OCP 8-bit floats in the E4M3 encoding (no infinities:
+ * sign bit 7, exponent bits 6-3 with bias 7, mantissa bits 2-0; exponent 0 is
+ * subnormal m/8 * 2^-6; exponent 15 with mantissa 7 is NaN), each output row
+ * carries one fp32 scale, weight = scale * value; activations stay bf16 and the
+ * shared expert stays bf16.
  */
 #include <math.h>
 #include <pthread.h>
@@ -325,22 +335,91 @@ int hyo_sherry_decode(const uint32_t* packed, const uint16_t* scale, int64_t row
   return HYO_OK;
 }
 
+/* ------------------------------------------------------- FP8 E4M3 ------- */
+
+/* Value of one E4M3 code, from the encoding's definition. */
+static double e4m3_value(uint8_t c) {
+  int neg = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  double v = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+  return neg ? -v : v;
+}
+
+/* Weights of one FP8 matrix: q [rows][cols] E4M3 codes, scale fp32 [rows] or
+ * NULL (taken as 1) -> w fp64 [rows][cols] = scale[r] * value(q[r][c]). */
+int hyo_fp8_decode(const uint8_t* q, const float* scale, int64_t rows, int64_t cols, double* w) {
+  if (rows < 0 || cols <= 0 || (rows > 0 && (!q || !w))) return HYO_ERR_ARG;
+  for (int64_t r = 0; r < rows; ++r) {
+    double s = scale ? (double)scale[r] : 1.0;
+    for (int64_t c = 0; c < cols; ++c) w[r * cols + c] = s * e4m3_value(q[r * cols + c]);
+  }
+  return HYO_OK;
+}
+
+/* The same expert FFN with fp64 weights (bf16 token rows):
+ *   h = silu(W_gate x_r) * (W_up x_r),   y_r = W_down h.
+ * x_rows: bf16 [n][d]; wg, wu: fp64 [I][d]; wd: fp64 [d][I]; y: fp64 [n][d]. */
+typedef struct {
+  const uint16_t* x;
+  const double *wg, *wu, *wd;
+  int64_t d, I;
+  double* h;
+  double* y;
+} ffn64_ctx;
+
+static void ffn64_hidden(void* p, int64_t i0, int64_t i1) {
+  ffn64_ctx* c = (ffn64_ctx*)p;
+  for (int64_t i = i0; i < i1; ++i) {
+    const double* g = c->wg + i * c->d;
+    const double* u = c->wu + i * c->d;
+    double sg = 0.0, su = 0.0;
+    for (int64_t j = 0; j < c->d; ++j) {
+      double xj = bf16_value(c->x[j]);
+      sg += g[j] * xj;
+      su += u[j] * xj;
+    }
+    c->h[i] = silu(sg) * su;
+  }
+}
+
+static void ffn64_out(void* p, int64_t m0, int64_t m1) {
+  ffn64_ctx* c = (ffn64_ctx*)p;
+  for (int64_t m = m0; m < m1; ++m) {
+    const double* dn = c->wd + m * c->I;
+    double s = 0.0;
+    for (int64_t i = 0; i < c->I; ++i) s += dn[i] * c->h[i];
+    c->y[m] = s;
+  }
+}
+
+int hyo_ffn_w64(const uint16_t* x_rows, int64_t n, const double* wg, const double* wu, const double* wd,
+                int64_t d, int64_t I, double* y, int nthreads) {
+  if (n < 0 || d <= 0 || I <= 0 || (n > 0 && (!x_rows || !wg || !wu || !wd || !y))) return HYO_ERR_ARG;
+  double* h = (double*)malloc(sizeof(double) * (size_t)I);
+  if (!h) return HYO_ERR_ARG;
+  for (int64_t r = 0; r < n; ++r) {
+    ffn64_ctx c = {x_rows + r * d, wg, wu, wd, d, I, h, y + r * d};
+    parallel_for(I, ffn64_hidden, &c, nthreads);
+    parallel_for(d, ffn64_out, &c, nthreads);
+  }
+  free(h);
+  return HYO_OK;
+}
+
 /* ------------------------------------------------------- whole layer ----- */
 
-/* Forward pass of the whole layer for small shapes (bf16 routed experts).
- *   x [T][d], wr [E][d], bias [E] fp32 or NULL,
- *   wg, wu [E][I][d], wd [E][d][I], sg, su [I][d], sd [d][I]   (bf16)
- * Outputs: out fp64 [T][d]; optional sets int32 [T][k], w fp64 [T][k],
- * margin fp64 [T], logits fp64 [T][E]. If sets_in is non-NULL it replaces the
- * top-k selection (used to substitute an admissible set for a near-tie token). */
-int hyo_forward(const uint16_t* x, const uint16_t* wr, const float* bias, const uint16_t* wg,
-                const uint16_t* wu, const uint16_t* wd, const uint16_t* sg, const uint16_t* su,
-                const uint16_t* sd, int64_t T, int64_t d, int64_t E, int64_t k, int64_t I,
-                const int32_t* sets_in, double* out, int32_t* sets_out, double* w_out,
-                double* margin_out, double* logits_out, int nthreads) {
+/* The whole layer; routed experts' weights as bf16 (wg..wd) or as fp64 (fg..fd, the
+ * other set NULL). */
+static int forward_impl(const uint16_t* x, const uint16_t* wr, const float* bias, const uint16_t* wg,
+                        const uint16_t* wu, const uint16_t* wd, const double* fg, const double* fu,
+                        const double* fd, const uint16_t* sg, const uint16_t* su, const uint16_t* sd, int64_t T,
+                        int64_t d, int64_t E, int64_t k, int64_t I, const int32_t* sets_in, double* out,
+                        int32_t* sets_out, double* w_out, double* margin_out, double* logits_out, int nthreads) {
   if (T < 0 || d <= 0 || E <= 0 || k < 1 || k > E || I <= 0) return HYO_ERR_ARG;
   if (T == 0) return HYO_OK;
-  if (!x || !wr || !wg || !wu || !wd || !sg || !su || !sd || !out) return HYO_ERR_ARG;
+  const int f64 = fg != NULL;
+  if (!x || !wr || !sg || !su || !sd || !out) return HYO_ERR_ARG;
+  if (f64 ? (!fu || !fd) : (!wg || !wu || !wd)) return HYO_ERR_ARG;
   int rc = HYO_OK;
   double* logits = (double*)malloc(sizeof(double) * (size_t)(T * E));
   int32_t* sets = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T * k));
@@ -356,8 +435,10 @@ int hyo_forward(const uint16_t* x, const uint16_t* wr, const float* bias, const 
   for (int64_t t = 0; t < T; ++t)
     for (int64_t j = 0; j < k; ++j) {
       int64_t e = sets[t * k + j];
-      rc = hyo_ffn(x + t * d, 1, wg + e * I * d, wu + e * I * d, wd + e * d * I, d, I,
-                   yr + (t * k + j) * d, nthreads);
+      rc = f64 ? hyo_ffn_w64(x + t * d, 1, fg + e * I * d, fu + e * I * d, fd + e * d * I, d, I,
+                             yr + (t * k + j) * d, nthreads)
+               : hyo_ffn(x + t * d, 1, wg + e * I * d, wu + e * I * d, wd + e * d * I, d, I,
+                         yr + (t * k + j) * d, nthreads);
       if (rc) goto done;
     }
   rc = hyo_combine(ys, yr, w, T, k, d, out);
@@ -367,4 +448,31 @@ int hyo_forward(const uint16_t* x, const uint16_t* wr, const float* bias, const 
 done:
   free(logits); free(sets); free(w); free(ys); free(yr);
   return rc;
+}
+
+/* Forward pass of the whole layer for small shapes (bf16 routed experts).
+ *   x [T][d], wr [E][d], bias [E] fp32 or NULL,
+ *   wg, wu [E][I][d], wd [E][d][I], sg, su [I][d], sd [d][I]   (bf16)
+ * Outputs: out fp64 [T][d]; optional sets int32 [T][k], w fp64 [T][k],
+ * margin fp64 [T], logits fp64 [T][E]. If sets_in is non-NULL it replaces the
+ * top-k selection (used to substitute an admissible set for a near-tie token). */
+int hyo_forward(const uint16_t* x, const uint16_t* wr, const float* bias, const uint16_t* wg,
+                const uint16_t* wu, const uint16_t* wd, const uint16_t* sg, const uint16_t* su,
+                const uint16_t* sd, int64_t T, int64_t d, int64_t E, int64_t k, int64_t I,
+                const int32_t* sets_in, double* out, int32_t* sets_out, double* w_out,
+                double* margin_out, double* logits_out, int nthreads) {
+  return forward_impl(x, wr, bias, wg, wu, wd, NULL, NULL, NULL, sg, su, sd, T, d, E, k, I, sets_in, out,
+                      sets_out, w_out, margin_out, logits_out, nthreads);
+}
+
+/* The same with fp64 routed weights fg, fu [E][I][d], fd [E][d][I] (e.g. decoded
+ * FP8 experts); the shared expert stays bf16. */
+int hyo_forward_w64(const uint16_t* x, const uint16_t* wr, const float* bias, const double* fg,
+                    const double* fu, const double* fd, const uint16_t* sg, const uint16_t* su,
+                    const uint16_t* sd, int64_t T, int64_t d, int64_t E, int64_t k, int64_t I,
+                    const int32_t* sets_in, double* out, int32_t* sets_out, double* w_out,
+                    double* margin_out, double* logits_out, int nthreads) {
+  if (!fg) return HYO_ERR_ARG;
+  return forward_impl(x, wr, bias, NULL, NULL, NULL, fg, fu, fd, sg, su, sd, T, d, E, k, I, sets_in, out,
+                      sets_out, w_out, margin_out, logits_out, nthreads);
 }

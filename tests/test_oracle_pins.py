@@ -390,3 +390,89 @@ def test_sherry_ternary_gemv_equals_dense_gemv():
     dense = bf(w) @ x
     factored = bf(scale) * (tern.astype(np.float64) @ x)
     assert np.allclose(dense, factored, rtol=1e-14, atol=1e-15)
+
+
+# ------------------------------------------------------------------- FP8 E4M3
+def test_fp8_hand_worked_codes():
+    for line in open(os.path.join(GOLDEN, "fp8_e4m3.txt")):
+        if not line.strip() or line.startswith("#"):
+            continue
+        code, val = line.split()
+        got = oracle.fp8_decode(np.array([[int(code, 16)]], np.uint8))[0, 0]
+        if val == "nan":
+            assert math.isnan(got), code
+        else:
+            assert got == float(val) and math.copysign(1.0, got) == math.copysign(1.0, float(val)), code
+
+
+def test_fp8_all_codes_match_torch_float8_e4m3fn():
+    torch = pytest.importorskip("torch")
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    got = oracle.fp8_decode(codes[None, :])[0]
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+    assert np.flatnonzero(np.isnan(got)).tolist() == [0x7F, 0xFF]
+
+
+def test_fp8_row_scales():
+    rng = np.random.default_rng(11)
+    q = rng.integers(0, 256, size=(5, 16), dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x38  # no NaN codes
+    s = np.array([0.5, -2.0, 3.0e-3, 1.0, 7.25], np.float32)
+    w1 = oracle.fp8_decode(q)
+    w = oracle.fp8_decode(q, s)
+    assert np.array_equal(w, w1 * s.astype(np.float64)[:, None])
+    assert np.array_equal(w[3], w1[3]) and np.array_equal(w[1], -2.0 * w1[1])
+
+
+def test_ffn_w64_equals_ffn_on_bf16_values():
+    # the fp64-weight FFN must reproduce the pinned bf16 FFN bit for bit when the
+    # weights are the same values (same sums in the same order)
+    rng = np.random.default_rng(12)
+    n, d, I = 3, 64, 40
+    x = f32_to_bf16_bits(rng.standard_normal((n, d)))
+    wg = f32_to_bf16_bits(rng.standard_normal((I, d)) / 8)
+    wu = f32_to_bf16_bits(rng.standard_normal((I, d)) / 8)
+    wd = f32_to_bf16_bits(rng.standard_normal((d, I)) / 7)
+    a = oracle.ffn(x, wg, wu, wd, nthreads=2)
+    b = oracle.ffn_w64(x, bf(wg), bf(wu), bf(wd), nthreads=2)
+    assert np.array_equal(a, b)
+    assert not np.array_equal(oracle.ffn_w64(x, bf(wu), bf(wg), bf(wd)), a)  # gate and up are not interchangeable
+
+
+@pytest.mark.parametrize("bias", [False, True])
+def test_forward_w64_equals_forward_on_bf16_values(bias):
+    cfg, L = small_layer(seed=3, bias=bias)
+    a = run_forward(L, cfg.k)
+    b = oracle.forward_w64(L["x"], L["router"], L["bias"], bf(L["gate"]), bf(L["up"]), bf(L["down"]),
+                           L["shared"]["gate"], L["shared"]["up"], L["shared"]["down"], cfg.k)
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_fp8_layer_matches_dense_masked_numpy():
+    # FP8 experts decoded by the oracle, then the whole layer against the
+    # independent dense formulation on the same (fp64) weights
+    cfg, L = small_layer(seed=4, T=16, d=64, E=6, k=2, I=32, bias=True)
+    rng = np.random.default_rng(13)
+    fw = {}
+    for key, rows, cols in (("gate", cfg.I, cfg.d), ("up", cfg.I, cfg.d), ("down", cfg.d, cfg.I)):
+        q = rng.integers(0, 256, size=(cfg.E, rows, cols), dtype=np.uint8)
+        q[(q & 0x7F) == 0x7F] = 0x30
+        s = (rng.random((cfg.E, rows)) * 0.05 + 0.01).astype(np.float32)
+        fw[key] = np.stack([oracle.fp8_decode(q[e], s[e]) for e in range(cfg.E)])
+    ref = oracle.forward_w64(L["x"], L["router"], L["bias"], fw["gate"], fw["up"], fw["down"],
+                             L["shared"]["gate"], L["shared"]["up"], L["shared"]["down"], cfg.k)
+    x = bf(L["x"])
+    lg = x @ bf(L["router"]).T + L["bias"].astype(np.float64)
+    out = np_swiglu(x, bf(L["shared"]["gate"]), bf(L["shared"]["up"]), bf(L["shared"]["down"]))
+    for t in range(cfg.T):
+        order = np.lexsort((np.arange(cfg.E), -lg[t]))[:cfg.k]
+        p = np.exp(lg[t, order] - lg[t, order].max())
+        p /= p.sum()
+        for pe, e in zip(p, order):
+            out[t] += pe * np_swiglu(x[t:t + 1], fw["gate"][e], fw["up"][e], fw["down"][e])[0]
+    assert np.allclose(ref["out"], out, rtol=1e-11, atol=1e-11)
