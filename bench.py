@@ -155,7 +155,7 @@ def run_config(name, args, hi, hm, torch, weights=None):
         inp["x"] = weights["x"][: cfg.T].contiguous()
         b = hi.host_bias(cfg)
         inp["bias"] = None if b is None else torch.from_numpy(b).to(dev)
-    fmt = hm.WEIGHTS_SHERRY_TERNARY if cfg.ternary else hm.WEIGHTS_BF16
+    fmt = hm.WEIGHTS_SHERRY_TERNARY if cfg.ternary else hm.WEIGHTS_FP8_E4M3 if cfg.fp8 else hm.WEIGHTS_BF16
     ws = hm.alloc_workspace(cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, fmt, device=dev)
     steps = args.steps
     dominant = hm.KERNELS.index("expert_gateup")
@@ -165,7 +165,7 @@ def run_config(name, args, hi, hm, torch, weights=None):
     torch.cuda.synchronize()
     counts = routing["counts"].cpu()
     touched = int((counts > 0).sum())
-    stream_path = cfg.T * cfg.k <= 16 * cfg.E  # the library's automatic path choice
+    stream_path = cfg.fp8 or cfg.T * cfg.k <= 16 * cfg.E  # the library's automatic path choice
     d, I = cfg.d, cfg.I
     kernel_file = "sparse_moe_transformer_route_amd/csrc/" + ("moe_stream.hip" if stream_path else "moe_gemm.hip")
     if stream_path:
@@ -175,6 +175,11 @@ def run_config(name, args, hi, hm, torch, weights=None):
             shared = 2 * I * d * 2
             alg = touched * unit + shared
             per_unit = f"{unit} B packed gate+up codes and scales per touched routed expert, plus {shared} B bf16 shared"
+        elif cfg.fp8:
+            unit = 2 * I * d + 2 * I * 4                    # E4M3 codes + fp32 row scales
+            shared = 2 * I * d * 2
+            alg = touched * unit + shared
+            per_unit = f"{unit} B of E4M3 gate+up codes and scales per touched routed expert, plus {shared} B bf16 shared"
         else:
             unit = 2 * I * d * 2
             alg = (touched + 1) * unit
@@ -185,11 +190,14 @@ def run_config(name, args, hi, hm, torch, weights=None):
         key = "ternary_gateup" if tern_lds else "stream_gateup"
         roof = {"bound": "hbm", "achieved": alg / sec / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                 "frac": alg / sec / PEAK_HBM, "traffic": traffic_for(f"{key}/{name}", touched + 1),
-                "kernel": "tern_lds_kernel<2>" if tern_lds else "stream_gateup_kernel", "per_unit": per_unit,
+                "kernel": ("tern_lds_kernel<2>" if tern_lds else "stream_gateup_kernel<2> (FP8 routed experts)" if cfg.fp8
+                           else "stream_gateup_kernel"), "per_unit": per_unit,
                 "units_per_launch": touched + 1, "kernel_ms": dom_ms}
         # whole-layer HBM fraction: every touched expert's weights once + router + x/out
         if cfg.ternary:
             layer_bytes = touched * (3 * I * (d // 128 * 5 * 4) + 2 * I * 2 + d * 2) + 3 * I * d * 2
+        elif cfg.fp8:
+            layer_bytes = touched * (3 * I * d + (2 * I + d) * 4) + 3 * I * d * 2
         else:
             layer_bytes = (touched + 1) * 3 * I * d * 2
         layer_bytes += cfg.E * d * 2 + 2 * cfg.T * d * 2
@@ -232,10 +240,13 @@ def cpu_baseline(cfg, hi, torch, inp, routing, budget_s):
     cache = {}
 
     def expert(e):
-        # bf16 weights of routed expert e; Sherry codes are decoded by the oracle
-        # here, outside the timed region (weight materialisation)
+        # bf16 weights of routed expert e; Sherry and FP8 codes are decoded by the
+        # oracle here, outside the timed region (weight materialisation)
         if e not in cache:
-            if "qgate" in inp:
+            if "fgate" in inp:
+                cache[e] = tuple(oracle.fp8_decode(inp[q][e].cpu().numpy(), inp[s][e].cpu().numpy())
+                                 for q, s in (("fgate", "fsgate"), ("fup", "fsup"), ("fdown", "fsdown")))
+            elif "qgate" in inp:
                 cache[e] = tuple(oracle.sherry_decode(inp[q][e].cpu().numpy().view(np.uint32), bits(inp[s][e]))[1]
                                  for q, s in (("qgate", "sgate"), ("qup", "sup"), ("qdown", "sdown")))
             else:
@@ -255,7 +266,8 @@ def cpu_baseline(cfg, hi, torch, inp, routing, budget_s):
         for i in range(len(tok)):
             for j, e in enumerate(sets[i]):
                 g, u, dn = expert(int(e))
-                yr[i, j] = oracle.ffn(x[tok[i]:tok[i] + 1], g, u, dn, nthreads=nthreads)[0]
+                ffn = oracle.ffn_w64 if "fgate" in inp else oracle.ffn
+                yr[i, j] = ffn(x[tok[i]:tok[i] + 1], g, u, dn, nthreads=nthreads)[0]
         oracle.combine(ys, yr, w)
         return time.perf_counter() - t0
 
@@ -285,7 +297,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed steps before the timed ones (default: at least 5 and %.1f s of them)" % WARMUP_MIN_S)
     ap.add_argument("--config", default="decode", choices=["tiny", "decode", "prefill", "skewed", "ternary",
-                                                                 "ternary_prefill"])
+                                                                 "ternary_prefill", "fp8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the T=8192 measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -314,7 +326,7 @@ def main():
 
     cfg = hi.CONFIGS[args.config]
     shared_weights = None
-    if not cfg.ternary and cfg.d == 6144:
+    if not cfg.ternary and not cfg.fp8 and cfg.d == 6144:
         log("[bench] generating the Hy4-shape bf16 layer (19.3 GB of expert weights) on the GPU")
         shared_weights = hi.dev_layer(hi.CONFIGS["prefill"], device="cuda:0")
         torch.cuda.synchronize()
@@ -366,7 +378,7 @@ def main():
         "metric": METRIC, "value": main_res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": main_res["warmup"], "ms_per_step": main_res["ms"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": "sherry-ternary+bf16" if c.ternary else "bf16", "data": "synthetic",
+        "dtype": "sherry-ternary+bf16" if c.ternary else "fp8-e4m3+bf16" if c.fp8 else "bf16", "data": "synthetic",
         "config": {"workload": f"{c.name} MoE FFN layer T={c.T} d={c.d} E={c.E} top-{c.k} + 1 shared I={c.I}"
                                + (" Sherry-ternary routed experts" if c.ternary else " bf16")
                                + (" Zipf(1.2) router bias" if c.zipf_s else ""),

@@ -32,6 +32,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # One Philox stream per tensor.
 S_X, S_WR, S_WG, S_WU, S_WD, S_WSG, S_WSU, S_WSD, S_BIAS = 1, 2, 3, 4, 5, 6, 7, 8, 9
 S_QG, S_QU, S_QD, S_SG, S_SU, S_SD = 10, 11, 12, 13, 14, 15
+S_FG, S_FU, S_FD, S_FSG, S_FSU, S_FSD = 16, 17, 18, 19, 20, 21
 
 QBLOCK_WEIGHTS = 128  # weights per packed ternary block
 QBLOCK_WORDS = 5      # uint32 words per packed ternary block (1.25 bits/weight)
@@ -46,6 +47,7 @@ class LayerConfig:
     k: int
     I: int
     ternary: bool = False
+    fp8: bool = False        # routed experts as E4M3 codes with fp32 row scales
     zipf_s: float = 0.0      # 0 => no router bias
     zipf_alpha: float = 1.0
     x_std: float = 1.0
@@ -62,6 +64,8 @@ CONFIGS = {
     "prefill": LayerConfig("prefill", T=8192, d=6144, E=256, k=8, I=2048),
     "skewed": LayerConfig("skewed", T=4096, d=6144, E=256, k=8, I=2048, zipf_s=1.2),
     "ternary": LayerConfig("ternary", T=32, d=6144, E=256, k=8, I=2048, ternary=True),
+    # routed experts as FP8 (E4M3 codes, fp32 row scales), decode batch
+    "fp8": LayerConfig("fp8", T=32, d=6144, E=256, k=8, I=2048, fp8=True),
     # the ternary experts at a prefill-sized batch (grouped GEMM on decoded codes)
     "ternary_prefill": LayerConfig("ternary_prefill", T=8192, d=6144, E=256, k=8, I=2048, ternary=True),
 }
@@ -221,11 +225,41 @@ def host_expert_ternary(cfg: LayerConfig, e: int) -> dict:
             "sdown": uniform_bf16(cfg.seed, S_SD, d, 0.5 * si, si, start=e * d)}
 
 
+def fp8_codes_from_bytes(b):
+    """Random bytes -> E4M3 codes: sign and mantissa bits kept, the exponent field
+    forced into 4..7 (|value| in [1/8, 15/8], never NaN). numpy or torch uint8."""
+    return (b & 0x87) | ((((b >> 3) & 3) + 4) << 3)
+
+
+def fp8_scale_exponent(cols: int) -> int:
+    """Row scales are m * 2^-(15 + p) with m in [0x6000, 0xE000): about 1/sqrt(cols)."""
+    return int(math.floor(0.5 * math.log2(cols)))
+
+
+def fp8_scales_from_words(w, cols: int):
+    """Random words -> fp32 row scales, exact on host and device: (w & 0x7FFF) + 0x6000
+    (an integer below 2^16) times a power of two."""
+    return ((w & 0x7FFF) + 0x6000) * (2.0 ** -(15 + fp8_scale_exponent(cols)))
+
+
+def host_expert_fp8(cfg: LayerConfig, e: int) -> dict:
+    """E4M3 codes (uint8 [rows][cols]) and fp32 row scales of routed expert e."""
+    d, I = cfg.d, cfg.I
+    def codes(stream, rows, cols):
+        n = rows * cols // 4
+        return fp8_codes_from_bytes(words_u32(cfg.seed, stream, n, start=e * n).view(np.uint8)).reshape(rows, cols)
+    def scales(stream, rows, cols):
+        return fp8_scales_from_words(words_u32(cfg.seed, stream, rows, start=e * rows), cols).astype(np.float32)
+    return {"fgate": codes(S_FG, I, d), "fup": codes(S_FU, I, d), "fdown": codes(S_FD, d, I),
+            "fsgate": scales(S_FSG, I, d), "fsup": scales(S_FSU, I, d), "fsdown": scales(S_FSD, d, I)}
+
+
 def host_layer(cfg: LayerConfig) -> dict:
     """Every input of a (small) layer as host arrays: bf16 as uint16 bit patterns."""
     out = {"x": host_x(cfg), "router": host_router(cfg), "bias": host_bias(cfg),
            "shared": host_shared(cfg)}
-    experts = [host_expert_ternary(cfg, e) if cfg.ternary else host_expert(cfg, e) for e in range(cfg.E)]
+    gen = host_expert_ternary if cfg.ternary else host_expert_fp8 if cfg.fp8 else host_expert
+    experts = [gen(cfg, e) for e in range(cfg.E)]
     keys = experts[0].keys()
     for key in keys:
         out[key] = np.stack([ex[key] for ex in experts])
@@ -285,6 +319,20 @@ def dev_layer(cfg: LayerConfig, device="cuda") -> dict:
         out["sgate"] = dev_uniform_(torch.empty(E, I, dtype=bf, device=device), cfg.seed, S_SG, 0.5 * sd, sd)
         out["sup"] = dev_uniform_(torch.empty(E, I, dtype=bf, device=device), cfg.seed, S_SU, 0.5 * sd, sd)
         out["sdown"] = dev_uniform_(torch.empty(E, d, dtype=bf, device=device), cfg.seed, S_SD, 0.5 * si, si)
+    elif cfg.fp8:
+        i32 = torch.int32
+
+        def codes(stream, rows, cols):
+            w = dev_words_(torch.empty(E, rows, cols // 4, dtype=i32, device=device), cfg.seed, stream)
+            b = w.view(torch.uint8).view(E, rows, cols)
+            return fp8_codes_from_bytes(b)
+
+        def scales(stream, rows, cols):
+            w = dev_words_(torch.empty(E, rows, dtype=i32, device=device), cfg.seed, stream)
+            return fp8_scales_from_words(w, cols).to(torch.float32)
+
+        out["fgate"], out["fup"], out["fdown"] = codes(S_FG, I, d), codes(S_FU, I, d), codes(S_FD, d, I)
+        out["fsgate"], out["fsup"], out["fsdown"] = scales(S_FSG, I, d), scales(S_FSU, I, d), scales(S_FSD, d, I)
     else:
         out["gate"] = dev_gauss_(torch.empty(E, I, d, dtype=bf, device=device), cfg.seed, S_WG, sd)
         out["up"] = dev_gauss_(torch.empty(E, I, d, dtype=bf, device=device), cfg.seed, S_WU, sd)

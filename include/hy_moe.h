@@ -70,7 +70,17 @@ typedef enum {
    * position of the zero in the group; bits 2, 3, 4 give the signs of the
    * first, second and third non-zero weight in ascending position (1 means -1).
    * Every bit pattern is a valid block. */
-  HY_MOE_WEIGHTS_SHERRY_TERNARY = 1
+  HY_MOE_WEIGHTS_SHERRY_TERNARY = 1,
+  /* FP8 weights (the Hy4 preview release ships BF16 and FP8 weights, FP8 halving
+   * the weight storage: fengxiaobai.com Hy4 preview overview, section "MTP、FP8
+   * 与低价 API"). The pages give no encoding or scale layout; taken here: each
+   * routed expert weight is one OCP 8-bit float in the E4M3 encoding (sign bit 7,
+   * exponent bits 6-3 with bias 7, mantissa bits 2-0; exponent 0 is subnormal,
+   * S.1111.111 is NaN, no infinities), each output row has one fp32 scale, and
+   * weight = scale * value. Activations and the shared expert stay bf16; a NaN
+   * code gives NaN outputs. Streaming path only (HY_MOE_PATH_GROUPED returns
+   * HY_MOE_ERR_UNSUPPORTED; HY_MOE_PATH_AUTO streams every batch size). */
+  HY_MOE_WEIGHTS_FP8_E4M3 = 2
 } hy_moe_wfmt;
 
 /* Which kernels run the experts. AUTO picks by the average rows per expert. */
@@ -116,12 +126,13 @@ typedef struct hy_moe_args {
   const void* W_gate;        /* BF16: bf16 [E][I][d] */
   const void* W_up;          /* BF16: bf16 [E][I][d] */
   const void* W_down;        /* BF16: bf16 [E][d][I] */
-  const void* Wq_gate;       /* SHERRY_TERNARY: uint32 [E][I][d/128*5] */
-  const void* Wq_up;         /* SHERRY_TERNARY: uint32 [E][I][d/128*5] */
-  const void* Wq_down;       /* SHERRY_TERNARY: uint32 [E][d][I/128*5] */
-  const void* S_gate;        /* SHERRY_TERNARY: bf16 [E][I] row scales */
-  const void* S_up;          /* SHERRY_TERNARY: bf16 [E][I] */
-  const void* S_down;        /* SHERRY_TERNARY: bf16 [E][d] */
+  const void* Wq_gate;       /* SHERRY_TERNARY: uint32 [E][I][d/128*5]; FP8_E4M3: uint8 [E][I][d] */
+  const void* Wq_up;         /* SHERRY_TERNARY: uint32 [E][I][d/128*5]; FP8_E4M3: uint8 [E][I][d] */
+  const void* Wq_down;       /* SHERRY_TERNARY: uint32 [E][d][I/128*5]; FP8_E4M3: uint8 [E][d][I]
+                                (FP8 codes 16-byte aligned, everything else 4-byte) */
+  const void* S_gate;        /* row scales. SHERRY_TERNARY: bf16 [E][I]; FP8_E4M3: fp32 [E][I] */
+  const void* S_up;          /* SHERRY_TERNARY: bf16 [E][I]; FP8_E4M3: fp32 [E][I] */
+  const void* S_down;        /* SHERRY_TERNARY: bf16 [E][d]; FP8_E4M3: fp32 [E][d] */
   const void* Ws_gate;       /* bf16 [I][d] */
   const void* Ws_up;         /* bf16 [I][d] */
   const void* Ws_down;       /* bf16 [d][I] */

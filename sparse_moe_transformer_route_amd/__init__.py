@@ -24,7 +24,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhy_moe.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
-WEIGHTS_BF16, WEIGHTS_SHERRY_TERNARY = 0, 1
+WEIGHTS_BF16, WEIGHTS_SHERRY_TERNARY, WEIGHTS_FP8_E4M3 = 0, 1, 2
 PATH_AUTO, PATH_STREAM, PATH_GROUPED = 0, 1, 2
 KERNELS = ["route_logits", "route_topk", "permute_scan", "permute_scatter", "expert_gateup", "expert_down",
            "combine"]
@@ -131,22 +131,36 @@ def forward_layer(inp: dict, k: int, *, want_routing=False, path=PATH_AUTO, work
                   stream=None, stage_events=None):
     """Runs hy_moe_forward_ex on a dict of device tensors as made by
     hy_inputs.dev_layer(): x, router, bias, shared{gate,up,down} and either
-    gate/up/down (bf16) or qgate/qup/qdown + sgate/sup/sdown (ternary).
+    gate/up/down (bf16), qgate/qup/qdown + sgate/sup/sdown (ternary) or
+    fgate/fup/fdown + fsgate/fsup/fsdown (FP8 E4M3 codes and fp32 scales).
     Returns dict(out, and with want_routing: topk_idx, topk_w, counts, offsets,
     perm_src, margin)."""
     import torch
     x = inp["x"]
     T, d = x.shape
     E = inp["router"].shape[0]
-    ternary = "qgate" in inp
-    I = inp["sgate"].shape[1] if ternary else inp["gate"].shape[1]
+    ternary, fp8 = "qgate" in inp, "fgate" in inp
+    # the library reads raw memory: reject element types it would misread
+    want = ({"fgate": torch.uint8, "fup": torch.uint8, "fdown": torch.uint8, "fsgate": torch.float32,
+             "fsup": torch.float32, "fsdown": torch.float32} if fp8 else
+            {"qgate": torch.int32, "qup": torch.int32, "qdown": torch.int32, "sgate": torch.bfloat16,
+             "sup": torch.bfloat16, "sdown": torch.bfloat16} if ternary else
+            {"gate": torch.bfloat16, "up": torch.bfloat16, "down": torch.bfloat16})
+    want.update(x=torch.bfloat16, router=torch.bfloat16)
+    for key, dt in want.items():
+        if inp[key].dtype != dt or not inp[key].is_contiguous():
+            raise TypeError(f"forward_layer: {key} must be a contiguous {dt} tensor, got {inp[key].dtype}")
+    I = inp["sgate"].shape[1] if ternary else inp["fsgate"].shape[1] if fp8 else inp["gate"].shape[1]
     dev = x.device
     a = HyMoeArgs()
     a.x, a.W_router, a.router_bias = _ptr(x), _ptr(inp["router"]), _ptr(inp.get("bias"))
-    a.expert_format = WEIGHTS_SHERRY_TERNARY if ternary else WEIGHTS_BF16
+    a.expert_format = WEIGHTS_SHERRY_TERNARY if ternary else WEIGHTS_FP8_E4M3 if fp8 else WEIGHTS_BF16
     if ternary:
         a.Wq_gate, a.Wq_up, a.Wq_down = _ptr(inp["qgate"]), _ptr(inp["qup"]), _ptr(inp["qdown"])
         a.S_gate, a.S_up, a.S_down = _ptr(inp["sgate"]), _ptr(inp["sup"]), _ptr(inp["sdown"])
+    elif fp8:
+        a.Wq_gate, a.Wq_up, a.Wq_down = _ptr(inp["fgate"]), _ptr(inp["fup"]), _ptr(inp["fdown"])
+        a.S_gate, a.S_up, a.S_down = _ptr(inp["fsgate"]), _ptr(inp["fsup"]), _ptr(inp["fsdown"])
     else:
         a.W_gate, a.W_up, a.W_down = _ptr(inp["gate"]), _ptr(inp["up"]), _ptr(inp["down"])
     sh = inp["shared"]

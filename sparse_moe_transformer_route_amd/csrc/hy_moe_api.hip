@@ -71,7 +71,8 @@ int check_args(const hy_moe_args* a) {
   if (!a) return HY_MOE_ERR_INVALID_ARG;
   int rc = check_shape(a->T, a->d, a->E, a->k, a->I);
   if (rc != HY_MOE_OK) return rc;
-  if (a->expert_format != HY_MOE_WEIGHTS_BF16 && a->expert_format != HY_MOE_WEIGHTS_SHERRY_TERNARY)
+  if (a->expert_format != HY_MOE_WEIGHTS_BF16 && a->expert_format != HY_MOE_WEIGHTS_SHERRY_TERNARY &&
+      a->expert_format != HY_MOE_WEIGHTS_FP8_E4M3)
     return HY_MOE_ERR_INVALID_ARG;
   if (a->path != HY_MOE_PATH_AUTO && a->path != HY_MOE_PATH_STREAM && a->path != HY_MOE_PATH_GROUPED)
     return HY_MOE_ERR_INVALID_ARG;
@@ -86,10 +87,18 @@ int check_args(const hy_moe_args* a) {
     const void* w[] = {a->W_gate, a->W_up, a->W_down};
     for (const void* p : w)
       if (!p || !aligned(p, 16)) return HY_MOE_ERR_INVALID_ARG;
-  } else {
+  } else if (a->expert_format == HY_MOE_WEIGHTS_SHERRY_TERNARY) {
     const void* w[] = {a->Wq_gate, a->Wq_up, a->Wq_down, a->S_gate, a->S_up, a->S_down};
     for (const void* p : w)
       if (!p || !aligned(p, 4)) return HY_MOE_ERR_INVALID_ARG;
+  } else {
+    const void* q[] = {a->Wq_gate, a->Wq_up, a->Wq_down};
+    for (const void* p : q)
+      if (!p || !aligned(p, 16)) return HY_MOE_ERR_INVALID_ARG;
+    const void* sc[] = {a->S_gate, a->S_up, a->S_down};
+    for (const void* p : sc)
+      if (!p || !aligned(p, 4)) return HY_MOE_ERR_INVALID_ARG;
+    if (a->path == HY_MOE_PATH_GROUPED) return HY_MOE_ERR_UNSUPPORTED;
   }
   if (a->path == HY_MOE_PATH_GROUPED && !grouped_fits(a->T, a->d, a->k, a->I)) return HY_MOE_ERR_UNSUPPORTED;
   const void* opt4[] = {a->topk_idx, a->topk_w, a->counts, a->offsets, a->perm_src, a->margin};
@@ -144,6 +153,13 @@ extern "C" int hy_moe_forward_ex(const hy_moe_args* a, void* stream) {
 
   ExpertWeights w{};
   w.ternary = a->expert_format == HY_MOE_WEIGHTS_SHERRY_TERNARY;
+  w.fp8 = a->expert_format == HY_MOE_WEIGHTS_FP8_E4M3;
+  w.f8gate = (const uint8_t*)a->Wq_gate;
+  w.f8up = (const uint8_t*)a->Wq_up;
+  w.f8down = (const uint8_t*)a->Wq_down;
+  w.f8sgate = (const float*)a->S_gate;
+  w.f8sup = (const float*)a->S_up;
+  w.f8sdown = (const float*)a->S_down;
   w.gate = (const uint16_t*)a->W_gate;
   w.up = (const uint16_t*)a->W_up;
   w.down = (const uint16_t*)a->W_down;
@@ -163,7 +179,7 @@ extern "C" int hy_moe_forward_ex(const hy_moe_args* a, void* stream) {
   else if (a->path == HY_MOE_PATH_GROUPED)
     stream_path = false;
   else
-    stream_path = (int64_t)p.Tk <= 16 * (int64_t)p.E || !grouped_fits(p.T, p.d, p.k, p.I);
+    stream_path = w.fp8 || (int64_t)p.Tk <= 16 * (int64_t)p.E || !grouped_fits(p.T, p.d, p.k, p.I);
 
   const uint16_t* x = (const uint16_t*)a->x;
   Marks marks{a->stage_events, 0};
@@ -201,7 +217,9 @@ extern "C" int hy_moe_forward(const void* x, const void* W_router, const void* W
 }
 
 extern "C" size_t hy_moe_workspace_size(int64_t T, int64_t d, int64_t E, int64_t k, int64_t I, int expert_format) {
-  if (expert_format != HY_MOE_WEIGHTS_BF16 && expert_format != HY_MOE_WEIGHTS_SHERRY_TERNARY) return 0;
+  if (expert_format != HY_MOE_WEIGHTS_BF16 && expert_format != HY_MOE_WEIGHTS_SHERRY_TERNARY &&
+      expert_format != HY_MOE_WEIGHTS_FP8_E4M3)
+    return 0;
   if (check_shape(T, d, E, k, I) != HY_MOE_OK) return 0;
   return make_layout(T, d, E, k, I).total;
 }

@@ -65,11 +65,19 @@ struct ExpertWeights {
   const uint16_t* sgate;
   const uint16_t* sup;
   const uint16_t* sdown;
+  // FP8 (E4M3) routed experts: codes [E][rows][cols], fp32 scales [E][rows]
+  const uint8_t* f8gate;
+  const uint8_t* f8up;
+  const uint8_t* f8down;
+  const float* f8sgate;
+  const float* f8sup;
+  const float* f8sdown;
   // bf16 shared expert
   const uint16_t* s_gate;
   const uint16_t* s_up;
   const uint16_t* s_down;
   bool ternary;
+  bool fp8;
 };
 
 hipError_t launch_stream_experts(const Plan& p, const uint16_t* x, const ExpertWeights& w, hipStream_t s,

@@ -13,7 +13,8 @@
 // [32g, 32g+32) of each chunk, with several chunks in flight. The 16 rows x 16 tokens
 // product runs on 16x16x32 bf16 MFMA with fp32 accumulation (experts with more than
 // 16 tokens take several passes). Sherry-ternary experts are decoded in registers from 5-bit codes
-// through a 32-entry LDS table into bf16 +-1/0 and scaled per row after the sum.
+// through a 32-entry LDS table into bf16 +-1/0 and scaled per row after the sum; FP8
+// (E4M3) experts are converted to bf16 in registers (exact) and scaled per row likewise.
 #include "common.h"
 #include "kernels.h"
 
@@ -49,6 +50,13 @@ constexpr int kDepthDown = 3;           // chunks in flight, down (one matrix)
 // In the ternary kernels only the shared expert streams bf16: a shallow ring keeps their
 // register count, and so the number of waves hiding the code-table lookups, in check.
 constexpr int kDepthSharedTern = 2;
+// FP8 experts: a chunk is half the bytes of a bf16 one, so the ring is deeper for a
+// similar number of weight bytes in flight.
+constexpr int kDepthFp8GateUp = 7;
+constexpr int kDepthFp8Down = 7;
+
+// Weight formats of the streaming kernels.
+constexpr int kWfBf16 = 0, kWfTern = 1, kWfFp8 = 2;
 
 // Drives a register ring of D + 1 slots over n items in order: load(i, slot) issues
 // the loads of item i into a slot, use(slot) consumes it, D items ahead of the loads.
@@ -109,6 +117,58 @@ __device__ __forceinline__ void gateup_bf16_block(const uint16_t* __restrict__ w
           accg = mfma16x16x32(rg[u][v], rx[u][v], accg);
           accu = mfma16x16x32(ru[u][v], rx[u][v], accu);
         }
+      });
+}
+
+// ------------------------------------------------------------- FP8 experts
+// Eight E4M3 codes (two words, code i in byte i) to eight bf16 values: every E4M3
+// value, subnormals included, is a bf16 value, so the conversion is exact (NaN codes
+// give NaN).
+template <bool HI>  // codes 0-1 or 2-3 of the word
+__device__ __forceinline__ uint32_t e4m3x2_bf16(uint32_t v) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, HI));
+}
+__device__ __forceinline__ uint4 e4m3x8_bf16(uint32_t lo, uint32_t hi) {
+  return make_uint4(e4m3x2_bf16<false>(lo), e4m3x2_bf16<true>(lo), e4m3x2_bf16<false>(hi), e4m3x2_bf16<true>(hi));
+}
+
+// As gateup_bf16_block with E4M3 weights: per chunk a lane loads the 16 codes of k
+// [16 g, 16 g + 16) of its gate and up rows (one 16-byte load each), the same k as
+// its two 8-element activation pieces.
+template <int D>
+__device__ __forceinline__ void gateup_fp8_block(const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu,
+                                                 const uint16_t* __restrict__ xr, int d, f32x4& accg, f32x4& accu) {
+  uint4 rg[D + 1], ru[D + 1], rx[D + 1][kKV];
+  ring_stream<D>(
+      d / kChunk,
+      [&](int ch, int slot) {
+        rg[slot] = ldg16(wg + ch * kChunk);
+        ru[slot] = ldg16(wu + ch * kChunk);
+#pragma unroll
+        for (int v = 0; v < kKV; ++v) rx[slot][v] = ldg16(xr + ch * kChunk + 8 * v);
+      },
+      [&](int u) {
+        accg = mfma16x16x32(e4m3x8_bf16(rg[u].x, rg[u].y), rx[u][0], accg);
+        accu = mfma16x16x32(e4m3x8_bf16(ru[u].x, ru[u].y), rx[u][0], accu);
+        accg = mfma16x16x32(e4m3x8_bf16(rg[u].z, rg[u].w), rx[u][1], accg);
+        accu = mfma16x16x32(e4m3x8_bf16(ru[u].z, ru[u].w), rx[u][1], accu);
+      });
+}
+
+template <int D>
+__device__ __forceinline__ void down_fp8_block(const uint8_t* __restrict__ wd, const uint16_t* __restrict__ hr, int I,
+                                               f32x4& acc) {
+  uint4 rw[D + 1], rx[D + 1][kKV];
+  ring_stream<D>(
+      I / kChunk,
+      [&](int ch, int slot) {
+        rw[slot] = ldg16(wd + ch * kChunk);
+#pragma unroll
+        for (int v = 0; v < kKV; ++v) rx[slot][v] = ldg16(hr + ch * kChunk + 8 * v);
+      },
+      [&](int u) {
+        acc = mfma16x16x32(e4m3x8_bf16(rw[u].x, rw[u].y), rx[u][0], acc);
+        acc = mfma16x16x32(e4m3x8_bf16(rw[u].z, rw[u].w), rx[u][1], acc);
       });
 }
 
@@ -217,8 +277,9 @@ __device__ __forceinline__ int shared_slots(const StreamArgs& a, bool tern) {
   return tern ? ((a.Tk / a.k + 15) / 16) * 2 : 1;
 }
 
-template <bool TERN>
+template <int WF>
 __global__ void __launch_bounds__(256) stream_gateup_kernel(StreamArgs a, ExpertWeights w, uint16_t* __restrict__ h) {
+  constexpr bool TERN = WF == kWfTern, FP8 = WF == kWfFp8;
   __shared__ uint2 lut[32];
   if (TERN) {
     build_code_table(lut);
@@ -240,6 +301,35 @@ __global__ void __launch_bounds__(256) stream_gateup_kernel(StreamArgs a, Expert
   const int r16 = lane & 15, g = lane >> 4;
   const int d = a.d, I = a.I;
   const bool routed = e < a.E;
+
+  if (FP8 && routed) {
+    // E4M3 routed expert: rows i0 + r16, 16 token columns per pass, each row's sums
+    // times its fp32 scale; D row 4g + j of the wave is hidden unit i0 + 4g + j
+    const int i0 = blockIdx.x * 64 + wv * 16;
+    const uint8_t* wg = w.f8gate + ((size_t)e * I + i0 + r16) * d + 16 * g;
+    const uint8_t* wu = w.f8up + ((size_t)e * I + i0 + r16) * d + 16 * g;
+    float sg[4], su[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sg[j] = w.f8sgate[(size_t)e * I + i0 + 4 * g + j];
+      su[j] = w.f8sup[(size_t)e * I + i0 + 4 * g + j];
+    }
+    for (int cb = 0; cb < n; cb += 16) {
+      const bool valid = cb + r16 < n;
+      const int col = valid ? row0 + cb + r16 : row0;
+      const uint16_t* xr = a.x + (size_t)row_token(col, a.perm_src, a.Tk, a.k) * d + 16 * g;
+      f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+      gateup_fp8_block<kDepthFp8GateUp>(wg, wu, xr, d, accg, accu);
+      if (valid) {
+        float hv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hv[j] = silu(accg[j] * sg[j]) * (accu[j] * su[j]);
+        *reinterpret_cast<uint2*>(h + (size_t)col * I + i0 + 4 * g) =
+            make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+      }
+    }
+    return;
+  }
 
   if (!TERN || !routed) {
     // bf16 weights: 64 rows per pass (a ternary-kernel workgroup covers 128 rows),
@@ -307,9 +397,10 @@ __global__ void __launch_bounds__(256) stream_gateup_kernel(StreamArgs a, Expert
   }
 }
 
-template <bool TERN>
+template <int WF>
 __global__ void __launch_bounds__(256) stream_down_kernel(StreamArgs a, ExpertWeights w,
                                                           const uint16_t* __restrict__ h, float* __restrict__ y) {
+  constexpr bool TERN = WF == kWfTern, FP8 = WF == kWfFp8;
   __shared__ uint2 lut[32];
   if (TERN) {
     build_code_table(lut);
@@ -331,6 +422,25 @@ __global__ void __launch_bounds__(256) stream_down_kernel(StreamArgs a, ExpertWe
   const int r16 = lane & 15, g = lane >> 4;
   const int d = a.d, I = a.I;
   const bool routed = e < a.E;
+
+  if (FP8 && routed) {
+    // E4M3 routed expert: output rows m0 + r16, sums times the rows' fp32 scales
+    const int m0 = blockIdx.x * 64 + wv * 16;
+    const uint8_t* wd = w.f8down + ((size_t)e * d + m0 + r16) * I + 16 * g;
+    float sd[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sd[j] = w.f8sdown[(size_t)e * d + m0 + 4 * g + j];
+    for (int cb = 0; cb < n; cb += 16) {
+      const bool valid = cb + r16 < n;
+      const int col = valid ? row0 + cb + r16 : row0;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      down_fp8_block<kDepthFp8Down>(wd, h + (size_t)col * I + 16 * g, I, acc);
+      if (valid)
+        *reinterpret_cast<float4*>(y + (size_t)col * d + m0 + 4 * g) =
+            make_float4(acc[0] * sd[0], acc[1] * sd[1], acc[2] * sd[2], acc[3] * sd[3]);
+    }
+    return;
+  }
 
   if (!TERN || !routed) {
 #pragma unroll 1
@@ -621,23 +731,18 @@ hipError_t launch_stream_experts(const Plan& p, const uint16_t* x, const ExpertW
   // ternary kernels: 128 rows per workgroup (d and I are multiples of 128)
   const int rows_wg = w.ternary ? 128 : 64;
   dim3 g1(p.I / rows_wg, slots), g2(p.d / rows_wg, slots);
-  hipError_t err;
-  if (w.ternary) {
-    hipLaunchKernelGGL(stream_gateup_kernel<true>, g1, dim3(256), 0, s, a, w, p.h);
-    err = hipGetLastError();
-  } else {
-    hipLaunchKernelGGL(stream_gateup_kernel<false>, g1, dim3(256), 0, s, a, w, p.h);
-    err = hipGetLastError();
-  }
+  const auto gu = w.ternary ? stream_gateup_kernel<kWfTern>
+                  : w.fp8   ? stream_gateup_kernel<kWfFp8>
+                            : stream_gateup_kernel<kWfBf16>;
+  const auto dn = w.ternary ? stream_down_kernel<kWfTern>
+                  : w.fp8   ? stream_down_kernel<kWfFp8>
+                            : stream_down_kernel<kWfBf16>;
+  hipLaunchKernelGGL(gu, g1, dim3(256), 0, s, a, w, p.h);
+  hipError_t err = hipGetLastError();
   if (err == hipSuccess) err = m.mark(s);
   if (err != hipSuccess) return err;
-  if (w.ternary) {
-    hipLaunchKernelGGL(stream_down_kernel<true>, g2, dim3(256), 0, s, a, w, p.h, (float*)p.y);
-    err = hipGetLastError();
-  } else {
-    hipLaunchKernelGGL(stream_down_kernel<false>, g2, dim3(256), 0, s, a, w, p.h, (float*)p.y);
-    err = hipGetLastError();
-  }
+  hipLaunchKernelGGL(dn, g2, dim3(256), 0, s, a, w, p.h, (float*)p.y);
+  err = hipGetLastError();
   return err == hipSuccess ? m.mark(s) : err;
 }
 

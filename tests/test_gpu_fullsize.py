@@ -6,6 +6,7 @@ path choice, caller workspace):
   skewed   T=4096, bf16 experts, Zipf(1.2) router bias
   ternary  T=32,   Sherry ternary routed experts, bf16 shared expert
   ternary_prefill  T=8192, the same weights on the grouped path
+  fp8      T=32,   FP8 (E4M3, fp32 row scales) routed experts, bf16 shared expert
 The routing of every token (sets, weights, counts, offsets, permutation) is
 compared with the oracle; outputs are compared on sampled tokens, for which the
 oracle regenerates the touched experts' weights on the host from the same
@@ -43,7 +44,7 @@ def hy4_weights():
     torch.cuda.empty_cache()
 
 
-def sampled_reference(cfg, x_host, sets, w, tokens, ternary=False):
+def sampled_reference(cfg, x_host, sets, w, tokens, ternary=False, fp8=False):
     """Oracle outputs of the sampled tokens, one expert's weights at a time."""
     sh = hi.host_shared(cfg)
     ys = oracle.ffn(x_host[tokens], sh["gate"], sh["up"], sh["down"])
@@ -53,6 +54,14 @@ def sampled_reference(cfg, x_host, sets, w, tokens, ternary=False):
         for j, e in enumerate(sets[t]):
             by_expert.setdefault(int(e), []).append((i, j))
     for e, pairs in sorted(by_expert.items()):
+        if fp8:
+            f = hi.host_expert_fp8(cfg, e)
+            rows = [tokens[i] for i, _ in pairs]
+            y = oracle.ffn_w64(x_host[rows], oracle.fp8_decode(f["fgate"], f["fsgate"]),
+                               oracle.fp8_decode(f["fup"], f["fsup"]), oracle.fp8_decode(f["fdown"], f["fsdown"]))
+            for (i, j), yy in zip(pairs, y):
+                yr[i, j] = yy
+            continue
         if ternary:
             q = hi.host_expert_ternary(cfg, e)
             gate = oracle.sherry_decode(q["qgate"], q["sgate"])[1]
@@ -70,8 +79,8 @@ def sampled_reference(cfg, x_host, sets, w, tokens, ternary=False):
 
 def run_full(cfg, inp, sample):
     say(f"[case] {cfg.name} T={cfg.T} full-size, sampled tokens {sample}")
-    ws = hm.alloc_workspace(cfg.T, cfg.d, cfg.E, cfg.k, cfg.I,
-                            hm.WEIGHTS_SHERRY_TERNARY if cfg.ternary else hm.WEIGHTS_BF16, device=DEV)
+    fmt = hm.WEIGHTS_SHERRY_TERNARY if cfg.ternary else hm.WEIGHTS_FP8_E4M3 if cfg.fp8 else hm.WEIGHTS_BF16
+    ws = hm.alloc_workspace(cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, fmt, device=DEV)
     res = hm.forward_layer(inp, cfg.k, want_routing=True, workspace=ws)
     torch.cuda.synchronize()
     g = routing_to_np(res)
@@ -87,7 +96,7 @@ def run_full(cfg, inp, sample):
     say(f"       routing of all {cfg.T} tokens ok: near-ties={near} substituted={subst} "
         f"max |dw|={werr:.2e} touched experts={int((g['counts'] > 0).sum())} ({time.time() - t0:.1f}s)")
     w_ref = oracle.weights(lg, sets)
-    ref = sampled_reference(cfg, x_host, sets, w_ref, sample, ternary=cfg.ternary)
+    ref = sampled_reference(cfg, x_host, sets, w_ref, sample, ternary=cfg.ternary, fp8=cfg.fp8)
     worst, mean = check_out(out[sample], ref)
     say(f"       sampled outputs ok: max_rel_err={worst:.3e} mean_abs_err={mean:.3e} ({time.time() - t0:.1f}s)")
     return res, g
@@ -134,6 +143,14 @@ def test_ternary_full_size():
     cfg = hi.CONFIGS["ternary"]
     inp = hi.dev_layer(cfg, device=DEV)
     run_full(cfg, inp, sample=[0, 9, 31])
+
+
+def test_fp8_full_size():
+    cfg = hi.CONFIGS["fp8"]
+    inp = hi.dev_layer(cfg, device=DEV)
+    run_full(cfg, inp, sample=[0, 13, 31])
+    del inp
+    torch.cuda.empty_cache()
 
 
 def test_ternary_prefill_full_size():

@@ -36,12 +36,16 @@ def host_weights_bf16(cfg, L):
     return gate, up, down
 
 
-def run_small(cfg, path, bias=None, x_host=None, label=""):
+def run_small(cfg, path, bias=None, x_host=None, label="", fp8_codes=None):
     """Full element-by-element comparison on a small layer."""
     say(f"[case] {label or cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} I={cfg.I} "
-        f"ternary={cfg.ternary} path={path}")
+        f"ternary={cfg.ternary} fp8={cfg.fp8} path={path}")
     L = hi.host_layer(cfg)
     inp = hi.dev_layer(cfg, device=DEV)
+    if fp8_codes is not None:  # caller-chosen codes and scales
+        for key, val in fp8_codes.items():
+            L[key] = val
+            inp[key] = torch.from_numpy(val).to(DEV)
     if bias is not None:
         L["bias"] = bias
         inp["bias"] = torch.from_numpy(bias).to(DEV)
@@ -51,13 +55,19 @@ def run_small(cfg, path, bias=None, x_host=None, label=""):
     res = hm.forward_layer(inp, cfg.k, want_routing=True, path=path)
     torch.cuda.synchronize()
     g = routing_to_np(res)
-    gate, up, down = host_weights_bf16(cfg, L)
     lg = oracle.logits(L["x"], L["router"], L["bias"])
     sets, near, subst = check_routing(g["topk_idx"], lg, cfg.k)
     check_permutation(g, sets, cfg.E)
     check_weights(g["topk_w"], lg, sets)
-    ref = oracle.forward(L["x"], L["router"], L["bias"], gate, up, down, L["shared"]["gate"], L["shared"]["up"],
-                         L["shared"]["down"], cfg.k, sets_in=sets)
+    if cfg.fp8:
+        fw = [np.stack([oracle.fp8_decode(L["f" + m][e], L["fs" + m][e]) for e in range(cfg.E)])
+              for m in ("gate", "up", "down")]
+        ref = oracle.forward_w64(L["x"], L["router"], L["bias"], *fw, L["shared"]["gate"], L["shared"]["up"],
+                                 L["shared"]["down"], cfg.k, sets_in=sets)
+    else:
+        gate, up, down = host_weights_bf16(cfg, L)
+        ref = oracle.forward(L["x"], L["router"], L["bias"], gate, up, down, L["shared"]["gate"], L["shared"]["up"],
+                             L["shared"]["down"], cfg.k, sets_in=sets)
     worst, mean = check_out(bf16_tensor_to_np(res["out"]), ref["out"])
     # margins: fp32 GPU margin vs fp64 oracle margin
     fin = np.isfinite(ref["margin"])
@@ -79,6 +89,10 @@ def test_device_generator_matches_host():
     u = torch.empty(5001, dtype=torch.bfloat16, device=DEV)
     hi.dev_uniform_(u, 2, 13, 0.01, 0.02)
     assert np.array_equal(bf16_tensor_bits(u), hi.uniform_bf16(2, 13, 5001, 0.01, 0.02))
+    cfg = hi.LayerConfig("f8", T=4, d=256, E=3, k=2, I=128, fp8=True, seed=4)
+    dl, hl = hi.dev_layer(cfg, device=DEV), hi.host_layer(cfg)
+    for key in ("fgate", "fup", "fdown", "fsgate", "fsup", "fsdown"):
+        assert np.array_equal(dl[key].cpu().numpy(), hl[key]), key
 
 
 # ------------------------------------------------------------ small layers
@@ -172,6 +186,44 @@ def test_ternary_paths_agree_mid_size():
         assert torch.equal(a[key], b[key]), key
     fa, fb = a["out"].float(), b["out"].float()
     assert ((fa - fb).abs() <= 2e-2 * (1 + fb.abs())).all()
+
+
+@pytest.mark.parametrize("shape", [
+    dict(T=1, d=256, E=16, k=2, I=256),       # one token
+    dict(T=32, d=512, E=16, k=4, I=256),      # ~8 tokens per expert
+    dict(T=100, d=256, E=8, k=2, I=512),      # ~25 tokens per expert: two 16-token passes
+    dict(T=40, d=1024, E=16, k=2, I=1024),    # chunk counts that fill the FP8 ring exactly (16)
+])
+def test_fp8_small(shape):
+    cfg = hi.LayerConfig("fp8", fp8=True, seed=6, **shape)
+    run_small(cfg, hm.PATH_STREAM)
+
+
+def test_fp8_every_code():
+    # Expert e's weights are all E4M3 code e (the two NaN codes replaced by +-1), and
+    # its row scales are 1 / |value|, so every expert computes +-1 weights: a wrong
+    # conversion of any code (subnormals, zeros, 448) shows as a large error.
+    cfg = hi.LayerConfig("fp8all", T=256, d=256, E=256, k=8, I=128, fp8=True, seed=7)
+    codes = np.arange(256, dtype=np.uint8)
+    codes[0x7F], codes[0xFF] = 0x38, 0xB8
+    val = np.abs(oracle.fp8_decode(codes[None, :])[0])
+    scale = np.where(val > 0, 1.0 / np.where(val > 0, val, 1.0), 1.0).astype(np.float32)
+    sd, si = 1.0 / np.sqrt(cfg.d), 1.0 / np.sqrt(cfg.I)
+    chosen = {}
+    for m, rows, cols, s in (("gate", cfg.I, cfg.d, sd), ("up", cfg.I, cfg.d, sd), ("down", cfg.d, cfg.I, si)):
+        chosen["f" + m] = np.ascontiguousarray(np.broadcast_to(codes[:, None, None], (cfg.E, rows, cols)))
+        chosen["fs" + m] = np.ascontiguousarray(np.broadcast_to((scale * s)[:, None], (cfg.E, rows)), np.float32)
+    res, _ = run_small(cfg, hm.PATH_STREAM, fp8_codes=chosen)
+    touched = int((res["counts"] > 0).sum().item())
+    say(f"       experts touched: {touched} of 256")
+    assert touched >= 240
+
+
+def test_fp8_grouped_path_unsupported():
+    cfg = hi.LayerConfig("fp8", T=8, d=256, E=16, k=2, I=128, fp8=True, seed=5)
+    inp = hi.dev_layer(cfg, device=DEV)
+    with pytest.raises(hm.HyMoeError):
+        hm.forward_layer(inp, cfg.k, path=hm.PATH_GROUPED)
 
 
 # ------------------------------------------------------------- determinism
