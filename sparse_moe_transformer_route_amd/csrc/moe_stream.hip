@@ -50,10 +50,12 @@ constexpr int kDepthDown = 3;           // chunks in flight, down (one matrix)
 // In the ternary kernels only the shared expert streams bf16: a shallow ring keeps their
 // register count, and so the number of waves hiding the code-table lookups, in check.
 constexpr int kDepthSharedTern = 2;
-// FP8 experts: a chunk is half the bytes of a bf16 one, so the ring is deeper for a
-// similar number of weight bytes in flight.
-constexpr int kDepthFp8GateUp = 7;
-constexpr int kDepthFp8Down = 7;
+// FP8 experts: each wave covers two 16-row blocks that share every activation load
+// (with one block the activation loads are half of all loads per weight byte: down was
+// 14% slower); rings of 3 chunks, as deeper ones measured no faster and cost occupancy.
+constexpr int kFp8RowBlocks = 2;
+constexpr int kDepthFp8GateUp = 3;
+constexpr int kDepthFp8Down = 3;
 
 // Weight formats of the streaming kernels.
 constexpr int kWfBf16 = 0, kWfTern = 1, kWfFp8 = 2;
@@ -132,43 +134,54 @@ __device__ __forceinline__ uint4 e4m3x8_bf16(uint32_t lo, uint32_t hi) {
   return make_uint4(e4m3x2_bf16<false>(lo), e4m3x2_bf16<true>(lo), e4m3x2_bf16<false>(hi), e4m3x2_bf16<true>(hi));
 }
 
-// As gateup_bf16_block with E4M3 weights: per chunk a lane loads the 16 codes of k
-// [16 g, 16 g + 16) of its gate and up rows (one 16-byte load each), the same k as
-// its two 8-element activation pieces.
-template <int D>
-__device__ __forceinline__ void gateup_fp8_block(const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu,
-                                                 const uint16_t* __restrict__ xr, int d, f32x4& accg, f32x4& accu) {
-  uint4 rg[D + 1], ru[D + 1], rx[D + 1][kKV];
+// As gateup_bf16_block with E4M3 weights, for NR row blocks sharing the activations:
+// per chunk a lane loads the 16 codes of k [16 g, 16 g + 16) of its gate and up row in
+// each block (one 16-byte load each), the same k as its two 8-element activation pieces.
+template <int D, int NR>
+__device__ __forceinline__ void gateup_fp8_block(const uint8_t* const (&wg)[NR], const uint8_t* const (&wu)[NR],
+                                                 const uint16_t* __restrict__ xr, int d, f32x4 (&accg)[NR],
+                                                 f32x4 (&accu)[NR]) {
+  uint4 rg[D + 1][NR], ru[D + 1][NR], rx[D + 1][kKV];
   ring_stream<D>(
       d / kChunk,
       [&](int ch, int slot) {
-        rg[slot] = ldg16(wg + ch * kChunk);
-        ru[slot] = ldg16(wu + ch * kChunk);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          rg[slot][r] = ldg16(wg[r] + ch * kChunk);
+          ru[slot][r] = ldg16(wu[r] + ch * kChunk);
+        }
 #pragma unroll
         for (int v = 0; v < kKV; ++v) rx[slot][v] = ldg16(xr + ch * kChunk + 8 * v);
       },
       [&](int u) {
-        accg = mfma16x16x32(e4m3x8_bf16(rg[u].x, rg[u].y), rx[u][0], accg);
-        accu = mfma16x16x32(e4m3x8_bf16(ru[u].x, ru[u].y), rx[u][0], accu);
-        accg = mfma16x16x32(e4m3x8_bf16(rg[u].z, rg[u].w), rx[u][1], accg);
-        accu = mfma16x16x32(e4m3x8_bf16(ru[u].z, ru[u].w), rx[u][1], accu);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          accg[r] = mfma16x16x32(e4m3x8_bf16(rg[u][r].x, rg[u][r].y), rx[u][0], accg[r]);
+          accu[r] = mfma16x16x32(e4m3x8_bf16(ru[u][r].x, ru[u][r].y), rx[u][0], accu[r]);
+          accg[r] = mfma16x16x32(e4m3x8_bf16(rg[u][r].z, rg[u][r].w), rx[u][1], accg[r]);
+          accu[r] = mfma16x16x32(e4m3x8_bf16(ru[u][r].z, ru[u][r].w), rx[u][1], accu[r]);
+        }
       });
 }
 
-template <int D>
-__device__ __forceinline__ void down_fp8_block(const uint8_t* __restrict__ wd, const uint16_t* __restrict__ hr, int I,
-                                               f32x4& acc) {
-  uint4 rw[D + 1], rx[D + 1][kKV];
+template <int D, int NR>
+__device__ __forceinline__ void down_fp8_block(const uint8_t* const (&wd)[NR], const uint16_t* __restrict__ hr, int I,
+                                               f32x4 (&acc)[NR]) {
+  uint4 rw[D + 1][NR], rx[D + 1][kKV];
   ring_stream<D>(
       I / kChunk,
       [&](int ch, int slot) {
-        rw[slot] = ldg16(wd + ch * kChunk);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) rw[slot][r] = ldg16(wd[r] + ch * kChunk);
 #pragma unroll
         for (int v = 0; v < kKV; ++v) rx[slot][v] = ldg16(hr + ch * kChunk + 8 * v);
       },
       [&](int u) {
-        acc = mfma16x16x32(e4m3x8_bf16(rw[u].x, rw[u].y), rx[u][0], acc);
-        acc = mfma16x16x32(e4m3x8_bf16(rw[u].z, rw[u].w), rx[u][1], acc);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          acc[r] = mfma16x16x32(e4m3x8_bf16(rw[u][r].x, rw[u][r].y), rx[u][0], acc[r]);
+          acc[r] = mfma16x16x32(e4m3x8_bf16(rw[u][r].z, rw[u][r].w), rx[u][1], acc[r]);
+        }
       });
 }
 
@@ -268,64 +281,75 @@ __device__ __forceinline__ void tern_rows_block(const uint32_t* const (*q)[NR], 
 }
 
 // ------------------------------------------------------------------ kernels
-// Grid rows (blockIdx.y): in the ternary kernels the first ones each take one 16-token
-// pass and one 64-row half of the shared expert (bf16 there, and much larger than a
-// ternary expert), so its passes run side by side from the start instead of one after
-// another; in the bf16 kernels the shared expert has one row. Then one touched routed
-// expert each (touched[0] is the shared expert).
+// Grid rows (blockIdx.y): in the ternary and FP8 kernels (128 rows per workgroup) the
+// first ones each take one 16-token pass and one 64-row half of the shared expert (bf16
+// there, and larger than a ternary or FP8 expert), so its passes run side by side from
+// the start instead of one after another; in the bf16 kernels the shared expert has one
+// row. Then one touched routed expert each (touched[0] is the shared expert).
 __device__ __forceinline__ int shared_slots(const StreamArgs& a, bool tern) {
   return tern ? ((a.Tk / a.k + 15) / 16) * 2 : 1;
 }
 
 template <int WF>
 __global__ void __launch_bounds__(256) stream_gateup_kernel(StreamArgs a, ExpertWeights w, uint16_t* __restrict__ h) {
-  constexpr bool TERN = WF == kWfTern, FP8 = WF == kWfFp8;
+  constexpr bool TERN = WF == kWfTern, FP8 = WF == kWfFp8, WIDE = TERN || FP8;
   __shared__ uint2 lut[32];
   if (TERN) {
     build_code_table(lut);
     __syncthreads();
   }
   // plain scalars (a struct here ended up in scratch memory)
-  const int sh = shared_slots(a, TERN), slot = blockIdx.y;
+  const int sh = shared_slots(a, WIDE), slot = blockIdx.y;
   const bool shared_part = slot < sh;
   const int ridx = slot - sh + 1;
   if (!shared_part && ridx >= a.meta[0]) return;
   const int e = shared_part ? a.E : a.touched[ridx];
-  // ternary kernels: a shared-expert row takes one 16-token pass and one 64-row half
-  const int cb_first = (TERN && shared_part) ? 16 * (slot >> 1) : 0;
-  const int sub_first = (TERN && shared_part) ? (slot & 1) : 0;
-  const int sub_last = TERN ? (shared_part ? sub_first + 1 : 2) : 1;
+  // ternary and FP8 kernels: a shared-expert row takes one 16-token pass and one 64-row half
+  const int cb_first = (WIDE && shared_part) ? 16 * (slot >> 1) : 0;
+  const int sub_first = (WIDE && shared_part) ? (slot & 1) : 0;
+  const int sub_last = WIDE ? (shared_part ? sub_first + 1 : 2) : 1;
   const int row0 = a.offs[e];
-  const int n = (TERN && shared_part) ? min(a.offs[e + 1] - row0, cb_first + 16) : a.offs[e + 1] - row0;
+  const int n = (WIDE && shared_part) ? min(a.offs[e + 1] - row0, cb_first + 16) : a.offs[e + 1] - row0;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int r16 = lane & 15, g = lane >> 4;
   const int d = a.d, I = a.I;
   const bool routed = e < a.E;
 
   if (FP8 && routed) {
-    // E4M3 routed expert: rows i0 + r16, 16 token columns per pass, each row's sums
-    // times its fp32 scale; D row 4g + j of the wave is hidden unit i0 + 4g + j
-    const int i0 = blockIdx.x * 64 + wv * 16;
-    const uint8_t* wg = w.f8gate + ((size_t)e * I + i0 + r16) * d + 16 * g;
-    const uint8_t* wu = w.f8up + ((size_t)e * I + i0 + r16) * d + 16 * g;
-    float sg[4], su[4];
+    // E4M3 routed expert: rows i0 + 16 r + r16 (r < NR), 16 token columns per pass, each
+    // row's sums times its fp32 scale; D row 4g + j of block r is unit i0 + 16r + 4g + j
+    constexpr int NR = kFp8RowBlocks;
+    const int i0 = blockIdx.x * 128 + wv * 16 * NR;
+    const uint8_t* wg[NR];
+    const uint8_t* wu[NR];
+    float sg[NR][4], su[NR][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sg[j] = w.f8sgate[(size_t)e * I + i0 + 4 * g + j];
-      su[j] = w.f8sup[(size_t)e * I + i0 + 4 * g + j];
+    for (int r = 0; r < NR; ++r) {
+      wg[r] = w.f8gate + ((size_t)e * I + i0 + 16 * r + r16) * d + 16 * g;
+      wu[r] = w.f8up + ((size_t)e * I + i0 + 16 * r + r16) * d + 16 * g;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sg[r][j] = w.f8sgate[(size_t)e * I + i0 + 16 * r + 4 * g + j];
+        su[r][j] = w.f8sup[(size_t)e * I + i0 + 16 * r + 4 * g + j];
+      }
     }
     for (int cb = 0; cb < n; cb += 16) {
       const bool valid = cb + r16 < n;
       const int col = valid ? row0 + cb + r16 : row0;
       const uint16_t* xr = a.x + (size_t)row_token(col, a.perm_src, a.Tk, a.k) * d + 16 * g;
-      f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-      gateup_fp8_block<kDepthFp8GateUp>(wg, wu, xr, d, accg, accu);
-      if (valid) {
-        float hv[4];
+      f32x4 accg[NR], accu[NR];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) hv[j] = silu(accg[j] * sg[j]) * (accu[j] * su[j]);
-        *reinterpret_cast<uint2*>(h + (size_t)col * I + i0 + 4 * g) =
-            make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+      for (int r = 0; r < NR; ++r) accg[r] = accu[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+      gateup_fp8_block<kDepthFp8GateUp, NR>(wg, wu, xr, d, accg, accu);
+      if (valid) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          float hv[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) hv[j] = silu(accg[r][j] * sg[r][j]) * (accu[r][j] * su[r][j]);
+          *reinterpret_cast<uint2*>(h + (size_t)col * I + i0 + 16 * r + 4 * g) =
+              make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+        }
       }
     }
     return;
@@ -336,7 +360,7 @@ __global__ void __launch_bounds__(256) stream_gateup_kernel(StreamArgs a, Expert
     // 16 token columns per pass
 #pragma unroll 1
     for (int sub = sub_first; sub < sub_last; ++sub) {
-    const int i0 = blockIdx.x * (TERN ? 128 : 64) + sub * 64 + wv * 16;
+    const int i0 = blockIdx.x * (WIDE ? 128 : 64) + sub * 64 + wv * 16;
     const uint16_t* wg = (routed ? w.gate + (size_t)e * I * d : w.s_gate) + (size_t)(i0 + r16) * d + kKV * 8 * g;
     const uint16_t* wu = (routed ? w.up + (size_t)e * I * d : w.s_up) + (size_t)(i0 + r16) * d + kKV * 8 * g;
     for (int cb = cb_first; cb < n; cb += 16) {
@@ -344,7 +368,7 @@ __global__ void __launch_bounds__(256) stream_gateup_kernel(StreamArgs a, Expert
       const int col = valid ? row0 + cb + r16 : row0;
       const uint16_t* xr = a.x + (size_t)row_token(col, a.perm_src, a.Tk, a.k) * d + kKV * 8 * g;
       f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-      gateup_bf16_block<TERN ? kDepthSharedTern : kDepthGateUp>(wg, wu, xr, d, accg, accu);
+      gateup_bf16_block<WIDE ? kDepthSharedTern : kDepthGateUp>(wg, wu, xr, d, accg, accu);
       if (valid) {
         uint2 v = make_uint2(pack_bf16x2(silu(accg[0]) * accu[0], silu(accg[1]) * accu[1]),
                              pack_bf16x2(silu(accg[2]) * accu[2], silu(accg[3]) * accu[3]));
@@ -400,44 +424,55 @@ __global__ void __launch_bounds__(256) stream_gateup_kernel(StreamArgs a, Expert
 template <int WF>
 __global__ void __launch_bounds__(256) stream_down_kernel(StreamArgs a, ExpertWeights w,
                                                           const uint16_t* __restrict__ h, float* __restrict__ y) {
-  constexpr bool TERN = WF == kWfTern, FP8 = WF == kWfFp8;
+  constexpr bool TERN = WF == kWfTern, FP8 = WF == kWfFp8, WIDE = TERN || FP8;
   __shared__ uint2 lut[32];
   if (TERN) {
     build_code_table(lut);
     __syncthreads();
   }
   // plain scalars (a struct here ended up in scratch memory)
-  const int sh = shared_slots(a, TERN), slot = blockIdx.y;
+  const int sh = shared_slots(a, WIDE), slot = blockIdx.y;
   const bool shared_part = slot < sh;
   const int ridx = slot - sh + 1;
   if (!shared_part && ridx >= a.meta[0]) return;
   const int e = shared_part ? a.E : a.touched[ridx];
-  // ternary kernels: a shared-expert row takes one 16-token pass and one 64-row half
-  const int cb_first = (TERN && shared_part) ? 16 * (slot >> 1) : 0;
-  const int sub_first = (TERN && shared_part) ? (slot & 1) : 0;
-  const int sub_last = TERN ? (shared_part ? sub_first + 1 : 2) : 1;
+  // ternary and FP8 kernels: a shared-expert row takes one 16-token pass and one 64-row half
+  const int cb_first = (WIDE && shared_part) ? 16 * (slot >> 1) : 0;
+  const int sub_first = (WIDE && shared_part) ? (slot & 1) : 0;
+  const int sub_last = WIDE ? (shared_part ? sub_first + 1 : 2) : 1;
   const int row0 = a.offs[e];
-  const int n = (TERN && shared_part) ? min(a.offs[e + 1] - row0, cb_first + 16) : a.offs[e + 1] - row0;
+  const int n = (WIDE && shared_part) ? min(a.offs[e + 1] - row0, cb_first + 16) : a.offs[e + 1] - row0;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int r16 = lane & 15, g = lane >> 4;
   const int d = a.d, I = a.I;
   const bool routed = e < a.E;
 
   if (FP8 && routed) {
-    // E4M3 routed expert: output rows m0 + r16, sums times the rows' fp32 scales
-    const int m0 = blockIdx.x * 64 + wv * 16;
-    const uint8_t* wd = w.f8down + ((size_t)e * d + m0 + r16) * I + 16 * g;
-    float sd[4];
+    // E4M3 routed expert: output rows m0 + 16 r + r16 (r < NR), sums times the rows'
+    // fp32 scales
+    constexpr int NR = kFp8RowBlocks;
+    const int m0 = blockIdx.x * 128 + wv * 16 * NR;
+    const uint8_t* wd[NR];
+    float sd[NR][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sd[j] = w.f8sdown[(size_t)e * d + m0 + 4 * g + j];
+    for (int r = 0; r < NR; ++r) {
+      wd[r] = w.f8down + ((size_t)e * d + m0 + 16 * r + r16) * I + 16 * g;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sd[r][j] = w.f8sdown[(size_t)e * d + m0 + 16 * r + 4 * g + j];
+    }
     for (int cb = 0; cb < n; cb += 16) {
       const bool valid = cb + r16 < n;
       const int col = valid ? row0 + cb + r16 : row0;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      down_fp8_block<kDepthFp8Down>(wd, h + (size_t)col * I + 16 * g, I, acc);
-      if (valid)
-        *reinterpret_cast<float4*>(y + (size_t)col * d + m0 + 4 * g) =
-            make_float4(acc[0] * sd[0], acc[1] * sd[1], acc[2] * sd[2], acc[3] * sd[3]);
+      f32x4 acc[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+      down_fp8_block<kDepthFp8Down, NR>(wd, h + (size_t)col * I + 16 * g, I, acc);
+      if (valid) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+          *reinterpret_cast<float4*>(y + (size_t)col * d + m0 + 16 * r + 4 * g) =
+              make_float4(acc[r][0] * sd[r][0], acc[r][1] * sd[r][1], acc[r][2] * sd[r][2], acc[r][3] * sd[r][3]);
+      }
     }
     return;
   }
@@ -445,13 +480,13 @@ __global__ void __launch_bounds__(256) stream_down_kernel(StreamArgs a, ExpertWe
   if (!TERN || !routed) {
 #pragma unroll 1
     for (int sub = sub_first; sub < sub_last; ++sub) {
-    const int m0 = blockIdx.x * (TERN ? 128 : 64) + sub * 64 + wv * 16;
+    const int m0 = blockIdx.x * (WIDE ? 128 : 64) + sub * 64 + wv * 16;
     const uint16_t* wd = (routed ? w.down + (size_t)e * d * I : w.s_down) + (size_t)(m0 + r16) * I + kKV * 8 * g;
     for (int cb = cb_first; cb < n; cb += 16) {
       const bool valid = cb + r16 < n;
       const int col = valid ? row0 + cb + r16 : row0;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      down_bf16_block<TERN ? kDepthSharedTern : kDepthDown>(wd, h + (size_t)col * I + kKV * 8 * g, I, acc);
+      down_bf16_block<WIDE ? kDepthSharedTern : kDepthDown>(wd, h + (size_t)col * I + kKV * 8 * g, I, acc);
       if (valid)
         *reinterpret_cast<float4*>(y + (size_t)col * d + m0 + 4 * g) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
@@ -713,7 +748,7 @@ hipError_t launch_stream_experts(const Plan& p, const uint16_t* x, const ExpertW
                                  Marks& m) {
   StreamArgs a{x, p.touched, p.meta, p.offs, p.perm_src, p.Tk, p.k, p.d, p.I, p.E};
   const int routed = p.Tk < p.E ? p.Tk : p.E;  // at most this many touched routed experts
-  const int sh = w.ternary ? ((p.T + 15) / 16) * 2 : 1;
+  const int sh = (w.ternary || w.fp8) ? ((p.T + 15) / 16) * 2 : 1;
   const int passes = (p.T + 15) / 16;
   if (tern_lds_eligible(p, w)) {
     // LDS-staged ternary kernels, the shared expert's rows first in each grid
@@ -728,8 +763,8 @@ hipError_t launch_stream_experts(const Plan& p, const uint16_t* x, const ExpertW
     return err == hipSuccess ? m.mark(s) : err;
   }
   const int slots = routed + sh;
-  // ternary kernels: 128 rows per workgroup (d and I are multiples of 128)
-  const int rows_wg = w.ternary ? 128 : 64;
+  // ternary and FP8 kernels: 128 rows per workgroup (d and I are multiples of 128)
+  const int rows_wg = (w.ternary || w.fp8) ? 128 : 64;
   dim3 g1(p.I / rows_wg, slots), g2(p.d / rows_wg, slots);
   const auto gu = w.ternary ? stream_gateup_kernel<kWfTern>
                   : w.fp8   ? stream_gateup_kernel<kWfFp8>
