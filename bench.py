@@ -165,7 +165,7 @@ def run_config(name, args, hi, hm, torch, weights=None):
     torch.cuda.synchronize()
     counts = routing["counts"].cpu()
     touched = int((counts > 0).sum())
-    stream_path = cfg.fp8 or cfg.T * cfg.k <= 16 * cfg.E  # the library's automatic path choice
+    stream_path = cfg.T * cfg.k <= 16 * cfg.E  # the library's automatic path choice
     d, I = cfg.d, cfg.I
     kernel_file = "sparse_moe_transformer_route_amd/csrc/" + ("moe_stream.hip" if stream_path else "moe_gemm.hip")
     if stream_path:
@@ -208,8 +208,10 @@ def run_config(name, args, hi, hm, torch, weights=None):
         sec = dom_ms * 1e-3
         roof = {"bound": "mfma", "achieved": alg / sec / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
                 "frac": alg / sec / PEAK_BF16, "traffic": traffic_for(f"grouped_gemm_gateup/{name}", rows),
-                "kernel": ("grouped_gemm_kernel<true, 0, true> (ternary routed tiles) + grouped_gemm_kernel<true, 0, "
-                           "false> (bf16 shared tiles): one timed stage" if cfg.ternary else "grouped_gemm_kernel<true>"),
+                "kernel": ("grouped_gemm_kernel<true, 0, 1> (ternary routed tiles) + grouped_gemm_kernel<true, 0, 0> "
+                           "(bf16 shared tiles): one timed stage" if cfg.ternary else
+                           "grouped_gemm_kernel<true, 0, 2> (FP8 routed tiles) + grouped_gemm_kernel<true, 0, 0> "
+                           "(bf16 shared tiles): one timed stage" if cfg.fp8 else "grouped_gemm_kernel<true, 0, 0>"),
                 "per_unit": f"{4 * d * I} flop per dispatched row "
                 f"(gate and up: 2*d*I each)", "units_per_launch": rows, "kernel_ms": dom_ms}
         flops = 2 * cfg.T * d * cfg.E + 6 * rows * d * I
@@ -297,7 +299,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed steps before the timed ones (default: at least 5 and %.1f s of them)" % WARMUP_MIN_S)
     ap.add_argument("--config", default="decode", choices=["tiny", "decode", "prefill", "skewed", "ternary",
-                                                                 "ternary_prefill", "fp8"])
+                                                                 "ternary_prefill", "fp8", "fp8_prefill"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the T=8192 measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)

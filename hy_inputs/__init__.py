@@ -66,6 +66,7 @@ CONFIGS = {
     "ternary": LayerConfig("ternary", T=32, d=6144, E=256, k=8, I=2048, ternary=True),
     # routed experts as FP8 (E4M3 codes, fp32 row scales), decode batch
     "fp8": LayerConfig("fp8", T=32, d=6144, E=256, k=8, I=2048, fp8=True),
+    "fp8_prefill": LayerConfig("fp8_prefill", T=8192, d=6144, E=256, k=8, I=2048, fp8=True),
     # the ternary experts at a prefill-sized batch (grouped GEMM on decoded codes)
     "ternary_prefill": LayerConfig("ternary_prefill", T=8192, d=6144, E=256, k=8, I=2048, ternary=True),
 }
@@ -232,8 +233,10 @@ def fp8_codes_from_bytes(b):
 
 
 def fp8_scale_exponent(cols: int) -> int:
-    """Row scales are m * 2^-(15 + p) with m in [0x6000, 0xE000): about 1/sqrt(cols)."""
-    return int(math.floor(0.5 * math.log2(cols)))
+    """Row scales are m * 2^-(15 + p) with m in [0x6000, 0xE000) (mean 1.25 * 2^-p); the
+    codes' mean |value| is 0.674, so p = round(log2(sqrt(cols) / 0.947)) makes the mean
+    |weight| that of the bf16 weights (std 1/sqrt(cols)) within a factor of sqrt(2)."""
+    return int(round(0.5 * math.log2(cols) + 0.078))
 
 
 def fp8_scales_from_words(w, cols: int):

@@ -78,8 +78,8 @@ typedef enum {
    * exponent bits 6-3 with bias 7, mantissa bits 2-0; exponent 0 is subnormal,
    * S.1111.111 is NaN, no infinities), each output row has one fp32 scale, and
    * weight = scale * value. Activations and the shared expert stay bf16; a NaN
-   * code gives NaN outputs. Streaming path only (HY_MOE_PATH_GROUPED returns
-   * HY_MOE_ERR_UNSUPPORTED; HY_MOE_PATH_AUTO streams every batch size). */
+   * code gives NaN outputs. The kernels convert the codes to bf16 exactly (every
+   * E4M3 value is a bf16 value) and scale the fp32 sums. */
   HY_MOE_WEIGHTS_FP8_E4M3 = 2
 } hy_moe_wfmt;
 
@@ -91,9 +91,9 @@ typedef enum {
                               used when d and I are multiples of 512); meant for decode-sized
                               batches */
   HY_MOE_PATH_GROUPED = 2  /* LDS-tiled grouped GEMM on bf16 MFMA; prefill-sized batches. Sherry
-                              codes are decoded to bf16 +1/0/-1 operands on the fly (the row scales
-                              are applied to the sums); the bf16 shared expert runs in its own
-                              launches of the bf16 kernel */
+                              and FP8 codes are decoded to bf16 operands on the fly (the row scales
+                              are applied to the sums); with them the bf16 shared expert runs in
+                              its own launches of the bf16 kernel */
 } hy_moe_path;
 
 /*

@@ -74,4 +74,15 @@ __device__ __forceinline__ int row_token(int r, const int* __restrict__ perm_src
   return r < Tk ? perm_src[r] / k : r - Tk;
 }
 
+// Eight FP8 E4M3 codes (code i in byte i of lo, hi) to eight bf16 values with the gfx950
+// conversion instruction; every E4M3 value, subnormals included, is a bf16 value, so the
+// conversion is exact (NaN codes give NaN).
+template <bool HI>  // codes 0-1 or 2-3 of the word
+__device__ __forceinline__ uint32_t e4m3x2_bf16(uint32_t v) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, HI));
+}
+__device__ __forceinline__ uint4 e4m3x8_bf16(uint32_t lo, uint32_t hi) {
+  return make_uint4(e4m3x2_bf16<false>(lo), e4m3x2_bf16<true>(lo), e4m3x2_bf16<false>(hi), e4m3x2_bf16<true>(hi));
+}
+
 }  // namespace hymoe

@@ -98,7 +98,6 @@ int check_args(const hy_moe_args* a) {
     const void* sc[] = {a->S_gate, a->S_up, a->S_down};
     for (const void* p : sc)
       if (!p || !aligned(p, 4)) return HY_MOE_ERR_INVALID_ARG;
-    if (a->path == HY_MOE_PATH_GROUPED) return HY_MOE_ERR_UNSUPPORTED;
   }
   if (a->path == HY_MOE_PATH_GROUPED && !grouped_fits(a->T, a->d, a->k, a->I)) return HY_MOE_ERR_UNSUPPORTED;
   const void* opt4[] = {a->topk_idx, a->topk_w, a->counts, a->offsets, a->perm_src, a->margin};
@@ -179,7 +178,7 @@ extern "C" int hy_moe_forward_ex(const hy_moe_args* a, void* stream) {
   else if (a->path == HY_MOE_PATH_GROUPED)
     stream_path = false;
   else
-    stream_path = w.fp8 || (int64_t)p.Tk <= 16 * (int64_t)p.E || !grouped_fits(p.T, p.d, p.k, p.I);
+    stream_path = (int64_t)p.Tk <= 16 * (int64_t)p.E || !grouped_fits(p.T, p.d, p.k, p.I);
 
   const uint16_t* x = (const uint16_t*)a->x;
   Marks marks{a->stage_events, 0};

@@ -63,6 +63,17 @@ constexpr int kCodePitch = 16;
 constexpr int kCodeSlot = kRowsMax * kCodePitch;  // 4 KB
 constexpr int kCodeOps = kCodeSlot / 4 / kThreads;  // 4
 constexpr int kScaleBytes = 512;                    // an item's 256 row scales (bf16)
+// FP8 (E4M3) weights: a row's 64 codes of a k step (4 pieces of 16 bytes) go to the
+// row's 64-byte line of a 16 KB slot, piece p at p ^ f8_key(row); each lane reads the
+// 8 codes of its fragment with one 8-byte LDS read and converts them to bf16 (exact).
+constexpr int kF8Pitch = 64;
+constexpr int kF8Slot = kRowsMax * kF8Pitch;         // 16 KB
+constexpr int kF8Ops = kF8Slot / 16 / kThreads;      // 4 direct-to-LDS ops per thread per step
+constexpr int kF8ScaleBytes = kRowsMax * 4;          // an item's 256 row scales (fp32)
+static_assert(kF8Ops == kCodeOps, "the code and FP8 load offsets share storage");
+
+// Weight formats of the routed experts' tiles.
+constexpr int kGemmBf16 = 0, kGemmTern = 1, kGemmFp8 = 2;
 
 
 int grouped_gemm_bm() { return kRowsMax; }
@@ -108,6 +119,10 @@ __device__ __forceinline__ void bare_barrier() {
 // row % 8 puts rows r and r + 8 on the same banks: every fragment read took twice
 // as long.)
 __device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
+
+// FP8 piece swizzle: 32 lanes reading 8 bytes at one logical piece of rows 0..31 fall
+// on 16 distinct bank pairs (2 lanes each) instead of 4.
+__device__ __forceinline__ int f8_key(int row) { return (row >> 2) & 3; }
 
 // Two floats to packed bf16 (round to nearest even, one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
@@ -167,24 +182,37 @@ __device__ __forceinline__ void for_seq(std::integer_sequence<int, T...>, F&& f)
 
 // TAILR = (K / kBK) mod 6 (0, 2 or 4: K is a multiple of 128): the k loop runs whole
 // periods of the 2 x 3 slot pattern and ends with a tail of that many steps.
-// TERN: routed experts' weights are Sherry ternary codes with bf16 row scales (the
-// shared expert's tiles run in the bf16 kernel); each lane decodes the codes of its
-// B fragments through a 32-entry LDS table into bf16 +1/0/-1, and the scales are
-// applied in the epilogue.
-template <bool GATEUP, int TAILR, bool TERN>
+// WF = kGemmTern: routed experts' weights are Sherry ternary codes with bf16 row scales
+// (the shared expert's tiles run in the bf16 kernel); each lane decodes the codes of
+// its B fragments through a 32-entry LDS table into bf16 +1/0/-1, and the scales are
+// applied in the epilogue. WF = kGemmFp8: E4M3 codes with fp32 row scales, converted
+// to bf16 per fragment, scales likewise in the epilogue.
+template <bool GATEUP, int TAILR, int WF>
 __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, ExpertWeights w,
                                                                    uint16_t* __restrict__ h,
                                                                    uint16_t* __restrict__ y) {
-  constexpr int BS = 3;                          // weight (or code) ring slots
-  constexpr int kBOps = TERN ? kCodeOps : kDma;  // weight-side load ops per thread per step
+  constexpr bool TERN = WF == kGemmTern, FP8 = WF == kGemmFp8;
+  constexpr int BS = 3;  // weight (or code) ring slots
+  constexpr int kBOps = TERN ? kCodeOps : FP8 ? kF8Ops : kDma;  // weight-side load ops per thread per step
   // Separate LDS arrays rather than one carved buffer: the compiler tells direct-to-LDS
   // loads and LDS reads of different arrays apart; within one array it would wait for
   // every such load in flight before each LDS read.
-  uint8_t *sa0, *sa1, *sb0, *sb1;  // activation slots; sb0, sb1: epilogue pieces 2 and 3
-  uint8_t* sr[3];                  // weight (bf16) or code (ternary) ring slots
+  uint8_t *sa0, *sa1, *sb0 = nullptr, *sb1 = nullptr;  // activation slots; sb0, sb1: epilogue pieces 2, 3
+  uint8_t* sr[3];                  // weight (bf16, FP8) or code (ternary) ring slots
   uint2* lut = nullptr;            // ternary: the code table
-  uint8_t* ssc = nullptr;          // ternary: the item's row scales
-  if constexpr (TERN) {
+  uint8_t* ssc = nullptr;          // ternary, FP8: the item's row scales
+  if constexpr (FP8) {
+    // the down epilogue stages its 4 pieces in two rounds through the activation slots
+    __shared__ __attribute__((aligned(16))) uint8_t fa0[kHalf];
+    __shared__ __attribute__((aligned(16))) uint8_t fa1[kHalf];
+    __shared__ __attribute__((aligned(16))) uint8_t fr0[kF8Slot];
+    __shared__ __attribute__((aligned(16))) uint8_t fr1[kF8Slot];
+    __shared__ __attribute__((aligned(16))) uint8_t fr2[kF8Slot];
+    __shared__ __attribute__((aligned(16))) uint8_t fsc[kF8ScaleBytes];
+    sa0 = fa0, sa1 = fa1;
+    sr[0] = fr0, sr[1] = fr1, sr[2] = fr2;
+    ssc = fsc;
+  } else if constexpr (TERN) {
     __shared__ __attribute__((aligned(16))) uint8_t ta0[kHalf];
     __shared__ __attribute__((aligned(16))) uint8_t ta1[kHalf];
     __shared__ __attribute__((aligned(16))) uint8_t te0[GATEUP ? 16 : kHalf];  // the down epilogue only
@@ -289,6 +317,11 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
     uint32_t frag_lo[kSub];
 #pragma unroll
     for (int s = 0; s < kSub; ++s) frag_lo[s] = (uint32_t)(r32 * kRowBytes + (((2 * s + hf) ^ swz_key(r32)) << 4));
+    // FP8: the 8 codes of group s (bytes [16 s + 8 hf, +8) of the row's step) sit in
+    // piece s ^ f8_key(r32) of the row's line (blocks start at multiples of 32 rows)
+    uint32_t f8o[kSub];
+#pragma unroll
+    for (int s = 0; s < kSub; ++s) f8o[s] = (uint32_t)(r32 * kF8Pitch + 16 * (s ^ f8_key(r32)) + 8 * hf);
     // items of one expert (its c M tiles x NT N tiles) are ordered in blocks of up to
     // 4 M tiles, N tile major within a block, so the workgroups running together on
     // an XCD share both the activation rows and the weight tiles through its L2
@@ -390,6 +423,44 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
         }
       }
     }
+    // FP8 codes: op i of a thread loads physical piece lane % 4 (logical piece
+    // (lane % 4) ^ f8_key(row)) of the step's 64 bytes of tile row 64 i + 16 wv + lane / 4
+    // (rows as for the ternary codes) into byte 16 (4 row + lane % 4) of the slot
+    if constexpr (FP8) {
+      const uint32_t rb = (uint32_t)K;  // code bytes per weight row
+      const int rr = 16 * wv + (lane >> 2);
+      const uint32_t po = 16u * (uint32_t)((lane & 3) ^ f8_key(rr));  // f8_key(64 i + rr) == f8_key(rr)
+#pragma unroll
+      for (int i = 0; i < kF8Ops; ++i) {
+        if (GATEUP) {
+          const uint8_t* mat = (i & 1) == 0 ? w.f8gate : w.f8up;
+          cbase[i] = reinterpret_cast<const char*>(mat) + ((size_t)e * a.I + nt * (kRowsMax / 2) + 64 * (i >> 1)) * rb;
+          coff[i] = (uint32_t)rr * rb + po;
+        } else {
+          cbase[i] = reinterpret_cast<const char*>(w.f8down) + ((size_t)e * a.d + nt * kRowsMax) * rb;
+          coff[i] = (uint32_t)(min(nt * kRowsMax + 64 * i + rr, a.d - 1) - nt * kRowsMax) * rb + po;
+        }
+      }
+      // the item's fp32 row scales into LDS (wave 0, older than every k-loop load):
+      // gate/up units nt*128 + [0, 128) of the gate then the up matrix, or down columns
+      // nt*256 + [0, 256) clamped past d
+      if (wv == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float* src = GATEUP ? (i < 2 ? w.f8sgate : w.f8sup) + (size_t)e * a.I + nt * (kRowsMax / 2) +
+                                          64 * (i & 1) + lane
+                                    : w.f8sdown + (size_t)e * a.d + min(nt * kRowsMax + 64 * i + lane, a.d - 1);
+          __builtin_amdgcn_global_load_lds((const void*)src, HY_LDS(ssc + 256 * i), 4, 0, 0);
+        }
+      }
+    }
+    auto issue_f8 = [&](int ks, uint8_t* st) {
+      uint8_t* dc = st + 1024 * wv;
+#pragma unroll
+      for (int i = 0; i < kF8Ops; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(cbase[i] + coff[i] + kF8Pitch * ks), HY_LDS(dc + 4096 * i), 16,
+                                         0, 0);
+    };
     // the step's code words: byte 4 floor(10 ks / 4) of each row
     auto issue_c = [&](int ks, uint8_t* st) {
       const uint32_t so = (uint32_t)(10 * ks) & ~3u;
@@ -434,6 +505,9 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
     if constexpr (TERN) {
       issue_c(0, sb[0]);
       issue_c(1, sb[1]);
+    } else if constexpr (FP8) {
+      issue_f8(0, sb[0]);
+      issue_f8(1, sb[1]);
     } else {
       issue_b(0, sb[0], C0{}, CF{});
       issue_b(1, sb[1], C0{}, CF{});
@@ -447,6 +521,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
     auto k_loop = [&](auto nact_tag) {
       constexpr int NACT = decltype(nact_tag)::value;
       uint4 fa[2][kWaveBlocks], fb[2][kNB];
+      uint2 fc[2][kNB];  // FP8: each group's raw codes, converted right before its MFMAs
       // The previous group's reads are waited for (long done: a whole MFMA group ran
       // since) before this group's are issued, so at most 8 are in flight and the
       // MFMAs that follow need no wait.
@@ -456,8 +531,12 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
         for (int j = 0; j < NACT; ++j)
           fa[s & 1][j] = *reinterpret_cast<const uint4*>(La + fa_off + j * 2 * kBlk * kRowBytes + frag_lo[s]);
 #pragma unroll
-        for (int nb = 0; nb < kNB; ++nb)
-          fb[s & 1][nb] = *reinterpret_cast<const uint4*>(Lb + fb_off + nb * kBlk * kRowBytes + frag_lo[s]);
+        for (int nb = 0; nb < kNB; ++nb) {
+          if constexpr (FP8)
+            fc[s & 1][nb] = *reinterpret_cast<const uint2*>(Lb + (128 * wn + 32 * nb) * kF8Pitch + f8o[s]);
+          else
+            fb[s & 1][nb] = *reinterpret_cast<const uint4*>(Lb + fb_off + nb * kBlk * kRowBytes + frag_lo[s]);
+        }
       };
       // Ternary: the step's code windows of the lane's 4 weight rows (128 wn + 32 nb +
       // r32), read once per step; group S of the step (k [8 (2S + hf), +8)) takes the two
@@ -505,7 +584,13 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
 #pragma unroll
           for (int nb = 0; nb < kNB; ++nb) acc[j][nb] = mfma32x32x16(fb[s & 1][nb], fa[s & 1][j], acc[j][nb]);
       };
-      auto mfmas = [&](int s) { mfmas_rows(s, std::integral_constant<int, 0>{}, std::integral_constant<int, NACT>{}); };
+      auto mfmas = [&](int s) {
+        if constexpr (FP8) {
+#pragma unroll
+          for (int nb = 0; nb < kNB; ++nb) fb[s & 1][nb] = e4m3x8_bf16(fc[s & 1][nb].x, fc[s & 1][nb].y);
+        }
+        mfmas_rows(s, std::integral_constant<int, 0>{}, std::integral_constant<int, NACT>{});
+      };
       // One step ks on activation slot UA = ks % 2 and weight slot UB = ks % BS. The
       // slots step ks-1 used were freed by the barrier that ended it; their next loads
       // (the second half of the activations of step ks+1, the weights of step ks+2) go
@@ -531,13 +616,15 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
           if constexpr (S == 1 && PA) issue_a(ks + 1, sa[UA ^ 1], CH{}, CF{});
           if constexpr (TERN) {
             if constexpr (S == 2 && PB) issue_c(ks + 2, sb[(UB + 2) % BS]);
+          } else if constexpr (FP8) {
+            if constexpr (S == 2 && PB) issue_f8(ks + 2, sb[(UB + 2) % BS]);
           } else {
             if constexpr (S == 2 && PB) issue_b(ks + 2, sb[(UB + 2) % BS], C0{}, CH{});
             if constexpr (S == 3 && PB) issue_b(ks + 2, sb[(UB + 2) % BS], CH{}, CF{});
           }
           mfmas(S - 1);
-          constexpr int NV = TERN ? ((S == 1 && PA) ? kDma / 2 : (S == 2 && PB) ? kCodeOps : 0)
-                                  : ((S == 1 && PA) || (S >= 2 && PB)) ? kDma / 2 : 0;
+          constexpr int NV = (TERN || FP8) ? ((S == 1 && PA) ? kDma / 2 : (S == 2 && PB) ? kBOps : 0)
+                                           : ((S == 1 && PA) || (S >= 2 && PB)) ? kDma / 2 : 0;
           interleave_group<NACT * kNB, NACT + (TERN ? 2 : 1) * kNB, NV>();
           __builtin_amdgcn_sched_barrier(0);
         });
@@ -613,55 +700,19 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
     bare_barrier();
 
     // Epilogue through LDS: the tile is written as 256-row x 64-column bf16 pieces of
-    // 32 KB (one ring slot each: sa0, sa1, sb0, sb1; 128 B per row; 16-byte chunk c of
-    // row r sits at c ^ swz_key(r)), then leaves with 16-byte stores of whole row
-    // segments. Accumulator i of lane (r32, hf) is output row r32 of its 32-row block,
-    // column 8 (i / 4) + 4 hf + i % 4 of its 32-column block, so each quad of
-    // accumulators is 8 contiguous bytes: one 8-byte LDS write. gate/up: piece wn holds
-    // h units nt*128 + 64 wn + [0, 64); down: piece 2 wn + nb/2 holds y columns
-    // nt*256 + 64 (2 wn + nb/2) + [0, 64).
-#pragma unroll
-    for (int j = 0; j < kWaveBlocks; ++j) {
-      const int rb = 2 * j + wm;
-      if (rb >= nrb) continue;  // wave-uniform
-      const int row = rb * kBlk + r32;
-#pragma unroll
-      for (int nb = 0; nb < (GATEUP ? kNB / 2 : kNB); ++nb) {
-        const int piece = GATEUP ? wn : 2 * wn + (nb >> 1);
-        uint8_t* const pb = piece == 0 ? sa0 : piece == 1 ? sa1 : piece == 2 ? sb0 : sb1;
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-          // ternary: the row scales of the quad's 4 columns (gate/up: unit 64 wn + 32 nb +
-          // 8 qd + 4 hf + t of the item's gate scales, then of its up scales at +128;
-          // down: column 128 wn + 32 nb + 8 qd + 4 hf + t)
-          float sg[4] = {1.f, 1.f, 1.f, 1.f}, su[4] = {1.f, 1.f, 1.f, 1.f};
-          if constexpr (TERN) {
-            const int c0 = (GATEUP ? 64 : 128) * wn + 32 * nb + 8 * qd + 4 * hf;
-            const uint2 g2 = *reinterpret_cast<const uint2*>(ssc + 2 * c0);
-            sg[0] = bf_lo(g2.x), sg[1] = bf_hi(g2.x), sg[2] = bf_lo(g2.y), sg[3] = bf_hi(g2.y);
-            if constexpr (GATEUP) {
-              const uint2 u2 = *reinterpret_cast<const uint2*>(ssc + 2 * (c0 + kRowsMax / 2));
-              su[0] = bf_lo(u2.x), su[1] = bf_hi(u2.x), su[2] = bf_lo(u2.y), su[3] = bf_hi(u2.y);
-            }
-          }
-          float v[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int i = 4 * qd + t;
-            if constexpr (TERN)
-              v[t] = GATEUP ? silu_fast(acc[j][nb][i] * sg[t]) * (acc[j][nb + kNB / 2][i] * su[t])
-                            : acc[j][nb][i] * sg[t];
-            else
-              v[t] = GATEUP ? silu_fast(acc[j][nb][i]) * acc[j][nb + kNB / 2][i] : acc[j][nb][i];
-          }
-          const int chunk = GATEUP ? 4 * nb + qd : 4 * (nb & 1) + qd;  // 16-byte chunk of the piece row
-          const uint32_t off = row * 128 + ((chunk ^ swz_key(row)) << 4) + 8 * hf;
-          *reinterpret_cast<uint2*>(pb + off) = make_uint2(pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3]));
-        }
-      }
-    }
-    wait_lds();
-    bare_barrier();
+    // 32 KB (sa0, sa1, sb0, sb1; 128 B per row; 16-byte chunk c of row r sits at
+    // c ^ swz_key(r)), then leaves with 16-byte stores of whole row segments. Accumulator
+    // i of lane (r32, hf) is output row r32 of its 32-row block, column 8 (i / 4) + 4 hf +
+    // i % 4 of its 32-column block, so each quad of accumulators is 8 contiguous bytes:
+    // one 8-byte LDS write. gate/up: piece wn holds h units nt*128 + 64 wn + [0, 64);
+    // down: piece 2 wn + nb/2 holds y columns nt*256 + 64 (2 wn + nb/2) + [0, 64). The FP8
+    // down kernel has no sb0/sb1 (its weight ring and the activation slots fill the LDS):
+    // it stages pieces 0-1 (waves wn = 0), writes them out, then pieces 2-3, both in
+    // sa0/sa1.
+    constexpr int NPIECE = GATEUP ? 2 : 4;
+    constexpr int ROUNDS = (FP8 && !GATEUP) ? 2 : 1;
+    constexpr int PPR = NPIECE / ROUNDS;  // pieces staged per round
+    auto piece_buf = [&](int lp) -> uint8_t* { return lp == 0 ? sa0 : lp == 1 ? sa1 : lp == 2 ? sb0 : sb1; };
     // A piece's 8 row groups are read from LDS first, then stored, so no store waits on
     // another.
     const int ldc = GATEUP ? a.I : a.d;
@@ -669,17 +720,78 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
     const uint32_t pl_off = (uint32_t)(orow * 128 + ((ch ^ swz_key(orow)) << 4));
     uint16_t* const obase = (GATEUP ? h : y) + (size_t)(ebase + m0 + orow) * ldc + ch * 8;
 #pragma unroll
-    for (int pc = 0; pc < (GATEUP ? 2 : 4); ++pc) {
-      const int col0 = GATEUP ? nt * (kRowsMax / 2) + 64 * pc : nt * kRowsMax + 64 * pc;
-      if (!GATEUP && col0 >= a.d) continue;  // d is a multiple of 128: whole pieces fall outside
-      const uint8_t* pbase = pc == 0 ? sa0 : pc == 1 ? sa1 : pc == 2 ? sb0 : sb1;
-      uint4 v[kRowsMax / 32];
+    for (int rd = 0; rd < ROUNDS; ++rd) {
 #pragma unroll
-      for (int it = 0; it < kRowsMax / 32; ++it)  // row it*32 + orow: same swizzle as orow
-        v[it] = *reinterpret_cast<const uint4*>(pbase + pl_off + it * 32 * 128);
+      for (int j = 0; j < kWaveBlocks; ++j) {
+        const int rb = 2 * j + wm;
+        if (rb >= nrb) continue;  // wave-uniform
+        const int row = rb * kBlk + r32;
 #pragma unroll
-      for (int it = 0; it < kRowsMax / 32; ++it)
-        if (it * 32 + orow < mrows) *reinterpret_cast<uint4*>(obase + (size_t)it * 32 * ldc + col0) = v[it];
+        for (int nb = 0; nb < (GATEUP ? kNB / 2 : kNB); ++nb) {
+          const int piece = GATEUP ? wn : 2 * wn + (nb >> 1);
+          if constexpr (ROUNDS > 1) {
+            if (piece / PPR != rd) continue;  // wave-uniform
+          }
+          uint8_t* const pb = piece_buf(piece - rd * PPR);
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            // ternary, FP8: the row scales of the quad's 4 columns (gate/up: unit 64 wn +
+            // 32 nb + 8 qd + 4 hf + t of the item's gate scales, then of its up scales at
+            // +128; down: column 128 wn + 32 nb + 8 qd + 4 hf + t)
+            float sg[4] = {1.f, 1.f, 1.f, 1.f}, su[4] = {1.f, 1.f, 1.f, 1.f};
+            const int c0 = (GATEUP ? 64 : 128) * wn + 32 * nb + 8 * qd + 4 * hf;
+            if constexpr (TERN) {
+              const uint2 g2 = *reinterpret_cast<const uint2*>(ssc + 2 * c0);
+              sg[0] = bf_lo(g2.x), sg[1] = bf_hi(g2.x), sg[2] = bf_lo(g2.y), sg[3] = bf_hi(g2.y);
+              if constexpr (GATEUP) {
+                const uint2 u2 = *reinterpret_cast<const uint2*>(ssc + 2 * (c0 + kRowsMax / 2));
+                su[0] = bf_lo(u2.x), su[1] = bf_hi(u2.x), su[2] = bf_lo(u2.y), su[3] = bf_hi(u2.y);
+              }
+            } else if constexpr (FP8) {
+              const float4 g4 = *reinterpret_cast<const float4*>(ssc + 4 * c0);
+              sg[0] = g4.x, sg[1] = g4.y, sg[2] = g4.z, sg[3] = g4.w;
+              if constexpr (GATEUP) {
+                const float4 u4 = *reinterpret_cast<const float4*>(ssc + 4 * (c0 + kRowsMax / 2));
+                su[0] = u4.x, su[1] = u4.y, su[2] = u4.z, su[3] = u4.w;
+              }
+            }
+            float v[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int i = 4 * qd + t;
+              if constexpr (TERN || FP8)
+                v[t] = GATEUP ? silu_fast(acc[j][nb][i] * sg[t]) * (acc[j][nb + kNB / 2][i] * su[t])
+                              : acc[j][nb][i] * sg[t];
+              else
+                v[t] = GATEUP ? silu_fast(acc[j][nb][i]) * acc[j][nb + kNB / 2][i] : acc[j][nb][i];
+            }
+            const int chunk = GATEUP ? 4 * nb + qd : 4 * (nb & 1) + qd;  // 16-byte chunk of the piece row
+            const uint32_t off = row * 128 + ((chunk ^ swz_key(row)) << 4) + 8 * hf;
+            *reinterpret_cast<uint2*>(pb + off) = make_uint2(pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3]));
+          }
+        }
+      }
+      wait_lds();
+      bare_barrier();
+#pragma unroll
+      for (int pc = rd * PPR; pc < (rd + 1) * PPR; ++pc) {
+        const int col0 = GATEUP ? nt * (kRowsMax / 2) + 64 * pc : nt * kRowsMax + 64 * pc;
+        if (!GATEUP && col0 >= a.d) continue;  // d is a multiple of 128: whole pieces fall outside
+        const uint8_t* pbase = piece_buf(pc - rd * PPR);
+        uint4 v[kRowsMax / 32];
+#pragma unroll
+        for (int it = 0; it < kRowsMax / 32; ++it)  // row it*32 + orow: same swizzle as orow
+          v[it] = *reinterpret_cast<const uint4*>(pbase + pl_off + it * 32 * 128);
+#pragma unroll
+        for (int it = 0; it < kRowsMax / 32; ++it)
+          if (it * 32 + orow < mrows) *reinterpret_cast<uint4*>(obase + (size_t)it * 32 * ldc + col0) = v[it];
+      }
+      if constexpr (ROUNDS > 1) {
+        if (rd + 1 < ROUNDS) {  // the next round's pieces overwrite the buffers just read
+          wait_lds();
+          bare_barrier();
+        }
+      }
     }
     // every thread has read its pieces before the next item's loads overwrite them
     wait_lds();
@@ -687,7 +799,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
   }
 }
 
-static int g_grid[4][64];  // persistent grid per (kernel kind, device), 0 = not yet computed
+static int g_grid[6][64];  // persistent grid per (kernel kind, device), 0 = not yet computed
 
 static int persistent_grid(int kind, const void* kernel) {
   int dev = 0;
@@ -705,10 +817,10 @@ static int persistent_grid(int kind, const void* kernel) {
 using GemmKern = void (*)(GemmArgs, ExpertWeights, uint16_t*, uint16_t*);
 
 // kernel for (phase, weight format, K): indexed by (K / kBK) mod 6 / 2
-template <bool GATEUP, bool TERN>
+template <bool GATEUP, int WF>
 static GemmKern pick_gemm(int K) {
-  static const GemmKern k[3] = {grouped_gemm_kernel<GATEUP, 0, TERN>, grouped_gemm_kernel<GATEUP, 2, TERN>,
-                                grouped_gemm_kernel<GATEUP, 4, TERN>};
+  static const GemmKern k[3] = {grouped_gemm_kernel<GATEUP, 0, WF>, grouped_gemm_kernel<GATEUP, 2, WF>,
+                                grouped_gemm_kernel<GATEUP, 4, WF>};
   return k[(K / kBK) % 6 / 2];
 }
 
@@ -724,18 +836,21 @@ hipError_t launch_grouped_experts(const Plan& p, const uint16_t* x, const Expert
                                   Marks& m) {
   GemmArgs a{x, p.perm_src, p.offs, p.meta, p.tiles, p.Tk, p.k, p.d, p.I, p.E, 0};
   hipError_t err;
-  if (!w.ternary) {
-    err = launch_gemm(pick_gemm<true, false>(p.d), 0, a, 0, w, p, s);
+  if (!w.ternary && !w.fp8) {
+    err = launch_gemm(pick_gemm<true, kGemmBf16>(p.d), 0, a, 0, w, p, s);
     if (err == hipSuccess) err = m.mark(s);
-    if (err == hipSuccess) err = launch_gemm(pick_gemm<false, false>(p.I), 1, a, 0, w, p, s);
+    if (err == hipSuccess) err = launch_gemm(pick_gemm<false, kGemmBf16>(p.I), 1, a, 0, w, p, s);
     return err == hipSuccess ? m.mark(s) : err;
   }
-  // ternary routed experts, then the bf16 shared expert, per phase
-  err = launch_gemm(pick_gemm<true, true>(p.d), 2, a, 1, w, p, s);
-  if (err == hipSuccess) err = launch_gemm(pick_gemm<true, false>(p.d), 0, a, 2, w, p, s);
+  // ternary or FP8 routed experts, then the bf16 shared expert, per phase
+  const GemmKern gu = w.ternary ? pick_gemm<true, kGemmTern>(p.d) : pick_gemm<true, kGemmFp8>(p.d);
+  const GemmKern dn = w.ternary ? pick_gemm<false, kGemmTern>(p.I) : pick_gemm<false, kGemmFp8>(p.I);
+  const int kind = w.ternary ? 2 : 4;
+  err = launch_gemm(gu, kind, a, 1, w, p, s);
+  if (err == hipSuccess) err = launch_gemm(pick_gemm<true, kGemmBf16>(p.d), 0, a, 2, w, p, s);
   if (err == hipSuccess) err = m.mark(s);
-  if (err == hipSuccess) err = launch_gemm(pick_gemm<false, true>(p.I), 3, a, 1, w, p, s);
-  if (err == hipSuccess) err = launch_gemm(pick_gemm<false, false>(p.I), 1, a, 2, w, p, s);
+  if (err == hipSuccess) err = launch_gemm(dn, kind + 1, a, 1, w, p, s);
+  if (err == hipSuccess) err = launch_gemm(pick_gemm<false, kGemmBf16>(p.I), 1, a, 2, w, p, s);
   return err == hipSuccess ? m.mark(s) : err;
 }
 

@@ -123,17 +123,6 @@ __device__ __forceinline__ void gateup_bf16_block(const uint16_t* __restrict__ w
 }
 
 // ------------------------------------------------------------- FP8 experts
-// Eight E4M3 codes (two words, code i in byte i) to eight bf16 values: every E4M3
-// value, subnormals included, is a bf16 value, so the conversion is exact (NaN codes
-// give NaN).
-template <bool HI>  // codes 0-1 or 2-3 of the word
-__device__ __forceinline__ uint32_t e4m3x2_bf16(uint32_t v) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, HI));
-}
-__device__ __forceinline__ uint4 e4m3x8_bf16(uint32_t lo, uint32_t hi) {
-  return make_uint4(e4m3x2_bf16<false>(lo), e4m3x2_bf16<true>(lo), e4m3x2_bf16<false>(hi), e4m3x2_bf16<true>(hi));
-}
-
 // As gateup_bf16_block with E4M3 weights, for NR row blocks sharing the activations:
 // per chunk a lane loads the 16 codes of k [16 g, 16 g + 16) of its gate and up row in
 // each block (one 16-byte load each), the same k as its two 8-element activation pieces.

@@ -7,6 +7,7 @@ path choice, caller workspace):
   ternary  T=32,   Sherry ternary routed experts, bf16 shared expert
   ternary_prefill  T=8192, the same weights on the grouped path
   fp8      T=32,   FP8 (E4M3, fp32 row scales) routed experts, bf16 shared expert
+  fp8_prefill  T=8192, the same weights on the grouped path
 The routing of every token (sets, weights, counts, offsets, permutation) is
 compared with the oracle; outputs are compared on sampled tokens, for which the
 oracle regenerates the touched experts' weights on the host from the same
@@ -149,6 +150,14 @@ def test_fp8_full_size():
     cfg = hi.CONFIGS["fp8"]
     inp = hi.dev_layer(cfg, device=DEV)
     run_full(cfg, inp, sample=[0, 13, 31])
+    del inp
+    torch.cuda.empty_cache()
+
+
+def test_fp8_prefill_full_size():
+    cfg = hi.CONFIGS["fp8_prefill"]
+    inp = hi.dev_layer(cfg, device=DEV)
+    run_full(cfg, inp, sample=[0, 4095, 8191])
     del inp
     torch.cuda.empty_cache()
 

@@ -199,7 +199,33 @@ def test_fp8_small(shape):
     run_small(cfg, hm.PATH_STREAM)
 
 
-def test_fp8_every_code():
+@pytest.mark.parametrize("shape", [
+    # grouped GEMM on FP8 codes; K / 64 mod 6 picks the k-loop tail (gate/up: d, down: I)
+    dict(T=64, d=256, E=16, k=2, I=128),     # one 32-row block per expert; tails 4 and 2
+    dict(T=300, d=768, E=8, k=2, I=384),     # ragged tiles; whole 6-step periods; 3 N tiles
+    dict(T=1100, d=640, E=4, k=1, I=256),    # two M tiles per expert; last down N tile half past d
+    dict(T=200, d=512, E=16, k=4, I=512),    # tails 2 and 2
+])
+def test_fp8_grouped_small(shape):
+    cfg = hi.LayerConfig("fp8g", fp8=True, seed=8, **shape)
+    run_small(cfg, hm.PATH_GROUPED)
+
+
+def test_fp8_paths_agree_mid_size():
+    say("[case] FP8 stream vs grouped at T=256 d=1024 E=32 k=4 I=512")
+    cfg = hi.LayerConfig("fp8mid", T=256, d=1024, E=32, k=4, I=512, fp8=True, seed=9)
+    inp = hi.dev_layer(cfg, device=DEV)
+    a = hm.forward_layer(inp, cfg.k, want_routing=True, path=hm.PATH_STREAM)
+    b = hm.forward_layer(inp, cfg.k, want_routing=True, path=hm.PATH_GROUPED)
+    torch.cuda.synchronize()
+    for key in ("topk_idx", "topk_w", "counts", "offsets", "perm_src", "margin"):
+        assert torch.equal(a[key], b[key]), key
+    fa, fb = a["out"].float(), b["out"].float()
+    assert ((fa - fb).abs() <= 2e-2 * (1 + fb.abs())).all()
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_fp8_every_code(path):
     # Expert e's weights are all E4M3 code e (the two NaN codes replaced by +-1), and
     # its row scales are 1 / |value|, so every expert computes +-1 weights: a wrong
     # conversion of any code (subnormals, zeros, 448) shows as a large error.
@@ -208,22 +234,18 @@ def test_fp8_every_code():
     codes[0x7F], codes[0xFF] = 0x38, 0xB8
     val = np.abs(oracle.fp8_decode(codes[None, :])[0])
     scale = np.where(val > 0, 1.0 / np.where(val > 0, val, 1.0), 1.0).astype(np.float32)
-    sd, si = 1.0 / np.sqrt(cfg.d), 1.0 / np.sqrt(cfg.I)
+    # gate/up sums over random activations grow like sqrt(d); the down sums add I equal
+    # terms (every hidden unit of an expert is the same), so that row scale is 1 / I and
+    # y stays O(1) (it is rounded to bf16 on the grouped path)
+    sd, si = 1.0 / np.sqrt(cfg.d), 1.0 / cfg.I
     chosen = {}
     for m, rows, cols, s in (("gate", cfg.I, cfg.d, sd), ("up", cfg.I, cfg.d, sd), ("down", cfg.d, cfg.I, si)):
         chosen["f" + m] = np.ascontiguousarray(np.broadcast_to(codes[:, None, None], (cfg.E, rows, cols)))
         chosen["fs" + m] = np.ascontiguousarray(np.broadcast_to((scale * s)[:, None], (cfg.E, rows)), np.float32)
-    res, _ = run_small(cfg, hm.PATH_STREAM, fp8_codes=chosen)
+    res, _ = run_small(cfg, path, fp8_codes=chosen)
     touched = int((res["counts"] > 0).sum().item())
     say(f"       experts touched: {touched} of 256")
     assert touched >= 240
-
-
-def test_fp8_grouped_path_unsupported():
-    cfg = hi.LayerConfig("fp8", T=8, d=256, E=16, k=2, I=128, fp8=True, seed=5)
-    inp = hi.dev_layer(cfg, device=DEV)
-    with pytest.raises(hm.HyMoeError):
-        hm.forward_layer(inp, cfg.k, path=hm.PATH_GROUPED)
 
 
 # ------------------------------------------------------------- determinism
