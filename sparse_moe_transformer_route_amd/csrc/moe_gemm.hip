@@ -64,8 +64,10 @@ constexpr int kCodeSlot = kRowsMax * kCodePitch;  // 4 KB
 constexpr int kCodeOps = kCodeSlot / 4 / kThreads;  // 4
 constexpr int kScaleBytes = 512;                    // an item's 256 row scales (bf16)
 // FP8 (E4M3) weights: a row's 64 codes of a k step (4 pieces of 16 bytes) go to the
-// row's 64-byte line of a 16 KB slot, piece p at p ^ f8_key(row); each lane reads the
-// 8 codes of its fragment with one 8-byte LDS read and converts them to bf16 (exact).
+// row's 64-byte line of a 16 KB slot, piece p at p ^ f8_key(row). The k order within a
+// step is permuted for FP8 (activations alike) so that each lane's codes for MFMA groups
+// 2q and 2q + 1 are one piece: one 16-byte LDS read per two groups, conflict free,
+// converted to bf16 (exact) right before each group's MFMAs.
 constexpr int kF8Pitch = 64;
 constexpr int kF8Slot = kRowsMax * kF8Pitch;         // 16 KB
 constexpr int kF8Ops = kF8Slot / 16 / kThreads;      // 4 direct-to-LDS ops per thread per step
@@ -120,8 +122,9 @@ __device__ __forceinline__ void bare_barrier() {
 // as long.)
 __device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
 
-// FP8 piece swizzle: 32 lanes reading 8 bytes at one logical piece of rows 0..31 fall
-// on 16 distinct bank pairs (2 lanes each) instead of 4.
+// FP8 piece swizzle: the 16 lanes of a 16-byte LDS read (rows r..r+15, one logical piece)
+// fall on 16 distinct bank quads; without it, on 4 (8-byte reads of the unpermuted order
+// measured ~3 conflict cycles per LDS instruction).
 __device__ __forceinline__ int f8_key(int row) { return (row >> 2) & 3; }
 
 // Two floats to packed bf16 (round to nearest even, one v_cvt_pk_bf16_f32).
@@ -314,14 +317,20 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
     // per-lane part of a fragment read for k group s: row r32 of a 32-row block, chunk
     // 2s + hf (lane half hf holds k [8(2s+hf), 8(2s+hf)+8) of the step), swizzled; the key
     // depends only on r32 because blocks start at multiples of 32
+    // (FP8: group s and half hf take chunk 4 (s / 2) + 2 hf + s % 2 instead of 2 s + hf,
+    // the same bijection of the step's 8 chunks for activations and weights)
     uint32_t frag_lo[kSub];
 #pragma unroll
-    for (int s = 0; s < kSub; ++s) frag_lo[s] = (uint32_t)(r32 * kRowBytes + (((2 * s + hf) ^ swz_key(r32)) << 4));
-    // FP8: the 8 codes of group s (bytes [16 s + 8 hf, +8) of the row's step) sit in
-    // piece s ^ f8_key(r32) of the row's line (blocks start at multiples of 32 rows)
-    uint32_t f8o[kSub];
+    for (int s = 0; s < kSub; ++s) {
+      const int c = FP8 ? 4 * (s >> 1) + 2 * hf + (s & 1) : 2 * s + hf;
+      frag_lo[s] = (uint32_t)(r32 * kRowBytes + ((c ^ swz_key(r32)) << 4));
+    }
+    // FP8: the codes of groups 2q, 2q + 1 (chunks 4q + 2hf, 4q + 2hf + 1: bytes
+    // [32 q + 16 hf, +16) of the row's step) are piece 2q + hf, stored at piece
+    // (2q + hf) ^ f8_key(r32) of the row's line (blocks start at multiples of 32 rows)
+    uint32_t f8o[kSub / 2];
 #pragma unroll
-    for (int s = 0; s < kSub; ++s) f8o[s] = (uint32_t)(r32 * kF8Pitch + 16 * (s ^ f8_key(r32)) + 8 * hf);
+    for (int q = 0; q < kSub / 2; ++q) f8o[q] = (uint32_t)(r32 * kF8Pitch + 16 * ((2 * q + hf) ^ f8_key(r32)));
     // items of one expert (its c M tiles x NT N tiles) are ordered in blocks of up to
     // 4 M tiles, N tile major within a block, so the workgroups running together on
     // an XCD share both the activation rows and the weight tiles through its L2
@@ -521,7 +530,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
     auto k_loop = [&](auto nact_tag) {
       constexpr int NACT = decltype(nact_tag)::value;
       uint4 fa[2][kWaveBlocks], fb[2][kNB];
-      uint2 fc[2][kNB];  // FP8: each group's raw codes, converted right before its MFMAs
+      uint4 fc[2][kNB];  // FP8: the raw codes of a pair of groups, converted right before each group's MFMAs
       // The previous group's reads are waited for (long done: a whole MFMA group ran
       // since) before this group's are issued, so at most 8 are in flight and the
       // MFMAs that follow need no wait.
@@ -532,9 +541,10 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
           fa[s & 1][j] = *reinterpret_cast<const uint4*>(La + fa_off + j * 2 * kBlk * kRowBytes + frag_lo[s]);
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb) {
-          if constexpr (FP8)
-            fc[s & 1][nb] = *reinterpret_cast<const uint2*>(Lb + (128 * wn + 32 * nb) * kF8Pitch + f8o[s]);
-          else
+          if constexpr (FP8) {
+            if ((s & 1) == 0)  // the pair's codes, read with its first group
+              fc[(s >> 1) & 1][nb] = *reinterpret_cast<const uint4*>(Lb + (128 * wn + 32 * nb) * kF8Pitch + f8o[s >> 1]);
+          } else
             fb[s & 1][nb] = *reinterpret_cast<const uint4*>(Lb + fb_off + nb * kBlk * kRowBytes + frag_lo[s]);
         }
       };
@@ -587,7 +597,10 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
       auto mfmas = [&](int s) {
         if constexpr (FP8) {
 #pragma unroll
-          for (int nb = 0; nb < kNB; ++nb) fb[s & 1][nb] = e4m3x8_bf16(fc[s & 1][nb].x, fc[s & 1][nb].y);
+          for (int nb = 0; nb < kNB; ++nb) {
+            const uint4 c = fc[(s >> 1) & 1][nb];
+            fb[s & 1][nb] = (s & 1) == 0 ? e4m3x8_bf16(c.x, c.y) : e4m3x8_bf16(c.z, c.w);
+          }
         }
         mfmas_rows(s, std::integral_constant<int, 0>{}, std::integral_constant<int, NACT>{});
       };
@@ -625,7 +638,8 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
           mfmas(S - 1);
           constexpr int NV = (TERN || FP8) ? ((S == 1 && PA) ? kDma / 2 : (S == 2 && PB) ? kBOps : 0)
                                            : ((S == 1 && PA) || (S >= 2 && PB)) ? kDma / 2 : 0;
-          interleave_group<NACT * kNB, NACT + (TERN ? 2 : 1) * kNB, NV>();
+          constexpr int NREAD = NACT + (TERN ? 2 * kNB : (FP8 && (S & 1)) ? 0 : kNB);
+          interleave_group<NACT * kNB, NREAD, NV>();
           __builtin_amdgcn_sched_barrier(0);
         });
         if constexpr (NEXT) {
