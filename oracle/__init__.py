@@ -38,6 +38,8 @@ def lib():
         L.hyo_fp8_decode.argtypes = [vp, vp, i64, i64, vp]
         L.hyo_ffn_w64.argtypes = [vp, i64, vp, vp, vp, i64, i64, vp, ci]
         L.hyo_forward_w64.argtypes = [vp] * 9 + [i64] * 5 + [vp] * 6 + [ci]
+        L.hyo_indexer_scores.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp]
+        L.hyo_topk_indices.argtypes = [vp, i64, i64, i64, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -191,3 +193,27 @@ def forward_w64(x, wr, bias, fg, fu, fd, sg, su, sd, k, sets_in=None, nthreads=N
                                  T, d, E, k, I, _p(sets_in), _p(out), _p(sets), _p(w), _p(margin), _p(lg),
                                  _threads(nthreads)), "hyo_forward_w64")
     return {"out": out, "sets": sets, "w": w, "margin": margin, "logits": lg}
+
+
+def indexer_scores(q, w, keys):
+    """Sparse-attention indexer scores: q bf16 [B][H][D], w fp32 [B][H], keys bf16
+    [B][S][D] -> fp64 [B][S], score = sum_h w[h] * max(0, q[h] . k)."""
+    q, w, keys = _c(q, np.uint16), _c(w, np.float32), _c(keys, np.uint16)
+    B, H, D = q.shape
+    S = keys.shape[1]
+    out = np.empty((B, S), np.float64)
+    _check(lib().hyo_indexer_scores(_p(q), _p(w), _p(keys), B, H, D, S, _p(out)), "hyo_indexer_scores")
+    return out
+
+
+def topk_indices(scores, K):
+    """Per row: the K highest scores (ties to the lower index) as ascending indices,
+    plus the K-th score and its margin over the (K+1)-th (+inf when S <= K)."""
+    scores = _c(np.atleast_2d(scores), np.float64)
+    B, S = scores.shape
+    n = min(K, S)
+    idx = np.empty((B, n), np.int32)
+    kth = np.empty(B, np.float64)
+    margin = np.empty(B, np.float64)
+    _check(lib().hyo_topk_indices(_p(scores), B, S, K, _p(idx), _p(kth), _p(margin)), "hyo_topk_indices")
+    return idx, kth, margin

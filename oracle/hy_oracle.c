@@ -48,6 +48,16 @@
  * subnormal m/8 * 2^-6; exponent 15 with mantissa 7 is NaN), each output row
  * carries one fp32 scale, weight = scale * value; activations stay bf16 and the
  * shared expert stays bf16.
+ *
+ * Sparse-attention indexer (Hy4 preview config summary, Tencent Hy4 preview model
+ * card: every layer is DeepSeek-style sparse attention with an indexer of 32 heads,
+ * head_dim 128 and top-k 2048, whose 128-dim key per token is shared by all heads;
+ * IndexCache: 21 "full" layers run the indexer, the other 57 reuse the top-k of the
+ * layer before them). The pages give no score function. Reading taken: score(t, s) =
+ * sum over heads h of w[t][h] * max(0, q[t][h] . k[s]) (per-head query and weight of
+ * the query token, shared key of token s); selection = the K highest scores among the
+ * visible keys, ties to the lower key index, reported in ascending key order (all
+ * visible keys when there are at most K).
  */
 #include <math.h>
 #include <pthread.h>
@@ -475,4 +485,66 @@ int hyo_forward_w64(const uint16_t* x, const uint16_t* wr, const float* bias, co
   if (!fg) return HYO_ERR_ARG;
   return forward_impl(x, wr, bias, NULL, NULL, NULL, fg, fu, fd, sg, su, sd, T, d, E, k, I, sets_in, out,
                       sets_out, w_out, margin_out, logits_out, nthreads);
+}
+
+/* ------------------------------------------------------- indexer --------- */
+
+/* Scores of B queries, each against its own S keys:
+ * q bf16 [B][H][D], w fp32 [B][H], keys bf16 [B][S][D] -> scores fp64 [B][S]. */
+int hyo_indexer_scores(const uint16_t* q, const float* w, const uint16_t* keys, int64_t B, int64_t H, int64_t D,
+                       int64_t S, double* scores) {
+  if (B < 0 || H <= 0 || D <= 0 || S < 0 || (B > 0 && S > 0 && (!q || !w || !keys || !scores))) return HYO_ERR_ARG;
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t s = 0; s < S; ++s) {
+      const uint16_t* kv = keys + (b * S + s) * D;
+      double acc = 0.0;
+      for (int64_t h = 0; h < H; ++h) {
+        const uint16_t* qv = q + (b * H + h) * D;
+        double dot = 0.0;
+        for (int64_t i = 0; i < D; ++i) dot += bf16_value(qv[i]) * bf16_value(kv[i]);
+        acc += (double)w[b * H + h] * (dot > 0.0 ? dot : 0.0);
+      }
+      scores[b * S + s] = acc;
+    }
+  return HYO_OK;
+}
+
+typedef struct {
+  double v;
+  int64_t i;
+} scored;
+
+/* by score descending, then key index ascending */
+static int by_score_desc_then_index(const void* a, const void* b) {
+  const scored* x = (const scored*)a;
+  const scored* y = (const scored*)b;
+  if (x->v != y->v) return x->v > y->v ? -1 : 1;
+  return x->i < y->i ? -1 : (x->i > y->i);
+}
+
+static int by_key_index(const void* a, const void* b) {
+  const int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+  return (x > y) - (x < y);
+}
+
+/* Top-K selection per row: scores fp64 [B][S] -> idx int32 [B][min(K, S)], the K
+ * highest scores (ties to the lower index), in ascending index order; kth fp64 [B]
+ * (optional) gets the K-th highest score and margin fp64 [B] (optional) its lead over
+ * the (K+1)-th (+inf when S <= K). */
+int hyo_topk_indices(const double* scores, int64_t B, int64_t S, int64_t K, int32_t* idx, double* kth,
+                     double* margin) {
+  if (B < 0 || S < 0 || K < 1 || (B > 0 && S > 0 && (!scores || !idx))) return HYO_ERR_ARG;
+  const int64_t n = S < K ? S : K;
+  scored* tmp = (scored*)malloc(sizeof(scored) * (size_t)(S > 0 ? S : 1));
+  if (!tmp) return HYO_ERR_ARG;
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t s = 0; s < S; ++s) tmp[s] = (scored){scores[b * S + s], s};
+    qsort(tmp, (size_t)S, sizeof(scored), by_score_desc_then_index);
+    for (int64_t j = 0; j < n; ++j) idx[b * n + j] = (int32_t)tmp[j].i;
+    qsort(idx + b * n, (size_t)n, sizeof(int32_t), by_key_index);
+    if (kth) kth[b] = n > 0 ? tmp[n - 1].v : NAN;
+    if (margin) margin[b] = S > K ? tmp[K - 1].v - tmp[K].v : INFINITY;
+  }
+  free(tmp);
+  return HYO_OK;
 }

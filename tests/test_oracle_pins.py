@@ -476,3 +476,59 @@ def test_fp8_layer_matches_dense_masked_numpy():
         for pe, e in zip(p, order):
             out[t] += pe * np_swiglu(x[t:t + 1], fw["gate"][e], fw["up"][e], fw["down"][e])[0]
     assert np.allclose(ref["out"], out, rtol=1e-11, atol=1e-11)
+
+
+# ------------------------------------------------------- sparse-attention indexer
+def test_indexer_hand_worked():
+    # H=2, D=2: q0=(1,2), q1=(-1,1), w=(0.5,2); key (3,-1): dots 1, -4 -> 0.5*1 + 2*0 = 0.5;
+    # key (0,1): dots 2, 1 -> 0.5*2 + 2*1 = 3
+    q = f32_to_bf16_bits(np.array([[[1.0, 2.0], [-1.0, 1.0]]]))
+    w = np.array([[0.5, 2.0]], np.float32)
+    keys = f32_to_bf16_bits(np.array([[[3.0, -1.0], [0.0, 1.0]]]))
+    assert oracle.indexer_scores(q, w, keys).tolist() == [[0.5, 3.0]]
+
+
+def test_indexer_unit_keys_read_the_query_through_relu():
+    rng = np.random.default_rng(21)
+    D = 16
+    qv = rng.standard_normal(D)
+    q = f32_to_bf16_bits(qv[None, None, :])
+    keys = f32_to_bf16_bits(np.eye(D)[None])          # key s = e_s
+    got = oracle.indexer_scores(q, np.ones((1, 1), np.float32), keys)[0]
+    assert np.array_equal(got, np.maximum(bf(q)[0, 0], 0.0))
+    assert (got[bf(q)[0, 0] < 0] == 0).all() and (got > 0).sum() == (bf(q)[0, 0] > 0).sum()
+
+
+def test_indexer_heads_weights_and_batches():
+    rng = np.random.default_rng(22)
+    B, H, D, S = 3, 4, 32, 40
+    q = f32_to_bf16_bits(rng.standard_normal((B, H, D)))
+    keys = f32_to_bf16_bits(rng.standard_normal((B, S, D)))
+    w = rng.random((B, H)).astype(np.float32)
+    base = oracle.indexer_scores(q, w, keys)
+    perm = np.array([2, 0, 3, 1])                       # heads are a sum: any order
+    assert np.allclose(oracle.indexer_scores(q[:, perm], w[:, perm], keys), base, rtol=1e-14, atol=1e-14)
+    per_head = [oracle.indexer_scores(q[:, h:h + 1], np.ones((B, 1), np.float32), keys) for h in range(H)]
+    assert np.allclose(sum(w[:, h:h + 1].astype(np.float64) * per_head[h] for h in range(H)), base, rtol=1e-13)
+    # each batch row scores only its own keys
+    one = oracle.indexer_scores(q[1:2], w[1:2], keys[1:2])
+    assert np.array_equal(one[0], base[1])
+    assert not np.allclose(oracle.indexer_scores(q[1:2], w[1:2], keys[0:1])[0], base[1])
+
+
+@pytest.mark.parametrize("S,K", [(50, 8), (300, 64), (20, 32), (64, 64)])
+def test_topk_indices_brute_force(S, K):
+    rng = np.random.default_rng(S + K)
+    sc = np.round(rng.standard_normal((4, S)) * 4) / 4  # many ties
+    idx, kth, margin = oracle.topk_indices(sc, K)
+    for b in range(4):
+        order = np.lexsort((np.arange(S), -sc[b]))      # score descending, index ascending
+        want = np.sort(order[:min(K, S)])
+        assert np.array_equal(idx[b], want)
+        assert kth[b] == sc[b, order[min(K, S) - 1]]
+        assert (margin[b] == np.inf) if S <= K else (margin[b] == sc[b, order[K - 1]] - sc[b, order[K]])
+
+
+def test_topk_indices_all_equal_take_lowest():
+    idx, _, margin = oracle.topk_indices(np.zeros((2, 100)), 10)
+    assert (idx == np.arange(10)).all() and (margin == 0).all()
