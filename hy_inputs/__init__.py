@@ -33,6 +33,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 S_X, S_WR, S_WG, S_WU, S_WD, S_WSG, S_WSU, S_WSD, S_BIAS = 1, 2, 3, 4, 5, 6, 7, 8, 9
 S_QG, S_QU, S_QD, S_SG, S_SU, S_SD = 10, 11, 12, 13, 14, 15
 S_FG, S_FU, S_FD, S_FSG, S_FSU, S_FSD = 16, 17, 18, 19, 20, 21
+S_IQ, S_IK, S_IW = 22, 23, 24  # sparse-attention indexer: queries, keys, head weights
 
 QBLOCK_WEIGHTS = 128  # weights per packed ternary block
 QBLOCK_WORDS = 5      # uint32 words per packed ternary block (1.25 bits/weight)
@@ -341,3 +342,49 @@ def dev_layer(cfg: LayerConfig, device="cuda") -> dict:
         out["up"] = dev_gauss_(torch.empty(E, I, d, dtype=bf, device=device), cfg.seed, S_WU, sd)
         out["down"] = dev_gauss_(torch.empty(E, d, I, dtype=bf, device=device), cfg.seed, S_WD, si)
     return out
+
+
+# ------------------------------------------------------ sparse-attention indexer
+@dataclass(frozen=True)
+class IndexerConfig:
+    """B queries (one per sequence), each scored against its own S keys by an H-head
+    indexer of key dimension D; the K best keys are selected."""
+    name: str
+    B: int
+    S: int
+    H: int = 32
+    D: int = 128
+    K: int = 2048
+    seed: int = 0
+
+
+INDEXER_CONFIGS = {
+    "indexer_tiny": IndexerConfig("indexer_tiny", B=4, S=3000, K=256),
+    # 32 decoding sequences with 64K-token contexts (indexer of the Hy4 preview config:
+    # 32 heads, head_dim 128, top-2048)
+    "indexer_decode": IndexerConfig("indexer_decode", B=32, S=65536),
+}
+
+
+def host_indexer_queries(cfg: IndexerConfig):
+    """(q bf16 bits [B][H][D], w fp32 [B][H]): q ~ N(0, 1/sqrt(D)), w ~ U(0.5, 1.5) / H."""
+    q = gauss_bf16(cfg.seed, S_IQ, cfg.B * cfg.H * cfg.D, 1.0 / math.sqrt(cfg.D)).reshape(cfg.B, cfg.H, cfg.D)
+    w = bf16_to_f32(uniform_bf16(cfg.seed, S_IW, cfg.B * cfg.H, 0.5 / cfg.H, 1.0 / cfg.H)).reshape(cfg.B, cfg.H)
+    return q, w.astype(np.float32)
+
+
+def host_indexer_keys(cfg: IndexerConfig, b: int) -> np.ndarray:
+    """Keys of sequence b: bf16 bits [S][D], ~ N(0, 1)."""
+    n = cfg.S * cfg.D
+    return gauss_bf16(cfg.seed, S_IK, n, 1.0, start=b * n).reshape(cfg.S, cfg.D)
+
+
+def dev_indexer(cfg: IndexerConfig, device="cuda") -> dict:
+    """q bf16 [B][H][D], w fp32 [B][H], keys bf16 [B][S][D] in device memory (values
+    equal the host generators')."""
+    import torch
+    bf = torch.bfloat16
+    q = dev_gauss_(torch.empty(cfg.B, cfg.H, cfg.D, dtype=bf, device=device), cfg.seed, S_IQ, 1.0 / math.sqrt(cfg.D))
+    w = dev_uniform_(torch.empty(cfg.B, cfg.H, dtype=bf, device=device), cfg.seed, S_IW, 0.5 / cfg.H, 1.0 / cfg.H)
+    keys = dev_gauss_(torch.empty(cfg.B, cfg.S, cfg.D, dtype=bf, device=device), cfg.seed, S_IK, 1.0)
+    return {"q": q, "w": w.float(), "keys": keys}

@@ -211,6 +211,29 @@ int hy_moe_sherry_pack_host(const int8_t* tern, int64_t rows, int64_t cols, uint
 int hy_moe_probe_mfma_bf16(const void* operands, size_t operand_bytes, float* tflops, void* stream);
 int hy_moe_probe_hbm_read(const void* buf, size_t bytes, float* gbps, void* stream);
 
+/*
+ * hy_indexer_topk — sparse-attention indexer of the Hy4 preview configuration (Tencent
+ * Hy4 preview model card, configuration summary: every layer uses DeepSeek-style sparse
+ * attention with an indexer of 32 heads, head_dim 128 and top-k 2048, whose key per
+ * token is shared by all heads; with IndexCache 57 of the 78 layers reuse the selection
+ * of the layer before them, so only 21 layers run it). The pages give no score formula;
+ * read here as score(s) = sum over heads h of w[h] * max(0, q[h] . k[s]).
+ *   q       DEVICE bf16 [B][H][D]  one query per sequence (16-byte aligned)
+ *   w       DEVICE fp32 [B][H]     per-head weights of each query
+ *   keys    DEVICE bf16 [B][S][D]  each sequence's keys (16-byte aligned)
+ *   idx     DEVICE int32 [B][min(K, S)]  out: the K highest-scoring keys of each
+ *           query, ties to the lower key index, in ascending key order
+ *   scores  DEVICE fp32 [B][S] or NULL: out, the scores (fp32 accumulation); when NULL
+ *           they go to `workspace` (256-byte aligned, hy_indexer_workspace_size bytes)
+ *   stream  hipStream_t; enqueued without blocking.
+ * Supported: H == 32, D == 128, B <= 65535, B * S < 2^31. Returns HY_MOE_OK, INVALID_ARG
+ * (null or misaligned pointers, negative sizes, K < 1), UNSUPPORTED, WORKSPACE or HIP;
+ * B == 0 or S == 0 is a no-op. Checks run before anything is enqueued.
+ */
+size_t hy_indexer_workspace_size(int64_t B, int64_t S);
+int hy_indexer_topk(const void* q, const float* w, const void* keys, int64_t B, int64_t H, int64_t D, int64_t S,
+                    int64_t K, int32_t* idx, float* scores, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,8 @@ KERNELS = ["route_logits", "route_topk", "permute_scan", "permute_scatter", "exp
 NUM_STAGE_EVENTS = len(KERNELS) + 1
 
 EXPORTED = ["hy_moe_forward", "hy_moe_forward_ex", "hy_moe_workspace_size", "hy_moe_status_string",
-            "hy_moe_sherry_pack_host", "hy_moe_probe_mfma_bf16", "hy_moe_probe_hbm_read"]
+            "hy_moe_sherry_pack_host", "hy_moe_probe_mfma_bf16", "hy_moe_probe_hbm_read",
+            "hy_indexer_workspace_size", "hy_indexer_topk"]
 PROBE_OPERAND_BYTES = 65536
 
 
@@ -80,6 +81,10 @@ def _load():
     L.hy_moe_probe_mfma_bf16.restype = ctypes.c_int
     L.hy_moe_probe_hbm_read.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_float), vp]
     L.hy_moe_probe_hbm_read.restype = ctypes.c_int
+    L.hy_indexer_workspace_size.argtypes = [i64, i64]
+    L.hy_indexer_workspace_size.restype = ctypes.c_size_t
+    L.hy_indexer_topk.argtypes = [vp, vp, vp] + [i64] * 5 + [vp, vp, vp, ctypes.c_size_t, vp]
+    L.hy_indexer_topk.restype = ctypes.c_int
     return L
 
 
@@ -228,3 +233,23 @@ def probe_hbm_read(buf, stream=None) -> float:
     if rc != OK:
         raise HyMoeError(rc, "hy_moe_probe_hbm_read")
     return gb.value
+
+
+def indexer_topk(q, w, keys, K, *, scores=None, workspace=None, stream=None):
+    """hy_indexer_topk on device tensors q bf16 [B][H][D], w fp32 [B][H], keys bf16
+    [B][S][D]. Returns (idx int32 [B][min(K, S)] ascending, scores fp32 [B][S] or None)."""
+    import torch
+    for name, t, dt in (("q", q, torch.bfloat16), ("w", w, torch.float32), ("keys", keys, torch.bfloat16)):
+        if t.dtype != dt or not t.is_contiguous():
+            raise TypeError(f"indexer_topk: {name} must be a contiguous {dt} tensor, got {t.dtype}")
+    B, H, D = q.shape
+    S = keys.shape[1]
+    idx = torch.empty(B, min(K, S), dtype=torch.int32, device=q.device)
+    if scores is None and workspace is None:
+        workspace = torch.empty(int(_lib.hy_indexer_workspace_size(B, S)), dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = _lib.hy_indexer_topk(q.data_ptr(), w.data_ptr(), keys.data_ptr(), B, H, D, S, K, idx.data_ptr(),
+                              _ptr(scores), _ptr(workspace), ws_bytes, _stream(stream))
+    if rc != OK:
+        raise HyMoeError(rc, "hy_indexer_topk")
+    return idx, scores

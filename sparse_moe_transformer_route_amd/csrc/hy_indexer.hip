@@ -1,0 +1,228 @@
+// Sparse-attention indexer: for each query, a score for every key of its sequence and
+// the K best keys (Tencent Hy4 preview model card, configuration summary: every layer
+// uses DeepSeek-style sparse attention whose indexer has 32 heads, head_dim 128 and
+// top-k 2048, one 128-dim key per token shared by all heads; IndexCache lets 57 of the
+// 78 layers reuse the selection of the layer before them, so only 21 layers run this).
+// The score is read as sum over heads h of w[h] * max(0, q[h] . k): the pages give the
+// indexer's shape, not its formula.
+//
+// indexer_scores_kernel: a workgroup takes 128 keys of one sequence. Their rows (256 B
+// each) arrive in LDS by direct global->LDS loads, 16 lanes per row, 16-byte chunk c of
+// key r stored at c ^ (r mod 16) so that the fragment reads (16 lanes = 16 keys, one
+// chunk) hit 16 distinct bank groups. Each wave runs 32x32x16 bf16 MFMAs with the
+// query's 32 heads as rows and 32 keys as columns: lane (key, half) then holds 16 heads
+// of one key, weights and clips them in registers, and one shuffle adds the two halves.
+// The kernel streams the keys once: HBM-bound.
+//
+// indexer_topk_kernel: one 1024-thread workgroup per query. An MSB-first radix select
+// over 8-bit digits of an order-preserving key of the fp32 scores finds the K-th
+// score; the first digit (sign and exponent) takes few values, so its histogram counts
+// are combined per wave (one LDS atomic per distinct digit), later digits are spread
+// and go straight to per-wave histograms. Keys above the K-th, then the lowest-index
+// keys equal to it, are written in ascending key order through block prefix sums.
+#include <stdint.h>
+#include <string.h>
+
+#include "hy_moe.h"
+#include "common.h"
+#include "dispatch.h"
+
+namespace hymoe {
+namespace {
+
+constexpr int kIxKeys = 128;      // keys per scoring workgroup (4 waves x 32)
+constexpr int kIxHeads = 32;      // MFMA rows
+constexpr int kIxSelThreads = 1024;
+
+#define IX_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+template <int D>
+__global__ void __launch_bounds__(256) indexer_scores_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
+                                                             const uint16_t* __restrict__ keys, int S,
+                                                             float* __restrict__ scores) {
+  constexpr int CH = D / 8;                   // 16-byte chunks per key row
+  constexpr int OPS = kIxKeys * CH / 256;     // direct-to-LDS ops per thread
+  constexpr int NS = D / 16;                  // MFMA k steps
+  static_assert(CH >= 16 && (CH & (CH - 1)) == 0, "D must be a power of two >= 128");
+  __shared__ __attribute__((aligned(16))) uint8_t lk[kIxKeys * D * 2];
+  const int b = blockIdx.y;
+  const int s0 = blockIdx.x * kIxKeys;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int col = lane & 31, hf = lane >> 5;
+  const uint16_t* kb = keys + (size_t)b * S * D;
+  // keys past S reload the last key (scores not stored)
+#pragma unroll
+  for (int i = 0; i < OPS; ++i) {
+    const int pq = 256 * i + tid;
+    const int row = pq / CH, lc = (pq % CH) ^ (row % 16);
+    const int key = min(s0 + row, S - 1);
+    __builtin_amdgcn_global_load_lds((const void*)(kb + (size_t)key * D + 8 * lc), IX_LDS(lk + 16 * (256 * i + 64 * wv)),
+                                     16, 0, 0);
+  }
+  // the query's fragments (row = head) and the lane's 16 head weights, while the keys land
+  uint4 fa[NS];
+  const uint16_t* qb = q + ((size_t)b * kIxHeads + col) * D + 8 * hf;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) fa[s] = *reinterpret_cast<const uint4*>(qb + 16 * s);
+  float wl[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) wl[i] = w[(size_t)b * kIxHeads + 8 * (i / 4) + 4 * hf + (i % 4)];
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int kr = 32 * wv + col;  // this lane's key row in the tile
+  f32x16 acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const uint4 fb = *reinterpret_cast<const uint4*>(lk + kr * D * 2 + 16 * ((2 * s + hf) ^ (kr % 16)));
+    acc = mfma32x32x16(fa[s], fb, acc);
+  }
+  // accumulator i: head 8 (i / 4) + 4 hf + i % 4 of key kr
+  float v = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v += wl[i] * fmaxf(acc[i], 0.f);
+  v += __shfl_xor(v, 32, 64);
+  if (hf == 0 && s0 + kr < S) scores[(size_t)b * S + s0 + kr] = v;
+}
+
+// order-preserving unsigned key of an fp32 value (larger value -> larger key)
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__global__ void __launch_bounds__(kIxSelThreads) indexer_topk_kernel(const float* __restrict__ scores, int S, int K,
+                                                                     int32_t* __restrict__ idx) {
+  constexpr int NW = kIxSelThreads / 64;
+  __shared__ uint32_t hist[NW][256];
+  __shared__ uint32_t total[256];
+  __shared__ uint32_t sh_prefix, sh_need;
+  __shared__ int wsum[17];
+  const int b = blockIdx.x;
+  const float* sc = scores + (size_t)b * S;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n = min(K, S);
+  uint32_t prefix = 0, mask = 0, need = (uint32_t)n;  // need: keys still to take at or below the prefix
+#pragma unroll 1
+  for (int d = 3; d >= 0; --d) {
+    for (int i = tid; i < NW * 256; i += kIxSelThreads) (&hist[0][0])[i] = 0u;
+    __syncthreads();
+    const int sh = 8 * d;
+    for (int i0 = 0; i0 < S; i0 += kIxSelThreads) {
+      const int i = i0 + tid;
+      const uint32_t key = i < S ? order_key(sc[i]) : 0u;
+      const bool act = i < S && (key & mask) == prefix;
+      const uint32_t dig = (key >> sh) & 255u;
+      if (d == 3) {
+        // few distinct leading digits: one atomic per distinct digit of the wave
+        unsigned long long pend = __ballot(act);
+        while (pend) {
+          const int leader = __builtin_ctzll(pend);
+          const uint32_t v = __shfl(dig, leader, 64);
+          const unsigned long long same = __ballot(act && dig == v) & pend;
+          if (lane == leader) atomicAdd(&hist[wv][v], (uint32_t)__popcll(same));
+          pend &= ~same;
+        }
+      } else if (act) {
+        atomicAdd(&hist[wv][dig], 1u);
+      }
+    }
+    __syncthreads();
+    if (tid < 256) {
+      uint32_t c = 0;
+#pragma unroll
+      for (int k = 0; k < NW; ++k) c += hist[k][tid];
+      total[tid] = c;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      // the digit holding the need-th largest remaining key, counting from 255 down
+      uint32_t rem = need;
+      int v = 255;
+      for (; v > 0; --v) {
+        if (rem <= total[v]) break;
+        rem -= total[v];
+      }
+      sh_prefix = prefix | ((uint32_t)v << sh);
+      sh_need = rem;
+    }
+    __syncthreads();
+    prefix = sh_prefix;
+    need = sh_need;
+    mask |= 255u << sh;
+  }
+  // prefix = the K-th largest key; take every key above it and the `need` lowest-index
+  // keys equal to it. Thread t owns indices [t c, t c + c).
+  const int c = (S + kIxSelThreads - 1) / kIxSelThreads;
+  const int lo = min(S, tid * c), hi = min(S, lo + c);
+  int n_gt = 0, n_eq = 0;
+  for (int i = lo; i < hi; ++i) {
+    const uint32_t key = order_key(sc[i]);
+    n_gt += key > prefix;
+    n_eq += key == prefix;
+  }
+  int tot = 0;
+  const int eq_before = block_exclusive_scan(n_eq, wsum, &tot);
+  const int take_eq = max(0, min(n_eq, (int)need - eq_before));
+  const int pos0 = block_exclusive_scan(n_gt + take_eq, wsum, &tot);
+  int pos = pos0, eq_seen = 0;
+  int32_t* out = idx + (size_t)b * n;
+  for (int i = lo; i < hi; ++i) {
+    const uint32_t key = order_key(sc[i]);
+    bool take = key > prefix;
+    if (key == prefix) {
+      take = eq_seen < take_eq;
+      ++eq_seen;
+    }
+    if (take && pos < n) out[pos++] = i;  // the bound only guards the buffer
+  }
+}
+
+}  // namespace
+}  // namespace hymoe
+
+namespace {
+
+size_t ix_align(size_t v) { return (v + 255) & ~(size_t)255; }
+
+int ix_check(int64_t B, int64_t H, int64_t D, int64_t S, int64_t K) {
+  if (B < 0 || H <= 0 || D <= 0 || S < 0 || K < 1) return HY_MOE_ERR_INVALID_ARG;
+  if (H != 32 || D != 128 || B > 65535 || S >= ((int64_t)1 << 31) / 128 || B * S >= ((int64_t)1 << 31))
+    return HY_MOE_ERR_UNSUPPORTED;
+  return HY_MOE_OK;
+}
+
+}  // namespace
+
+extern "C" size_t hy_indexer_workspace_size(int64_t B, int64_t S) {
+  if (B < 0 || S < 0) return 0;
+  return ix_align(sizeof(float) * (size_t)(B * S > 0 ? B * S : 1));
+}
+
+extern "C" int hy_indexer_topk(const void* q, const float* w, const void* keys, int64_t B, int64_t H, int64_t D,
+                               int64_t S, int64_t K, int32_t* idx, float* scores, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  using namespace hymoe;
+  const int rc = ix_check(B, H, D, S, K);
+  if (rc != HY_MOE_OK) return rc;
+  if (B == 0 || S == 0) return HY_MOE_OK;
+  if (!q || !w || !keys || !idx) return HY_MOE_ERR_INVALID_ARG;
+  if (((uintptr_t)q & 15) || ((uintptr_t)keys & 15) || ((uintptr_t)w & 3) || ((uintptr_t)idx & 3) ||
+      ((uintptr_t)scores & 3) || ((uintptr_t)workspace & 255))
+    return HY_MOE_ERR_INVALID_ARG;
+  float* sc = scores;
+  if (!sc) {
+    if (!workspace) return HY_MOE_ERR_INVALID_ARG;
+    if (workspace_bytes < hy_indexer_workspace_size(B, S)) return HY_MOE_ERR_WORKSPACE;
+    sc = (float*)workspace;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  hipLaunchKernelGGL(indexer_scores_kernel<128>, dim3((unsigned)((S + kIxKeys - 1) / kIxKeys), (unsigned)B), dim3(256),
+                     0, s, (const uint16_t*)q, w, (const uint16_t*)keys, (int)S, sc);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return HY_MOE_ERR_HIP;
+  hipLaunchKernelGGL(indexer_topk_kernel, dim3((unsigned)B), dim3(kIxSelThreads), 0, s, (const float*)sc, (int)S,
+                     (int)(K < S ? K : S), idx);
+  return hipGetLastError() == hipSuccess ? HY_MOE_OK : HY_MOE_ERR_HIP;
+}

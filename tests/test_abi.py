@@ -19,7 +19,7 @@ HEADER = os.path.join(ROOT, "include", "hy_moe.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(hy_moe_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(hy_(?:moe|indexer)_\w+)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported():
@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
     for n in names:
         assert hasattr(L, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", hm.LIB_PATH], capture_output=True, text=True).stdout
-    exported = set(re.findall(r"\bT (hy_moe_\w+)", out))
+    exported = set(re.findall(r"\bT (hy_(?:moe|indexer)_\w+)", out))
     assert set(names) <= exported
 
 
@@ -193,3 +193,23 @@ def test_one_hip_runtime_in_process():
     maps = open("/proc/self/maps").read().splitlines()
     runtimes = {line.split()[-1] for line in maps if "libamdhip64" in line}
     assert len(runtimes) == 1, runtimes
+
+
+def test_indexer_argument_checks():
+    L = hm.lib()
+    out = FAKE
+
+    def ix(q=FAKE, w=FAKE, keys=FAKE, B=2, H=32, D=128, S=1000, K=64, idx=out, scores=FAKE, ws=None, wsb=0):
+        return L.hy_indexer_topk(q, w, keys, B, H, D, S, K, idx, scores, ws, wsb, None)
+    assert ix(H=16) == hm.ERR_UNSUPPORTED
+    assert ix(D=64) == hm.ERR_UNSUPPORTED
+    assert ix(B=70000) == hm.ERR_UNSUPPORTED
+    assert ix(K=0) == hm.ERR_INVALID_ARG
+    assert ix(S=-1) == hm.ERR_INVALID_ARG
+    assert ix(q=None) == hm.ERR_INVALID_ARG
+    assert ix(keys=FAKE + 8) == hm.ERR_INVALID_ARG          # keys must be 16-byte aligned
+    assert ix(scores=None) == hm.ERR_INVALID_ARG            # neither scores nor workspace
+    assert ix(scores=None, ws=FAKE, wsb=16) == hm.ERR_WORKSPACE
+    assert ix(B=0, q=None, keys=None) == hm.OK              # empty: no pointer is touched
+    assert ix(S=0, q=None, keys=None) == hm.OK
+    assert L.hy_indexer_workspace_size(4, 1000) >= 4 * 1000 * 4
