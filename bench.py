@@ -292,6 +292,79 @@ def cpu_baseline(cfg, hi, torch, inp, routing, budget_s):
                       f"{cfg.k} routed + 1 shared SwiGLU experts, combine); {el:.1f} s on {nthreads} threads"}
 
 
+def run_indexer(args, hi, hm, torch):
+    """The sparse-attention indexer of one full layer over B decoding sequences: every
+    query scores its sequence's S keys and keeps the top K (hy_indexer_topk)."""
+    import numpy as np
+    cfg = hi.INDEXER_CONFIGS[args.config]
+    log(f"[bench] generating the indexer inputs (B={cfg.B}, S={cfg.S}) on the GPU")
+    inp = hi.dev_indexer(cfg, device="cuda:0")
+    ws = torch.empty(hm.lib().hy_indexer_workspace_size(cfg.B, cfg.S), dtype=torch.uint8, device="cuda:0")
+    torch.cuda.synchronize()
+
+    def call(ev=None):
+        return hm.indexer_topk(inp["q"], inp["w"], inp["keys"], cfg.K, workspace=ws, stage_events=ev)
+
+    done, t_w = 0, time.perf_counter()
+    while (args.warmup is None and (done < 5 or time.perf_counter() - t_w < WARMUP_MIN_S)) or \
+            (args.warmup is not None and done < args.warmup):
+        call()
+        done += 1
+        if done % 5 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    steps = args.steps
+    ev = Events(3 * steps)
+    arrays = [ev.array(i, 3) for i in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        idx, _ = call(arrays[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    score_ms = sum(ev.ms(3 * i, 3 * i + 1) for i in range(steps)) / steps
+    select_ms = sum(ev.ms(3 * i + 1, 3 * i + 2) for i in range(steps)) / steps
+    ev.close()
+    B, S, H, D = cfg.B, cfg.S, cfg.H, cfg.D
+    unit = S * D * 2 + S * 4            # keys read + scores written per query
+    alg = B * unit + B * H * D * 2 + B * H * 4
+    roof = {"bound": "hbm", "achieved": alg / (score_ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+            "frac": alg / (score_ms * 1e-3) / PEAK_HBM, "traffic": traffic_for(f"indexer_scores/{cfg.name}", B),
+            "kernel": "indexer_scores_kernel<128>", "per_unit": f"{unit} B per query (its {S} keys of {D} bf16, its "
+            f"{S} fp32 scores), plus the queries and head weights", "units_per_launch": B, "kernel_ms": score_ms,
+            "kernel_source_sha256_16": source_digest(os.path.join(ROOT, "sparse_moe_transformer_route_amd/csrc/"
+                                                                  "hy_indexer.hip"))}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        log("[bench] timing the oracle on the host")
+        q, w = hi.host_indexer_queries(cfg)
+        el, nq = 0.0, 0
+        while nq == 0 or (el < args.cpu_seconds and nq < B):
+            keys = hi.host_indexer_keys(cfg, nq)   # generation is not timed
+            t1 = time.perf_counter()
+            sc = oracle.indexer_scores(q[nq:nq + 1], w[nq:nq + 1], keys[None])
+            oracle.topk_indices(sc, cfg.K)
+            el += time.perf_counter() - t1
+            nq += 1
+        cpu = {"value": nq / el, "unit": "queries/s", "cores": 1, "kind": "oracle",
+               "sample": f"{nq} of the {B} queries (fp64 scores of all {S} keys and the top-{cfg.K} sort each); "
+                         f"{el:.1f} s on 1 thread"}
+    log(f"[bench] {cfg.name}: {ms:.3f} ms/step, {B / (ms * 1e-3):.0f} queries/s, scoring {score_ms:.4f} ms, "
+        f"selection {select_ms:.4f} ms")
+    line = {
+        "metric": "sparse-attention indexer throughput (one full indexer layer)", "value": B / (ms * 1e-3),
+        "unit": "queries/s", "n_gpus": 1, "steps": steps, "warmup": done, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: B={B} sequences x S={S} keys, H={H} heads, D={D}, top-{cfg.K}",
+                   "B": B, "S": S, "H": H, "D": D, "K": cfg.K, "seed": cfg.seed},
+        "roofline": roof, "kernels_ms": {"indexer_scores": score_ms, "indexer_topk": select_ms},
+        "indexcache": {"layers": 78, "full_layers": 21, "ms_per_step_all_layers": 21 * ms,
+                       "note": "57 of 78 layers reuse the previous layer's selection and run no indexer kernel"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -299,7 +372,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed steps before the timed ones (default: at least 5 and %.1f s of them)" % WARMUP_MIN_S)
     ap.add_argument("--config", default="decode", choices=["tiny", "decode", "prefill", "skewed", "ternary",
-                                                                 "ternary_prefill", "fp8", "fp8_prefill"])
+                                                                 "ternary_prefill", "fp8", "fp8_prefill",
+                                                                 "indexer_tiny", "indexer_decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the T=8192 measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -326,6 +400,9 @@ def main():
         print(json.dumps({"calibration": "copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n}))
         return
 
+    if args.config.startswith("indexer"):
+        run_indexer(args, hi, hm, torch)
+        return
     cfg = hi.CONFIGS[args.config]
     shared_weights = None
     if not cfg.ternary and not cfg.fp8 and cfg.d == 6144:

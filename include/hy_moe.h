@@ -225,6 +225,8 @@ int hy_moe_probe_hbm_read(const void* buf, size_t bytes, float* gbps, void* stre
  *           query, ties to the lower key index, in ascending key order
  *   scores  DEVICE fp32 [B][S] or NULL: out, the scores (fp32 accumulation); when NULL
  *           they go to `workspace` (256-byte aligned, hy_indexer_workspace_size bytes)
+ *   stage_events  NULL or 3 hipEvent_t (caller-created; NULL entries skipped) recorded
+ *           before the scoring kernel, after it and after the selection kernel
  *   stream  hipStream_t; enqueued without blocking.
  * Supported: H == 32, D == 128, B <= 65535, B * S < 2^31. Returns HY_MOE_OK, INVALID_ARG
  * (null or misaligned pointers, negative sizes, K < 1), UNSUPPORTED, WORKSPACE or HIP;
@@ -232,7 +234,8 @@ int hy_moe_probe_hbm_read(const void* buf, size_t bytes, float* gbps, void* stre
  */
 size_t hy_indexer_workspace_size(int64_t B, int64_t S);
 int hy_indexer_topk(const void* q, const float* w, const void* keys, int64_t B, int64_t H, int64_t D, int64_t S,
-                    int64_t K, int32_t* idx, float* scores, void* workspace, size_t workspace_bytes, void* stream);
+                    int64_t K, int32_t* idx, float* scores, void* workspace, size_t workspace_bytes,
+                    void* const* stage_events, void* stream);
 
 #ifdef __cplusplus
 }

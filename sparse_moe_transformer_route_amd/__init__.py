@@ -83,7 +83,7 @@ def _load():
     L.hy_moe_probe_hbm_read.restype = ctypes.c_int
     L.hy_indexer_workspace_size.argtypes = [i64, i64]
     L.hy_indexer_workspace_size.restype = ctypes.c_size_t
-    L.hy_indexer_topk.argtypes = [vp, vp, vp] + [i64] * 5 + [vp, vp, vp, ctypes.c_size_t, vp]
+    L.hy_indexer_topk.argtypes = [vp, vp, vp] + [i64] * 5 + [vp, vp, vp, ctypes.c_size_t, vp, vp]
     L.hy_indexer_topk.restype = ctypes.c_int
     return L
 
@@ -235,7 +235,7 @@ def probe_hbm_read(buf, stream=None) -> float:
     return gb.value
 
 
-def indexer_topk(q, w, keys, K, *, scores=None, workspace=None, stream=None):
+def indexer_topk(q, w, keys, K, *, scores=None, workspace=None, stream=None, stage_events=None):
     """hy_indexer_topk on device tensors q bf16 [B][H][D], w fp32 [B][H], keys bf16
     [B][S][D]. Returns (idx int32 [B][min(K, S)] ascending, scores fp32 [B][S] or None)."""
     import torch
@@ -249,7 +249,9 @@ def indexer_topk(q, w, keys, K, *, scores=None, workspace=None, stream=None):
         workspace = torch.empty(int(_lib.hy_indexer_workspace_size(B, S)), dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = _lib.hy_indexer_topk(q.data_ptr(), w.data_ptr(), keys.data_ptr(), B, H, D, S, K, idx.data_ptr(),
-                              _ptr(scores), _ptr(workspace), ws_bytes, _stream(stream))
+                              _ptr(scores), _ptr(workspace), ws_bytes,
+                              None if stage_events is None else ctypes.cast(stage_events, ctypes.c_void_p),
+                              _stream(stream))
     if rc != OK:
         raise HyMoeError(rc, "hy_indexer_topk")
     return idx, scores

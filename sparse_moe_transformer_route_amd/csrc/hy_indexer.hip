@@ -14,9 +14,9 @@
 // of one key, weights and clips them in registers, and one shuffle adds the two halves.
 // The kernel streams the keys once: HBM-bound.
 //
-// indexer_topk_kernel: one 1024-thread workgroup per query. An MSB-first radix select
-// over 8-bit digits of an order-preserving key of the fp32 scores finds the K-th
-// score; the first digit (sign and exponent) takes few values, so its histogram counts
+// indexer_topk_kernel: one 1024-thread workgroup per query (for up to 64K keys each
+// thread holds 64 of them, loaded once: 32 in registers, 32 in LDS). An MSB-first radix select over
+// 8-bit digits of an order-preserving key of the fp32 scores finds the K-th score; the first digit (sign and exponent) takes few values, so its histogram counts
 // are combined per wave (one LDS atomic per distinct digit), later digits are spread
 // and go straight to per-wave histograms. Keys above the K-th, then the lowest-index
 // keys equal to it, are written in ascending key order through block prefix sums.
@@ -33,6 +33,7 @@ namespace {
 constexpr int kIxKeys = 128;      // keys per scoring workgroup (4 waves x 32)
 constexpr int kIxHeads = 32;      // MFMA rows
 constexpr int kIxSelThreads = 1024;
+constexpr int kIxKeysPerThread = 64;  // selection keys held in registers per thread (S <= 64K)
 
 #define IX_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -92,60 +93,100 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// KPT > 0: S <= kIxSelThreads * KPT, each thread holds the keys of indices
+// [t KPT, t KPT + KPT) (loaded once, all loads in flight together);
+// KPT == 0: any S, every pass reads the scores again (thread t: indices t, t + 1024, ...
+// for the histograms, a contiguous range for the output).
+template <int KPT>
 __global__ void __launch_bounds__(kIxSelThreads) indexer_topk_kernel(const float* __restrict__ scores, int S, int K,
                                                                      int32_t* __restrict__ idx) {
   constexpr int NW = kIxSelThreads / 64;
   __shared__ uint32_t hist[NW][256];
   __shared__ uint32_t total[256];
+  __shared__ int runc[256];  // per-wave running counts of the digit search
   __shared__ uint32_t sh_prefix, sh_need;
   __shared__ int wsum[17];
   const int b = blockIdx.x;
   const float* sc = scores + (size_t)b * S;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n = min(K, S);
+  // contiguous range of this thread (the output is written in index order)
+  const int c = KPT > 0 ? KPT : (S + kIxSelThreads - 1) / kIxSelThreads;
+  const int lo = min(S, tid * c), hi = min(S, lo + c);
+  // keys j < KREG in registers, the rest in LDS (word [j - KREG][tid]: consecutive
+  // threads on consecutive banks); all in registers spilled
+  constexpr int KREG = KPT > 0 ? KPT / 2 : 1;
+  __shared__ uint32_t kl[KPT > 0 ? KPT - KPT / 2 : 1][kIxSelThreads];
+  uint32_t kr[KREG];
+  auto kget = [&](int j) -> uint32_t { return j < KREG ? kr[j] : kl[j - KREG][tid]; };
+  if constexpr (KPT > 0) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const uint32_t key = lo + j < hi ? order_key(sc[lo + j]) : 0u;
+      if (j < KREG)
+        kr[j] = key;
+      else
+        kl[j - KREG][tid] = key;
+    }
+  }
   uint32_t prefix = 0, mask = 0, need = (uint32_t)n;  // need: keys still to take at or below the prefix
+  // one key of the histogram pass: act = the key is a candidate
+  auto count = [&](bool act, uint32_t dig, bool first) {
+    if (first) {
+      // few distinct leading digits: one atomic per distinct digit of the wave
+      unsigned long long pend = __ballot(act);
+      while (pend) {
+        const int leader = __builtin_ctzll(pend);
+        const uint32_t v = __shfl(dig, leader, 64);
+        const unsigned long long same = __ballot(act && dig == v) & pend;
+        if (lane == leader) atomicAdd(&hist[wv][v], (uint32_t)__popcll(same));
+        pend &= ~same;
+      }
+    } else if (act) {
+      atomicAdd(&hist[wv][dig], 1u);
+    }
+  };
 #pragma unroll 1
   for (int d = 3; d >= 0; --d) {
     for (int i = tid; i < NW * 256; i += kIxSelThreads) (&hist[0][0])[i] = 0u;
     __syncthreads();
     const int sh = 8 * d;
-    for (int i0 = 0; i0 < S; i0 += kIxSelThreads) {
-      const int i = i0 + tid;
-      const uint32_t key = i < S ? order_key(sc[i]) : 0u;
-      const bool act = i < S && (key & mask) == prefix;
-      const uint32_t dig = (key >> sh) & 255u;
-      if (d == 3) {
-        // few distinct leading digits: one atomic per distinct digit of the wave
-        unsigned long long pend = __ballot(act);
-        while (pend) {
-          const int leader = __builtin_ctzll(pend);
-          const uint32_t v = __shfl(dig, leader, 64);
-          const unsigned long long same = __ballot(act && dig == v) & pend;
-          if (lane == leader) atomicAdd(&hist[wv][v], (uint32_t)__popcll(same));
-          pend &= ~same;
-        }
-      } else if (act) {
-        atomicAdd(&hist[wv][dig], 1u);
+    if constexpr (KPT > 0) {
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const uint32_t key = kget(j);
+        count(lo + j < hi && (key & mask) == prefix, (key >> sh) & 255u, d == 3);
       }
+    } else {
+      for (int i0 = 0; i0 < S; i0 += kIxSelThreads) {
+        const int i = i0 + tid;
+        const uint32_t key = i < S ? order_key(sc[i]) : 0u;
+        count(i < S && (key & mask) == prefix, (key >> sh) & 255u, d == 3);
+      }
+    }
+    __syncthreads();
+    // thread t < 256 takes digit 255 - t: its count, and by a scan over the 4 waves the
+    // count of candidates with that digit or a larger one; the digit holding the
+    // need-th largest candidate is the one where that running count reaches need
+    if (tid < 256) {
+      const int v = 255 - tid;
+      int cnt = 0;
+#pragma unroll
+      for (int k = 0; k < NW; ++k) cnt += (int)hist[k][v];
+      const int incl = wave_inclusive_scan(cnt);
+      if (lane == 63) wsum[wv] = incl;
+      total[tid] = (uint32_t)cnt;
+      runc[tid] = incl;
     }
     __syncthreads();
     if (tid < 256) {
-      uint32_t c = 0;
-#pragma unroll
-      for (int k = 0; k < NW; ++k) c += hist[k][tid];
-      total[tid] = c;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      // the digit holding the need-th largest remaining key, counting from 255 down
-      uint32_t rem = need;
-      int v = 255;
-      for (; v > 0; --v) {
-        if (rem <= total[v]) break;
-        rem -= total[v];
+      int base = 0;
+      for (int k = 0; k < wv; ++k) base += wsum[k];
+      const int incl = base + runc[tid], cnt = (int)total[tid];
+      if (incl >= (int)need && incl - cnt < (int)need) {
+        sh_prefix = prefix | ((uint32_t)(255 - tid) << sh);
+        sh_need = need - (uint32_t)(incl - cnt);
       }
-      sh_prefix = prefix | ((uint32_t)v << sh);
-      sh_need = rem;
     }
     __syncthreads();
     prefix = sh_prefix;
@@ -153,29 +194,49 @@ __global__ void __launch_bounds__(kIxSelThreads) indexer_topk_kernel(const float
     mask |= 255u << sh;
   }
   // prefix = the K-th largest key; take every key above it and the `need` lowest-index
-  // keys equal to it. Thread t owns indices [t c, t c + c).
-  const int c = (S + kIxSelThreads - 1) / kIxSelThreads;
-  const int lo = min(S, tid * c), hi = min(S, lo + c);
+  // keys equal to it
+  auto key_at = [&](int j) -> uint32_t {
+    if constexpr (KPT > 0)
+      return kget(j);
+    else
+      return order_key(sc[lo + j]);
+  };
   int n_gt = 0, n_eq = 0;
-  for (int i = lo; i < hi; ++i) {
-    const uint32_t key = order_key(sc[i]);
-    n_gt += key > prefix;
-    n_eq += key == prefix;
+  if constexpr (KPT > 0) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      if (lo + j < hi) {
+        const uint32_t key = kget(j);
+        n_gt += key > prefix;
+        n_eq += key == prefix;
+      }
+  } else {
+    for (int j = 0; lo + j < hi; ++j) {
+      const uint32_t key = key_at(j);
+      n_gt += key > prefix;
+      n_eq += key == prefix;
+    }
   }
   int tot = 0;
   const int eq_before = block_exclusive_scan(n_eq, wsum, &tot);
   const int take_eq = max(0, min(n_eq, (int)need - eq_before));
-  const int pos0 = block_exclusive_scan(n_gt + take_eq, wsum, &tot);
-  int pos = pos0, eq_seen = 0;
+  int pos = block_exclusive_scan(n_gt + take_eq, wsum, &tot);
+  int eq_seen = 0;
   int32_t* out = idx + (size_t)b * n;
-  for (int i = lo; i < hi; ++i) {
-    const uint32_t key = order_key(sc[i]);
+  auto emit = [&](int j, uint32_t key) {
     bool take = key > prefix;
     if (key == prefix) {
       take = eq_seen < take_eq;
       ++eq_seen;
     }
-    if (take && pos < n) out[pos++] = i;  // the bound only guards the buffer
+    if (take && pos < n) out[pos++] = lo + j;  // the bound only guards the buffer
+  };
+  if constexpr (KPT > 0) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      if (lo + j < hi) emit(j, kget(j));
+  } else {
+    for (int j = 0; lo + j < hi; ++j) emit(j, key_at(j));
   }
 }
 
@@ -202,7 +263,7 @@ extern "C" size_t hy_indexer_workspace_size(int64_t B, int64_t S) {
 
 extern "C" int hy_indexer_topk(const void* q, const float* w, const void* keys, int64_t B, int64_t H, int64_t D,
                                int64_t S, int64_t K, int32_t* idx, float* scores, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+                               size_t workspace_bytes, void* const* stage_events, void* stream) {
   using namespace hymoe;
   const int rc = ix_check(B, H, D, S, K);
   if (rc != HY_MOE_OK) return rc;
@@ -218,11 +279,21 @@ extern "C" int hy_indexer_topk(const void* q, const float* w, const void* keys, 
     sc = (float*)workspace;
   }
   hipStream_t s = (hipStream_t)stream;
+  // optional profiling events: before the scores, after them, after the selection
+  auto mark = [&](int i) {
+    return (stage_events && stage_events[i]) ? hipEventRecord((hipEvent_t)stage_events[i], s) : hipSuccess;
+  };
+  if (mark(0) != hipSuccess) return HY_MOE_ERR_HIP;
   hipLaunchKernelGGL(indexer_scores_kernel<128>, dim3((unsigned)((S + kIxKeys - 1) / kIxKeys), (unsigned)B), dim3(256),
                      0, s, (const uint16_t*)q, w, (const uint16_t*)keys, (int)S, sc);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return HY_MOE_ERR_HIP;
-  hipLaunchKernelGGL(indexer_topk_kernel, dim3((unsigned)B), dim3(kIxSelThreads), 0, s, (const float*)sc, (int)S,
-                     (int)(K < S ? K : S), idx);
-  return hipGetLastError() == hipSuccess ? HY_MOE_OK : HY_MOE_ERR_HIP;
+  if (err != hipSuccess || mark(1) != hipSuccess) return HY_MOE_ERR_HIP;
+  if (S <= kIxSelThreads * kIxKeysPerThread)
+    hipLaunchKernelGGL(indexer_topk_kernel<kIxKeysPerThread>, dim3((unsigned)B), dim3(kIxSelThreads), 0, s,
+                       (const float*)sc, (int)S, (int)(K < S ? K : S), idx);
+  else
+    hipLaunchKernelGGL(indexer_topk_kernel<0>, dim3((unsigned)B), dim3(kIxSelThreads), 0, s, (const float*)sc, (int)S,
+                       (int)(K < S ? K : S), idx);
+  if (hipGetLastError() != hipSuccess || mark(2) != hipSuccess) return HY_MOE_ERR_HIP;
+  return HY_MOE_OK;
 }

@@ -200,7 +200,7 @@ def test_indexer_argument_checks():
     out = FAKE
 
     def ix(q=FAKE, w=FAKE, keys=FAKE, B=2, H=32, D=128, S=1000, K=64, idx=out, scores=FAKE, ws=None, wsb=0):
-        return L.hy_indexer_topk(q, w, keys, B, H, D, S, K, idx, scores, ws, wsb, None)
+        return L.hy_indexer_topk(q, w, keys, B, H, D, S, K, idx, scores, ws, wsb, None, None)
     assert ix(H=16) == hm.ERR_UNSUPPORTED
     assert ix(D=64) == hm.ERR_UNSUPPORTED
     assert ix(B=70000) == hm.ERR_UNSUPPORTED
