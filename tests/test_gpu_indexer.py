@@ -87,6 +87,8 @@ def run_case(cfg, keys_dev=None, keys_host=None):
     (1, 1, 1),
     (2, 5000, 2048),
     (5, 129, 128),     # one key past a tile
+    (2, 70001, 2048),  # more keys than the selection holds on chip (64K): scores re-read per pass
+    (1, 65536, 4096),  # exactly the on-chip capacity, 16-byte loads
 ])
 def test_indexer_small(B, S, K):
     run_case(hi.IndexerConfig("ix", B=B, S=S, K=K, seed=3))
