@@ -224,7 +224,10 @@ int hy_moe_probe_hbm_read(const void* buf, size_t bytes, float* gbps, void* stre
  *   idx     DEVICE int32 [B][min(K, S)]  out: the K highest-scoring keys of each
  *           query, ties to the lower key index, in ascending key order
  *   scores  DEVICE fp32 [B][S] or NULL: out, the scores (fp32 accumulation); when NULL
- *           they go to `workspace` (256-byte aligned, hy_indexer_workspace_size bytes)
+ *           they stay in the workspace
+ *   workspace  DEVICE, 256-byte aligned, hy_indexer_workspace_size(B, S) bytes: the
+ *           scores and the candidates of the two-stage selection (chunks of 8192 keys
+ *           each keep their top K in parallel, then one merge per query)
  *   stage_events  NULL or 3 hipEvent_t (caller-created; NULL entries skipped) recorded
  *           before the scoring kernel, after it and after the selection kernel
  *   stream  hipStream_t; enqueued without blocking.

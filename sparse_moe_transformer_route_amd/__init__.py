@@ -245,7 +245,7 @@ def indexer_topk(q, w, keys, K, *, scores=None, workspace=None, stream=None, sta
     B, H, D = q.shape
     S = keys.shape[1]
     idx = torch.empty(B, min(K, S), dtype=torch.int32, device=q.device)
-    if scores is None and workspace is None:
+    if workspace is None:
         workspace = torch.empty(int(_lib.hy_indexer_workspace_size(B, S)), dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = _lib.hy_indexer_topk(q.data_ptr(), w.data_ptr(), keys.data_ptr(), B, H, D, S, K, idx.data_ptr(),

@@ -23,6 +23,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "hy_moe.h"
 #include "common.h"
 #include "dispatch.h"
@@ -33,7 +35,8 @@ namespace {
 constexpr int kIxKeys = 128;      // keys per scoring workgroup (4 waves x 32)
 constexpr int kIxHeads = 32;      // MFMA rows
 constexpr int kIxSelThreads = 1024;
-constexpr int kIxKeysPerThread = 64;  // selection keys held in registers per thread (S <= 64K)
+constexpr int kIxKeysPerThread = 64;  // selection keys held on chip per thread (S <= 64K)
+constexpr int kIxChunk = 8192;        // keys per workgroup in the first stage of the two-stage selection
 
 #define IX_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -97,17 +100,18 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 // [t KPT, t KPT + KPT) (loaded once, all loads in flight together);
 // KPT == 0: any S, every pass reads the scores again (thread t: indices t, t + 1024, ...
 // for the histograms, a contiguous range for the output).
+// The K highest of the S scores sc[0..S) (ties to the lower position), written in
+// ascending position order: out_idx[r] = remap ? remap[p] : offset + p, out_sc[r] = sc[p]
+// when out_sc is given. Called by every thread of a kIxSelThreads block.
 template <int KPT>
-__global__ void __launch_bounds__(kIxSelThreads) indexer_topk_kernel(const float* __restrict__ scores, int S, int K,
-                                                                     int32_t* __restrict__ idx) {
+__device__ __forceinline__ void topk_rows(const float* __restrict__ sc, int S, int K, const int32_t* __restrict__ remap,
+                                          int offset, int32_t* __restrict__ out_idx, float* __restrict__ out_sc) {
   constexpr int NW = kIxSelThreads / 64;
   __shared__ uint32_t hist[NW][256];
   __shared__ uint32_t total[256];
   __shared__ int runc[256];  // per-wave running counts of the digit search
   __shared__ uint32_t sh_prefix, sh_need;
   __shared__ int wsum[17];
-  const int b = blockIdx.x;
-  const float* sc = scores + (size_t)b * S;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n = min(K, S);
   // contiguous range of this thread (the output is written in index order)
@@ -115,12 +119,12 @@ __global__ void __launch_bounds__(kIxSelThreads) indexer_topk_kernel(const float
   const int lo = min(S, tid * c), hi = min(S, lo + c);
   // keys j < KREG in registers, the rest in LDS (word [j - KREG][tid]: consecutive
   // threads on consecutive banks); all in registers spilled
-  constexpr int KREG = KPT > 0 ? KPT / 2 : 1;
-  __shared__ uint32_t kl[KPT > 0 ? KPT - KPT / 2 : 1][kIxSelThreads];
+  constexpr int KREG = KPT > 32 ? KPT / 2 : KPT > 0 ? KPT : 1;
+  __shared__ uint32_t kl[KPT > 32 ? KPT - KPT / 2 : 1][kIxSelThreads];
   uint32_t kr[KREG];
   auto kget = [&](int j) -> uint32_t { return j < KREG ? kr[j] : kl[j - KREG][tid]; };
   if constexpr (KPT > 0) {
-    if ((S & 3) == 0 && hi - lo == KPT) {
+    if (KPT % 4 == 0 && ((uintptr_t)(sc + lo) & 15) == 0 && hi - lo == KPT) {
       // 16-byte loads: a quarter of the cache-line requests of 4-byte ones (a wave's
       // lanes are KPT * 4 bytes apart, each on its own line)
 #pragma unroll
@@ -240,14 +244,17 @@ __global__ void __launch_bounds__(kIxSelThreads) indexer_topk_kernel(const float
   const int take_eq = max(0, min(n_eq, (int)need - eq_before));
   int pos = block_exclusive_scan(n_gt + take_eq, wsum, &tot);
   int eq_seen = 0;
-  int32_t* out = idx + (size_t)b * n;
+  auto put = [&](int pos, int p) {
+    out_idx[pos] = remap ? remap[p] : offset + p;
+    if (out_sc) out_sc[pos] = sc[p];
+  };
   auto emit = [&](int j, uint32_t key) {
     bool take = key > prefix;
     if (key == prefix) {
       take = eq_seen < take_eq;
       ++eq_seen;
     }
-    if (take && pos < n) out[pos++] = lo + j;  // the bound only guards the buffer
+    if (take && pos < n) put(pos++, lo + j);  // the bound only guards the buffer
   };
   if constexpr (KPT > 0) {
 #pragma unroll
@@ -256,6 +263,39 @@ __global__ void __launch_bounds__(kIxSelThreads) indexer_topk_kernel(const float
   } else {
     for (int j = 0; lo + j < hi; ++j) emit(j, key_at(j));
   }
+}
+
+// One query per workgroup, all its scores at once.
+template <int KPT>
+__global__ void __launch_bounds__(kIxSelThreads) indexer_topk_kernel(const float* __restrict__ scores, int S, int K,
+                                                                     int32_t* __restrict__ idx) {
+  const int b = blockIdx.x;
+  topk_rows<KPT>(scores + (size_t)b * S, S, K, nullptr, 0, idx + (size_t)b * min(K, S), nullptr);
+}
+
+// Two-stage selection, stage 1: workgroup (g, b) keeps the K best keys of [g C, g C + C)
+// of query b (every key of the query's top K is among its chunk's top K), as (score,
+// index) pairs in index order at slots [g K, ...) of the query's G K candidate slots
+// (only the last chunk can hold fewer than K).
+template <int KPT>
+__global__ void __launch_bounds__(kIxSelThreads) indexer_topk_chunk_kernel(const float* __restrict__ scores, int S,
+                                                                           int K, int C, float* __restrict__ cand_sc,
+                                                                           int32_t* __restrict__ cand_idx) {
+  const int g = blockIdx.x, b = blockIdx.y, G = gridDim.x;
+  const int lo = g * C, len = min(C, S - lo);
+  const size_t slot = ((size_t)b * G + g) * K;
+  topk_rows<KPT>(scores + (size_t)b * S + lo, len, K, nullptr, lo, cand_idx + slot, cand_sc + slot);
+}
+
+// Stage 2: the K best of a query's L candidates (in index order, so ties still go to the
+// lower key and the output stays ascending).
+template <int KPT>
+__global__ void __launch_bounds__(kIxSelThreads) indexer_topk_merge_kernel(const float* __restrict__ cand_sc,
+                                                                           const int32_t* __restrict__ cand_idx, int L,
+                                                                           int stride, int K, int32_t* __restrict__ idx) {
+  const int b = blockIdx.x;
+  topk_rows<KPT>(cand_sc + (size_t)b * stride, L, K, cand_idx + (size_t)b * stride, 0, idx + (size_t)b * min(K, L),
+                 nullptr);
 }
 
 }  // namespace
@@ -275,8 +315,11 @@ int ix_check(int64_t B, int64_t H, int64_t D, int64_t S, int64_t K) {
 }  // namespace
 
 extern "C" size_t hy_indexer_workspace_size(int64_t B, int64_t S) {
+  using namespace hymoe;
   if (B < 0 || S < 0) return 0;
-  return ix_align(sizeof(float) * (size_t)(B * S > 0 ? B * S : 1));
+  // the scores, then the two-stage selection's candidates (G chunks x at most C each)
+  const size_t n = (size_t)(B * S > 0 ? B * S : 1), nc = (size_t)B * (size_t)(S + kIxChunk);
+  return ix_align(sizeof(float) * n) + ix_align(sizeof(float) * nc) + ix_align(sizeof(int32_t) * nc);
 }
 
 extern "C" int hy_indexer_topk(const void* q, const float* w, const void* keys, int64_t B, int64_t H, int64_t D,
@@ -286,16 +329,16 @@ extern "C" int hy_indexer_topk(const void* q, const float* w, const void* keys, 
   const int rc = ix_check(B, H, D, S, K);
   if (rc != HY_MOE_OK) return rc;
   if (B == 0 || S == 0) return HY_MOE_OK;
-  if (!q || !w || !keys || !idx) return HY_MOE_ERR_INVALID_ARG;
+  if (!q || !w || !keys || !idx || !workspace) return HY_MOE_ERR_INVALID_ARG;
   if (((uintptr_t)q & 15) || ((uintptr_t)keys & 15) || ((uintptr_t)w & 3) || ((uintptr_t)idx & 3) ||
       ((uintptr_t)scores & 3) || ((uintptr_t)workspace & 255))
     return HY_MOE_ERR_INVALID_ARG;
-  float* sc = scores;
-  if (!sc) {
-    if (!workspace) return HY_MOE_ERR_INVALID_ARG;
-    if (workspace_bytes < hy_indexer_workspace_size(B, S)) return HY_MOE_ERR_WORKSPACE;
-    sc = (float*)workspace;
-  }
+  if (workspace_bytes < hy_indexer_workspace_size(B, S)) return HY_MOE_ERR_WORKSPACE;
+  uint8_t* ws = (uint8_t*)workspace;
+  float* sc = scores ? scores : (float*)ws;
+  const size_t nc = (size_t)B * (size_t)(S + kIxChunk);
+  float* cand_sc = (float*)(ws + ix_align(sizeof(float) * (size_t)(B * S)));
+  int32_t* cand_idx = (int32_t*)((uint8_t*)cand_sc + ix_align(sizeof(float) * nc));
   hipStream_t s = (hipStream_t)stream;
   // optional profiling events: before the scores, after them, after the selection
   auto mark = [&](int i) {
@@ -304,14 +347,29 @@ extern "C" int hy_indexer_topk(const void* q, const float* w, const void* keys, 
   if (mark(0) != hipSuccess) return HY_MOE_ERR_HIP;
   hipLaunchKernelGGL(indexer_scores_kernel<128>, dim3((unsigned)((S + kIxKeys - 1) / kIxKeys), (unsigned)B), dim3(256),
                      0, s, (const uint16_t*)q, w, (const uint16_t*)keys, (int)S, sc);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || mark(1) != hipSuccess) return HY_MOE_ERR_HIP;
-  if (S <= kIxSelThreads * kIxKeysPerThread)
-    hipLaunchKernelGGL(indexer_topk_kernel<kIxKeysPerThread>, dim3((unsigned)B), dim3(kIxSelThreads), 0, s,
-                       (const float*)sc, (int)S, (int)(K < S ? K : S), idx);
-  else
-    hipLaunchKernelGGL(indexer_topk_kernel<0>, dim3((unsigned)B), dim3(kIxSelThreads), 0, s, (const float*)sc, (int)S,
-                       (int)(K < S ? K : S), idx);
+  if (hipGetLastError() != hipSuccess || mark(1) != hipSuccess) return HY_MOE_ERR_HIP;
+  const int k = (int)(K < S ? K : S);
+  const int64_t G = (S + kIxChunk - 1) / kIxChunk;
+  const int64_t L = (G - 1) * k + std::min<int64_t>(k, S - (G - 1) * kIxChunk);  // candidates per query
+  const dim3 blk(kIxSelThreads);
+  if (G >= 4 && k <= kIxChunk && L <= kIxSelThreads * 32) {
+    // two stages: G chunks per query select in parallel, then one merge per query
+    hipLaunchKernelGGL(indexer_topk_chunk_kernel<kIxChunk / kIxSelThreads>, dim3((unsigned)G, (unsigned)B), blk, 0, s,
+                       (const float*)sc, (int)S, k, kIxChunk, cand_sc, cand_idx);
+    if (hipGetLastError() != hipSuccess) return HY_MOE_ERR_HIP;
+    const int stride = (int)(G * k);
+    if (L <= kIxSelThreads * 16)
+      hipLaunchKernelGGL(indexer_topk_merge_kernel<16>, dim3((unsigned)B), blk, 0, s, (const float*)cand_sc,
+                         (const int32_t*)cand_idx, (int)L, stride, k, idx);
+    else
+      hipLaunchKernelGGL(indexer_topk_merge_kernel<32>, dim3((unsigned)B), blk, 0, s, (const float*)cand_sc,
+                         (const int32_t*)cand_idx, (int)L, stride, k, idx);
+  } else if (S <= kIxSelThreads * kIxKeysPerThread) {
+    hipLaunchKernelGGL(indexer_topk_kernel<kIxKeysPerThread>, dim3((unsigned)B), blk, 0, s, (const float*)sc, (int)S,
+                       k, idx);
+  } else {
+    hipLaunchKernelGGL(indexer_topk_kernel<0>, dim3((unsigned)B), blk, 0, s, (const float*)sc, (int)S, k, idx);
+  }
   if (hipGetLastError() != hipSuccess || mark(2) != hipSuccess) return HY_MOE_ERR_HIP;
   return HY_MOE_OK;
 }

@@ -208,7 +208,7 @@ def test_indexer_argument_checks():
     assert ix(S=-1) == hm.ERR_INVALID_ARG
     assert ix(q=None) == hm.ERR_INVALID_ARG
     assert ix(keys=FAKE + 8) == hm.ERR_INVALID_ARG          # keys must be 16-byte aligned
-    assert ix(scores=None) == hm.ERR_INVALID_ARG            # neither scores nor workspace
+    assert ix(scores=None) == hm.ERR_INVALID_ARG            # no workspace
     assert ix(scores=None, ws=FAKE, wsb=16) == hm.ERR_WORKSPACE
     assert ix(B=0, q=None, keys=None) == hm.OK              # empty: no pointer is touched
     assert ix(S=0, q=None, keys=None) == hm.OK

@@ -87,8 +87,10 @@ def run_case(cfg, keys_dev=None, keys_host=None):
     (1, 1, 1),
     (2, 5000, 2048),
     (5, 129, 128),     # one key past a tile
-    (2, 70001, 2048),  # more keys than the selection holds on chip (64K): scores re-read per pass
-    (1, 65536, 4096),  # exactly the on-chip capacity, 16-byte loads
+    (2, 70001, 2048),  # two-stage selection: 9 chunks of 8192 keys (the last one short), one merge
+    (1, 65536, 4096),  # two stages with the larger merge (32K candidates)
+    (1, 70001, 9000),  # K above a chunk: one pass over more keys than fit on chip (scores re-read)
+    (2, 20000, 100),   # 3 chunks of 8192 (fewer than 4): one pass on chip
 ])
 def test_indexer_small(B, S, K):
     run_case(hi.IndexerConfig("ix", B=B, S=S, K=K, seed=3))
