@@ -52,10 +52,14 @@ constexpr int kDepthDown = 3;           // chunks in flight, down (one matrix)
 constexpr int kDepthSharedTern = 2;
 // FP8 experts: each wave covers two 16-row blocks that share every activation load
 // (with one block the activation loads are half of all loads per weight byte: down was
-// 14% slower); rings of 3 chunks, as deeper ones measured no faster and cost occupancy.
+// 14% slower). A chunk is 128 codes of a row, one whole 128-byte line, as in the bf16
+// kernels: with 64-code chunks each load instruction took half lines and gate/up moved
+// 5.0 TB/s instead of 6.0. Ring depths: 2 chunks for gate/up (2 waves per SIMD), 1 for
+// down (4 waves per SIMD).
 constexpr int kFp8RowBlocks = 2;
-constexpr int kDepthFp8GateUp = 3;
-constexpr int kDepthFp8Down = 3;
+constexpr int kFp8Chunk = 128;
+constexpr int kDepthFp8GateUp = 2;
+constexpr int kDepthFp8Down = 1;
 
 // Weight formats of the streaming kernels.
 constexpr int kWfBf16 = 0, kWfTern = 1, kWfFp8 = 2;
@@ -123,54 +127,62 @@ __device__ __forceinline__ void gateup_bf16_block(const uint16_t* __restrict__ w
 }
 
 // ------------------------------------------------------------- FP8 experts
-// As gateup_bf16_block with E4M3 weights, for NR row blocks sharing the activations:
-// per chunk a lane loads the 16 codes of k [16 g, 16 g + 16) of its gate and up row in
-// each block (one 16-byte load each), the same k as its two 8-element activation pieces.
+// Per chunk, lane group g loads the 32 codes of k [32 g, 32 g + 32) of each of its rows
+// (two 16-byte loads) and the 32 matching activations (four); MFMA m of the chunk takes
+// k [32 g + 8 m, +8) in every lane group, codes widened to bf16 right before it.
 template <int D, int NR>
 __device__ __forceinline__ void gateup_fp8_block(const uint8_t* const (&wg)[NR], const uint8_t* const (&wu)[NR],
                                                  const uint16_t* __restrict__ xr, int d, f32x4 (&accg)[NR],
                                                  f32x4 (&accu)[NR]) {
-  uint4 rg[D + 1][NR], ru[D + 1][NR], rx[D + 1][kKV];
+  uint4 rg[D + 1][NR][2], ru[D + 1][NR][2], rx[D + 1][4];
   ring_stream<D>(
-      d / kChunk,
+      d / kFp8Chunk,
       [&](int ch, int slot) {
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          rg[slot][r] = ldg16(wg[r] + ch * kChunk);
-          ru[slot][r] = ldg16(wu[r] + ch * kChunk);
-        }
+        for (int r = 0; r < NR; ++r)
 #pragma unroll
-        for (int v = 0; v < kKV; ++v) rx[slot][v] = ldg16(xr + ch * kChunk + 8 * v);
+          for (int v = 0; v < 2; ++v) {
+            rg[slot][r][v] = ldg16(wg[r] + ch * kFp8Chunk + 16 * v);
+            ru[slot][r][v] = ldg16(wu[r] + ch * kFp8Chunk + 16 * v);
+          }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) rx[slot][m] = ldg16(xr + ch * kFp8Chunk + 8 * m);
       },
       [&](int u) {
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          accg[r] = mfma16x16x32(e4m3x8_bf16(rg[u][r].x, rg[u][r].y), rx[u][0], accg[r]);
-          accu[r] = mfma16x16x32(e4m3x8_bf16(ru[u][r].x, ru[u][r].y), rx[u][0], accu[r]);
-          accg[r] = mfma16x16x32(e4m3x8_bf16(rg[u][r].z, rg[u][r].w), rx[u][1], accg[r]);
-          accu[r] = mfma16x16x32(e4m3x8_bf16(ru[u][r].z, ru[u][r].w), rx[u][1], accu[r]);
-        }
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+          for (int v = 0; v < 2; ++v) {
+            accg[r] = mfma16x16x32(e4m3x8_bf16(rg[u][r][v].x, rg[u][r][v].y), rx[u][2 * v], accg[r]);
+            accu[r] = mfma16x16x32(e4m3x8_bf16(ru[u][r][v].x, ru[u][r][v].y), rx[u][2 * v], accu[r]);
+            accg[r] = mfma16x16x32(e4m3x8_bf16(rg[u][r][v].z, rg[u][r][v].w), rx[u][2 * v + 1], accg[r]);
+            accu[r] = mfma16x16x32(e4m3x8_bf16(ru[u][r][v].z, ru[u][r][v].w), rx[u][2 * v + 1], accu[r]);
+          }
       });
 }
 
 template <int D, int NR>
 __device__ __forceinline__ void down_fp8_block(const uint8_t* const (&wd)[NR], const uint16_t* __restrict__ hr, int I,
                                                f32x4 (&acc)[NR]) {
-  uint4 rw[D + 1][NR], rx[D + 1][kKV];
+  uint4 rw[D + 1][NR][2], rx[D + 1][4];
   ring_stream<D>(
-      I / kChunk,
+      I / kFp8Chunk,
       [&](int ch, int slot) {
 #pragma unroll
-        for (int r = 0; r < NR; ++r) rw[slot][r] = ldg16(wd[r] + ch * kChunk);
+        for (int r = 0; r < NR; ++r)
 #pragma unroll
-        for (int v = 0; v < kKV; ++v) rx[slot][v] = ldg16(hr + ch * kChunk + 8 * v);
+          for (int v = 0; v < 2; ++v) rw[slot][r][v] = ldg16(wd[r] + ch * kFp8Chunk + 16 * v);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) rx[slot][m] = ldg16(hr + ch * kFp8Chunk + 8 * m);
       },
       [&](int u) {
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          acc[r] = mfma16x16x32(e4m3x8_bf16(rw[u][r].x, rw[u][r].y), rx[u][0], acc[r]);
-          acc[r] = mfma16x16x32(e4m3x8_bf16(rw[u][r].z, rw[u][r].w), rx[u][1], acc[r]);
-        }
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+          for (int v = 0; v < 2; ++v) {
+            acc[r] = mfma16x16x32(e4m3x8_bf16(rw[u][r][v].x, rw[u][r][v].y), rx[u][2 * v], acc[r]);
+            acc[r] = mfma16x16x32(e4m3x8_bf16(rw[u][r][v].z, rw[u][r][v].w), rx[u][2 * v + 1], acc[r]);
+          }
       });
 }
 
@@ -311,21 +323,15 @@ __global__ void __launch_bounds__(256) stream_gateup_kernel(StreamArgs a, Expert
     const int i0 = blockIdx.x * 128 + wv * 16 * NR;
     const uint8_t* wg[NR];
     const uint8_t* wu[NR];
-    float sg[NR][4], su[NR][4];
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-      wg[r] = w.f8gate + ((size_t)e * I + i0 + 16 * r + r16) * d + 16 * g;
-      wu[r] = w.f8up + ((size_t)e * I + i0 + 16 * r + r16) * d + 16 * g;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sg[r][j] = w.f8sgate[(size_t)e * I + i0 + 16 * r + 4 * g + j];
-        su[r][j] = w.f8sup[(size_t)e * I + i0 + 16 * r + 4 * g + j];
-      }
+      wg[r] = w.f8gate + ((size_t)e * I + i0 + 16 * r + r16) * d + 32 * g;
+      wu[r] = w.f8up + ((size_t)e * I + i0 + 16 * r + r16) * d + 32 * g;
     }
     for (int cb = 0; cb < n; cb += 16) {
       const bool valid = cb + r16 < n;
       const int col = valid ? row0 + cb + r16 : row0;
-      const uint16_t* xr = a.x + (size_t)row_token(col, a.perm_src, a.Tk, a.k) * d + 16 * g;
+      const uint16_t* xr = a.x + (size_t)row_token(col, a.perm_src, a.Tk, a.k) * d + 32 * g;
       f32x4 accg[NR], accu[NR];
 #pragma unroll
       for (int r = 0; r < NR; ++r) accg[r] = accu[r] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -335,7 +341,11 @@ __global__ void __launch_bounds__(256) stream_gateup_kernel(StreamArgs a, Expert
         for (int r = 0; r < NR; ++r) {
           float hv[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) hv[j] = silu(accg[r][j] * sg[r][j]) * (accu[r][j] * su[r][j]);
+          for (int j = 0; j < 4; ++j) {
+            // the scales are read here, not kept across the ring (registers: occupancy)
+            const size_t unit = (size_t)e * I + i0 + 16 * r + 4 * g + j;
+            hv[j] = silu(accg[r][j] * w.f8sgate[unit]) * (accu[r][j] * w.f8sup[unit]);
+          }
           *reinterpret_cast<uint2*>(h + (size_t)col * I + i0 + 16 * r + 4 * g) =
               make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
         }
@@ -445,7 +455,7 @@ __global__ void __launch_bounds__(256) stream_down_kernel(StreamArgs a, ExpertWe
     float sd[NR][4];
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-      wd[r] = w.f8down + ((size_t)e * d + m0 + 16 * r + r16) * I + 16 * g;
+      wd[r] = w.f8down + ((size_t)e * d + m0 + 16 * r + r16) * I + 32 * g;
 #pragma unroll
       for (int j = 0; j < 4; ++j) sd[r][j] = w.f8sdown[(size_t)e * d + m0 + 16 * r + 4 * g + j];
     }
@@ -455,7 +465,7 @@ __global__ void __launch_bounds__(256) stream_down_kernel(StreamArgs a, ExpertWe
       f32x4 acc[NR];
 #pragma unroll
       for (int r = 0; r < NR; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-      down_fp8_block<kDepthFp8Down, NR>(wd, h + (size_t)col * I + 16 * g, I, acc);
+      down_fp8_block<kDepthFp8Down, NR>(wd, h + (size_t)col * I + 32 * g, I, acc);
       if (valid) {
 #pragma unroll
         for (int r = 0; r < NR; ++r)
