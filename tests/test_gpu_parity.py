@@ -192,7 +192,9 @@ def test_ternary_paths_agree_mid_size():
     dict(T=1, d=256, E=16, k=2, I=256),       # one token
     dict(T=32, d=512, E=16, k=4, I=256),      # ~8 tokens per expert
     dict(T=100, d=256, E=8, k=2, I=512),      # ~25 tokens per expert: two 16-token passes
-    dict(T=40, d=1024, E=16, k=2, I=1024),    # chunk counts that fill the FP8 ring exactly (16)
+    # 128-code chunks: gate/up d / 128, down I / 128; rings of 3 and 2 slots
+    dict(T=40, d=768, E=16, k=2, I=1024),     # 6 and 8 chunks: both rings filled exactly
+    dict(T=24, d=1024, E=8, k=2, I=384),      # 8 and 3 chunks: both ring loops guarded
 ])
 def test_fp8_small(shape):
     cfg = hi.LayerConfig("fp8", fp8=True, seed=6, **shape)
