@@ -144,6 +144,52 @@ def time_layer(hm, torch, inp, k, ws, steps, warmup, dominant):
     return total_ms, dom_ms, dict(zip(hm.KERNELS, per)), done
 
 
+def stream_work(cfg, touched):
+    """Algorithmic HBM bytes of a decode-size layer on the streaming path with `touched`
+    routed experts: the dominant gate/up launch (one unit per touched routed expert,
+    plus the shared expert) and the whole layer (every touched expert's weights once,
+    the router, x and the output)."""
+    d, I = cfg.d, cfg.I
+    if cfg.ternary:
+        unit = 2 * I * (d // 128 * 5 * 4) + 2 * I * 2    # packed codes + bf16 row scales
+        shared = 2 * I * d * 2
+        alg = touched * unit + shared
+        per_unit = f"{unit} B packed gate+up codes and scales per touched routed expert, plus {shared} B bf16 shared"
+        layer_bytes = touched * (3 * I * (d // 128 * 5 * 4) + 2 * I * 2 + d * 2) + 3 * I * d * 2
+    elif cfg.fp8:
+        unit = 2 * I * d + 2 * I * 4                    # E4M3 codes + fp32 row scales
+        shared = 2 * I * d * 2
+        alg = touched * unit + shared
+        per_unit = f"{unit} B of E4M3 gate+up codes and scales per touched routed expert, plus {shared} B bf16 shared"
+        layer_bytes = touched * (3 * I * d + (2 * I + d) * 4) + 3 * I * d * 2
+    else:
+        unit = 2 * I * d * 2
+        alg = (touched + 1) * unit
+        per_unit = f"{unit} B of bf16 gate+up weights per touched expert (routed + shared)"
+        layer_bytes = (touched + 1) * 3 * I * d * 2
+    layer_bytes += cfg.E * d * 2 + 2 * cfg.T * d * 2
+    # ternary weights with d and I multiples of 512 run in the LDS-staged kernel
+    tern_lds = cfg.ternary and d % 512 == 0 and I % 512 == 0
+    kernel = ("tern_lds_kernel<2>" if tern_lds else "stream_gateup_kernel<2> (FP8 routed experts)" if cfg.fp8
+              else "stream_gateup_kernel")
+    return {"unit": unit, "alg": alg, "per_unit": per_unit, "layer_bytes": layer_bytes,
+            "key": "ternary_gateup" if tern_lds else "stream_gateup", "kernel": kernel}
+
+
+def gemm_work(cfg):
+    """Algorithmic flops of a layer on the grouped path: the dominant gate/up stage
+    (4 d I per dispatched row, routed and shared) and the whole layer (router + all
+    three expert products)."""
+    d, I = cfg.d, cfg.I
+    rows = cfg.T * cfg.k + cfg.T
+    kernel = ("grouped_gemm_kernel<true, 0, 1> (ternary routed tiles) + grouped_gemm_kernel<true, 0, 0> "
+              "(bf16 shared tiles): one timed stage" if cfg.ternary else
+              "grouped_gemm_kernel<true, 0, 2> (FP8 routed tiles) + grouped_gemm_kernel<true, 0, 0> "
+              "(bf16 shared tiles): one timed stage" if cfg.fp8 else "grouped_gemm_kernel<true, 0, 0>")
+    return {"rows": rows, "alg": 4 * rows * d * I, "layer_flop": 2 * cfg.T * d * cfg.E + 6 * rows * d * I,
+            "per_unit": f"{4 * d * I} flop per dispatched row (gate and up: 2*d*I each)", "kernel": kernel}
+
+
 def run_config(name, args, hi, hm, torch, weights=None):
     cfg = hi.CONFIGS[name]
     dev = "cuda:0"
@@ -166,56 +212,23 @@ def run_config(name, args, hi, hm, torch, weights=None):
     counts = routing["counts"].cpu()
     touched = int((counts > 0).sum())
     stream_path = cfg.T * cfg.k <= 16 * cfg.E  # the library's automatic path choice
-    d, I = cfg.d, cfg.I
     kernel_file = "sparse_moe_transformer_route_amd/csrc/" + ("moe_stream.hip" if stream_path else "moe_gemm.hip")
     if stream_path:
-        # dominant kernel: gate/up streaming; unit = one touched expert's gate+up weights
-        if cfg.ternary:
-            unit = 2 * I * (d // 128 * 5 * 4) + 2 * I * 2    # packed codes + row scales
-            shared = 2 * I * d * 2
-            alg = touched * unit + shared
-            per_unit = f"{unit} B packed gate+up codes and scales per touched routed expert, plus {shared} B bf16 shared"
-        elif cfg.fp8:
-            unit = 2 * I * d + 2 * I * 4                    # E4M3 codes + fp32 row scales
-            shared = 2 * I * d * 2
-            alg = touched * unit + shared
-            per_unit = f"{unit} B of E4M3 gate+up codes and scales per touched routed expert, plus {shared} B bf16 shared"
-        else:
-            unit = 2 * I * d * 2
-            alg = (touched + 1) * unit
-            per_unit = f"{unit} B of bf16 gate+up weights per touched expert (routed + shared)"
+        w = stream_work(cfg, touched)
         sec = dom_ms * 1e-3
-        # ternary weights with d and I multiples of 512 run in the LDS-staged kernel
-        tern_lds = cfg.ternary and d % 512 == 0 and I % 512 == 0
-        key = "ternary_gateup" if tern_lds else "stream_gateup"
+        alg = w["alg"]
         roof = {"bound": "hbm", "achieved": alg / sec / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                "frac": alg / sec / PEAK_HBM, "traffic": traffic_for(f"{key}/{name}", touched + 1),
-                "kernel": ("tern_lds_kernel<2>" if tern_lds else "stream_gateup_kernel<2> (FP8 routed experts)" if cfg.fp8
-                           else "stream_gateup_kernel"), "per_unit": per_unit,
-                "units_per_launch": touched + 1, "kernel_ms": dom_ms}
-        # whole-layer HBM fraction: every touched expert's weights once + router + x/out
-        if cfg.ternary:
-            layer_bytes = touched * (3 * I * (d // 128 * 5 * 4) + 2 * I * 2 + d * 2) + 3 * I * d * 2
-        elif cfg.fp8:
-            layer_bytes = touched * (3 * I * d + (2 * I + d) * 4) + 3 * I * d * 2
-        else:
-            layer_bytes = (touched + 1) * 3 * I * d * 2
-        layer_bytes += cfg.E * d * 2 + 2 * cfg.T * d * 2
-        layer = {"bytes": layer_bytes, "hbm_frac": layer_bytes / (ms * 1e-3) / PEAK_HBM}
+                "frac": alg / sec / PEAK_HBM, "traffic": traffic_for(f"{w['key']}/{name}", touched + 1),
+                "kernel": w["kernel"], "per_unit": w["per_unit"], "units_per_launch": touched + 1, "kernel_ms": dom_ms}
+        layer = {"bytes": w["layer_bytes"], "hbm_frac": w["layer_bytes"] / (ms * 1e-3) / PEAK_HBM}
     else:
-        rows = cfg.T * cfg.k + cfg.T
-        alg = 4 * rows * d * I
+        w = gemm_work(cfg)
+        rows, alg = w["rows"], w["alg"]
         sec = dom_ms * 1e-3
         roof = {"bound": "mfma", "achieved": alg / sec / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
                 "frac": alg / sec / PEAK_BF16, "traffic": traffic_for(f"grouped_gemm_gateup/{name}", rows),
-                "kernel": ("grouped_gemm_kernel<true, 0, 1> (ternary routed tiles) + grouped_gemm_kernel<true, 0, 0> "
-                           "(bf16 shared tiles): one timed stage" if cfg.ternary else
-                           "grouped_gemm_kernel<true, 0, 2> (FP8 routed tiles) + grouped_gemm_kernel<true, 0, 0> "
-                           "(bf16 shared tiles): one timed stage" if cfg.fp8 else "grouped_gemm_kernel<true, 0, 0>"),
-                "per_unit": f"{4 * d * I} flop per dispatched row "
-                f"(gate and up: 2*d*I each)", "units_per_launch": rows, "kernel_ms": dom_ms}
-        flops = 2 * cfg.T * d * cfg.E + 6 * rows * d * I
-        layer = {"flop": flops, "mfma_frac": flops / (ms * 1e-3) / PEAK_BF16}
+                "kernel": w["kernel"], "per_unit": w["per_unit"], "units_per_launch": rows, "kernel_ms": dom_ms}
+        layer = {"flop": w["layer_flop"], "mfma_frac": w["layer_flop"] / (ms * 1e-3) / PEAK_BF16}
     roof["kernel_source_sha256_16"] = source_digest(os.path.join(ROOT, kernel_file))
     return {"cfg": cfg, "inp": inp, "ms": ms, "tokens_per_s": cfg.T / (ms * 1e-3), "kernels_ms": kern,
             "roofline": roof, "layer": layer, "touched": touched, "counts": counts, "routing": routing,
