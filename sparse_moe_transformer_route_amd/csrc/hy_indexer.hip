@@ -96,14 +96,20 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// the float an order key came from (order_key is a bijection on bit patterns)
+__device__ __forceinline__ float key_float(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
 // KPT > 0: S <= kIxSelThreads * KPT, each thread holds the keys of indices
 // [t KPT, t KPT + KPT) (loaded once, all loads in flight together);
 // KPT == 0: any S, every pass reads the scores again (thread t: indices t, t + 1024, ...
 // for the histograms, a contiguous range for the output).
 // The K highest of the S scores sc[0..S) (ties to the lower position), written in
 // ascending position order: out_idx[r] = remap ? remap[p] : offset + p, out_sc[r] = sc[p]
-// when out_sc is given. Called by every thread of a kIxSelThreads block.
-template <int KPT>
+// when out_sc is given (REMAP: remap is given, and held in registers). Called by every
+// thread of a kIxSelThreads block.
+template <int KPT, bool REMAP = false>
 __device__ __forceinline__ void topk_rows(const float* __restrict__ sc, int S, int K, const int32_t* __restrict__ remap,
                                           int offset, int32_t* __restrict__ out_idx, float* __restrict__ out_sc) {
   constexpr int NW = kIxSelThreads / 64;
@@ -149,6 +155,25 @@ __device__ __forceinline__ void topk_rows(const float* __restrict__ sc, int S, i
         else
           kl[j - KREG][tid] = key;
       }
+    }
+  }
+  // REMAP: the positions' output indices, loaded with the keys so that writing the
+  // output waits on no load (a gather per taken key was a quarter of the merge stage)
+  static_assert(!REMAP || (KPT > 0 && KPT <= 32), "remapped rows are held in registers");
+  int32_t rv[REMAP ? KPT : 1];
+  if constexpr (REMAP) {
+    if (KPT % 4 == 0 && ((uintptr_t)(remap + lo) & 15) == 0 && hi - lo == KPT) {
+#pragma unroll
+      for (int m = 0; m < KPT / 4; ++m) {
+        const int4 v = *reinterpret_cast<const int4*>(remap + lo + 4 * m);
+        rv[4 * m] = v.x;
+        rv[4 * m + 1] = v.y;
+        rv[4 * m + 2] = v.z;
+        rv[4 * m + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) rv[j] = lo + j < hi ? remap[lo + j] : 0;
     }
   }
   uint32_t prefix = 0, mask = 0, need = (uint32_t)n;  // need: keys still to take at or below the prefix
@@ -244,9 +269,13 @@ __device__ __forceinline__ void topk_rows(const float* __restrict__ sc, int S, i
   const int take_eq = max(0, min(n_eq, (int)need - eq_before));
   int pos = block_exclusive_scan(n_gt + take_eq, wsum, &tot);
   int eq_seen = 0;
-  auto put = [&](int pos, int p) {
-    out_idx[pos] = remap ? remap[p] : offset + p;
-    if (out_sc) out_sc[pos] = sc[p];
+  // the score written back is the key's own float (bit-exact), not a reload
+  auto put = [&](int pos, int j, uint32_t key) {
+    if constexpr (REMAP)
+      out_idx[pos] = rv[j];
+    else
+      out_idx[pos] = remap ? remap[lo + j] : offset + lo + j;
+    if (out_sc) out_sc[pos] = key_float(key);
   };
   auto emit = [&](int j, uint32_t key) {
     bool take = key > prefix;
@@ -254,7 +283,7 @@ __device__ __forceinline__ void topk_rows(const float* __restrict__ sc, int S, i
       take = eq_seen < take_eq;
       ++eq_seen;
     }
-    if (take && pos < n) put(pos++, lo + j);  // the bound only guards the buffer
+    if (take && pos < n) put(pos++, j, key);  // the bound only guards the buffer
   };
   if constexpr (KPT > 0) {
 #pragma unroll
@@ -294,8 +323,8 @@ __global__ void __launch_bounds__(kIxSelThreads) indexer_topk_merge_kernel(const
                                                                            const int32_t* __restrict__ cand_idx, int L,
                                                                            int stride, int K, int32_t* __restrict__ idx) {
   const int b = blockIdx.x;
-  topk_rows<KPT>(cand_sc + (size_t)b * stride, L, K, cand_idx + (size_t)b * stride, 0, idx + (size_t)b * min(K, L),
-                 nullptr);
+  topk_rows<KPT, true>(cand_sc + (size_t)b * stride, L, K, cand_idx + (size_t)b * stride, 0,
+                       idx + (size_t)b * min(K, L), nullptr);
 }
 
 }  // namespace
