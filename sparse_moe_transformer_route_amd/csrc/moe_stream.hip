@@ -14,7 +14,9 @@
 // product runs on 16x16x32 bf16 MFMA with fp32 accumulation (experts with more than
 // 16 tokens take several passes). Sherry-ternary experts are decoded in registers from 5-bit codes
 // through a 32-entry LDS table into bf16 +-1/0 and scaled per row after the sum; FP8
-// (E4M3) experts are converted to bf16 in registers (exact) and scaled per row likewise.
+// (E4M3) experts stream 128-code chunks (one 128-byte line per row: lane (r, g) reads
+// bytes [32g, 32g+32)) for two 16-row blocks per wave, 128 rows per workgroup, are
+// converted to bf16 in registers (exact) and scaled per row likewise.
 #include "common.h"
 #include "kernels.h"
 
