@@ -74,7 +74,9 @@ CONFIGS = {
 
 
 def _load_host():
-    path = os.path.join(_HERE, "libhy_gen.so")
+    # HY_GEN_LIB: another build of gen_host.c (the sanitizer test loads an
+    # AddressSanitizer/UBSan build through it)
+    path = os.environ.get("HY_GEN_LIB") or os.path.join(_HERE, "libhy_gen.so")
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")
     lib = ctypes.CDLL(path)

@@ -72,8 +72,8 @@ typedef enum {
    * Every bit pattern is a valid block. */
   HY_MOE_WEIGHTS_SHERRY_TERNARY = 1,
   /* FP8 weights (the Hy4 preview release ships BF16 and FP8 weights, FP8 halving
-   * the weight storage: fengxiaobai.com Hy4 preview overview, section "MTP、FP8
-   * 与低价 API"). The pages give no encoding or scale layout; taken here: each
+   * the weight storage: app.myzaker.com Hy4 Preview news, section "MTP、FP8 与
+   * 低价 API"). The pages give no encoding or scale layout; taken here: each
    * routed expert weight is one OCP 8-bit float in the E4M3 encoding (sign bit 7,
    * exponent bits 6-3 with bias 7, mantissa bits 2-0; exponent 0 is subnormal,
    * S.1111.111 is NaN, no infinities), each output row has one fp32 scale, and

@@ -22,7 +22,9 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        path = os.path.join(_HERE, "libhy_oracle.so")
+        # HY_ORACLE_LIB: another build of hy_oracle.c (the sanitizer test loads an
+        # AddressSanitizer/UBSan build through it)
+        path = os.environ.get("HY_ORACLE_LIB") or os.path.join(_HERE, "libhy_oracle.so")
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")
         L = ctypes.CDLL(path)

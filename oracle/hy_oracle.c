@@ -40,8 +40,8 @@
  * the row's bf16 scale times the ternary value.
  *
  * FP8 weights (the Hy4 preview release ships BF16 and FP8 weights, FP8 halving
- * the weight storage: fengxiaobai.com Hy4 preview overview, section "MTP、FP8
- * 与低价 API"; the model card lists an official FP8 checkpoint). The pages fix
+ * the weight storage: app.myzaker.com Hy4 Preview news, section "MTP、FP8 与
+ * 低价 API"; the model card lists an official FP8 checkpoint). The pages fix
  * no format, scale layout or activation precision. Reading taken here: routed
  * experts' weights are OCP 8-bit floats in the E4M3 encoding (no infinities:
  * sign bit 7, exponent bits 6-3 with bias 7, mantissa bits 2-0; exponent 0 is

@@ -621,7 +621,8 @@ __global__ void __launch_bounds__(256, kTlWgPerCu) tern_lds_kernel(StreamArgs a,
   }
   const int ridx = blockIdx.y - sh + 1;  // touched[0] is the shared expert
   if (ridx >= a.meta[0]) return;         // whole workgroup
-  build_code_table(lut);                 // visible after the first barrier below
+  build_code_table(lut);
+  __syncthreads();  // the table's LDS writes are visible to every wave before the first decode
   const int e = a.touched[ridx];
   const int row0 = a.offs[e], n = a.offs[e + 1] - row0;
   const int K = NM == 2 ? a.d : a.I;

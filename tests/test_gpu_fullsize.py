@@ -9,9 +9,11 @@ path choice, caller workspace):
   fp8      T=32,   FP8 (E4M3, fp32 row scales) routed experts, bf16 shared expert
   fp8_prefill  T=8192, the same weights on the grouped path
 The routing of every token (sets, weights, counts, offsets, permutation) is
-compared with the oracle; outputs are compared on sampled tokens, for which the
-oracle regenerates the touched experts' weights on the host from the same
-seeded streams. Rules and tolerances: tests/parity.py.
+compared with the oracle. Outputs: every token of the decode batches; at
+prefill sizes a sample chosen from the routing so that it covers the grouped
+GEMM's schedule (tile_sample). The oracle's expert weights are copies of the
+generator's device tensors (never a result of the HIP path), taken one expert at
+a time. Rules and tolerances: tests/parity.py.
 """
 import time
 
@@ -20,7 +22,8 @@ import pytest
 
 import hy_inputs as hi
 import oracle
-from parity import bf16_tensor_to_np, check_out, check_permutation, check_routing, check_weights, routing_to_np
+from parity import (bf16_tensor_bits, bf16_tensor_to_np, check_out, check_permutation, check_routing,
+                    check_weights, routing_to_np, tile_sample)
 
 torch = pytest.importorskip("torch")
 hm = pytest.importorskip("sparse_moe_transformer_route_amd")
@@ -45,41 +48,46 @@ def hy4_weights():
     torch.cuda.empty_cache()
 
 
-def sampled_reference(cfg, x_host, sets, w, tokens, ternary=False, fp8=False):
-    """Oracle outputs of the sampled tokens, one expert's weights at a time."""
-    sh = hi.host_shared(cfg)
+class DeviceExperts:
+    """Routed experts' weights for the oracle, copied from the generator's device
+    tensors one expert at a time (bf16 bits, or decoded Sherry / FP8 weights)."""
+
+    def __init__(self, inp):
+        self.inp = inp
+
+    def get(self, e):
+        inp = self.inp
+        if "fgate" in inp:
+            return tuple(oracle.fp8_decode(inp[q][e].cpu().numpy(), inp[s][e].cpu().numpy())
+                         for q, s in (("fgate", "fsgate"), ("fup", "fsup"), ("fdown", "fsdown"))), True
+        if "qgate" in inp:
+            return tuple(oracle.sherry_decode(inp[q][e].cpu().numpy().view(np.uint32), bf16_tensor_bits(inp[s][e]))[1]
+                         for q, s in (("qgate", "sgate"), ("qup", "sup"), ("qdown", "sdown"))), False
+        return tuple(bf16_tensor_bits(inp[n][e]) for n in ("gate", "up", "down")), False
+
+
+def reference_outputs(cfg, inp, x_host, sets, w, tokens):
+    """Oracle outputs of `tokens`: the shared expert, then each routed expert the
+    tokens use, one expert's weights at a time, combined in fp64."""
+    sh = {n: bf16_tensor_bits(v) for n, v in inp["shared"].items()}
     ys = oracle.ffn(x_host[tokens], sh["gate"], sh["up"], sh["down"])
     yr = np.zeros((len(tokens), cfg.k, cfg.d))
     by_expert = {}
     for i, t in enumerate(tokens):
         for j, e in enumerate(sets[t]):
             by_expert.setdefault(int(e), []).append((i, j))
+    src = DeviceExperts(inp)
     for e, pairs in sorted(by_expert.items()):
-        if fp8:
-            f = hi.host_expert_fp8(cfg, e)
-            rows = [tokens[i] for i, _ in pairs]
-            y = oracle.ffn_w64(x_host[rows], oracle.fp8_decode(f["fgate"], f["fsgate"]),
-                               oracle.fp8_decode(f["fup"], f["fsup"]), oracle.fp8_decode(f["fdown"], f["fsdown"]))
-            for (i, j), yy in zip(pairs, y):
-                yr[i, j] = yy
-            continue
-        if ternary:
-            q = hi.host_expert_ternary(cfg, e)
-            gate = oracle.sherry_decode(q["qgate"], q["sgate"])[1]
-            up = oracle.sherry_decode(q["qup"], q["sup"])[1]
-            down = oracle.sherry_decode(q["qdown"], q["sdown"])[1]
-        else:
-            ex = hi.host_expert(cfg, e)
-            gate, up, down = ex["gate"], ex["up"], ex["down"]
-        rows = [tokens[i] for i, _ in pairs]
-        y = oracle.ffn(x_host[rows], gate, up, down)
+        (gate, up, down), w64 = src.get(e)
+        rows = x_host[[tokens[i] for i, _ in pairs]]
+        y = (oracle.ffn_w64 if w64 else oracle.ffn)(rows, gate, up, down)
         for (i, j), yy in zip(pairs, y):
             yr[i, j] = yy
     return oracle.combine(ys, yr, w[tokens])
 
 
-def run_full(cfg, inp, sample):
-    say(f"[case] {cfg.name} T={cfg.T} full-size, sampled tokens {sample}")
+def run_full(cfg, inp, sample="all"):
+    say(f"[case] {cfg.name} T={cfg.T} full-size")
     fmt = hm.WEIGHTS_SHERRY_TERNARY if cfg.ternary else hm.WEIGHTS_FP8_E4M3 if cfg.fp8 else hm.WEIGHTS_BF16
     ws = hm.alloc_workspace(cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, fmt, device=DEV)
     res = hm.forward_layer(inp, cfg.k, want_routing=True, workspace=ws)
@@ -88,19 +96,25 @@ def run_full(cfg, inp, sample):
     out = bf16_tensor_to_np(res["out"])
     assert np.isfinite(out).all()
     t0 = time.time()
-    x_host = hi.host_x(cfg)
-    lg = oracle.logits(x_host, hi.host_router(cfg), hi.host_bias(cfg))
+    x_host = bf16_tensor_bits(inp["x"])
+    bias = None if inp.get("bias") is None else inp["bias"].cpu().numpy()
+    lg = oracle.logits(x_host, bf16_tensor_bits(inp["router"]), bias)
     sets, near, subst = check_routing(g["topk_idx"], lg, cfg.k)
     check_permutation(g, sets, cfg.E)
     werr = check_weights(g["topk_w"], lg, sets)
     assert g["counts"].sum() == cfg.T * cfg.k
     say(f"       routing of all {cfg.T} tokens ok: near-ties={near} substituted={subst} "
         f"max |dw|={werr:.2e} touched experts={int((g['counts'] > 0).sum())} ({time.time() - t0:.1f}s)")
+    if sample == "all":
+        tokens, why = list(range(cfg.T)), {"every token": cfg.T}
+    else:
+        tokens, why = tile_sample(cfg, g)
+    say(f"       comparing {len(tokens)} tokens: {why}")
     w_ref = oracle.weights(lg, sets)
-    ref = sampled_reference(cfg, x_host, sets, w_ref, sample, ternary=cfg.ternary, fp8=cfg.fp8)
-    worst, mean = check_out(out[sample], ref)
-    say(f"       sampled outputs ok: max_rel_err={worst:.3e} mean_abs_err={mean:.3e} ({time.time() - t0:.1f}s)")
-    return res, g
+    ref = reference_outputs(cfg, inp, x_host, sets, w_ref, tokens)
+    worst, mean = check_out(out[tokens], ref)
+    say(f"       outputs ok: max_rel_err={worst:.3e} mean_abs_err={mean:.3e} ({time.time() - t0:.1f}s)")
+    return res, g, tokens
 
 
 def with_x(cfg, weights):
@@ -113,17 +127,17 @@ def with_x(cfg, weights):
 
 def test_decode_full_size(hy4_weights):
     cfg = hi.CONFIGS["decode"]
-    run_full(cfg, with_x(cfg, hy4_weights), sample=[0, 5, 17, 31])
+    run_full(cfg, with_x(cfg, hy4_weights))
 
 
 def test_prefill_full_size(hy4_weights):
     cfg = hi.CONFIGS["prefill"]
-    run_full(cfg, with_x(cfg, hy4_weights), sample=[0, 4095, 8191])
+    run_full(cfg, with_x(cfg, hy4_weights), sample="tiles")
 
 
 def test_skewed_full_size(hy4_weights):
     cfg = hi.CONFIGS["skewed"]
-    res, g = run_full(cfg, with_x(cfg, hy4_weights), sample=[0, 2047, 4095])
+    res, g, _ = run_full(cfg, with_x(cfg, hy4_weights), sample="tiles")
     counts = g["counts"]
     say(f"       skew: hottest expert {int(counts.max())} rows, empty experts {int((counts == 0).sum())}")
     assert (counts == 0).any(), "the Zipf bias should leave some experts empty"
@@ -143,13 +157,13 @@ def test_skewed_paths_agree(hy4_weights):
 def test_ternary_full_size():
     cfg = hi.CONFIGS["ternary"]
     inp = hi.dev_layer(cfg, device=DEV)
-    run_full(cfg, inp, sample=[0, 9, 31])
+    run_full(cfg, inp)
 
 
 def test_fp8_full_size():
     cfg = hi.CONFIGS["fp8"]
     inp = hi.dev_layer(cfg, device=DEV)
-    run_full(cfg, inp, sample=[0, 13, 31])
+    run_full(cfg, inp)
     del inp
     torch.cuda.empty_cache()
 
@@ -157,7 +171,7 @@ def test_fp8_full_size():
 def test_fp8_prefill_full_size():
     cfg = hi.CONFIGS["fp8_prefill"]
     inp = hi.dev_layer(cfg, device=DEV)
-    run_full(cfg, inp, sample=[0, 4095, 8191])
+    run_full(cfg, inp, sample="tiles")
     del inp
     torch.cuda.empty_cache()
 
@@ -165,6 +179,6 @@ def test_fp8_prefill_full_size():
 def test_ternary_prefill_full_size():
     cfg = hi.CONFIGS["ternary_prefill"]
     inp = hi.dev_layer(cfg, device=DEV)
-    run_full(cfg, inp, sample=[0, 4095, 8191])
+    run_full(cfg, inp, sample="tiles")
     del inp
     torch.cuda.empty_cache()

@@ -116,7 +116,7 @@ def test_indexer_device_keys_match_host_generator():
 
 def test_indexer_full_size():
     # 32 sequences x 64K keys, top-2048: every row's selection is checked against its own
-    # scores; three rows are checked against the oracle
+    # scores and against the oracle (keys copied from the generator's device tensor)
     cfg = hi.INDEXER_CONFIGS["indexer_decode"]
     say(f"[case] indexer full size B={cfg.B} S={cfg.S} K={cfg.K}")
     inp = hi.dev_indexer(cfg, device=DEV)
@@ -127,9 +127,12 @@ def test_indexer_full_size():
     own, _, _ = oracle.topk_indices(sc.astype(np.float64), cfg.K)
     assert np.array_equal(idx, own)
     q, w = hi.host_indexer_queries(cfg)
-    for b in (0, 17, 31):
-        e, near = check_row(idx[b], sc[b], q[b], w[b], hi.host_indexer_keys(cfg, b), cfg.K, cfg.D, cfg.H, f"b={b}")
-        say(f"       row {b}: max score error {e:.3e} near-tie={near}")
+    worst, nnear = 0.0, 0
+    for b in range(cfg.B):
+        e, near = check_row(idx[b], sc[b], q[b], w[b], bf16_tensor_bits(inp["keys"][b]), cfg.K, cfg.D, cfg.H,
+                            f"b={b}")
+        worst, nnear = max(worst, e), nnear + near
+    say(f"       all {cfg.B} rows ok: max score error {worst:.3e}, near-tie rows {nnear}")
     del inp
     torch.cuda.empty_cache()
 
