@@ -82,6 +82,8 @@ def routing_to_np(res):
 def m_tiles(n):
     """The grouped GEMM's M tiles of an expert with n rows: ceil(n/256) tiles of equal
     whole 32-row blocks, the last taking the rest. Returns [(first row, rows)]."""
+    if n <= 0:
+        return []
     nt = -(-n // TILE_ROWS)
     span = -(-(-(-n // BLOCK_ROWS)) // nt) * BLOCK_ROWS
     return [(i * span, min(span, n - i * span)) for i in range(nt)]
@@ -101,7 +103,7 @@ def tile_sample(cfg, g, extra=16, seed=0):
     T, k, E = cfg.T, cfg.k, cfg.E
     tiles = []  # (expert, first row within expert, rows) in the library's order
     for e in range(E):
-        for m0, rows in m_tiles(int(counts[e])) if counts[e] else []:
+        for m0, rows in m_tiles(int(counts[e])):
             tiles.append((e, m0, rows))
     for m0, rows in m_tiles(T):
         tiles.append((E, m0, rows))

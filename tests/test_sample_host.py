@@ -28,3 +28,4 @@ def test_m_tiles_match_library_rule():
     assert m_tiles(257) == [(0, 160), (160, 97)]
     assert m_tiles(4000) == [(i * 256, 256) for i in range(15)] + [(3840, 160)]
     assert m_tiles(1) == [(0, 1)]
+    assert m_tiles(0) == []
