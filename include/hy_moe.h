@@ -175,6 +175,26 @@ enum {
 /* hy_moe_forward_ex — the layer with every option. Returns a hy_moe_status. */
 int hy_moe_forward_ex(const hy_moe_args* args, void* stream);
 
+/*
+ * hy_moe_forward_noalloc — hy_moe_forward_ex for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. The same layer and the same kernels; the scratch memory is a buffer of
+ * HY_MOE_NOALLOC_SCRATCH_BYTES that the library keeps per device (a device global,
+ * present from the library's load on that device until the process ends). The call
+ * allocates nothing and frees nothing.
+ *   args  as for hy_moe_forward_ex, with workspace NULL and workspace_bytes 0
+ *         (HY_MOE_ERR_INVALID_ARG otherwise).
+ * Shapes whose hy_moe_workspace_size() exceeds HY_MOE_NOALLOC_SCRATCH_BYTES are
+ * rejected with HY_MOE_ERR_WORKSPACE before anything is enqueued; at the Hy4 preview
+ * layer shape (d = 6144, E = 256, k = 8, I = 2048) that admits T <= 251. All calls on
+ * one device share that device's buffer and it keeps the last call's contents: calls
+ * that overlap in time on one device (other streams, other threads) race and their
+ * results are undefined, so serialize them. Nothing in the buffer needs to start at
+ * zero: each call writes everything it reads before reading it.
+ */
+#define HY_MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int hy_moe_forward_noalloc(const hy_moe_args* args, void* stream);
+
 /* Bytes of DEVICE workspace hy_moe_forward_ex needs for this shape (for the
  * largest of the paths it may pick); 0 for invalid shapes. Alignment: 256 B. */
 size_t hy_moe_workspace_size(int64_t T, int64_t d, int64_t E, int64_t k, int64_t I, int expert_format);

@@ -17,8 +17,8 @@ import os
 # library binds to that same runtime instead of loading a second copy.
 import torch  # noqa: F401
 
-__all__ = ["forward", "forward_ex", "forward_layer", "workspace_size", "status_string", "sherry_pack_host",
-           "HyMoeError", "lib", "LIB_PATH"]
+__all__ = ["forward", "forward_ex", "forward_noalloc", "forward_layer", "workspace_size", "status_string",
+           "sherry_pack_host", "HyMoeError", "lib", "LIB_PATH"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhy_moe.so")
@@ -30,10 +30,11 @@ KERNELS = ["route_logits", "route_topk", "permute_scan", "permute_scatter", "exp
            "combine"]
 NUM_STAGE_EVENTS = len(KERNELS) + 1
 
-EXPORTED = ["hy_moe_forward", "hy_moe_forward_ex", "hy_moe_workspace_size", "hy_moe_status_string",
-            "hy_moe_sherry_pack_host", "hy_moe_probe_mfma_bf16", "hy_moe_probe_hbm_read",
+EXPORTED = ["hy_moe_forward", "hy_moe_forward_ex", "hy_moe_forward_noalloc", "hy_moe_workspace_size",
+            "hy_moe_status_string", "hy_moe_sherry_pack_host", "hy_moe_probe_mfma_bf16", "hy_moe_probe_hbm_read",
             "hy_indexer_workspace_size", "hy_indexer_topk"]
 PROBE_OPERAND_BYTES = 65536
+NOALLOC_SCRATCH_BYTES = 64 << 20  # HY_MOE_NOALLOC_SCRATCH_BYTES
 
 
 class HyMoeArgs(ctypes.Structure):
@@ -71,6 +72,8 @@ def _load():
     L.hy_moe_forward.restype = ctypes.c_int
     L.hy_moe_forward_ex.argtypes = [ctypes.POINTER(HyMoeArgs), vp]
     L.hy_moe_forward_ex.restype = ctypes.c_int
+    L.hy_moe_forward_noalloc.argtypes = [ctypes.POINTER(HyMoeArgs), vp]
+    L.hy_moe_forward_noalloc.restype = ctypes.c_int
     L.hy_moe_workspace_size.argtypes = [i64] * 5 + [ctypes.c_int]
     L.hy_moe_workspace_size.restype = ctypes.c_size_t
     L.hy_moe_status_string.argtypes = [ctypes.c_int]
@@ -132,14 +135,20 @@ def forward_ex(args: HyMoeArgs, stream=None) -> int:
     return _lib.hy_moe_forward_ex(ctypes.byref(args), _stream(stream))
 
 
+def forward_noalloc(args: HyMoeArgs, stream=None) -> int:
+    """hy_moe_forward_noalloc (scratch from the library's static per-device buffer);
+    returns the status code unchanged."""
+    return _lib.hy_moe_forward_noalloc(ctypes.byref(args), _stream(stream))
+
+
 def forward_layer(inp: dict, k: int, *, want_routing=False, path=PATH_AUTO, workspace=None, out=None,
-                  stream=None, stage_events=None):
+                  stream=None, stage_events=None, noalloc=False):
     """Runs hy_moe_forward_ex on a dict of device tensors as made by
     hy_inputs.dev_layer(): x, router, bias, shared{gate,up,down} and either
     gate/up/down (bf16), qgate/qup/qdown + sgate/sup/sdown (ternary) or
     fgate/fup/fdown + fsgate/fsup/fsdown (FP8 E4M3 codes and fp32 scales).
     Returns dict(out, and with want_routing: topk_idx, topk_w, counts, offsets,
-    perm_src, margin)."""
+    perm_src, margin). noalloc: call hy_moe_forward_noalloc (no workspace)."""
     import torch
     x = inp["x"]
     T, d = x.shape
@@ -188,6 +197,13 @@ def forward_layer(inp: dict, k: int, *, want_routing=False, path=PATH_AUTO, work
     a.path = path
     if stage_events is not None:
         a.stage_events = ctypes.cast(stage_events, ctypes.c_void_p)
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("forward_layer: noalloc takes no workspace")
+        rc = forward_noalloc(a, stream)
+        if rc != OK:
+            raise HyMoeError(rc, "hy_moe_forward_noalloc")
+        return res
     rc = forward_ex(a, stream)
     if rc != OK:
         raise HyMoeError(rc, "hy_moe_forward_ex")

@@ -3,6 +3,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "hy_moe.h"
 #include "common.h"
 #include "kernels.h"
@@ -193,6 +195,55 @@ extern "C" int hy_moe_forward_ex(const hy_moe_args* a, void* stream) {
     if (hipFreeAsync(ws, s) != hipSuccess && err == hipSuccess) err = hipErrorUnknown;
   }
   return err == hipSuccess ? HY_MOE_OK : HY_MOE_ERR_HIP;
+}
+
+// Scratch of hy_moe_forward_noalloc: a device global, one copy per device, resolved to
+// its device address once per device. In host code `scratch` names a host-side stand-in,
+// never the device memory: only the address from hipGetSymbolAddress is used.
+static_assert(HY_MOE_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) uint8_t scratch[HY_MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_dev[kMaxDevices];  // device address of `scratch` per device, NULL until resolved
+std::mutex g_scratch_mu;
+
+// The current device's copy of `scratch`, resolved on the first call on that device.
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return HY_MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return HY_MOE_ERR_UNSUPPORTED;
+  void* p = __atomic_load_n(&g_scratch_dev[dev], __ATOMIC_ACQUIRE);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_dev[dev];
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return HY_MOE_ERR_HIP;
+      __atomic_store_n(&g_scratch_dev[dev], p, __ATOMIC_RELEASE);
+    }
+  }
+  *out = p;
+  return HY_MOE_OK;
+}
+
+}  // namespace
+
+extern "C" int hy_moe_forward_noalloc(const hy_moe_args* a, void* stream) {
+  if (!a) return HY_MOE_ERR_INVALID_ARG;
+  if (a->workspace || a->workspace_bytes) return HY_MOE_ERR_INVALID_ARG;
+  int rc = check_args(a);
+  if (rc != HY_MOE_OK) return rc;
+  if (a->T == 0) return HY_MOE_OK;
+  if (make_layout(a->T, a->d, a->E, a->k, a->I).total > (size_t)HY_MOE_NOALLOC_SCRATCH_BYTES)
+    return HY_MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  rc = scratch_of_current_device(&ws);
+  if (rc != HY_MOE_OK) return rc;
+  hy_moe_args b = *a;
+  b.workspace = ws;
+  b.workspace_bytes = HY_MOE_NOALLOC_SCRATCH_BYTES;
+  return hy_moe_forward_ex(&b, stream);
 }
 
 extern "C" int hy_moe_forward(const void* x, const void* W_router, const void* W_gate, const void* W_up,

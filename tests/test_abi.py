@@ -213,3 +213,41 @@ def test_indexer_argument_checks():
     assert ix(B=0, q=None, keys=None) == hm.OK              # empty: no pointer is touched
     assert ix(S=0, q=None, keys=None) == hm.OK
     assert L.hy_indexer_workspace_size(4, 1000) >= 4 * 1000 * 4
+
+
+def call_noalloc(a):
+    return hm.lib().hy_moe_forward_noalloc(ctypes.byref(a), None)
+
+
+def test_noalloc_argument_checks_run_before_any_hip_call():
+    # every rejection below happens on the host, before the static scratch is resolved
+    a = base_args()
+    a.workspace, a.workspace_bytes = FAKE, hm.workspace_size(4, 256, 16, 2, 128)
+    assert call_noalloc(a) == hm.ERR_INVALID_ARG           # no workspace may be passed
+    a = base_args()
+    a.workspace_bytes = 1
+    assert call_noalloc(a) == hm.ERR_INVALID_ARG
+    a = base_args()
+    a.k = 0
+    assert call_noalloc(a) == hm.ERR_INVALID_ARG
+    a = base_args()
+    a.x = None
+    assert call_noalloc(a) == hm.ERR_INVALID_ARG
+    assert hm.lib().hy_moe_forward_noalloc(None, None) == hm.ERR_INVALID_ARG
+    a = base_args(T=0)
+    assert call_noalloc(a) == hm.OK                        # empty batch: a no-op
+    a = base_args(T=252, d=6144, E=256, k=8, I=2048)        # needs more than the static scratch
+    assert hm.workspace_size(252, 6144, 256, 8, 2048) > hm.NOALLOC_SCRATCH_BYTES
+    assert call_noalloc(a) == hm.ERR_WORKSPACE
+
+
+def test_noalloc_limit_stated_in_header():
+    # the header states the largest Hy4-shape batch the static scratch admits
+    text = open(HEADER).read()
+    assert "#define HY_MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in text
+    assert hm.NOALLOC_SCRATCH_BYTES == 64 << 20
+    limit = int(re.search(r"that admits T <= (\d+)", text).group(1))
+    for fmt in (hm.WEIGHTS_BF16, hm.WEIGHTS_SHERRY_TERNARY, hm.WEIGHTS_FP8_E4M3):
+        assert hm.workspace_size(limit, 6144, 256, 8, 2048, fmt) <= hm.NOALLOC_SCRATCH_BYTES
+        assert hm.workspace_size(limit + 1, 6144, 256, 8, 2048, fmt) > hm.NOALLOC_SCRATCH_BYTES
+
