@@ -3,14 +3,19 @@
 A step is one full layer forward (router -> top-k -> dispatch -> experts +
 shared expert -> combine) over one batch of seeded synthetic inputs already
 resident in HBM, through the C ABI (hy_moe_forward_ex, automatic path choice,
-caller workspace). Default workload: the Hy4-shape decode layer (T=32 tokens,
-d=6144, 256 routed experts top-8 + 1 shared, I=2048, bf16), which is bound by
-streaming every touched expert's weights from HBM. The same run also measures
-the prefill layer (T=8192), bound by bf16 MFMA, because the headline metric
-names both.
+caller workspace). The headline workload is the Hy4-shape decode layer (T=32
+tokens, d=6144, 256 routed experts top-8 + 1 shared, I=2048, bf16), bound by
+streaming every touched expert's weights from HBM. The default run also times
+the layer's other workloads, each as an object of the same JSON line: the tiny
+layer, the prefill layer (T=8192, bound by bf16 MFMA), the skewed-routing
+prefill (T=4096, Zipf router bias) and the Sherry-ternary decode layer.
 
-Prints one JSON line. Per-kernel durations come from HIP events the library
-records on its stream around each kernel (stage_events), over the timed steps.
+Per workload: W untimed warm-up steps, then K timed steps; ms_per_step is the
+host clock around the K steps (synchronised on both sides); the per-step median
+and p10/p90 come from HIP events recorded on the library's stream at each
+step's first and last kernel; the dominant kernel's time from events around it
+in the same steps. Before the first workload the machine-peak probes run, which
+also brings the shader clock up from idle. Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -95,13 +100,28 @@ def traffic_for(kernel_key, units):
 WARMUP_MIN_S = 0.5  # default warm-up length: the shader clock climbs for ~60 ms of load after idle
 
 
-def time_layer(hm, torch, inp, k, ws, steps, warmup, dominant):
+def _pct(vals, q):
+    v = sorted(vals)
+    if not v:
+        return None
+    pos = (len(v) - 1) * q
+    lo, hi = int(math.floor(pos)), int(math.ceil(pos))
+    return v[lo] + (v[hi] - v[lo]) * (pos - lo)
+
+
+def step_stats(vals):
+    return {"median": _pct(vals, 0.5), "p10": _pct(vals, 0.1), "p90": _pct(vals, 0.9), "n": len(vals)}
+
+
+def time_layer(hm, torch, inp, k, ws, steps, warmup, dominant, flush=None):
     """Times `steps` forwards after `warmup` untimed ones (None: at least 5 steps and
-    WARMUP_MIN_S seconds of them). Returns (total ms by the host clock around the syncs,
-    mean ms of kernel `dominant` from events recorded around it in those same steps,
-    mean ms per kernel from a separate pass of stage events after the timed region,
-    warm-up steps run). Only the dominant kernel's two events are recorded while timing:
-    an event between every kernel would add its own gaps to the step."""
+    WARMUP_MIN_S seconds of them). Returns dict(total_ms by the host clock around the
+    synchronised steps, step_ms (per step, from events at the first and last kernel of
+    the step), dom_ms (per step, events around kernel `dominant`), kernels (mean ms per
+    kernel from a separate pass of stage events after the timed region), warmup (steps
+    run), cold_ms (per step with `flush` run between steps outside the events, or None)).
+    Only the step's two ends and the dominant kernel's two ends are recorded while
+    timing: an event between every kernel would add its own gaps to the step."""
     nk = len(hm.KERNELS)
     done = 0
     t_w = time.perf_counter()
@@ -116,19 +136,34 @@ def time_layer(hm, torch, inp, k, ws, steps, warmup, dominant):
             done += 5
             torch.cuda.synchronize()
     torch.cuda.synchronize()
-    ev = Events(2 * steps)
+    ev = Events(4 * steps)
     arrays = []
     for i in range(steps):
         arr = (ctypes.c_void_p * (nk + 1))()
-        arr[dominant] = ev.handles[2 * i]
-        arr[dominant + 1] = ev.handles[2 * i + 1]
+        arr[0] = ev.handles[4 * i]
+        arr[nk] = ev.handles[4 * i + 1]
+        arr[dominant] = ev.handles[4 * i + 2] if dominant > 0 else arr[0]
+        arr[dominant + 1] = ev.handles[4 * i + 3] if dominant + 1 < nk else arr[nk]
         arrays.append(arr)
     t0 = time.perf_counter()
     for i in range(steps):
         hm.forward_layer(inp, k, workspace=ws, stage_events=arrays[i])
     torch.cuda.synchronize()
     total_ms = (time.perf_counter() - t0) * 1e3
-    dom_ms = sum(ev.ms(2 * i, 2 * i + 1) for i in range(steps)) / steps
+    step_ms = [ev.ms(4 * i, 4 * i + 1) for i in range(steps)]
+    da = (lambda i: 4 * i + 2) if dominant > 0 else (lambda i: 4 * i)
+    db = (lambda i: 4 * i + 3) if dominant + 1 < nk else (lambda i: 4 * i + 1)
+    dom_ms = [ev.ms(da(i), db(i)) for i in range(steps)]
+    cold = None
+    if flush is not None:
+        # the same steps with a cache-flushing write between them (outside the events)
+        cold = []
+        for i in range(steps):
+            flush()
+            hm.forward_layer(inp, k, workspace=ws, stage_events=arrays[i])
+        torch.cuda.synchronize()
+        cold = [ev.ms(4 * i, 4 * i + 1) for i in range(steps)]
+        cold_dom = [ev.ms(da(i), db(i)) for i in range(steps)]
     ev.close()
     # per-kernel breakdown (untimed)
     nb = min(steps, 20)
@@ -141,7 +176,8 @@ def time_layer(hm, torch, inp, k, ws, steps, warmup, dominant):
         for j in range(nk):
             per[j] += ev.ms(i * (nk + 1) + j, i * (nk + 1) + j + 1) / nb
     ev.close()
-    return total_ms, dom_ms, dict(zip(hm.KERNELS, per)), done
+    return {"total_ms": total_ms, "step_ms": step_ms, "dom_ms": dom_ms, "kernels": dict(zip(hm.KERNELS, per)),
+            "warmup": done, "cold_ms": cold, "cold_dom_ms": cold_dom if cold is not None else None}
 
 
 def stream_work(cfg, touched):
@@ -190,7 +226,19 @@ def gemm_work(cfg):
             "per_unit": f"{4 * d * I} flop per dispatched row (gate and up: 2*d*I each)", "kernel": kernel}
 
 
-def run_config(name, args, hi, hm, torch, weights=None):
+def input_digest(inp, torch):
+    """sha256 (first 16 hex digits) of the step's inputs that are not regenerated by
+    stream id alone: x, the router weights and the bias, plus the first routed expert's
+    and the shared expert's weights as a check of the generator."""
+    h = hashlib.sha256()
+    keys = [k for k in ("x", "router", "bias") if inp.get(k) is not None]
+    first = [k for k in ("gate", "qgate", "fgate") if k in inp][0]
+    for t in [inp[k] for k in keys] + [inp[first][0]] + [inp["shared"][k] for k in ("gate", "up", "down")]:
+        h.update(t.detach().contiguous().view(torch.uint8).cpu().numpy().tobytes())
+    return h.hexdigest()[:16]
+
+
+def run_config(name, args, hi, hm, torch, weights=None, steps=None, flush=None):
     cfg = hi.CONFIGS[name]
     dev = "cuda:0"
     if weights is None:
@@ -203,36 +251,72 @@ def run_config(name, args, hi, hm, torch, weights=None):
         inp["bias"] = None if b is None else torch.from_numpy(b).to(dev)
     fmt = hm.WEIGHTS_SHERRY_TERNARY if cfg.ternary else hm.WEIGHTS_FP8_E4M3 if cfg.fp8 else hm.WEIGHTS_BF16
     ws = hm.alloc_workspace(cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, fmt, device=dev)
-    steps = args.steps
+    steps = args.steps if steps is None else steps
     dominant = hm.KERNELS.index("expert_gateup")
-    total_ms, dom_ms, kern, warmup_done = time_layer(hm, torch, inp, cfg.k, ws, steps, args.warmup, dominant)
-    ms = total_ms / steps
+    r = time_layer(hm, torch, inp, cfg.k, ws, steps, args.warmup, dominant, flush=flush)
+    ms = r["total_ms"] / steps
+    dom_ms = sum(r["dom_ms"]) / steps
     routing = hm.forward_layer(inp, cfg.k, want_routing=True, workspace=ws)
     torch.cuda.synchronize()
     counts = routing["counts"].cpu()
     touched = int((counts > 0).sum())
+    near = int((routing["margin"] <= 1e-4).sum().item())
     stream_path = cfg.T * cfg.k <= 16 * cfg.E  # the library's automatic path choice
     kernel_file = "sparse_moe_transformer_route_amd/csrc/" + ("moe_stream.hip" if stream_path else "moe_gemm.hip")
+    # algorithmic bytes and flops of the whole layer (both reported for every workload)
+    lw = stream_work(cfg, touched)
+    gw = gemm_work(cfg)
+    layer = {"bytes": lw["layer_bytes"], "flop": gw["layer_flop"],
+             "hbm_frac": lw["layer_bytes"] / (ms * 1e-3) / PEAK_HBM,
+             "mfma_frac": gw["layer_flop"] / (ms * 1e-3) / PEAK_BF16}
+    sec = dom_ms * 1e-3
     if stream_path:
-        w = stream_work(cfg, touched)
-        sec = dom_ms * 1e-3
-        alg = w["alg"]
+        alg = lw["alg"]
         roof = {"bound": "hbm", "achieved": alg / sec / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                "frac": alg / sec / PEAK_HBM, "traffic": traffic_for(f"{w['key']}/{name}", touched + 1),
-                "kernel": w["kernel"], "per_unit": w["per_unit"], "units_per_launch": touched + 1, "kernel_ms": dom_ms}
-        layer = {"bytes": w["layer_bytes"], "hbm_frac": w["layer_bytes"] / (ms * 1e-3) / PEAK_HBM}
+                "frac": alg / sec / PEAK_HBM, "traffic": traffic_for(f"{lw['key']}/{name}", touched + 1),
+                "kernel": lw["kernel"], "per_unit": lw["per_unit"], "units_per_launch": touched + 1,
+                "kernel_ms": dom_ms}
     else:
-        w = gemm_work(cfg)
-        rows, alg = w["rows"], w["alg"]
-        sec = dom_ms * 1e-3
+        rows, alg = gw["rows"], gw["alg"]
         roof = {"bound": "mfma", "achieved": alg / sec / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
                 "frac": alg / sec / PEAK_BF16, "traffic": traffic_for(f"grouped_gemm_gateup/{name}", rows),
-                "kernel": w["kernel"], "per_unit": w["per_unit"], "units_per_launch": rows, "kernel_ms": dom_ms}
-        layer = {"flop": w["layer_flop"], "mfma_frac": w["layer_flop"] / (ms * 1e-3) / PEAK_BF16}
+                "kernel": gw["kernel"], "per_unit": gw["per_unit"], "units_per_launch": rows, "kernel_ms": dom_ms}
     roof["kernel_source_sha256_16"] = source_digest(os.path.join(ROOT, kernel_file))
-    return {"cfg": cfg, "inp": inp, "ms": ms, "tokens_per_s": cfg.T / (ms * 1e-3), "kernels_ms": kern,
-            "roofline": roof, "layer": layer, "touched": touched, "counts": counts, "routing": routing,
-            "warmup": warmup_done}
+    res = {"cfg": cfg, "inp": inp, "ms": ms, "tokens_per_s": cfg.T / (ms * 1e-3), "kernels_ms": r["kernels"],
+           "roofline": roof, "layer": layer, "touched": touched, "counts": counts, "routing": routing,
+           "warmup": r["warmup"], "steps": steps, "step_ms": step_stats(r["step_ms"]),
+           "kernel_step_ms": step_stats(r["dom_ms"]), "near_ties": near, "input_sha256_16": input_digest(inp, torch)}
+    if r["cold_ms"] is not None:
+        cold = step_stats(r["cold_ms"])
+        cold_dom = sum(r["cold_dom_ms"]) / steps * 1e-3
+        res["cold"] = {"step_ms": cold, "tokens_per_s_at_median": cfg.T / (cold["median"] * 1e-3),
+                       "layer_hbm_frac_at_median": lw["layer_bytes"] / (cold["median"] * 1e-3) / PEAK_HBM,
+                       "kernel_ms": cold_dom * 1e3,
+                       "kernel_frac": (lw["alg"] if stream_path else gw["alg"]) / cold_dom /
+                       (PEAK_HBM if stream_path else PEAK_BF16),
+                       "how": "a 512 MiB write between steps (outside the events) evicts the 256 MB last-level cache"}
+    return res
+
+
+def workload_object(res, extra=None):
+    """The JSON object of one workload (the headline one is the top level)."""
+    c = res["cfg"]
+    o = {"workload": workload_name(c), "T": c.T, "ms_per_step": res["ms"], "steps": res["steps"],
+         "warmup": res["warmup"], "step_ms": res["step_ms"], "tokens_per_s": res["tokens_per_s"],
+         "roofline": res["roofline"], "layer": res["layer"], "kernels_ms": res["kernels_ms"],
+         "touched_experts": res["touched"], "near_tie_tokens": res["near_ties"],
+         "input_sha256_16": res["input_sha256_16"]}
+    if "cold" in res:
+        o["cold"] = res["cold"]
+    if extra:
+        o.update(extra)
+    return o
+
+
+def workload_name(c):
+    return (f"{c.name} MoE FFN layer T={c.T} d={c.d} E={c.E} top-{c.k} + 1 shared I={c.I}"
+            + (" Sherry-ternary routed experts" if c.ternary else " FP8-E4M3 routed experts" if c.fp8 else " bf16")
+            + (" Zipf(1.2) router bias" if c.zipf_s else ""))
 
 
 def cpu_baseline(cfg, hi, torch, inp, routing, budget_s):
@@ -302,7 +386,42 @@ def cpu_baseline(cfg, hi, torch, inp, routing, budget_s):
         done, what = passes * cfg.T, f"{passes} passes over all {cfg.T} tokens of the same batch"
     return {"value": done / el, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
             "sample": f"{what} (full fp64 layer per token: router over {cfg.E} experts, top-{cfg.k}, "
-                      f"{cfg.k} routed + 1 shared SwiGLU experts, combine); {el:.1f} s on {nthreads} threads"}
+                      f"{cfg.k} routed + 1 shared SwiGLU experts, combine); {el:.1f} s on {nthreads} threads",
+            "host": host_info(), "tiny_1thread": tiny_one_thread(hi)}
+
+
+def host_info():
+    """CPU model and core counts of this host."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = None
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable}
+
+
+def tiny_one_thread(hi, budget_s=1.0):
+    """The oracle's whole tiny layer (T=64, d=256, E=16, top-2, I=128) on one thread,
+    repeated for about budget_s; host-generated inputs, generation not timed."""
+    import oracle
+    cfg = hi.CONFIGS["tiny"]
+    L = hi.host_layer(cfg)
+    el, passes = 0.0, 0
+    while passes == 0 or el < budget_s:
+        t0 = time.perf_counter()
+        oracle.forward(L["x"], L["router"], L["bias"], L["gate"], L["up"], L["down"], L["shared"]["gate"],
+                       L["shared"]["up"], L["shared"]["down"], cfg.k, nthreads=1)
+        el += time.perf_counter() - t0
+        passes += 1
+    return {"value": passes * cfg.T / el, "unit": "tokens/s", "cores": 1,
+            "sample": f"{passes} passes of the whole tiny layer (T={cfg.T}), {el:.2f} s"}
 
 
 def run_indexer(args, hi, hm, torch):
@@ -378,6 +497,29 @@ def run_indexer(args, hi, hm, torch):
     print(json.dumps(line), flush=True)
 
 
+def library_gemm_reference(torch, seconds=0.5):
+    """torch.matmul (hipBLASLt) on one dense bf16 GEMM of the prefill gate/up shape
+    (73728 x 6144 @ 6144 x 4096, N(0,1)-like operands): what AMD's GEMM library reaches on
+    this part for the same arithmetic without routing, gathering or ragged experts."""
+    g = torch.Generator(device="cuda:0").manual_seed(1)
+    a = torch.randn(73728, 6144, generator=g, device="cuda:0").to(torch.bfloat16)
+    b = (torch.randn(6144, 4096, generator=g, device="cuda:0") / 78.0).to(torch.bfloat16).contiguous()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        torch.matmul(a, b)
+        torch.cuda.synchronize()
+    n = 10
+    t0 = time.perf_counter()
+    for _ in range(n):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / n
+    del a, b
+    torch.cuda.empty_cache()
+    return {"tflops": 2 * 73728 * 6144 * 4096 / dt / 1e12, "ms": dt * 1e3,
+            "how": "torch.matmul bf16 [73728 x 6144] @ [6144 x 4096] (hipBLASLt), mean of 10 after 0.5 s warm"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -387,8 +529,9 @@ def main():
     ap.add_argument("--config", default="decode", choices=["tiny", "decode", "prefill", "skewed", "ternary",
                                                                  "ternary_prefill", "fp8", "fp8_prefill",
                                                                  "indexer_tiny", "indexer_decode"])
+    ap.add_argument("--only", action="store_true",
+                    help="time --config alone (no other workloads, probes or oracle): for profiler runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-prefill", action="store_true", help="skip the T=8192 measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
                     help="only run 3 device-to-device copies of this many GiB (counter calibration) and exit")
@@ -417,68 +560,105 @@ def main():
         run_indexer(args, hi, hm, torch)
         return
     cfg = hi.CONFIGS[args.config]
+    full = args.config == "decode" and not args.only
+    bf16_hy4 = not cfg.ternary and not cfg.fp8 and cfg.d == 6144
     shared_weights = None
-    if not cfg.ternary and not cfg.fp8 and cfg.d == 6144:
+    if bf16_hy4 or full:
         log("[bench] generating the Hy4-shape bf16 layer (19.3 GB of expert weights) on the GPU")
         shared_weights = hi.dev_layer(hi.CONFIGS["prefill"], device="cuda:0")
         torch.cuda.synchronize()
-    main_res = run_config(args.config, args, hi, hm, torch, shared_weights)
-    log(f"[bench] {args.config}: {main_res['ms']:.3f} ms/step, {main_res['tokens_per_s']:.1f} tokens/s, "
-        f"kernels {json.dumps({k: round(v, 4) for k, v in main_res['kernels_ms'].items()})}")
+
+    # measured peaks next to the published ones (these also bring the shader clock up
+    # from idle before the first timed workload): bf16 MFMA on random operand bits (the
+    # power-capped clock depends on operand activity), one streaming read of HBM, and
+    # hipBLASLt's dense GEMM of the prefill gate/up shape
+    peaks = None
+    if not args.only:
+        gen = torch.Generator(device="cuda:0").manual_seed(0)
+        ops = torch.randn(hm.PROBE_OPERAND_BYTES // 2, generator=gen, device="cuda:0").to(torch.bfloat16)
+        read_buf = shared_weights["gate"] if shared_weights is not None else torch.empty(
+            4 << 30, dtype=torch.uint8, device="cuda:0")
+        peaks = {"mfma_bf16_tflops": hm.probe_mfma_bf16(ops), "hbm_read_gbs": hm.probe_hbm_read(read_buf),
+                 "hbm_read_bytes": read_buf.numel() * read_buf.element_size(),
+                 "how": "hy_moe_probe_mfma_bf16 (32x32x16 bf16 MFMAs, 4 workgroups per CU, random N(0,1) operands, "
+                        "~40 ms) and hy_moe_probe_hbm_read (best of three timed streaming passes of 16-byte loads "
+                        "after an untimed one)"}
+        del read_buf
+        if full:
+            peaks["library_gemm_bf16"] = library_gemm_reference(torch)
+        log(f"[bench] measured peaks: {peaks['mfma_bf16_tflops']:.0f} TFLOP/s bf16 MFMA, "
+            f"{peaks['hbm_read_gbs']:.0f} GB/s HBM read"
+            + (f", hipBLASLt dense GEMM {peaks['library_gemm_bf16']['tflops']:.0f} TFLOP/s" if full else ""))
+        # back to load right away: the clock drops when the GPU idles
+        hm.probe_mfma_bf16(ops)
+
+    def report(res):
+        log(f"[bench] {res['cfg'].name}: {res['ms']:.3f} ms/step (median {res['step_ms']['median']:.3f}, "
+            f"p10 {res['step_ms']['p10']:.3f}, p90 {res['step_ms']['p90']:.3f}), {res['tokens_per_s']:.1f} tokens/s, "
+            f"kernels {json.dumps({k: round(v, 4) for k, v in res['kernels_ms'].items()})}")
 
     extra = {}
-    if args.config == "decode" and not args.no_prefill:
-        pre_args = argparse.Namespace(**vars(args))
-        pre_args.steps = min(args.steps, 10)
-        pre = run_config("prefill", pre_args, hi, hm, torch, shared_weights)
-        log(f"[bench] prefill: {pre['ms']:.3f} ms/step, {pre['tokens_per_s']:.0f} tokens/s")
-        extra["prefill"] = {"workload": "prefill T=8192 d=6144 E=256 k=8 I=2048 bf16", "ms_per_step": pre["ms"],
-                            "steps": pre_args.steps, "warmup": pre["warmup"],
-                            "tokens_per_s": pre["tokens_per_s"], "layer_mfma_frac": pre["layer"]["mfma_frac"],
-                            "roofline": pre["roofline"], "kernels_ms": pre["kernels_ms"]}
+    if full:
+        t = run_config("tiny", args, hi, hm, torch)
+        report(t)
+        extra["tiny"] = workload_object(t, {"us_per_step": t["ms"] * 1e3})
+        del t
+    main_res = run_config(args.config, args, hi, hm, torch, shared_weights)
+    report(main_res)
+    if full:
+        pre = run_config("prefill", args, hi, hm, torch, shared_weights)
+        report(pre)
+        extra["prefill"] = workload_object(pre)
         del pre
+        sk = run_config("skewed", args, hi, hm, torch, shared_weights)
+        report(sk)
+        cnt = sk["counts"]
+        extra["skewed"] = workload_object(sk, {"hottest_expert_rows": int(cnt.max()),
+                                               "empty_experts": int((cnt == 0).sum())})
+        del sk
+        torch.cuda.empty_cache()
+        flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+        n_flush = [0]
+
+        def flush():
+            n_flush[0] += 1
+            flush_buf.fill_(n_flush[0] & 0xFF)
+        tn = run_config("ternary", args, hi, hm, torch, flush=flush)
+        report(tn)
+        extra["ternary"] = workload_object(tn)
+        del tn, flush_buf
         torch.cuda.empty_cache()
 
-    # measured peaks next to the published ones: bf16 MFMA on random operand bits (the
-    # power-capped clock depends on operand activity) and one streaming read of HBM
-    gen = torch.Generator(device="cuda:0").manual_seed(0)
-    ops = torch.randn(hm.PROBE_OPERAND_BYTES // 2, generator=gen, device="cuda:0").to(torch.bfloat16)
-    read_buf = shared_weights["gate"] if shared_weights is not None else torch.empty(4 << 30, dtype=torch.uint8,
-                                                                                     device="cuda:0")
-    peaks = {"mfma_bf16_tflops": hm.probe_mfma_bf16(ops), "hbm_read_gbs": hm.probe_hbm_read(read_buf),
-             "hbm_read_bytes": read_buf.numel() * read_buf.element_size(),
-             "how": "hy_moe_probe_mfma_bf16 (32x32x16 bf16 MFMAs, 4 workgroups per CU, random N(0,1) operands, "
-                    "~40 ms) and hy_moe_probe_hbm_read (best of three timed streaming passes of 16-byte loads after "
-                    "an untimed one)"}
-    del read_buf
-    log(f"[bench] measured peaks: {peaks['mfma_bf16_tflops']:.0f} TFLOP/s bf16 MFMA, "
-        f"{peaks['hbm_read_gbs']:.0f} GB/s HBM read")
     roof = main_res["roofline"]
-    meas = peaks["hbm_read_gbs"] if roof["unit"] == "GB/s" else peaks["mfma_bf16_tflops"]
-    roof["frac_of_measured_peak"] = roof["achieved"] / meas
-    if "prefill" in extra:
-        extra["prefill"]["roofline"]["frac_of_measured_peak"] = (extra["prefill"]["roofline"]["achieved"]
-                                                                 / peaks["mfma_bf16_tflops"])
+    if peaks is not None:
+        meas = peaks["hbm_read_gbs"] if roof["unit"] == "GB/s" else peaks["mfma_bf16_tflops"]
+        roof["frac_of_measured_peak"] = roof["achieved"] / meas
+        for o in extra.values():
+            r = o["roofline"]
+            r["frac_of_measured_peak"] = r["achieved"] / (peaks["hbm_read_gbs"] if r["unit"] == "GB/s"
+                                                          else peaks["mfma_bf16_tflops"])
+            if r["unit"] == "TFLOP/s" and "library_gemm_bf16" in peaks:
+                r["frac_of_library_dense_gemm"] = r["achieved"] / peaks["library_gemm_bf16"]["tflops"]
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.only:
         log("[bench] timing the oracle on the host")
         cpu = cpu_baseline(cfg, hi, torch, main_res["inp"], main_res["routing"], args.cpu_seconds)
 
     c = main_res["cfg"]
     line = {
         "metric": METRIC, "value": main_res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": main_res["warmup"], "ms_per_step": main_res["ms"], "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None,
+        "steps": main_res["steps"], "warmup": main_res["warmup"], "ms_per_step": main_res["ms"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "sherry-ternary+bf16" if c.ternary else "fp8-e4m3+bf16" if c.fp8 else "bf16", "data": "synthetic",
-        "config": {"workload": f"{c.name} MoE FFN layer T={c.T} d={c.d} E={c.E} top-{c.k} + 1 shared I={c.I}"
-                               + (" Sherry-ternary routed experts" if c.ternary else " bf16")
-                               + (" Zipf(1.2) router bias" if c.zipf_s else ""),
-                   "T": c.T, "d": c.d, "E": c.E, "k": c.k, "I": c.I, "seed": c.seed,
+        "config": {"workload": workload_name(c), "T": c.T, "d": c.d, "E": c.E, "k": c.k, "I": c.I, "seed": c.seed,
                    "touched_experts": main_res["touched"]},
+        "step_ms": main_res["step_ms"],
         "roofline": main_res["roofline"],
         "layer": main_res["layer"],
         "kernels_ms": main_res["kernels_ms"],
+        "near_tie_tokens": main_res["near_ties"],
+        "input_sha256_16": main_res["input_sha256_16"],
         "measured_peak": peaks,
         "cpu_baseline": cpu,
     }
