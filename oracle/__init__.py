@@ -40,6 +40,9 @@ def lib():
         L.hyo_fp8_decode.argtypes = [vp, vp, i64, i64, vp]
         L.hyo_ffn_w64.argtypes = [vp, i64, vp, vp, vp, i64, i64, vp, ci]
         L.hyo_forward_w64.argtypes = [vp] * 9 + [i64] * 5 + [vp] * 6 + [ci]
+        L.hyo_mx_quantize.argtypes = [vp, i64, i64, vp, vp]
+        L.hyo_ffn_w8a8.argtypes = [vp, i64, vp, vp, vp, i64, i64, vp, ci]
+        L.hyo_forward_w8a8.argtypes = [vp] * 9 + [i64] * 5 + [vp] * 6 + [ci]
         L.hyo_indexer_scores.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp]
         L.hyo_topk_indices.argtypes = [vp, i64, i64, i64, vp, vp, vp]
         _lib = L
@@ -194,6 +197,53 @@ def forward_w64(x, wr, bias, fg, fu, fd, sg, su, sd, k, sets_in=None, nthreads=N
     _check(lib().hyo_forward_w64(_p(x), _p(wr), _p(bias), _p(fg), _p(fu), _p(fd), _p(sg), _p(su), _p(sd),
                                  T, d, E, k, I, _p(sets_in), _p(out), _p(sets), _p(w), _p(margin), _p(lg),
                                  _threads(nthreads)), "hyo_forward_w64")
+    return {"out": out, "sets": sets, "w": w, "margin": margin, "logits": lg}
+
+
+def mx_quantize(v):
+    """MXFP8 quantization (E4M3 codes, one E8M0 scale per 32 consecutive values along a
+    row) of fp32 rows v [rows][cols]. Returns (codes uint8 [rows][cols], scales uint8
+    [rows][cols / 32]); value = e4m3(code) * 2^(scale - 127)."""
+    v = _c(np.atleast_2d(v), np.float32)
+    rows, cols = v.shape
+    codes = np.empty((rows, cols), np.uint8)
+    scales = np.empty((rows, max(cols // 32, 1)), np.uint8)
+    _check(lib().hyo_mx_quantize(_p(v), rows, cols, _p(codes), _p(scales)), "hyo_mx_quantize")
+    return codes, scales
+
+
+def ffn_w8a8(x_rows, wg, wu, wd, nthreads=None):
+    """Expert FFN with fp64 weights and MXFP8 activations (x and the hidden rows
+    quantized) on bf16 token rows."""
+    x_rows = _c(np.atleast_2d(x_rows), np.uint16)
+    wg, wu, wd = _c(wg, np.float64), _c(wu, np.float64), _c(wd, np.float64)
+    n, d = x_rows.shape
+    I = wg.shape[0]
+    y = np.empty((n, d), np.float64)
+    _check(lib().hyo_ffn_w8a8(_p(x_rows), n, _p(wg), _p(wu), _p(wd), d, I, _p(y), _threads(nthreads)),
+           "hyo_ffn_w8a8")
+    return y
+
+
+def forward_w8a8(x, wr, bias, fg, fu, fd, sg, su, sd, k, sets_in=None, nthreads=None):
+    """Whole layer with fp64 (decoded FP8) routed weights and MXFP8 activations in the
+    routed experts; bf16 router and shared expert. Returns dict(out, sets, w, margin,
+    logits)."""
+    x, wr, bias = _c(x, np.uint16), _c(wr, np.uint16), _c(bias, np.float32)
+    fg, fu, fd = _c(fg, np.float64), _c(fu, np.float64), _c(fd, np.float64)
+    sg, su, sd = _c(sg, np.uint16), _c(su, np.uint16), _c(sd, np.uint16)
+    sets_in = _c(sets_in, np.int32)
+    T, d = x.shape
+    E = wr.shape[0]
+    I = sg.shape[0]
+    out = np.empty((T, d), np.float64)
+    sets = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    margin = np.empty(T, np.float64)
+    lg = np.empty((T, E), np.float64)
+    _check(lib().hyo_forward_w8a8(_p(x), _p(wr), _p(bias), _p(fg), _p(fu), _p(fd), _p(sg), _p(su), _p(sd),
+                                  T, d, E, k, I, _p(sets_in), _p(out), _p(sets), _p(w), _p(margin), _p(lg),
+                                  _threads(nthreads)), "hyo_forward_w8a8")
     return {"out": out, "sets": sets, "w": w, "margin": margin, "logits": lg}
 
 

@@ -49,6 +49,19 @@
  * carries one fp32 scale, weight = scale * value; activations stay bf16 and the
  * shared expert stays bf16.
  *
+ * FP8 weights with FP8 activations (W8A8; same pages and section, which name no
+ * activation format). Reading taken here: the routed experts take the FP8 weights
+ * above, and their activations (the token rows entering gate/up and the hidden
+ * rows entering down) are quantized to MXFP8 as the OCP Microscaling Formats v1.0
+ * specification defines it: along K, each block of 32 consecutive values shares
+ * one power-of-two scale 2^e stored as an E8M0 byte e + 127, with
+ * e = floor(log2(max |v|)) - 8 (8 being the exponent of E4M3's largest normal,
+ * 448 = 1.75 * 2^8) clamped to [-127, 127] (a block of zeros takes -127), and
+ * each value becomes the E4M3 value nearest to v * 2^-e, ties to the even
+ * mantissa, saturated to +-448. The hidden values are rounded to fp32 before they
+ * are quantized (the precision in which the GPU path quantizes them). The router
+ * and the shared expert stay bf16.
+ *
  * Sparse-attention indexer (Hy4 preview config summary, Tencent Hy4 preview model
  * card: every layer is DeepSeek-style sparse attention with an indexer of 32 heads,
  * head_dim 128 and top-k 2048, whose 128-dim key per token is shared by all heads;
@@ -416,15 +429,158 @@ int hyo_ffn_w64(const uint16_t* x_rows, int64_t n, const double* wg, const doubl
   return HYO_OK;
 }
 
+/* ------------------------------------- FP8 activations (MXFP8) -------- */
+
+/* x rounded to the nearest integer, ties to the even one (exact for |x| < 2^52). */
+static double round_half_even(double x) {
+  double f = floor(x), r = x - f;
+  if (r > 0.5) return f + 1.0;
+  if (r < 0.5) return f;
+  return fmod(f, 2.0) == 0.0 ? f : f + 1.0;
+}
+
+/* E4M3 code of the value nearest to v (ties to the even mantissa), saturated to
+ * +-448; the sign of zero is kept. From the encoding's definition: normals are
+ * (1 + m/8) 2^(E) for E in [-6, 8], subnormals m/8 * 2^-6. */
+static uint8_t e4m3_encode(double v) {
+  const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+  const double a = fabs(v);
+  if (a == 0.0) return sign;
+  int ex;
+  frexp(a, &ex);
+  int E = ex - 1; /* floor(log2 a) */
+  if (E < -6) {   /* subnormal range: multiples of 2^-9 */
+    const double n = round_half_even(ldexp(a, 9));
+    return n >= 8.0 ? (uint8_t)(sign | 0x08) : (uint8_t)(sign | (uint8_t)n);
+  }
+  double m = round_half_even(ldexp(a, 3 - E)); /* 8..16: the significand in eighths */
+  if (m == 16.0) {
+    m = 8.0;
+    E += 1;
+  }
+  if (E > 8 || (E == 8 && m > 14.0)) return (uint8_t)(sign | 0x7E); /* 448 */
+  return (uint8_t)(sign | (uint8_t)(((E + 7) << 3) | ((int)m - 8)));
+}
+
+/* MXFP8 quantization of rows of fp32 values, blocks of 32 along a row:
+ * v [rows][cols] (cols % 32 == 0) -> codes uint8 [rows][cols] (E4M3),
+ * scales uint8 [rows][cols / 32] (E8M0: the block's scale is 2^(byte - 127)). */
+int hyo_mx_quantize(const float* v, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales) {
+  if (rows < 0 || cols <= 0 || cols % 32 != 0 || (rows > 0 && (!v || !codes || !scales))) return HYO_ERR_ARG;
+  const int64_t nb = cols / 32;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t b = 0; b < nb; ++b) {
+      const float* blk = v + r * cols + 32 * b;
+      double amax = 0.0;
+      for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs((double)blk[i]));
+      int e = -127;
+      if (amax > 0.0) {
+        int ex;
+        frexp(amax, &ex);
+        e = ex - 1 - 8;
+        if (e < -127) e = -127;
+        if (e > 127) e = 127;
+      }
+      scales[r * nb + b] = (uint8_t)(e + 127);
+      for (int i = 0; i < 32; ++i) codes[r * cols + 32 * b + i] = e4m3_encode(ldexp((double)blk[i], -e));
+    }
+  return HYO_OK;
+}
+
+/* The values an MXFP8 row stands for: code value * 2^(scale - 127). */
+static void mx_values(const uint8_t* codes, const uint8_t* scales, int64_t cols, double* out) {
+  for (int64_t c = 0; c < cols; ++c) out[c] = ldexp(e4m3_value(codes[c]), (int)scales[c / 32] - 127);
+}
+
+/* A row quantized to MXFP8 and read back: fp32 in, fp64 values out. */
+static int mx_round_trip(const float* v, int64_t cols, double* out) {
+  uint8_t* q = (uint8_t*)malloc((size_t)cols);
+  uint8_t* sc = (uint8_t*)malloc((size_t)(cols / 32));
+  if (!q || !sc) {
+    free(q);
+    free(sc);
+    return HYO_ERR_ARG;
+  }
+  int rc = hyo_mx_quantize(v, 1, cols, q, sc);
+  if (rc == HYO_OK) mx_values(q, sc, cols, out);
+  free(q);
+  free(sc);
+  return rc;
+}
+
+typedef struct {
+  const double *x, *wg, *wu, *wd; /* x: the row's MXFP8 values [d] */
+  int64_t d, I;
+  double* h; /* [I]: silu(g) * u, then its MXFP8 values */
+  double* y; /* [d] */
+} ffn8_ctx;
+
+static void ffn8_hidden(void* p, int64_t i0, int64_t i1) {
+  ffn8_ctx* c = (ffn8_ctx*)p;
+  for (int64_t i = i0; i < i1; ++i) {
+    const double* g = c->wg + i * c->d;
+    const double* u = c->wu + i * c->d;
+    double sg = 0.0, su = 0.0;
+    for (int64_t j = 0; j < c->d; ++j) {
+      sg += g[j] * c->x[j];
+      su += u[j] * c->x[j];
+    }
+    c->h[i] = silu(sg) * su;
+  }
+}
+
+static void ffn8_out(void* p, int64_t m0, int64_t m1) {
+  ffn8_ctx* c = (ffn8_ctx*)p;
+  for (int64_t m = m0; m < m1; ++m) {
+    const double* dn = c->wd + m * c->I;
+    double s = 0.0;
+    for (int64_t i = 0; i < c->I; ++i) s += dn[i] * c->h[i];
+    c->y[m] = s;
+  }
+}
+
+/* One routed expert with fp64 (decoded FP8) weights and MXFP8 activations:
+ *   x~ = MXFP8(x_r), h = silu(W_gate x~) * (W_up x~), h~ = MXFP8(fp32(h)),
+ *   y_r = W_down h~.
+ * x_rows: bf16 [n][d]; wg, wu: fp64 [I][d]; wd: fp64 [d][I]; y: fp64 [n][d];
+ * d % 32 == 0, I % 32 == 0. */
+int hyo_ffn_w8a8(const uint16_t* x_rows, int64_t n, const double* wg, const double* wu, const double* wd,
+                 int64_t d, int64_t I, double* y, int nthreads) {
+  if (n < 0 || d <= 0 || I <= 0 || d % 32 || I % 32 || (n > 0 && (!x_rows || !wg || !wu || !wd || !y)))
+    return HYO_ERR_ARG;
+  int rc = HYO_OK;
+  float* xf = (float*)malloc(sizeof(float) * (size_t)d);
+  double* xq = (double*)malloc(sizeof(double) * (size_t)d);
+  double* h = (double*)malloc(sizeof(double) * (size_t)I);
+  float* hf = (float*)malloc(sizeof(float) * (size_t)I);
+  if (!xf || !xq || !h || !hf) {
+    rc = HYO_ERR_ARG;
+    goto done;
+  }
+  for (int64_t r = 0; r < n; ++r) {
+    for (int64_t j = 0; j < d; ++j) xf[j] = (float)bf16_value(x_rows[r * d + j]);
+    if ((rc = mx_round_trip(xf, d, xq))) goto done;
+    ffn8_ctx c = {xq, wg, wu, wd, d, I, h, y + r * d};
+    parallel_for(I, ffn8_hidden, &c, nthreads);
+    for (int64_t i = 0; i < I; ++i) hf[i] = (float)h[i];
+    if ((rc = mx_round_trip(hf, I, h))) goto done;
+    parallel_for(d, ffn8_out, &c, nthreads);
+  }
+done:
+  free(xf); free(xq); free(h); free(hf);
+  return rc;
+}
+
 /* ------------------------------------------------------- whole layer ----- */
 
 /* The whole layer; routed experts' weights as bf16 (wg..wd) or as fp64 (fg..fd, the
  * other set NULL). */
 static int forward_impl(const uint16_t* x, const uint16_t* wr, const float* bias, const uint16_t* wg,
                         const uint16_t* wu, const uint16_t* wd, const double* fg, const double* fu,
-                        const double* fd, const uint16_t* sg, const uint16_t* su, const uint16_t* sd, int64_t T,
-                        int64_t d, int64_t E, int64_t k, int64_t I, const int32_t* sets_in, double* out,
-                        int32_t* sets_out, double* w_out, double* margin_out, double* logits_out, int nthreads) {
+                        const double* fd, int a8, const uint16_t* sg, const uint16_t* su, const uint16_t* sd,
+                        int64_t T, int64_t d, int64_t E, int64_t k, int64_t I, const int32_t* sets_in,
+                        double* out, int32_t* sets_out, double* w_out, double* margin_out, double* logits_out,
+                        int nthreads) {
   if (T < 0 || d <= 0 || E <= 0 || k < 1 || k > E || I <= 0) return HYO_ERR_ARG;
   if (T == 0) return HYO_OK;
   const int f64 = fg != NULL;
@@ -445,10 +601,15 @@ static int forward_impl(const uint16_t* x, const uint16_t* wr, const float* bias
   for (int64_t t = 0; t < T; ++t)
     for (int64_t j = 0; j < k; ++j) {
       int64_t e = sets[t * k + j];
-      rc = f64 ? hyo_ffn_w64(x + t * d, 1, fg + e * I * d, fu + e * I * d, fd + e * d * I, d, I,
-                             yr + (t * k + j) * d, nthreads)
-               : hyo_ffn(x + t * d, 1, wg + e * I * d, wu + e * I * d, wd + e * d * I, d, I,
-                         yr + (t * k + j) * d, nthreads);
+      if (a8)
+        rc = hyo_ffn_w8a8(x + t * d, 1, fg + e * I * d, fu + e * I * d, fd + e * d * I, d, I, yr + (t * k + j) * d,
+                          nthreads);
+      else if (f64)
+        rc = hyo_ffn_w64(x + t * d, 1, fg + e * I * d, fu + e * I * d, fd + e * d * I, d, I, yr + (t * k + j) * d,
+                         nthreads);
+      else
+        rc = hyo_ffn(x + t * d, 1, wg + e * I * d, wu + e * I * d, wd + e * d * I, d, I, yr + (t * k + j) * d,
+                     nthreads);
       if (rc) goto done;
     }
   rc = hyo_combine(ys, yr, w, T, k, d, out);
@@ -471,7 +632,7 @@ int hyo_forward(const uint16_t* x, const uint16_t* wr, const float* bias, const 
                 const uint16_t* sd, int64_t T, int64_t d, int64_t E, int64_t k, int64_t I,
                 const int32_t* sets_in, double* out, int32_t* sets_out, double* w_out,
                 double* margin_out, double* logits_out, int nthreads) {
-  return forward_impl(x, wr, bias, wg, wu, wd, NULL, NULL, NULL, sg, su, sd, T, d, E, k, I, sets_in, out,
+  return forward_impl(x, wr, bias, wg, wu, wd, NULL, NULL, NULL, 0, sg, su, sd, T, d, E, k, I, sets_in, out,
                       sets_out, w_out, margin_out, logits_out, nthreads);
 }
 
@@ -483,7 +644,19 @@ int hyo_forward_w64(const uint16_t* x, const uint16_t* wr, const float* bias, co
                     const int32_t* sets_in, double* out, int32_t* sets_out, double* w_out,
                     double* margin_out, double* logits_out, int nthreads) {
   if (!fg) return HYO_ERR_ARG;
-  return forward_impl(x, wr, bias, NULL, NULL, NULL, fg, fu, fd, sg, su, sd, T, d, E, k, I, sets_in, out,
+  return forward_impl(x, wr, bias, NULL, NULL, NULL, fg, fu, fd, 0, sg, su, sd, T, d, E, k, I, sets_in, out,
+                      sets_out, w_out, margin_out, logits_out, nthreads);
+}
+
+/* The same with the routed experts on MXFP8 activations (hyo_ffn_w8a8); the router
+ * and the shared expert stay bf16. d % 32 == 0, I % 32 == 0. */
+int hyo_forward_w8a8(const uint16_t* x, const uint16_t* wr, const float* bias, const double* fg,
+                     const double* fu, const double* fd, const uint16_t* sg, const uint16_t* su,
+                     const uint16_t* sd, int64_t T, int64_t d, int64_t E, int64_t k, int64_t I,
+                     const int32_t* sets_in, double* out, int32_t* sets_out, double* w_out,
+                     double* margin_out, double* logits_out, int nthreads) {
+  if (!fg || d % 32 || I % 32) return HYO_ERR_ARG;
+  return forward_impl(x, wr, bias, NULL, NULL, NULL, fg, fu, fd, 1, sg, su, sd, T, d, E, k, I, sets_in, out,
                       sets_out, w_out, margin_out, logits_out, nthreads);
 }
 

@@ -479,6 +479,146 @@ def test_fp8_layer_matches_dense_masked_numpy():
 
 
 # ------------------------------------------------------- sparse-attention indexer
+# --------------------------------------------------- MXFP8 activations (W8A8)
+def read_mx_blocks():
+    blocks, cur = [], None
+    for line in open(os.path.join(GOLDEN, "mxfp8_blocks.txt")):
+        if not line.strip() or line.startswith("#"):
+            continue
+        parts = line.split()
+        if parts[0] == "block":
+            cur = {"name": parts[1], "scale": int(parts[2]), "v": np.zeros(32, np.float32),
+                   "codes": np.zeros(32, np.uint8)}
+            blocks.append(cur)
+        else:
+            i, val, code = int(parts[0]), parts[1], int(parts[2], 16)
+            cur["v"][i] = np.float32(float.fromhex(val) if "0x" in val else float(val))
+            cur["codes"][i] = code
+    return blocks
+
+
+def mx_values(codes, scales):
+    """Values of MXFP8 rows from the (separately pinned) E4M3 decoder and the scale bytes."""
+    v = oracle.fp8_decode(codes)
+    return v * np.exp2(np.repeat(scales.astype(np.float64) - 127.0, 32, axis=-1))
+
+
+def test_mx_hand_worked_blocks():
+    blocks = read_mx_blocks()
+    assert len(blocks) == 6
+    q, sc = oracle.mx_quantize(np.stack([b["v"] for b in blocks]))
+    for i, b in enumerate(blocks):
+        assert sc[i, 0] == b["scale"], b["name"]
+        assert np.array_equal(q[i], b["codes"]), (b["name"], q[i][:8], b["codes"][:8])
+
+
+def test_mx_codes_match_torch_float8_conversion():
+    # the element rounding against torch's own float -> float8_e4m3fn conversion (round to
+    # nearest even, an independent implementation), below the saturation threshold; the
+    # block exponent from numpy's frexp
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(21)
+    rows = (rng.standard_normal((64, 96)) * np.exp2(rng.integers(-30, 30, (64, 1)))).astype(np.float32)
+    rows[3, :40] = 0.0
+    q, sc = oracle.mx_quantize(rows)
+    blk = rows.astype(np.float64).reshape(64, 3, 32)
+    amax = np.abs(blk).max(axis=2)
+    _, ex = np.frexp(amax)
+    e = np.where(amax > 0, np.clip(ex - 1 - 8, -127, 127), -127)
+    assert np.array_equal(sc.astype(np.int64), e + 127)
+    scaled = blk * np.exp2(-e)[:, :, None]
+    ref = torch.from_numpy(scaled.reshape(64, 96).astype(np.float32)).to(torch.float8_e4m3fn)
+    ref = ref.view(torch.uint8).numpy()
+    ok = np.abs(scaled.reshape(64, 96)) < 448.0
+    assert ok.mean() > 0.95
+    assert np.array_equal(q[ok], ref[ok])
+    assert np.all((q[~ok] & 0x7F) == 0x7E)  # at or beyond 448: saturated
+
+
+def test_mx_error_bounds_and_round_trip():
+    rng = np.random.default_rng(22)
+    rows = (rng.standard_normal((40, 128)) * np.exp2(rng.integers(-12, 12, (40, 1)))).astype(np.float32)
+    q, sc = oracle.mx_quantize(rows)
+    v = mx_values(q, sc)
+    x = rows.astype(np.float64)
+    e = np.repeat(sc.astype(np.float64) - 127.0, 32, axis=1)
+    # each value within half a step of the E4M3 grid at its own magnitude (steps are
+    # 2^(E - 3) for normals, 2^-9 in the subnormal range, in units of the block scale)
+    _, ex = np.frexp(np.abs(x) * np.exp2(-e))
+    E = np.maximum(ex - 1, -6)
+    step = np.exp2(E - 3 + e)
+    scaled = np.abs(x) * np.exp2(-e)
+    sat = scaled >= 464.0  # rounds past 448: saturated (the scale rule lets amax reach 2^9)
+    assert np.all(np.abs(v - x)[~sat] <= 0.5 * step[~sat] * (1 + 1e-12))
+    assert np.array_equal(np.abs(v)[sat], (448.0 * np.exp2(e))[sat]) and np.all(np.sign(v[sat]) == np.sign(x[sat]))
+    assert sat.any()
+    assert np.all(np.abs(v) <= 448.0 * np.exp2(e))
+    # the largest value of each block lands in the top binade of E4M3 (field 15)
+    blk_q = q.reshape(40, 4, 32)
+    top = np.take_along_axis(blk_q, np.abs(x).reshape(40, 4, 32).argmax(axis=2)[:, :, None], axis=2)
+    assert np.all(((top >> 3) & 15) == 15)
+    # values already on the grid are reproduced: quantizing the read-back values is exact
+    q2, sc2 = oracle.mx_quantize(v.astype(np.float32))
+    assert np.array_equal(q2, q) and np.array_equal(sc2, sc)
+    assert np.array_equal(mx_values(q2, sc2), v)
+
+
+def _fp8_expert(rng, I, d, scale=0.05):
+    def mat(rows, cols):
+        q = rng.integers(0, 256, size=(rows, cols), dtype=np.uint8)
+        q[(q & 0x7F) == 0x7F] = 0x30
+        s = (rng.random(rows) * scale + scale / 4).astype(np.float32)
+        return oracle.fp8_decode(q, s)
+    return mat(I, d), mat(I, d), mat(d, I)
+
+
+def test_ffn_w8a8_composition():
+    # the FFN's steps in their order, composed in numpy from the pinned quantizer: x
+    # quantized along d, the hidden rows rounded to fp32 and quantized along I, fp64 sums
+    rng = np.random.default_rng(23)
+    n, d, I = 3, 96, 64
+    x = f32_to_bf16_bits(rng.standard_normal((n, d)))
+    wg, wu, wd = _fp8_expert(rng, I, d)
+    got = oracle.ffn_w8a8(x, wg, wu, wd, nthreads=2)
+    xq = mx_values(*oracle.mx_quantize(bf(x).astype(np.float32)))
+    g, u = xq @ wg.T, xq @ wu.T
+    h = (np_silu(g) * u).astype(np.float32)
+    hq = mx_values(*oracle.mx_quantize(h))
+    assert np.allclose(got, hq @ wd.T, rtol=1e-12, atol=1e-12)
+    # the quantization is there: it differs from the FP8-weight FFN on bf16 activations, by
+    # about the E4M3 rounding (relative 2^-4 per value)
+    ref = oracle.ffn_w64(x, wg, wu, wd, nthreads=2)
+    err = np.abs(got - ref).max() / np.abs(ref).max()
+    assert 1e-4 < err < 0.1
+    # gate and up are not interchangeable, and the down input is the hidden row
+    assert not np.allclose(oracle.ffn_w8a8(x, wu, wg, wd), got)
+
+
+def test_forward_w8a8_matches_dense_masked_numpy():
+    cfg, L = small_layer(seed=5, T=12, d=64, E=6, k=2, I=32, bias=True)
+    rng = np.random.default_rng(24)
+    exp = [_fp8_expert(rng, cfg.I, cfg.d) for _ in range(cfg.E)]
+    fg, fu, fd = (np.stack([e[i] for e in exp]) for i in range(3))
+    ref = oracle.forward_w8a8(L["x"], L["router"], L["bias"], fg, fu, fd, L["shared"]["gate"],
+                              L["shared"]["up"], L["shared"]["down"], cfg.k)
+    x = bf(L["x"])
+    lg = x @ bf(L["router"]).T + L["bias"].astype(np.float64)
+    out = np_swiglu(x, bf(L["shared"]["gate"]), bf(L["shared"]["up"]), bf(L["shared"]["down"]))
+    xq = mx_values(*oracle.mx_quantize(x.astype(np.float32)))
+    for t in range(cfg.T):
+        order = np.lexsort((np.arange(cfg.E), -lg[t]))[:cfg.k]
+        p = np.exp(lg[t, order] - lg[t, order].max())
+        p /= p.sum()
+        for pe, e in zip(p, order):
+            h = (np_silu(xq[t] @ fg[e].T) * (xq[t] @ fu[e].T)).astype(np.float32)
+            out[t] += pe * (mx_values(*oracle.mx_quantize(h[None]))[0] @ fd[e].T)
+    assert np.allclose(ref["out"], out, rtol=1e-11, atol=1e-11)
+    # routing is that of the other formats
+    w64 = oracle.forward_w64(L["x"], L["router"], L["bias"], fg, fu, fd, L["shared"]["gate"],
+                             L["shared"]["up"], L["shared"]["down"], cfg.k)
+    assert np.array_equal(ref["sets"], w64["sets"]) and np.array_equal(ref["w"], w64["w"])
+
+
 def test_indexer_hand_worked():
     # H=2, D=2: q0=(1,2), q1=(-1,1), w=(0.5,2); key (3,-1): dots 1, -4 -> 0.5*1 + 2*0 = 0.5;
     # key (0,1): dots 2, 1 -> 0.5*2 + 2*1 = 3
