@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s; %bf16 MFMA peak (T=8192), %HBM BW (T=32)"
 PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
 PEAK_BF16 = 2.5e15         # flop/s, MI355X dense bf16 MFMA
+PEAK_FP8 = 5.0e15          # flop/s, MI355X dense fp8 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -113,7 +114,7 @@ def step_stats(vals):
     return {"median": _pct(vals, 0.5), "p10": _pct(vals, 0.1), "p90": _pct(vals, 0.9), "n": len(vals)}
 
 
-def time_layer(hm, torch, inp, k, ws, steps, warmup, dominant, flush=None):
+def time_layer(hm, torch, inp, k, ws, steps, warmup, dominant, flush=None, fwd_kw=None):
     """Times `steps` forwards after `warmup` untimed ones (None: at least 5 steps and
     WARMUP_MIN_S seconds of them). Returns dict(total_ms by the host clock around the
     synchronised steps, step_ms (per step, from events at the first and last kernel of
@@ -121,18 +122,20 @@ def time_layer(hm, torch, inp, k, ws, steps, warmup, dominant, flush=None):
     kernel from a separate pass of stage events after the timed region), warmup (steps
     run), cold_ms (per step with `flush` run between steps outside the events, or None)).
     Only the step's two ends and the dominant kernel's two ends are recorded while
-    timing: an event between every kernel would add its own gaps to the step."""
+    timing: an event between every kernel would add its own gaps to the step.
+    fwd_kw: extra keyword arguments of every forward_layer call."""
     nk = len(hm.KERNELS)
+    kw = dict(fwd_kw or {})
     done = 0
     t_w = time.perf_counter()
     if warmup is not None:
         for _ in range(warmup):
-            hm.forward_layer(inp, k, workspace=ws)
+            hm.forward_layer(inp, k, workspace=ws, **kw)
         done = warmup
     else:
         while done < 5 or time.perf_counter() - t_w < WARMUP_MIN_S:
             for _ in range(5):
-                hm.forward_layer(inp, k, workspace=ws)
+                hm.forward_layer(inp, k, workspace=ws, **kw)
             done += 5
             torch.cuda.synchronize()
     torch.cuda.synchronize()
@@ -147,7 +150,7 @@ def time_layer(hm, torch, inp, k, ws, steps, warmup, dominant, flush=None):
         arrays.append(arr)
     t0 = time.perf_counter()
     for i in range(steps):
-        hm.forward_layer(inp, k, workspace=ws, stage_events=arrays[i])
+        hm.forward_layer(inp, k, workspace=ws, stage_events=arrays[i], **kw)
     torch.cuda.synchronize()
     total_ms = (time.perf_counter() - t0) * 1e3
     step_ms = [ev.ms(4 * i, 4 * i + 1) for i in range(steps)]
@@ -160,7 +163,7 @@ def time_layer(hm, torch, inp, k, ws, steps, warmup, dominant, flush=None):
         cold = []
         for i in range(steps):
             flush()
-            hm.forward_layer(inp, k, workspace=ws, stage_events=arrays[i])
+            hm.forward_layer(inp, k, workspace=ws, stage_events=arrays[i], **kw)
         torch.cuda.synchronize()
         cold = [ev.ms(4 * i, 4 * i + 1) for i in range(steps)]
         cold_dom = [ev.ms(da(i), db(i)) for i in range(steps)]
@@ -169,7 +172,7 @@ def time_layer(hm, torch, inp, k, ws, steps, warmup, dominant, flush=None):
     nb = min(steps, 20)
     ev = Events((nk + 1) * nb)
     for i in range(nb):
-        hm.forward_layer(inp, k, workspace=ws, stage_events=ev.array(i, nk + 1))
+        hm.forward_layer(inp, k, workspace=ws, stage_events=ev.array(i, nk + 1), **kw)
     torch.cuda.synchronize()
     per = [0.0] * nk
     for i in range(nb):
@@ -220,10 +223,23 @@ def gemm_work(cfg):
     rows = cfg.T * cfg.k + cfg.T
     kernel = ("grouped_gemm_kernel<true, 0, 1> (ternary routed tiles) + grouped_gemm_kernel<true, 0, 0> "
               "(bf16 shared tiles): one timed stage" if cfg.ternary else
+              "mx_quantize_kernel (token rows to MXFP8) + grouped_gemm_kernel<true, 0, 3> (FP8 MFMAs on the W8A8 "
+              "routed tiles) + grouped_gemm_kernel<true, 0, 0> (bf16 shared tiles): one timed stage" if cfg.a8 else
               "grouped_gemm_kernel<true, 0, 2> (FP8 routed tiles) + grouped_gemm_kernel<true, 0, 0> "
               "(bf16 shared tiles): one timed stage" if cfg.fp8 else "grouped_gemm_kernel<true, 0, 0>")
+    # W8A8: the routed rows run on FP8 MFMAs and the shared rows on bf16 ones, so the
+    # stage's peak is the time both take at their own peaks
+    routed, shared = cfg.T * cfg.k, cfg.T
+    peak = rows / (routed / PEAK_FP8 + shared / PEAK_BF16) if cfg.a8 else PEAK_BF16
+    layer_peak = ((2 * cfg.T * d * cfg.E + 6 * rows * d * I) /
+                  ((2 * cfg.T * d * cfg.E + 6 * shared * d * I) / PEAK_BF16 + 6 * routed * d * I / PEAK_FP8)
+                  if cfg.a8 else PEAK_BF16)
     return {"rows": rows, "alg": 4 * rows * d * I, "layer_flop": 2 * cfg.T * d * cfg.E + 6 * rows * d * I,
-            "per_unit": f"{4 * d * I} flop per dispatched row (gate and up: 2*d*I each)", "kernel": kernel}
+            "per_unit": f"{4 * d * I} flop per dispatched row (gate and up: 2*d*I each)", "kernel": kernel,
+            "peak": peak, "layer_peak": layer_peak,
+            "peak_how": (f"{routed} routed rows at the FP8 dense peak ({PEAK_FP8 / 1e15:.1f} PFLOP/s) and {shared} "
+                         f"shared rows at the bf16 one ({PEAK_BF16 / 1e15:.1f}): total flops / the time both take "
+                         f"at their peaks" if cfg.a8 else "bf16 dense MFMA peak")}
 
 
 def input_digest(inp, torch):
@@ -249,26 +265,28 @@ def run_config(name, args, hi, hm, torch, weights=None, steps=None, flush=None):
         inp["x"] = weights["x"][: cfg.T].contiguous()
         b = hi.host_bias(cfg)
         inp["bias"] = None if b is None else torch.from_numpy(b).to(dev)
-    fmt = hm.WEIGHTS_SHERRY_TERNARY if cfg.ternary else hm.WEIGHTS_FP8_E4M3 if cfg.fp8 else hm.WEIGHTS_BF16
+    fmt = (hm.WEIGHTS_SHERRY_TERNARY if cfg.ternary else hm.WEIGHTS_FP8_W8A8 if cfg.a8 else
+           hm.WEIGHTS_FP8_E4M3 if cfg.fp8 else hm.WEIGHTS_BF16)
+    fwd_kw = {"fp8_activations": True} if cfg.a8 else {}
     ws = hm.alloc_workspace(cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, fmt, device=dev)
     steps = args.steps if steps is None else steps
     dominant = hm.KERNELS.index("expert_gateup")
-    r = time_layer(hm, torch, inp, cfg.k, ws, steps, args.warmup, dominant, flush=flush)
+    r = time_layer(hm, torch, inp, cfg.k, ws, steps, args.warmup, dominant, flush=flush, fwd_kw=fwd_kw)
     ms = r["total_ms"] / steps
     dom_ms = sum(r["dom_ms"]) / steps
-    routing = hm.forward_layer(inp, cfg.k, want_routing=True, workspace=ws)
+    routing = hm.forward_layer(inp, cfg.k, want_routing=True, workspace=ws, **fwd_kw)
     torch.cuda.synchronize()
     counts = routing["counts"].cpu()
     touched = int((counts > 0).sum())
     near = int((routing["margin"] <= 1e-4).sum().item())
-    stream_path = cfg.T * cfg.k <= 16 * cfg.E  # the library's automatic path choice
+    stream_path = cfg.T * cfg.k <= 16 * cfg.E and not cfg.a8  # the library's automatic path choice
     kernel_file = "sparse_moe_transformer_route_amd/csrc/" + ("moe_stream.hip" if stream_path else "moe_gemm.hip")
     # algorithmic bytes and flops of the whole layer (both reported for every workload)
     lw = stream_work(cfg, touched)
     gw = gemm_work(cfg)
     layer = {"bytes": lw["layer_bytes"], "flop": gw["layer_flop"],
              "hbm_frac": lw["layer_bytes"] / (ms * 1e-3) / PEAK_HBM,
-             "mfma_frac": gw["layer_flop"] / (ms * 1e-3) / PEAK_BF16}
+             "mfma_frac": gw["layer_flop"] / (ms * 1e-3) / gw["layer_peak"]}
     sec = dom_ms * 1e-3
     if stream_path:
         alg = lw["alg"]
@@ -278,9 +296,10 @@ def run_config(name, args, hi, hm, torch, weights=None, steps=None, flush=None):
                 "kernel_ms": dom_ms}
     else:
         rows, alg = gw["rows"], gw["alg"]
-        roof = {"bound": "mfma", "achieved": alg / sec / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
-                "frac": alg / sec / PEAK_BF16, "traffic": traffic_for(f"grouped_gemm_gateup/{name}", rows),
-                "kernel": gw["kernel"], "per_unit": gw["per_unit"], "units_per_launch": rows, "kernel_ms": dom_ms}
+        roof = {"bound": "mfma", "achieved": alg / sec / 1e12, "peak": gw["peak"] / 1e12, "unit": "TFLOP/s",
+                "frac": alg / sec / gw["peak"], "traffic": traffic_for(f"grouped_gemm_gateup/{name}", rows),
+                "kernel": gw["kernel"], "per_unit": gw["per_unit"], "units_per_launch": rows, "kernel_ms": dom_ms,
+                "peak_how": gw["peak_how"]}
     roof["kernel_source_sha256_16"] = source_digest(os.path.join(ROOT, kernel_file))
     res = {"cfg": cfg, "inp": inp, "ms": ms, "tokens_per_s": cfg.T / (ms * 1e-3), "kernels_ms": r["kernels"],
            "roofline": roof, "layer": layer, "touched": touched, "counts": counts, "routing": routing,
@@ -293,7 +312,7 @@ def run_config(name, args, hi, hm, torch, weights=None, steps=None, flush=None):
                        "layer_hbm_frac_at_median": lw["layer_bytes"] / (cold["median"] * 1e-3) / PEAK_HBM,
                        "kernel_ms": cold_dom * 1e3,
                        "kernel_frac": (lw["alg"] if stream_path else gw["alg"]) / cold_dom /
-                       (PEAK_HBM if stream_path else PEAK_BF16),
+                       (PEAK_HBM if stream_path else gw["peak"]),
                        "how": "a 512 MiB write between steps (outside the events) evicts the 256 MB last-level cache"}
     return res
 
@@ -313,9 +332,16 @@ def workload_object(res, extra=None):
     return o
 
 
+def dtype_name(c):
+    return ("sherry-ternary+bf16" if c.ternary else "fp8-e4m3+mxfp8-activations+bf16" if c.a8 else
+            "fp8-e4m3+bf16" if c.fp8 else "bf16")
+
+
 def workload_name(c):
     return (f"{c.name} MoE FFN layer T={c.T} d={c.d} E={c.E} top-{c.k} + 1 shared I={c.I}"
-            + (" Sherry-ternary routed experts" if c.ternary else " FP8-E4M3 routed experts" if c.fp8 else " bf16")
+            + (" Sherry-ternary routed experts" if c.ternary else
+               " FP8-E4M3 routed experts with MXFP8 activations (W8A8)" if c.a8 else
+               " FP8-E4M3 routed experts" if c.fp8 else " bf16")
             + (" Zipf(1.2) router bias" if c.zipf_s else ""))
 
 
@@ -365,7 +391,7 @@ def cpu_baseline(cfg, hi, torch, inp, routing, budget_s):
         for i in range(len(tok)):
             for j, e in enumerate(sets[i]):
                 g, u, dn = expert(int(e))
-                ffn = oracle.ffn_w64 if "fgate" in inp else oracle.ffn
+                ffn = oracle.ffn_w8a8 if cfg.a8 else oracle.ffn_w64 if "fgate" in inp else oracle.ffn
                 yr[i, j] = ffn(x[tok[i]:tok[i] + 1], g, u, dn, nthreads=nthreads)[0]
         oracle.combine(ys, yr, w)
         return time.perf_counter() - t0
@@ -528,6 +554,7 @@ def main():
                     help="untimed steps before the timed ones (default: at least 5 and %.1f s of them)" % WARMUP_MIN_S)
     ap.add_argument("--config", default="decode", choices=["tiny", "decode", "prefill", "skewed", "ternary",
                                                                  "ternary_prefill", "fp8", "fp8_prefill",
+                                                                 "fp8_w8a8_prefill",
                                                                  "indexer_tiny", "indexer_decode"])
     ap.add_argument("--only", action="store_true",
                     help="time --config alone (no other workloads, probes or oracle): for profiler runs")
@@ -628,13 +655,20 @@ def main():
         extra["ternary"] = workload_object(tn)
         del tn, flush_buf
         torch.cuda.empty_cache()
+        w8 = run_config("fp8_w8a8_prefill", args, hi, hm, torch)
+        report(w8)
+        extra["fp8_w8a8_prefill"] = workload_object(w8)
+        del w8
+        torch.cuda.empty_cache()
 
     roof = main_res["roofline"]
-    if peaks is not None:
+    if peaks is not None and (roof["unit"] == "GB/s" or roof["peak_how"].startswith("bf16")):
         meas = peaks["hbm_read_gbs"] if roof["unit"] == "GB/s" else peaks["mfma_bf16_tflops"]
         roof["frac_of_measured_peak"] = roof["achieved"] / meas
         for o in extra.values():
             r = o["roofline"]
+            if r["unit"] == "TFLOP/s" and not r["peak_how"].startswith("bf16"):
+                continue  # no measured FP8 rate to set it against
             r["frac_of_measured_peak"] = r["achieved"] / (peaks["hbm_read_gbs"] if r["unit"] == "GB/s"
                                                           else peaks["mfma_bf16_tflops"])
             if r["unit"] == "TFLOP/s" and "library_gemm_bf16" in peaks:
@@ -650,7 +684,7 @@ def main():
         "metric": METRIC, "value": main_res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
         "steps": main_res["steps"], "warmup": main_res["warmup"], "ms_per_step": main_res["ms"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "sherry-ternary+bf16" if c.ternary else "fp8-e4m3+bf16" if c.fp8 else "bf16", "data": "synthetic",
+        "dtype": dtype_name(c), "data": "synthetic",
         "config": {"workload": workload_name(c), "T": c.T, "d": c.d, "E": c.E, "k": c.k, "I": c.I, "seed": c.seed,
                    "touched_experts": main_res["touched"]},
         "step_ms": main_res["step_ms"],

@@ -49,6 +49,7 @@ class LayerConfig:
     I: int
     ternary: bool = False
     fp8: bool = False        # routed experts as E4M3 codes with fp32 row scales
+    a8: bool = False         # with fp8: the routed experts' activations in MXFP8 (W8A8)
     zipf_s: float = 0.0      # 0 => no router bias
     zipf_alpha: float = 1.0
     x_std: float = 1.0
@@ -68,6 +69,9 @@ CONFIGS = {
     # routed experts as FP8 (E4M3 codes, fp32 row scales), decode batch
     "fp8": LayerConfig("fp8", T=32, d=6144, E=256, k=8, I=2048, fp8=True),
     "fp8_prefill": LayerConfig("fp8_prefill", T=8192, d=6144, E=256, k=8, I=2048, fp8=True),
+    # FP8 weights with MXFP8 activations (W8A8) on the FP8 matrix cores
+    "fp8_w8a8_prefill": LayerConfig("fp8_w8a8_prefill", T=8192, d=6144, E=256, k=8, I=2048, fp8=True, a8=True),
+    "fp8_w8a8": LayerConfig("fp8_w8a8", T=32, d=6144, E=256, k=8, I=2048, fp8=True, a8=True),
     # the ternary experts at a prefill-sized batch (grouped GEMM on decoded codes)
     "ternary_prefill": LayerConfig("ternary_prefill", T=8192, d=6144, E=256, k=8, I=2048, ternary=True),
 }

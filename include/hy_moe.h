@@ -80,7 +80,17 @@ typedef enum {
    * weight = scale * value. Activations and the shared expert stay bf16; a NaN
    * code gives NaN outputs. The kernels convert the codes to bf16 exactly (every
    * E4M3 value is a bf16 value) and scale the fp32 sums. */
-  HY_MOE_WEIGHTS_FP8_E4M3 = 2
+  HY_MOE_WEIGHTS_FP8_E4M3 = 2,
+  /* FP8 weights with FP8 activations (W8A8; same pages, which name no activation
+   * format). Weights, scales and their layout exactly as HY_MOE_WEIGHTS_FP8_E4M3.
+   * The routed experts' activations (the token rows entering gate/up and the hidden
+   * rows entering down) are quantized to MXFP8 as OCP Microscaling Formats v1.0
+   * defines it (see hy_moe_mxfp8_quantize) and the products run on the FP8 matrix
+   * cores, block scales applied in hardware, fp32 accumulation; the hidden rows are
+   * quantized from fp32. The router and the shared expert stay bf16. Runs on the
+   * grouped path only (AUTO picks it; HY_MOE_PATH_STREAM -> HY_MOE_ERR_UNSUPPORTED) and
+   * needs d % 256 == 0 and I % 256 == 0. */
+  HY_MOE_WEIGHTS_FP8_W8A8 = 3
 } hy_moe_wfmt;
 
 /* Which kernels run the experts. AUTO picks by the average rows per expert. */
@@ -156,6 +166,13 @@ typedef struct hy_moe_args {
      in the order listed below; event i+1 minus event i is the duration of kernel i. A NULL
      entry is skipped (that point is not recorded). */
   void** stage_events;
+  /* optional hidden-row output, HY_MOE_WEIGHTS_FP8_W8A8 only (DEVICE, NULL to skip; both or
+     neither): the routed experts' hidden rows exactly as the down projection reads them,
+     in dispatched-row order (row p belongs to the pair perm_src[p]). hidden_codes: uint8
+     [T*k][I] E4M3 codes, 16-byte aligned; hidden_scales: uint8 [T*k][I/32] E8M0 block
+     scales. When given they replace the workspace's copy (no extra traffic). */
+  void* hidden_codes;
+  void* hidden_scales;
 } hy_moe_args;
 
 /* Kernels of one call, in launch order (indices into the stage events). */
@@ -186,7 +203,8 @@ int hy_moe_forward_ex(const hy_moe_args* args, void* stream);
  *         (HY_MOE_ERR_INVALID_ARG otherwise).
  * Shapes whose hy_moe_workspace_size() exceeds HY_MOE_NOALLOC_SCRATCH_BYTES are
  * rejected with HY_MOE_ERR_WORKSPACE before anything is enqueued; at the Hy4 preview
- * layer shape (d = 6144, E = 256, k = 8, I = 2048) that admits T <= 251. All calls on
+ * layer shape (d = 6144, E = 256, k = 8, I = 2048) that admits T <= 251 (T <= 383 with
+ * HY_MOE_WEIGHTS_FP8_W8A8, whose grouped path keeps its expert outputs in bf16). All calls on
  * one device share that device's buffer and it keeps the last call's contents: calls
  * that overlap in time on one device (other streams, other threads) race and their
  * results are undefined, so serialize them. Nothing in the buffer needs to start at
@@ -209,6 +227,23 @@ const char* hy_moe_status_string(int status);
  * Returns HY_MOE_ERR_INVALID_ARG (packed untouched) if a group breaks the rule.
  */
 int hy_moe_sherry_pack_host(const int8_t* tern, int64_t rows, int64_t cols, uint32_t* packed);
+
+/*
+ * hy_moe_mxfp8_quantize — the activation quantization of HY_MOE_WEIGHTS_FP8_W8A8 on its
+ * own (OCP Microscaling Formats v1.0, MXFP8): each row is cut into blocks of 32
+ * consecutive values; a block shares the scale 2^e, e = floor(log2 max|v|) - 8 clamped
+ * to [-127, 127] (-127 for a block of zeros), stored as the E8M0 byte e + 127; each
+ * value becomes the E4M3 code (the encoding of HY_MOE_WEIGHTS_FP8_E4M3) of the value
+ * nearest to v * 2^-e, ties to the even mantissa, saturated to +-448.
+ *   x       DEVICE bf16 [rows][cols], 16-byte aligned; cols % 32 == 0
+ *   codes   DEVICE uint8 [rows][cols], 16-byte aligned (out)
+ *   scales  DEVICE uint8 [rows][cols / 32] (out)
+ * Enqueued on `stream` without blocking. Returns HY_MOE_OK, HY_MOE_ERR_INVALID_ARG
+ * (null or misaligned pointers, rows < 0, cols not a positive multiple of 32; nothing
+ * enqueued), HY_MOE_ERR_UNSUPPORTED (rows * cols >= 2^40) or HY_MOE_ERR_HIP.
+ * rows == 0 is a no-op.
+ */
+int hy_moe_mxfp8_quantize(const void* x, int64_t rows, int64_t cols, void* codes, void* scales, void* stream);
 
 /*
  * Machine-peak probes (not part of the layer): the rates this GPU reaches, for

@@ -42,6 +42,7 @@ def lib():
         L.hyo_forward_w64.argtypes = [vp] * 9 + [i64] * 5 + [vp] * 6 + [ci]
         L.hyo_mx_quantize.argtypes = [vp, i64, i64, vp, vp]
         L.hyo_ffn_w8a8.argtypes = [vp, i64, vp, vp, vp, i64, i64, vp, ci]
+        L.hyo_ffn_w8a8_ex.argtypes = [vp, i64, vp, vp, vp, i64, i64, vp, vp, vp, vp, ci]
         L.hyo_forward_w8a8.argtypes = [vp] * 9 + [i64] * 5 + [vp] * 6 + [ci]
         L.hyo_indexer_scores.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp]
         L.hyo_topk_indices.argtypes = [vp, i64, i64, i64, vp, vp, vp]
@@ -223,6 +224,22 @@ def ffn_w8a8(x_rows, wg, wu, wd, nthreads=None):
     _check(lib().hyo_ffn_w8a8(_p(x_rows), n, _p(wg), _p(wu), _p(wd), d, I, _p(y), _threads(nthreads)),
            "hyo_ffn_w8a8")
     return y
+
+
+def ffn_w8a8_ex(x_rows, wg, wu, wd, hq=None, hs=None, want_hidden=False, nthreads=None):
+    """ffn_w8a8 with the hidden rows' fp32 values returned (want_hidden) and, where hq, hs
+    are given (E4M3 codes [n][I], E8M0 scales [n][I / 32]), those codes used as the hidden
+    rows instead of the oracle's own quantization. Returns y or (y, h32)."""
+    x_rows = _c(np.atleast_2d(x_rows), np.uint16)
+    wg, wu, wd = _c(wg, np.float64), _c(wu, np.float64), _c(wd, np.float64)
+    n, d = x_rows.shape
+    I = wg.shape[0]
+    hq, hs = _c(hq, np.uint8), _c(hs, np.uint8)
+    y = np.empty((n, d), np.float64)
+    h32 = np.empty((n, I), np.float32) if want_hidden else None
+    _check(lib().hyo_ffn_w8a8_ex(_p(x_rows), n, _p(wg), _p(wu), _p(wd), d, I, _p(hq), _p(hs), _p(h32), _p(y),
+                                 _threads(nthreads)), "hyo_ffn_w8a8_ex")
+    return (y, h32) if want_hidden else y
 
 
 def forward_w8a8(x, wr, bias, fg, fu, fd, sg, su, sd, k, sets_in=None, nthreads=None):

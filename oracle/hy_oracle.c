@@ -543,11 +543,16 @@ static void ffn8_out(void* p, int64_t m0, int64_t m1) {
  *   x~ = MXFP8(x_r), h = silu(W_gate x~) * (W_up x~), h~ = MXFP8(fp32(h)),
  *   y_r = W_down h~.
  * x_rows: bf16 [n][d]; wg, wu: fp64 [I][d]; wd: fp64 [d][I]; y: fp64 [n][d];
- * d % 32 == 0, I % 32 == 0. */
-int hyo_ffn_w8a8(const uint16_t* x_rows, int64_t n, const double* wg, const double* wu, const double* wd,
-                 int64_t d, int64_t I, double* y, int nthreads) {
+ * d % 32 == 0, I % 32 == 0. h32_out (fp32 [n][I], or NULL) receives fp32(h). If hq_in and
+ * hs_in are given (E4M3 codes [n][I] and E8M0 scales [n][I / 32]), h~ is read from them
+ * instead of quantized from h: the substitution of a hidden code that lies on the other
+ * side of a rounding boundary (the test decides which codes are admissible). */
+int hyo_ffn_w8a8_ex(const uint16_t* x_rows, int64_t n, const double* wg, const double* wu, const double* wd,
+                    int64_t d, int64_t I, const uint8_t* hq_in, const uint8_t* hs_in, float* h32_out, double* y,
+                    int nthreads) {
   if (n < 0 || d <= 0 || I <= 0 || d % 32 || I % 32 || (n > 0 && (!x_rows || !wg || !wu || !wd || !y)))
     return HYO_ERR_ARG;
+  if ((hq_in == NULL) != (hs_in == NULL)) return HYO_ERR_ARG;
   int rc = HYO_OK;
   float* xf = (float*)malloc(sizeof(float) * (size_t)d);
   double* xq = (double*)malloc(sizeof(double) * (size_t)d);
@@ -563,12 +568,21 @@ int hyo_ffn_w8a8(const uint16_t* x_rows, int64_t n, const double* wg, const doub
     ffn8_ctx c = {xq, wg, wu, wd, d, I, h, y + r * d};
     parallel_for(I, ffn8_hidden, &c, nthreads);
     for (int64_t i = 0; i < I; ++i) hf[i] = (float)h[i];
-    if ((rc = mx_round_trip(hf, I, h))) goto done;
+    if (h32_out) memcpy(h32_out + r * I, hf, sizeof(float) * (size_t)I);
+    if (hq_in)
+      mx_values(hq_in + r * I, hs_in + r * (I / 32), I, h);
+    else if ((rc = mx_round_trip(hf, I, h)))
+      goto done;
     parallel_for(d, ffn8_out, &c, nthreads);
   }
 done:
   free(xf); free(xq); free(h); free(hf);
   return rc;
+}
+
+int hyo_ffn_w8a8(const uint16_t* x_rows, int64_t n, const double* wg, const double* wu, const double* wd,
+                 int64_t d, int64_t I, double* y, int nthreads) {
+  return hyo_ffn_w8a8_ex(x_rows, n, wg, wu, wd, d, I, NULL, NULL, NULL, y, nthreads);
 }
 
 /* ------------------------------------------------------- whole layer ----- */

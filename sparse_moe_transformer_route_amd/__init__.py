@@ -24,14 +24,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhy_moe.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
-WEIGHTS_BF16, WEIGHTS_SHERRY_TERNARY, WEIGHTS_FP8_E4M3 = 0, 1, 2
+WEIGHTS_BF16, WEIGHTS_SHERRY_TERNARY, WEIGHTS_FP8_E4M3, WEIGHTS_FP8_W8A8 = 0, 1, 2, 3
 PATH_AUTO, PATH_STREAM, PATH_GROUPED = 0, 1, 2
 KERNELS = ["route_logits", "route_topk", "permute_scan", "permute_scatter", "expert_gateup", "expert_down",
            "combine"]
 NUM_STAGE_EVENTS = len(KERNELS) + 1
 
 EXPORTED = ["hy_moe_forward", "hy_moe_forward_ex", "hy_moe_forward_noalloc", "hy_moe_workspace_size",
-            "hy_moe_status_string", "hy_moe_sherry_pack_host", "hy_moe_probe_mfma_bf16", "hy_moe_probe_hbm_read",
+            "hy_moe_status_string", "hy_moe_sherry_pack_host", "hy_moe_mxfp8_quantize", "hy_moe_probe_mfma_bf16", "hy_moe_probe_hbm_read",
             "hy_indexer_workspace_size", "hy_indexer_topk"]
 PROBE_OPERAND_BYTES = 65536
 NOALLOC_SCRATCH_BYTES = 64 << 20  # HY_MOE_NOALLOC_SCRATCH_BYTES
@@ -54,6 +54,7 @@ class HyMoeArgs(ctypes.Structure):
         ("offsets", ctypes.c_void_p), ("perm_src", ctypes.c_void_p), ("margin", ctypes.c_void_p),
         ("path", ctypes.c_int),
         ("stage_events", ctypes.c_void_p),
+        ("hidden_codes", ctypes.c_void_p), ("hidden_scales", ctypes.c_void_p),
     ]
 
 
@@ -80,6 +81,8 @@ def _load():
     L.hy_moe_status_string.restype = ctypes.c_char_p
     L.hy_moe_sherry_pack_host.argtypes = [vp, i64, i64, vp]
     L.hy_moe_sherry_pack_host.restype = ctypes.c_int
+    L.hy_moe_mxfp8_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
+    L.hy_moe_mxfp8_quantize.restype = ctypes.c_int
     L.hy_moe_probe_mfma_bf16.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_float), vp]
     L.hy_moe_probe_mfma_bf16.restype = ctypes.c_int
     L.hy_moe_probe_hbm_read.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_float), vp]
@@ -142,13 +145,16 @@ def forward_noalloc(args: HyMoeArgs, stream=None) -> int:
 
 
 def forward_layer(inp: dict, k: int, *, want_routing=False, path=PATH_AUTO, workspace=None, out=None,
-                  stream=None, stage_events=None, noalloc=False):
+                  stream=None, stage_events=None, noalloc=False, fp8_activations=False, want_hidden=False):
     """Runs hy_moe_forward_ex on a dict of device tensors as made by
     hy_inputs.dev_layer(): x, router, bias, shared{gate,up,down} and either
     gate/up/down (bf16), qgate/qup/qdown + sgate/sup/sdown (ternary) or
     fgate/fup/fdown + fsgate/fsup/fsdown (FP8 E4M3 codes and fp32 scales).
     Returns dict(out, and with want_routing: topk_idx, topk_w, counts, offsets,
-    perm_src, margin). noalloc: call hy_moe_forward_noalloc (no workspace)."""
+    perm_src, margin). noalloc: call hy_moe_forward_noalloc (no workspace).
+    fp8_activations (FP8 weights only): the W8A8 format, MXFP8 activations; with
+    want_hidden also hidden_codes [T*k][I] and hidden_scales [T*k][I/32] (the routed
+    hidden rows as the down projection reads them, dispatched-row order)."""
     import torch
     x = inp["x"]
     T, d = x.shape
@@ -168,7 +174,10 @@ def forward_layer(inp: dict, k: int, *, want_routing=False, path=PATH_AUTO, work
     dev = x.device
     a = HyMoeArgs()
     a.x, a.W_router, a.router_bias = _ptr(x), _ptr(inp["router"]), _ptr(inp.get("bias"))
-    a.expert_format = WEIGHTS_SHERRY_TERNARY if ternary else WEIGHTS_FP8_E4M3 if fp8 else WEIGHTS_BF16
+    if fp8_activations and not fp8:
+        raise ValueError("forward_layer: fp8_activations needs FP8 weights")
+    a.expert_format = (WEIGHTS_SHERRY_TERNARY if ternary else
+                       (WEIGHTS_FP8_W8A8 if fp8_activations else WEIGHTS_FP8_E4M3) if fp8 else WEIGHTS_BF16)
     if ternary:
         a.Wq_gate, a.Wq_up, a.Wq_down = _ptr(inp["qgate"]), _ptr(inp["qup"]), _ptr(inp["qdown"])
         a.S_gate, a.S_up, a.S_down = _ptr(inp["sgate"]), _ptr(inp["sup"]), _ptr(inp["sdown"])
@@ -194,6 +203,12 @@ def forward_layer(inp: dict, k: int, *, want_routing=False, path=PATH_AUTO, work
         a.topk_idx, a.topk_w = _ptr(res["topk_idx"]), _ptr(res["topk_w"])
         a.counts, a.offsets = _ptr(res["counts"]), _ptr(res["offsets"])
         a.perm_src, a.margin = _ptr(res["perm_src"]), _ptr(res["margin"])
+    if want_hidden:
+        if not fp8_activations:
+            raise ValueError("forward_layer: want_hidden needs fp8_activations")
+        res.update(hidden_codes=torch.empty(T * k, I, dtype=torch.uint8, device=dev),
+                   hidden_scales=torch.empty(T * k, I // 32, dtype=torch.uint8, device=dev))
+        a.hidden_codes, a.hidden_scales = _ptr(res["hidden_codes"]), _ptr(res["hidden_scales"])
     a.path = path
     if stage_events is not None:
         a.stage_events = ctypes.cast(stage_events, ctypes.c_void_p)
@@ -228,6 +243,21 @@ def sherry_pack_host(tern):
     if rc != OK:
         raise HyMoeError(rc, "hy_moe_sherry_pack_host")
     return packed
+
+
+def mxfp8_quantize(x, stream=None):
+    """hy_moe_mxfp8_quantize on a device bf16 tensor [rows][cols] (cols % 32 == 0).
+    Returns (codes uint8 [rows][cols], scales uint8 [rows][cols / 32])."""
+    import torch
+    if x.dtype != torch.bfloat16 or not x.is_contiguous() or x.dim() != 2:
+        raise TypeError("mxfp8_quantize: x must be a contiguous 2-d bf16 tensor")
+    rows, cols = x.shape
+    codes = torch.empty(rows, cols, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(rows, max(cols // 32, 1), dtype=torch.uint8, device=x.device)
+    rc = _lib.hy_moe_mxfp8_quantize(x.data_ptr(), rows, cols, codes.data_ptr(), scales.data_ptr(), _stream(stream))
+    if rc != OK:
+        raise HyMoeError(rc, "hy_moe_mxfp8_quantize")
+    return codes, scales
 
 
 def probe_mfma_bf16(operands, stream=None) -> float:

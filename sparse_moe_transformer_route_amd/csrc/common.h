@@ -85,4 +85,22 @@ __device__ __forceinline__ uint4 e4m3x8_bf16(uint32_t lo, uint32_t hi) {
   return make_uint4(e4m3x2_bf16<false>(lo), e4m3x2_bf16<true>(lo), e4m3x2_bf16<false>(hi), e4m3x2_bf16<true>(hi));
 }
 
+// ---- MXFP8 (OCP Microscaling v1.0): blocks of 32 values share a scale 2^e (E8M0 byte
+// e + 127), e = floor(log2 amax) - 8 clamped to [-127, 127] (-127 for a zero block);
+// elements are E4M3 (nearest, ties to even) of v * 2^-e saturated to +-448.
+
+// The block exponent e of a block whose largest magnitude is amax (finite).
+__device__ __forceinline__ int mx_exponent(float amax) {
+  if (!(amax > 0.f)) return -127;
+  const int e = __builtin_amdgcn_frexp_expf(amax) - 9;  // frexp exponent - 1 = floor(log2 amax)
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Four values scaled by 2^-e to four E4M3 codes in one word (value i in byte i).
+__device__ __forceinline__ uint32_t mx_pack4(float v0, float v1, float v2, float v3, int e) {
+  auto q = [e](float v) { return __builtin_amdgcn_fmed3f(__builtin_ldexpf(v, -e), -448.f, 448.f); };
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q(v0), q(v1), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q(v2), q(v3), lo, true);
+}
+
 }  // namespace hymoe

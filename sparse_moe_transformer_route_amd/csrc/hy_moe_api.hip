@@ -19,11 +19,19 @@ constexpr int64_t kMaxK = 16;
 size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t part, topk_idx, topk_w, mask, blk_base, offs, meta, touched, tiles, perm_src, pos, h, y, total;
+  size_t part, topk_idx, topk_w, mask, blk_base, offs, meta, touched, tiles, perm_src, pos, h, y, xq, xs, hq, hs,
+      total;
   int ks, nblk, max_tiles;
 };
 
-Layout make_layout(int64_t T, int64_t d, int64_t E, int64_t k, int64_t I) {
+bool valid_format(int f) {
+  return f == HY_MOE_WEIGHTS_BF16 || f == HY_MOE_WEIGHTS_SHERRY_TERNARY || f == HY_MOE_WEIGHTS_FP8_E4M3 ||
+         f == HY_MOE_WEIGHTS_FP8_W8A8;
+}
+
+// W8A8 runs on the grouped path only, whose y is bf16; it adds the MXFP8 codes and
+// scales of the token rows and of the routed hidden rows.
+Layout make_layout(int64_t T, int64_t d, int64_t E, int64_t k, int64_t I, int fmt) {
   Layout L{};
   L.ks = route_split_for((int)T, (int)d, (int)E);
   L.nblk = (int)((T + kMaskBlock - 1) / kMaskBlock);
@@ -48,7 +56,14 @@ Layout make_layout(int64_t T, int64_t d, int64_t E, int64_t k, int64_t I) {
   L.perm_src = take(sizeof(int32_t) * (size_t)Tk);
   L.pos = take(sizeof(int32_t) * (size_t)Tk);
   L.h = take(sizeof(uint16_t) * (size_t)rows * I);
-  L.y = take(sizeof(float) * (size_t)rows * d);  // fp32 for the streaming path, bf16 for the grouped path
+  const bool a8 = fmt == HY_MOE_WEIGHTS_FP8_W8A8;
+  L.y = take((a8 ? 2 : 4) * (size_t)rows * d);  // fp32 for the streaming path, bf16 for the grouped path
+  if (a8) {
+    L.xq = take((size_t)T * d);
+    L.xs = take((size_t)T * (d / 32));
+    L.hq = take((size_t)Tk * I);
+    L.hs = take((size_t)Tk * (I / 32));
+  }
   L.total = off;
   return L;
 }
@@ -73,9 +88,7 @@ int check_args(const hy_moe_args* a) {
   if (!a) return HY_MOE_ERR_INVALID_ARG;
   int rc = check_shape(a->T, a->d, a->E, a->k, a->I);
   if (rc != HY_MOE_OK) return rc;
-  if (a->expert_format != HY_MOE_WEIGHTS_BF16 && a->expert_format != HY_MOE_WEIGHTS_SHERRY_TERNARY &&
-      a->expert_format != HY_MOE_WEIGHTS_FP8_E4M3)
-    return HY_MOE_ERR_INVALID_ARG;
+  if (!valid_format(a->expert_format)) return HY_MOE_ERR_INVALID_ARG;
   if (a->path != HY_MOE_PATH_AUTO && a->path != HY_MOE_PATH_STREAM && a->path != HY_MOE_PATH_GROUPED)
     return HY_MOE_ERR_INVALID_ARG;
   if (a->T == 0) return HY_MOE_OK;
@@ -102,12 +115,21 @@ int check_args(const hy_moe_args* a) {
       if (!p || !aligned(p, 4)) return HY_MOE_ERR_INVALID_ARG;
   }
   if (a->path == HY_MOE_PATH_GROUPED && !grouped_fits(a->T, a->d, a->k, a->I)) return HY_MOE_ERR_UNSUPPORTED;
+  if (a->expert_format == HY_MOE_WEIGHTS_FP8_W8A8) {
+    // grouped path only, two 128-code k steps at least in both products
+    if (a->path == HY_MOE_PATH_STREAM || !grouped_fits(a->T, a->d, a->k, a->I)) return HY_MOE_ERR_UNSUPPORTED;
+    if (a->d % 256 != 0 || a->I % 256 != 0) return HY_MOE_ERR_UNSUPPORTED;
+  }
+  if ((a->hidden_codes == nullptr) != (a->hidden_scales == nullptr)) return HY_MOE_ERR_INVALID_ARG;
+  if (a->hidden_codes && (a->expert_format != HY_MOE_WEIGHTS_FP8_W8A8 || !aligned(a->hidden_codes, 16)))
+    return HY_MOE_ERR_INVALID_ARG;
   const void* opt4[] = {a->topk_idx, a->topk_w, a->counts, a->offsets, a->perm_src, a->margin};
   for (const void* p : opt4)
     if (p && !aligned(p, 4)) return HY_MOE_ERR_INVALID_ARG;
   if (a->workspace) {
     if (!aligned(a->workspace, 256)) return HY_MOE_ERR_INVALID_ARG;
-    if (a->workspace_bytes < make_layout(a->T, a->d, a->E, a->k, a->I).total) return HY_MOE_ERR_WORKSPACE;
+    if (a->workspace_bytes < make_layout(a->T, a->d, a->E, a->k, a->I, a->expert_format).total)
+      return HY_MOE_ERR_WORKSPACE;
   }
   return HY_MOE_OK;
 }
@@ -120,7 +142,7 @@ extern "C" int hy_moe_forward_ex(const hy_moe_args* a, void* stream) {
   if (a->T == 0) return HY_MOE_OK;
 
   hipStream_t s = (hipStream_t)stream;
-  const Layout L = make_layout(a->T, a->d, a->E, a->k, a->I);
+  const Layout L = make_layout(a->T, a->d, a->E, a->k, a->I, a->expert_format);
   uint8_t* ws = (uint8_t*)a->workspace;
   bool owned = false;
   if (!ws) {
@@ -151,10 +173,18 @@ extern "C" int hy_moe_forward_ex(const hy_moe_args* a, void* stream) {
   p.pos = (int32_t*)(ws + L.pos);
   p.h = (uint16_t*)(ws + L.h);
   p.y = (void*)(ws + L.y);
+  const bool a8 = a->expert_format == HY_MOE_WEIGHTS_FP8_W8A8;
+  if (a8) {
+    p.xq = ws + L.xq;
+    p.xs = ws + L.xs;
+    p.hq = a->hidden_codes ? (uint8_t*)a->hidden_codes : ws + L.hq;
+    p.hs = a->hidden_scales ? (uint8_t*)a->hidden_scales : ws + L.hs;
+  }
 
   ExpertWeights w{};
   w.ternary = a->expert_format == HY_MOE_WEIGHTS_SHERRY_TERNARY;
-  w.fp8 = a->expert_format == HY_MOE_WEIGHTS_FP8_E4M3;
+  w.fp8 = a->expert_format == HY_MOE_WEIGHTS_FP8_E4M3 || a8;
+  w.a8 = a8;
   w.f8gate = (const uint8_t*)a->Wq_gate;
   w.f8up = (const uint8_t*)a->Wq_up;
   w.f8down = (const uint8_t*)a->Wq_down;
@@ -180,7 +210,7 @@ extern "C" int hy_moe_forward_ex(const hy_moe_args* a, void* stream) {
   else if (a->path == HY_MOE_PATH_GROUPED)
     stream_path = false;
   else
-    stream_path = (int64_t)p.Tk <= 16 * (int64_t)p.E || !grouped_fits(p.T, p.d, p.k, p.I);
+    stream_path = !a8 && ((int64_t)p.Tk <= 16 * (int64_t)p.E || !grouped_fits(p.T, p.d, p.k, p.I));
 
   const uint16_t* x = (const uint16_t*)a->x;
   Marks marks{a->stage_events, 0};
@@ -235,7 +265,7 @@ extern "C" int hy_moe_forward_noalloc(const hy_moe_args* a, void* stream) {
   int rc = check_args(a);
   if (rc != HY_MOE_OK) return rc;
   if (a->T == 0) return HY_MOE_OK;
-  if (make_layout(a->T, a->d, a->E, a->k, a->I).total > (size_t)HY_MOE_NOALLOC_SCRATCH_BYTES)
+  if (make_layout(a->T, a->d, a->E, a->k, a->I, a->expert_format).total > (size_t)HY_MOE_NOALLOC_SCRATCH_BYTES)
     return HY_MOE_ERR_WORKSPACE;
   void* ws = nullptr;
   rc = scratch_of_current_device(&ws);
@@ -267,11 +297,9 @@ extern "C" int hy_moe_forward(const void* x, const void* W_router, const void* W
 }
 
 extern "C" size_t hy_moe_workspace_size(int64_t T, int64_t d, int64_t E, int64_t k, int64_t I, int expert_format) {
-  if (expert_format != HY_MOE_WEIGHTS_BF16 && expert_format != HY_MOE_WEIGHTS_SHERRY_TERNARY &&
-      expert_format != HY_MOE_WEIGHTS_FP8_E4M3)
-    return 0;
+  if (!valid_format(expert_format)) return 0;
   if (check_shape(T, d, E, k, I) != HY_MOE_OK) return 0;
-  return make_layout(T, d, E, k, I).total;
+  return make_layout(T, d, E, k, I, expert_format).total;
 }
 
 extern "C" const char* hy_moe_status_string(int status) {

@@ -47,6 +47,11 @@ struct Plan {
   int32_t* pos;              // [T*k] inverse of perm_src
   uint16_t* h;               // bf16 [rows][I]
   void* y;                   // [rows][d]: fp32 (stream path) or bf16 (grouped path)
+  // FP8 W8A8 only (MXFP8 activations of the routed experts)
+  uint8_t* xq;               // [T][d] E4M3 codes of the token rows
+  uint8_t* xs;               // [T][d / 32] E8M0 block scales
+  uint8_t* hq;               // [T*k][I] codes of the routed hidden rows
+  uint8_t* hs;               // [T*k][I / 32] their block scales
 };
 
 hipError_t launch_route(const Plan& p, const uint16_t* x, const uint16_t* w_router, const float* bias,
@@ -78,6 +83,7 @@ struct ExpertWeights {
   const uint16_t* s_down;
   bool ternary;
   bool fp8;
+  bool a8;  // with fp8: MXFP8 activations (W8A8)
 };
 
 hipError_t launch_stream_experts(const Plan& p, const uint16_t* x, const ExpertWeights& w, hipStream_t s,
@@ -85,6 +91,9 @@ hipError_t launch_stream_experts(const Plan& p, const uint16_t* x, const ExpertW
 hipError_t launch_grouped_experts(const Plan& p, const uint16_t* x, const ExpertWeights& w, hipStream_t s,
                                   Marks& m);
 hipError_t launch_combine(const Plan& p, bool y_is_f32, uint16_t* out, hipStream_t s, Marks& m);
+
+hipError_t launch_mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                              hipStream_t s);
 
 int grouped_gemm_bm();
 int route_split_for(int T, int d, int E);

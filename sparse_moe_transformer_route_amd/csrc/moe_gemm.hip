@@ -74,14 +74,45 @@ constexpr int kF8Ops = kF8Slot / 16 / kThreads;      // 4 direct-to-LDS ops per 
 constexpr int kF8ScaleBytes = kRowsMax * 4;          // an item's 256 row scales (fp32)
 static_assert(kF8Ops == kCodeOps, "the code and FP8 load offsets share storage");
 
-// Weight formats of the routed experts' tiles.
-constexpr int kGemmBf16 = 0, kGemmTern = 1, kGemmFp8 = 2;
+// Weight formats of the routed experts' tiles. kGemmW8A8: FP8 weights and MXFP8
+// activations on the FP8 matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4): a k step is
+// 128 codes (128 bytes per row, as the bf16 step's 64 values), two MFMA groups of 64;
+// the activations' E8M0 block scales reach the MFMAs from registers.
+constexpr int kGemmBf16 = 0, kGemmTern = 1, kGemmFp8 = 2, kGemmW8A8 = 3;
+constexpr int kBK8 = 128;        // W8A8: k per step
+constexpr int kSub8 = kBK8 / 64;  // W8A8: MFMA groups per step
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// D[32x32] += A[32x64] B[64x32] on E4M3 codes with E8M0 block scales sa (A) and sb (B)
+// (byte 0 of each; 127 = 1). Lane (r, h) holds row / column r: bytes 0-15 are k
+// [16h, 16h + 16) and bytes 16-31 are k [32 + 16h, 32 + 16h + 16) of the 64, and the scale
+// of 32-k block b of row / column r comes from lane (r, b). D as the bf16 32x32 MFMA.
+__device__ __forceinline__ f32x16 mfma32x32x64_f8(i32x8 a, i32x8 b, f32x16 c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+// Two 16-byte LDS reads into one 8-register operand.
+__device__ __forceinline__ i32x8 lds_pair(const uint8_t* p0, const uint8_t* p1) {
+  const i32x4 lo = *reinterpret_cast<const i32x4*>(p0);
+  const i32x4 hi = *reinterpret_cast<const i32x4*>(p1);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 
 int grouped_gemm_bm() { return kRowsMax; }
 
 struct GemmArgs {
   const uint16_t* x;
+  // W8A8: this launch's activation codes and block scales (gate/up: the token rows,
+  // [T][d] and [T][d / 32]; down: the routed hidden rows, [T k][I] and [T k][I / 32]) and,
+  // for gate/up, where the hidden rows' codes and scales go
+  const uint8_t* aq;
+  const uint8_t* as;
+  uint8_t* hq;
+  uint8_t* hs;
   const int32_t* perm_src;
   const int32_t* offs;
   int32_t* meta;  // [1] M tiles, [2] routed M tiles; [kMetaSched..] per-XCD work counters, zeroed by the
@@ -194,9 +225,11 @@ template <bool GATEUP, int TAILR, int WF>
 __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, ExpertWeights w,
                                                                    uint16_t* __restrict__ h,
                                                                    uint16_t* __restrict__ y) {
-  constexpr bool TERN = WF == kGemmTern, FP8 = WF == kGemmFp8;
+  constexpr bool TERN = WF == kGemmTern, FP8 = WF == kGemmFp8, A8 = WF == kGemmW8A8;
   constexpr int BS = 3;  // weight (or code) ring slots
   constexpr int kBOps = TERN ? kCodeOps : FP8 ? kF8Ops : kDma;  // weight-side load ops per thread per step
+  constexpr int SUB = A8 ? kSub8 : kSub;   // MFMA groups per step
+  constexpr int BKE = A8 ? kBK8 : kBK;     // k per step (128 bytes per row either way)
   // Separate LDS arrays rather than one carved buffer: the compiler tells direct-to-LDS
   // loads and LDS reads of different arrays apart; within one array it would wait for
   // every such load in flight before each LDS read.
@@ -291,7 +324,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
   };
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, kept scalar
   const int wm = wv & 1, wn = wv >> 1;
-  const int nks = K / kBK;
+  const int nks = K / BKE;
   const uint32_t fa_off = wm * kBlk * kRowBytes;              // block 2j + wm
   const uint32_t fb_off = wn * (kRowsMax / 2) * kRowBytes;    // columns 128 wn..
 
@@ -331,6 +364,14 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
     uint32_t f8o[kSub / 2];
 #pragma unroll
     for (int q = 0; q < kSub / 2; ++q) f8o[q] = (uint32_t)(r32 * kF8Pitch + 16 * ((2 * q + hf) ^ f8_key(r32)));
+    // W8A8: group s (k [64 s, 64 s + 64) of the step) takes the lane's two 16-byte pieces,
+    // chunks 4 s + hf and 4 s + 2 + hf of the row's 128 bytes (the FP8 MFMA's byte order)
+    uint32_t a8o[kSub8][2];
+#pragma unroll
+    for (int q = 0; q < kSub8; ++q)
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+        a8o[q][p] = (uint32_t)(r32 * kRowBytes + (((4 * q + 2 * p + hf) ^ swz_key(r32)) << 4));
     // items of one expert (its c M tiles x NT N tiles) are ordered in blocks of up to
     // 4 M tiles, N tile major within a block, so the workgroups running together on
     // an XCD share both the activation rows and the weight tiles through its L2
@@ -362,7 +403,8 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
     // stored).
     // Addresses are a workgroup-uniform base (scalar registers) plus a 32-bit byte offset
     // per lane (the grouped path requires x, h and every expert matrix under 4 GiB).
-    const char* const abase = reinterpret_cast<const char*>(GATEUP ? a.x : h);
+    const char* const abase = A8 ? reinterpret_cast<const char*>(a.aq)
+                                 : reinterpret_cast<const char*>(GATEUP ? a.x : h);
     uint32_t aoff[kDma], boff[kDma];
     const char* bbase[kDma];
     // gate/up: the token of each loaded row (rows past Tk are the shared expert's, in
@@ -385,7 +427,19 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
       const int q = kThreads * i + 64 * wv + lane;
       const int row = q >> 3, lc = (q & 7) ^ swz_key(row);
       const int grow = ebase + m0 + min(row, mrows - 1);
-      if (GATEUP) {
+      if constexpr (A8) {  // byte addressing of E4M3 codes (routed tiles only)
+        if (GATEUP) {
+          aoff[i] = src[i] * (uint32_t)a.d + 16 * lc;
+          const int qq = i >> 1;
+          const uint8_t* mat = ((qq & 1) == 0 ? w.f8gate : w.f8up) + (size_t)e * a.I * a.d;
+          bbase[i] = reinterpret_cast<const char*>(mat + (size_t)(nt * (kRowsMax / 2) + 64 * (qq >> 1)) * a.d);
+          boff[i] = (uint32_t)(row & 63) * (uint32_t)a.d + 16 * lc;
+        } else {
+          aoff[i] = (uint32_t)grow * (uint32_t)a.I + 16 * lc;
+          bbase[i] = reinterpret_cast<const char*>(w.f8down + ((size_t)e * a.d + (size_t)nt * kRowsMax) * a.I);
+          boff[i] = (uint32_t)(min(nt * kRowsMax + row, a.d - 1) - nt * kRowsMax) * (uint32_t)a.I + 16 * lc;
+        }
+      } else if (GATEUP) {
         aoff[i] = (src[i] * (uint32_t)a.d + 8 * lc) * 2u;
         const int qq = i >> 1;  // 64-row quarter of the tile
         const uint16_t* mat = (qq & 1) == 0 ? (routed ? w.gate + (size_t)e * a.I * a.d : w.s_gate)
@@ -463,6 +517,27 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
         }
       }
     }
+    // W8A8: the activation block scales of the lane's 4 row blocks (rows (2 j + wm) 32 +
+    // r32, clamped to the tile), one word per row per step (blocks 4 ks .. 4 ks + 3),
+    // loaded into registers one step ahead and double-buffered by step parity
+    uint32_t soff[kWaveBlocks];
+    uint32_t sreg[2][kWaveBlocks];
+    if constexpr (A8) {
+      const uint32_t bpr = (uint32_t)(K / 32);  // scale bytes per row
+#pragma unroll
+      for (int j = 0; j < kWaveBlocks; ++j) {
+        const int grow = ebase + m0 + min((2 * j + wm) * kBlk + r32, mrows - 1);
+        const uint32_t srow = GATEUP ? (uint32_t)a.perm_src[grow] / (uint32_t)a.k : (uint32_t)grow;
+        soff[j] = srow * bpr;
+      }
+    }
+    auto issue_s = [&](int ks, auto par_tag) __attribute__((always_inline)) {
+      if constexpr (A8) {
+#pragma unroll
+        for (int j = 0; j < kWaveBlocks; ++j)
+          sreg[decltype(par_tag)::value][j] = *reinterpret_cast<const uint32_t*>(a.as + soff[j] + 4 * ks);
+      }
+    };
     auto issue_f8 = [&](int ks, uint8_t* st) {
       uint8_t* dc = st + 1024 * wv;
 #pragma unroll
@@ -479,20 +554,21 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
         __builtin_amdgcn_global_load_lds((const void*)(cbase[i] + coff[i] + so), HY_LDS(dc + 1024 * i), 4, 0, 0);
     };
     // ops [I0, I1) of a step's activation / weight load group
+    // (a step is 128 bytes of every row: 64 bf16 values or 128 E4M3 codes)
     auto issue_a = [&](int ks, uint8_t* st, auto i0_tag, auto i1_tag) {
-      const int kk = ks * kBK;
+      const int kb = ks * kRowBytes;
       uint8_t* da = st + (64 * wv) * 16;
 #pragma unroll
       for (int i = decltype(i0_tag)::value; i < decltype(i1_tag)::value; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(abase + aoff[i] + 2 * kk), HY_LDS(da + kThreads * 16 * i), 16, 0,
+        __builtin_amdgcn_global_load_lds((const void*)(abase + aoff[i] + kb), HY_LDS(da + kThreads * 16 * i), 16, 0,
                                          0);
     };
     auto issue_b = [&](int ks, uint8_t* st, auto i0_tag, auto i1_tag) {
-      const int kk = ks * kBK;
+      const int kb = ks * kRowBytes;
       uint8_t* db = st + (64 * wv) * 16;
 #pragma unroll
       for (int i = decltype(i0_tag)::value; i < decltype(i1_tag)::value; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(bbase[i] + boff[i] + 2 * kk), HY_LDS(db + kThreads * 16 * i), 16,
+        __builtin_amdgcn_global_load_lds((const void*)(bbase[i] + boff[i] + kb), HY_LDS(db + kThreads * 16 * i), 16,
                                          0, 0);
     };
     using C0 = std::integral_constant<int, 0>;
@@ -510,6 +586,12 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
     // prologue: steps 0 and 1 of the weights, step 0 and the first half of step 1 of
     // the activations in flight (K >= 128 gives at least 2 steps), step 0 landed
     // everywhere; the rest of step 1 and the weights of step 2 follow in step 0
+    // W8A8: the scales of steps 0 and 1 go out first, fenced off: the counted wait below
+    // takes them as the oldest loads (were the compiler to place an ordinary load after
+    // the weights' direct-to-LDS loads, the count would leave some of those unwaited)
+    issue_s(0, std::integral_constant<int, 0>{});
+    issue_s(1, std::integral_constant<int, 1>{});
+    __builtin_amdgcn_sched_barrier(0);
     issue_a(0, sa0, C0{}, CF{});
     if constexpr (TERN) {
       issue_c(0, sb[0]);
@@ -531,6 +613,9 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
       constexpr int NACT = decltype(nact_tag)::value;
       uint4 fa[2][kWaveBlocks], fb[2][kNB];
       uint4 fc[2][kNB];  // FP8: the raw codes of a pair of groups, converted right before each group's MFMAs
+      // W8A8: 32 codes per lane per operand (two pieces), one buffer: each register is
+      // refilled with the next group's fragment right after the MFMA that last reads it
+      i32x8 fa8[kWaveBlocks], fb8[kNB];
       // The previous group's reads are waited for (long done: a whole MFMA group ran
       // since) before this group's are issued, so at most 8 are in flight and the
       // MFMAs that follow need no wait.
@@ -594,6 +679,51 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
 #pragma unroll
           for (int nb = 0; nb < kNB; ++nb) acc[j][nb] = mfma32x32x16(fb[s & 1][nb], fa[s & 1][j], acc[j][nb]);
       };
+      // W8A8 group S of a step of parity PAR: MFMAs column block major (nb, then row
+      // block j); the lane's activation scale for row block j is byte 2 S + hf of that
+      // step's scale word. With REFILL, fb8[nb] takes the fragment of group SN from
+      // (La, Lb) right after its last MFMA (row block NACT - 1), and fa8[j] right after
+      // column block kNB - 1's MFMA of row block j; NV vector-memory ops issued before the
+      // group are spread over its first MFMAs.
+      auto rd_a8 = [&](const uint8_t* La, int s, int j) __attribute__((always_inline)) {
+        const uint8_t* base = La + fa_off + j * 2 * kBlk * kRowBytes;
+        fa8[j] = lds_pair(base + a8o[s][0], base + a8o[s][1]);
+      };
+      auto rd_b8 = [&](const uint8_t* Lb, int s, int nb) __attribute__((always_inline)) {
+        const uint8_t* base = Lb + fb_off + nb * kBlk * kRowBytes;
+        fb8[nb] = lds_pair(base + a8o[s][0], base + a8o[s][1]);
+      };
+      auto group8 = [&](auto s_tag, auto par_tag, auto refill_tag, auto sn_tag, auto nv_tag, const uint8_t* La,
+                        const uint8_t* Lb) __attribute__((always_inline)) {
+        constexpr int S = decltype(s_tag)::value, PAR = decltype(par_tag)::value;
+        constexpr bool REFILL = decltype(refill_tag)::value;
+        constexpr int SN = decltype(sn_tag)::value, NV = decltype(nv_tag)::value;
+        if constexpr (NACT > 0) {
+          int one = 127;  // E8M0 1.0 for the weights (their fp32 row scales apply in the epilogue)
+          asm volatile("" : "+v"(one));
+          int sc[kWaveBlocks];
+#pragma unroll
+          for (int j = 0; j < NACT; ++j) sc[j] = (int)((sreg[PAR][j] >> (16 * S + 8 * hf)) & 0xFFu);
+          for_seq(std::make_integer_sequence<int, kNB>{}, [&](auto nb_tag) {
+            constexpr int NB = decltype(nb_tag)::value;
+            for_seq(std::make_integer_sequence<int, NACT>{}, [&](auto j_tag) {
+              constexpr int J = decltype(j_tag)::value;
+              acc[J][NB] = mfma32x32x64_f8(fb8[NB], fa8[J], acc[J][NB], one, sc[J]);
+              if constexpr (REFILL && J == NACT - 1) rd_b8(Lb, SN, NB);
+              if constexpr (REFILL && NB == kNB - 1) rd_a8(La, SN, J);
+            });
+          });
+          // MFMA m = NB NACT + J, then a vector-memory op (the first NV MFMAs), then the
+          // reads that follow it
+          for_seq(std::make_integer_sequence<int, kNB * NACT>{}, [&](auto m_tag) {
+            constexpr int M = decltype(m_tag)::value, NB = M / NACT, J = M % NACT;
+            constexpr int NR = REFILL ? 2 * ((J == NACT - 1) ? 1 : 0) + 2 * ((NB == kNB - 1) ? 1 : 0) : 0;
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if constexpr (M < NV) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+            if constexpr (NR > 0) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+          });
+        }
+      };
       auto mfmas = [&](int s) {
         if constexpr (FP8) {
 #pragma unroll
@@ -623,7 +753,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
         for_seq(std::integer_sequence<int, 1, 2, 3>{}, [&](auto s_tag) {
           constexpr int S = decltype(s_tag)::value;
           if constexpr (TERN)
-            read_frags_t(sa[UA], s_tag, ua_tag);  // ks % 2 == UA
+            read_frags_t(sa[UA], std::integral_constant<int, S>{}, ua_tag);  // ks % 2 == UA
           else
             read_frags(sa[UA], sb[UB], S);
           if constexpr (S == 1 && PA) issue_a(ks + 1, sa[UA ^ 1], CH{}, CF{});
@@ -673,29 +803,86 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
         }
         __builtin_amdgcn_sched_barrier(0);
       };
+      // W8A8 step ks: group 0 on fragments already in registers (refilling group 1's from
+      // this step's slots) with the second half of step ks+1's activations and step ks+2's
+      // weights issued over it; then the barrier that frees this step's slots and lands
+      // step ks+1's; group 1 refilling the next step's group 0; then the scales of step
+      // ks+2 into the parity's registers, which group 1 was the last to read.
+      auto step8 = [&](auto ua_tag, auto ub_tag, auto next_tag, auto pa_tag, auto pb_tag, int ks)
+                       __attribute__((always_inline)) {
+        constexpr int UA = decltype(ua_tag)::value;
+        constexpr int UB = decltype(ub_tag)::value;
+        constexpr bool NEXT = decltype(next_tag)::value;
+        constexpr bool PA = decltype(pa_tag)::value;
+        constexpr bool PB = decltype(pb_tag)::value;
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        if constexpr (PA) issue_a(ks + 1, sa[UA ^ 1], CH{}, CF{});
+        if constexpr (PB) issue_b(ks + 2, sb[(UB + 2) % BS], C0{}, CF{});
+        group8(I0{}, ua_tag, std::true_type{}, I1{}, std::integral_constant<int, (PA ? kDma / 2 : 0) + (PB ? kDma : 0)>{},
+               sa[UA], sb[UB]);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (NEXT) {
+          wait_vm<PB ? kBOps : 0>();  // all but step ks+2's weights (the newest)
+          wait_lds();
+          bare_barrier();
+          if constexpr (PB) issue_a(ks + 2, sa[UA], C0{}, CH{});
+          group8(I1{}, ua_tag, std::true_type{}, I0{}, std::integral_constant<int, PB ? kDma / 2 : 0>{}, sa[UA ^ 1],
+                 sb[(UB + 1) % BS]);
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (PB) issue_s(ks + 2, ua_tag);
+        } else {
+          group8(I1{}, ua_tag, std::false_type{}, I0{}, I0{}, nullptr, nullptr);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      };
       // whole periods of P = 6 steps (slots repeat with period 6), then the last R steps
       // (R = TAILR, or 6 when TAILR is 0), all with compile-time slots
       constexpr int P = 6;
       constexpr int R = TAILR == 0 ? P : TAILR;
-      if constexpr (TERN) {
-        read_codes(sb[0]);
-        read_frags_t(sa[0], std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-      } else {
-        read_frags(sa[0], sb[0], 0);
-      }
-      int k0 = 0;
-      for (; k0 + R < nks; k0 += P)
-        for_seq(std::make_integer_sequence<int, P>{}, [&](auto t) {
+      if constexpr (A8) {
+#pragma unroll
+        for (int j = 0; j < NACT; ++j) rd_a8(sa[0], 0, j);
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) rd_b8(sb[0], 0, nb);
+        int k0 = 0;
+        for (; k0 + R < nks; k0 += P)
+          for_seq(std::make_integer_sequence<int, P>{}, [&](auto t) {
+            constexpr int T = decltype(t)::value;
+            step8(std::integral_constant<int, T % 2>{}, std::integral_constant<int, T % 3>{}, std::true_type{},
+                  std::true_type{}, std::true_type{}, k0 + T);
+          });
+        // the next item's claim goes out before the last steps rather than inside the last
+        // one: a branch after the tail's MFMAs let the compiler sink them all below it,
+        // away from their fragment reads (every fragment of the tail live at once)
+        if (threadIdx.x == 0) own_ticket = atomicAdd(&counters[xcd], 1);
+        for_seq(std::make_integer_sequence<int, R>{}, [&](auto t) {
           constexpr int T = decltype(t)::value;
-          step(std::integral_constant<int, T % 2>{}, std::integral_constant<int, T % 3>{}, std::true_type{},
-               std::true_type{}, std::true_type{}, k0 + T);
+          step8(std::integral_constant<int, T % 2>{}, std::integral_constant<int, T % 3>{},
+                std::integral_constant<bool, (T + 1 < R)>{}, std::integral_constant<bool, (T + 1 < R)>{},
+                std::integral_constant<bool, (T + 2 < R)>{}, k0 + T);
         });
-      for_seq(std::make_integer_sequence<int, R>{}, [&](auto t) {
-        constexpr int T = decltype(t)::value;
-        step(std::integral_constant<int, T % 2>{}, std::integral_constant<int, T % 3>{},
-             std::integral_constant<bool, (T + 1 < R)>{}, std::integral_constant<bool, (T + 1 < R)>{},
-             std::integral_constant<bool, (T + 2 < R)>{}, k0 + T);
-      });
+      } else {
+        if constexpr (TERN) {
+          read_codes(sb[0]);
+          read_frags_t(sa[0], std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+        } else {
+          read_frags(sa[0], sb[0], 0);
+        }
+        int k0 = 0;
+        for (; k0 + R < nks; k0 += P)
+          for_seq(std::make_integer_sequence<int, P>{}, [&](auto t) {
+            constexpr int T = decltype(t)::value;
+            step(std::integral_constant<int, T % 2>{}, std::integral_constant<int, T % 3>{}, std::true_type{},
+                 std::true_type{}, std::true_type{}, k0 + T);
+          });
+        for_seq(std::make_integer_sequence<int, R>{}, [&](auto t) {
+          constexpr int T = decltype(t)::value;
+          step(std::integral_constant<int, T % 2>{}, std::integral_constant<int, T % 3>{},
+               std::integral_constant<bool, (T + 1 < R)>{}, std::integral_constant<bool, (T + 1 < R)>{},
+               std::integral_constant<bool, (T + 2 < R)>{}, k0 + T);
+        });
+      }
     };
     const int nact = min(kWaveBlocks, max(0, (nrb - wm + 1) >> 1));
     if (nact == 4)
@@ -723,6 +910,64 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
     // down kernel has no sb0/sb1 (its weight ring and the activation slots fill the LDS):
     // it stages pieces 0-1 (waves wn = 0), writes them out, then pieces 2-3, both in
     // sa0/sa1.
+    if constexpr (A8 && GATEUP) {
+      // W8A8 gate/up: h = silu(g) * u in fp32 (weight row scales from memory), quantized
+      // to MXFP8 per 32 hidden units of a row: the two lanes (r32, 0) and (r32, 1) hold a
+      // block's 32 values, so one exchange gives its largest magnitude. The codes are
+      // staged in sa0 (row r's 128 codes of the item, 16-byte chunk c at c ^ swz_key(r))
+      // and leave as 16-byte row segments; lane (r32, 0) writes the block's scale byte.
+      const size_t sbase = (size_t)e * a.I + nt * (kRowsMax / 2);
+      const int hbpr = a.I / 32;
+#pragma unroll
+      for (int j = 0; j < kWaveBlocks; ++j) {
+        const int rb = 2 * j + wm;
+        if (rb >= nrb) continue;  // wave-uniform
+        const int row = rb * kBlk + r32;
+#pragma unroll
+        for (int nb = 0; nb < kNB / 2; ++nb) {
+          float v[16];
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const int c0 = 64 * wn + 32 * nb + 8 * qd + 4 * hf;
+            float sg[4], su[4];  // (scales are only 4-byte aligned: one load each)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) sg[t] = w.f8sgate[sbase + c0 + t], su[t] = w.f8sup[sbase + c0 + t];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              v[4 * qd + t] = silu_fast(acc[j][nb][4 * qd + t] * sg[t]) * (acc[j][nb + kNB / 2][4 * qd + t] * su[t]);
+          }
+          float amax = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+          amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+          const int ex = mx_exponent(amax);
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const int chunk = 4 * wn + 2 * nb + (qd >> 1);
+            *reinterpret_cast<uint32_t*>(sa0 + row * kRowBytes + ((chunk ^ swz_key(row)) << 4) + 8 * (qd & 1) +
+                                         4 * hf) = mx_pack4(v[4 * qd], v[4 * qd + 1], v[4 * qd + 2], v[4 * qd + 3], ex);
+          }
+          if (hf == 0 && row < mrows)
+            a.hs[(size_t)(ebase + m0 + row) * hbpr + nt * 4 + 2 * wn + nb] = (uint8_t)(ex + 127);
+        }
+      }
+      wait_lds();
+      bare_barrier();
+      {
+        const int orow = tid >> 3, ch = tid & 7;
+        const uint32_t pl = (uint32_t)(orow * kRowBytes + ((ch ^ swz_key(orow)) << 4));
+        uint8_t* const ob = a.hq + (size_t)(ebase + m0 + orow) * a.I + nt * (kRowsMax / 2) + 16 * ch;
+        uint4 v[kRowsMax / 32];
+#pragma unroll
+        for (int it = 0; it < kRowsMax / 32; ++it) v[it] = *reinterpret_cast<const uint4*>(sa0 + pl + it * 32 * kRowBytes);
+#pragma unroll
+        for (int it = 0; it < kRowsMax / 32; ++it)
+          if (it * 32 + orow < mrows) *reinterpret_cast<uint4*>(ob + (size_t)it * 32 * a.I) = v[it];
+      }
+      wait_lds();
+      bare_barrier();
+      continue;
+    }
     constexpr int NPIECE = GATEUP ? 2 : 4;
     constexpr int ROUNDS = (FP8 && !GATEUP) ? 2 : 1;
     constexpr int PPR = NPIECE / ROUNDS;  // pieces staged per round
@@ -761,6 +1006,9 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
                 const uint2 u2 = *reinterpret_cast<const uint2*>(ssc + 2 * (c0 + kRowsMax / 2));
                 su[0] = bf_lo(u2.x), su[1] = bf_hi(u2.x), su[2] = bf_lo(u2.y), su[3] = bf_hi(u2.y);
               }
+            } else if constexpr (A8) {  // down: the output columns' row scales, from memory
+#pragma unroll
+              for (int t = 0; t < 4; ++t) sg[t] = w.f8sdown[(size_t)e * a.d + nt * kRowsMax + c0 + t];
             } else if constexpr (FP8) {
               const float4 g4 = *reinterpret_cast<const float4*>(ssc + 4 * c0);
               sg[0] = g4.x, sg[1] = g4.y, sg[2] = g4.z, sg[3] = g4.w;
@@ -773,7 +1021,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
               const int i = 4 * qd + t;
-              if constexpr (TERN || FP8)
+              if constexpr (TERN || FP8 || A8)
                 v[t] = GATEUP ? silu_fast(acc[j][nb][i] * sg[t]) * (acc[j][nb + kNB / 2][i] * su[t])
                               : acc[j][nb][i] * sg[t];
               else
@@ -813,7 +1061,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
   }
 }
 
-static int g_grid[6][64];  // persistent grid per (kernel kind, device), 0 = not yet computed
+static int g_grid[8][64];  // persistent grid per (kernel kind, device), 0 = not yet computed
 
 static int persistent_grid(int kind, const void* kernel) {
   int dev = 0;
@@ -830,12 +1078,12 @@ static int persistent_grid(int kind, const void* kernel) {
 
 using GemmKern = void (*)(GemmArgs, ExpertWeights, uint16_t*, uint16_t*);
 
-// kernel for (phase, weight format, K): indexed by (K / kBK) mod 6 / 2
+// kernel for (phase, weight format, K): indexed by (steps of K) mod 6 / 2
 template <bool GATEUP, int WF>
 static GemmKern pick_gemm(int K) {
   static const GemmKern k[3] = {grouped_gemm_kernel<GATEUP, 0, WF>, grouped_gemm_kernel<GATEUP, 2, WF>,
                                 grouped_gemm_kernel<GATEUP, 4, WF>};
-  return k[(K / kBK) % 6 / 2];
+  return k[(K / (WF == kGemmW8A8 ? kBK8 : kBK)) % 6 / 2];
 }
 
 static hipError_t launch_gemm(GemmKern kern, int kind, GemmArgs a, int sel, const ExpertWeights& w, const Plan& p,
@@ -848,8 +1096,22 @@ static hipError_t launch_gemm(GemmKern kern, int kind, GemmArgs a, int sel, cons
 
 hipError_t launch_grouped_experts(const Plan& p, const uint16_t* x, const ExpertWeights& w, hipStream_t s,
                                   Marks& m) {
-  GemmArgs a{x, p.perm_src, p.offs, p.meta, p.tiles, p.Tk, p.k, p.d, p.I, p.E, 0};
+  GemmArgs a{x, nullptr, nullptr, nullptr, nullptr, p.perm_src, p.offs, p.meta, p.tiles, p.Tk, p.k, p.d, p.I, p.E, 0};
   hipError_t err;
+  if (w.a8) {
+    // W8A8: the token rows to MXFP8, then the FP8-MFMA kernels over the routed tiles and
+    // the bf16 kernels over the shared expert's, per phase (the quantization is timed
+    // with gate/up)
+    err = launch_mx_quantize(x, p.T, p.d, p.xq, p.xs, s);
+    a.aq = p.xq, a.as = p.xs, a.hq = p.hq, a.hs = p.hs;
+    if (err == hipSuccess) err = launch_gemm(pick_gemm<true, kGemmW8A8>(p.d), 6, a, 1, w, p, s);
+    if (err == hipSuccess) err = launch_gemm(pick_gemm<true, kGemmBf16>(p.d), 0, a, 2, w, p, s);
+    if (err == hipSuccess) err = m.mark(s);
+    a.aq = p.hq, a.as = p.hs, a.hq = nullptr, a.hs = nullptr;
+    if (err == hipSuccess) err = launch_gemm(pick_gemm<false, kGemmW8A8>(p.I), 7, a, 1, w, p, s);
+    if (err == hipSuccess) err = launch_gemm(pick_gemm<false, kGemmBf16>(p.I), 1, a, 2, w, p, s);
+    return err == hipSuccess ? m.mark(s) : err;
+  }
   if (!w.ternary && !w.fp8) {
     err = launch_gemm(pick_gemm<true, kGemmBf16>(p.d), 0, a, 0, w, p, s);
     if (err == hipSuccess) err = m.mark(s);

@@ -19,6 +19,13 @@ TILE_ROWS = 256   # the grouped GEMM's largest M tile
 BLOCK_ROWS = 32   # its row-block granularity
 
 
+def f32_to_bf16_bits(a):
+    """Round fp32 -> bf16 (nearest even) as uint16 bit patterns (input preparation)."""
+    u = np.asarray(a, np.float32).view(np.uint32).astype(np.uint64)
+    u = u + 0x7FFF + ((u >> 16) & 1)
+    return (u >> 16).astype(np.uint16)
+
+
 def bf16_tensor_to_np(t):
     """bf16 torch tensor -> float64 numpy (exact)."""
     import torch
@@ -67,12 +74,91 @@ def check_weights(w_gpu, lg, sets):
     return err
 
 
-def check_out(out_gpu, ref):
-    rel = np.abs(out_gpu - ref) / (1.0 + np.abs(ref))
+def check_out(out_gpu, ref, extra=None):
+    """|out - ref| <= OUT_TOL (1 + |ref|) (+ extra, a per-element allowance, where given)."""
+    err = np.abs(out_gpu - ref)
+    tol = OUT_TOL * (1.0 + np.abs(ref)) + (0.0 if extra is None else extra)
+    rel = err / tol * OUT_TOL
     worst = float(rel.max()) if rel.size else 0.0
     assert np.isfinite(out_gpu).all()
     assert worst <= OUT_TOL, f"max |gpu-ref|/(1+|ref|) = {worst:.3e} > {OUT_TOL}"
-    return worst, float(np.abs(out_gpu - ref).mean()) if rel.size else 0.0
+    return worst, float(err.mean()) if rel.size else 0.0
+
+
+# MXFP8 hidden rows (W8A8). The two sides quantize fp32 hidden values that differ by
+# their sums' rounding, so a value lying that close to an E4M3 rounding boundary (or a
+# block maximum that close to a power of two) may take the neighbouring code (scale) on
+# the GPU: the quantization counterpart of a routing near tie. The GPU's hidden rows are
+# read back (hy_moe_args.hidden_codes/hidden_scales) and checked to be admissible: every
+# block scale is that of the block's largest oracle value moved by at most HID_REL, and
+# every value lies within half an E4M3 step (at its size) plus HID_REL |h| + HID_ABS amax
+# of the oracle's fp32 value. The oracle then recomputes the down projection from the
+# GPU's admissible codes, and outputs are compared under the usual tolerance.
+HID_REL = 2.0 ** -8
+HID_ABS = 2.0 ** -10
+HID_MAX_FLIP_FRACTION = 0.01
+
+
+def _block_exp(amax):
+    _, ex = np.frexp(amax)
+    return np.where(amax > 0, np.clip(ex - 9, -127, 127), -127)
+
+
+def check_hidden_rows(h32, gq, gs):
+    """h32 fp32 [n][I] (oracle), gq uint8 [n][I], gs uint8 [n][I / 32] (GPU). Asserts
+    admissibility; returns (codes differing from the oracle's own, blocks whose scale differs)."""
+    n, I = h32.shape
+    h = h32.astype(np.float64).reshape(n, I // 32, 32)
+    amax = np.abs(h).max(axis=2)
+    ge = gs.astype(np.int64) - 127
+    lo, hi = _block_exp(amax * (1 - HID_REL)), _block_exp(amax * (1 + HID_REL))
+    bad = ~((ge == lo) | (ge == hi))
+    if bad.any():
+        rows = np.argwhere(bad)
+        info = "; ".join(f"row {r} block {b}: gpu e={ge[r, b]} oracle amax {amax[r, b]:.6g} -> e in [{lo[r, b]}, "
+                         f"{hi[r, b]}]" for r, b in rows[:6])
+        raise AssertionError(f"{len(rows)} hidden block scales inadmissible (rows {sorted(set(rows[:, 0].tolist()))[:20]}, "
+                             f"blocks {sorted(set(rows[:, 1].tolist()))}): {info}")
+    scale = np.exp2(ge.astype(np.float64))[:, :, None]
+    vg = oracle.fp8_decode(gq.reshape(n, I)).reshape(n, I // 32, 32) * scale
+
+    def step(v):  # E4M3 spacing at |v| (in the block's units), doubled at the top of a binade
+        _, ex = np.frexp(np.minimum(np.abs(v) / scale, 448.0))
+        return np.exp2(np.maximum(ex - 1, -6) - 3) * scale
+
+    hc = np.clip(h, -448.0 * scale, 448.0 * scale)  # values past 448 saturate
+    dev = np.abs(vg - hc) - 0.5 * np.maximum(step(hc), step(vg)) - HID_REL * np.abs(h) - HID_ABS * amax[:, :, None]
+    sat = np.abs(h) >= 464.0 * scale * (1 + HID_REL)  # saturated on either side: exactly +-448
+    dev = np.where(sat, np.abs(vg - np.sign(h) * 448.0 * scale), dev)
+    worst = np.unravel_index(np.argmax(dev), dev.shape)
+    assert dev.max() <= 0, f"hidden value inadmissible at row {worst[0]}, unit {32 * worst[1] + worst[2]}: " \
+                           f"gpu {vg[worst]:.6g} oracle {h[worst]:.6g}"
+    oq, osc = oracle.mx_quantize(h32)
+    flips = int((oq != gq).sum())
+    assert flips <= HID_MAX_FLIP_FRACTION * gq.size + 1, f"{flips} of {gq.size} hidden codes differ"
+    return flips, int((osc != gs).sum())
+
+
+def gpu_hidden_rows(res, t, j, k):
+    """The GPU's hidden codes and scales of pair (token t, slot j) from a forward_layer
+    result (dispatched-row order: row p holds the pair perm_src[p])."""
+    perm = res["_perm_np"] if "_perm_np" in res else res["perm_src"].cpu().numpy()
+    res["_perm_np"] = perm
+    if "_pos_np" not in res:
+        pos = np.empty_like(perm)
+        pos[perm] = np.arange(perm.size, dtype=perm.dtype)
+        res["_pos_np"] = pos
+    p = res["_pos_np"][np.asarray(t) * k + np.asarray(j)]
+    return res["_hq_np"][p], res["_hs_np"][p]
+
+
+def hidden_to_np(res):
+    res["_hq_np"] = res["hidden_codes"].cpu().numpy()
+    res["_hs_np"] = res["hidden_scales"].cpu().numpy()
+
+
+def bf16_bits_to_f32(b):
+    return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
 def routing_to_np(res):

@@ -247,7 +247,42 @@ def test_noalloc_limit_stated_in_header():
     assert "#define HY_MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in text
     assert hm.NOALLOC_SCRATCH_BYTES == 64 << 20
     limit = int(re.search(r"that admits T <= (\d+)", text).group(1))
-    for fmt in (hm.WEIGHTS_BF16, hm.WEIGHTS_SHERRY_TERNARY, hm.WEIGHTS_FP8_E4M3):
-        assert hm.workspace_size(limit, 6144, 256, 8, 2048, fmt) <= hm.NOALLOC_SCRATCH_BYTES
-        assert hm.workspace_size(limit + 1, 6144, 256, 8, 2048, fmt) > hm.NOALLOC_SCRATCH_BYTES
+    limit8 = int(re.search(r"\(T <= (\d+) with\s+\*\s+HY_MOE_WEIGHTS_FP8_W8A8", text).group(1))
+    for fmt, lim in ((hm.WEIGHTS_BF16, limit), (hm.WEIGHTS_SHERRY_TERNARY, limit), (hm.WEIGHTS_FP8_E4M3, limit),
+                     (hm.WEIGHTS_FP8_W8A8, limit8)):
+        assert hm.workspace_size(lim, 6144, 256, 8, 2048, fmt) <= hm.NOALLOC_SCRATCH_BYTES
+        assert hm.workspace_size(lim + 1, 6144, 256, 8, 2048, fmt) > hm.NOALLOC_SCRATCH_BYTES
+
+
+def test_fp8_w8a8_argument_checks():
+    a = base_args(T=4, d=512, E=16, k=2, I=256)
+    a.expert_format = hm.WEIGHTS_FP8_W8A8
+    a.W_gate = a.W_up = a.W_down = None
+    a.Wq_gate = a.Wq_up = a.Wq_down = a.S_gate = a.S_up = a.S_down = FAKE
+    a.workspace = FAKE
+    a.workspace_bytes = hm.workspace_size(4, 512, 16, 2, 256, hm.WEIGHTS_FP8_W8A8) - 1
+    assert call(a) == hm.ERR_WORKSPACE
+    a.workspace, a.workspace_bytes = None, 0
+    a.path = hm.PATH_STREAM
+    assert call(a) == hm.ERR_UNSUPPORTED              # grouped path only
+    a.path = hm.PATH_AUTO
+    a.d = 384
+    assert call(a) == hm.ERR_UNSUPPORTED              # d % 256
+    a.d, a.I = 512, 128
+    assert call(a) == hm.ERR_UNSUPPORTED              # I % 256
+    a.I = 256
+    a.S_down = FAKE + 2
+    assert call(a) == hm.ERR_INVALID_ARG
+    # the W8A8 workspace holds the MXFP8 rows: larger than the weight-only FP8 one at prefill
+    # sizes would be without its bf16 expert outputs
+    assert hm.workspace_size(8192, 6144, 256, 8, 2048, hm.WEIGHTS_FP8_W8A8) > 0
+
+
+def test_mxfp8_quantize_argument_checks():
+    L = hm.lib()
+    assert L.hy_moe_mxfp8_quantize(FAKE, 4, 48, FAKE, FAKE, None) == hm.ERR_INVALID_ARG   # cols % 32
+    assert L.hy_moe_mxfp8_quantize(FAKE, -1, 64, FAKE, FAKE, None) == hm.ERR_INVALID_ARG
+    assert L.hy_moe_mxfp8_quantize(None, 4, 64, FAKE, FAKE, None) == hm.ERR_INVALID_ARG
+    assert L.hy_moe_mxfp8_quantize(FAKE + 8, 4, 64, FAKE, FAKE, None) == hm.ERR_INVALID_ARG
+    assert L.hy_moe_mxfp8_quantize(FAKE, 0, 64, None, None, None) == hm.OK              # empty: no-op
 

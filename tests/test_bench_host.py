@@ -110,3 +110,14 @@ def test_prefill_flops():
     assert w["layer_flop"] == 2 * 8192 * 6144 * 256 + w["rows"] * 3 * 2 * 6144 * 2048
     # a different expert format changes the kernel, not the flop count
     assert bench.gemm_work(dataclasses.replace(cfg, fp8=True))["alg"] == w["alg"]
+
+
+def test_w8a8_blended_peak():
+    # routed rows run on FP8 MFMAs (5.0 PFLOP/s), shared rows on bf16 ones (2.5): with
+    # 8 routed rows per shared row the stage's peak is 9 / (8 / 5.0 + 1 / 2.5) PFLOP/s
+    cfg = hi.CONFIGS["fp8_w8a8_prefill"]
+    w = bench.gemm_work(cfg)
+    assert w["alg"] == bench.gemm_work(hi.CONFIGS["prefill"])["alg"]
+    assert abs(w["peak"] - 9 / (8 / 5.0e15 + 1 / 2.5e15)) < 1e3
+    assert bench.PEAK_BF16 < w["layer_peak"] < bench.PEAK_FP8
+    assert bench.gemm_work(hi.CONFIGS["prefill"])["peak"] == bench.PEAK_BF16

@@ -8,6 +8,7 @@ path choice, caller workspace):
   ternary_prefill  T=8192, the same weights on the grouped path
   fp8      T=32,   FP8 (E4M3, fp32 row scales) routed experts, bf16 shared expert
   fp8_prefill  T=8192, the same weights on the grouped path
+  fp8_w8a8, fp8_w8a8_prefill  T=32 and T=8192, the same weights with MXFP8 activations
 The routing of every token (sets, weights, counts, offsets, permutation) is
 compared with the oracle. Outputs: every token of the decode batches; at
 prefill sizes a sample chosen from the routing so that it covers the grouped
@@ -23,7 +24,7 @@ import pytest
 import hy_inputs as hi
 import oracle
 from parity import (bf16_tensor_bits, bf16_tensor_to_np, check_out, check_permutation, check_routing,
-                    check_weights, routing_to_np, tile_sample)
+                    check_weights, routing_to_np, tile_sample, check_hidden_rows, gpu_hidden_rows, hidden_to_np)
 
 torch = pytest.importorskip("torch")
 hm = pytest.importorskip("sparse_moe_transformer_route_amd")
@@ -66,7 +67,7 @@ class DeviceExperts:
         return tuple(bf16_tensor_bits(inp[n][e]) for n in ("gate", "up", "down")), False
 
 
-def reference_outputs(cfg, inp, x_host, sets, w, tokens):
+def reference_outputs(cfg, inp, x_host, sets, w, tokens, gpu_res=None):
     """Oracle outputs of `tokens`: the shared expert, then each routed expert the
     tokens use, one expert's weights at a time, combined in fp64."""
     sh = {n: bf16_tensor_bits(v) for n, v in inp["shared"].items()}
@@ -77,21 +78,37 @@ def reference_outputs(cfg, inp, x_host, sets, w, tokens):
         for j, e in enumerate(sets[t]):
             by_expert.setdefault(int(e), []).append((i, j))
     src = DeviceExperts(inp)
+    flips = [0, 0]
     for e, pairs in sorted(by_expert.items()):
         (gate, up, down), w64 = src.get(e)
         rows = x_host[[tokens[i] for i, _ in pairs]]
-        y = (oracle.ffn_w64 if w64 else oracle.ffn)(rows, gate, up, down)
+        if cfg.a8:
+            # the GPU's hidden rows must be admissible; the oracle's down projection runs on
+            # them (tests/parity.py)
+            _, h32 = oracle.ffn_w8a8_ex(rows, gate, up, down, want_hidden=True)
+            gq, gs = gpu_hidden_rows(gpu_res, [tokens[i] for i, _ in pairs], [j for _, j in pairs], cfg.k)
+            f1, f2 = check_hidden_rows(h32, gq, gs)
+            flips[0] += f1
+            flips[1] += f2
+            y = oracle.ffn_w8a8_ex(rows, gate, up, down, hq=gq, hs=gs)
+        else:
+            y = (oracle.ffn_w64 if w64 else oracle.ffn)(rows, gate, up, down)
         for (i, j), yy in zip(pairs, y):
             yr[i, j] = yy
+    if cfg.a8:
+        say(f"       hidden rows admissible: {flips[0]} codes and {flips[1]} block scales substituted")
     return oracle.combine(ys, yr, w[tokens])
 
 
 def run_full(cfg, inp, sample="all"):
     say(f"[case] {cfg.name} T={cfg.T} full-size")
-    fmt = hm.WEIGHTS_SHERRY_TERNARY if cfg.ternary else hm.WEIGHTS_FP8_E4M3 if cfg.fp8 else hm.WEIGHTS_BF16
+    fmt = (hm.WEIGHTS_SHERRY_TERNARY if cfg.ternary else
+           (hm.WEIGHTS_FP8_W8A8 if cfg.a8 else hm.WEIGHTS_FP8_E4M3) if cfg.fp8 else hm.WEIGHTS_BF16)
     ws = hm.alloc_workspace(cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, fmt, device=DEV)
-    res = hm.forward_layer(inp, cfg.k, want_routing=True, workspace=ws)
+    res = hm.forward_layer(inp, cfg.k, want_routing=True, workspace=ws, fp8_activations=cfg.a8, want_hidden=cfg.a8)
     torch.cuda.synchronize()
+    if cfg.a8:
+        hidden_to_np(res)
     g = routing_to_np(res)
     out = bf16_tensor_to_np(res["out"])
     assert np.isfinite(out).all()
@@ -111,7 +128,7 @@ def run_full(cfg, inp, sample="all"):
         tokens, why = tile_sample(cfg, g)
     say(f"       comparing {len(tokens)} tokens: {why}")
     w_ref = oracle.weights(lg, sets)
-    ref = reference_outputs(cfg, inp, x_host, sets, w_ref, tokens)
+    ref = reference_outputs(cfg, inp, x_host, sets, w_ref, tokens, gpu_res=res)
     worst, mean = check_out(out[tokens], ref)
     say(f"       outputs ok: max_rel_err={worst:.3e} mean_abs_err={mean:.3e} ({time.time() - t0:.1f}s)")
     return res, g, tokens
@@ -172,6 +189,16 @@ def test_fp8_prefill_full_size():
     cfg = hi.CONFIGS["fp8_prefill"]
     inp = hi.dev_layer(cfg, device=DEV)
     run_full(cfg, inp, sample="tiles")
+    del inp
+    torch.cuda.empty_cache()
+
+
+def test_fp8_w8a8_full_size():
+    # decode batch and prefill batch on the same FP8 weights with MXFP8 activations
+    cfg = hi.CONFIGS["fp8_w8a8"]
+    inp = hi.dev_layer(hi.CONFIGS["fp8_w8a8_prefill"], device=DEV)
+    run_full(cfg, with_x(cfg, inp))
+    run_full(hi.CONFIGS["fp8_w8a8_prefill"], inp, sample="tiles")
     del inp
     torch.cuda.empty_cache()
 

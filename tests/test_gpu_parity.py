@@ -12,7 +12,8 @@ import pytest
 
 import hy_inputs as hi
 import oracle
-from parity import (bf16_tensor_bits, bf16_tensor_to_np, check_out, check_permutation, check_routing,
+from parity import (bf16_tensor_bits, bf16_tensor_to_np, check_out, check_permutation, check_routing, f32_to_bf16_bits,
+                    check_hidden_rows, gpu_hidden_rows, hidden_to_np,
                     check_weights, routing_to_np)
 
 torch = pytest.importorskip("torch")
@@ -39,7 +40,7 @@ def host_weights_bf16(cfg, L):
 def run_small(cfg, path, bias=None, x_host=None, label="", fp8_codes=None):
     """Full element-by-element comparison on a small layer."""
     say(f"[case] {label or cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} I={cfg.I} "
-        f"ternary={cfg.ternary} fp8={cfg.fp8} path={path}")
+        f"ternary={cfg.ternary} fp8={cfg.fp8} w8a8={cfg.a8} path={path}")
     L = hi.host_layer(cfg)
     inp = hi.dev_layer(cfg, device=DEV)
     if fp8_codes is not None:  # caller-chosen codes and scales
@@ -52,7 +53,7 @@ def run_small(cfg, path, bias=None, x_host=None, label="", fp8_codes=None):
     if x_host is not None:
         L["x"] = x_host
         inp["x"] = torch.from_numpy(x_host.view(np.int16)).to(DEV).view(torch.bfloat16)
-    res = hm.forward_layer(inp, cfg.k, want_routing=True, path=path)
+    res = hm.forward_layer(inp, cfg.k, want_routing=True, path=path, fp8_activations=cfg.a8, want_hidden=cfg.a8)
     torch.cuda.synchronize()
     g = routing_to_np(res)
     lg = oracle.logits(L["x"], L["router"], L["bias"])
@@ -62,12 +63,31 @@ def run_small(cfg, path, bias=None, x_host=None, label="", fp8_codes=None):
     if cfg.fp8:
         fw = [np.stack([oracle.fp8_decode(L["f" + m][e], L["fs" + m][e]) for e in range(cfg.E)])
               for m in ("gate", "up", "down")]
-        ref = oracle.forward_w64(L["x"], L["router"], L["bias"], *fw, L["shared"]["gate"], L["shared"]["up"],
-                                 L["shared"]["down"], cfg.k, sets_in=sets)
+        fwd = oracle.forward_w8a8 if cfg.a8 else oracle.forward_w64
+        ref = fwd(L["x"], L["router"], L["bias"], *fw, L["shared"]["gate"], L["shared"]["up"], L["shared"]["down"],
+                  cfg.k, sets_in=sets)
     else:
         gate, up, down = host_weights_bf16(cfg, L)
         ref = oracle.forward(L["x"], L["router"], L["bias"], gate, up, down, L["shared"]["gate"], L["shared"]["up"],
                              L["shared"]["down"], cfg.k, sets_in=sets)
+    if cfg.a8:
+        # the GPU's hidden rows must be admissible quantizations of the oracle's; the
+        # oracle's down projection then runs on them (tests/parity.py)
+        hidden_to_np(res)
+        yr = np.zeros((cfg.T, cfg.k, cfg.d))
+        flips = sflips = 0
+        for e in range(cfg.E):
+            tk, slot = np.nonzero(sets == e)
+            if not tk.size:
+                continue
+            _, h32 = oracle.ffn_w8a8_ex(L["x"][tk], fw[0][e], fw[1][e], fw[2][e], want_hidden=True)
+            gq, gs = gpu_hidden_rows(res, tk, slot, cfg.k)
+            f1, f2 = check_hidden_rows(h32, gq, gs)
+            flips, sflips = flips + f1, sflips + f2
+            yr[tk, slot] = oracle.ffn_w8a8_ex(L["x"][tk], fw[0][e], fw[1][e], fw[2][e], hq=gq, hs=gs)
+        ys = oracle.ffn(L["x"], L["shared"]["gate"], L["shared"]["up"], L["shared"]["down"])
+        ref["out"] = oracle.combine(ys, yr, ref["w"])
+        say(f"       hidden rows admissible: {flips} codes and {sflips} block scales substituted")
     worst, mean = check_out(bf16_tensor_to_np(res["out"]), ref["out"])
     # margins: fp32 GPU margin vs fp64 oracle margin
     fin = np.isfinite(ref["margin"])
@@ -248,6 +268,81 @@ def test_fp8_every_code(path):
     touched = int((res["counts"] > 0).sum().item())
     say(f"       experts touched: {touched} of 256")
     assert touched >= 240
+
+
+# ------------------------------------------------- FP8 W8A8 (MXFP8 activations)
+def test_mxfp8_quantize_bit_exact():
+    # codes and scales of the C-ABI quantizer against the oracle's, bit for bit, on rows
+    # of very different magnitudes (subnormal codes, saturation, zero blocks, +-0)
+    say("[case] hy_moe_mxfp8_quantize vs oracle")
+    rng = np.random.default_rng(31)
+    rows, cols = 257, 2048
+    v = rng.standard_normal((rows, cols)) * np.exp2(rng.integers(-40, 40, (rows, 1)))
+    v[5, :64] = 0.0
+    v[6, :32] = -0.0
+    v[7, :32] = np.exp2(-np.arange(32, dtype=np.float64))  # spans the subnormal range of its block
+    v[8, 32:64] = [448.0, 449.0, 463.9, 464.0, 480.0, 500.0] + [1.0] * 26  # saturation ties
+    xb = f32_to_bf16_bits(v.astype(np.float32))
+    xt = torch.from_numpy(xb.view(np.int16)).to(DEV).view(torch.bfloat16)
+    codes, scales = hm.mxfp8_quantize(xt)
+    torch.cuda.synchronize()
+    rq, rs = oracle.mx_quantize(hi.bf16_to_f32(xb))
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    got = codes.cpu().numpy()
+    bad = np.argwhere(got != rq)
+    assert bad.size == 0, f"{len(bad)} codes differ, first {bad[:3].tolist()}: gpu {got[tuple(bad[0])]:#x} " \
+                          f"oracle {rq[tuple(bad[0])]:#x}"
+
+
+W8A8_SHAPES = [
+    # K / 128 mod 6 picks the k-loop tail (gate/up: d, down: I); d, I multiples of 256
+    dict(T=64, d=256, E=16, k=2, I=256),      # one 32-row block per expert; 2 k steps each (tails 2, 2)
+    dict(T=300, d=768, E=8, k=2, I=512),      # ragged tiles; 6 steps (a whole period) and 4
+    dict(T=1100, d=512, E=4, k=1, I=256),     # two M tiles per expert (275 rows)
+    dict(T=200, d=1536, E=16, k=4, I=768),    # 12 steps (two periods) and 6
+]
+
+
+W8A8_SHAPES += [
+    dict(T=200, d=512, E=16, k=2, I=256),     # gate/up 4 steps (tail 4), one M tile per expert
+    dict(T=1100, d=768, E=4, k=1, I=256),     # two M tiles per expert, gate/up 6 steps
+]
+
+
+@pytest.mark.parametrize("shape", W8A8_SHAPES)
+def test_fp8_w8a8_small(shape):
+    cfg = hi.LayerConfig("w8a8", fp8=True, a8=True, seed=10, **shape)
+    run_small(cfg, hm.PATH_AUTO)
+
+
+def test_fp8_w8a8_routes_like_weight_only_fp8():
+    # the same FP8 weights with bf16 and MXFP8 activations: identical routing, outputs that
+    # differ by the activation quantization only (a few percent, not more)
+    cfg = hi.LayerConfig("w8a8cmp", T=256, d=1024, E=32, k=4, I=512, fp8=True, seed=11)
+    inp = hi.dev_layer(cfg, device=DEV)
+    a = hm.forward_layer(inp, cfg.k, want_routing=True, path=hm.PATH_GROUPED)
+    b = hm.forward_layer(inp, cfg.k, want_routing=True, fp8_activations=True)
+    torch.cuda.synchronize()
+    for key in ("topk_idx", "topk_w", "counts", "offsets", "perm_src", "margin"):
+        assert torch.equal(a[key], b[key]), key
+    fa, fb = a["out"].float(), b["out"].float()
+    rel = ((fa - fb).abs() / (1 + fa.abs()))
+    say(f"       W8A8 vs weight-only FP8: max rel difference {rel.max().item():.3e}, rms {rel.pow(2).mean().sqrt().item():.3e}")
+    # E4M3 activations: about 2^-4 relative rounding per value, averaging over each sum
+    assert 1e-4 < rel.pow(2).mean().sqrt().item() < 0.06 and rel.max().item() < 0.3
+
+
+def test_fp8_w8a8_rejects_stream_path_and_odd_shapes():
+    cfg = hi.LayerConfig("w8a8bad", T=16, d=384, E=8, k=2, I=256, fp8=True, seed=12)
+    inp = hi.dev_layer(cfg, device=DEV)
+    with pytest.raises(hm.HyMoeError) as e:
+        hm.forward_layer(inp, cfg.k, fp8_activations=True)  # d % 256 != 0
+    assert e.value.status == hm.ERR_UNSUPPORTED
+    cfg = hi.LayerConfig("w8a8s", T=16, d=256, E=8, k=2, I=256, fp8=True, seed=12)
+    inp = hi.dev_layer(cfg, device=DEV)
+    with pytest.raises(hm.HyMoeError) as e:
+        hm.forward_layer(inp, cfg.k, fp8_activations=True, path=hm.PATH_STREAM)
+    assert e.value.status == hm.ERR_UNSUPPORTED
 
 
 # ------------------------------------------------------------- determinism

@@ -594,6 +594,31 @@ def test_ffn_w8a8_composition():
     assert not np.allclose(oracle.ffn_w8a8(x, wu, wg, wd), got)
 
 
+def test_ffn_w8a8_hidden_rows_and_substitution():
+    rng = np.random.default_rng(25)
+    n, d, I = 2, 64, 96
+    x = f32_to_bf16_bits(rng.standard_normal((n, d)))
+    wg, wu, wd = _fp8_expert(rng, I, d)
+    y0 = oracle.ffn_w8a8(x, wg, wu, wd)
+    y, h32 = oracle.ffn_w8a8_ex(x, wg, wu, wd, want_hidden=True)
+    assert np.array_equal(y, y0) and h32.dtype == np.float32
+    # the hidden rows are fp32 of the composition's silu(g) * u
+    xq = mx_values(*oracle.mx_quantize(bf(x).astype(np.float32)))
+    g, u = xq @ wg.T, xq @ wu.T
+    assert np.allclose(h32, (np_silu(g) * u).astype(np.float32), rtol=1e-6, atol=1e-30)
+    # substituting the oracle's own codes changes nothing; one code one step up moves the
+    # output by that column of W_down times the step, exactly as the values say
+    hq, hs = oracle.mx_quantize(h32)
+    assert np.array_equal(oracle.ffn_w8a8_ex(x, wg, wu, wd, hq=hq, hs=hs), y)
+    i = int(np.argmax(np.abs(h32[0]) < 400 * np.exp2(hs[0, 0] - 127.0)))  # a non-saturated code in block 0
+    hq2 = hq.copy()
+    hq2[0, i] = hq[0, i] + 1 if hq[0, i] & 0x7F < 0x7E else hq[0, i] - 1
+    y2 = oracle.ffn_w8a8_ex(x, wg, wu, wd, hq=hq2, hs=hs)
+    dv = (mx_values(hq2, hs) - mx_values(hq, hs))[0, i]
+    assert dv != 0 and np.allclose(y2[0] - y[0], wd[:, i] * dv, rtol=1e-6, atol=1e-12 * np.abs(y).max())
+    assert np.array_equal(y2[1], y[1])
+
+
 def test_forward_w8a8_matches_dense_masked_numpy():
     cfg, L = small_layer(seed=5, T=12, d=64, E=6, k=2, I=32, bias=True)
     rng = np.random.default_rng(24)
