@@ -242,6 +242,19 @@ def gemm_work(cfg):
                          f"at their peaks" if cfg.a8 else "bf16 dense MFMA peak")}
 
 
+def measured_peak_of(roof, peaks):
+    """The rate this GPU measured for a roofline's bound: HBM read for bytes, the bf16
+    MFMA probe for flops, and for a W8A8 stage its rows at the FP8 and bf16 probes'
+    rates combined as the published peaks are."""
+    if roof["unit"] == "GB/s":
+        return peaks["hbm_read_gbs"]
+    mix = roof.get("peak_mix")
+    if mix is None:
+        return peaks["mfma_bf16_tflops"]
+    return (mix["fp8_rows"] + mix["bf16_rows"]) / (mix["fp8_rows"] / peaks["mfma_fp8_tflops"] +
+                                                   mix["bf16_rows"] / peaks["mfma_bf16_tflops"])
+
+
 def input_digest(inp, torch):
     """sha256 (first 16 hex digits) of the step's inputs that are not regenerated by
     stream id alone: x, the router weights and the bias, plus the first routed expert's
@@ -300,6 +313,8 @@ def run_config(name, args, hi, hm, torch, weights=None, steps=None, flush=None):
                 "frac": alg / sec / gw["peak"], "traffic": traffic_for(f"grouped_gemm_gateup/{name}", rows),
                 "kernel": gw["kernel"], "per_unit": gw["per_unit"], "units_per_launch": rows, "kernel_ms": dom_ms,
                 "peak_how": gw["peak_how"]}
+        if cfg.a8:
+            roof["peak_mix"] = {"fp8_rows": cfg.T * cfg.k, "bf16_rows": cfg.T}
     roof["kernel_source_sha256_16"] = source_digest(os.path.join(ROOT, kernel_file))
     res = {"cfg": cfg, "inp": inp, "ms": ms, "tokens_per_s": cfg.T / (ms * 1e-3), "kernels_ms": r["kernels"],
            "roofline": roof, "layer": layer, "touched": touched, "counts": counts, "routing": routing,
@@ -605,10 +620,14 @@ def main():
         ops = torch.randn(hm.PROBE_OPERAND_BYTES // 2, generator=gen, device="cuda:0").to(torch.bfloat16)
         read_buf = shared_weights["gate"] if shared_weights is not None else torch.empty(
             4 << 30, dtype=torch.uint8, device="cuda:0")
-        peaks = {"mfma_bf16_tflops": hm.probe_mfma_bf16(ops), "hbm_read_gbs": hm.probe_hbm_read(read_buf),
+        codes = ops.float().to(torch.float8_e4m3fn).view(torch.uint8)
+        codes = torch.cat([codes, codes])  # E4M3 codes of the same values: PROBE_OPERAND_BYTES of them
+        peaks = {"mfma_bf16_tflops": hm.probe_mfma_bf16(ops), "mfma_fp8_tflops": hm.probe_mfma_fp8(codes),
+                 "hbm_read_gbs": hm.probe_hbm_read(read_buf),
                  "hbm_read_bytes": read_buf.numel() * read_buf.element_size(),
                  "how": "hy_moe_probe_mfma_bf16 (32x32x16 bf16 MFMAs, 4 workgroups per CU, random N(0,1) operands, "
-                        "~40 ms) and hy_moe_probe_hbm_read (best of three timed streaming passes of 16-byte loads "
+                        "~40 ms), hy_moe_probe_mfma_fp8 (32x32x64 E4M3 MFMAs with unit block scales on the same "
+                        "values as E4M3 codes, ~40 ms) and hy_moe_probe_hbm_read (best of three timed streaming passes of 16-byte loads "
                         "after an untimed one)"}
         del read_buf
         if full:
@@ -662,15 +681,9 @@ def main():
         torch.cuda.empty_cache()
 
     roof = main_res["roofline"]
-    if peaks is not None and (roof["unit"] == "GB/s" or roof["peak_how"].startswith("bf16")):
-        meas = peaks["hbm_read_gbs"] if roof["unit"] == "GB/s" else peaks["mfma_bf16_tflops"]
-        roof["frac_of_measured_peak"] = roof["achieved"] / meas
-        for o in extra.values():
-            r = o["roofline"]
-            if r["unit"] == "TFLOP/s" and not r["peak_how"].startswith("bf16"):
-                continue  # no measured FP8 rate to set it against
-            r["frac_of_measured_peak"] = r["achieved"] / (peaks["hbm_read_gbs"] if r["unit"] == "GB/s"
-                                                          else peaks["mfma_bf16_tflops"])
+    if peaks is not None:
+        for r in [roof] + [o["roofline"] for o in extra.values()]:
+            r["frac_of_measured_peak"] = r["achieved"] / measured_peak_of(r, peaks)
             if r["unit"] == "TFLOP/s" and "library_gemm_bf16" in peaks:
                 r["frac_of_library_dense_gemm"] = r["achieved"] / peaks["library_gemm_bf16"]["tflops"]
 

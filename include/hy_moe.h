@@ -258,12 +258,16 @@ int hy_moe_mxfp8_quantize(const void* x, int64_t rows, int64_t cols, void* codes
  *   values give the rate of real data: under the power cap the clock depends on
  *   operand bit activity). Writes TFLOP/s (2 flop per multiply-add) to *tflops
  *   (HOST).
+ * hy_moe_probe_mfma_fp8: the same with 32x32x64 E4M3 MFMAs (block scales of 1.0) for
+ *   about 40 ms at the FP8 rate. operands: as above, filled with E4M3 codes (finite
+ *   values: random bytes include NaN codes). 2 flop per multiply-add.
  * hy_moe_probe_hbm_read: reads buf (DEVICE, 16-byte aligned, `bytes` >= 16; use
  *   much more than the 256 MB last-level cache) once untimed, then three times timed
  *   with 16-byte loads. Writes the best pass's GB/s (1e9 B/s) to *gbps (HOST).
  */
 #define HY_MOE_PROBE_OPERAND_BYTES 65536
 int hy_moe_probe_mfma_bf16(const void* operands, size_t operand_bytes, float* tflops, void* stream);
+int hy_moe_probe_mfma_fp8(const void* operands, size_t operand_bytes, float* tflops, void* stream);
 int hy_moe_probe_hbm_read(const void* buf, size_t bytes, float* gbps, void* stream);
 
 /*

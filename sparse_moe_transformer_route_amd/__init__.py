@@ -31,7 +31,7 @@ KERNELS = ["route_logits", "route_topk", "permute_scan", "permute_scatter", "exp
 NUM_STAGE_EVENTS = len(KERNELS) + 1
 
 EXPORTED = ["hy_moe_forward", "hy_moe_forward_ex", "hy_moe_forward_noalloc", "hy_moe_workspace_size",
-            "hy_moe_status_string", "hy_moe_sherry_pack_host", "hy_moe_mxfp8_quantize", "hy_moe_probe_mfma_bf16", "hy_moe_probe_hbm_read",
+            "hy_moe_status_string", "hy_moe_sherry_pack_host", "hy_moe_mxfp8_quantize", "hy_moe_probe_mfma_bf16", "hy_moe_probe_mfma_fp8", "hy_moe_probe_hbm_read",
             "hy_indexer_workspace_size", "hy_indexer_topk"]
 PROBE_OPERAND_BYTES = 65536
 NOALLOC_SCRATCH_BYTES = 64 << 20  # HY_MOE_NOALLOC_SCRATCH_BYTES
@@ -85,6 +85,8 @@ def _load():
     L.hy_moe_mxfp8_quantize.restype = ctypes.c_int
     L.hy_moe_probe_mfma_bf16.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_float), vp]
     L.hy_moe_probe_mfma_bf16.restype = ctypes.c_int
+    L.hy_moe_probe_mfma_fp8.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_float), vp]
+    L.hy_moe_probe_mfma_fp8.restype = ctypes.c_int
     L.hy_moe_probe_hbm_read.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_float), vp]
     L.hy_moe_probe_hbm_read.restype = ctypes.c_int
     L.hy_indexer_workspace_size.argtypes = [i64, i64]
@@ -268,6 +270,17 @@ def probe_mfma_bf16(operands, stream=None) -> float:
                                      ctypes.byref(tf), _stream(stream))
     if rc != OK:
         raise HyMoeError(rc, "hy_moe_probe_mfma_bf16")
+    return tf.value
+
+
+def probe_mfma_fp8(operands, stream=None) -> float:
+    """hy_moe_probe_mfma_fp8: TFLOP/s of dense E4M3 MFMAs (32x32x64, block scales 1.0)
+    on the given codes (a device tensor of at least PROBE_OPERAND_BYTES bytes)."""
+    tf = ctypes.c_float()
+    rc = _lib.hy_moe_probe_mfma_fp8(operands.data_ptr(), operands.numel() * operands.element_size(),
+                                    ctypes.byref(tf), _stream(stream))
+    if rc != OK:
+        raise HyMoeError(rc, "hy_moe_probe_mfma_fp8")
     return tf.value
 
 

@@ -46,6 +46,18 @@ __device__ __forceinline__ f32x16 mfma32x32x16(uint4 a, uint4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// D[32x32] += A[32x64] B[64x32] on E4M3 codes with E8M0 block scales sa (A) and sb (B)
+// (byte 0 of each; 127 = 1). Lane (r, h) holds row / column r: bytes 0-15 are k
+// [16h, 16h + 16) and bytes 16-31 are k [32 + 16h, 32 + 16h + 16) of the 64, and the scale
+// of 32-k block b of row / column r comes from lane (r, b). D as the bf16 32x32 MFMA.
+__device__ __forceinline__ f32x16 mfma32x32x64_f8(i32x8 a, i32x8 b, f32x16 c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
 // Streaming load of data read exactly once (expert weights): non-temporal hint.

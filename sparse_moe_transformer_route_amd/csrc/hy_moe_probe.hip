@@ -1,4 +1,4 @@
-// Machine-peak probes: the bf16 MFMA rate and the HBM read rate this GPU reaches,
+// Machine-peak probes: the bf16 and FP8 MFMA rates and the HBM read rate this GPU reaches,
 // measured so that a layer's roofline fraction can be read against what the chip
 // delivers as well as against its published peaks. Not part of the layer.
 //
@@ -46,6 +46,40 @@ __global__ void __launch_bounds__(kProbeThreads, 1) probe_mfma_kernel(const uint
     for (int i = 0; i < 8; ++i) acc[i] = mfma32x32x16(a[i], b[7 - i], acc[i]);
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = mfma32x32x16(a[(i + 3) & 7], b[(i + 5) & 7], acc[i]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += acc[i][j];
+  if (s == 1.2345f) g_probe_sink = s;  // keeps the MFMAs live
+}
+
+// The FP8 probe: 32x32x64 E4M3 MFMAs with E8M0 block scales of 1.0 (the form the W8A8
+// GEMM issues), 8 independent accumulators, operands of 8 registers rotated as above.
+__global__ void __launch_bounds__(kProbeThreads, 1) probe_mfma_fp8_kernel(const uint4* __restrict__ ops, int iters) {
+  i32x8 a[4], b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 lo = ops[threadIdx.x * kProbeOps + 2 * i], hi = ops[threadIdx.x * kProbeOps + 2 * i + 1];
+    const uint4 lo2 = ops[threadIdx.x * kProbeOps + 8 + 2 * i], hi2 = ops[threadIdx.x * kProbeOps + 9 + 2 * i];
+    a[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    b[i] = i32x8{(int)lo2.x, (int)lo2.y, (int)lo2.z, (int)lo2.w, (int)hi2.x, (int)hi2.y, (int)hi2.z, (int)hi2.w};
+  }
+  int one = 127;  // E8M0 1.0, in a register (the scale operands are VGPRs)
+  asm volatile("" : "+v"(one));
+  f32x16 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[i][j] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      acc[i] = mfma32x32x64_f8(a[i & 3], b[(7 - i) & 3], acc[i], one, one);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      acc[i] = mfma32x32x64_f8(a[(i + 3) & 3], b[(i + 5) & 3], acc[i], one, one);
   }
   float s = 0.f;
 #pragma unroll
@@ -126,6 +160,25 @@ extern "C" int hy_moe_probe_mfma_bf16(const void* operands, size_t operand_bytes
   });
   if (ms <= 0.f) return HY_MOE_ERR_HIP;
   *tflops = (float)((double)grid * 4 * iters * 16 * 32768.0 / (ms * 1e-3) / 1e12);
+  return HY_MOE_OK;
+}
+
+extern "C" int hy_moe_probe_mfma_fp8(const void* operands, size_t operand_bytes, float* tflops, void* stream) {
+  if (!operands || !tflops || ((uintptr_t)operands & 15) || operand_bytes < HY_MOE_PROBE_OPERAND_BYTES)
+    return HY_MOE_ERR_INVALID_ARG;
+  const int cus = cus_of_current_device();
+  if (cus <= 0) return HY_MOE_ERR_HIP;
+  hipStream_t s = (hipStream_t)stream;
+  const int grid = 4 * cus;
+  // about 40 ms at 5 PFLOP/s
+  const int iters = (int)(2.0e14 / ((double)grid * 4 * 16 * 131072.0));
+  hipLaunchKernelGGL(probe_mfma_fp8_kernel, dim3(grid), dim3(kProbeThreads), 0, s, (const uint4*)operands, 64);
+  if (hipGetLastError() != hipSuccess) return HY_MOE_ERR_HIP;
+  const float ms = time_launch(s, [&] {
+    hipLaunchKernelGGL(probe_mfma_fp8_kernel, dim3(grid), dim3(kProbeThreads), 0, s, (const uint4*)operands, iters);
+  });
+  if (ms <= 0.f) return HY_MOE_ERR_HIP;
+  *tflops = (float)((double)grid * 4 * iters * 16 * 131072.0 / (ms * 1e-3) / 1e12);
   return HY_MOE_OK;
 }
 

@@ -82,18 +82,6 @@ constexpr int kGemmBf16 = 0, kGemmTern = 1, kGemmFp8 = 2, kGemmW8A8 = 3;
 constexpr int kBK8 = 128;        // W8A8: k per step
 constexpr int kSub8 = kBK8 / 64;  // W8A8: MFMA groups per step
 
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// D[32x32] += A[32x64] B[64x32] on E4M3 codes with E8M0 block scales sa (A) and sb (B)
-// (byte 0 of each; 127 = 1). Lane (r, h) holds row / column r: bytes 0-15 are k
-// [16h, 16h + 16) and bytes 16-31 are k [32 + 16h, 32 + 16h + 16) of the 64, and the scale
-// of 32-k block b of row / column r comes from lane (r, b). D as the bf16 32x32 MFMA.
-__device__ __forceinline__ f32x16 mfma32x32x64_f8(i32x8 a, i32x8 b, f32x16 c, int sa, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
-}
-
 // Two 16-byte LDS reads into one 8-register operand.
 __device__ __forceinline__ i32x8 lds_pair(const uint8_t* p0, const uint8_t* p1) {
   const i32x4 lo = *reinterpret_cast<const i32x4*>(p0);

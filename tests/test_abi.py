@@ -96,6 +96,10 @@ def test_probe_argument_checks():
     assert L.hy_moe_probe_mfma_bf16(FAKE, hm.PROBE_OPERAND_BYTES - 16, ctypes.byref(out), None) == hm.ERR_INVALID_ARG
     assert L.hy_moe_probe_mfma_bf16(FAKE + 8, hm.PROBE_OPERAND_BYTES, ctypes.byref(out), None) == hm.ERR_INVALID_ARG
     assert L.hy_moe_probe_mfma_bf16(FAKE, hm.PROBE_OPERAND_BYTES, None, None) == hm.ERR_INVALID_ARG
+    assert L.hy_moe_probe_mfma_fp8(None, hm.PROBE_OPERAND_BYTES, ctypes.byref(out), None) == hm.ERR_INVALID_ARG
+    assert L.hy_moe_probe_mfma_fp8(FAKE, hm.PROBE_OPERAND_BYTES - 16, ctypes.byref(out), None) == hm.ERR_INVALID_ARG
+    assert L.hy_moe_probe_mfma_fp8(FAKE + 8, hm.PROBE_OPERAND_BYTES, ctypes.byref(out), None) == hm.ERR_INVALID_ARG
+    assert L.hy_moe_probe_mfma_fp8(FAKE, hm.PROBE_OPERAND_BYTES, None, None) == hm.ERR_INVALID_ARG
     assert L.hy_moe_probe_hbm_read(None, 1 << 20, ctypes.byref(out), None) == hm.ERR_INVALID_ARG
     assert L.hy_moe_probe_hbm_read(FAKE, 8, ctypes.byref(out), None) == hm.ERR_INVALID_ARG
     assert L.hy_moe_probe_hbm_read(FAKE + 4, 1 << 20, ctypes.byref(out), None) == hm.ERR_INVALID_ARG

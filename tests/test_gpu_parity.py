@@ -363,6 +363,52 @@ def test_bitwise_deterministic_and_workspace_independent(path):
         assert torch.equal(r1[key], r3[key]), key
 
 
+# ------------------------------------------------- large cancelling expert outputs
+def _bits_to_f32(b):
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_large_cancelling_expert_outputs(path):
+    """Experts in pairs (0, 1) and (2, 3) share router rows (so equal weights) and
+    gate/up weights (so equal hidden rows), and the second's down projection is minus
+    256 times the first's plus an ordinary matrix: each y row is ~256 times the output
+    it sums to. The grouped path stores y rows in bf16 (RNE, relative error <= 2^-8),
+    so its error may reach 2^-8 (sum_j w_j |y_j| + |y_shared|) on top of the usual
+    tolerance; the streaming path keeps y in fp32 and meets the usual tolerance alone."""
+    cfg = hi.LayerConfig("cancel", T=300, d=256, E=4, k=4, I=256, seed=21)
+    say(f"[case] large cancelling outputs T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} I={cfg.I} path={path}")
+    L = hi.host_layer(cfg)
+    router, gate, up, down = L["router"].copy(), L["gate"].copy(), L["up"].copy(), L["down"].copy()
+    for a, b in ((0, 1), (2, 3)):
+        router[b], gate[b], up[b] = router[a], gate[a], up[a]
+        big = _bits_to_f32(down[a]) * np.float32(256.0)  # exact: a power of two
+        down[b] = f32_to_bf16_bits(-big + _bits_to_f32(down[b]))
+        down[a] = f32_to_bf16_bits(big)
+    def dev(arr):
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(DEV).view(torch.bfloat16)
+    inp = {"x": dev(L["x"]), "router": dev(router), "bias": None, "gate": dev(gate), "up": dev(up), "down": dev(down),
+           "shared": {m: dev(L["shared"][m]) for m in ("gate", "up", "down")}}
+    res = hm.forward_layer(inp, cfg.k, want_routing=True, path=path)
+    torch.cuda.synchronize()
+    assert (res["topk_idx"].cpu().numpy() == np.arange(4)).all()
+    ref = oracle.forward(L["x"], router, None, gate, up, down, L["shared"]["gate"], L["shared"]["up"],
+                         L["shared"]["down"], cfg.k)
+    ys = oracle.ffn(L["x"], L["shared"]["gate"], L["shared"]["up"], L["shared"]["down"])
+    mag = np.abs(ys)
+    for e in range(cfg.E):
+        ye = oracle.ffn(L["x"], gate[e], up[e], down[e])
+        mag += ref["w"][:, e:e + 1] * np.abs(ye)
+    out = bf16_tensor_to_np(res["out"])
+    plain = np.abs(out - ref["out"]) / (1.0 + np.abs(ref["out"]))
+    say(f"       sum w|y| / |out| median {np.median(mag / (1e-3 + np.abs(ref['out']))):.0f}; "
+        f"max |gpu-ref|/(1+|ref|) = {plain.max():.3e}")
+    if path == hm.PATH_GROUPED:
+        check_out(out, ref["out"], extra=2.0 ** -8 * mag)
+    else:
+        check_out(out, ref["out"])
+
+
 def test_plain_entry_point_matches_ex():
     say("[case] hy_moe_forward vs hy_moe_forward_ex")
     cfg = hi.LayerConfig("plain", T=64, d=256, E=16, k=2, I=128, seed=7)

@@ -1,5 +1,5 @@
 """The machine-peak probes run and report rates inside physical limits (the
-published MI355X peaks: 2.5 PFLOP/s dense bf16, 8 TB/s HBM)."""
+published MI355X peaks: 2.5 PFLOP/s dense bf16, 5.0 dense FP8, 8 TB/s HBM)."""
 import pytest
 
 import sparse_moe_transformer_route_amd as hm
@@ -13,8 +13,12 @@ def test_probes_report_plausible_rates():
     g = torch.Generator(device="cuda:0").manual_seed(0)
     ops = torch.randn(hm.PROBE_OPERAND_BYTES // 2, generator=g, device="cuda:0").to(torch.bfloat16)
     tf = hm.probe_mfma_bf16(ops)
+    codes = ops.float().to(torch.float8_e4m3fn).view(torch.uint8)
+    codes = torch.cat([codes, codes])  # 1 byte per code: twice the bf16 count fills the buffer
+    tf8 = hm.probe_mfma_fp8(codes)
     buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
     gb = hm.probe_hbm_read(buf)
-    print(f"       bf16 MFMA {tf:.0f} TFLOP/s, HBM read {gb:.0f} GB/s", flush=True)
+    print(f"       bf16 MFMA {tf:.0f} TFLOP/s, FP8 MFMA {tf8:.0f} TFLOP/s, HBM read {gb:.0f} GB/s", flush=True)
     assert 300 < tf < 2600
+    assert 600 < tf8 < 5200
     assert 1000 < gb < 8200
