@@ -216,7 +216,6 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
   constexpr bool TERN = WF == kGemmTern, FP8 = WF == kGemmFp8, A8 = WF == kGemmW8A8;
   constexpr int BS = 3;  // weight (or code) ring slots
   constexpr int kBOps = TERN ? kCodeOps : FP8 ? kF8Ops : kDma;  // weight-side load ops per thread per step
-  constexpr int SUB = A8 ? kSub8 : kSub;   // MFMA groups per step
   constexpr int BKE = A8 ? kBK8 : kBK;     // k per step (128 bytes per row either way)
   // Separate LDS arrays rather than one carved buffer: the compiler tells direct-to-LDS
   // loads and LDS reads of different arrays apart; within one array it would wait for
@@ -591,8 +590,12 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
       issue_b(0, sb[0], C0{}, CF{});
       issue_b(1, sb[1], C0{}, CF{});
     }
-    issue_a(1, sa1, C0{}, CH{});
-    wait_vm<kBOps + kDma / 2>();
+    // (W8A8: all of step 1's activations; its steps load the activations two steps ahead)
+    if constexpr (A8)
+      issue_a(1, sa1, C0{}, CF{});
+    else
+      issue_a(1, sa1, C0{}, CH{});
+    wait_vm<kBOps + (A8 ? kDma : kDma / 2)>();
     bare_barrier();
 
     // the k loop, with this wave's number of active row blocks fixed at compile time
@@ -671,8 +674,10 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
       // block j); the lane's activation scale for row block j is byte 2 S + hf of that
       // step's scale word. With REFILL, fb8[nb] takes the fragment of group SN from
       // (La, Lb) right after its last MFMA (row block NACT - 1), and fa8[j] right after
-      // column block kNB - 1's MFMA of row block j; NV vector-memory ops issued before the
-      // group are spread over its first MFMAs.
+      // column block kNB - 1's MFMA of row block j. vm(t) issues the group's vector-memory
+      // op t (t < NV): op m goes out right after MFMA m, in program order as well as in
+      // the scheduling pattern (issued ahead of the group, the scheduler sent all of them
+      // in one burst before the first MFMA), and ops past the group's MFMAs follow them.
       auto rd_a8 = [&](const uint8_t* La, int s, int j) __attribute__((always_inline)) {
         const uint8_t* base = La + fa_off + j * 2 * kBlk * kRowBytes;
         fa8[j] = lds_pair(base + a8o[s][0], base + a8o[s][1]);
@@ -682,10 +687,11 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
         fb8[nb] = lds_pair(base + a8o[s][0], base + a8o[s][1]);
       };
       auto group8 = [&](auto s_tag, auto par_tag, auto refill_tag, auto sn_tag, auto nv_tag, const uint8_t* La,
-                        const uint8_t* Lb) __attribute__((always_inline)) {
+                        const uint8_t* Lb, auto&& vm) __attribute__((always_inline)) {
         constexpr int S = decltype(s_tag)::value, PAR = decltype(par_tag)::value;
         constexpr bool REFILL = decltype(refill_tag)::value;
         constexpr int SN = decltype(sn_tag)::value, NV = decltype(nv_tag)::value;
+        constexpr int NM = kNB * NACT;  // the group's MFMAs
         if constexpr (NACT > 0) {
           int one = 127;  // E8M0 1.0 for the weights (their fp32 row scales apply in the epilogue)
           asm volatile("" : "+v"(one));
@@ -697,6 +703,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
             for_seq(std::make_integer_sequence<int, NACT>{}, [&](auto j_tag) {
               constexpr int J = decltype(j_tag)::value;
               acc[J][NB] = mfma32x32x64_f8(fb8[NB], fa8[J], acc[J][NB], one, sc[J]);
+              if constexpr (NB * NACT + J < NV) vm(std::integral_constant<int, NB * NACT + J>{});
               if constexpr (REFILL && J == NACT - 1) rd_b8(Lb, SN, NB);
               if constexpr (REFILL && NB == kNB - 1) rd_a8(La, SN, J);
             });
@@ -710,6 +717,12 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
             if constexpr (M < NV) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
             if constexpr (NR > 0) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
           });
+        }
+        if constexpr (NV > NM) {
+          for_seq(std::make_integer_sequence<int, NV - NM>{}, [&](auto t_tag) {
+            vm(std::integral_constant<int, NM + decltype(t_tag)::value>{});
+          });
+          __builtin_amdgcn_sched_group_barrier(0x010, NV - NM, 0);
         }
       };
       auto mfmas = [&](int s) {
@@ -792,35 +805,44 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
         __builtin_amdgcn_sched_barrier(0);
       };
       // W8A8 step ks: group 0 on fragments already in registers (refilling group 1's from
-      // this step's slots) with the second half of step ks+1's activations and step ks+2's
-      // weights issued over it; then the barrier that frees this step's slots and lands
-      // step ks+1's; group 1 refilling the next step's group 0; then the scales of step
-      // ks+2 into the parity's registers, which group 1 was the last to read.
+      // this step's slots) with step ks+2's weights issued over it; then the barrier that
+      // frees this step's activation slot and lands step ks+1's; group 1 refilling the next
+      // step's group 0, with all of step ks+2's activations issued over it into the slot
+      // just freed; then the scales of step ks+2 into the parity's registers, which group 1
+      // was the last to read. Each load thus has two (activations) or three (weights) MFMA
+      // groups to land before the barrier that waits for it (with half of step ks+1's
+      // activations issued over group 0 instead, they had one group: gate/up 1.5% slower).
       auto step8 = [&](auto ua_tag, auto ub_tag, auto next_tag, auto pa_tag, auto pb_tag, int ks)
                        __attribute__((always_inline)) {
         constexpr int UA = decltype(ua_tag)::value;
         constexpr int UB = decltype(ub_tag)::value;
         constexpr bool NEXT = decltype(next_tag)::value;
-        constexpr bool PA = decltype(pa_tag)::value;
-        constexpr bool PB = decltype(pb_tag)::value;
+        constexpr bool PB = decltype(pb_tag)::value;  // (step ks+1's loads went out in step ks-1)
         using I0 = std::integral_constant<int, 0>;
         using I1 = std::integral_constant<int, 1>;
-        if constexpr (PA) issue_a(ks + 1, sa[UA ^ 1], CH{}, CF{});
-        if constexpr (PB) issue_b(ks + 2, sb[(UB + 2) % BS], C0{}, CF{});
-        group8(I0{}, ua_tag, std::true_type{}, I1{}, std::integral_constant<int, (PA ? kDma / 2 : 0) + (PB ? kDma : 0)>{},
-               sa[UA], sb[UB]);
+        // group 0's ops: step ks+2's weights
+        auto vm0 = [&](auto t_tag) __attribute__((always_inline)) {
+          constexpr int T = decltype(t_tag)::value;
+          issue_b(ks + 2, sb[(UB + 2) % BS], std::integral_constant<int, T>{}, std::integral_constant<int, T + 1>{});
+        };
+        group8(I0{}, ua_tag, std::true_type{}, I1{}, std::integral_constant<int, PB ? kDma : 0>{}, sa[UA], sb[UB],
+               vm0);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (NEXT) {
           wait_vm<PB ? kBOps : 0>();  // all but step ks+2's weights (the newest)
           wait_lds();
           bare_barrier();
-          if constexpr (PB) issue_a(ks + 2, sa[UA], C0{}, CH{});
-          group8(I1{}, ua_tag, std::true_type{}, I0{}, std::integral_constant<int, PB ? kDma / 2 : 0>{}, sa[UA ^ 1],
-                 sb[(UB + 1) % BS]);
+          // group 1's ops: step ks+2's activations
+          auto vm1 = [&](auto t_tag) __attribute__((always_inline)) {
+            constexpr int T = decltype(t_tag)::value;
+            issue_a(ks + 2, sa[UA], std::integral_constant<int, T>{}, std::integral_constant<int, T + 1>{});
+          };
+          group8(I1{}, ua_tag, std::true_type{}, I0{}, std::integral_constant<int, PB ? kDma : 0>{}, sa[UA ^ 1],
+                 sb[(UB + 1) % BS], vm1);
           __builtin_amdgcn_sched_barrier(0);
           if constexpr (PB) issue_s(ks + 2, ua_tag);
         } else {
-          group8(I1{}, ua_tag, std::false_type{}, I0{}, I0{}, nullptr, nullptr);
+          group8(I1{}, ua_tag, std::false_type{}, I0{}, I0{}, nullptr, nullptr, [](auto) {});
         }
         __builtin_amdgcn_sched_barrier(0);
       };
