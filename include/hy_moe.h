@@ -215,7 +215,7 @@ int hy_moe_forward_noalloc(const hy_moe_args* args, void* stream);
 
 /* Bytes of DEVICE workspace hy_moe_forward_ex needs for this shape (for the
  * largest of the paths it may pick); 0 for invalid shapes. Alignment: 256 B. */
-size_t hy_moe_workspace_size(int64_t T, int64_t d, int64_t E, int64_t k, int64_t I, int expert_format);
+size_t hy_moe_workspace_size(int64_t T, int64_t d, int64_t E, int64_t k, int64_t I, hy_moe_wfmt expert_format);
 
 /* Static text for a status code. */
 const char* hy_moe_status_string(int status);

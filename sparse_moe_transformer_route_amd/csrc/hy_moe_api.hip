@@ -296,7 +296,8 @@ extern "C" int hy_moe_forward(const void* x, const void* W_router, const void* W
   return hy_moe_forward_ex(&a, stream);
 }
 
-extern "C" size_t hy_moe_workspace_size(int64_t T, int64_t d, int64_t E, int64_t k, int64_t I, int expert_format) {
+extern "C" size_t hy_moe_workspace_size(int64_t T, int64_t d, int64_t E, int64_t k, int64_t I,
+                                        hy_moe_wfmt expert_format) {
   if (!valid_format(expert_format)) return 0;
   if (check_shape(T, d, E, k, I) != HY_MOE_OK) return 0;
   return make_layout(T, d, E, k, I, expert_format).total;
