@@ -2,8 +2,8 @@
 hy_moe_forward_ex with a caller workspace, through the C ABI: the same kernels run
 on the same inputs, so outputs and routing must be bitwise identical. Calls run back
 to back on one device with shrinking and growing batches (each call must rewrite
-whatever it reads of the buffer), on both expert paths and on Sherry weights; the
-first case is also checked against the fp64 oracle."""
+whatever it reads of the buffer), on both expert paths, on Sherry weights and on the
+W8A8 format; the first case is also checked against the fp64 oracle."""
 import pytest
 
 import hy_inputs as hi
@@ -22,15 +22,16 @@ def say(msg):
     print(msg, flush=True)
 
 
-def compare(inp, k, path, label):
-    fmt = hm.WEIGHTS_SHERRY_TERNARY if "qgate" in inp else hm.WEIGHTS_BF16
+def compare(inp, k, path, label, a8=False):
+    fmt = (hm.WEIGHTS_SHERRY_TERNARY if "qgate" in inp else hm.WEIGHTS_FP8_W8A8 if a8 else
+           hm.WEIGHTS_FP8_E4M3 if "fgate" in inp else hm.WEIGHTS_BF16)
     T, d = inp["x"].shape
     E = inp["router"].shape[0]
-    I = inp["sgate"].shape[1] if "qgate" in inp else inp["gate"].shape[1]
-    say(f"[case] {label}: T={T} d={d} E={E} k={k} I={I} path={path}")
+    I = (inp["sgate"] if "qgate" in inp else inp["fsgate"] if "fgate" in inp else inp["gate"]).shape[1]
+    say(f"[case] {label}: T={T} d={d} E={E} k={k} I={I} path={path} w8a8={a8}")
     ws = hm.alloc_workspace(T, d, E, k, I, fmt, device=DEV)
-    ref = hm.forward_layer(inp, k, want_routing=True, path=path, workspace=ws)
-    got = hm.forward_layer(inp, k, want_routing=True, path=path, noalloc=True)
+    ref = hm.forward_layer(inp, k, want_routing=True, path=path, workspace=ws, fp8_activations=a8)
+    got = hm.forward_layer(inp, k, want_routing=True, path=path, noalloc=True, fp8_activations=a8)
     torch.cuda.synchronize()
     assert torch.equal(got["out"].view(torch.int16), ref["out"].view(torch.int16)), label
     for key in KEYS:
@@ -74,8 +75,23 @@ def test_noalloc_ternary_and_hy4_decode_shape():
     compare(small, cfg.k, hm.PATH_AUTO, "T=32 after it")
 
 
+def test_noalloc_w8a8():
+    # W8A8 runs the grouped path with the token rows' and hidden rows' MXFP8 codes and
+    # scales in the buffer as well: a larger call, then a smaller one
+    cfg = hi.LayerConfig("naw", T=300, d=512, E=8, k=2, I=512, fp8=True, a8=True, seed=14)
+    inp = hi.dev_layer(cfg, device=DEV)
+    compare(inp, cfg.k, hm.PATH_AUTO, "W8A8", a8=True)
+    small = dict(inp)
+    small["x"] = inp["x"][:70].contiguous()
+    compare(small, cfg.k, hm.PATH_AUTO, "W8A8, smaller second call", a8=True)
+
+
 def test_noalloc_rejects_batches_beyond_the_buffer():
+    # the limits the header states at the Hy4 layer shape: T <= 251, and T <= 383 for W8A8
+    assert hm.workspace_size(251, 6144, 256, 8, 2048) <= hm.NOALLOC_SCRATCH_BYTES
     assert hm.workspace_size(252, 6144, 256, 8, 2048) > hm.NOALLOC_SCRATCH_BYTES
+    assert hm.workspace_size(383, 6144, 256, 8, 2048, hm.WEIGHTS_FP8_W8A8) <= hm.NOALLOC_SCRATCH_BYTES
+    assert hm.workspace_size(384, 6144, 256, 8, 2048, hm.WEIGHTS_FP8_W8A8) > hm.NOALLOC_SCRATCH_BYTES
     # the check is on the host and needs no weights: the pointers (one small device
     # buffer) are never dereferenced when the call is rejected or the batch is empty
     a = hm.HyMoeArgs()
