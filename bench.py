@@ -183,7 +183,7 @@ def time_layer(hm, torch, inp, k, ws, steps, warmup, dominant, flush=None, fwd_k
             "warmup": done, "cold_ms": cold, "cold_dom_ms": cold_dom if cold is not None else None}
 
 
-def stream_work(cfg, touched):
+def stream_work(cfg, touched, blocked=False):
     """Algorithmic HBM bytes of a decode-size layer on the streaming path with `touched`
     routed experts: the dominant gate/up launch (one unit per touched routed expert,
     plus the shared expert) and the whole layer (every touched expert's weights once,
@@ -210,12 +210,12 @@ def stream_work(cfg, touched):
     # ternary weights with d and I multiples of 512 run in the LDS-staged kernel
     tern_lds = cfg.ternary and d % 512 == 0 and I % 512 == 0
     kernel = ("tern_lds_kernel<2>" if tern_lds else "stream_gateup_kernel<2> (FP8 routed experts)" if cfg.fp8
-              else "stream_gateup_kernel")
+              else "stream_gateup_kernel<3> (blocked bf16 weights)" if blocked else "stream_gateup_kernel<0>")
     return {"unit": unit, "alg": alg, "per_unit": per_unit, "layer_bytes": layer_bytes,
             "key": "ternary_gateup" if tern_lds else "stream_gateup", "kernel": kernel}
 
 
-def gemm_work(cfg):
+def gemm_work(cfg, blocked=False):
     """Algorithmic flops of a layer on the grouped path: the dominant gate/up stage
     (4 d I per dispatched row, routed and shared) and the whole layer (router + all
     three expert products)."""
@@ -226,7 +226,8 @@ def gemm_work(cfg):
               "mx_quantize_kernel (token rows to MXFP8) + grouped_gemm_kernel<true, 0, 3> (FP8 MFMAs on the W8A8 "
               "routed tiles) + grouped_gemm_kernel<true, 0, 0> (bf16 shared tiles): one timed stage" if cfg.a8 else
               "grouped_gemm_kernel<true, 0, 2> (FP8 routed tiles) + grouped_gemm_kernel<true, 0, 0> "
-              "(bf16 shared tiles): one timed stage" if cfg.fp8 else "grouped_gemm_kernel<true, 0, 0>")
+              "(bf16 shared tiles): one timed stage" if cfg.fp8 else
+              "grouped_gemm_kernel<true, 0, 4> (blocked bf16 weights)" if blocked else "grouped_gemm_kernel<true, 0, 0>")
     # W8A8: the routed rows run on FP8 MFMAs and the shared rows on bf16 ones, so the
     # stage's peak is the time both take at their own peaks
     routed, shared = cfg.T * cfg.k, cfg.T
@@ -267,20 +268,33 @@ def input_digest(inp, torch):
     return h.hexdigest()[:16]
 
 
-def run_config(name, args, hi, hm, torch, weights=None, steps=None, flush=None):
+def run_config(name, args, hi, hm, torch, weights=None, steps=None, flush=None, blocked=False, rm_weights=None):
+    """Times workload `name`. weights: a bf16 layer dict to take the expert weights from
+    (already in the blocked layout when blocked is set; rm_weights then holds the same
+    weights row-major). blocked (bf16 workloads): the HY_MOE_WEIGHTS_BF16_BLOCKED format,
+    weights converted once before anything is timed. res["inp_rm"] is the input set with
+    row-major weights (what the oracle reads)."""
     cfg = hi.CONFIGS[name]
     dev = "cuda:0"
+    bf16 = not cfg.ternary and not cfg.fp8
+    blocked = blocked and bf16
+
+    def with_x(wts):
+        d = dict(wts)
+        d["x"] = wts["x"][: cfg.T].contiguous()
+        b = hi.host_bias(cfg)
+        d["bias"] = None if b is None else torch.from_numpy(b).to(dev)
+        return d
     if weights is None:
         log(f"[bench] generating inputs for {name} on the GPU")
-        inp = hi.dev_layer(cfg, device=dev)
+        inp_rm = hi.dev_layer(cfg, device=dev)
+        inp = hm.block_layer(inp_rm) if blocked else inp_rm
     else:
-        inp = dict(weights)
-        inp["x"] = weights["x"][: cfg.T].contiguous()
-        b = hi.host_bias(cfg)
-        inp["bias"] = None if b is None else torch.from_numpy(b).to(dev)
+        inp = with_x(weights)
+        inp_rm = with_x(rm_weights) if blocked else inp
     fmt = (hm.WEIGHTS_SHERRY_TERNARY if cfg.ternary else hm.WEIGHTS_FP8_W8A8 if cfg.a8 else
-           hm.WEIGHTS_FP8_E4M3 if cfg.fp8 else hm.WEIGHTS_BF16)
-    fwd_kw = {"fp8_activations": True} if cfg.a8 else {}
+           hm.WEIGHTS_FP8_E4M3 if cfg.fp8 else hm.WEIGHTS_BF16_BLOCKED if blocked else hm.WEIGHTS_BF16)
+    fwd_kw = {"fp8_activations": True} if cfg.a8 else {"weights_blocked": True} if blocked else {}
     ws = hm.alloc_workspace(cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, fmt, device=dev)
     steps = args.steps if steps is None else steps
     dominant = hm.KERNELS.index("expert_gateup")
@@ -295,8 +309,8 @@ def run_config(name, args, hi, hm, torch, weights=None, steps=None, flush=None):
     stream_path = cfg.T * cfg.k <= 16 * cfg.E and not cfg.a8  # the library's automatic path choice
     kernel_file = "sparse_moe_transformer_route_amd/csrc/" + ("moe_stream.hip" if stream_path else "moe_gemm.hip")
     # algorithmic bytes and flops of the whole layer (both reported for every workload)
-    lw = stream_work(cfg, touched)
-    gw = gemm_work(cfg)
+    lw = stream_work(cfg, touched, blocked)
+    gw = gemm_work(cfg, blocked)
     layer = {"bytes": lw["layer_bytes"], "flop": gw["layer_flop"],
              "hbm_frac": lw["layer_bytes"] / (ms * 1e-3) / PEAK_HBM,
              "mfma_frac": gw["layer_flop"] / (ms * 1e-3) / gw["layer_peak"]}
@@ -316,10 +330,12 @@ def run_config(name, args, hi, hm, torch, weights=None, steps=None, flush=None):
         if cfg.a8:
             roof["peak_mix"] = {"fp8_rows": cfg.T * cfg.k, "bf16_rows": cfg.T}
     roof["kernel_source_sha256_16"] = source_digest(os.path.join(ROOT, kernel_file))
-    res = {"cfg": cfg, "inp": inp, "ms": ms, "tokens_per_s": cfg.T / (ms * 1e-3), "kernels_ms": r["kernels"],
+    res = {"cfg": cfg, "inp": inp, "inp_rm": inp_rm, "blocked": blocked, "ms": ms, "tokens_per_s": cfg.T / (ms * 1e-3),
+           "kernels_ms": r["kernels"],
            "roofline": roof, "layer": layer, "touched": touched, "counts": counts, "routing": routing,
            "warmup": r["warmup"], "steps": steps, "step_ms": step_stats(r["step_ms"]),
-           "kernel_step_ms": step_stats(r["dom_ms"]), "near_ties": near, "input_sha256_16": input_digest(inp, torch)}
+           "kernel_step_ms": step_stats(r["dom_ms"]), "near_ties": near,
+           "input_sha256_16": input_digest(inp_rm, torch)}
     if r["cold_ms"] is not None:
         cold = step_stats(r["cold_ms"])
         cold_dom = sum(r["cold_dom_ms"]) / steps * 1e-3
@@ -335,7 +351,8 @@ def run_config(name, args, hi, hm, torch, weights=None, steps=None, flush=None):
 def workload_object(res, extra=None):
     """The JSON object of one workload (the headline one is the top level)."""
     c = res["cfg"]
-    o = {"workload": workload_name(c), "T": c.T, "ms_per_step": res["ms"], "steps": res["steps"],
+    o = {"workload": workload_name(c), "T": c.T, "weights_layout": layout_name(res), "ms_per_step": res["ms"],
+         "steps": res["steps"],
          "warmup": res["warmup"], "step_ms": res["step_ms"], "tokens_per_s": res["tokens_per_s"],
          "roofline": res["roofline"], "layer": res["layer"], "kernels_ms": res["kernels_ms"],
          "touched_experts": res["touched"], "near_tie_tokens": res["near_ties"],
@@ -345,6 +362,16 @@ def workload_object(res, extra=None):
     if extra:
         o.update(extra)
     return o
+
+
+def layout_name(res):
+    c = res["cfg"]
+    if c.ternary:
+        return "Sherry-packed routed experts, row-major bf16 shared expert"
+    if c.fp8:
+        return "row-major E4M3 routed experts, row-major bf16 shared expert"
+    return ("blocked bf16 (16 rows x 64 columns per 2 KB block, hy_moe_block_bf16, converted once before timing)"
+            if res["blocked"] else "row-major bf16")
 
 
 def dtype_name(c):
@@ -643,9 +670,13 @@ def main():
             f"p10 {res['step_ms']['p10']:.3f}, p90 {res['step_ms']['p90']:.3f}), {res['tokens_per_s']:.1f} tokens/s, "
             f"kernels {json.dumps({k: round(v, 4) for k, v in res['kernels_ms'].items()})}")
 
+    # bf16 workloads run on the blocked layout of the same weights (one conversion,
+    # outside every timed region); the headline is timed on row-major weights as well
+    blocked_weights = hm.block_layer(shared_weights) if shared_weights is not None else None
+    torch.cuda.synchronize()
     extra = {}
     if full:
-        t = run_config("tiny", args, hi, hm, torch)
+        t = run_config("tiny", args, hi, hm, torch, blocked=True)
         report(t)
         extra["tiny"] = workload_object(t, {"us_per_step": t["ms"] * 1e3})
         del t
@@ -658,14 +689,23 @@ def main():
     def flush():
         n_flush[0] += 1
         flush_buf.fill_(n_flush[0] & 0xFF)
-    main_res = run_config(args.config, args, hi, hm, torch, shared_weights, flush=flush if full else None)
+    main_res = run_config(args.config, args, hi, hm, torch, blocked_weights if bf16_hy4 or full else None,
+                          flush=flush if full else None, blocked=True, rm_weights=shared_weights)
     report(main_res)
     if full:
-        pre = run_config("prefill", args, hi, hm, torch, shared_weights)
+        rm = run_config(args.config, args, hi, hm, torch, shared_weights)
+        report(rm)
+        extra["row_major_weights"] = {"weights_layout": layout_name(rm), "ms_per_step": rm["ms"],
+                                      "tokens_per_s": rm["tokens_per_s"], "step_ms": rm["step_ms"],
+                                      "roofline_frac": rm["roofline"]["frac"], "kernels_ms": rm["kernels_ms"],
+                                      "note": "the same weights in row-major order (HY_MOE_WEIGHTS_BF16)"}
+        del rm
+    if full:
+        pre = run_config("prefill", args, hi, hm, torch, blocked_weights, blocked=True, rm_weights=shared_weights)
         report(pre)
         extra["prefill"] = workload_object(pre)
         del pre
-        sk = run_config("skewed", args, hi, hm, torch, shared_weights)
+        sk = run_config("skewed", args, hi, hm, torch, blocked_weights, blocked=True, rm_weights=shared_weights)
         report(sk)
         cnt = sk["counts"]
         extra["skewed"] = workload_object(sk, {"hottest_expert_rows": int(cnt.max()),
@@ -685,7 +725,7 @@ def main():
 
     roof = main_res["roofline"]
     if peaks is not None:
-        for r in [roof] + [o["roofline"] for o in extra.values()]:
+        for r in [roof] + [o["roofline"] for o in extra.values() if "roofline" in o]:
             r["frac_of_measured_peak"] = r["achieved"] / measured_peak_of(r, peaks)
             if r["unit"] == "TFLOP/s" and "library_gemm_bf16" in peaks:
                 r["frac_of_library_dense_gemm"] = r["achieved"] / peaks["library_gemm_bf16"]["tflops"]
@@ -693,7 +733,8 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and not args.only:
         log("[bench] timing the oracle on the host")
-        cpu = cpu_baseline(cfg, hi, torch, main_res["inp"], main_res["routing"], args.cpu_seconds)
+        # the oracle takes row-major weights
+        cpu = cpu_baseline(cfg, hi, torch, main_res["inp_rm"], main_res["routing"], args.cpu_seconds)
 
     c = main_res["cfg"]
     line = {
@@ -701,7 +742,8 @@ def main():
         "steps": main_res["steps"], "warmup": main_res["warmup"], "ms_per_step": main_res["ms"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": dtype_name(c), "data": "synthetic",
-        "config": {"workload": workload_name(c), "T": c.T, "d": c.d, "E": c.E, "k": c.k, "I": c.I, "seed": c.seed,
+        "config": {"workload": workload_name(c), "weights_layout": layout_name(main_res),
+                   "T": c.T, "d": c.d, "E": c.E, "k": c.k, "I": c.I, "seed": c.seed,
                    "touched_experts": main_res["touched"]},
         "step_ms": main_res["step_ms"],
         "roofline": main_res["roofline"],

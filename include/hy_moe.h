@@ -90,7 +90,18 @@ typedef enum {
    * quantized from fp32. The router and the shared expert stay bf16. Runs on the
    * grouped path only (AUTO picks it; HY_MOE_PATH_STREAM -> HY_MOE_ERR_UNSUPPORTED) and
    * needs d % 256 == 0 and I % 256 == 0. */
-  HY_MOE_WEIGHTS_FP8_W8A8 = 3
+  HY_MOE_WEIGHTS_FP8_W8A8 = 3,
+  /* bf16 weights as HY_MOE_WEIGHTS_BF16 (the same layer, m.xxqk.cn Hy4 preview explainer
+   * section 2.1; the same pointers W_gate/W_up/W_down and Ws_gate/Ws_up/Ws_down, the same
+   * sizes), every expert matrix, routed and shared, stored in this library's blocked
+   * layout: a matrix of R rows by K columns (R = I and K = d for gate and up, R = d and
+   * K = I for down) becomes [R/16][K/64][16][64]: the 64 values of row r in columns
+   * [64 c, 64 c + 64) start at element 1024 * ((r / 16) * (K / 64) + c) + 64 * (r % 16).
+   * Each 16-row group's 64-column slab is then one contiguous 2 KB run, which the
+   * streaming path reads from HBM faster than 16 rows a whole row apart. Results are
+   * bitwise identical to HY_MOE_WEIGHTS_BF16 on the same weights. hy_moe_block_bf16
+   * converts row-major matrices. */
+  HY_MOE_WEIGHTS_BF16_BLOCKED = 4
 } hy_moe_wfmt;
 
 /* Which kernels run the experts. AUTO picks by the average rows per expert. */
@@ -244,6 +255,18 @@ int hy_moe_sherry_pack_host(const int8_t* tern, int64_t rows, int64_t cols, uint
  * rows == 0 is a no-op.
  */
 int hy_moe_mxfp8_quantize(const void* x, int64_t rows, int64_t cols, void* codes, void* scales, void* stream);
+
+/*
+ * hy_moe_block_bf16 — rewrites row-major bf16 matrices in the layout of
+ * HY_MOE_WEIGHTS_BF16_BLOCKED (a one-time conversion of a model's expert weights).
+ *   src    DEVICE bf16, `count` matrices of [rows][cols] back to back, 16-byte aligned
+ *   dst    DEVICE bf16, the same size, 16-byte aligned, not overlapping src (out)
+ *   count >= 0, rows % 16 == 0, cols % 64 == 0, rows > 0, cols > 0
+ * Enqueued on `stream` without blocking. Returns HY_MOE_OK, HY_MOE_ERR_INVALID_ARG
+ * (null or misaligned pointers, overlapping buffers, bad sizes; nothing enqueued) or
+ * HY_MOE_ERR_HIP. count == 0 is a no-op.
+ */
+int hy_moe_block_bf16(const void* src, void* dst, int64_t count, int64_t rows, int64_t cols, void* stream);
 
 /*
  * Machine-peak probes (not part of the layer): the rates this GPU reaches, for

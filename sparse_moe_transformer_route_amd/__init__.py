@@ -24,14 +24,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhy_moe.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
-WEIGHTS_BF16, WEIGHTS_SHERRY_TERNARY, WEIGHTS_FP8_E4M3, WEIGHTS_FP8_W8A8 = 0, 1, 2, 3
+WEIGHTS_BF16, WEIGHTS_SHERRY_TERNARY, WEIGHTS_FP8_E4M3, WEIGHTS_FP8_W8A8, WEIGHTS_BF16_BLOCKED = 0, 1, 2, 3, 4
 PATH_AUTO, PATH_STREAM, PATH_GROUPED = 0, 1, 2
 KERNELS = ["route_logits", "route_topk", "permute_scan", "permute_scatter", "expert_gateup", "expert_down",
            "combine"]
 NUM_STAGE_EVENTS = len(KERNELS) + 1
 
 EXPORTED = ["hy_moe_forward", "hy_moe_forward_ex", "hy_moe_forward_noalloc", "hy_moe_workspace_size",
-            "hy_moe_status_string", "hy_moe_sherry_pack_host", "hy_moe_mxfp8_quantize", "hy_moe_probe_mfma_bf16", "hy_moe_probe_mfma_fp8", "hy_moe_probe_hbm_read",
+            "hy_moe_status_string", "hy_moe_sherry_pack_host", "hy_moe_mxfp8_quantize", "hy_moe_block_bf16", "hy_moe_probe_mfma_bf16", "hy_moe_probe_mfma_fp8", "hy_moe_probe_hbm_read",
             "hy_indexer_workspace_size", "hy_indexer_topk"]
 PROBE_OPERAND_BYTES = 65536
 NOALLOC_SCRATCH_BYTES = 64 << 20  # HY_MOE_NOALLOC_SCRATCH_BYTES
@@ -83,6 +83,8 @@ def _load():
     L.hy_moe_sherry_pack_host.restype = ctypes.c_int
     L.hy_moe_mxfp8_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
     L.hy_moe_mxfp8_quantize.restype = ctypes.c_int
+    L.hy_moe_block_bf16.argtypes = [vp, vp, i64, i64, i64, vp]
+    L.hy_moe_block_bf16.restype = ctypes.c_int
     L.hy_moe_probe_mfma_bf16.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_float), vp]
     L.hy_moe_probe_mfma_bf16.restype = ctypes.c_int
     L.hy_moe_probe_mfma_fp8.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_float), vp]
@@ -147,7 +149,8 @@ def forward_noalloc(args: HyMoeArgs, stream=None) -> int:
 
 
 def forward_layer(inp: dict, k: int, *, want_routing=False, path=PATH_AUTO, workspace=None, out=None,
-                  stream=None, stage_events=None, noalloc=False, fp8_activations=False, want_hidden=False):
+                  stream=None, stage_events=None, noalloc=False, fp8_activations=False, want_hidden=False,
+                  weights_blocked=False):
     """Runs hy_moe_forward_ex on a dict of device tensors as made by
     hy_inputs.dev_layer(): x, router, bias, shared{gate,up,down} and either
     gate/up/down (bf16), qgate/qup/qdown + sgate/sup/sdown (ternary) or
@@ -156,7 +159,9 @@ def forward_layer(inp: dict, k: int, *, want_routing=False, path=PATH_AUTO, work
     perm_src, margin). noalloc: call hy_moe_forward_noalloc (no workspace).
     fp8_activations (FP8 weights only): the W8A8 format, MXFP8 activations; with
     want_hidden also hidden_codes [T*k][I] and hidden_scales [T*k][I/32] (the routed
-    hidden rows as the down projection reads them, dispatched-row order)."""
+    hidden rows as the down projection reads them, dispatched-row order).
+    weights_blocked (bf16 weights only): gate/up/down and the shared expert's matrices
+    are in the blocked layout (block_layer), the HY_MOE_WEIGHTS_BF16_BLOCKED format."""
     import torch
     x = inp["x"]
     T, d = x.shape
@@ -178,8 +183,11 @@ def forward_layer(inp: dict, k: int, *, want_routing=False, path=PATH_AUTO, work
     a.x, a.W_router, a.router_bias = _ptr(x), _ptr(inp["router"]), _ptr(inp.get("bias"))
     if fp8_activations and not fp8:
         raise ValueError("forward_layer: fp8_activations needs FP8 weights")
+    if weights_blocked and (fp8 or ternary):
+        raise ValueError("forward_layer: weights_blocked applies to bf16 weights")
     a.expert_format = (WEIGHTS_SHERRY_TERNARY if ternary else
-                       (WEIGHTS_FP8_W8A8 if fp8_activations else WEIGHTS_FP8_E4M3) if fp8 else WEIGHTS_BF16)
+                       (WEIGHTS_FP8_W8A8 if fp8_activations else WEIGHTS_FP8_E4M3) if fp8 else
+                       WEIGHTS_BF16_BLOCKED if weights_blocked else WEIGHTS_BF16)
     if ternary:
         a.Wq_gate, a.Wq_up, a.Wq_down = _ptr(inp["qgate"]), _ptr(inp["qup"]), _ptr(inp["qdown"])
         a.S_gate, a.S_up, a.S_down = _ptr(inp["sgate"]), _ptr(inp["sup"]), _ptr(inp["sdown"])
@@ -260,6 +268,31 @@ def mxfp8_quantize(x, stream=None):
     if rc != OK:
         raise HyMoeError(rc, "hy_moe_mxfp8_quantize")
     return codes, scales
+
+
+def block_bf16(t, stream=None):
+    """hy_moe_block_bf16: a new device tensor holding the bf16 matrices of t (contiguous,
+    [..., rows, cols], rows % 16 == 0, cols % 64 == 0) in the blocked layout."""
+    import torch
+    if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.dim() < 2:
+        raise TypeError("block_bf16: a contiguous bf16 tensor of at least 2 dimensions")
+    rows, cols = t.shape[-2], t.shape[-1]
+    count = t.numel() // (rows * cols) if rows * cols else 0
+    out = torch.empty_like(t)
+    rc = _lib.hy_moe_block_bf16(t.data_ptr(), out.data_ptr(), count, rows, cols, _stream(stream))
+    if rc != OK:
+        raise HyMoeError(rc, "hy_moe_block_bf16")
+    return out
+
+
+def block_layer(inp, stream=None):
+    """A copy of a bf16 layer dict (hy_inputs.dev_layer) whose routed and shared expert
+    matrices are in the blocked layout (the other entries are shared, not copied)."""
+    out = dict(inp)
+    for key in ("gate", "up", "down"):
+        out[key] = block_bf16(inp[key], stream)
+    out["shared"] = {key: block_bf16(v, stream) for key, v in inp["shared"].items()}
+    return out
 
 
 def probe_mfma_bf16(operands, stream=None) -> float:

@@ -12,7 +12,7 @@ OBJ = os.path.join(PKG, "_build_obj")
 LIB = os.path.join(PKG, "libhy_moe.so")
 
 SOURCES = ["hy_moe_api.hip", "moe_route.hip", "moe_permute.hip", "moe_stream.hip", "moe_gemm.hip",
-           "moe_combine.hip", "hy_moe_probe.hip", "hy_indexer.hip", "moe_quant.hip"]
+           "moe_combine.hip", "hy_moe_probe.hip", "hy_indexer.hip", "moe_quant.hip", "moe_layout.hip"]
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -26,7 +26,7 @@ struct Layout {
 
 bool valid_format(int f) {
   return f == HY_MOE_WEIGHTS_BF16 || f == HY_MOE_WEIGHTS_SHERRY_TERNARY || f == HY_MOE_WEIGHTS_FP8_E4M3 ||
-         f == HY_MOE_WEIGHTS_FP8_W8A8;
+         f == HY_MOE_WEIGHTS_FP8_W8A8 || f == HY_MOE_WEIGHTS_BF16_BLOCKED;
 }
 
 // W8A8 runs on the grouped path only, whose y is bf16; it adds the MXFP8 codes and
@@ -98,7 +98,7 @@ int check_args(const hy_moe_args* a) {
   for (const void* p : req)
     if (!aligned(p, 16)) return HY_MOE_ERR_INVALID_ARG;
   if (a->router_bias && !aligned(a->router_bias, 4)) return HY_MOE_ERR_INVALID_ARG;
-  if (a->expert_format == HY_MOE_WEIGHTS_BF16) {
+  if (a->expert_format == HY_MOE_WEIGHTS_BF16 || a->expert_format == HY_MOE_WEIGHTS_BF16_BLOCKED) {
     const void* w[] = {a->W_gate, a->W_up, a->W_down};
     for (const void* p : w)
       if (!p || !aligned(p, 16)) return HY_MOE_ERR_INVALID_ARG;
@@ -183,6 +183,7 @@ extern "C" int hy_moe_forward_ex(const hy_moe_args* a, void* stream) {
 
   ExpertWeights w{};
   w.ternary = a->expert_format == HY_MOE_WEIGHTS_SHERRY_TERNARY;
+  w.blocked = a->expert_format == HY_MOE_WEIGHTS_BF16_BLOCKED;
   w.fp8 = a->expert_format == HY_MOE_WEIGHTS_FP8_E4M3 || a8;
   w.a8 = a8;
   w.f8gate = (const uint8_t*)a->Wq_gate;

@@ -83,7 +83,8 @@ struct ExpertWeights {
   const uint16_t* s_down;
   bool ternary;
   bool fp8;
-  bool a8;  // with fp8: MXFP8 activations (W8A8)
+  bool a8;       // with fp8: MXFP8 activations (W8A8)
+  bool blocked;  // bf16 in the blocked layout ([rows/16][cols/64][16][64] per matrix, shared expert too)
 };
 
 hipError_t launch_stream_experts(const Plan& p, const uint16_t* x, const ExpertWeights& w, hipStream_t s,
@@ -94,6 +95,8 @@ hipError_t launch_combine(const Plan& p, bool y_is_f32, uint16_t* out, hipStream
 
 hipError_t launch_mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
                               hipStream_t s);
+hipError_t launch_block_bf16(const uint16_t* src, uint16_t* dst, int64_t count, int64_t rows, int64_t cols,
+                             hipStream_t s);
 
 int grouped_gemm_bm();
 int route_split_for(int T, int d, int E);

@@ -78,7 +78,10 @@ static_assert(kF8Ops == kCodeOps, "the code and FP8 load offsets share storage")
 // activations on the FP8 matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4): a k step is
 // 128 codes (128 bytes per row, as the bf16 step's 64 values), two MFMA groups of 64;
 // the activations' E8M0 block scales reach the MFMAs from registers.
-constexpr int kGemmBf16 = 0, kGemmTern = 1, kGemmFp8 = 2, kGemmW8A8 = 3;
+// kGemmBf16Blk: bf16 weights in the blocked layout ([rows/16][cols/64][16][64] per
+// matrix): the bf16 kernel with the weight rows' 128-byte pieces of step ks at
+// 2048 ((row / 16) K/64 + ks) + 128 (row % 16) instead of 2 K row + 128 ks.
+constexpr int kGemmBf16 = 0, kGemmTern = 1, kGemmFp8 = 2, kGemmW8A8 = 3, kGemmBf16Blk = 4;
 constexpr int kBK8 = 128;        // W8A8: k per step
 constexpr int kSub8 = kBK8 / 64;  // W8A8: MFMA groups per step
 
@@ -213,7 +216,7 @@ template <bool GATEUP, int TAILR, int WF>
 __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, ExpertWeights w,
                                                                    uint16_t* __restrict__ h,
                                                                    uint16_t* __restrict__ y) {
-  constexpr bool TERN = WF == kGemmTern, FP8 = WF == kGemmFp8, A8 = WF == kGemmW8A8;
+  constexpr bool TERN = WF == kGemmTern, FP8 = WF == kGemmFp8, A8 = WF == kGemmW8A8, BLK = WF == kGemmBf16Blk;
   constexpr int BS = 3;  // weight (or code) ring slots
   constexpr int kBOps = TERN ? kCodeOps : FP8 ? kF8Ops : kDma;  // weight-side load ops per thread per step
   constexpr int BKE = A8 ? kBK8 : kBK;     // k per step (128 bytes per row either way)
@@ -431,13 +434,25 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
         const int qq = i >> 1;  // 64-row quarter of the tile
         const uint16_t* mat = (qq & 1) == 0 ? (routed ? w.gate + (size_t)e * a.I * a.d : w.s_gate)
                                             : (routed ? w.up + (size_t)e * a.I * a.d : w.s_up);
-        bbase[i] = reinterpret_cast<const char*>(mat + (size_t)(nt * (kRowsMax / 2) + 64 * (qq >> 1)) * a.d);
-        boff[i] = ((uint32_t)(row & 63) * (uint32_t)a.d + 8 * lc) * 2u;
+        const int r0 = nt * (kRowsMax / 2) + 64 * (qq >> 1), rr = row & 63;  // the quarter's first unit, row in it
+        if constexpr (BLK) {
+          bbase[i] = reinterpret_cast<const char*>(mat + (size_t)(r0 / 16) * (a.d / 64) * 1024);
+          boff[i] = ((uint32_t)(rr / 16) * (uint32_t)(a.d / 64) * 1024u + (uint32_t)(rr % 16) * 64u + 8 * lc) * 2u;
+        } else {
+          bbase[i] = reinterpret_cast<const char*>(mat + (size_t)r0 * a.d);
+          boff[i] = ((uint32_t)rr * (uint32_t)a.d + 8 * lc) * 2u;
+        }
       } else {
         aoff[i] = ((uint32_t)grow * (uint32_t)a.I + 8 * lc) * 2u;
         const uint16_t* mat = routed ? w.down + (size_t)e * a.d * a.I : w.s_down;
-        bbase[i] = reinterpret_cast<const char*>(mat + (size_t)nt * kRowsMax * a.I);
-        boff[i] = ((uint32_t)(min(nt * kRowsMax + row, a.d - 1) - nt * kRowsMax) * (uint32_t)a.I + 8 * lc) * 2u;
+        const int rr = min(nt * kRowsMax + row, a.d - 1) - nt * kRowsMax;  // output column in the tile, clamped
+        if constexpr (BLK) {
+          bbase[i] = reinterpret_cast<const char*>(mat + (size_t)(nt * kRowsMax / 16) * (a.I / 64) * 1024);
+          boff[i] = ((uint32_t)(rr / 16) * (uint32_t)(a.I / 64) * 1024u + (uint32_t)(rr % 16) * 64u + 8 * lc) * 2u;
+        } else {
+          bbase[i] = reinterpret_cast<const char*>(mat + (size_t)nt * kRowsMax * a.I);
+          boff[i] = ((uint32_t)rr * (uint32_t)a.I + 8 * lc) * 2u;
+        }
       }
     }
     // Ternary codes: op i of a thread loads word min(lane % 4, 2) of the step's window of
@@ -551,7 +566,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
                                          0);
     };
     auto issue_b = [&](int ks, uint8_t* st, auto i0_tag, auto i1_tag) {
-      const int kb = ks * kRowBytes;
+      const int kb = ks * (BLK ? 16 * kRowBytes : kRowBytes);  // blocked: the next 2 KB block
       uint8_t* db = st + (64 * wv) * 16;
 #pragma unroll
       for (int i = decltype(i0_tag)::value; i < decltype(i1_tag)::value; ++i)
@@ -1071,7 +1086,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
   }
 }
 
-static int g_grid[8][64];  // persistent grid per (kernel kind, device), 0 = not yet computed
+static int g_grid[10][64];  // persistent grid per (kernel kind, device), 0 = not yet computed
 
 static int persistent_grid(int kind, const void* kernel) {
   int dev = 0;
@@ -1123,9 +1138,11 @@ hipError_t launch_grouped_experts(const Plan& p, const uint16_t* x, const Expert
     return err == hipSuccess ? m.mark(s) : err;
   }
   if (!w.ternary && !w.fp8) {
-    err = launch_gemm(pick_gemm<true, kGemmBf16>(p.d), 0, a, 0, w, p, s);
+    const GemmKern gu = w.blocked ? pick_gemm<true, kGemmBf16Blk>(p.d) : pick_gemm<true, kGemmBf16>(p.d);
+    const GemmKern dn = w.blocked ? pick_gemm<false, kGemmBf16Blk>(p.I) : pick_gemm<false, kGemmBf16>(p.I);
+    err = launch_gemm(gu, w.blocked ? 8 : 0, a, 0, w, p, s);
     if (err == hipSuccess) err = m.mark(s);
-    if (err == hipSuccess) err = launch_gemm(pick_gemm<false, kGemmBf16>(p.I), 1, a, 0, w, p, s);
+    if (err == hipSuccess) err = launch_gemm(dn, w.blocked ? 9 : 1, a, 0, w, p, s);
     return err == hipSuccess ? m.mark(s) : err;
   }
   // ternary or FP8 routed experts, then the bf16 shared expert, per phase

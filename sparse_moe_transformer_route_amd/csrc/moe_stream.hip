@@ -64,7 +64,11 @@ constexpr int kDepthFp8GateUp = 2;
 constexpr int kDepthFp8Down = 1;
 
 // Weight formats of the streaming kernels.
-constexpr int kWfBf16 = 0, kWfTern = 1, kWfFp8 = 2;
+// kWfBf16Blk: bf16 in the blocked layout ([rows/16][cols/64][16][64] per matrix): a
+// wave's 16 rows of one 64-column chunk are one contiguous 2 KB run, the next chunk
+// 2 KB further on.
+constexpr int kWfBf16 = 0, kWfTern = 1, kWfFp8 = 2, kWfBf16Blk = 3;
+constexpr int kBlkChunk = 16 * kChunk;  // elements from one chunk of a row to the next, blocked layout
 
 // Drives a register ring of D + 1 slots over n items in order: load(i, slot) issues
 // the loads of item i into a slot, use(slot) consumes it, D items ahead of the loads.
@@ -104,7 +108,8 @@ __device__ __forceinline__ void ring_stream(int n, Load&& load, Use&& use) {
   }
 }
 
-template <int D>
+// WS: elements from one chunk of a weight row to the next (kChunk row-major, kBlkChunk blocked)
+template <int D, int WS = kChunk>
 __device__ __forceinline__ void gateup_bf16_block(const uint16_t* __restrict__ wg, const uint16_t* __restrict__ wu,
                                                   const uint16_t* __restrict__ xr, int d, f32x4& accg,
                                                   f32x4& accu) {
@@ -114,8 +119,8 @@ __device__ __forceinline__ void gateup_bf16_block(const uint16_t* __restrict__ w
       [&](int ch, int slot) {
 #pragma unroll
         for (int v = 0; v < kKV; ++v) {
-          rg[slot][v] = ldg16(wg + ch * kChunk + 8 * v);
-          ru[slot][v] = ldg16(wu + ch * kChunk + 8 * v);
+          rg[slot][v] = ldg16(wg + ch * WS + 8 * v);
+          ru[slot][v] = ldg16(wu + ch * WS + 8 * v);
           rx[slot][v] = ldg16(xr + ch * kChunk + 8 * v);
         }
       },
@@ -188,7 +193,7 @@ __device__ __forceinline__ void down_fp8_block(const uint8_t* const (&wd)[NR], c
       });
 }
 
-template <int D>
+template <int D, int WS = kChunk>
 __device__ __forceinline__ void down_bf16_block(const uint16_t* __restrict__ wd, const uint16_t* __restrict__ hr,
                                                 int I, f32x4& acc) {
   uint4 rw[D + 1][kKV], rx[D + 1][kKV];
@@ -197,7 +202,7 @@ __device__ __forceinline__ void down_bf16_block(const uint16_t* __restrict__ wd,
       [&](int ch, int slot) {
 #pragma unroll
         for (int v = 0; v < kKV; ++v) {
-          rw[slot][v] = ldg16(wd + ch * kChunk + 8 * v);
+          rw[slot][v] = ldg16(wd + ch * WS + 8 * v);
           rx[slot][v] = ldg16(hr + ch * kChunk + 8 * v);
         }
       },
@@ -295,7 +300,7 @@ __device__ __forceinline__ int shared_slots(const StreamArgs& a, bool tern) {
 
 template <int WF>
 __global__ void __launch_bounds__(256) stream_gateup_kernel(StreamArgs a, ExpertWeights w, uint16_t* __restrict__ h) {
-  constexpr bool TERN = WF == kWfTern, FP8 = WF == kWfFp8, WIDE = TERN || FP8;
+  constexpr bool TERN = WF == kWfTern, FP8 = WF == kWfFp8, WIDE = TERN || FP8, BLK = WF == kWfBf16Blk;
   __shared__ uint2 lut[32];
   if (TERN) {
     build_code_table(lut);
@@ -362,14 +367,16 @@ __global__ void __launch_bounds__(256) stream_gateup_kernel(StreamArgs a, Expert
 #pragma unroll 1
     for (int sub = sub_first; sub < sub_last; ++sub) {
     const int i0 = blockIdx.x * (WIDE ? 128 : 64) + sub * 64 + wv * 16;
-    const uint16_t* wg = (routed ? w.gate + (size_t)e * I * d : w.s_gate) + (size_t)(i0 + r16) * d + kKV * 8 * g;
-    const uint16_t* wu = (routed ? w.up + (size_t)e * I * d : w.s_up) + (size_t)(i0 + r16) * d + kKV * 8 * g;
+    // row i0 + r16: row-major, or row r16 of block row i0 / 16 in the blocked layout
+    const size_t roff = BLK ? (size_t)(i0 / 16) * (d / 64) * 1024 + 64 * r16 : (size_t)(i0 + r16) * d;
+    const uint16_t* wg = (routed ? w.gate + (size_t)e * I * d : w.s_gate) + roff + kKV * 8 * g;
+    const uint16_t* wu = (routed ? w.up + (size_t)e * I * d : w.s_up) + roff + kKV * 8 * g;
     for (int cb = cb_first; cb < n; cb += 16) {
       const bool valid = cb + r16 < n;
       const int col = valid ? row0 + cb + r16 : row0;
       const uint16_t* xr = a.x + (size_t)row_token(col, a.perm_src, a.Tk, a.k) * d + kKV * 8 * g;
       f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-      gateup_bf16_block<WIDE ? kDepthSharedTern : kDepthGateUp>(wg, wu, xr, d, accg, accu);
+      gateup_bf16_block<WIDE ? kDepthSharedTern : kDepthGateUp, BLK ? kBlkChunk : kChunk>(wg, wu, xr, d, accg, accu);
       if (valid) {
         uint2 v = make_uint2(pack_bf16x2(silu(accg[0]) * accu[0], silu(accg[1]) * accu[1]),
                              pack_bf16x2(silu(accg[2]) * accu[2], silu(accg[3]) * accu[3]));
@@ -425,7 +432,7 @@ __global__ void __launch_bounds__(256) stream_gateup_kernel(StreamArgs a, Expert
 template <int WF>
 __global__ void __launch_bounds__(256) stream_down_kernel(StreamArgs a, ExpertWeights w,
                                                           const uint16_t* __restrict__ h, float* __restrict__ y) {
-  constexpr bool TERN = WF == kWfTern, FP8 = WF == kWfFp8, WIDE = TERN || FP8;
+  constexpr bool TERN = WF == kWfTern, FP8 = WF == kWfFp8, WIDE = TERN || FP8, BLK = WF == kWfBf16Blk;
   __shared__ uint2 lut[32];
   if (TERN) {
     build_code_table(lut);
@@ -482,12 +489,14 @@ __global__ void __launch_bounds__(256) stream_down_kernel(StreamArgs a, ExpertWe
 #pragma unroll 1
     for (int sub = sub_first; sub < sub_last; ++sub) {
     const int m0 = blockIdx.x * (WIDE ? 128 : 64) + sub * 64 + wv * 16;
-    const uint16_t* wd = (routed ? w.down + (size_t)e * d * I : w.s_down) + (size_t)(m0 + r16) * I + kKV * 8 * g;
+    const size_t roff = BLK ? (size_t)(m0 / 16) * (I / 64) * 1024 + 64 * r16 : (size_t)(m0 + r16) * I;
+    const uint16_t* wd = (routed ? w.down + (size_t)e * d * I : w.s_down) + roff + kKV * 8 * g;
     for (int cb = cb_first; cb < n; cb += 16) {
       const bool valid = cb + r16 < n;
       const int col = valid ? row0 + cb + r16 : row0;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      down_bf16_block<WIDE ? kDepthSharedTern : kDepthDown>(wd, h + (size_t)col * I + kKV * 8 * g, I, acc);
+      down_bf16_block<WIDE ? kDepthSharedTern : kDepthDown, BLK ? kBlkChunk : kChunk>(
+          wd, h + (size_t)col * I + kKV * 8 * g, I, acc);
       if (valid)
         *reinterpret_cast<float4*>(y + (size_t)col * d + m0 + 4 * g) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
@@ -770,10 +779,12 @@ hipError_t launch_stream_experts(const Plan& p, const uint16_t* x, const ExpertW
   dim3 g1(p.I / rows_wg, slots), g2(p.d / rows_wg, slots);
   const auto gu = w.ternary ? stream_gateup_kernel<kWfTern>
                   : w.fp8   ? stream_gateup_kernel<kWfFp8>
-                            : stream_gateup_kernel<kWfBf16>;
+                  : w.blocked ? stream_gateup_kernel<kWfBf16Blk>
+                              : stream_gateup_kernel<kWfBf16>;
   const auto dn = w.ternary ? stream_down_kernel<kWfTern>
                   : w.fp8   ? stream_down_kernel<kWfFp8>
-                            : stream_down_kernel<kWfBf16>;
+                  : w.blocked ? stream_down_kernel<kWfBf16Blk>
+                              : stream_down_kernel<kWfBf16>;
   hipLaunchKernelGGL(gu, g1, dim3(256), 0, s, a, w, p.h);
   hipError_t err = hipGetLastError();
   if (err == hipSuccess) err = m.mark(s);

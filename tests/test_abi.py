@@ -290,3 +290,31 @@ def test_mxfp8_quantize_argument_checks():
     assert L.hy_moe_mxfp8_quantize(FAKE + 8, 4, 64, FAKE, FAKE, None) == hm.ERR_INVALID_ARG
     assert L.hy_moe_mxfp8_quantize(FAKE, 0, 64, None, None, None) == hm.OK              # empty: no-op
 
+
+
+def test_block_bf16_argument_checks():
+    L = hm.lib()
+    BIG = 0x10000000  # far from FAKE: the buffers do not overlap
+    assert L.hy_moe_block_bf16(FAKE, BIG, 2, 24, 128, None) == hm.ERR_INVALID_ARG     # rows % 16
+    assert L.hy_moe_block_bf16(FAKE, BIG, 2, 32, 96, None) == hm.ERR_INVALID_ARG      # cols % 64
+    assert L.hy_moe_block_bf16(FAKE, BIG, -1, 32, 128, None) == hm.ERR_INVALID_ARG
+    assert L.hy_moe_block_bf16(None, BIG, 2, 32, 128, None) == hm.ERR_INVALID_ARG
+    assert L.hy_moe_block_bf16(FAKE, BIG + 8, 2, 32, 128, None) == hm.ERR_INVALID_ARG  # misaligned
+    # overlapping buffers: 2 x 32 x 128 bf16 = 16 KB from FAKE; dst 4 KB in
+    assert L.hy_moe_block_bf16(FAKE, FAKE + 4096, 2, 32, 128, None) == hm.ERR_INVALID_ARG
+    assert L.hy_moe_block_bf16(FAKE + 4096, FAKE, 2, 32, 128, None) == hm.ERR_INVALID_ARG
+    assert L.hy_moe_block_bf16(None, None, 0, 32, 128, None) == hm.OK                  # empty: no-op
+
+
+def test_blocked_format_checks_and_workspace():
+    # the blocked format takes the bf16 pointers, checks and workspace
+    a = base_args(T=4, d=512, E=16, k=2, I=256)
+    a.expert_format = hm.WEIGHTS_BF16_BLOCKED
+    a.W_down = FAKE + 2
+    assert call(a) == hm.ERR_INVALID_ARG
+    a.W_down = None
+    assert call(a) == hm.ERR_INVALID_ARG
+    for T in (1, 32, 8192):
+        assert hm.workspace_size(T, 6144, 256, 8, 2048, hm.WEIGHTS_BF16_BLOCKED) == \
+            hm.workspace_size(T, 6144, 256, 8, 2048, hm.WEIGHTS_BF16)
+    assert hm.workspace_size(4, 512, 16, 2, 256, 5) == 0  # no such format

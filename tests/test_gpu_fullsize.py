@@ -171,6 +171,24 @@ def test_skewed_paths_agree(hy4_weights):
     assert ((fa - fb).abs() <= 2e-2 * (1 + fb.abs())).all()
 
 
+def test_blocked_weights_full_size(hy4_weights):
+    """The blocked layout of the same weights gives bitwise the same outputs and routing
+    as the row-major one at the decode, prefill and skewed sizes (the streaming path, the
+    grouped path at every tile height, and the skewed hottest expert's 16 M tiles)."""
+    blk = hm.block_layer(hy4_weights)
+    for name in ("decode", "prefill", "skewed"):
+        cfg = hi.CONFIGS[name]
+        say(f"[case] {name} T={cfg.T}: blocked bf16 weights vs row-major")
+        ref = hm.forward_layer(with_x(cfg, hy4_weights), cfg.k, want_routing=True)
+        got = hm.forward_layer(with_x(cfg, blk), cfg.k, want_routing=True, weights_blocked=True)
+        torch.cuda.synchronize()
+        assert torch.equal(got["out"].view(torch.int16), ref["out"].view(torch.int16)), name
+        for key in ("topk_idx", "counts", "perm_src"):
+            assert torch.equal(got[key], ref[key]), (name, key)
+    del blk
+    torch.cuda.empty_cache()
+
+
 def test_ternary_full_size():
     cfg = hi.CONFIGS["ternary"]
     inp = hi.dev_layer(cfg, device=DEV)

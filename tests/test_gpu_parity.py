@@ -363,6 +363,43 @@ def test_bitwise_deterministic_and_workspace_independent(path):
         assert torch.equal(r1[key], r3[key]), key
 
 
+# ------------------------------------------------------------ blocked bf16 layout
+def test_block_bf16_matches_layout_definition():
+    """hy_moe_block_bf16 against the layout's definition, written out element by element:
+    row r's 64 values in columns [64 c, 64 c + 64) start at element
+    1024 ((r / 16) (K / 64) + c) + 64 (r % 16) of its matrix."""
+    say("[case] block_bf16 on 3 matrices of 48 x 192")
+    g = torch.Generator(device=DEV).manual_seed(5)
+    t = torch.randn(3, 48, 192, generator=g, device=DEV).to(torch.bfloat16)
+    b = hm.block_bf16(t)
+    torch.cuda.synchronize()
+    src = t.view(torch.int16).cpu().numpy()
+    got = b.view(torch.int16).cpu().numpy().reshape(3, -1)
+    R, K = 48, 192
+    exp = np.zeros_like(got)
+    for m in range(3):
+        for r in range(R):
+            for c in range(K // 64):
+                o = 1024 * ((r // 16) * (K // 64) + c) + 64 * (r % 16)
+                exp[m, o:o + 64] = src[m, r, 64 * c:64 * c + 64]
+    assert np.array_equal(got, exp)
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("shape", [(40, 512, 16, 2, 256), (300, 768, 8, 2, 384), (33, 256, 4, 4, 128)])
+def test_blocked_weights_match_row_major(shape, path):
+    T, d, E, k, I = shape
+    say(f"[case] blocked bf16 weights T={T} d={d} E={E} k={k} I={I} path={path}")
+    cfg = hi.LayerConfig("blk", T=T, d=d, E=E, k=k, I=I, seed=31)
+    inp = hi.dev_layer(cfg, device=DEV)
+    ref = hm.forward_layer(inp, k, want_routing=True, path=path)
+    got = hm.forward_layer(hm.block_layer(inp), k, want_routing=True, path=path, weights_blocked=True)
+    torch.cuda.synchronize()
+    assert torch.equal(got["out"].view(torch.int16), ref["out"].view(torch.int16))
+    for key in ("topk_idx", "counts", "perm_src"):
+        assert torch.equal(got[key], ref[key])
+
+
 # ------------------------------------------------- large cancelling expert outputs
 def _bits_to_f32(b):
     return (b.astype(np.uint32) << 16).view(np.float32)
