@@ -209,7 +209,8 @@ def stream_work(cfg, touched, blocked=False):
     layer_bytes += cfg.E * d * 2 + 2 * cfg.T * d * 2
     # ternary weights with d and I multiples of 512 run in the LDS-staged kernel
     tern_lds = cfg.ternary and d % 512 == 0 and I % 512 == 0
-    kernel = ("tern_lds_kernel<2>" if tern_lds else "stream_gateup_kernel<2> (FP8 routed experts)" if cfg.fp8
+    kernel = (("tern_lds_kernel<2, true> (blocked Sherry codes)" if blocked else "tern_lds_kernel<2, false>")
+              if tern_lds else "stream_gateup_kernel<2> (FP8 routed experts)" if cfg.fp8
               else "stream_gateup_kernel<3> (blocked bf16 weights)" if blocked else "stream_gateup_kernel<0>")
     return {"unit": unit, "alg": alg, "per_unit": per_unit, "layer_bytes": layer_bytes,
             "key": "ternary_gateup" if tern_lds else "stream_gateup", "kernel": kernel}
@@ -221,7 +222,8 @@ def gemm_work(cfg, blocked=False):
     three expert products)."""
     d, I = cfg.d, cfg.I
     rows = cfg.T * cfg.k + cfg.T
-    kernel = ("grouped_gemm_kernel<true, 0, 1> (ternary routed tiles) + grouped_gemm_kernel<true, 0, 0> "
+    kernel = (f"grouped_gemm_kernel<true, 0, {5 if blocked else 1}> (ternary routed tiles"
+              f"{', blocked Sherry codes' if blocked else ''}) + grouped_gemm_kernel<true, 0, 0> "
               "(bf16 shared tiles): one timed stage" if cfg.ternary else
               "mx_quantize_kernel (token rows to MXFP8) + grouped_gemm_kernel<true, 0, 3> (FP8 MFMAs on the W8A8 "
               "routed tiles) + grouped_gemm_kernel<true, 0, 0> (bf16 shared tiles): one timed stage" if cfg.a8 else
@@ -271,13 +273,14 @@ def input_digest(inp, torch):
 def run_config(name, args, hi, hm, torch, weights=None, steps=None, flush=None, blocked=False, rm_weights=None):
     """Times workload `name`. weights: a bf16 layer dict to take the expert weights from
     (already in the blocked layout when blocked is set; rm_weights then holds the same
-    weights row-major). blocked (bf16 workloads): the HY_MOE_WEIGHTS_BF16_BLOCKED format,
-    weights converted once before anything is timed. res["inp_rm"] is the input set with
-    row-major weights (what the oracle reads)."""
+    weights row-major). blocked: the blocked layout of bf16 weights
+    (HY_MOE_WEIGHTS_BF16_BLOCKED) or of Sherry codes (HY_MOE_WEIGHTS_SHERRY_BLOCKED, d and I
+    multiples of 512), converted once before anything is timed; FP8 workloads ignore it.
+    res["inp_rm"] is the input set with row-major weights (what the oracle reads)."""
     cfg = hi.CONFIGS[name]
     dev = "cuda:0"
     bf16 = not cfg.ternary and not cfg.fp8
-    blocked = blocked and bf16
+    blocked = blocked and (bf16 or (cfg.ternary and cfg.d % 512 == 0 and cfg.I % 512 == 0))
 
     def with_x(wts):
         d = dict(wts)
@@ -292,7 +295,8 @@ def run_config(name, args, hi, hm, torch, weights=None, steps=None, flush=None, 
     else:
         inp = with_x(weights)
         inp_rm = with_x(rm_weights) if blocked else inp
-    fmt = (hm.WEIGHTS_SHERRY_TERNARY if cfg.ternary else hm.WEIGHTS_FP8_W8A8 if cfg.a8 else
+    fmt = ((hm.WEIGHTS_SHERRY_BLOCKED if blocked else hm.WEIGHTS_SHERRY_TERNARY) if cfg.ternary else
+           hm.WEIGHTS_FP8_W8A8 if cfg.a8 else
            hm.WEIGHTS_FP8_E4M3 if cfg.fp8 else hm.WEIGHTS_BF16_BLOCKED if blocked else hm.WEIGHTS_BF16)
     fwd_kw = {"fp8_activations": True} if cfg.a8 else {"weights_blocked": True} if blocked else {}
     ws = hm.alloc_workspace(cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, fmt, device=dev)
@@ -367,7 +371,9 @@ def workload_object(res, extra=None):
 def layout_name(res):
     c = res["cfg"]
     if c.ternary:
-        return "Sherry-packed routed experts, row-major bf16 shared expert"
+        return ("Sherry-packed routed experts in the blocked layout (16 rows x 512 weights per 1280 B block, "
+                "hy_moe_block_sherry, converted once before timing), row-major bf16 shared expert" if res["blocked"]
+                else "Sherry-packed routed experts (row-major codes), row-major bf16 shared expert")
     if c.fp8:
         return "row-major E4M3 routed experts, row-major bf16 shared expert"
     return ("blocked bf16 (16 rows x 64 columns per 2 KB block, hy_moe_block_bf16, converted once before timing)"
@@ -670,8 +676,9 @@ def main():
             f"p10 {res['step_ms']['p10']:.3f}, p90 {res['step_ms']['p90']:.3f}), {res['tokens_per_s']:.1f} tokens/s, "
             f"kernels {json.dumps({k: round(v, 4) for k, v in res['kernels_ms'].items()})}")
 
-    # bf16 workloads run on the blocked layout of the same weights (one conversion,
-    # outside every timed region); the headline is timed on row-major weights as well
+    # bf16 and ternary workloads run on the blocked layout of the same weights (one
+    # conversion, outside every timed region); the headline is timed on row-major
+    # weights as well
     blocked_weights = hm.block_layer(shared_weights) if shared_weights is not None else None
     torch.cuda.synchronize()
     extra = {}
@@ -712,7 +719,7 @@ def main():
                                                "empty_experts": int((cnt == 0).sum())})
         del sk
         torch.cuda.empty_cache()
-        tn = run_config("ternary", args, hi, hm, torch, flush=flush)
+        tn = run_config("ternary", args, hi, hm, torch, flush=flush, blocked=True)
         report(tn)
         extra["ternary"] = workload_object(tn)
         del tn

@@ -101,7 +101,18 @@ typedef enum {
    * streaming path reads from HBM faster than 16 rows a whole row apart. Results are
    * bitwise identical to HY_MOE_WEIGHTS_BF16 on the same weights. hy_moe_block_bf16
    * converts row-major matrices. */
-  HY_MOE_WEIGHTS_BF16_BLOCKED = 4
+  HY_MOE_WEIGHTS_BF16_BLOCKED = 4,
+  /* Sherry ternary codes as HY_MOE_WEIGHTS_SHERRY_TERNARY (the same pointers, scales and
+   * sizes; ai.chattools.top article, section on Sherry and MIX-STQ1_0), each code matrix
+   * stored in this library's blocked layout: a matrix of R rows whose K weights per row
+   * pack into K/128 * 20 bytes becomes [R/16][K/512][16][80 bytes]: the 80 code bytes of
+   * row r for weights [512 c, 512 c + 512) start at byte 1280 * ((r / 16) * (K / 512) + c)
+   * + 80 * (r % 16). Each 16-row group's slab is then 1280 bytes, exactly ten 128-byte
+   * lines, instead of 16 pieces of 80 bytes that straddle lines. Needs d % 512 == 0 and
+   * I % 512 == 0 and 16-byte aligned code arrays (HY_MOE_ERR_UNSUPPORTED /
+   * HY_MOE_ERR_INVALID_ARG otherwise). Results are bitwise identical to
+   * HY_MOE_WEIGHTS_SHERRY_TERNARY on the same codes. hy_moe_block_sherry converts. */
+  HY_MOE_WEIGHTS_SHERRY_BLOCKED = 5
 } hy_moe_wfmt;
 
 /* Which kernels run the experts. AUTO picks by the average rows per expert. */
@@ -267,6 +278,19 @@ int hy_moe_mxfp8_quantize(const void* x, int64_t rows, int64_t cols, void* codes
  * HY_MOE_ERR_HIP. count == 0 is a no-op.
  */
 int hy_moe_block_bf16(const void* src, void* dst, int64_t count, int64_t rows, int64_t cols, void* stream);
+
+/*
+ * hy_moe_block_sherry — rewrites Sherry code matrices (the packing of
+ * HY_MOE_WEIGHTS_SHERRY_TERNARY) in the layout of HY_MOE_WEIGHTS_SHERRY_BLOCKED.
+ *   src    DEVICE, `count` code matrices of `rows` rows of cols / 128 * 20 bytes (cols
+ *          weights per row) back to back, 16-byte aligned
+ *   dst    DEVICE, the same size, 16-byte aligned, not overlapping src (out)
+ *   count >= 0, rows % 16 == 0, cols % 512 == 0, rows > 0, cols > 0
+ * Enqueued on `stream` without blocking. Returns HY_MOE_OK, HY_MOE_ERR_INVALID_ARG
+ * (null or misaligned pointers, overlapping buffers, bad sizes; nothing enqueued) or
+ * HY_MOE_ERR_HIP. count == 0 is a no-op.
+ */
+int hy_moe_block_sherry(const void* src, void* dst, int64_t count, int64_t rows, int64_t cols, void* stream);
 
 /*
  * Machine-peak probes (not part of the layer): the rates this GPU reaches, for

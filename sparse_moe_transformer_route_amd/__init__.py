@@ -24,14 +24,15 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhy_moe.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
-WEIGHTS_BF16, WEIGHTS_SHERRY_TERNARY, WEIGHTS_FP8_E4M3, WEIGHTS_FP8_W8A8, WEIGHTS_BF16_BLOCKED = 0, 1, 2, 3, 4
+WEIGHTS_BF16, WEIGHTS_SHERRY_TERNARY, WEIGHTS_FP8_E4M3, WEIGHTS_FP8_W8A8 = 0, 1, 2, 3
+WEIGHTS_BF16_BLOCKED, WEIGHTS_SHERRY_BLOCKED = 4, 5
 PATH_AUTO, PATH_STREAM, PATH_GROUPED = 0, 1, 2
 KERNELS = ["route_logits", "route_topk", "permute_scan", "permute_scatter", "expert_gateup", "expert_down",
            "combine"]
 NUM_STAGE_EVENTS = len(KERNELS) + 1
 
 EXPORTED = ["hy_moe_forward", "hy_moe_forward_ex", "hy_moe_forward_noalloc", "hy_moe_workspace_size",
-            "hy_moe_status_string", "hy_moe_sherry_pack_host", "hy_moe_mxfp8_quantize", "hy_moe_block_bf16", "hy_moe_probe_mfma_bf16", "hy_moe_probe_mfma_fp8", "hy_moe_probe_hbm_read",
+            "hy_moe_status_string", "hy_moe_sherry_pack_host", "hy_moe_mxfp8_quantize", "hy_moe_block_bf16", "hy_moe_block_sherry", "hy_moe_probe_mfma_bf16", "hy_moe_probe_mfma_fp8", "hy_moe_probe_hbm_read",
             "hy_indexer_workspace_size", "hy_indexer_topk"]
 PROBE_OPERAND_BYTES = 65536
 NOALLOC_SCRATCH_BYTES = 64 << 20  # HY_MOE_NOALLOC_SCRATCH_BYTES
@@ -85,6 +86,8 @@ def _load():
     L.hy_moe_mxfp8_quantize.restype = ctypes.c_int
     L.hy_moe_block_bf16.argtypes = [vp, vp, i64, i64, i64, vp]
     L.hy_moe_block_bf16.restype = ctypes.c_int
+    L.hy_moe_block_sherry.argtypes = [vp, vp, i64, i64, i64, vp]
+    L.hy_moe_block_sherry.restype = ctypes.c_int
     L.hy_moe_probe_mfma_bf16.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_float), vp]
     L.hy_moe_probe_mfma_bf16.restype = ctypes.c_int
     L.hy_moe_probe_mfma_fp8.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_float), vp]
@@ -160,8 +163,9 @@ def forward_layer(inp: dict, k: int, *, want_routing=False, path=PATH_AUTO, work
     fp8_activations (FP8 weights only): the W8A8 format, MXFP8 activations; with
     want_hidden also hidden_codes [T*k][I] and hidden_scales [T*k][I/32] (the routed
     hidden rows as the down projection reads them, dispatched-row order).
-    weights_blocked (bf16 weights only): gate/up/down and the shared expert's matrices
-    are in the blocked layout (block_layer), the HY_MOE_WEIGHTS_BF16_BLOCKED format."""
+    weights_blocked: the weights are in the blocked layout (block_layer): bf16 gate/up/down
+    and the shared expert's matrices (HY_MOE_WEIGHTS_BF16_BLOCKED), or the Sherry code
+    matrices (HY_MOE_WEIGHTS_SHERRY_BLOCKED; the bf16 shared expert stays row-major)."""
     import torch
     x = inp["x"]
     T, d = x.shape
@@ -183,9 +187,9 @@ def forward_layer(inp: dict, k: int, *, want_routing=False, path=PATH_AUTO, work
     a.x, a.W_router, a.router_bias = _ptr(x), _ptr(inp["router"]), _ptr(inp.get("bias"))
     if fp8_activations and not fp8:
         raise ValueError("forward_layer: fp8_activations needs FP8 weights")
-    if weights_blocked and (fp8 or ternary):
-        raise ValueError("forward_layer: weights_blocked applies to bf16 weights")
-    a.expert_format = (WEIGHTS_SHERRY_TERNARY if ternary else
+    if weights_blocked and fp8:
+        raise ValueError("forward_layer: weights_blocked applies to bf16 and Sherry weights")
+    a.expert_format = ((WEIGHTS_SHERRY_BLOCKED if weights_blocked else WEIGHTS_SHERRY_TERNARY) if ternary else
                        (WEIGHTS_FP8_W8A8 if fp8_activations else WEIGHTS_FP8_E4M3) if fp8 else
                        WEIGHTS_BF16_BLOCKED if weights_blocked else WEIGHTS_BF16)
     if ternary:
@@ -285,10 +289,30 @@ def block_bf16(t, stream=None):
     return out
 
 
+def block_sherry(q, stream=None):
+    """hy_moe_block_sherry: a new device tensor holding the Sherry code matrices of q
+    (contiguous int32, [..., rows, K/128*5], rows % 16 == 0, K % 512 == 0) blocked."""
+    import torch
+    if q.dtype != torch.int32 or not q.is_contiguous() or q.dim() < 2:
+        raise TypeError("block_sherry: a contiguous int32 tensor of at least 2 dimensions")
+    rows, words = q.shape[-2], q.shape[-1]
+    count = q.numel() // (rows * words) if rows * words else 0
+    out = torch.empty_like(q)
+    rc = _lib.hy_moe_block_sherry(q.data_ptr(), out.data_ptr(), count, rows, words // 5 * 128, _stream(stream))
+    if rc != OK:
+        raise HyMoeError(rc, "hy_moe_block_sherry")
+    return out
+
+
 def block_layer(inp, stream=None):
-    """A copy of a bf16 layer dict (hy_inputs.dev_layer) whose routed and shared expert
-    matrices are in the blocked layout (the other entries are shared, not copied)."""
+    """A copy of a layer dict (hy_inputs.dev_layer) with its weights in the blocked
+    layout: a bf16 layer's routed and shared expert matrices, or a Sherry layer's code
+    matrices (the other entries are shared, not copied)."""
     out = dict(inp)
+    if "qgate" in inp:
+        for key in ("qgate", "qup", "qdown"):
+            out[key] = block_sherry(inp[key], stream)
+        return out
     for key in ("gate", "up", "down"):
         out[key] = block_bf16(inp[key], stream)
     out["shared"] = {key: block_bf16(v, stream) for key, v in inp["shared"].items()}

@@ -26,7 +26,7 @@ struct Layout {
 
 bool valid_format(int f) {
   return f == HY_MOE_WEIGHTS_BF16 || f == HY_MOE_WEIGHTS_SHERRY_TERNARY || f == HY_MOE_WEIGHTS_FP8_E4M3 ||
-         f == HY_MOE_WEIGHTS_FP8_W8A8 || f == HY_MOE_WEIGHTS_BF16_BLOCKED;
+         f == HY_MOE_WEIGHTS_FP8_W8A8 || f == HY_MOE_WEIGHTS_BF16_BLOCKED || f == HY_MOE_WEIGHTS_SHERRY_BLOCKED;
 }
 
 // W8A8 runs on the grouped path only, whose y is bf16; it adds the MXFP8 codes and
@@ -102,10 +102,17 @@ int check_args(const hy_moe_args* a) {
     const void* w[] = {a->W_gate, a->W_up, a->W_down};
     for (const void* p : w)
       if (!p || !aligned(p, 16)) return HY_MOE_ERR_INVALID_ARG;
-  } else if (a->expert_format == HY_MOE_WEIGHTS_SHERRY_TERNARY) {
+  } else if (a->expert_format == HY_MOE_WEIGHTS_SHERRY_TERNARY || a->expert_format == HY_MOE_WEIGHTS_SHERRY_BLOCKED) {
     const void* w[] = {a->Wq_gate, a->Wq_up, a->Wq_down, a->S_gate, a->S_up, a->S_down};
     for (const void* p : w)
       if (!p || !aligned(p, 4)) return HY_MOE_ERR_INVALID_ARG;
+    if (a->expert_format == HY_MOE_WEIGHTS_SHERRY_BLOCKED) {
+      // the blocked codes run in the LDS-staged kernels only: 512-weight slabs, 16-byte loads
+      const void* q[] = {a->Wq_gate, a->Wq_up, a->Wq_down};
+      for (const void* p : q)
+        if (!aligned(p, 16)) return HY_MOE_ERR_INVALID_ARG;
+      if (a->d % 512 != 0 || a->I % 512 != 0) return HY_MOE_ERR_UNSUPPORTED;
+    }
   } else {
     const void* q[] = {a->Wq_gate, a->Wq_up, a->Wq_down};
     for (const void* p : q)
@@ -182,7 +189,8 @@ extern "C" int hy_moe_forward_ex(const hy_moe_args* a, void* stream) {
   }
 
   ExpertWeights w{};
-  w.ternary = a->expert_format == HY_MOE_WEIGHTS_SHERRY_TERNARY;
+  w.tblocked = a->expert_format == HY_MOE_WEIGHTS_SHERRY_BLOCKED;
+  w.ternary = a->expert_format == HY_MOE_WEIGHTS_SHERRY_TERNARY || w.tblocked;
   w.blocked = a->expert_format == HY_MOE_WEIGHTS_BF16_BLOCKED;
   w.fp8 = a->expert_format == HY_MOE_WEIGHTS_FP8_E4M3 || a8;
   w.a8 = a8;

@@ -84,7 +84,8 @@ struct ExpertWeights {
   bool ternary;
   bool fp8;
   bool a8;       // with fp8: MXFP8 activations (W8A8)
-  bool blocked;  // bf16 in the blocked layout ([rows/16][cols/64][16][64] per matrix, shared expert too)
+  bool blocked;   // bf16 in the blocked layout ([rows/16][cols/64][16][64] per matrix, shared expert too)
+  bool tblocked;  // with ternary: code matrices in the blocked layout ([rows/16][cols/512][16][80 B])
 };
 
 hipError_t launch_stream_experts(const Plan& p, const uint16_t* x, const ExpertWeights& w, hipStream_t s,
@@ -97,6 +98,8 @@ hipError_t launch_mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, uin
                               hipStream_t s);
 hipError_t launch_block_bf16(const uint16_t* src, uint16_t* dst, int64_t count, int64_t rows, int64_t cols,
                              hipStream_t s);
+hipError_t launch_block_sherry(const uint32_t* src, uint32_t* dst, int64_t count, int64_t rows, int64_t cols,
+                               hipStream_t s);
 
 int grouped_gemm_bm();
 int route_split_for(int T, int d, int E);

@@ -81,7 +81,10 @@ static_assert(kF8Ops == kCodeOps, "the code and FP8 load offsets share storage")
 // kGemmBf16Blk: bf16 weights in the blocked layout ([rows/16][cols/64][16][64] per
 // matrix): the bf16 kernel with the weight rows' 128-byte pieces of step ks at
 // 2048 ((row / 16) K/64 + ks) + 128 (row % 16) instead of 2 K row + 128 ks.
-constexpr int kGemmBf16 = 0, kGemmTern = 1, kGemmFp8 = 2, kGemmW8A8 = 3, kGemmBf16Blk = 4;
+// kGemmTernBlk: Sherry codes in the blocked layout ([rows/16][K/512][16][80 B]): the
+// ternary kernel with row r's window of step ks at 1280 ((r / 16) K/512 + ks / 8) +
+// 80 (r % 16) + 4 floor(10 (ks % 8) / 4) instead of K/128 20 r + 4 floor(10 ks / 4).
+constexpr int kGemmBf16 = 0, kGemmTern = 1, kGemmFp8 = 2, kGemmW8A8 = 3, kGemmBf16Blk = 4, kGemmTernBlk = 5;
 constexpr int kBK8 = 128;        // W8A8: k per step
 constexpr int kSub8 = kBK8 / 64;  // W8A8: MFMA groups per step
 
@@ -216,7 +219,8 @@ template <bool GATEUP, int TAILR, int WF>
 __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, ExpertWeights w,
                                                                    uint16_t* __restrict__ h,
                                                                    uint16_t* __restrict__ y) {
-  constexpr bool TERN = WF == kGemmTern, FP8 = WF == kGemmFp8, A8 = WF == kGemmW8A8, BLK = WF == kGemmBf16Blk;
+  constexpr bool TERN = WF == kGemmTern || WF == kGemmTernBlk, FP8 = WF == kGemmFp8, A8 = WF == kGemmW8A8,
+                 BLK = WF == kGemmBf16Blk, TB = WF == kGemmTernBlk;
   constexpr int BS = 3;  // weight (or code) ring slots
   constexpr int kBOps = TERN ? kCodeOps : FP8 ? kF8Ops : kDma;  // weight-side load ops per thread per step
   constexpr int BKE = A8 ? kBK8 : kBK;     // k per step (128 bytes per row either way)
@@ -464,15 +468,20 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
       const uint32_t rw = (uint32_t)(K / 128 * 20);  // code bytes per weight row
       const int rr = 16 * wv + (lane >> 2);
       const uint32_t wo = 4u * (uint32_t)min(lane & 3, 2);
+      const uint32_t bstride = (uint32_t)(K / 512) * 1280u;  // blocked: bytes per 16-row group
 #pragma unroll
       for (int i = 0; i < kCodeOps; ++i) {
-        if (GATEUP) {
-          const uint32_t* mat = (i & 1) == 0 ? w.qgate : w.qup;
-          cbase[i] = reinterpret_cast<const char*>(mat) + ((size_t)e * a.I + nt * (kRowsMax / 2) + 64 * (i >> 1)) * rw;
-          coff[i] = (uint32_t)rr * rw + wo;
+        // the quarter's (or tile's) first row b0 and this lane's row relative to it
+        const int b0 = GATEUP ? nt * (kRowsMax / 2) + 64 * (i >> 1) : nt * kRowsMax;
+        const int rel = GATEUP ? rr : min(nt * kRowsMax + 64 * i + rr, a.d - 1) - nt * kRowsMax;
+        const uint32_t* mat = GATEUP ? ((i & 1) == 0 ? w.qgate : w.qup) : w.qdown;
+        const char* m = reinterpret_cast<const char*>(mat) + (size_t)e * (GATEUP ? a.I : a.d) * rw;
+        if constexpr (TB) {
+          cbase[i] = m + (size_t)(b0 / 16) * bstride;
+          coff[i] = (uint32_t)(rel / 16) * bstride + (uint32_t)(rel % 16) * 80u + wo;
         } else {
-          cbase[i] = reinterpret_cast<const char*>(w.qdown) + ((size_t)e * a.d + nt * kRowsMax) * rw;
-          coff[i] = (uint32_t)(min(nt * kRowsMax + 64 * i + rr, a.d - 1) - nt * kRowsMax) * rw + wo;
+          cbase[i] = m + (size_t)b0 * rw;
+          coff[i] = (uint32_t)rel * rw + wo;
         }
       }
       // the item's row scales into LDS (wave 0; these loads are older than every k-loop
@@ -547,9 +556,10 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
         __builtin_amdgcn_global_load_lds((const void*)(cbase[i] + coff[i] + kF8Pitch * ks), HY_LDS(dc + 4096 * i), 16,
                                          0, 0);
     };
-    // the step's code words: byte 4 floor(10 ks / 4) of each row
+    // the step's code words: byte 4 floor(10 ks / 4) of each row (blocked: of its 512-weight
+    // slab ks / 8, 1280 bytes per slab); the codes start at bit 16 (ks % 2) either way
     auto issue_c = [&](int ks, uint8_t* st) {
-      const uint32_t so = (uint32_t)(10 * ks) & ~3u;
+      const uint32_t so = TB ? (uint32_t)(ks >> 3) * 1280u + ((uint32_t)(10 * (ks & 7)) & ~3u) : (uint32_t)(10 * ks) & ~3u;
       uint8_t* dc = st + 256 * wv;
 #pragma unroll
       for (int i = 0; i < kCodeOps; ++i)
@@ -1086,7 +1096,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
   }
 }
 
-static int g_grid[10][64];  // persistent grid per (kernel kind, device), 0 = not yet computed
+static int g_grid[12][64];  // persistent grid per (kernel kind, device), 0 = not yet computed
 
 static int persistent_grid(int kind, const void* kernel) {
   int dev = 0;
@@ -1146,9 +1156,13 @@ hipError_t launch_grouped_experts(const Plan& p, const uint16_t* x, const Expert
     return err == hipSuccess ? m.mark(s) : err;
   }
   // ternary or FP8 routed experts, then the bf16 shared expert, per phase
-  const GemmKern gu = w.ternary ? pick_gemm<true, kGemmTern>(p.d) : pick_gemm<true, kGemmFp8>(p.d);
-  const GemmKern dn = w.ternary ? pick_gemm<false, kGemmTern>(p.I) : pick_gemm<false, kGemmFp8>(p.I);
-  const int kind = w.ternary ? 2 : 4;
+  const GemmKern gu = w.tblocked  ? pick_gemm<true, kGemmTernBlk>(p.d)
+                     : w.ternary ? pick_gemm<true, kGemmTern>(p.d)
+                                 : pick_gemm<true, kGemmFp8>(p.d);
+  const GemmKern dn = w.tblocked  ? pick_gemm<false, kGemmTernBlk>(p.I)
+                     : w.ternary ? pick_gemm<false, kGemmTern>(p.I)
+                                 : pick_gemm<false, kGemmFp8>(p.I);
+  const int kind = w.tblocked ? 10 : w.ternary ? 2 : 4;
   err = launch_gemm(gu, kind, a, 1, w, p, s);
   if (err == hipSuccess) err = launch_gemm(pick_gemm<true, kGemmBf16>(p.d), 0, a, 2, w, p, s);
   if (err == hipSuccess) err = m.mark(s);

@@ -1,4 +1,5 @@
-// moe_layout: the blocked layout of HY_MOE_WEIGHTS_BF16_BLOCKED. A row-major bf16
+// moe_layout: the blocked layouts of HY_MOE_WEIGHTS_BF16_BLOCKED and
+// HY_MOE_WEIGHTS_SHERRY_BLOCKED (the latter below). A row-major bf16
 // matrix [rows][cols] becomes [rows/16][cols/64][16][64]: every 16-row group's 64-column
 // slab is one contiguous 2 KB run. The streaming kernels read a wave's 16 rows one
 // 64-column chunk at a time; with row-major weights those 16 pieces of 128 bytes lie a
@@ -31,6 +32,34 @@ __global__ void __launch_bounds__(kBlockThreads) block_bf16_kernel(const uint4* 
   }
 }
 
+// Sherry codes: a row's K/512 slabs of 80 bytes (5 pieces each); slab c of row r lands at
+// piece 80 ((r / 16) K/512 + c) + 5 (r % 16) of the matrix: 16 rows' slabs make one
+// 1280-byte block, ten whole 128-byte lines (80-byte slabs at 80-byte strides straddle
+// lines: the decode kernel fetched 1.57 times the code bytes it used).
+__global__ void __launch_bounds__(kBlockThreads) block_sherry_kernel(const uint4* __restrict__ src,
+                                                                      uint4* __restrict__ dst, int64_t pieces,
+                                                                      int64_t rows, int64_t slabs) {
+  const int64_t per_row = slabs * 5, per_mat = rows * per_row;
+  for (int64_t t = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x; t < pieces;
+       t += (int64_t)gridDim.x * kBlockThreads) {
+    const int64_t m = t / per_mat, rem = t - m * per_mat;
+    const int64_t r = rem / per_row, q = rem - r * per_row;
+    const int64_t c = q / 5, j = q - c * 5;
+    dst[m * per_mat + ((r / 16) * slabs + c) * 80 + (r % 16) * 5 + j] = src[t];
+  }
+}
+
+hipError_t launch_block_sherry(const uint32_t* src, uint32_t* dst, int64_t count, int64_t rows, int64_t cols,
+                               hipStream_t s) {
+  const int64_t slabs = cols / 512, pieces = count * rows * slabs * 5;
+  if (pieces == 0) return hipSuccess;
+  const int64_t want = (pieces + kBlockThreads - 1) / kBlockThreads;
+  const unsigned grid = (unsigned)(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(block_sherry_kernel, dim3(grid), dim3(kBlockThreads), 0, s, reinterpret_cast<const uint4*>(src),
+                     reinterpret_cast<uint4*>(dst), pieces, rows, slabs);
+  return hipGetLastError();
+}
+
 hipError_t launch_block_bf16(const uint16_t* src, uint16_t* dst, int64_t count, int64_t rows, int64_t cols,
                              hipStream_t s) {
   const int64_t pieces = count * rows * (cols / 8);
@@ -55,5 +84,19 @@ extern "C" int hy_moe_block_bf16(const void* src, void* dst, int64_t count, int6
   if (a < b + bytes && b < a + bytes) return HY_MOE_ERR_INVALID_ARG;  // overlapping buffers
   const hipError_t err = hymoe::launch_block_bf16((const uint16_t*)src, (uint16_t*)dst, count, rows, cols,
                                                   (hipStream_t)stream);
+  return err == hipSuccess ? HY_MOE_OK : HY_MOE_ERR_HIP;
+}
+
+extern "C" int hy_moe_block_sherry(const void* src, void* dst, int64_t count, int64_t rows, int64_t cols,
+                                   void* stream) {
+  if (count < 0 || rows <= 0 || cols <= 0 || rows % 16 != 0 || cols % 512 != 0) return HY_MOE_ERR_INVALID_ARG;
+  if (count == 0) return HY_MOE_OK;
+  if (!src || !dst || ((uintptr_t)src & 15) || ((uintptr_t)dst & 15)) return HY_MOE_ERR_INVALID_ARG;
+  if (rows > ((int64_t)1 << 40) / cols || count > ((int64_t)1 << 40) / (rows * cols)) return HY_MOE_ERR_INVALID_ARG;
+  const uintptr_t bytes = (uintptr_t)(count * rows * (cols / 128 * 20));
+  const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
+  if (a < b + bytes && b < a + bytes) return HY_MOE_ERR_INVALID_ARG;  // overlapping buffers
+  const hipError_t err = hymoe::launch_block_sherry((const uint32_t*)src, (uint32_t*)dst, count, rows, cols,
+                                                    (hipStream_t)stream);
   return err == hipSuccess ? HY_MOE_OK : HY_MOE_ERR_HIP;
 }

@@ -610,7 +610,9 @@ bool tern_lds_eligible(const Plan& p, const ExpertWeights& w) {
 template <int NM>
 __host__ __device__ constexpr int tern_shared_subs() { return kTlRows / NM / 64; }
 
-template <int NM>
+// TB: code matrices in the blocked layout ([rows/16][K/512][16][80 B]): a 16-row group's
+// chunk is one 1280-byte run and the next chunk of a row is 1280 bytes on.
+template <int NM, bool TB>
 __global__ void __launch_bounds__(256, kTlWgPerCu) tern_lds_kernel(StreamArgs a, ExpertWeights w,
                                                         const uint16_t* __restrict__ act, void* __restrict__ out) {
   __shared__ uint2 lut[32];
@@ -650,8 +652,10 @@ __global__ void __launch_bounds__(256, kTlWgPerCu) tern_lds_kernel(StreamArgs a,
   for (int i = 0; i < kTlCodeOps; ++i) {
     const int j = 256 * i + tid, row = j / 5, piece = j - 5 * row;
     const int mat = NM == 2 ? row >> 7 : 0, rr = NM == 2 ? (row & 127) : row;
-    const uint32_t* q = (NM == 2 ? (mat ? w.qup : w.qgate) : w.qdown) + ((size_t)e * R + rbase + rr) * wpr;
-    csrc[i] = reinterpret_cast<const char*>(q) + 16 * piece;
+    const uint32_t* m = (NM == 2 ? (mat ? w.qup : w.qgate) : w.qdown) + (size_t)e * R * wpr;  // the expert's matrix
+    const int mr = rbase + rr;  // matrix row
+    csrc[i] = TB ? reinterpret_cast<const char*>(m) + (size_t)(mr / 16) * (K / 512) * 1280 + 80 * (mr % 16) + 16 * piece
+                 : reinterpret_cast<const char*>(m + (size_t)mr * wpr) + 16 * piece;
   }
   // this wave's row blocks: NM = 2: (gate, up) x 2 blocks of 16 units at rbase + 32 wv;
   // NM = 1: 4 blocks of 16 output rows at rbase + 64 wv
@@ -684,7 +688,7 @@ __global__ void __launch_bounds__(256, kTlWgPerCu) tern_lds_kernel(StreamArgs a,
       // (the LDS operand is the wave's base: lane l writes 16 bytes at base + 16 l)
 #pragma unroll
       for (int i = 0; i < kTlCodeOps; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(csrc[i] + kTlRowBytes * c),
+        __builtin_amdgcn_global_load_lds((const void*)(csrc[i] + (TB ? 16 * kTlRowBytes : kTlRowBytes) * c),
                                          (__attribute__((address_space(3))) void*)(slot + 4096 * i + 1024 * wv), 16, 0,
                                          0);
 #pragma unroll
@@ -763,13 +767,15 @@ hipError_t launch_stream_experts(const Plan& p, const uint16_t* x, const ExpertW
   const int passes = (p.T + 15) / 16;
   if (tern_lds_eligible(p, w)) {
     // LDS-staged ternary kernels, the shared expert's rows first in each grid
-    hipLaunchKernelGGL(tern_lds_kernel<2>, dim3(p.I / (kTlRows / 2), passes * tern_shared_subs<2>() + routed),
-                       dim3(256), 0, s, a, w, x, (void*)p.h);
+    const auto gu = w.tblocked ? tern_lds_kernel<2, true> : tern_lds_kernel<2, false>;
+    const auto dn = w.tblocked ? tern_lds_kernel<1, true> : tern_lds_kernel<1, false>;
+    hipLaunchKernelGGL(gu, dim3(p.I / (kTlRows / 2), passes * tern_shared_subs<2>() + routed), dim3(256), 0, s, a, w, x,
+                       (void*)p.h);
     hipError_t err = hipGetLastError();
     if (err == hipSuccess) err = m.mark(s);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(tern_lds_kernel<1>, dim3(p.d / kTlRows, passes * tern_shared_subs<1>() + routed), dim3(256),
-                       0, s, a, w, (const uint16_t*)p.h, (void*)p.y);
+    hipLaunchKernelGGL(dn, dim3(p.d / kTlRows, passes * tern_shared_subs<1>() + routed), dim3(256), 0, s, a, w,
+                       (const uint16_t*)p.h, (void*)p.y);
     err = hipGetLastError();
     return err == hipSuccess ? m.mark(s) : err;
   }

@@ -147,7 +147,7 @@ def test_workspace_size_monotone_and_zero_for_invalid():
     assert all(s > 0 for s in sizes) and sizes == sorted(sizes)
     assert hm.workspace_size(8, 6144, 256, 0, 2048) == 0
     assert hm.workspace_size(8, 100, 256, 8, 2048) == 0
-    assert hm.workspace_size(8, 6144, 256, 8, 2048, 5) == 0
+    assert hm.workspace_size(8, 6144, 256, 8, 2048, 6) == 0
     assert hm.workspace_size(8192, 6144, 256, 8, 2048) % 256 == 0
 
 
@@ -317,4 +317,37 @@ def test_blocked_format_checks_and_workspace():
     for T in (1, 32, 8192):
         assert hm.workspace_size(T, 6144, 256, 8, 2048, hm.WEIGHTS_BF16_BLOCKED) == \
             hm.workspace_size(T, 6144, 256, 8, 2048, hm.WEIGHTS_BF16)
-    assert hm.workspace_size(4, 512, 16, 2, 256, 5) == 0  # no such format
+    assert hm.workspace_size(4, 512, 16, 2, 256, 6) == 0  # no such format
+
+
+def test_block_sherry_argument_checks():
+    L = hm.lib()
+    BIG = 0x10000000
+    assert L.hy_moe_block_sherry(FAKE, BIG, 2, 24, 512, None) == hm.ERR_INVALID_ARG     # rows % 16
+    assert L.hy_moe_block_sherry(FAKE, BIG, 2, 32, 384, None) == hm.ERR_INVALID_ARG     # cols % 512
+    assert L.hy_moe_block_sherry(FAKE, BIG, -1, 32, 512, None) == hm.ERR_INVALID_ARG
+    assert L.hy_moe_block_sherry(FAKE, None, 2, 32, 512, None) == hm.ERR_INVALID_ARG
+    assert L.hy_moe_block_sherry(FAKE + 4, BIG, 2, 32, 512, None) == hm.ERR_INVALID_ARG  # misaligned
+    # 2 x 32 rows x 80 bytes = 5 KB of codes from FAKE; dst 4 KB in overlaps, 5 KB in does not
+    assert L.hy_moe_block_sherry(FAKE, FAKE + 4096, 2, 32, 512, None) == hm.ERR_INVALID_ARG
+    assert L.hy_moe_block_sherry(FAKE + 4096, FAKE, 2, 32, 512, None) == hm.ERR_INVALID_ARG
+    assert L.hy_moe_block_sherry(None, None, 0, 32, 512, None) == hm.OK                  # empty: no-op
+
+
+def test_blocked_sherry_format_checks_and_workspace():
+    # the blocked Sherry format takes the ternary pointers; codes 16-byte aligned, d and I % 512
+    a = base_args(T=4, d=512, E=16, k=2, I=512)
+    a.expert_format = hm.WEIGHTS_SHERRY_BLOCKED
+    assert call(a) == hm.ERR_INVALID_ARG  # no codes or scales
+    a.Wq_gate = a.Wq_up = a.Wq_down = a.S_gate = a.S_up = a.S_down = FAKE
+    a.Wq_up = FAKE + 4  # 4-byte alignment suffices for row-major codes, not for blocked ones
+    assert call(a) == hm.ERR_INVALID_ARG
+    a.Wq_up = FAKE
+    for d, I in ((512, 256), (384, 512)):
+        b = base_args(T=4, d=d, E=16, k=2, I=I)
+        b.expert_format = hm.WEIGHTS_SHERRY_BLOCKED
+        b.Wq_gate = b.Wq_up = b.Wq_down = b.S_gate = b.S_up = b.S_down = FAKE
+        assert call(b) == hm.ERR_UNSUPPORTED
+    for T in (1, 32, 8192):
+        assert hm.workspace_size(T, 6144, 256, 8, 2048, hm.WEIGHTS_SHERRY_BLOCKED) == \
+            hm.workspace_size(T, 6144, 256, 8, 2048, hm.WEIGHTS_SHERRY_TERNARY)

@@ -195,6 +195,25 @@ def test_ternary_full_size():
     run_full(cfg, inp)
 
 
+def test_blocked_sherry_full_size():
+    """Blocked Sherry codes give bitwise the same outputs and routing as row-major ones at
+    the ternary decode (LDS-staged streaming kernels) and ternary prefill (grouped GEMM)
+    sizes."""
+    for name in ("ternary", "ternary_prefill"):
+        cfg = hi.CONFIGS[name]
+        say(f"[case] {name} T={cfg.T}: blocked Sherry codes vs row-major")
+        inp = hi.dev_layer(cfg, device=DEV)
+        ref = hm.forward_layer(inp, cfg.k, want_routing=True)
+        blk = hm.block_layer(inp)
+        got = hm.forward_layer(blk, cfg.k, want_routing=True, weights_blocked=True)
+        torch.cuda.synchronize()
+        assert torch.equal(got["out"].view(torch.int16), ref["out"].view(torch.int16)), name
+        for key in ("topk_idx", "counts", "perm_src"):
+            assert torch.equal(got[key], ref[key]), (name, key)
+        del inp, blk, ref, got
+        torch.cuda.empty_cache()
+
+
 def test_fp8_full_size():
     cfg = hi.CONFIGS["fp8"]
     inp = hi.dev_layer(cfg, device=DEV)

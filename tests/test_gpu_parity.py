@@ -400,6 +400,42 @@ def test_blocked_weights_match_row_major(shape, path):
         assert torch.equal(got[key], ref[key])
 
 
+def test_block_sherry_matches_layout_definition():
+    """hy_moe_block_sherry against the layout's definition, written out byte by byte: row
+    r's 80-byte slab of weights [512 c, 512 c + 512) starts at byte
+    1280 ((r / 16) (K / 512) + c) + 80 (r % 16) of its matrix."""
+    say("[case] block_sherry on 3 matrices of 48 x 1536 weights")
+    R, K = 48, 1536
+    g = torch.Generator(device=DEV).manual_seed(6)
+    q = torch.randint(-2 ** 31, 2 ** 31 - 1, (3, R, K // 128 * 5), generator=g, device=DEV, dtype=torch.int32)
+    b = hm.block_sherry(q)
+    torch.cuda.synchronize()
+    src = q.cpu().numpy().view(np.uint8).reshape(3, R, K // 128 * 20)
+    got = b.cpu().numpy().view(np.uint8).reshape(3, -1)
+    exp = np.zeros_like(got)
+    for m in range(3):
+        for r in range(R):
+            for c in range(K // 512):
+                o = 1280 * ((r // 16) * (K // 512) + c) + 80 * (r % 16)
+                exp[m, o:o + 80] = src[m, r, 80 * c:80 * c + 80]
+    assert np.array_equal(got, exp)
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("shape", [(1, 512, 16, 2, 512), (40, 1024, 16, 4, 512), (300, 512, 8, 2, 1536)])
+def test_blocked_sherry_match_row_major(shape, path):
+    T, d, E, k, I = shape
+    say(f"[case] blocked Sherry codes T={T} d={d} E={E} k={k} I={I} path={path}")
+    cfg = hi.LayerConfig("tblk", T=T, d=d, E=E, k=k, I=I, ternary=True, seed=33)
+    inp = hi.dev_layer(cfg, device=DEV)
+    ref = hm.forward_layer(inp, k, want_routing=True, path=path)
+    got = hm.forward_layer(hm.block_layer(inp), k, want_routing=True, path=path, weights_blocked=True)
+    torch.cuda.synchronize()
+    assert torch.equal(got["out"].view(torch.int16), ref["out"].view(torch.int16))
+    for key in ("topk_idx", "counts", "perm_src"):
+        assert torch.equal(got[key], ref[key])
+
+
 # ------------------------------------------------- large cancelling expert outputs
 def _bits_to_f32(b):
     return (b.astype(np.uint32) << 16).view(np.float32)
