@@ -108,9 +108,9 @@ typedef enum {
    * pack into K/128 * 20 bytes becomes [R/16][K/512][16][80 bytes]: the 80 code bytes of
    * row r for weights [512 c, 512 c + 512) start at byte 1280 * ((r / 16) * (K / 512) + c)
    * + 80 * (r % 16). Each 16-row group's slab is then 1280 bytes, exactly ten 128-byte
-   * lines, instead of 16 pieces of 80 bytes that straddle lines. Needs d % 512 == 0 and
-   * I % 512 == 0 and 16-byte aligned code arrays (HY_MOE_ERR_UNSUPPORTED /
-   * HY_MOE_ERR_INVALID_ARG otherwise). Results are bitwise identical to
+   * lines, instead of 16 pieces of 80 bytes that straddle lines. Needs d % 512 == 0,
+   * I % 512 == 0 and I * d * 20 / 128 < 2^31 (one expert's code matrix), and 16-byte
+   * aligned code arrays (HY_MOE_ERR_UNSUPPORTED / HY_MOE_ERR_INVALID_ARG otherwise). Results are bitwise identical to
    * HY_MOE_WEIGHTS_SHERRY_TERNARY on the same codes. hy_moe_block_sherry converts. */
   HY_MOE_WEIGHTS_SHERRY_BLOCKED = 5
 } hy_moe_wfmt;

@@ -48,6 +48,11 @@ __device__ __forceinline__ f32x16 mfma32x32x16(uint4 a, uint4 b, f32x16 c) {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
+// Fourth word of a raw buffer resource (no index stride, no swizzle): data format
+// 32-bit (field value 4 at bit 15), the value CDNA buffer loads expect for untyped
+// byte-addressed access.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // D[32x32] += A[32x64] B[64x32] on E4M3 codes with E8M0 block scales sa (A) and sb (B)

@@ -112,6 +112,8 @@ int check_args(const hy_moe_args* a) {
       for (const void* p : q)
         if (!aligned(p, 16)) return HY_MOE_ERR_INVALID_ARG;
       if (a->d % 512 != 0 || a->I % 512 != 0) return HY_MOE_ERR_UNSUPPORTED;
+      // and address one expert's code matrix (I d 20 / 128 bytes) with 32-bit offsets
+      if (a->I * (a->d / 128 * 20) >= ((int64_t)1 << 31)) return HY_MOE_ERR_UNSUPPORTED;
     }
   } else {
     const void* q[] = {a->Wq_gate, a->Wq_up, a->Wq_down};

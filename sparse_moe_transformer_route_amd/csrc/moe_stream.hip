@@ -593,13 +593,15 @@ constexpr int kTlTokBytes = kTlBlocks * 128 * 2;         // activation bytes per
 constexpr int kTlXBytes = kTlTok * kTlTokBytes;          // 4 KB
 constexpr int kTlSlot = kTlCodeBytes + kTlXBytes;        // 24 KB per ring slot
 constexpr int kTlCodeOps = kTlCodeBytes / (256 * 16);    // 16-byte loads per thread per chunk: 5
-constexpr int kTlXOps = kTlXBytes / (256 * 16);          // 1
 constexpr int kTlWgPerCu = 3;                            // workgroups per CU (2 slots: 48 KB each)
-static_assert(kTlCodeOps * 256 * 16 == kTlCodeBytes && kTlXOps * 256 * 16 == kTlXBytes, "whole load ops");
+// one 1 KB activation piece per wave and token slot
+static_assert(kTlCodeOps * 256 * 16 == kTlCodeBytes && kTlXBytes == 4 * 1024 && kTlTok == 4, "whole load ops");
 
 bool tern_lds_eligible(const Plan& p, const ExpertWeights& w) {
   auto a16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
-  return w.ternary && p.d % 512 == 0 && p.I % 512 == 0 && a16(w.qgate) && a16(w.qup) && a16(w.qdown);
+  // (buffer resources address one expert's code matrix, I d 20 / 128 bytes, with 32-bit offsets)
+  return w.ternary && p.d % 512 == 0 && p.I % 512 == 0 && a16(w.qgate) && a16(w.qup) && a16(w.qdown) &&
+         (int64_t)p.I * (p.d / 128 * 20) < ((int64_t)1 << 31);
 }
 
 // NM = 2: gate and up (act = x through the permutation, out = h bf16, K = d);
@@ -645,17 +647,21 @@ __global__ void __launch_bounds__(256, kTlWgPerCu) tern_lds_kernel(StreamArgs a,
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
 
-  // code piece j = 256 i + tid: workgroup code row j / 5 (matrix row / 128 when NM = 2),
-  // 16-byte piece j % 5 of the row's 80 chunk bytes; LDS [row][80 B]
-  const char* csrc[kTlCodeOps];
+  // Direct-to-LDS loads go through buffer resources (wave-uniform base and size, 32-bit
+  // per-lane offsets): the compiler then counts LDS reads in order and waits only for
+  // the ones an MFMA needs (with global_load_lds ops in flight it waits for every LDS
+  // read). Code op i of wave wv fills LDS piece q = 5 wv + i (1 KB): pieces j = 64 q +
+  // lane, workgroup code row j / 5, 16-byte piece j % 5 of the row's 80 chunk bytes
+  // (LDS [row][80 B]). With NM = 2, waves 0-1 load gate rows and waves 2-3 up rows.
+  const uint32_t* cm = (NM == 2 ? (wv >= 2 ? w.qup : w.qgate) : w.qdown) + (size_t)e * R * wpr;  // the expert's matrix
+  const __amdgpu_buffer_rsrc_t crs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(cm), (short)0, R * wpr * 4, kBufferRsrcWord3);
+  int coff[kTlCodeOps];
 #pragma unroll
   for (int i = 0; i < kTlCodeOps; ++i) {
-    const int j = 256 * i + tid, row = j / 5, piece = j - 5 * row;
-    const int mat = NM == 2 ? row >> 7 : 0, rr = NM == 2 ? (row & 127) : row;
-    const uint32_t* m = (NM == 2 ? (mat ? w.qup : w.qgate) : w.qdown) + (size_t)e * R * wpr;  // the expert's matrix
-    const int mr = rbase + rr;  // matrix row
-    csrc[i] = TB ? reinterpret_cast<const char*>(m) + (size_t)(mr / 16) * (K / 512) * 1280 + 80 * (mr % 16) + 16 * piece
-                 : reinterpret_cast<const char*>(m + (size_t)mr * wpr) + 16 * piece;
+    const int j = 64 * (5 * wv + i) + lane, row = j / 5, piece = j - 5 * row;
+    const int mr = rbase + (NM == 2 ? (row & 127) : row);  // matrix row
+    coff[i] = TB ? (mr / 16) * (K / 512) * 1280 + 80 * (mr % 16) + 16 * piece : mr * wpr * 4 + 16 * piece;
   }
   // this wave's row blocks: NM = 2: (gate, up) x 2 blocks of 16 units at rbase + 32 wv;
   // NM = 1: 4 blocks of 16 output rows at rbase + 64 wv
@@ -673,51 +679,67 @@ __global__ void __launch_bounds__(256, kTlWgPerCu) tern_lds_kernel(StreamArgs a,
     }
 
   for (int cb = 0; cb < n; cb += kTlTok) {  // token passes (uniform)
-    // activation piece j = 256 i + tid: token slot j / 64 of the pass, stored piece j % 64
-    const char* xsrc[kTlXOps];
-#pragma unroll
-    for (int i = 0; i < kTlXOps; ++i) {
-      const int j = 256 * i + tid, t = j >> 6, pp = j & 63;
-      const int col = cb + t < n ? row0 + cb + t : row0;  // unused slots repeat a valid row
-      // (routed rows are below Tk: their token is perm_src / k, loaded without a branch)
-      const uint16_t* arow = NM == 2 ? act + (size_t)((uint32_t)a.perm_src[col] / (uint32_t)a.k) * a.d
-                                     : act + (size_t)col * a.I;
-      xsrc[i] = reinterpret_cast<const char*>(arow) + 16 * (pp ^ t);
-    }
+    // activations: wave wv loads token slot wv of the pass (unused slots repeat a valid
+    // row), lane l piece l of each chunk's 1 KB, stored at piece l ^ wv
+    const int col = cb + wv < n ? row0 + cb + wv : row0;
+    // (routed rows are below Tk: their token is perm_src / k)
+    const uint16_t* arow = NM == 2 ? act + (size_t)((uint32_t)a.perm_src[col] / (uint32_t)a.k) * a.d
+                                   : act + (size_t)col * a.I;
+    const __amdgpu_buffer_rsrc_t xrs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(arow), (short)0, K * 2, kBufferRsrcWord3);
+    const int xoff = 16 * (lane ^ wv);
     auto issue = [&](int c, uint8_t* slot) {
       // (the LDS operand is the wave's base: lane l writes 16 bytes at base + 16 l)
 #pragma unroll
       for (int i = 0; i < kTlCodeOps; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(csrc[i] + (TB ? 16 * kTlRowBytes : kTlRowBytes) * c),
-                                         (__attribute__((address_space(3))) void*)(slot + 4096 * i + 1024 * wv), 16, 0,
-                                         0);
-#pragma unroll
-      for (int i = 0; i < kTlXOps; ++i)
-        __builtin_amdgcn_global_load_lds(
-            (const void*)(xsrc[i] + kTlTokBytes * c),
-            (__attribute__((address_space(3))) void*)(slot + kTlCodeBytes + 4096 * i + 1024 * wv), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, (__attribute__((address_space(3))) void*)(slot + 1024 * (5 * wv + i)),
+                                                 16, coff[i], (TB ? 16 * kTlRowBytes : kTlRowBytes) * c, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (__attribute__((address_space(3))) void*)(slot + kTlCodeBytes + 1024 * wv),
+                                               16, xoff, kTlTokBytes * c, 0, 0);
     };
     f32x4 acc[4];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) acc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // A chunk is 16 MFMA groups i = 4 b + qb (block b, row block qb), each 4 MFMAs. The
+    // LDS reads run ahead in program order, fenced by scheduling barriers: group i+2's
+    // code words, group i+1's table lookups and (in the second group of a block) the next
+    // block's activations are issued before group i's MFMAs, so each MFMA waits for
+    // lookups issued a whole group earlier rather than right before it.
     auto compute = [&](const uint8_t* slot) {
+      constexpr int NG = 4 * kTlBlocks;
+      const int tk = min(r16, kTlTok - 1);  // this lane's token column (repeats past the pass)
+      const uint8_t* xs = slot + kTlCodeBytes + tk * kTlTokBytes;
+      auto xload = [&](int b, uint4* xf) {
 #pragma unroll
-      for (int b = 0; b < kTlBlocks; ++b) {
-        uint4 xf[4];
-        const int tk = min(r16, kTlTok - 1);  // this lane's token column (repeats past the pass)
+        for (int m = 0; m < 4; ++m) xf[m] = *reinterpret_cast<const uint4*>(xs + 16 * ((16 * b + 4 * g + m) ^ tk));
+      };
+      auto words = [&](int i, uint32_t* cw) {
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(slot + crow(i & 3) * kTlRowBytes + 20 * (i >> 2)) + w0;
+        cw[0] = p[0];
+        cw[1] = p[1];
+      };
+      auto decode = [&](const uint32_t* cw, uint4* op) {
+        const uint64_t v = tern_window(cw, g);
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-          xf[m] = *reinterpret_cast<const uint4*>(slot + kTlCodeBytes + tk * kTlTokBytes +
-                                                  16 * ((16 * b + 4 * g + m) ^ tk));
+        for (int m = 0; m < 4; ++m) op[m] = tern_operand(v, m, lut);
+      };
+      uint32_t cw[3][2];
+      uint4 op[2][4], xf[2][4];
+      xload(0, xf[0]);
+      words(0, cw[0]);
+      words(1, cw[1]);
+      decode(cw[0], op[0]);
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb) {
-          const uint32_t* cw = reinterpret_cast<const uint32_t*>(slot + crow(qb) * kTlRowBytes + 20 * b) + w0;
-          const uint32_t c2[2] = {cw[0], cw[1]};
-          const uint64_t v = tern_window(c2, g);
+      for (int i = 0; i < NG; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + 2 < NG) words(i + 2, cw[(i + 2) % 3]);
+        if (i + 1 < NG) decode(cw[(i + 1) % 3], op[(i + 1) & 1]);
+        if ((i & 3) == 1 && (i >> 2) + 1 < kTlBlocks) xload((i >> 2) + 1, xf[((i >> 2) + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int m = 0; m < 4; ++m) acc[qb] = mfma16x16x32(tern_operand(v, m, lut), xf[m], acc[qb]);
-        }
+        for (int m = 0; m < 4; ++m) acc[i & 3] = mfma16x16x32(op[i & 1][m], xf[(i >> 2) & 1][m], acc[i & 3]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     };
     // chunk c: its loads (issued a chunk earlier) landed everywhere and every wave is
     // done with chunk c-1, whose slot then receives chunk c+1 while chunk c computes

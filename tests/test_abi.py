@@ -343,7 +343,7 @@ def test_blocked_sherry_format_checks_and_workspace():
     a.Wq_up = FAKE + 4  # 4-byte alignment suffices for row-major codes, not for blocked ones
     assert call(a) == hm.ERR_INVALID_ARG
     a.Wq_up = FAKE
-    for d, I in ((512, 256), (384, 512)):
+    for d, I in ((512, 256), (384, 512), (2 ** 20, 2 ** 17)):  # the last: one code matrix of 2^31 bytes
         b = base_args(T=4, d=d, E=16, k=2, I=I)
         b.expert_format = hm.WEIGHTS_SHERRY_BLOCKED
         b.Wq_gate = b.Wq_up = b.Wq_down = b.S_gate = b.S_up = b.S_down = FAKE
