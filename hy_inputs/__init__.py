@@ -50,6 +50,7 @@ class LayerConfig:
     ternary: bool = False
     fp8: bool = False        # routed experts as E4M3 codes with fp32 row scales
     a8: bool = False         # with fp8: the routed experts' activations in MXFP8 (W8A8)
+    tshared: bool = False    # with ternary: the shared expert Sherry-packed too, as expert E of the code arrays
     zipf_s: float = 0.0      # 0 => no router bias
     zipf_alpha: float = 1.0
     x_std: float = 1.0
@@ -269,7 +270,8 @@ def host_layer(cfg: LayerConfig) -> dict:
     out = {"x": host_x(cfg), "router": host_router(cfg), "bias": host_bias(cfg),
            "shared": host_shared(cfg)}
     gen = host_expert_ternary if cfg.ternary else host_expert_fp8 if cfg.fp8 else host_expert
-    experts = [gen(cfg, e) for e in range(cfg.E)]
+    # (a Sherry-packed shared expert continues the routed experts' streams as expert E)
+    experts = [gen(cfg, e) for e in range(cfg.E + (1 if cfg.ternary and cfg.tshared else 0))]
     keys = experts[0].keys()
     for key in keys:
         out[key] = np.stack([ex[key] for ex in experts])
@@ -323,12 +325,14 @@ def dev_layer(cfg: LayerConfig, device="cuda") -> dict:
     if cfg.ternary:
         wg, wd = qwords_per_row(d), qwords_per_row(I)
         i32 = torch.int32
-        out["qgate"] = dev_words_(torch.empty(E, I, wg, dtype=i32, device=device), cfg.seed, S_QG)
-        out["qup"] = dev_words_(torch.empty(E, I, wg, dtype=i32, device=device), cfg.seed, S_QU)
-        out["qdown"] = dev_words_(torch.empty(E, d, wd, dtype=i32, device=device), cfg.seed, S_QD)
-        out["sgate"] = dev_uniform_(torch.empty(E, I, dtype=bf, device=device), cfg.seed, S_SG, 0.5 * sd, sd)
-        out["sup"] = dev_uniform_(torch.empty(E, I, dtype=bf, device=device), cfg.seed, S_SU, 0.5 * sd, sd)
-        out["sdown"] = dev_uniform_(torch.empty(E, d, dtype=bf, device=device), cfg.seed, S_SD, 0.5 * si, si)
+        EQ = E + 1 if cfg.tshared else E  # a Sherry-packed shared expert is expert E
+        out["qgate"] = dev_words_(torch.empty(EQ, I, wg, dtype=i32, device=device), cfg.seed, S_QG)
+        out["qup"] = dev_words_(torch.empty(EQ, I, wg, dtype=i32, device=device), cfg.seed, S_QU)
+        out["qdown"] = dev_words_(torch.empty(EQ, d, wd, dtype=i32, device=device), cfg.seed, S_QD)
+        out["sgate"] = dev_uniform_(torch.empty(EQ, I, dtype=bf, device=device), cfg.seed, S_SG, 0.5 * sd, sd)
+        out["sup"] = dev_uniform_(torch.empty(EQ, I, dtype=bf, device=device), cfg.seed, S_SU, 0.5 * sd, sd)
+        out["sdown"] = dev_uniform_(torch.empty(EQ, d, dtype=bf, device=device), cfg.seed, S_SD, 0.5 * si, si)
+        out["shared_sherry"] = cfg.tshared
     elif cfg.fp8:
         i32 = torch.int32
 

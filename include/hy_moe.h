@@ -195,6 +195,16 @@ typedef struct hy_moe_args {
      scales. When given they replace the workspace's copy (no extra traffic). */
   void* hidden_codes;
   void* hidden_scales;
+  /* The shared expert's weight format (ai.chattools.top article, section on Sherry and
+     MIX-STQ1_0: Sherry packing is chosen per layer, so a layer's shared expert may be
+     packed like its routed experts). HY_MOE_WEIGHTS_BF16 (0, what a zero-initialized
+     struct holds): bf16 Ws_gate/Ws_up/Ws_down. Or the expert format itself, when that is
+     HY_MOE_WEIGHTS_SHERRY_TERNARY or HY_MOE_WEIGHTS_SHERRY_BLOCKED: the shared expert is
+     expert E of Wq_gate/Wq_up/Wq_down and S_gate/S_up/S_down, which then hold E+1
+     experts; Ws_* are not read (may be NULL). This needs d % 512 == 0, I % 512 == 0,
+     I * d * 20 / 128 < 2^31 and 16-byte aligned code arrays (HY_MOE_ERR_UNSUPPORTED /
+     HY_MOE_ERR_INVALID_ARG otherwise); any other value is HY_MOE_ERR_INVALID_ARG. */
+  hy_moe_wfmt shared_format;
 } hy_moe_args;
 
 /* Kernels of one call, in launch order (indices into the stage events). */

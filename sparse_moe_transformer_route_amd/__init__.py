@@ -56,6 +56,7 @@ class HyMoeArgs(ctypes.Structure):
         ("path", ctypes.c_int),
         ("stage_events", ctypes.c_void_p),
         ("hidden_codes", ctypes.c_void_p), ("hidden_scales", ctypes.c_void_p),
+        ("shared_format", ctypes.c_int),
     ]
 
 
@@ -165,7 +166,10 @@ def forward_layer(inp: dict, k: int, *, want_routing=False, path=PATH_AUTO, work
     hidden rows as the down projection reads them, dispatched-row order).
     weights_blocked: the weights are in the blocked layout (block_layer): bf16 gate/up/down
     and the shared expert's matrices (HY_MOE_WEIGHTS_BF16_BLOCKED), or the Sherry code
-    matrices (HY_MOE_WEIGHTS_SHERRY_BLOCKED; the bf16 shared expert stays row-major)."""
+    matrices (HY_MOE_WEIGHTS_SHERRY_BLOCKED; the bf16 shared expert stays row-major).
+    A ternary dict with shared_sherry true holds the shared expert Sherry-packed as
+    expert E of qgate/qup/qdown and sgate/sup/sdown (E+1 experts; shared_format set to
+    the expert format, "shared" not read)."""
     import torch
     x = inp["x"]
     T, d = x.shape
@@ -182,6 +186,11 @@ def forward_layer(inp: dict, k: int, *, want_routing=False, path=PATH_AUTO, work
         if inp[key].dtype != dt or not inp[key].is_contiguous():
             raise TypeError(f"forward_layer: {key} must be a contiguous {dt} tensor, got {inp[key].dtype}")
     I = inp["sgate"].shape[1] if ternary else inp["fsgate"].shape[1] if fp8 else inp["gate"].shape[1]
+    tshared = ternary and bool(inp.get("shared_sherry", False))
+    first = "qgate" if ternary else "fgate" if fp8 else "gate"
+    if inp[first].shape[0] != E + (1 if tshared else 0):  # the library reads E (or E+1) experts
+        raise ValueError(f"forward_layer: {first} holds {inp[first].shape[0]} experts, expected "
+                         f"{E + (1 if tshared else 0)}")
     dev = x.device
     a = HyMoeArgs()
     a.x, a.W_router, a.router_bias = _ptr(x), _ptr(inp["router"]), _ptr(inp.get("bias"))
@@ -200,8 +209,11 @@ def forward_layer(inp: dict, k: int, *, want_routing=False, path=PATH_AUTO, work
         a.S_gate, a.S_up, a.S_down = _ptr(inp["fsgate"]), _ptr(inp["fsup"]), _ptr(inp["fsdown"])
     else:
         a.W_gate, a.W_up, a.W_down = _ptr(inp["gate"]), _ptr(inp["up"]), _ptr(inp["down"])
-    sh = inp["shared"]
-    a.Ws_gate, a.Ws_up, a.Ws_down = _ptr(sh["gate"]), _ptr(sh["up"]), _ptr(sh["down"])
+    if tshared:
+        a.shared_format = a.expert_format
+    else:
+        sh = inp["shared"]
+        a.Ws_gate, a.Ws_up, a.Ws_down = _ptr(sh["gate"]), _ptr(sh["up"]), _ptr(sh["down"])
     a.T, a.d, a.E, a.k, a.I = T, d, E, k, I
     if out is None:
         out = torch.empty(T, d, dtype=torch.bfloat16, device=dev)

@@ -91,12 +91,27 @@ int check_args(const hy_moe_args* a) {
   if (!valid_format(a->expert_format)) return HY_MOE_ERR_INVALID_ARG;
   if (a->path != HY_MOE_PATH_AUTO && a->path != HY_MOE_PATH_STREAM && a->path != HY_MOE_PATH_GROUPED)
     return HY_MOE_ERR_INVALID_ARG;
+  // the shared expert: bf16 (Ws_*), or Sherry codes as expert E of the routed arrays
+  const bool tshared = a->shared_format != HY_MOE_WEIGHTS_BF16;
+  if (tshared && (a->shared_format != a->expert_format || (a->expert_format != HY_MOE_WEIGHTS_SHERRY_TERNARY &&
+                                                          a->expert_format != HY_MOE_WEIGHTS_SHERRY_BLOCKED)))
+    return HY_MOE_ERR_INVALID_ARG;
   if (a->T == 0) return HY_MOE_OK;
-  const void* req[] = {a->x, a->W_router, a->Ws_gate, a->Ws_up, a->Ws_down, a->out};
+  const void* req[] = {a->x, a->W_router, a->out};
   for (const void* p : req)
-    if (!p) return HY_MOE_ERR_INVALID_ARG;
-  for (const void* p : req)
-    if (!aligned(p, 16)) return HY_MOE_ERR_INVALID_ARG;
+    if (!p || !aligned(p, 16)) return HY_MOE_ERR_INVALID_ARG;
+  if (!tshared) {
+    const void* sw[] = {a->Ws_gate, a->Ws_up, a->Ws_down};
+    for (const void* p : sw)
+      if (!p || !aligned(p, 16)) return HY_MOE_ERR_INVALID_ARG;
+  } else {
+    // it runs in the LDS-staged decode kernels (16-byte code loads, 512-weight chunks)
+    const void* q[] = {a->Wq_gate, a->Wq_up, a->Wq_down};
+    for (const void* p : q)
+      if (!p || !aligned(p, 16)) return HY_MOE_ERR_INVALID_ARG;
+    if (a->d % 512 != 0 || a->I % 512 != 0 || a->I * (a->d / 128 * 20) >= ((int64_t)1 << 31))
+      return HY_MOE_ERR_UNSUPPORTED;
+  }
   if (a->router_bias && !aligned(a->router_bias, 4)) return HY_MOE_ERR_INVALID_ARG;
   if (a->expert_format == HY_MOE_WEIGHTS_BF16 || a->expert_format == HY_MOE_WEIGHTS_BF16_BLOCKED) {
     const void* w[] = {a->W_gate, a->W_up, a->W_down};
@@ -211,6 +226,7 @@ extern "C" int hy_moe_forward_ex(const hy_moe_args* a, void* stream) {
   w.sgate = (const uint16_t*)a->S_gate;
   w.sup = (const uint16_t*)a->S_up;
   w.sdown = (const uint16_t*)a->S_down;
+  w.tshared = a->shared_format != HY_MOE_WEIGHTS_BF16;
   w.s_gate = (const uint16_t*)a->Ws_gate;
   w.s_up = (const uint16_t*)a->Ws_up;
   w.s_down = (const uint16_t*)a->Ws_down;

@@ -86,6 +86,7 @@ struct ExpertWeights {
   bool a8;       // with fp8: MXFP8 activations (W8A8)
   bool blocked;   // bf16 in the blocked layout ([rows/16][cols/64][16][64] per matrix, shared expert too)
   bool tblocked;  // with ternary: code matrices in the blocked layout ([rows/16][cols/512][16][80 B])
+  bool tshared;   // with ternary: the shared expert is Sherry-packed, expert E of the code and scale arrays
 };
 
 hipError_t launch_stream_experts(const Plan& p, const uint16_t* x, const ExpertWeights& w, hipStream_t s,

@@ -1163,6 +1163,13 @@ hipError_t launch_grouped_experts(const Plan& p, const uint16_t* x, const Expert
                      : w.ternary ? pick_gemm<false, kGemmTern>(p.I)
                                  : pick_gemm<false, kGemmFp8>(p.I);
   const int kind = w.tblocked ? 10 : w.ternary ? 2 : 4;
+  if (w.tshared) {
+    // a Sherry-packed shared expert is expert E of the code arrays: one launch over every tile
+    err = launch_gemm(gu, kind, a, 0, w, p, s);
+    if (err == hipSuccess) err = m.mark(s);
+    if (err == hipSuccess) err = launch_gemm(dn, kind + 1, a, 0, w, p, s);
+    return err == hipSuccess ? m.mark(s) : err;
+  }
   err = launch_gemm(gu, kind, a, 1, w, p, s);
   if (err == hipSuccess) err = launch_gemm(pick_gemm<true, kGemmBf16>(p.d), 0, a, 2, w, p, s);
   if (err == hipSuccess) err = m.mark(s);

@@ -622,8 +622,8 @@ __global__ void __launch_bounds__(256, kTlWgPerCu) tern_lds_kernel(StreamArgs a,
   __shared__ __attribute__((aligned(16))) uint8_t s1[kTlSlot];
   constexpr int SUBS = tern_shared_subs<NM>();
   const int T = a.Tk / a.k;
-  const int sh = ((T + 15) / 16) * SUBS;
-  if ((int)blockIdx.y < sh) {
+  const int sh = w.tshared ? (T + kTlTok - 1) / kTlTok : ((T + 15) / 16) * SUBS;
+  if (!w.tshared && (int)blockIdx.y < sh) {
     const int pass = blockIdx.y / SUBS, sub = blockIdx.y - pass * SUBS;
     const int r0 = blockIdx.x * (kTlRows / NM) + sub * 64 + (threadIdx.x >> 6) * 16;
     if (NM == 2)
@@ -632,12 +632,18 @@ __global__ void __launch_bounds__(256, kTlWgPerCu) tern_lds_kernel(StreamArgs a,
       shared_down_pass(a, w, act, reinterpret_cast<float*>(out), r0, a.offs[a.E], 16 * pass, T);
     return;
   }
-  const int ridx = blockIdx.y - sh + 1;  // touched[0] is the shared expert
-  if (ridx >= a.meta[0]) return;         // whole workgroup
+  // a Sherry-packed shared expert (expert E, all T tokens) takes the first grid rows, one
+  // pass of kTlTok tokens each; then one touched routed expert per row (touched[0] is the
+  // shared expert)
+  const bool shared_row = (int)blockIdx.y < sh;
+  const int ridx = blockIdx.y - sh + 1;
+  if (!shared_row && ridx >= a.meta[0]) return;  // whole workgroup
   build_code_table(lut);
   __syncthreads();  // the table's LDS writes are visible to every wave before the first decode
-  const int e = a.touched[ridx];
-  const int row0 = a.offs[e], n = a.offs[e + 1] - row0;
+  const int e = shared_row ? a.E : a.touched[ridx];
+  const int row0 = a.offs[e];
+  const int cb_first = shared_row ? kTlTok * (int)blockIdx.y : 0;
+  const int n = shared_row ? min(a.offs[e + 1] - row0, cb_first + kTlTok) : a.offs[e + 1] - row0;
   const int K = NM == 2 ? a.d : a.I;
   const int R = NM == 2 ? a.I : a.d;  // rows of each matrix
   const int wpr = K / 128 * 5;        // code words per row
@@ -678,12 +684,14 @@ __global__ void __launch_bounds__(256, kTlWgPerCu) tern_lds_kernel(StreamArgs a,
       sc[qb][j] = bf16_bits_to_f32(sp[(size_t)e * R + rbase + rr]);
     }
 
-  for (int cb = 0; cb < n; cb += kTlTok) {  // token passes (uniform)
+  for (int cb = cb_first; cb < n; cb += kTlTok) {  // token passes (uniform)
     // activations: wave wv loads token slot wv of the pass (unused slots repeat a valid
     // row), lane l piece l of each chunk's 1 KB, stored at piece l ^ wv
-    const int col = cb + wv < n ? row0 + cb + wv : row0;
-    // (routed rows are below Tk: their token is perm_src / k)
-    const uint16_t* arow = NM == 2 ? act + (size_t)((uint32_t)a.perm_src[col] / (uint32_t)a.k) * a.d
+    const int col = cb + wv < n ? row0 + cb + wv : row0 + cb_first;
+    // (routed rows are below Tk: their token is perm_src / k; the shared expert's rows
+    // follow in token order)
+    const uint16_t* arow = NM == 2 ? act + (size_t)(col < a.Tk ? (uint32_t)a.perm_src[col] / (uint32_t)a.k
+                                                               : (uint32_t)(col - a.Tk)) * a.d
                                    : act + (size_t)col * a.I;
     const __amdgpu_buffer_rsrc_t xrs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(arow), (short)0, K * 2, kBufferRsrcWord3);
@@ -788,16 +796,18 @@ hipError_t launch_stream_experts(const Plan& p, const uint16_t* x, const ExpertW
   const int sh = (w.ternary || w.fp8) ? ((p.T + 15) / 16) * 2 : 1;
   const int passes = (p.T + 15) / 16;
   if (tern_lds_eligible(p, w)) {
-    // LDS-staged ternary kernels, the shared expert's rows first in each grid
+    // LDS-staged ternary kernels, the shared expert's rows first in each grid (bf16: one
+    // row per 16-token pass and row quarter; Sherry: one per kTlTok-token pass)
     const auto gu = w.tblocked ? tern_lds_kernel<2, true> : tern_lds_kernel<2, false>;
     const auto dn = w.tblocked ? tern_lds_kernel<1, true> : tern_lds_kernel<1, false>;
-    hipLaunchKernelGGL(gu, dim3(p.I / (kTlRows / 2), passes * tern_shared_subs<2>() + routed), dim3(256), 0, s, a, w, x,
-                       (void*)p.h);
+    const int tsh = (p.T + kTlTok - 1) / kTlTok;
+    hipLaunchKernelGGL(gu, dim3(p.I / (kTlRows / 2), (w.tshared ? tsh : passes * tern_shared_subs<2>()) + routed),
+                       dim3(256), 0, s, a, w, x, (void*)p.h);
     hipError_t err = hipGetLastError();
     if (err == hipSuccess) err = m.mark(s);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(dn, dim3(p.d / kTlRows, passes * tern_shared_subs<1>() + routed), dim3(256), 0, s, a, w,
-                       (const uint16_t*)p.h, (void*)p.y);
+    hipLaunchKernelGGL(dn, dim3(p.d / kTlRows, (w.tshared ? tsh : passes * tern_shared_subs<1>()) + routed),
+                       dim3(256), 0, s, a, w, (const uint16_t*)p.h, (void*)p.y);
     err = hipGetLastError();
     return err == hipSuccess ? m.mark(s) : err;
   }

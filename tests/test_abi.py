@@ -351,3 +351,34 @@ def test_blocked_sherry_format_checks_and_workspace():
     for T in (1, 32, 8192):
         assert hm.workspace_size(T, 6144, 256, 8, 2048, hm.WEIGHTS_SHERRY_BLOCKED) == \
             hm.workspace_size(T, 6144, 256, 8, 2048, hm.WEIGHTS_SHERRY_TERNARY)
+
+
+def test_shared_format_checks():
+    # a Sherry shared expert needs the Sherry expert format itself, d and I % 512 and
+    # 16-byte aligned codes; the bf16 shared pointers are then not required
+    def sherry_args(d=512, I=512, fmt=None):
+        a = base_args(T=4, d=d, E=16, k=2, I=I)
+        a.expert_format = hm.WEIGHTS_SHERRY_TERNARY if fmt is None else fmt
+        a.Wq_gate = a.Wq_up = a.Wq_down = a.S_gate = a.S_up = a.S_down = FAKE
+        a.Ws_gate = a.Ws_up = a.Ws_down = None
+        a.shared_format = a.expert_format
+        return a
+    a = base_args()
+    a.shared_format = hm.WEIGHTS_SHERRY_TERNARY  # bf16 routed experts
+    assert call(a) == hm.ERR_INVALID_ARG
+    a = sherry_args(fmt=hm.WEIGHTS_FP8_E4M3)
+    assert call(a) == hm.ERR_INVALID_ARG
+    a = sherry_args()
+    a.shared_format = 7
+    assert call(a) == hm.ERR_INVALID_ARG
+    a = sherry_args()
+    a.shared_format = hm.WEIGHTS_SHERRY_BLOCKED  # must equal the expert format
+    assert call(a) == hm.ERR_INVALID_ARG
+    a = sherry_args()
+    a.Wq_up = FAKE + 4
+    assert call(a) == hm.ERR_INVALID_ARG
+    assert call(sherry_args(I=256)) == hm.ERR_UNSUPPORTED
+    assert call(sherry_args(d=384)) == hm.ERR_UNSUPPORTED
+    a = sherry_args()
+    a.shared_format = hm.WEIGHTS_BF16  # then the bf16 shared pointers are required
+    assert call(a) == hm.ERR_INVALID_ARG

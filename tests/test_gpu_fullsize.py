@@ -16,6 +16,7 @@ GEMM's schedule (tile_sample). The oracle's expert weights are copies of the
 generator's device tensors (never a result of the HIP path), taken one expert at
 a time. Rules and tolerances: tests/parity.py.
 """
+import dataclasses
 import time
 
 import numpy as np
@@ -70,8 +71,12 @@ class DeviceExperts:
 def reference_outputs(cfg, inp, x_host, sets, w, tokens, gpu_res=None):
     """Oracle outputs of `tokens`: the shared expert, then each routed expert the
     tokens use, one expert's weights at a time, combined in fp64."""
-    sh = {n: bf16_tensor_bits(v) for n, v in inp["shared"].items()}
-    ys = oracle.ffn(x_host[tokens], sh["gate"], sh["up"], sh["down"])
+    if inp.get("shared_sherry"):  # expert E of the Sherry arrays
+        (sg, su, sdn), _ = DeviceExperts(inp).get(cfg.E)
+        ys = oracle.ffn(x_host[tokens], sg, su, sdn)
+    else:
+        sh = {n: bf16_tensor_bits(v) for n, v in inp["shared"].items()}
+        ys = oracle.ffn(x_host[tokens], sh["gate"], sh["up"], sh["down"])
     yr = np.zeros((len(tokens), cfg.k, cfg.d))
     by_expert = {}
     for i, t in enumerate(tokens):
@@ -211,6 +216,17 @@ def test_blocked_sherry_full_size():
         for key in ("topk_idx", "counts", "perm_src"):
             assert torch.equal(got[key], ref[key]), (name, key)
         del inp, blk, ref, got
+        torch.cuda.empty_cache()
+
+
+def test_sherry_shared_expert_full_size():
+    """A Sherry-packed shared expert at the ternary decode size (every token against the
+    oracle) and the ternary prefill size (tile-covering sample)."""
+    for name, sample in (("ternary", "all"), ("ternary_prefill", "tiles")):
+        cfg = dataclasses.replace(hi.CONFIGS[name], tshared=True)
+        inp = hi.dev_layer(cfg, device=DEV)
+        run_full(cfg, inp, sample=sample)
+        del inp
         torch.cuda.empty_cache()
 
 

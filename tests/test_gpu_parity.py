@@ -37,10 +37,19 @@ def host_weights_bf16(cfg, L):
     return gate, up, down
 
 
+def host_shared_bf16(cfg, L):
+    """The shared expert's (gate, up, down) bf16 bit arrays for the oracle: the bf16
+    matrices, or expert E of the Sherry arrays decoded."""
+    if not (cfg.ternary and cfg.tshared):
+        return L["shared"]["gate"], L["shared"]["up"], L["shared"]["down"]
+    E = cfg.E
+    return tuple(oracle.sherry_decode(L["q" + m][E], L["s" + m][E])[1] for m in ("gate", "up", "down"))
+
+
 def run_small(cfg, path, bias=None, x_host=None, label="", fp8_codes=None):
     """Full element-by-element comparison on a small layer."""
     say(f"[case] {label or cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} I={cfg.I} "
-        f"ternary={cfg.ternary} fp8={cfg.fp8} w8a8={cfg.a8} path={path}")
+        f"ternary={cfg.ternary} tshared={cfg.tshared} fp8={cfg.fp8} w8a8={cfg.a8} path={path}")
     L = hi.host_layer(cfg)
     inp = hi.dev_layer(cfg, device=DEV)
     if fp8_codes is not None:  # caller-chosen codes and scales
@@ -68,8 +77,8 @@ def run_small(cfg, path, bias=None, x_host=None, label="", fp8_codes=None):
                   cfg.k, sets_in=sets)
     else:
         gate, up, down = host_weights_bf16(cfg, L)
-        ref = oracle.forward(L["x"], L["router"], L["bias"], gate, up, down, L["shared"]["gate"], L["shared"]["up"],
-                             L["shared"]["down"], cfg.k, sets_in=sets)
+        ref = oracle.forward(L["x"], L["router"], L["bias"], gate[:cfg.E], up[:cfg.E], down[:cfg.E],
+                             *host_shared_bf16(cfg, L), cfg.k, sets_in=sets)
     if cfg.a8:
         # the GPU's hidden rows must be admissible quantizations of the oracle's; the
         # oracle's down projection then runs on them (tests/parity.py)
@@ -434,6 +443,30 @@ def test_blocked_sherry_match_row_major(shape, path):
     assert torch.equal(got["out"].view(torch.int16), ref["out"].view(torch.int16))
     for key in ("topk_idx", "counts", "perm_src"):
         assert torch.equal(got[key], ref[key])
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("shape", [
+    dict(T=1, d=512, E=16, k=2, I=512),      # one token: one shared pass of 4
+    dict(T=43, d=1024, E=16, k=4, I=512),    # ragged last shared pass (43 = 10 x 4 + 3)
+    dict(T=300, d=512, E=8, k=2, I=1024),    # grouped: two shared M tiles
+])
+def test_sherry_shared_expert(shape, path):
+    """The shared expert Sherry-packed as expert E of the code arrays (shared_format)."""
+    cfg = hi.LayerConfig("tsh", ternary=True, tshared=True, seed=8, **shape)
+    run_small(cfg, path)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_sherry_shared_expert_blocked(path):
+    T, d, E, k, I = 70, 512, 16, 2, 1536
+    say(f"[case] blocked Sherry codes with a Sherry shared expert T={T} d={d} E={E} k={k} I={I} path={path}")
+    cfg = hi.LayerConfig("tshb", T=T, d=d, E=E, k=k, I=I, ternary=True, tshared=True, seed=34)
+    inp = hi.dev_layer(cfg, device=DEV)
+    ref = hm.forward_layer(inp, k, want_routing=True, path=path)
+    got = hm.forward_layer(hm.block_layer(inp), k, want_routing=True, path=path, weights_blocked=True)
+    torch.cuda.synchronize()
+    assert torch.equal(got["out"].view(torch.int16), ref["out"].view(torch.int16))
 
 
 # ------------------------------------------------- large cancelling expert outputs
