@@ -2,8 +2,9 @@
 hy_moe_forward_ex with a caller workspace, through the C ABI: the same kernels run
 on the same inputs, so outputs and routing must be bitwise identical. Calls run back
 to back on one device with shrinking and growing batches (each call must rewrite
-whatever it reads of the buffer), on both expert paths, on Sherry weights and on the
-W8A8 format; the first case is also checked against the fp64 oracle."""
+whatever it reads of the buffer), on both expert paths, on Sherry weights (with a bf16
+or a Sherry shared expert) and on the W8A8 format; the first case is also checked
+against the fp64 oracle."""
 import pytest
 
 import hy_inputs as hi
@@ -65,6 +66,8 @@ def test_noalloc_ternary_and_hy4_decode_shape():
     tern = hi.LayerConfig("nat", T=24, d=1024, E=16, k=4, I=512, ternary=True, seed=12)
     inp = hi.dev_layer(tern, device=DEV)
     compare(inp, tern.k, hm.PATH_AUTO, "Sherry weights")
+    tsh = hi.LayerConfig("nats", T=24, d=1024, E=16, k=4, I=512, ternary=True, tshared=True, seed=15)
+    compare(hi.dev_layer(tsh, device=DEV), tsh.k, hm.PATH_AUTO, "Sherry weights, Sherry shared expert")
     # the Hy4 decode batch at its largest admitted size and at T=32, on a few experts'
     # worth of shape (d, I as the Hy4 layer; fewer experts keep the weights small)
     cfg = hi.LayerConfig("nah", T=251, d=6144, E=16, k=8, I=2048, seed=13)
