@@ -95,12 +95,15 @@ typedef enum {
    * section 2.1; the same pointers W_gate/W_up/W_down and Ws_gate/Ws_up/Ws_down, the same
    * sizes), every expert matrix, routed and shared, stored in this library's blocked
    * layout: a matrix of R rows by K columns (R = I and K = d for gate and up, R = d and
-   * K = I for down) becomes [R/16][K/64][16][64]: the 64 values of row r in columns
-   * [64 c, 64 c + 64) start at element 1024 * ((r / 16) * (K / 64) + c) + 64 * (r % 16).
-   * Each 16-row group's 64-column slab is then one contiguous 2 KB run, which the
-   * streaming path reads from HBM faster than 16 rows a whole row apart. Results are
-   * bitwise identical to HY_MOE_WEIGHTS_BF16 on the same weights. hy_moe_block_bf16
-   * converts row-major matrices. */
+   * K = I for down) becomes one 1024-value (2 KB) block per 16-row group and 64-column
+   * slab, blocks in (row group, slab) order; the 8 values of row r in columns
+   * [64 c + 8 q, 64 c + 8 q + 8) (q < 8) start at element
+   * 1024 * ((r / 16) * (K / 64) + c) + 8 * (64 * (q % 2) + 16 * (q / 2) + r % 16).
+   * Each 16-row group's 64-column slab is then one contiguous 2 KB run, in the order the
+   * streaming path's load instructions take it (1 KB in order each), which HBM delivers
+   * faster than 16 rows a whole row apart. Results are bitwise identical to
+   * HY_MOE_WEIGHTS_BF16 on the same weights. hy_moe_block_bf16 converts row-major
+   * matrices. */
   HY_MOE_WEIGHTS_BF16_BLOCKED = 4,
   /* Sherry ternary codes as HY_MOE_WEIGHTS_SHERRY_TERNARY (the same pointers, scales and
    * sizes; ai.chattools.top article, section on Sherry and MIX-STQ1_0), each code matrix

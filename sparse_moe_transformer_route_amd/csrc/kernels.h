@@ -84,7 +84,7 @@ struct ExpertWeights {
   bool ternary;
   bool fp8;
   bool a8;       // with fp8: MXFP8 activations (W8A8)
-  bool blocked;   // bf16 in the blocked layout ([rows/16][cols/64][16][64] per matrix, shared expert too)
+  bool blocked;   // bf16 in the blocked layout (2 KB per 16 rows x 64 columns, per matrix, shared expert too)
   bool tblocked;  // with ternary: code matrices in the blocked layout ([rows/16][cols/512][16][80 B])
   bool tshared;   // with ternary: the shared expert is Sherry-packed, expert E of the code and scale arrays
 };

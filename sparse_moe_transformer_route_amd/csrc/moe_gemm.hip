@@ -78,15 +78,24 @@ static_assert(kF8Ops == kCodeOps, "the code and FP8 load offsets share storage")
 // activations on the FP8 matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4): a k step is
 // 128 codes (128 bytes per row, as the bf16 step's 64 values), two MFMA groups of 64;
 // the activations' E8M0 block scales reach the MFMAs from registers.
-// kGemmBf16Blk: bf16 weights in the blocked layout ([rows/16][cols/64][16][64] per
-// matrix): the bf16 kernel with the weight rows' 128-byte pieces of step ks at
-// 2048 ((row / 16) K/64 + ks) + 128 (row % 16) instead of 2 K row + 128 ks.
+// kGemmBf16Blk: bf16 weights in the blocked layout (2 KB per 16 rows x 64 columns, pieces
+// in lane order, blk_piece): a step's weight slot holds the tile's 16 blocks of that step
+// as they are in memory (block g of the slot: tile rows 16 g .. 16 g + 15), so each load
+// op copies 1 KB in order (half a block), and a fragment read (32 rows of one 16-byte
+// column piece) takes two runs of 256 contiguous bytes: no conflicts without a swizzle.
 // kGemmTernBlk: Sherry codes in the blocked layout ([rows/16][K/512][16][80 B]): the
 // ternary kernel with row r's window of step ks at 1280 ((r / 16) K/512 + ks / 8) +
 // 80 (r % 16) + 4 floor(10 (ks % 8) / 4) instead of K/128 20 r + 4 floor(10 ks / 4).
 constexpr int kGemmBf16 = 0, kGemmTern = 1, kGemmFp8 = 2, kGemmW8A8 = 3, kGemmBf16Blk = 4, kGemmTernBlk = 5;
 constexpr int kBK8 = 128;        // W8A8: k per step
 constexpr int kSub8 = kBK8 / 64;  // W8A8: MFMA groups per step
+
+// Blocked bf16 layout: the 16-byte piece of row r (< 16) holding its columns
+// [8 q, 8 q + 8) of a 64-column slab is piece 64 (q % 2) + 16 (q / 2) + r of the slab's
+// 2 KB block.
+__device__ __forceinline__ uint32_t blk_piece(int r, int q) {
+  return 64u * (uint32_t)(q & 1) + 16u * (uint32_t)(q >> 1) + (uint32_t)r;
+}
 
 // Two 16-byte LDS reads into one 8-register operand.
 __device__ __forceinline__ i32x8 lds_pair(const uint8_t* p0, const uint8_t* p1) {
@@ -352,6 +361,12 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
       const int c = FP8 ? 4 * (s >> 1) + 2 * hf + (s & 1) : 2 * s + hf;
       frag_lo[s] = (uint32_t)(r32 * kRowBytes + ((c ^ swz_key(r32)) << 4));
     }
+    // blocked weights: piece c of block row r32 within the 32-row block (blocks of 16 rows,
+    // 2 KB apart)
+    uint32_t fragb_lo[kSub];
+#pragma unroll
+    for (int s = 0; s < kSub; ++s)
+      fragb_lo[s] = BLK ? 2048u * (uint32_t)(r32 >> 4) + 16u * blk_piece(r32 & 15, 2 * s + hf) : frag_lo[s];
     // FP8: the codes of groups 2q, 2q + 1 (chunks 4q + 2hf, 4q + 2hf + 1: bytes
     // [32 q + 16 hf, +16) of the row's step) are piece 2q + hf, stored at piece
     // (2q + hf) ^ f8_key(r32) of the row's line (blocks start at multiples of 32 rows)
@@ -440,8 +455,11 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
                                             : (routed ? w.up + (size_t)e * a.I * a.d : w.s_up);
         const int r0 = nt * (kRowsMax / 2) + 64 * (qq >> 1), rr = row & 63;  // the quarter's first unit, row in it
         if constexpr (BLK) {
+          // slot piece q of the step: block q / 128 of the tile (block 2 (i % 2) + wv / 2 of
+          // quarter qq = i / 2), piece q % 128 of it
           bbase[i] = reinterpret_cast<const char*>(mat + (size_t)(r0 / 16) * (a.d / 64) * 1024);
-          boff[i] = ((uint32_t)(rr / 16) * (uint32_t)(a.d / 64) * 1024u + (uint32_t)(rr % 16) * 64u + 8 * lc) * 2u;
+          boff[i] = ((uint32_t)(2 * (i & 1) + (wv >> 1)) * (uint32_t)(a.d / 64) * 1024u +
+                     8u * (uint32_t)(q & 127)) * 2u;
         } else {
           bbase[i] = reinterpret_cast<const char*>(mat + (size_t)r0 * a.d);
           boff[i] = ((uint32_t)rr * (uint32_t)a.d + 8 * lc) * 2u;
@@ -451,8 +469,11 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
         const uint16_t* mat = routed ? w.down + (size_t)e * a.d * a.I : w.s_down;
         const int rr = min(nt * kRowsMax + row, a.d - 1) - nt * kRowsMax;  // output column in the tile, clamped
         if constexpr (BLK) {
+          // slot piece q: block q / 128 of the tile (output columns nt*256 + 16 (q / 128) ..,
+          // a block past d clamped to the last one: not stored), piece q % 128 of it
+          const int gb = min(nt * (kRowsMax / 16) + (q >> 7), a.d / 16 - 1) - nt * (kRowsMax / 16);
           bbase[i] = reinterpret_cast<const char*>(mat + (size_t)(nt * kRowsMax / 16) * (a.I / 64) * 1024);
-          boff[i] = ((uint32_t)(rr / 16) * (uint32_t)(a.I / 64) * 1024u + (uint32_t)(rr % 16) * 64u + 8 * lc) * 2u;
+          boff[i] = ((uint32_t)gb * (uint32_t)(a.I / 64) * 1024u + 8u * (uint32_t)(q & 127)) * 2u;
         } else {
           bbase[i] = reinterpret_cast<const char*>(mat + (size_t)nt * kRowsMax * a.I);
           boff[i] = ((uint32_t)rr * (uint32_t)a.I + 8 * lc) * 2u;
@@ -646,7 +667,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs a, E
             if ((s & 1) == 0)  // the pair's codes, read with its first group
               fc[(s >> 1) & 1][nb] = *reinterpret_cast<const uint4*>(Lb + (128 * wn + 32 * nb) * kF8Pitch + f8o[s >> 1]);
           } else
-            fb[s & 1][nb] = *reinterpret_cast<const uint4*>(Lb + fb_off + nb * kBlk * kRowBytes + frag_lo[s]);
+            fb[s & 1][nb] = *reinterpret_cast<const uint4*>(Lb + fb_off + nb * kBlk * kRowBytes + fragb_lo[s]);
         }
       };
       // Ternary: the step's code windows of the lane's 4 weight rows (128 wn + 32 nb +

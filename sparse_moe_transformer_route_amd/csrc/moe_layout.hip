@@ -1,12 +1,16 @@
 // moe_layout: the blocked layouts of HY_MOE_WEIGHTS_BF16_BLOCKED and
-// HY_MOE_WEIGHTS_SHERRY_BLOCKED (the latter below). A row-major bf16
-// matrix [rows][cols] becomes [rows/16][cols/64][16][64]: every 16-row group's 64-column
-// slab is one contiguous 2 KB run. The streaming kernels read a wave's 16 rows one
-// 64-column chunk at a time; with row-major weights those 16 pieces of 128 bytes lie a
-// whole row apart (12 KB at d = 6144) and HBM delivered ~5.75 TB/s for that pattern, with
-// the blocked layout ~6.15 TB/s (the sequential rate). The grouped GEMM still reads each
-// row's 128-byte piece as one line. The conversion is a plain permutation of 16-byte
-// pieces, run once when a model's weights are loaded.
+// HY_MOE_WEIGHTS_SHERRY_BLOCKED (the latter below). A row-major bf16 matrix
+// [rows][cols] becomes one 2 KB block per 16-row group and 64-column slab, blocks in
+// (row group, slab) order. Inside a block, the 16-byte piece q (columns [8 q, 8 q + 8) of
+// the slab) of row r sits at piece 64 (q % 2) + 16 (q / 2) + r: the order in which the
+// lanes of a streaming wave take them (lane 16 g + r holds row r, columns 16 g .. 16 g +
+// 15 of the slab, as its pieces 16 g + r and 64 + 16 g + r), so each load instruction
+// reads 1 KB in order. With row-major weights a wave's 16 rows lie a whole row apart (12
+// KB at d = 6144) and HBM delivered ~5.75 TB/s for that pattern; whole 2 KB runs with
+// rows in order inside gave ~6.15 TB/s; runs read in lane order with non-temporal loads
+// ~7 TB/s. The grouped GEMM's load ops cover 8 rows x 8 pieces, still 8 whole lines. The
+// conversion is a plain permutation of 16-byte pieces, run once when a model's weights
+// are loaded.
 #include "hy_moe.h"
 #include "common.h"
 #include "kernels.h"
@@ -15,8 +19,8 @@ namespace hymoe {
 
 constexpr int kBlockThreads = 256;
 
-// One thread per 16-byte piece (8 values) of the source, read in order; it lands at the
-// same place of its row's 128-byte piece in the block of (row / 16, col / 64).
+// One thread per 16-byte piece (8 values) of the source, read in order; piece q of row r's
+// 64-column slab c lands at piece 64 (q % 2) + 16 (q / 2) + r % 16 of block (r / 16, c).
 __global__ void __launch_bounds__(kBlockThreads) block_bf16_kernel(const uint4* __restrict__ src,
                                                                     uint4* __restrict__ dst, int64_t pieces,
                                                                     int64_t rows, int64_t cols) {
@@ -26,8 +30,8 @@ __global__ void __launch_bounds__(kBlockThreads) block_bf16_kernel(const uint4* 
     const int64_t m = t / per_mat, rem = t - m * per_mat;
     const int64_t r = rem / per_row, q = rem - r * per_row;
     const int64_t c = q / 8, j = q - c * 8;
-    // in 16-byte pieces: block (r / 16, c) holds 128 pieces, row r % 16 of it 8
-    const int64_t o = m * per_mat + ((r / 16) * chunks + c) * 128 + (r % 16) * 8 + j;
+    // in 16-byte pieces: block (r / 16, c) holds 128 pieces
+    const int64_t o = m * per_mat + ((r / 16) * chunks + c) * 128 + 64 * (j & 1) + 16 * (j >> 1) + (r % 16);
     dst[o] = src[t];
   }
 }

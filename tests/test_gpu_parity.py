@@ -374,9 +374,9 @@ def test_bitwise_deterministic_and_workspace_independent(path):
 
 # ------------------------------------------------------------ blocked bf16 layout
 def test_block_bf16_matches_layout_definition():
-    """hy_moe_block_bf16 against the layout's definition, written out element by element:
-    row r's 64 values in columns [64 c, 64 c + 64) start at element
-    1024 ((r / 16) (K / 64) + c) + 64 (r % 16) of its matrix."""
+    """hy_moe_block_bf16 against the layout's definition, written out piece by piece: the
+    8 values of row r in columns [64 c + 8 q, 64 c + 8 q + 8) start at element
+    1024 ((r / 16) (K / 64) + c) + 8 (64 (q % 2) + 16 (q / 2) + r % 16) of its matrix."""
     say("[case] block_bf16 on 3 matrices of 48 x 192")
     g = torch.Generator(device=DEV).manual_seed(5)
     t = torch.randn(3, 48, 192, generator=g, device=DEV).to(torch.bfloat16)
@@ -389,8 +389,9 @@ def test_block_bf16_matches_layout_definition():
     for m in range(3):
         for r in range(R):
             for c in range(K // 64):
-                o = 1024 * ((r // 16) * (K // 64) + c) + 64 * (r % 16)
-                exp[m, o:o + 64] = src[m, r, 64 * c:64 * c + 64]
+                for q in range(8):
+                    o = 1024 * ((r // 16) * (K // 64) + c) + 8 * (64 * (q % 2) + 16 * (q // 2) + r % 16)
+                    exp[m, o:o + 8] = src[m, r, 64 * c + 8 * q:64 * c + 8 * q + 8]
     assert np.array_equal(got, exp)
 
 
