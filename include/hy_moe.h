@@ -323,7 +323,8 @@ int hy_moe_block_sherry(const void* src, void* dst, int64_t count, int64_t rows,
  *   values: random bytes include NaN codes). 2 flop per multiply-add.
  * hy_moe_probe_hbm_read: reads buf (DEVICE, 16-byte aligned, `bytes` >= 16; use
  *   much more than the 256 MB last-level cache) once untimed, then three times timed
- *   with 16-byte loads. Writes the best pass's GB/s (1e9 B/s) to *gbps (HOST).
+ *   with non-temporal 16-byte loads, 1 KB in order per wave instruction. Writes the best
+ *   pass's GB/s (1e9 B/s) to *gbps (HOST).
  */
 #define HY_MOE_PROBE_OPERAND_BYTES 65536
 int hy_moe_probe_mfma_bf16(const void* operands, size_t operand_bytes, float* tflops, void* stream);

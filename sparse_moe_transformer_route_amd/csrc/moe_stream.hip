@@ -51,8 +51,11 @@ __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 // rate from ~6.3 to ~7.0 TB/s (weights are read exactly once per layer).
 constexpr int kKV = 2;                  // 16-byte loads per lane per matrix per chunk
 constexpr int kChunk = 4 * kKV * 8;     // elements of a row per chunk (4 lane groups)
-constexpr int kDepthGateUp = 5;         // chunks in flight, gate/up (two matrices)
-constexpr int kDepthDown = 3;           // chunks in flight, down (one matrix)
+// Ring depths with non-temporal blocked loads (same-process A/B, decode T=32, gate/up
+// depth / down depth: 5/3 1.800 ms, 3/5 1.788, 5/5 1.793, 6/5 1.776: within ~1%);
+// depth 3 keeps gate/up at 148 registers, three waves per SIMD.
+constexpr int kDepthGateUp = 3;         // chunks in flight, gate/up (two matrices)
+constexpr int kDepthDown = 5;           // chunks in flight, down (one matrix)
 // In the ternary kernels only the shared expert streams bf16: a shallow ring keeps their
 // register count, and so the number of waves hiding the code-table lookups, in check.
 constexpr int kDepthSharedTern = 2;
