@@ -660,8 +660,8 @@ def main():
                  "hbm_read_bytes": read_buf.numel() * read_buf.element_size(),
                  "how": "hy_moe_probe_mfma_bf16 (32x32x16 bf16 MFMAs, 4 workgroups per CU, random N(0,1) operands, "
                         "~40 ms), hy_moe_probe_mfma_fp8 (32x32x64 E4M3 MFMAs with unit block scales on the same "
-                        "values as E4M3 codes, ~40 ms) and hy_moe_probe_hbm_read (best of three timed streaming passes of 16-byte loads "
-                        "after an untimed one)"}
+                        "values as E4M3 codes, ~40 ms) and hy_moe_probe_hbm_read (best of three timed streaming passes of "
+                        "non-temporal 16-byte loads, 1 KB in order per wave instruction, after an untimed one)"}
         del read_buf
         if full:
             peaks["library_gemm_bf16"] = library_gemm_reference(torch)
