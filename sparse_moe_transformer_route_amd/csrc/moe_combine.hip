@@ -17,8 +17,11 @@ __device__ __forceinline__ void load8(const float* p, float* v) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
+// bf16 expert outputs (grouped path): every y row is read once, and a wave reads 1 KB of
+// it in order, so the loads take the non-temporal hint (T=8192: ~25 us off the combine's
+// ~0.21 ms; results unchanged)
 __device__ __forceinline__ void load8(const uint16_t* p, float* v) {
-  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  const uint4 a = ldg16_stream(p);
   const uint32_t u[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
