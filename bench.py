@@ -571,6 +571,30 @@ def run_indexer(args, hi, hm, torch):
     print(json.dumps(line), flush=True)
 
 
+def library_batched_gemm_reference(torch, seconds=0.5):
+    """torch.bmm (hipBLASLt) on 256 batched bf16 GEMMs of 288 x 6144 @ 6144 x 4096: the prefill
+    gate/up work (73728 rows in all) with one weight matrix per expert, 12.9 GB of distinct
+    weights as in the layer, but equal batches, contiguous rows and no gather."""
+    g = torch.Generator(device="cuda:0").manual_seed(2)
+    a = torch.randn(256, 288, 6144, generator=g, device="cuda:0", dtype=torch.bfloat16)
+    b = (torch.randn(256, 6144, 4096, generator=g, device="cuda:0", dtype=torch.bfloat16) / 78.0).contiguous()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        torch.bmm(a, b)
+        torch.cuda.synchronize()
+    n = 10
+    t0 = time.perf_counter()
+    for _ in range(n):
+        torch.bmm(a, b)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / n
+    del a, b
+    torch.cuda.empty_cache()
+    return {"tflops": 2 * 73728 * 6144 * 4096 / dt / 1e12, "ms": dt * 1e3,
+            "how": "torch.bmm bf16 [256 x 288 x 6144] @ [256 x 6144 x 4096] (hipBLASLt; one weight matrix per "
+                   "batch, 12.9 GB), mean of 10 after 0.5 s warm"}
+
+
 def library_gemm_reference(torch, seconds=0.5):
     """torch.matmul (hipBLASLt) on one dense bf16 GEMM of the prefill gate/up shape
     (73728 x 6144 @ 6144 x 4096, N(0,1)-like operands): what AMD's GEMM library reaches on
@@ -665,9 +689,11 @@ def main():
         del read_buf
         if full:
             peaks["library_gemm_bf16"] = library_gemm_reference(torch)
+            peaks["library_batched_gemm_bf16"] = library_batched_gemm_reference(torch)
         log(f"[bench] measured peaks: {peaks['mfma_bf16_tflops']:.0f} TFLOP/s bf16 MFMA, "
             f"{peaks['hbm_read_gbs']:.0f} GB/s HBM read"
-            + (f", hipBLASLt dense GEMM {peaks['library_gemm_bf16']['tflops']:.0f} TFLOP/s" if full else ""))
+            + (f", hipBLASLt dense GEMM {peaks['library_gemm_bf16']['tflops']:.0f} TFLOP/s, batched per-expert GEMM "
+               f"{peaks['library_batched_gemm_bf16']['tflops']:.0f} TFLOP/s" if full else ""))
         # back to load right away: the clock drops when the GPU idles
         hm.probe_mfma_bf16(ops)
 
@@ -736,6 +762,8 @@ def main():
             r["frac_of_measured_peak"] = r["achieved"] / measured_peak_of(r, peaks)
             if r["unit"] == "TFLOP/s" and "library_gemm_bf16" in peaks:
                 r["frac_of_library_dense_gemm"] = r["achieved"] / peaks["library_gemm_bf16"]["tflops"]
+            if r["unit"] == "TFLOP/s" and "library_batched_gemm_bf16" in peaks:
+                r["frac_of_library_batched_gemm"] = r["achieved"] / peaks["library_batched_gemm_bf16"]["tflops"]
 
     cpu = None
     if not args.no_cpu_baseline and not args.only:
