@@ -19,8 +19,9 @@ namespace hymoe {
 
 constexpr int kBlockThreads = 256;
 
-// One thread per 16-byte piece (8 values) of the source, read in order; piece q of row r's
-// 64-column slab c lands at piece 64 (q % 2) + 16 (q / 2) + r % 16 of block (r / 16, c).
+// One thread per 16-byte piece (8 values) of the destination, written in order (whole
+// lines); piece P of block (row group G, slab c) is piece q = 2 ((P / 16) % 4) + P / 64 of
+// row 16 G + P % 16's slab c: a block's 128 threads read its 16 rows' 128-byte pieces whole.
 __global__ void __launch_bounds__(kBlockThreads) block_bf16_kernel(const uint4* __restrict__ src,
                                                                     uint4* __restrict__ dst, int64_t pieces,
                                                                     int64_t rows, int64_t cols) {
@@ -28,11 +29,10 @@ __global__ void __launch_bounds__(kBlockThreads) block_bf16_kernel(const uint4* 
   for (int64_t t = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x; t < pieces;
        t += (int64_t)gridDim.x * kBlockThreads) {
     const int64_t m = t / per_mat, rem = t - m * per_mat;
-    const int64_t r = rem / per_row, q = rem - r * per_row;
-    const int64_t c = q / 8, j = q - c * 8;
-    // in 16-byte pieces: block (r / 16, c) holds 128 pieces
-    const int64_t o = m * per_mat + ((r / 16) * chunks + c) * 128 + 64 * (j & 1) + 16 * (j >> 1) + (r % 16);
-    dst[o] = src[t];
+    const int64_t b = rem / 128, pc = rem - b * 128;  // block (row group, slab) and its piece
+    const int64_t g = b / chunks, c = b - g * chunks;
+    const int64_t r = 16 * g + (pc & 15), q = 2 * ((pc >> 4) & 3) + (pc >> 6);
+    dst[t] = src[m * per_mat + r * per_row + 8 * c + q];
   }
 }
 
