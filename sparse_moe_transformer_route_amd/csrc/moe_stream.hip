@@ -148,6 +148,60 @@ __device__ __forceinline__ void gateup_bf16_block(const uint16_t* __restrict__ w
       });
 }
 
+// The same for two 16-token passes at once (the shared expert, whose rows are all T
+// tokens): each weight chunk is loaded once for both activation sets. Depth 2 keeps the
+// ring at the routed path's register count.
+template <int D, bool BLK>
+__device__ __forceinline__ void gateup_bf16_block_x2(const uint16_t* __restrict__ wg, const uint16_t* __restrict__ wu,
+                                                     const uint16_t* __restrict__ xr0, const uint16_t* __restrict__ xr1,
+                                                     int d, f32x4 (&accg)[2], f32x4 (&accu)[2]) {
+  constexpr int WS = BLK ? kBlkChunk : kChunk, VS = BLK ? 512 : 8;
+  uint4 rg[D + 1][kKV], ru[D + 1][kKV], rx[D + 1][2][kKV];
+  ring_stream<D>(
+      d / kChunk,
+      [&](int ch, int slot) {
+#pragma unroll
+        for (int v = 0; v < kKV; ++v) {
+          rg[slot][v] = ldw<BLK>(wg + ch * WS + VS * v);
+          ru[slot][v] = ldw<BLK>(wu + ch * WS + VS * v);
+          rx[slot][0][v] = ldg16(xr0 + ch * kChunk + 8 * v);
+          rx[slot][1][v] = ldg16(xr1 + ch * kChunk + 8 * v);
+        }
+      },
+      [&](int u) {
+#pragma unroll
+        for (int v = 0; v < kKV; ++v)
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            accg[p] = mfma16x16x32(rg[u][v], rx[u][p][v], accg[p]);
+            accu[p] = mfma16x16x32(ru[u][v], rx[u][p][v], accu[p]);
+          }
+      });
+}
+
+template <int D, bool BLK>
+__device__ __forceinline__ void down_bf16_block_x2(const uint16_t* __restrict__ wd, const uint16_t* __restrict__ hr0,
+                                                   const uint16_t* __restrict__ hr1, int I, f32x4 (&acc)[2]) {
+  constexpr int WS = BLK ? kBlkChunk : kChunk, VS = BLK ? 512 : 8;
+  uint4 rw[D + 1][kKV], rx[D + 1][2][kKV];
+  ring_stream<D>(
+      I / kChunk,
+      [&](int ch, int slot) {
+#pragma unroll
+        for (int v = 0; v < kKV; ++v) {
+          rw[slot][v] = ldw<BLK>(wd + ch * WS + VS * v);
+          rx[slot][0][v] = ldg16(hr0 + ch * kChunk + 8 * v);
+          rx[slot][1][v] = ldg16(hr1 + ch * kChunk + 8 * v);
+        }
+      },
+      [&](int u) {
+#pragma unroll
+        for (int v = 0; v < kKV; ++v)
+#pragma unroll
+          for (int p = 0; p < 2; ++p) acc[p] = mfma16x16x32(rw[u][v], rx[u][p][v], acc[p]);
+      });
+}
+
 // ------------------------------------------------------------- FP8 experts
 // Per chunk, lane group g loads the 32 codes of k [32 g, 32 g + 32) of each of its rows
 // (two 16-byte loads) and the 32 matching activations (four); MFMA m of the chunk takes
@@ -314,8 +368,11 @@ __device__ __forceinline__ int shared_slots(const StreamArgs& a, bool tern) {
   return tern ? ((a.Tk / a.k + 15) / 16) * 2 : 1;
 }
 
+// bf16 kernels: three workgroups (waves per SIMD) per CU, the shared expert's two-pass
+// path included
 template <int WF>
-__global__ void __launch_bounds__(256) stream_gateup_kernel(StreamArgs a, ExpertWeights w, uint16_t* __restrict__ h) {
+__global__ void __launch_bounds__(256, (WF == kWfBf16 || WF == kWfBf16Blk) ? 3 : 1)
+    stream_gateup_kernel(StreamArgs a, ExpertWeights w, uint16_t* __restrict__ h) {
   constexpr bool TERN = WF == kWfTern, FP8 = WF == kWfFp8, WIDE = TERN || FP8, BLK = WF == kWfBf16Blk;
   __shared__ uint2 lut[32];
   if (TERN) {
@@ -389,7 +446,31 @@ __global__ void __launch_bounds__(256) stream_gateup_kernel(StreamArgs a, Expert
     const size_t roff = BLK ? (size_t)(i0 / 16) * (d / 64) * 1024 + 8 * lane : (size_t)(i0 + r16) * d + kKV * 8 * g;
     const uint16_t* wg = (routed ? w.gate + (size_t)e * I * d : w.s_gate) + roff;
     const uint16_t* wu = (routed ? w.up + (size_t)e * I * d : w.s_up) + roff;
-    for (int cb = cb_first; cb < n; cb += 16) {
+    int cb = cb_first;
+    if (!WIDE && !routed) {
+      // the shared expert: two 16-token passes per weight stream
+      for (; cb + 16 < n; cb += 32) {
+        int col[2];
+        bool valid[2];
+        const uint16_t* xr[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          valid[p] = cb + 16 * p + r16 < n;
+          col[p] = valid[p] ? row0 + cb + 16 * p + r16 : row0;
+          xr[p] = a.x + (size_t)row_token(col[p], a.perm_src, a.Tk, a.k) * d + kKV * 8 * g;
+        }
+        f32x4 accg[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, accu[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        gateup_bf16_block_x2<2, BLK>(wg, wu, xr[0], xr[1], d, accg, accu);
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+          if (valid[p]) {
+            uint2 v = make_uint2(pack_bf16x2(silu(accg[p][0]) * accu[p][0], silu(accg[p][1]) * accu[p][1]),
+                                 pack_bf16x2(silu(accg[p][2]) * accu[p][2], silu(accg[p][3]) * accu[p][3]));
+            *reinterpret_cast<uint2*>(h + (size_t)col[p] * I + i0 + 4 * g) = v;
+          }
+      }
+    }
+    for (; cb < n; cb += 16) {
       const bool valid = cb + r16 < n;
       const int col = valid ? row0 + cb + r16 : row0;
       const uint16_t* xr = a.x + (size_t)row_token(col, a.perm_src, a.Tk, a.k) * d + kKV * 8 * g;
@@ -510,7 +591,28 @@ __global__ void __launch_bounds__(256) stream_down_kernel(StreamArgs a, ExpertWe
     // (lane pieces of the blocked layout as in the gate/up kernel)
     const size_t roff = BLK ? (size_t)(m0 / 16) * (I / 64) * 1024 + 8 * lane : (size_t)(m0 + r16) * I + kKV * 8 * g;
     const uint16_t* wd = (routed ? w.down + (size_t)e * d * I : w.s_down) + roff;
-    for (int cb = cb_first; cb < n; cb += 16) {
+    int cb = cb_first;
+    if (!WIDE && !routed) {
+      // the shared expert: two 16-token passes per weight stream
+      for (; cb + 16 < n; cb += 32) {
+        int col[2];
+        bool valid[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          valid[p] = cb + 16 * p + r16 < n;
+          col[p] = valid[p] ? row0 + cb + 16 * p + r16 : row0;
+        }
+        f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        down_bf16_block_x2<2, BLK>(wd, h + (size_t)col[0] * I + kKV * 8 * g, h + (size_t)col[1] * I + kKV * 8 * g, I,
+                                   acc);
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+          if (valid[p])
+            *reinterpret_cast<float4*>(y + (size_t)col[p] * d + m0 + 4 * g) =
+                make_float4(acc[p][0], acc[p][1], acc[p][2], acc[p][3]);
+      }
+    }
+    for (; cb < n; cb += 16) {
       const bool valid = cb + r16 < n;
       const int col = valid ? row0 + cb + r16 : row0;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
