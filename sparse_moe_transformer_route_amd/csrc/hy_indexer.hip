@@ -54,14 +54,16 @@ __global__ void __launch_bounds__(256) indexer_scores_kernel(const uint16_t* __r
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int col = lane & 31, hf = lane >> 5;
   const uint16_t* kb = keys + (size_t)b * S * D;
-  // keys past S reload the last key (scores not stored)
+  // keys past S reload the last key (scores not stored); each key row is read once per
+  // query and a wave's op covers 4 whole rows, so the loads take the non-temporal hint
+  // (scoring 0.0953 -> 0.0914 ms at 32 x 64K keys)
 #pragma unroll
   for (int i = 0; i < OPS; ++i) {
     const int pq = 256 * i + tid;
     const int row = pq / CH, lc = (pq % CH) ^ (row % 16);
     const int key = min(s0 + row, S - 1);
     __builtin_amdgcn_global_load_lds((const void*)(kb + (size_t)key * D + 8 * lc), IX_LDS(lk + 16 * (256 * i + 64 * wv)),
-                                     16, 0, 0);
+                                     16, 0, 2);
   }
   // the query's fragments (row = head) and the lane's 16 head weights, while the keys land
   uint4 fa[NS];
