@@ -396,7 +396,9 @@ def test_block_bf16_matches_layout_definition():
 
 
 @pytest.mark.parametrize("path", PATHS)
-@pytest.mark.parametrize("shape", [(40, 512, 16, 2, 256), (300, 768, 8, 2, 384), (33, 256, 4, 4, 128)])
+# T=50: the shared expert's second pair of 16-token passes holds 16 + 2 valid tokens
+@pytest.mark.parametrize("shape", [(40, 512, 16, 2, 256), (300, 768, 8, 2, 384), (33, 256, 4, 4, 128),
+                                   (50, 256, 16, 4, 128)])
 def test_blocked_weights_match_row_major(shape, path):
     T, d, E, k, I = shape
     say(f"[case] blocked bf16 weights T={T} d={d} E={E} k={k} I={I} path={path}")
